@@ -1,0 +1,733 @@
+/*
+ * GPT-2 training-step ORACLE.  Test infrastructure only.
+ *
+ * This file is the plain, slow, obviously-correct CPU definition of one GPT-2
+ * training step: token+position embedding, L pre-LN transformer blocks,
+ * tied classifier, softmax cross-entropy, a hand-derived backward pass,
+ * global-norm gradient clipping and AdamW.  Only the tests, the smoke check
+ * and the benchmark's CPU-baseline leg may load it; the product library
+ * shares no code, header, table or helper with it.
+ *
+ * It is compiled twice from this one source: REAL=float (the fp32 oracle the
+ * GPU path is compared against) and REAL=double (used for central finite
+ * difference checks of every backward function).  Every reduction accumulates
+ * in double and runs in one fixed order, and OpenMP only splits loops over
+ * independent outputs, so results do not depend on the thread count.
+ *
+ * Sources (the pages describing llm.c):
+ *  [P5]  "llm.c: GPT-2 training in plain C, with every gradient written by
+ *        hand" (fernfant learning-robotics lesson): section 2 "How the code
+ *        works" lists the layer pairs (encoder, layernorm, matmul, attention,
+ *        gelu, residual, softmax, crossentropy), the per-layer forward call
+ *        sequence, the attention-backward accumulation rule, the causal
+ *        t2 <= t loop, the saved mean/rstd and attention weights, and the
+ *        single-block memory layout; section 3 "Run it, tested" prints the
+ *        model config (V=50257 padded to 50304, L=12, NH=12, C=768,
+ *        maxT=1024) and the counts N=124,475,904 and 73,347,840 activations.
+ *  [P4]  pyshine.com tour of llm.c: the fused classifier (output projection
+ *        merged with the softmax loss), the AdamW and global-norm headers.
+ *  [P1]  "llm.c's Origin and the Future of LLM Compilers" transcript,
+ *        section "Pure C": m and v buffers of AdamW, mean/rstd saved for the
+ *        layernorm backward, one up-front allocation.
+ *
+ * Readings where the pages are silent (GELU form, LN epsilon, weight tying,
+ * init RNG, AdamW details) are the plain ones: tanh-approximation GELU,
+ * eps=1e-5 with biased variance, classifier tied to wte (pinned by N),
+ * SplitMix64 + Box-Muller init, bias-corrected decoupled AdamW.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#ifndef REAL
+#define REAL float
+#endif
+typedef double ACC;
+
+typedef struct {
+    int L, C, NH, maxT, V, Vp;
+} orc_config;
+
+enum { NPARAM = 16, NACT = 23 };
+
+/* ------------------------------------------------------------------------ */
+/* sizes and layout                                                          */
+/* ------------------------------------------------------------------------ */
+
+/* Parameter tensors, in this fixed order (names from [P5] section 2):
+ * wte (Vp,C), wpe (maxT,C), ln1w (L,C), ln1b (L,C), qkvw (L,3C,C),
+ * qkvb (L,3C), attprojw (L,C,C), attprojb (L,C), ln2w (L,C), ln2b (L,C),
+ * fcw (L,4C,C), fcb (L,4C), fcprojw (L,C,4C), fcprojb (L,C), lnfw (C),
+ * lnfb (C).  Weight matrices are (out, in) row-major; the classifier
+ * reuses wte (tied), which is what makes N come out at 124,475,904. */
+void orc_param_sizes(const orc_config* g, size_t* s) {
+    size_t L = g->L, C = g->C;
+    s[0] = (size_t)g->Vp * C;
+    s[1] = (size_t)g->maxT * C;
+    s[2] = L * C;
+    s[3] = L * C;
+    s[4] = L * 3 * C * C;
+    s[5] = L * 3 * C;
+    s[6] = L * C * C;
+    s[7] = L * C;
+    s[8] = L * C;
+    s[9] = L * C;
+    s[10] = L * 4 * C * C;
+    s[11] = L * 4 * C;
+    s[12] = L * C * 4 * C;
+    s[13] = L * C;
+    s[14] = C;
+    s[15] = C;
+}
+
+size_t orc_num_params(const orc_config* g) {
+    size_t s[NPARAM], n = 0;
+    orc_param_sizes(g, s);
+    for (int i = 0; i < NPARAM; i++) n += s[i];
+    return n;
+}
+
+/* Activation tensors of the CPU layout ([P5] section 2: the forward pass
+ * keeps att, the layernorm mean and rstd, ... for the backward pass):
+ * encoded, ln1, ln1_mean, ln1_rstd, qkv, atty, preatt, att, attproj,
+ * residual2, ln2, ln2_mean, ln2_rstd, fch, fch_gelu, fcproj, residual3,
+ * lnf, lnf_mean, lnf_rstd, logits, probs, losses. */
+void orc_act_sizes(const orc_config* g, int B, int T, size_t* s) {
+    size_t L = g->L, C = g->C, NH = g->NH, BT = (size_t)B * T, Vp = g->Vp;
+    s[0] = BT * C;
+    s[1] = L * BT * C;
+    s[2] = L * BT;
+    s[3] = L * BT;
+    s[4] = L * BT * 3 * C;
+    s[5] = L * BT * C;
+    s[6] = L * B * NH * (size_t)T * T;
+    s[7] = L * B * NH * (size_t)T * T;
+    s[8] = L * BT * C;
+    s[9] = L * BT * C;
+    s[10] = L * BT * C;
+    s[11] = L * BT;
+    s[12] = L * BT;
+    s[13] = L * BT * 4 * C;
+    s[14] = L * BT * 4 * C;
+    s[15] = L * BT * C;
+    s[16] = L * BT * C;
+    s[17] = BT * C;
+    s[18] = BT;
+    s[19] = BT;
+    s[20] = BT * Vp;
+    s[21] = BT * Vp;
+    s[22] = BT;
+}
+
+size_t orc_num_acts(const orc_config* g, int B, int T) {
+    size_t s[NACT], n = 0;
+    orc_act_sizes(g, B, T, s);
+    for (int i = 0; i < NACT; i++) n += s[i];
+    return n;
+}
+
+/* ------------------------------------------------------------------------ */
+/* initialisation: SplitMix64 (Steele, Lea & Flood 2014) + Box-Muller        */
+/* ------------------------------------------------------------------------ */
+
+/* SplitMix64 output function applied to the state seed + n*golden_gamma. */
+static uint64_t sm64_draw(uint64_t seed, uint64_t n) {
+    uint64_t z = seed + n * 0x9E3779B97F4A7C15ULL;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ULL;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBULL;
+    return z ^ (z >> 31);
+}
+
+/* Standard normal for flat parameter index gidx: draws 2*gidx+1 and
+ * 2*gidx+2 of the SplitMix64 stream, Box-Muller cosine branch, in double. */
+static double normal_at(uint64_t seed, uint64_t gidx) {
+    uint64_t w0 = sm64_draw(seed, 2 * gidx + 1);
+    uint64_t w1 = sm64_draw(seed, 2 * gidx + 2);
+    double u1 = ((double)(w0 >> 11) + 0.5) * (1.0 / 9007199254740992.0);
+    double u2 = (double)(w1 >> 11) * (1.0 / 9007199254740992.0);
+    double r = sqrt(-2.0 * log(u1));
+    return r * cos(6.283185307179586 * u2);
+}
+
+/* GPT-2 init as fixed for the workloads: wte rows [0,V), wpe, qkvw, fcw ~
+ * N(0, 0.02); the residual projections attprojw, fcprojw ~ N(0, 0.02 /
+ * sqrt(2L)); biases 0, LN gains 1, LN biases 0, padded wte rows 0.
+ * Each value is (float)(std * z) with z from normal_at(seed, flat index). */
+void orc_init_params(const orc_config* g, uint64_t seed, REAL* params) {
+    size_t s[NPARAM], off[NPARAM], o = 0;
+    orc_param_sizes(g, s);
+    for (int i = 0; i < NPARAM; i++) { off[i] = o; o += s[i]; }
+    double std_main = 0.02;
+    double std_res = 0.02 / sqrt(2.0 * (double)g->L);
+    for (int i = 0; i < NPARAM; i++) {
+        REAL* p = params + off[i];
+        size_t n = s[i];
+        if (i == 0 || i == 1 || i == 4 || i == 10 || i == 6 || i == 12) {
+            double sd = (i == 6 || i == 12) ? std_res : std_main;
+            size_t nlive = (i == 0) ? (size_t)g->V * g->C : n;
+            #pragma omp parallel for schedule(static)
+            for (size_t j = 0; j < n; j++) {
+                if (j < nlive) p[j] = (REAL)(float)(sd * normal_at(seed, off[i] + j));
+                else p[j] = 0;
+            }
+        } else if (i == 2 || i == 8 || i == 14) {
+            for (size_t j = 0; j < n; j++) p[j] = 1;
+        } else {
+            for (size_t j = 0; j < n; j++) p[j] = 0;
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* layer functions (forward / backward pairs of [P5] section 2)             */
+/* ------------------------------------------------------------------------ */
+
+/* out[b,t,:] = wte[inp[b,t],:] + wpe[t,:] */
+void orc_encoder_forward(REAL* out, const int* inp, const REAL* wte, const REAL* wpe,
+                         int B, int T, int C) {
+    #pragma omp parallel for collapse(2)
+    for (int b = 0; b < B; b++)
+        for (int t = 0; t < T; t++) {
+            REAL* o = out + ((size_t)b * T + t) * C;
+            const REAL* we = wte + (size_t)inp[b * T + t] * C;
+            const REAL* pe = wpe + (size_t)t * C;
+            for (int c = 0; c < C; c++) o[c] = we[c] + pe[c];
+        }
+}
+
+/* dwte[inp[b,t],:] += dout[b,t,:]; dwpe[t,:] += dout[b,t,:].  Parallel over
+ * channels only, each channel summed over (b,t) in order. */
+void orc_encoder_backward(REAL* dwte, REAL* dwpe, const REAL* dout, const int* inp,
+                          int B, int T, int C) {
+    #pragma omp parallel for
+    for (int c = 0; c < C; c++) {
+        for (int b = 0; b < B; b++)
+            for (int t = 0; t < T; t++) {
+                REAL d = dout[((size_t)b * T + t) * C + c];
+                dwte[(size_t)inp[b * T + t] * C + c] += d;
+                dwpe[(size_t)t * C + c] += d;
+            }
+    }
+}
+
+/* LayerNorm over the last dim of N rows: biased variance, eps = 1e-5;
+ * saves mean and rstd = 1/sqrt(var+eps) for the backward ([P1] "Pure C"). */
+void orc_layernorm_forward(REAL* out, REAL* mean, REAL* rstd, const REAL* inp,
+                           const REAL* w, const REAL* b, int N, int C) {
+    #pragma omp parallel for
+    for (int n = 0; n < N; n++) {
+        const REAL* x = inp + (size_t)n * C;
+        ACC m = 0;
+        for (int c = 0; c < C; c++) m += x[c];
+        m /= C;
+        ACC v = 0;
+        for (int c = 0; c < C; c++) { ACC d = x[c] - m; v += d * d; }
+        v /= C;
+        ACC r = 1.0 / sqrt(v + 1e-5);
+        REAL* o = out + (size_t)n * C;
+        for (int c = 0; c < C; c++) o[c] = (REAL)(((x[c] - m) * r) * w[c] + b[c]);
+        mean[n] = (REAL)m;
+        rstd[n] = (REAL)r;
+    }
+}
+
+/* With xhat = (x-mean)*rstd and g = dout*w:
+ *   dinp += rstd * (g - mean_c(g) - xhat * mean_c(g*xhat))
+ *   dw   += sum_rows dout*xhat,   db += sum_rows dout. */
+void orc_layernorm_backward(REAL* dinp, REAL* dw, REAL* db, const REAL* dout,
+                            const REAL* inp, const REAL* w, const REAL* mean,
+                            const REAL* rstd, int N, int C) {
+    #pragma omp parallel for
+    for (int n = 0; n < N; n++) {
+        const REAL* x = inp + (size_t)n * C;
+        const REAL* dy = dout + (size_t)n * C;
+        ACC m = mean[n], r = rstd[n];
+        ACC sg = 0, sgx = 0;
+        for (int c = 0; c < C; c++) {
+            ACC xh = (x[c] - m) * r;
+            ACC gg = (ACC)dy[c] * w[c];
+            sg += gg;
+            sgx += gg * xh;
+        }
+        sg /= C;
+        sgx /= C;
+        REAL* dx = dinp + (size_t)n * C;
+        for (int c = 0; c < C; c++) {
+            ACC xh = (x[c] - m) * r;
+            ACC gg = (ACC)dy[c] * w[c];
+            dx[c] = (REAL)(dx[c] + r * (gg - sg - xh * sgx));
+        }
+    }
+    #pragma omp parallel for
+    for (int c = 0; c < C; c++) {
+        ACC aw = 0, ab = 0;
+        for (int n = 0; n < N; n++) {
+            ACC xh = (inp[(size_t)n * C + c] - (ACC)mean[n]) * rstd[n];
+            ACC d = dout[(size_t)n * C + c];
+            aw += d * xh;
+            ab += d;
+        }
+        dw[c] = (REAL)(dw[c] + aw);
+        db[c] = (REAL)(db[c] + ab);
+    }
+}
+
+/* Linear layer y = x W^T + b on N rows: inp (N,C), w (OC,C), bias (OC) or
+ * NULL, out (N,OC).  ([P5] section 2: matmul_forward(out, inp, w, b, ...)) */
+void orc_matmul_forward(REAL* out, const REAL* inp, const REAL* w, const REAL* bias,
+                        int N, int C, int OC) {
+    #pragma omp parallel for
+    for (int n = 0; n < N; n++) {
+        const REAL* x = inp + (size_t)n * C;
+        for (int o = 0; o < OC; o++) {
+            const REAL* wr = w + (size_t)o * C;
+            ACC acc = bias ? (ACC)bias[o] : 0.0;
+            #pragma omp simd reduction(+:acc)
+            for (int c = 0; c < C; c++) acc += (ACC)x[c] * wr[c];
+            out[(size_t)n * OC + o] = (REAL)acc;
+        }
+    }
+}
+
+/* Backward of the linear layer, each forward "out += inp*w" read in reverse:
+ *   dinp += dout W,  dw += dout^T inp,  dbias += sum_rows dout. */
+void orc_matmul_backward(REAL* dinp, REAL* dw, REAL* dbias, const REAL* dout,
+                         const REAL* inp, const REAL* w, int N, int C, int OC) {
+    #pragma omp parallel
+    {
+        ACC* acc = (ACC*)malloc(sizeof(ACC) * (size_t)C);
+        #pragma omp for
+        for (int n = 0; n < N; n++) {
+            for (int c = 0; c < C; c++) acc[c] = 0;
+            for (int o = 0; o < OC; o++) {
+                ACC d = dout[(size_t)n * OC + o];
+                const REAL* wr = w + (size_t)o * C;
+                #pragma omp simd
+                for (int c = 0; c < C; c++) acc[c] += d * wr[c];
+            }
+            REAL* dx = dinp + (size_t)n * C;
+            for (int c = 0; c < C; c++) dx[c] = (REAL)(dx[c] + acc[c]);
+        }
+        #pragma omp for
+        for (int o = 0; o < OC; o++) {
+            for (int c = 0; c < C; c++) acc[c] = 0;
+            ACC ab = 0;
+            for (int n = 0; n < N; n++) {
+                ACC d = dout[(size_t)n * OC + o];
+                const REAL* x = inp + (size_t)n * C;
+                ab += d;
+                #pragma omp simd
+                for (int c = 0; c < C; c++) acc[c] += d * x[c];
+            }
+            REAL* dwr = dw + (size_t)o * C;
+            for (int c = 0; c < C; c++) dwr[c] = (REAL)(dwr[c] + acc[c]);
+            if (dbias) dbias[o] = (REAL)(dbias[o] + ab);
+        }
+        free(acc);
+    }
+}
+
+/* Causal multi-head self-attention on qkv (B,T,3C) packed q|k|v, head h
+ * owning channels [h*hs, (h+1)*hs) of each block.  For t2 <= t:
+ * preatt = q_t . k_t2 / sqrt(hs); att = softmax over t2 <= t (max
+ * subtracted); out_t = sum_t2 att * v_t2.  Entries with t2 > t are 0. */
+void orc_attention_forward(REAL* out, REAL* preatt, REAL* att, const REAL* qkv,
+                           int B, int T, int C, int NH) {
+    int hs = C / NH;
+    ACC scale = 1.0 / sqrt((ACC)hs);
+    size_t C3 = 3 * (size_t)C;
+    #pragma omp parallel for collapse(3)
+    for (int b = 0; b < B; b++)
+        for (int t = 0; t < T; t++)
+            for (int h = 0; h < NH; h++) {
+                const REAL* q = qkv + ((size_t)b * T + t) * C3 + (size_t)h * hs;
+                REAL* pre = preatt + (((size_t)b * NH + h) * T + t) * T;
+                REAL* a = att + (((size_t)b * NH + h) * T + t) * T;
+                ACC mx = -INFINITY;
+                for (int t2 = 0; t2 <= t; t2++) {
+                    const REAL* k = qkv + ((size_t)b * T + t2) * C3 + C + (size_t)h * hs;
+                    ACC s = 0;
+                    for (int i = 0; i < hs; i++) s += (ACC)q[i] * k[i];
+                    s *= scale;
+                    pre[t2] = (REAL)s;
+                    if (s > mx) mx = s;
+                }
+                ACC den = 0;
+                for (int t2 = 0; t2 <= t; t2++) den += exp((ACC)pre[t2] - mx);
+                for (int t2 = 0; t2 < T; t2++) {
+                    if (t2 <= t) a[t2] = (REAL)(exp((ACC)pre[t2] - mx) / den);
+                    else { a[t2] = 0; pre[t2] = 0; }
+                }
+                REAL* o = out + ((size_t)b * T + t) * C + (size_t)h * hs;
+                for (int i = 0; i < hs; i++) {
+                    ACC y = 0;
+                    for (int t2 = 0; t2 <= t; t2++) {
+                        const REAL* v = qkv + ((size_t)b * T + t2) * C3 + 2 * (size_t)C + (size_t)h * hs;
+                        y += (ACC)a[t2] * v[i];
+                    }
+                    o[i] = (REAL)y;
+                }
+            }
+}
+
+/* Attention backward ([P5] section 2: "out += att*value" becomes
+ * datt += value*dout and dvalue += att*dout):
+ *   datt_t2 = v_t2 . dout_t;  dv_t2 += att_t2 dout_t;
+ *   dpre_t2 = att_t2 (datt_t2 - sum_t3 att_t3 datt_t3);
+ *   dq_t += dpre_t2 k_t2 / sqrt(hs);  dk_t2 += dpre_t2 q_t / sqrt(hs).
+ * One (b,h) pair owns every row it writes, so (b,h) is the parallel loop. */
+void orc_attention_backward(REAL* dqkv, const REAL* dout, const REAL* qkv,
+                            const REAL* att, int B, int T, int C, int NH) {
+    int hs = C / NH;
+    ACC scale = 1.0 / sqrt((ACC)hs);
+    size_t C3 = 3 * (size_t)C;
+    #pragma omp parallel
+    {
+        ACC* datt = (ACC*)malloc(sizeof(ACC) * (size_t)T);
+        ACC* dpre = (ACC*)malloc(sizeof(ACC) * (size_t)T);
+        #pragma omp for collapse(2)
+        for (int b = 0; b < B; b++)
+            for (int h = 0; h < NH; h++) {
+                for (int t = 0; t < T; t++) {
+                    const REAL* a = att + (((size_t)b * NH + h) * T + t) * T;
+                    const REAL* dy = dout + ((size_t)b * T + t) * C + (size_t)h * hs;
+                    const REAL* q = qkv + ((size_t)b * T + t) * C3 + (size_t)h * hs;
+                    REAL* dq = dqkv + ((size_t)b * T + t) * C3 + (size_t)h * hs;
+                    for (int t2 = 0; t2 <= t; t2++) {
+                        const REAL* v = qkv + ((size_t)b * T + t2) * C3 + 2 * (size_t)C + (size_t)h * hs;
+                        REAL* dv = dqkv + ((size_t)b * T + t2) * C3 + 2 * (size_t)C + (size_t)h * hs;
+                        ACC s = 0;
+                        for (int i = 0; i < hs; i++) {
+                            s += (ACC)v[i] * dy[i];
+                            dv[i] = (REAL)(dv[i] + (ACC)a[t2] * dy[i]);
+                        }
+                        datt[t2] = s;
+                    }
+                    ACC inner = 0;
+                    for (int t3 = 0; t3 <= t; t3++) inner += (ACC)a[t3] * datt[t3];
+                    for (int t2 = 0; t2 <= t; t2++) dpre[t2] = (ACC)a[t2] * (datt[t2] - inner);
+                    for (int t2 = 0; t2 <= t; t2++) {
+                        const REAL* k = qkv + ((size_t)b * T + t2) * C3 + C + (size_t)h * hs;
+                        REAL* dk = dqkv + ((size_t)b * T + t2) * C3 + C + (size_t)h * hs;
+                        ACC g = dpre[t2] * scale;
+                        for (int i = 0; i < hs; i++) {
+                            dq[i] = (REAL)(dq[i] + g * k[i]);
+                            dk[i] = (REAL)(dk[i] + g * q[i]);
+                        }
+                    }
+                }
+            }
+        free(datt);
+        free(dpre);
+    }
+}
+
+/* GELU, tanh approximation: 0.5 u (1 + tanh(k (u + 0.044715 u^3))),
+ * k = sqrt(2/pi). */
+static ACC gelu_k(void) { return sqrt(2.0 / 3.14159265358979323846); }
+
+void orc_gelu_forward(REAL* out, const REAL* inp, size_t n) {
+    ACC k = gelu_k();
+    #pragma omp parallel for
+    for (size_t i = 0; i < n; i++) {
+        ACC u = inp[i];
+        out[i] = (REAL)(0.5 * u * (1.0 + tanh(k * (u + 0.044715 * u * u * u))));
+    }
+}
+
+/* d/du of the above: 0.5(1+tau) + 0.5 u (1-tau^2) k (1 + 3*0.044715 u^2). */
+void orc_gelu_backward(REAL* dinp, const REAL* inp, const REAL* dout, size_t n) {
+    ACC k = gelu_k();
+    #pragma omp parallel for
+    for (size_t i = 0; i < n; i++) {
+        ACC u = inp[i];
+        ACC tau = tanh(k * (u + 0.044715 * u * u * u));
+        ACC d = 0.5 * (1.0 + tau) + 0.5 * u * (1.0 - tau * tau) * k * (1.0 + 3.0 * 0.044715 * u * u);
+        dinp[i] = (REAL)(dinp[i] + d * dout[i]);
+    }
+}
+
+/* Softmax over the real vocabulary v < V of each of N rows of width Vp
+ * (padded columns excluded, their probability set to 0), and the
+ * cross-entropy loss_n = logsumexp - logit[target]. */
+void orc_softmax_ce_forward(REAL* losses, REAL* probs, const REAL* logits,
+                            const int* targets, int N, int V, int Vp) {
+    #pragma omp parallel for
+    for (int n = 0; n < N; n++) {
+        const REAL* z = logits + (size_t)n * Vp;
+        REAL* p = probs + (size_t)n * Vp;
+        ACC mx = -INFINITY;
+        for (int v = 0; v < V; v++) if (z[v] > mx) mx = z[v];
+        ACC s = 0;
+        for (int v = 0; v < V; v++) s += exp((ACC)z[v] - mx);
+        for (int v = 0; v < Vp; v++) p[v] = (v < V) ? (REAL)(exp((ACC)z[v] - mx) / s) : 0;
+        if (targets) losses[n] = (REAL)(mx + log(s) - (ACC)z[targets[n]]);
+    }
+}
+
+/* dlogits[n,v] = (probs[n,v] - [v == target]) * dloss[n] for v < V; 0 for
+ * the padded columns. */
+void orc_softmax_ce_backward(REAL* dlogits, const REAL* dlosses, const REAL* probs,
+                             const int* targets, int N, int V, int Vp) {
+    #pragma omp parallel for
+    for (int n = 0; n < N; n++) {
+        REAL* d = dlogits + (size_t)n * Vp;
+        const REAL* p = probs + (size_t)n * Vp;
+        for (int v = 0; v < Vp; v++) {
+            if (v < V) d[v] = (REAL)(d[v] + ((ACC)p[v] - (v == targets[n] ? 1.0 : 0.0)) * dlosses[n]);
+        }
+    }
+}
+
+/* sqrt(sum g^2) over n values, summed in index order in double. */
+double orc_global_norm(const REAL* g, size_t n) {
+    ACC s = 0;
+    for (size_t i = 0; i < n; i++) s += (ACC)g[i] * g[i];
+    return sqrt(s);
+}
+
+/* Decoupled, bias-corrected AdamW for step t >= 1:
+ *   m = b1 m + (1-b1) g;  v = b2 v + (1-b2) g^2;
+ *   mhat = m/(1-b1^t);  vhat = v/(1-b2^t);
+ *   theta -= lr (mhat/(sqrt(vhat)+eps) + wd theta).
+ * grad_scale multiplies g first (the global-norm clip factor, 1 if none). */
+void orc_adamw_update(REAL* params, const REAL* grads, REAL* m, REAL* v, size_t n,
+                      double lr, double b1, double b2, double eps, double wd, int t,
+                      double grad_scale) {
+    ACC c1 = 1.0 - pow(b1, t), c2 = 1.0 - pow(b2, t);
+    #pragma omp parallel for
+    for (size_t i = 0; i < n; i++) {
+        ACC g = (ACC)grads[i] * grad_scale;
+        ACC mi = b1 * (ACC)m[i] + (1.0 - b1) * g;
+        ACC vi = b2 * (ACC)v[i] + (1.0 - b2) * g * g;
+        ACC mh = mi / c1, vh = vi / c2;
+        ACC th = params[i];
+        params[i] = (REAL)(th - lr * (mh / (sqrt(vh) + eps) + wd * th));
+        m[i] = (REAL)mi;
+        v[i] = (REAL)vi;
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* the model: one allocation for params, grads, m, v, acts, act grads       */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+    orc_config cfg;
+    int B, T;
+    size_t psz[NPARAM], np;
+    size_t asz[NACT], na;
+    REAL *params, *grads, *m, *v, *acts, *gacts;
+    REAL *P[NPARAM], *G[NPARAM], *A[NACT], *GA[NACT];
+    int *inputs, *targets;
+    int have_targets;
+    double grad_scale;
+} orc_model;
+
+orc_model* orc_create(const orc_config* cfg, int B, int T) {
+    if (cfg->C % cfg->NH != 0 || T > cfg->maxT || cfg->V > cfg->Vp) return NULL;
+    orc_model* M = (orc_model*)calloc(1, sizeof(orc_model));
+    M->cfg = *cfg;
+    M->B = B;
+    M->T = T;
+    orc_param_sizes(cfg, M->psz);
+    orc_act_sizes(cfg, B, T, M->asz);
+    M->np = orc_num_params(cfg);
+    M->na = orc_num_acts(cfg, B, T);
+    M->params = (REAL*)calloc(M->np, sizeof(REAL));
+    M->grads = (REAL*)calloc(M->np, sizeof(REAL));
+    M->m = (REAL*)calloc(M->np, sizeof(REAL));
+    M->v = (REAL*)calloc(M->np, sizeof(REAL));
+    M->acts = (REAL*)calloc(M->na, sizeof(REAL));
+    M->gacts = (REAL*)calloc(M->na, sizeof(REAL));
+    M->inputs = (int*)calloc((size_t)B * T, sizeof(int));
+    M->targets = (int*)calloc((size_t)B * T, sizeof(int));
+    if (!M->params || !M->grads || !M->m || !M->v || !M->acts || !M->gacts) return NULL;
+    size_t o = 0;
+    for (int i = 0; i < NPARAM; i++) { M->P[i] = M->params + o; M->G[i] = M->grads + o; o += M->psz[i]; }
+    o = 0;
+    for (int i = 0; i < NACT; i++) { M->A[i] = M->acts + o; M->GA[i] = M->gacts + o; o += M->asz[i]; }
+    M->grad_scale = 1.0;
+    return M;
+}
+
+void orc_free(orc_model* M) {
+    if (!M) return;
+    free(M->params); free(M->grads); free(M->m); free(M->v);
+    free(M->acts); free(M->gacts); free(M->inputs); free(M->targets);
+    free(M);
+}
+
+REAL* orc_params(orc_model* M) { return M->params; }
+REAL* orc_grads(orc_model* M) { return M->grads; }
+REAL* orc_mbuf(orc_model* M) { return M->m; }
+REAL* orc_vbuf(orc_model* M) { return M->v; }
+REAL* orc_acts(orc_model* M) { return M->acts; }
+REAL* orc_act_grads(orc_model* M) { return M->gacts; }
+size_t orc_model_num_params(orc_model* M) { return M->np; }
+size_t orc_model_num_acts(orc_model* M) { return M->na; }
+
+/* Forward pass ([P5] section 2: gpt2_forward calls each layer in order; per
+ * layer LN1 -> qkv -> attention -> attproj -> residual -> LN2 -> fc -> GELU
+ * -> fcproj -> residual).  Returns the mean loss over the B*T positions, or
+ * NaN when targets is NULL (then only logits and probs are produced). */
+double orc_forward(orc_model* M, const int* inputs, const int* targets) {
+    const orc_config* g = &M->cfg;
+    int B = M->B, T = M->T, C = g->C, L = g->L, NH = g->NH, V = g->V, Vp = g->Vp;
+    int BT = B * T;
+    memcpy(M->inputs, inputs, sizeof(int) * (size_t)BT);
+    M->have_targets = targets != NULL;
+    if (targets) memcpy(M->targets, targets, sizeof(int) * (size_t)BT);
+    REAL** P = M->P;
+    REAL** A = M->A;
+    size_t BTC = (size_t)BT * C;
+    orc_encoder_forward(A[0], M->inputs, P[0], P[1], B, T, C);
+    const REAL* residual = A[0];
+    for (int l = 0; l < L; l++) {
+        REAL* ln1 = A[1] + l * BTC;
+        REAL* ln1m = A[2] + (size_t)l * BT;
+        REAL* ln1r = A[3] + (size_t)l * BT;
+        REAL* qkv = A[4] + l * BTC * 3;
+        REAL* atty = A[5] + l * BTC;
+        REAL* pre = A[6] + (size_t)l * B * NH * T * T;
+        REAL* att = A[7] + (size_t)l * B * NH * T * T;
+        REAL* attproj = A[8] + l * BTC;
+        REAL* res2 = A[9] + l * BTC;
+        REAL* ln2 = A[10] + l * BTC;
+        REAL* ln2m = A[11] + (size_t)l * BT;
+        REAL* ln2r = A[12] + (size_t)l * BT;
+        REAL* fch = A[13] + l * BTC * 4;
+        REAL* fchg = A[14] + l * BTC * 4;
+        REAL* fcproj = A[15] + l * BTC;
+        REAL* res3 = A[16] + l * BTC;
+        orc_layernorm_forward(ln1, ln1m, ln1r, residual, P[2] + (size_t)l * C, P[3] + (size_t)l * C, BT, C);
+        orc_matmul_forward(qkv, ln1, P[4] + (size_t)l * 3 * C * C, P[5] + (size_t)l * 3 * C, BT, C, 3 * C);
+        orc_attention_forward(atty, pre, att, qkv, B, T, C, NH);
+        orc_matmul_forward(attproj, atty, P[6] + (size_t)l * C * C, P[7] + (size_t)l * C, BT, C, C);
+        for (size_t i = 0; i < BTC; i++) res2[i] = residual[i] + attproj[i];
+        orc_layernorm_forward(ln2, ln2m, ln2r, res2, P[8] + (size_t)l * C, P[9] + (size_t)l * C, BT, C);
+        orc_matmul_forward(fch, ln2, P[10] + (size_t)l * 4 * C * C, P[11] + (size_t)l * 4 * C, BT, C, 4 * C);
+        orc_gelu_forward(fchg, fch, BTC * 4);
+        orc_matmul_forward(fcproj, fchg, P[12] + (size_t)l * 4 * C * C, P[13] + (size_t)l * C, BT, 4 * C, C);
+        for (size_t i = 0; i < BTC; i++) res3[i] = res2[i] + fcproj[i];
+        residual = res3;
+    }
+    orc_layernorm_forward(A[17], A[18], A[19], residual, P[14], P[15], BT, C);
+    orc_matmul_forward(A[20], A[17], P[0], NULL, BT, C, Vp);
+    orc_softmax_ce_forward(A[22], A[21], A[20], targets ? M->targets : NULL, BT, V, Vp);
+    if (!targets) return NAN;
+    ACC s = 0;
+    for (int i = 0; i < BT; i++) s += A[22][i];
+    return s / BT;
+}
+
+void orc_zero_grad(orc_model* M) {
+    memset(M->grads, 0, sizeof(REAL) * M->np);
+    M->grad_scale = 1.0;
+}
+
+/* Backward pass: the forward list in reverse, seeding dloss = 1/(B*T) per
+ * position ([P5] section 2).  Parameter gradients accumulate (+=);
+ * activation gradients are recomputed from zero on every call. */
+int orc_backward(orc_model* M) {
+    if (!M->have_targets) return -1;
+    const orc_config* g = &M->cfg;
+    int B = M->B, T = M->T, C = g->C, L = g->L, NH = g->NH, V = g->V, Vp = g->Vp;
+    int BT = B * T;
+    size_t BTC = (size_t)BT * C;
+    REAL** P = M->P;
+    REAL** G = M->G;
+    REAL** A = M->A;
+    REAL** D = M->GA;
+    memset(M->gacts, 0, sizeof(REAL) * M->na);
+    for (int i = 0; i < BT; i++) D[22][i] = (REAL)(1.0 / BT);
+    orc_softmax_ce_backward(D[20], D[22], A[21], M->targets, BT, V, Vp);
+    orc_matmul_backward(D[17], G[0], NULL, D[20], A[17], P[0], BT, C, Vp);
+    const REAL* residual = A[16] + (size_t)(L - 1) * BTC;
+    REAL* dresidual = D[16] + (size_t)(L - 1) * BTC;
+    orc_layernorm_backward(dresidual, G[14], G[15], D[17], residual, P[14], A[18], A[19], BT, C);
+    for (int l = L - 1; l >= 0; l--) {
+        const REAL* res_in = l == 0 ? A[0] : A[16] + (size_t)(l - 1) * BTC;
+        REAL* dres_in = l == 0 ? D[0] : D[16] + (size_t)(l - 1) * BTC;
+        REAL* dres3 = D[16] + (size_t)l * BTC;
+        REAL* ln1 = A[1] + l * BTC;
+        REAL* ln1m = A[2] + (size_t)l * BT;
+        REAL* ln1r = A[3] + (size_t)l * BT;
+        REAL* qkv = A[4] + l * BTC * 3;
+        REAL* atty = A[5] + l * BTC;
+        REAL* att = A[7] + (size_t)l * B * NH * T * T;
+        REAL* res2 = A[9] + l * BTC;
+        REAL* ln2 = A[10] + l * BTC;
+        REAL* ln2m = A[11] + (size_t)l * BT;
+        REAL* ln2r = A[12] + (size_t)l * BT;
+        REAL* fch = A[13] + l * BTC * 4;
+        REAL* fchg = A[14] + l * BTC * 4;
+        REAL* dln1 = D[1] + l * BTC;
+        REAL* dqkv = D[4] + l * BTC * 3;
+        REAL* datty = D[5] + l * BTC;
+        REAL* dattproj = D[8] + l * BTC;
+        REAL* dres2 = D[9] + l * BTC;
+        REAL* dln2 = D[10] + l * BTC;
+        REAL* dfch = D[13] + l * BTC * 4;
+        REAL* dfchg = D[14] + l * BTC * 4;
+        REAL* dfcproj = D[15] + l * BTC;
+        /* res3 = res2 + fcproj: the gradient flows unchanged to both */
+        for (size_t i = 0; i < BTC; i++) { dres2[i] += dres3[i]; dfcproj[i] += dres3[i]; }
+        orc_matmul_backward(dfchg, G[12] + (size_t)l * 4 * C * C, G[13] + (size_t)l * C, dfcproj, fchg,
+                            P[12] + (size_t)l * 4 * C * C, BT, 4 * C, C);
+        orc_gelu_backward(dfch, fch, dfchg, BTC * 4);
+        orc_matmul_backward(dln2, G[10] + (size_t)l * 4 * C * C, G[11] + (size_t)l * 4 * C, dfch, ln2,
+                            P[10] + (size_t)l * 4 * C * C, BT, C, 4 * C);
+        orc_layernorm_backward(dres2, G[8] + (size_t)l * C, G[9] + (size_t)l * C, dln2, res2,
+                               P[8] + (size_t)l * C, ln2m, ln2r, BT, C);
+        /* res2 = res_in + attproj */
+        for (size_t i = 0; i < BTC; i++) { dres_in[i] += dres2[i]; dattproj[i] += dres2[i]; }
+        orc_matmul_backward(datty, G[6] + (size_t)l * C * C, G[7] + (size_t)l * C, dattproj, atty,
+                            P[6] + (size_t)l * C * C, BT, C, C);
+        orc_attention_backward(dqkv, datty, qkv, att, B, T, C, NH);
+        orc_matmul_backward(dln1, G[4] + (size_t)l * 3 * C * C, G[5] + (size_t)l * 3 * C, dqkv, ln1,
+                            P[4] + (size_t)l * 3 * C * C, BT, C, 3 * C);
+        orc_layernorm_backward(dres_in, G[2] + (size_t)l * C, G[3] + (size_t)l * C, dln1, res_in,
+                               P[2] + (size_t)l * C, ln1m, ln1r, BT, C);
+    }
+    orc_encoder_backward(G[0], G[1], D[0], M->inputs, B, T, C);
+    return 0;
+}
+
+/* Global-norm clipping: n = ||g||_2 over all parameters; with n > max_norm
+ * the gradients are scaled by max_norm / n.  max_norm <= 0 disables the
+ * clip.  Returns n (before clipping). */
+double orc_clip_grad_norm(orc_model* M, double max_norm) {
+    double n = orc_global_norm(M->grads, M->np);
+    if (max_norm > 0 && n > max_norm) {
+        double s = max_norm / n;
+        for (size_t i = 0; i < M->np; i++) M->grads[i] = (REAL)((ACC)M->grads[i] * s);
+    }
+    return n;
+}
+
+int orc_adamw(orc_model* M, double lr, double b1, double b2, double eps, double wd, int t) {
+    if (t < 1) return -1;
+    orc_adamw_update(M->params, M->grads, M->m, M->v, M->np, lr, b1, b2, eps, wd, t, 1.0);
+    return 0;
+}
+
+int orc_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+void orc_set_num_threads(int n) {
+#ifdef _OPENMP
+    omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}

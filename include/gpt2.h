@@ -1,0 +1,206 @@
+/*
+ * gpt2.h -- C ABI of the GPT-2 training-step library for MI355X (gfx950).
+ *
+ * One GPT-2 training step (the method the llm.c pages describe) on one GPU:
+ * token + position embedding, L pre-LayerNorm transformer blocks (LayerNorm,
+ * QKV / attention-projection / MLP linears, causal multi-head attention,
+ * GELU, residual adds), a tied classifier with a fused softmax
+ * cross-entropy, a hand-derived backward pass and an AdamW update, all over
+ * ONE device buffer whose layout is planned up front.
+ *
+ * Sources (the pages): "llm.c: GPT-2 training in plain C, with every
+ * gradient written by hand" (fernfant learning-robotics lesson), section 2
+ * "How the code works" (gpt2_forward, gpt2_backward, gpt2_update over a
+ * GPT2 struct with a single allocation; the per-layer call sequence) and
+ * section 3 "Run it, tested" (the GPT-2 124M config); the pyshine.com tour
+ * of llm.c (fused classifier, AdamW and global-norm headers, mixed
+ * precision); "llm.c's Origin and the Future of LLM Compilers", sections
+ * "Pure C" and "Avengers" (one up-front allocation, fp32 vs bf16 per tensor,
+ * kernel fusion).
+ *
+ * Conventions
+ *  - Every call returns 0 on success or a negative errno-style code
+ *    (GPT2_E*), and then gpt2_last_error() holds a message for the calling
+ *    thread.  No C++ exception crosses the ABI.
+ *  - Device memory is owned by the caller: gpt2_build() carves the buffer
+ *    it is given (size from gpt2_plan()) and never allocates device memory
+ *    itself.  The library owns only the small host handle (gpt2_destroy).
+ *  - All GPU work is queued on the HIP stream given to gpt2_build(), in
+ *    call order.  A call blocks the host only when it returns a value read
+ *    from the device (a loss, a norm, a copy to host memory).
+ *  - Host arrays passed in may be freed or reused as soon as a call returns.
+ *  - Layouts: parameters are one flat fp32 array of N floats holding, in
+ *    this order, wte (Vp,C), wpe (maxT,C), ln1w (L,C), ln1b (L,C),
+ *    qkvw (L,3C,C), qkvb (L,3C), attprojw (L,C,C), attprojb (L,C),
+ *    ln2w (L,C), ln2b (L,C), fcw (L,4C,C), fcb (L,4C), fcprojw (L,C,4C),
+ *    fcprojb (L,C), lnfw (C), lnfb (C); matrices are (out,in) row-major;
+ *    the classifier reuses wte.  N = Vp*C + maxT*C + L*(12C^2+13C) + 2C.
+ *    Token arrays are int32 [B,T] row-major.
+ */
+#ifndef GPT2_MI355X_H
+#define GPT2_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* error codes */
+#define GPT2_OK 0
+#define GPT2_EINVAL (-22)  /* bad argument or configuration */
+#define GPT2_ENOMEM (-12)  /* device buffer smaller than gpt2_plan() asked for */
+#define GPT2_EPERM (-1)    /* call out of order (e.g. backward before a forward with targets) */
+#define GPT2_ERANGE (-34)  /* non-finite gradient norm; the AdamW update is refused */
+#define GPT2_EIO (-5)      /* a HIP runtime call failed */
+
+/* arithmetic modes */
+#define GPT2_FP32 0        /* fp32 everywhere (params, activations, matmuls) */
+#define GPT2_BF16_MIXED 1  /* bf16 activations and MFMA matmuls with fp32 accumulation;
+                              fp32 master params, grads, AdamW m/v, LN statistics, losses */
+
+typedef struct {
+    int32_t num_layers;        /* L */
+    int32_t channels;          /* C; multiple of num_heads */
+    int32_t num_heads;         /* NH; head size hs = C/NH (64 required in BF16_MIXED) */
+    int32_t max_seq_len;       /* maxT: rows of wpe */
+    int32_t vocab_size;        /* V: real vocabulary, softmax runs over v < V */
+    int32_t padded_vocab_size; /* Vp >= V: rows of wte and columns of the logits */
+    int32_t batch_size;        /* B */
+    int32_t seq_len;           /* T <= maxT */
+    int32_t precision;         /* GPT2_FP32 or GPT2_BF16_MIXED */
+} gpt2_config;
+
+typedef struct gpt2_model gpt2_t;
+
+/* Size in bytes of the single device buffer for cfg: parameters, gradients,
+ * AdamW m and v, the bf16 weight shadow (BF16_MIXED), every activation the
+ * backward needs, activation gradients and small scratch, each region
+ * 256-byte aligned.  Pure host function.  GPT2_EINVAL on a bad config:
+ * C % NH != 0, T > maxT, V > Vp, a non-positive size, an unknown precision,
+ * or in BF16_MIXED: hs != 64, C % 64 != 0 or (B*T) % 64 != 0. */
+int gpt2_plan(const gpt2_config* cfg, size_t* device_bytes);
+
+/* Carve device_buf (device memory of at least gpt2_plan() bytes, 256-byte
+ * aligned, owned by the caller and kept alive until gpt2_destroy) and
+ * initialise the parameters from seed: wte rows [0,V), wpe, qkvw and fcw
+ * ~ N(0, 0.02); attprojw and fcprojw ~ N(0, 0.02/sqrt(2L)); biases 0, LN
+ * gains 1, padded wte rows 0 (the GPT-2 init the workloads fix).  Normals
+ * come from SplitMix64 draws 2g+1 and 2g+2 for flat parameter index g and
+ * the Box-Muller cosine branch in double, rounded once to fp32.  Gradients
+ * and AdamW state start at zero.  hip_stream is a hipStream_t (NULL = the
+ * default stream).  On success *out holds the handle. */
+int gpt2_build(const gpt2_config* cfg, uint64_t seed, void* device_buf, size_t bytes,
+               void* hip_stream, gpt2_t** out);
+
+/* Forward pass on host int32 arrays tokens[B*T] and targets[B*T] (ids in
+ * [0,V), checked on the host: GPT2_EINVAL otherwise).  With targets, the
+ * fused softmax cross-entropy also writes d(loss)/d(logits) in place of the
+ * logits for gpt2_backward, and *mean_loss receives the mean over the B*T
+ * positions of -log softmax(logits)[target] (one stream sync).  With
+ * targets == NULL the logits are kept (no backward possible) and
+ * *mean_loss, if given, is NaN.  mean_loss may be NULL: then nothing is
+ * read back and the call does not block. */
+int gpt2_forward(gpt2_t* m, const int32_t* tokens, const int32_t* targets, float* mean_loss);
+
+/* As gpt2_forward, but tokens and targets are device int32 arrays already
+ * resident on the GPU (targets may be NULL).  Ids are checked on the device:
+ * an id outside [0,V) is replaced by 0 and flagged, and the next call that
+ * reads a value back (mean_loss here, or gpt2_read_loss) reports
+ * GPT2_EINVAL. */
+int gpt2_forward_device(gpt2_t* m, const int32_t* d_tokens, const int32_t* d_targets,
+                        float* mean_loss);
+
+/* Mean loss of the last forward with targets (blocks on the stream). */
+int gpt2_read_loss(gpt2_t* m, float* mean_loss);
+
+/* Parameter gradients <- 0.  (Activation gradients are overwritten by every
+ * backward, never accumulated.) */
+int gpt2_zero_grad(gpt2_t* m);
+
+/* Backward pass of the last forward-with-targets: the forward's layers in
+ * reverse, ACCUMULATING (+=) into the parameter gradients.  GPT2_EPERM if
+ * there was no forward with targets since the last build/update. */
+int gpt2_backward(gpt2_t* m);
+
+/* Global-norm gradient clipping: n = ||g||_2 over all N gradients, computed
+ * on the device; with max_norm > 0 and n > max_norm the next
+ * gpt2_adamw_step uses g * max_norm/n (the gradients in memory are not
+ * rewritten).  max_norm <= 0 only measures.  If norm != NULL, *norm = n
+ * (one stream sync); a non-finite n returns GPT2_ERANGE and makes the next
+ * gpt2_adamw_step refuse to update. */
+int gpt2_clip_grad_norm(gpt2_t* m, float max_norm, float* norm);
+
+/* AdamW (decoupled weight decay, bias-corrected, step t >= 1) over all N
+ * parameters, then the bf16 weight shadow is refreshed (BF16_MIXED):
+ *   m = b1 m + (1-b1) g;  v = b2 v + (1-b2) g^2;
+ *   theta -= lr * ( m/(1-b1^t) / (sqrt(v/(1-b2^t)) + eps) + wd * theta ).
+ * GPT2_EINVAL if t < 1. */
+int gpt2_adamw_step(gpt2_t* m, float lr, float beta1, float beta2, float eps,
+                    float weight_decay, int t);
+
+/* Free the handle (not the device buffer). NULL is accepted. */
+int gpt2_destroy(gpt2_t* m);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* gpt2_last_error(void);
+
+/* ---- inspection and test access (block on the stream) ---------------- */
+
+/* Number of parameters N. */
+size_t gpt2_num_params(const gpt2_t* m);
+
+/* Offsets (in floats) of the 16 parameter tensors in the flat layout. */
+int gpt2_param_offsets(const gpt2_t* m, size_t offsets[16]);
+
+/* Copy fp32 master parameters / gradients / AdamW m and v to host arrays of
+ * N floats; m_dst or v_dst may be NULL. */
+int gpt2_copy_params(gpt2_t* m, float* host_dst);
+int gpt2_copy_grads(gpt2_t* m, float* host_dst);
+int gpt2_copy_opt_state(gpt2_t* m, float* m_dst, float* v_dst);
+
+/* Copy the last forward's logits [B*T, Vp] to host as fp32.  Only valid
+ * after a forward with targets == NULL (a forward with targets overwrites
+ * them with dlogits); GPT2_EPERM otherwise. */
+int gpt2_copy_logits(gpt2_t* m, float* host_dst);
+
+/* Copy the per-position losses [B*T] of the last forward with targets. */
+int gpt2_copy_losses(gpt2_t* m, float* host_dst);
+
+/* Overwrite the fp32 master parameters from a host array of N floats and
+ * refresh the bf16 shadow. */
+int gpt2_set_params(gpt2_t* m, const float* host_src);
+
+/* Device pointer of the planned buffer region holding the fp32 master
+ * parameters, gradients and the bf16 weight shadow (NULL in FP32 mode). */
+void* gpt2_device_params(gpt2_t* m);
+void* gpt2_device_grads(gpt2_t* m);
+void* gpt2_device_shadow(gpt2_t* m);
+
+/* ---- single-kernel entry points, for kernel tests and timing ---------- */
+
+/* Kernel timing: when enabled, HIP events bracket every launch of the
+ * named kernel class on the library's stream; gpt2_kernel_timing_read()
+ * blocks on the stream and returns the launch count and summed milliseconds
+ * since the last enable.  Class names: "gemm_classifier_fwd",
+ * "gemm_classifier_dw", "gemm_classifier_dx", "gemm_fwd", "gemm_dx",
+ * "gemm_dw", "attention_fwd", "attention_bwd", "softmax_ce", "adamw",
+ * "layernorm_fwd", "layernorm_bwd". */
+int gpt2_kernel_timing_enable(gpt2_t* m, const char* kernel_class, int enable);
+int gpt2_kernel_timing_read(gpt2_t* m, int* launches, double* total_ms);
+
+/* out[M,N] (dtype of precision) = A[M,K] * W[N,K]^T (+ bias[N] fp32), all
+ * row-major device arrays in the model's activation dtype (fp32 or bf16);
+ * the same kernel the forward linears use.  Runs on the model's stream. */
+int gpt2_test_gemm_nt(gpt2_t* m, void* out, const void* a, const void* w, const float* bias,
+                      int M, int N, int K);
+/* dX[M,K] = dY[M,N] * W[N,K]   (the backward-data kernel) */
+int gpt2_test_gemm_nn(gpt2_t* m, void* dx, const void* dy, const void* w, int M, int N, int K);
+/* dW[N,K] (fp32) += dY[M,N]^T * X[M,K]   (the backward-weight kernel) */
+int gpt2_test_gemm_tn(gpt2_t* m, float* dw, const void* dy, const void* x, int M, int N, int K);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,73 @@
+"""CPU-side checks of the C-ABI library: it loads, exports every entry point
+include/gpt2.h declares, and its host-only logic (the planner and config
+validation) behaves as documented.  No GPU call is made here."""
+import os
+import re
+import subprocess
+
+import pytest
+
+from transformer_lm_train_amd import gpt2 as G
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gpt2.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gpt2_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) >= 20
+    lib = G.lib()
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+    out = subprocess.run(["nm", "-D", "--defined-only", G.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (gpt2_\w+)", out))
+    assert set(names) <= exported, set(names) - exported
+
+
+def test_binding_covers_the_abi():
+    for n in declared_functions():
+        if n in ("gpt2_last_error", "gpt2_device_params", "gpt2_device_grads", "gpt2_device_shadow"):
+            continue
+        assert hasattr(G, n), n
+
+
+def _cfg(**kw):
+    base = dict(L=12, C=768, NH=12, maxT=1024, V=50257, Vp=50304, B=16, T=1024, precision=G.GPT2_BF16_MIXED)
+    base.update(kw)
+    return G.make_config(base["L"], base["C"], base["NH"], base["maxT"], base["V"], base["Vp"], base["B"],
+                         base["T"], base["precision"])
+
+
+def test_plan_sizes():
+    n = 124475904
+    size = G.gpt2_plan(_cfg())
+    # params + grads + m + v (fp32) + bf16 shadow at least
+    assert size >= 18 * n
+    # activations of 12 layers at B*T = 16384 in bf16 are a few GB, well under 288 GB
+    assert size < 16 * 2**30
+    fp32 = G.gpt2_plan(_cfg(B=4, T=64, precision=G.GPT2_FP32))
+    assert fp32 >= 16 * n
+    tiny = G.gpt2_plan(G.make_config(2, 64, 4, 32, 512, 512, 4, 32, G.GPT2_FP32))
+    assert tiny >= 16 * 134912
+
+
+@pytest.mark.parametrize("kw,msg", [
+    (dict(C=770), "num_heads"),
+    (dict(T=2048), "seq_len"),
+    (dict(V=50305), "vocab_size"),
+    (dict(precision=7), "precision"),
+    (dict(NH=6), "head size 64"),             # bf16 mode needs hs = 64
+    (dict(B=1, T=63), "multiples of 64"),     # bf16 mode needs B*T % 64 == 0
+    (dict(L=0), "positive"),
+])
+def test_plan_rejects_bad_configs(kw, msg):
+    with pytest.raises(G.GPT2Error) as e:
+        G.gpt2_plan(_cfg(**kw))
+    assert e.value.code == G.GPT2_EINVAL
+    assert msg in str(e.value)

@@ -1,0 +1,85 @@
+// Internal launch interface of the GPT-2 step kernels.  Every launcher queues
+// work on the given stream and returns hipSuccess or the launch error.
+#pragma once
+#include "common.h"
+
+// ---- matrix products --------------------------------------------------------
+// acc[m][n] = sum_k A(m,k) * B(n,k); an operand is "k-contiguous" when
+// A(m,k) = a[m*lda + k] and "mn-contiguous" when A(m,k) = a[k*lda + m]
+// (likewise B with n).  The epilogue then writes, for m < M and n < N:
+enum GemmEpi {
+    EPI_STORE = 0,       // out = acc
+    EPI_BIAS = 1,        // out = acc + bias[n]
+    EPI_BIAS_RESID = 2,  // out = resid[m][n] + acc + bias[n]
+    EPI_BIAS_GELU = 3,   // out = acc + bias[n] (pre-activation); out2 = GELU(that)
+    EPI_GELU_BWD = 4,    // out = acc * GELU'(aux[m][n])
+    EPI_ACC_F32 = 5,     // out (fp32) += acc
+};
+
+struct GemmArgs {
+    int M, N, K;
+    const void* a;
+    int64_t lda;
+    bool a_kcontig;
+    const void* b;
+    int64_t ldb;
+    bool b_kcontig;
+    void* out;  // activation dtype, or fp32 for EPI_ACC_F32
+    int64_t ldo;
+    const float* bias;   // may be NULL (treated as zeros)
+    const void* resid;   // activation dtype, leading dim ldo
+    const void* aux;     // activation dtype, leading dim ldo
+    void* out2;          // activation dtype, leading dim ldo
+    int epi;
+};
+
+// fp32-accumulating SIMT kernel for any shapes (activation dtype T).
+template <typename T> hipError_t gemm_simt(const GemmArgs& g, hipStream_t s);
+// bf16 MFMA kernel (gfx950 v_mfma_f32_32x32x16_bf16), fp32 accumulation.
+// Needs K % 64 == 0, M % 8 == 0, N % 8 == 0, leading dims % 8 == 0 and
+// 16-byte aligned operands; returns hipErrorInvalidValue otherwise.
+hipError_t gemm_mfma_bf16(const GemmArgs& g, hipStream_t s);
+
+// ---- element-wise and row kernels ------------------------------------------
+template <typename T>
+hipError_t encoder_fwd(T* out, int* tokens, const float* wte, const float* wpe, int B, int T_,
+                       int C, int V, int* err_flag, hipStream_t s);
+template <typename T>
+hipError_t encoder_bwd(float* dwte, float* dwpe, const T* dx, const int* tokens, int B, int T_, int C,
+                       hipStream_t s);
+template <typename T>
+hipError_t layernorm_fwd(T* out, float* mean, float* rstd, const T* x, const float* w, const float* b,
+                         int N, int C, hipStream_t s);
+// dres (+)= LN backward of dy; per-block partial dw/db go to partial[2][G][C]
+// and are then summed in block order into dw, db.
+template <typename T>
+hipError_t layernorm_bwd(T* dres, const T* dy, const T* x, const float* w, const float* mean,
+                         const float* rstd, float* dw, float* db, float* partial, int N, int C,
+                         bool overwrite, hipStream_t s);
+// dbias[n] += sum_m dy[m][n] (deterministic two-stage sum via partial).
+template <typename T>
+hipError_t colsum_accum(float* dbias, const T* dy, int M, int N, float* partial, hipStream_t s);
+// Fused softmax + cross-entropy + dlogits, in place over logits [BT, Vp]:
+// losses[r] = logsumexp_{v<V} z - z[target]; z <- (softmax - onehot) * dscale
+// for v < V and 0 for v >= V.
+template <typename T>
+hipError_t softmax_ce(T* logits, float* losses, const int* targets, int BT, int V, int Vp, float dscale,
+                      int* err_flag, hipStream_t s);
+hipError_t loss_mean(float* out, const float* losses, int n, hipStream_t s);
+// norm_scale[0] = ||g||, norm_scale[1] = clip factor (1 if no clip).
+// adamw multiplies g by norm_scale[1], or by 1 when norm_scale is NULL.
+hipError_t grad_norm(float* partial, float* norm_scale, const float* g, size_t n, float max_norm,
+                     hipStream_t s);
+hipError_t adamw(float* p, const float* g, float* m, float* v, bf16* shadow, size_t n, float lr, float b1,
+                 float b2, float eps, float wd, float c1, float c2, const float* norm_scale, hipStream_t s);
+hipError_t cast_bf16(bf16* dst, const float* src, size_t n, hipStream_t s);
+template <typename T> hipError_t widen_f32(float* dst, const T* src, size_t n, hipStream_t s);
+
+// ---- attention ---------------------------------------------------------------
+// Causal multi-head attention over qkv [B,T,3C] (q|k|v, head h owns
+// channels [h*hs,(h+1)*hs) of each); out [B,T,C]; lse [B,NH,T] fp32.
+template <typename T>
+hipError_t attention_fwd(T* out, float* lse, const T* qkv, int B, int T_, int C, int NH, hipStream_t s);
+template <typename T>
+hipError_t attention_bwd(T* dqkv, const T* dout, const T* qkv, const T* out, const float* lse, float* dbuf,
+                         int B, int T_, int C, int NH, hipStream_t s);

@@ -1,0 +1,562 @@
+// Memory-bound kernels of the GPT-2 step: embedding, LayerNorm fwd/bwd,
+// bias-gradient column sums, fused softmax cross-entropy, loss mean, global
+// gradient norm and AdamW.  Rows are processed one wavefront (64 lanes) per
+// row with 16-byte loads; reductions are wavefront butterflies and
+// fixed-order block partials, so results do not depend on scheduling.
+#include "kernels.h"
+
+#define LAUNCH_CHECK() hipGetLastError()
+
+// ============================================================================
+// encoder: x[b,t,:] = wte[tok[b,t],:] + wpe[t,:]   (llm.c lesson, section 2:
+// encoder_forward, token + position embedding)
+// ============================================================================
+template <typename T>
+__global__ void encoder_fwd_kernel(T* out, int* tokens, const float* wte, const float* wpe, int T_,
+                                   int C, int V, int BT, int* err) {
+    constexpr int VN = Vec16<T>::N;
+    int chunks = C / VN;
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (int64_t)BT * chunks) return;
+    int row = (int)(i / chunks), ch = (int)(i % chunks);
+    int t = row % T_;
+    int tok = tokens[row];
+    if (tok < 0 || tok >= V) {
+        // flag it and replace it by 0 in the model's own token copy, so the
+        // backward's scatter into dwte stays in bounds
+        if (ch == 0) {
+            atomicOr(err, 1);
+            tokens[row] = 0;
+        }
+        tok = 0;
+    }
+    const float* we = wte + (int64_t)tok * C + ch * VN;
+    const float* pe = wpe + (int64_t)t * C + ch * VN;
+    Vec16<T> o;
+#pragma unroll
+    for (int j = 0; j < VN; j += 4) {
+        float4 a = *reinterpret_cast<const float4*>(we + j);
+        float4 b = *reinterpret_cast<const float4*>(pe + j);
+        o.v[j + 0] = from_f32<T>(a.x + b.x);
+        o.v[j + 1] = from_f32<T>(a.y + b.y);
+        o.v[j + 2] = from_f32<T>(a.z + b.z);
+        o.v[j + 3] = from_f32<T>(a.w + b.w);
+    }
+    st16(out + (int64_t)row * C + ch * VN, o);
+}
+
+template <typename T>
+hipError_t encoder_fwd(T* out, int* tokens, const float* wte, const float* wpe, int B, int T_, int C,
+                       int V, int* err, hipStream_t s) {
+    int BT = B * T_;
+    int64_t n = (int64_t)BT * (C / Vec16<T>::N);
+    encoder_fwd_kernel<T><<<cdiv(n, 256), 256, 0, s>>>(out, tokens, wte, wpe, T_, C, V, BT, err);
+    return LAUNCH_CHECK();
+}
+
+// dwte[tok] += dx (fp32 atomics: a token id may repeat within the batch);
+// dwpe[t] += sum_b dx[b,t] (each (t, c) summed over b in order).
+template <typename T>
+__global__ void encoder_bwd_wte_kernel(float* dwte, const T* dx, const int* tokens, int C, int BT) {
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (int64_t)BT * C) return;
+    int row = (int)(i / C), c = (int)(i % C);
+    atomicAdd(dwte + (int64_t)tokens[row] * C + c, to_f32(dx[i]));
+}
+template <typename T>
+__global__ void encoder_bwd_wpe_kernel(float* dwpe, const T* dx, int B, int T_, int C) {
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (int64_t)T_ * C) return;
+    int t = (int)(i / C), c = (int)(i % C);
+    float acc = 0.f;
+    for (int b = 0; b < B; b++) acc += to_f32(dx[((int64_t)b * T_ + t) * C + c]);
+    dwpe[i] += acc;
+}
+
+template <typename T>
+hipError_t encoder_bwd(float* dwte, float* dwpe, const T* dx, const int* tokens, int B, int T_, int C,
+                       hipStream_t s) {
+    int64_t n = (int64_t)B * T_ * C;
+    encoder_bwd_wte_kernel<T><<<cdiv(n, 256), 256, 0, s>>>(dwte, dx, tokens, C, B * T_);
+    encoder_bwd_wpe_kernel<T><<<cdiv((int64_t)T_ * C, 256), 256, 0, s>>>(dwpe, dx, B, T_, C);
+    return LAUNCH_CHECK();
+}
+
+// ============================================================================
+// LayerNorm forward: mean, biased variance, rstd = 1/sqrt(var + 1e-5);
+// y = (x - mean) * rstd * w + b; mean and rstd saved for the backward
+// (origin-of-llm.c transcript, "Pure C").  One wavefront per row, the row
+// held in registers (up to MAXV 16-byte chunks per lane).
+// ============================================================================
+constexpr int LN_MAXV = 8;
+
+template <typename T, int MAXV>
+__global__ __launch_bounds__(256) void layernorm_fwd_kernel(T* out, float* mean, float* rstd, const T* x,
+                                                            const float* w, const float* b, int N, int C) {
+    constexpr int VN = Vec16<T>::N;
+    int lane = threadIdx.x & 63;
+    int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= N) return;
+    int chunks = C / VN;
+    const T* xr = x + (int64_t)row * C;
+    float v[MAXV][VN];
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < MAXV; i++) {
+        int ch = lane + i * 64;
+        if (ch < chunks) {
+            Vec16<T> q = ld16(xr + ch * VN);
+#pragma unroll
+            for (int j = 0; j < VN; j++) { v[i][j] = to_f32(q.v[j]); s += v[i][j]; }
+        }
+    }
+    float mu = wave_sum(s) / C;
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < MAXV; i++) {
+        int ch = lane + i * 64;
+        if (ch < chunks) {
+#pragma unroll
+            for (int j = 0; j < VN; j++) { float d = v[i][j] - mu; ss += d * d; }
+        }
+    }
+    float var = wave_sum(ss) / C;
+    float rs = rsqrtf(var + 1e-5f);
+    T* orow = out + (int64_t)row * C;
+#pragma unroll
+    for (int i = 0; i < MAXV; i++) {
+        int ch = lane + i * 64;
+        if (ch < chunks) {
+            Vec16<T> o;
+#pragma unroll
+            for (int j = 0; j < VN; j++) {
+                int c = ch * VN + j;
+                o.v[j] = from_f32<T>((v[i][j] - mu) * rs * w[c] + b[c]);
+            }
+            st16(orow + ch * VN, o);
+        }
+    }
+    if (lane == 0) {
+        mean[row] = mu;
+        rstd[row] = rs;
+    }
+}
+
+template <typename T>
+hipError_t layernorm_fwd(T* out, float* mean, float* rstd, const T* x, const float* w, const float* b, int N,
+                         int C, hipStream_t s) {
+    if (C % Vec16<T>::N || C / Vec16<T>::N > LN_MAXV * 64) return hipErrorInvalidValue;
+    int per_lane = (int)cdiv(C / Vec16<T>::N, 64);
+    if (per_lane <= 1)
+        layernorm_fwd_kernel<T, 1><<<cdiv(N, 4), 256, 0, s>>>(out, mean, rstd, x, w, b, N, C);
+    else if (per_lane <= 2)
+        layernorm_fwd_kernel<T, 2><<<cdiv(N, 4), 256, 0, s>>>(out, mean, rstd, x, w, b, N, C);
+    else if (per_lane <= 4)
+        layernorm_fwd_kernel<T, 4><<<cdiv(N, 4), 256, 0, s>>>(out, mean, rstd, x, w, b, N, C);
+    else
+        layernorm_fwd_kernel<T, 8><<<cdiv(N, 4), 256, 0, s>>>(out, mean, rstd, x, w, b, N, C);
+    return LAUNCH_CHECK();
+}
+
+// ============================================================================
+// LayerNorm backward.  With xhat = (x-mean)*rstd and g = dy*w:
+//   dx = rstd * (g - mean_c(g) - xhat * mean_c(g*xhat)),  dres (+)= dx;
+//   dw += sum_rows dy*xhat,  db += sum_rows dy.
+// Each block handles rows blk*4+wave, stepping by 4*G, keeps per-channel
+// dw/db sums in registers, reduces its 4 waves in LDS and writes one
+// partial row; a second kernel sums the G partials in block order.
+// ============================================================================
+constexpr int LN_BWD_G = 256;
+
+template <typename T, int MAXV>
+__global__ __launch_bounds__(256) void layernorm_bwd_kernel(T* dres, const T* dy, const T* x, const float* w,
+                                                            const float* mean, const float* rstd,
+                                                            float* partial, int N, int C, int overwrite) {
+    constexpr int VN = Vec16<T>::N;
+    extern __shared__ float smem[];  // [4][2][C]
+    int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    int chunks = C / VN;
+    float aw[MAXV][VN], ab[MAXV][VN];
+#pragma unroll
+    for (int i = 0; i < MAXV; i++)
+#pragma unroll
+        for (int j = 0; j < VN; j++) { aw[i][j] = 0.f; ab[i][j] = 0.f; }
+    for (int row = blockIdx.x * 4 + wv; row < N; row += gridDim.x * 4) {
+        float mu = mean[row], rs = rstd[row];
+        const T* xr = x + (int64_t)row * C;
+        const T* dr = dy + (int64_t)row * C;
+        float xh[MAXV][VN], gg[MAXV][VN];
+        float sg = 0.f, sgx = 0.f;
+#pragma unroll
+        for (int i = 0; i < MAXV; i++) {
+            int ch = lane + i * 64;
+            if (ch < chunks) {
+                Vec16<T> xv = ld16(xr + ch * VN);
+                Vec16<T> dv = ld16(dr + ch * VN);
+#pragma unroll
+                for (int j = 0; j < VN; j++) {
+                    int c = ch * VN + j;
+                    float d = to_f32(dv.v[j]);
+                    xh[i][j] = (to_f32(xv.v[j]) - mu) * rs;
+                    gg[i][j] = d * w[c];
+                    sg += gg[i][j];
+                    sgx += gg[i][j] * xh[i][j];
+                    aw[i][j] += d * xh[i][j];
+                    ab[i][j] += d;
+                }
+            }
+        }
+        sg = wave_sum(sg) / C;
+        sgx = wave_sum(sgx) / C;
+        T* orow = dres + (int64_t)row * C;
+#pragma unroll
+        for (int i = 0; i < MAXV; i++) {
+            int ch = lane + i * 64;
+            if (ch < chunks) {
+                Vec16<T> o;
+                if (!overwrite) o = ld16(orow + ch * VN);
+#pragma unroll
+                for (int j = 0; j < VN; j++) {
+                    float dx = rs * (gg[i][j] - sg - xh[i][j] * sgx);
+                    o.v[j] = from_f32<T>(overwrite ? dx : to_f32(o.v[j]) + dx);
+                }
+                st16(orow + ch * VN, o);
+            }
+        }
+    }
+    // block reduction of the per-channel sums over the 4 waves
+#pragma unroll
+    for (int i = 0; i < MAXV; i++) {
+        int ch = lane + i * 64;
+        if (ch < chunks) {
+#pragma unroll
+            for (int j = 0; j < VN; j++) {
+                smem[(wv * 2 + 0) * C + ch * VN + j] = aw[i][j];
+                smem[(wv * 2 + 1) * C + ch * VN + j] = ab[i][j];
+            }
+        }
+    }
+    __syncthreads();
+    for (int c = threadIdx.x; c < C; c += 256) {
+        float sw = 0.f, sb = 0.f;
+        for (int q = 0; q < 4; q++) {
+            sw += smem[(q * 2 + 0) * C + c];
+            sb += smem[(q * 2 + 1) * C + c];
+        }
+        partial[(int64_t)blockIdx.x * C + c] = sw;
+        partial[((int64_t)gridDim.x + blockIdx.x) * C + c] = sb;
+    }
+}
+
+// out0[c] += sum_g partial[g][c]; out1[c] += sum_g partial[G+g][c] (if out1)
+__global__ void sum_partials_kernel(float* out0, float* out1, const float* partial, int G, int C) {
+    int c = blockIdx.x * blockDim.x + threadIdx.x;
+    if (c >= C) return;
+    float s0 = 0.f, s1 = 0.f;
+    for (int g = 0; g < G; g++) s0 += partial[(int64_t)g * C + c];
+    out0[c] += s0;
+    if (out1) {
+        for (int g = 0; g < G; g++) s1 += partial[((int64_t)G + g) * C + c];
+        out1[c] += s1;
+    }
+}
+
+template <typename T>
+hipError_t layernorm_bwd(T* dres, const T* dy, const T* x, const float* w, const float* mean, const float* rstd,
+                         float* dw, float* db, float* partial, int N, int C, bool overwrite, hipStream_t s) {
+    if (C % Vec16<T>::N || C / Vec16<T>::N > LN_MAXV * 64) return hipErrorInvalidValue;
+    int G = (int)cdiv(N, 4);
+    if (G > LN_BWD_G) G = LN_BWD_G;
+    size_t lds = sizeof(float) * 8 * C;
+    int per_lane = (int)cdiv(C / Vec16<T>::N, 64);
+    int ow = overwrite ? 1 : 0;
+    if (per_lane <= 1)
+        layernorm_bwd_kernel<T, 1><<<G, 256, lds, s>>>(dres, dy, x, w, mean, rstd, partial, N, C, ow);
+    else if (per_lane <= 2)
+        layernorm_bwd_kernel<T, 2><<<G, 256, lds, s>>>(dres, dy, x, w, mean, rstd, partial, N, C, ow);
+    else if (per_lane <= 4)
+        layernorm_bwd_kernel<T, 4><<<G, 256, lds, s>>>(dres, dy, x, w, mean, rstd, partial, N, C, ow);
+    else
+        layernorm_bwd_kernel<T, 8><<<G, 256, lds, s>>>(dres, dy, x, w, mean, rstd, partial, N, C, ow);
+    sum_partials_kernel<<<cdiv(C, 256), 256, 0, s>>>(dw, db, partial, G, C);
+    return LAUNCH_CHECK();
+}
+
+// ============================================================================
+// bias gradient: dbias[n] += sum_m dy[m][n]
+// Block: 64 column chunks x 4 row lanes; grid.y = G row groups.
+// ============================================================================
+constexpr int COLSUM_G = 64;
+
+template <typename T>
+__global__ __launch_bounds__(256) void colsum_kernel(float* partial, const T* dy, int M, int N) {
+    constexpr int VN = Vec16<T>::N;
+    __shared__ float red[4][64][VN];
+    int cx = threadIdx.x & 63, ry = threadIdx.x >> 6;
+    int ch = blockIdx.x * 64 + cx;
+    int chunks = N / VN;
+    float acc[VN];
+#pragma unroll
+    for (int j = 0; j < VN; j++) acc[j] = 0.f;
+    if (ch < chunks) {
+        for (int m = blockIdx.y * 4 + ry; m < M; m += gridDim.y * 4) {
+            Vec16<T> q = ld16(dy + (int64_t)m * N + ch * VN);
+#pragma unroll
+            for (int j = 0; j < VN; j++) acc[j] += to_f32(q.v[j]);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < VN; j++) red[ry][cx][j] = acc[j];
+    __syncthreads();
+    if (ry == 0 && ch < chunks) {
+#pragma unroll
+        for (int j = 0; j < VN; j++) {
+            float s = red[0][cx][j] + red[1][cx][j] + red[2][cx][j] + red[3][cx][j];
+            partial[(int64_t)blockIdx.y * N + ch * VN + j] = s;
+        }
+    }
+}
+
+template <typename T>
+hipError_t colsum_accum(float* dbias, const T* dy, int M, int N, float* partial, hipStream_t s) {
+    constexpr int VN = Vec16<T>::N;
+    if (N % VN) return hipErrorInvalidValue;
+    int G = COLSUM_G;
+    dim3 grid(cdiv(N / VN, 64), G);
+    colsum_kernel<T><<<grid, 256, 0, s>>>(partial, dy, M, N);
+    sum_partials_kernel<<<cdiv(N, 256), 256, 0, s>>>(dbias, nullptr, partial, G, N);
+    return LAUNCH_CHECK();
+}
+
+// ============================================================================
+// Fused softmax + cross-entropy + dlogits (the pyshine tour's "fused
+// classifier": the softmax loss merged with the output projection's
+// backward seed).  One block per row; pass 1 keeps an online (max, sum) per
+// thread over the real columns v < V, pass 2 rewrites the row in place as
+// (softmax - onehot(target)) * dscale and zeros the padded columns.
+// ============================================================================
+constexpr int CE_THREADS = 1024;
+
+template <typename T>
+__global__ __launch_bounds__(CE_THREADS) void softmax_ce_kernel(T* logits, float* losses, const int* targets,
+                                                                int V, int Vp, float dscale, int* err) {
+    constexpr int VN = Vec16<T>::N;
+    __shared__ float sm[CE_THREADS / 64], ss[CE_THREADS / 64];
+    __shared__ float s_max, s_sum;
+    int row = blockIdx.x;
+    T* z = logits + (int64_t)row * Vp;
+    int chunks = Vp / VN;
+    float m = -INFINITY, s = 0.f;
+    for (int ch = threadIdx.x; ch < chunks; ch += CE_THREADS) {
+        Vec16<T> q = ld16(z + ch * VN);
+#pragma unroll
+        for (int j = 0; j < VN; j++) {
+            int v = ch * VN + j;
+            if (v < V) {
+                float x = to_f32(q.v[j]);
+                if (x > m) {
+                    s = s * __expf(m - x) + 1.f;
+                    m = x;
+                } else {
+                    s += __expf(x - m);
+                }
+            }
+        }
+    }
+    // wavefront then block combine of (m, s)
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        float m2 = __shfl_xor(m, o, 64), s2 = __shfl_xor(s, o, 64);
+        float mn = fmaxf(m, m2);
+        s = (m == -INFINITY ? 0.f : s * __expf(m - mn)) + (m2 == -INFINITY ? 0.f : s2 * __expf(m2 - mn));
+        m = mn;
+    }
+    int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    if (lane == 0) { sm[wv] = m; ss[wv] = s; }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float M = -INFINITY;
+        for (int i = 0; i < CE_THREADS / 64; i++) M = fmaxf(M, sm[i]);
+        float S = 0.f;
+        for (int i = 0; i < CE_THREADS / 64; i++) S += sm[i] == -INFINITY ? 0.f : ss[i] * __expf(sm[i] - M);
+        s_max = M;
+        s_sum = S;
+    }
+    __syncthreads();
+    float M = s_max, invS = 1.f / s_sum;
+    int tgt = targets[row];
+    if (tgt < 0 || tgt >= V) {
+        if (threadIdx.x == 0) atomicOr(err, 2);
+        tgt = 0;
+    }
+    if (threadIdx.x == 0) losses[row] = M + logf(s_sum) - to_f32(z[tgt]);
+    __syncthreads();  // the target logit is read before any thread overwrites it
+    for (int ch = threadIdx.x; ch < chunks; ch += CE_THREADS) {
+        Vec16<T> q = ld16(z + ch * VN);
+#pragma unroll
+        for (int j = 0; j < VN; j++) {
+            int v = ch * VN + j;
+            float d = 0.f;
+            if (v < V) d = (__expf(to_f32(q.v[j]) - M) * invS - (v == tgt ? 1.f : 0.f)) * dscale;
+            q.v[j] = from_f32<T>(d);
+        }
+        st16(z + ch * VN, q);
+    }
+}
+
+template <typename T>
+hipError_t softmax_ce(T* logits, float* losses, const int* targets, int BT, int V, int Vp, float dscale, int* err,
+                      hipStream_t s) {
+    if (Vp % Vec16<T>::N) return hipErrorInvalidValue;
+    softmax_ce_kernel<T><<<BT, CE_THREADS, 0, s>>>(logits, losses, targets, V, Vp, dscale, err);
+    return LAUNCH_CHECK();
+}
+
+// mean of n losses, summed in a fixed order in double by one block
+__global__ __launch_bounds__(256) void loss_mean_kernel(float* out, const float* losses, int n) {
+    __shared__ double red[256];
+    double s = 0.0;
+    for (int i = threadIdx.x; i < n; i += 256) s += losses[i];
+    red[threadIdx.x] = s;
+    __syncthreads();
+    for (int o = 128; o >= 1; o >>= 1) {
+        if (threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) out[0] = (float)(red[0] / n);
+}
+
+hipError_t loss_mean(float* out, const float* losses, int n, hipStream_t s) {
+    loss_mean_kernel<<<1, 256, 0, s>>>(out, losses, n);
+    return LAUNCH_CHECK();
+}
+
+// ============================================================================
+// global gradient norm (pyshine tour: global-norm header) and clip factor
+// ============================================================================
+constexpr int NORM_G = 1024;
+
+__global__ __launch_bounds__(256) void sumsq_kernel(float* partial, const float* g, size_t n) {
+    __shared__ float red[4];
+    float s = 0.f;
+    size_t n4 = n / 4;
+    const float4* g4 = reinterpret_cast<const float4*>(g);
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (size_t)gridDim.x * 256) {
+        float4 q = g4[i];
+        s += q.x * q.x + q.y * q.y + q.z * q.z + q.w * q.w;
+    }
+    if (blockIdx.x == 0 && threadIdx.x < (n & 3)) {
+        float q = g[n4 * 4 + threadIdx.x];
+        s += q * q;
+    }
+    s = wave_sum(s);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
+    __syncthreads();
+    if (threadIdx.x == 0) partial[blockIdx.x] = red[0] + red[1] + red[2] + red[3];
+}
+
+__global__ void norm_final_kernel(float* norm_scale, const float* partial, int G, float max_norm) {
+    if (threadIdx.x != 0) return;
+    double s = 0.0;
+    for (int i = 0; i < G; i++) s += partial[i];
+    float n = (float)sqrt(s);
+    norm_scale[0] = n;
+    norm_scale[1] = (max_norm > 0.f && n > max_norm) ? max_norm / n : 1.f;
+}
+
+hipError_t grad_norm(float* partial, float* norm_scale, const float* g, size_t n, float max_norm, hipStream_t s) {
+    sumsq_kernel<<<NORM_G, 256, 0, s>>>(partial, g, n);
+    norm_final_kernel<<<1, 64, 0, s>>>(norm_scale, partial, NORM_G, max_norm);
+    return LAUNCH_CHECK();
+}
+
+// ============================================================================
+// AdamW (decoupled weight decay, bias-corrected; c1 = 1-b1^t, c2 = 1-b2^t),
+// gradient times the clip factor norm_scale[1]; refreshes the bf16 shadow.
+// ============================================================================
+DEVI void adamw_one(float& p, float g, float& m, float& v, float lr, float b1, float b2, float eps, float wd,
+                    float c1, float c2) {
+    m = b1 * m + (1.f - b1) * g;
+    v = b2 * v + (1.f - b2) * g * g;
+    float mh = m / c1, vh = v / c2;
+    p = p - lr * (mh / (sqrtf(vh) + eps) + wd * p);
+}
+
+__global__ __launch_bounds__(256) void adamw_kernel(float* p, const float* g, float* m, float* v, bf16* shadow,
+                                                    size_t n, float lr, float b1, float b2, float eps, float wd,
+                                                    float c1, float c2, const float* norm_scale) {
+    float sc = norm_scale ? norm_scale[1] : 1.f;
+    size_t n4 = n / 4;
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (size_t)gridDim.x * 256) {
+        float4 pp = reinterpret_cast<float4*>(p)[i];
+        float4 gg = reinterpret_cast<const float4*>(g)[i];
+        float4 mm = reinterpret_cast<float4*>(m)[i];
+        float4 vv = reinterpret_cast<float4*>(v)[i];
+        adamw_one(pp.x, gg.x * sc, mm.x, vv.x, lr, b1, b2, eps, wd, c1, c2);
+        adamw_one(pp.y, gg.y * sc, mm.y, vv.y, lr, b1, b2, eps, wd, c1, c2);
+        adamw_one(pp.z, gg.z * sc, mm.z, vv.z, lr, b1, b2, eps, wd, c1, c2);
+        adamw_one(pp.w, gg.w * sc, mm.w, vv.w, lr, b1, b2, eps, wd, c1, c2);
+        reinterpret_cast<float4*>(p)[i] = pp;
+        reinterpret_cast<float4*>(m)[i] = mm;
+        reinterpret_cast<float4*>(v)[i] = vv;
+        if (shadow) {
+            typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
+            bf16x4 o = {(bf16)pp.x, (bf16)pp.y, (bf16)pp.z, (bf16)pp.w};
+            reinterpret_cast<bf16x4*>(shadow)[i] = o;
+        }
+    }
+    if (blockIdx.x == 0 && threadIdx.x < (n & 3)) {
+        size_t i = n4 * 4 + threadIdx.x;
+        float pp = p[i], mm = m[i], vv = v[i];
+        adamw_one(pp, g[i] * sc, mm, vv, lr, b1, b2, eps, wd, c1, c2);
+        p[i] = pp;
+        m[i] = mm;
+        v[i] = vv;
+        if (shadow) shadow[i] = (bf16)pp;
+    }
+}
+
+hipError_t adamw(float* p, const float* g, float* m, float* v, bf16* shadow, size_t n, float lr, float b1, float b2,
+                 float eps, float wd, float c1, float c2, const float* norm_scale, hipStream_t s) {
+    size_t blocks = cdiv(n / 4 + 1, 256);
+    if (blocks > 8192) blocks = 8192;
+    adamw_kernel<<<(unsigned)blocks, 256, 0, s>>>(p, g, m, v, shadow, n, lr, b1, b2, eps, wd, c1, c2, norm_scale);
+    return LAUNCH_CHECK();
+}
+
+__global__ void cast_bf16_kernel(bf16* dst, const float* src, size_t n) {
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+        dst[i] = (bf16)src[i];
+}
+hipError_t cast_bf16(bf16* dst, const float* src, size_t n, hipStream_t s) {
+    size_t blocks = cdiv(n, 256);
+    if (blocks > 8192) blocks = 8192;
+    cast_bf16_kernel<<<(unsigned)blocks, 256, 0, s>>>(dst, src, n);
+    return LAUNCH_CHECK();
+}
+
+template <typename T> __global__ void widen_kernel(float* dst, const T* src, size_t n) {
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+        dst[i] = to_f32(src[i]);
+}
+template <typename T> hipError_t widen_f32(float* dst, const T* src, size_t n, hipStream_t s) {
+    size_t blocks = cdiv(n, 256);
+    if (blocks > 8192) blocks = 8192;
+    widen_kernel<T><<<(unsigned)blocks, 256, 0, s>>>(dst, src, n);
+    return LAUNCH_CHECK();
+}
+
+// ---- explicit instantiations ------------------------------------------------
+#define INST(T)                                                                                              \
+    template hipError_t encoder_fwd<T>(T*, int*, const float*, const float*, int, int, int, int, int*,       \
+                                       hipStream_t);                                                         \
+    template hipError_t encoder_bwd<T>(float*, float*, const T*, const int*, int, int, int, hipStream_t);    \
+    template hipError_t layernorm_fwd<T>(T*, float*, float*, const T*, const float*, const float*, int, int, \
+                                         hipStream_t);                                                       \
+    template hipError_t layernorm_bwd<T>(T*, const T*, const T*, const float*, const float*, const float*,   \
+                                         float*, float*, float*, int, int, bool, hipStream_t);               \
+    template hipError_t colsum_accum<T>(float*, const T*, int, int, float*, hipStream_t);                    \
+    template hipError_t softmax_ce<T>(T*, float*, const int*, int, int, int, float, int*, hipStream_t);      \
+    template hipError_t widen_f32<T>(float*, const T*, size_t, hipStream_t);
+INST(float)
+INST(bf16)

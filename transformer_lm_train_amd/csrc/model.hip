@@ -1,0 +1,743 @@
+// Host side of the GPT-2 step library: buffer planner, parameter init, step
+// orchestration and the C ABI declared in include/gpt2.h.
+//
+// The step follows the llm.c lesson ("llm.c: GPT-2 training in plain C, with
+// every gradient written by hand", section 2 "How the code works"):
+// gpt2_forward calls each layer in order, gpt2_backward the matching
+// backward functions in reverse, gpt2_update applies AdamW, and everything
+// lives in one allocation made up front.  Here that allocation is the
+// caller's device buffer, carved by the planner below.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+#include <thread>
+#include <type_traits>
+#include <vector>
+
+#include "../../include/gpt2.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+#define HIPCHK(expr)                                                                                     \
+    do {                                                                                                 \
+        hipError_t e_ = (expr);                                                                          \
+        if (e_ != hipSuccess) return fail(GPT2_EIO, "%s failed: %s", #expr, hipGetErrorString(e_));      \
+    } while (0)
+
+enum { P_WTE, P_WPE, P_LN1W, P_LN1B, P_QKVW, P_QKVB, P_ATTPROJW, P_ATTPROJB, P_LN2W, P_LN2B, P_FCW, P_FCB,
+       P_FCPROJW, P_FCPROJB, P_LNFW, P_LNFB, NPARAM };
+
+void param_sizes(const gpt2_config& c, size_t s[NPARAM]) {
+    size_t L = c.num_layers, C = c.channels;
+    s[P_WTE] = (size_t)c.padded_vocab_size * C;
+    s[P_WPE] = (size_t)c.max_seq_len * C;
+    s[P_LN1W] = s[P_LN1B] = L * C;
+    s[P_QKVW] = L * 3 * C * C;
+    s[P_QKVB] = L * 3 * C;
+    s[P_ATTPROJW] = L * C * C;
+    s[P_ATTPROJB] = L * C;
+    s[P_LN2W] = s[P_LN2B] = L * C;
+    s[P_FCW] = L * 4 * C * C;
+    s[P_FCB] = L * 4 * C;
+    s[P_FCPROJW] = L * C * 4 * C;
+    s[P_FCPROJB] = L * C;
+    s[P_LNFW] = s[P_LNFB] = C;
+}
+
+// Byte offsets of every region of the single device buffer.
+struct Layout {
+    size_t N, poff[NPARAM];
+    size_t params, grads, m, v, shadow;
+    size_t encoded, ln1, qkv, atty, res2, ln2, fch, fchg, res3, lnf, logits;
+    size_t ln1_mean, ln1_rstd, ln2_mean, ln2_rstd, lnf_mean, lnf_rstd, lse, losses;
+    size_t dres, dbig, dmid, attD, partial, norm_partial, scalars, err, tokens, targets;
+    size_t total;
+};
+
+int validate(const gpt2_config* c) {
+    if (!c) return fail(GPT2_EINVAL, "config is NULL");
+    if (c->num_layers <= 0 || c->channels <= 0 || c->num_heads <= 0 || c->max_seq_len <= 0 || c->vocab_size <= 0 ||
+        c->padded_vocab_size <= 0 || c->batch_size <= 0 || c->seq_len <= 0)
+        return fail(GPT2_EINVAL, "every config size must be positive");
+    if (c->channels % c->num_heads) return fail(GPT2_EINVAL, "channels %% num_heads != 0");
+    if (c->seq_len > c->max_seq_len) return fail(GPT2_EINVAL, "seq_len > max_seq_len");
+    if (c->vocab_size > c->padded_vocab_size) return fail(GPT2_EINVAL, "vocab_size > padded_vocab_size");
+    if (c->precision != GPT2_FP32 && c->precision != GPT2_BF16_MIXED) return fail(GPT2_EINVAL, "unknown precision");
+    if (c->channels % 8 || c->padded_vocab_size % 8)
+        return fail(GPT2_EINVAL, "channels and padded_vocab_size must be multiples of 8");
+    int hs = c->channels / c->num_heads;
+    if (c->seq_len > 1024 || hs > 128) return fail(GPT2_EINVAL, "seq_len <= 1024 and head size <= 128 required");
+    if (c->channels > 4096) return fail(GPT2_EINVAL, "channels <= 4096 required");
+    if (c->precision == GPT2_BF16_MIXED) {
+        if (hs != 64) return fail(GPT2_EINVAL, "BF16_MIXED needs head size 64");
+        if (c->channels % 64 || c->padded_vocab_size % 64 || ((int64_t)c->batch_size * c->seq_len) % 64)
+            return fail(GPT2_EINVAL, "BF16_MIXED needs C, Vp and B*T to be multiples of 64");
+    }
+    return GPT2_OK;
+}
+
+Layout make_layout(const gpt2_config& c) {
+    Layout L{};
+    size_t s[NPARAM];
+    param_sizes(c, s);
+    L.N = 0;
+    for (int i = 0; i < NPARAM; i++) { L.poff[i] = L.N; L.N += s[i]; }
+    size_t total = 0;
+    auto add = [&](size_t bytes) {
+        size_t off = (total + 255) & ~(size_t)255;
+        total = off + bytes;
+        return off;
+    };
+    const size_t A = c.precision == GPT2_BF16_MIXED ? 2 : 4;  // activation bytes
+    const size_t Ly = c.num_layers, C = c.channels, BT = (size_t)c.batch_size * c.seq_len;
+    L.params = add(4 * L.N);
+    L.grads = add(4 * L.N);
+    L.m = add(4 * L.N);
+    L.v = add(4 * L.N);
+    L.shadow = c.precision == GPT2_BF16_MIXED ? add(2 * L.N) : 0;
+    L.encoded = add(A * BT * C);
+    L.ln1 = add(A * Ly * BT * C);
+    L.qkv = add(A * Ly * BT * 3 * C);
+    L.atty = add(A * Ly * BT * C);
+    L.res2 = add(A * Ly * BT * C);
+    L.ln2 = add(A * Ly * BT * C);
+    L.fch = add(A * Ly * BT * 4 * C);
+    L.fchg = add(A * Ly * BT * 4 * C);
+    L.res3 = add(A * Ly * BT * C);
+    L.lnf = add(A * BT * C);
+    L.logits = add(A * BT * c.padded_vocab_size);
+    L.ln1_mean = add(4 * Ly * BT);
+    L.ln1_rstd = add(4 * Ly * BT);
+    L.ln2_mean = add(4 * Ly * BT);
+    L.ln2_rstd = add(4 * Ly * BT);
+    L.lnf_mean = add(4 * BT);
+    L.lnf_rstd = add(4 * BT);
+    L.lse = add(4 * Ly * BT * c.num_heads);
+    L.losses = add(4 * BT);
+    L.dres = add(A * BT * C);
+    L.dbig = add(A * BT * 4 * C);
+    L.dmid = add(A * BT * C);
+    L.attD = add(4 * BT * c.num_heads);
+    L.partial = add(4 * 512 * C);
+    L.norm_partial = add(4 * 1024);
+    L.scalars = add(64);
+    L.err = add(64);
+    L.tokens = add(4 * BT);
+    L.targets = add(4 * BT);
+    L.total = add(0);
+    return L;
+}
+
+// ---- init: SplitMix64 (Steele, Lea & Flood 2014) + Box-Muller -------------
+inline uint64_t splitmix64_at(uint64_t seed, uint64_t n) {
+    uint64_t z = seed + n * 0x9E3779B97F4A7C15ULL;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ULL;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBULL;
+    return z ^ (z >> 31);
+}
+inline double gaussian_at(uint64_t seed, uint64_t idx) {
+    const double two_pow_m53 = 1.0 / 9007199254740992.0;
+    double u1 = ((double)(splitmix64_at(seed, 2 * idx + 1) >> 11) + 0.5) * two_pow_m53;
+    double u2 = (double)(splitmix64_at(seed, 2 * idx + 2) >> 11) * two_pow_m53;
+    double radius = sqrt(-2.0 * log(u1));
+    return radius * cos(6.283185307179586 * u2);
+}
+
+void init_params_host(const gpt2_config& c, const Layout& L, uint64_t seed, float* p) {
+    size_t s[NPARAM];
+    param_sizes(c, s);
+    const double sd = 0.02, sd_res = 0.02 / sqrt(2.0 * (double)c.num_layers);
+    struct Job { size_t off, n, live; double std; };
+    std::vector<Job> jobs;
+    for (int i = 0; i < NPARAM; i++) {
+        size_t off = L.poff[i];
+        switch (i) {
+            case P_WTE: jobs.push_back({off, s[i], (size_t)c.vocab_size * c.channels, sd}); break;
+            case P_WPE: case P_QKVW: case P_FCW: jobs.push_back({off, s[i], s[i], sd}); break;
+            case P_ATTPROJW: case P_FCPROJW: jobs.push_back({off, s[i], s[i], sd_res}); break;
+            case P_LN1W: case P_LN2W: case P_LNFW:
+                for (size_t j = 0; j < s[i]; j++) p[off + j] = 1.f;
+                break;
+            default:
+                for (size_t j = 0; j < s[i]; j++) p[off + j] = 0.f;
+        }
+    }
+    unsigned nt = std::thread::hardware_concurrency();
+    if (nt == 0) nt = 4;
+    if (nt > 64) nt = 64;
+    std::vector<std::thread> th;
+    for (unsigned w = 0; w < nt; w++) {
+        th.emplace_back([&, w]() {
+            for (const Job& j : jobs) {
+                size_t lo = j.n * w / nt, hi = j.n * (w + 1) / nt;
+                for (size_t k = lo; k < hi; k++)
+                    p[j.off + k] = k < j.live ? (float)(j.std * gaussian_at(seed, j.off + k)) : 0.f;
+            }
+        });
+    }
+    for (auto& t : th) t.join();
+}
+
+}  // namespace
+
+// ============================================================================
+struct gpt2_model {
+    gpt2_config cfg;
+    Layout L;
+    hipStream_t stream;
+    char* base;
+    size_t bytes;
+    int32_t* h_tok;      // pinned staging for host token arrays
+    float* h_scalars;    // pinned readback
+    hipEvent_t staged;   // last H2D from the staging buffer
+    bool have_targets = false;
+    bool logits_valid = false;
+    bool norm_bad = false;
+    bool clip_pending = false;  // gpt2_clip_grad_norm ran since the last update
+    // kernel timing
+    std::string t_cls;
+    bool t_on = false;
+    std::vector<hipEvent_t> t_ev;
+    size_t t_used = 0;
+
+    template <typename T> T* P(size_t off) { return reinterpret_cast<T*>(base + off); }
+    float* params() { return P<float>(L.params); }
+    float* grads() { return P<float>(L.grads); }
+    bool bf16mode() const { return cfg.precision == GPT2_BF16_MIXED; }
+};
+
+namespace {
+
+struct TimeScope {
+    gpt2_t* m;
+    bool on;
+    TimeScope(gpt2_t* m_, const char* cls) : m(m_), on(m_->t_on && m_->t_cls == cls) {
+        if (on) rec();
+    }
+    ~TimeScope() {
+        if (on) rec();
+    }
+    void rec() {
+        if (m->t_used >= m->t_ev.size()) {
+            hipEvent_t e;
+            if (hipEventCreate(&e) != hipSuccess) return;
+            m->t_ev.push_back(e);
+        }
+        (void)hipEventRecord(m->t_ev[m->t_used++], m->stream);
+    }
+};
+
+#define RUN(cls, expr)                                                                          \
+    do {                                                                                        \
+        TimeScope ts_(M, cls);                                                                  \
+        hipError_t e_ = (expr);                                                                 \
+        if (e_ != hipSuccess) return fail(GPT2_EIO, "%s: %s", #expr, hipGetErrorString(e_));   \
+    } while (0)
+
+template <typename T> hipError_t gemm(gpt2_t* M, const GemmArgs& g) {
+    if constexpr (std::is_same<T, bf16>::value) return gemm_mfma_bf16(g, M->stream);
+    else return gemm_simt<float>(g, M->stream);
+}
+
+// out[M,N] = X[M,K] W[N,K]^T + epilogue
+template <typename T>
+hipError_t lin_fwd(gpt2_t* Mo, T* out, const T* X, const T* W, const float* bias, int M, int N, int K, int epi,
+                   const T* resid = nullptr, T* out2 = nullptr) {
+    GemmArgs g{};
+    g.M = M; g.N = N; g.K = K;
+    g.a = X; g.lda = K; g.a_kcontig = true;
+    g.b = W; g.ldb = K; g.b_kcontig = true;
+    g.out = out; g.ldo = N; g.bias = bias; g.resid = resid; g.out2 = out2; g.epi = epi;
+    return gemm<T>(Mo, g);
+}
+// dX[M,K] = dY[M,N] W[N,K]  (+ GELU' epilogue with aux)
+template <typename T>
+hipError_t lin_dx(gpt2_t* Mo, T* dX, const T* dY, const T* W, int M, int N, int K, int epi, const T* aux = nullptr) {
+    GemmArgs g{};
+    g.M = M; g.N = K; g.K = N;
+    g.a = dY; g.lda = N; g.a_kcontig = true;
+    g.b = W; g.ldb = K; g.b_kcontig = false;
+    g.out = dX; g.ldo = K; g.aux = aux; g.epi = epi;
+    return gemm<T>(Mo, g);
+}
+// dW[N,K] += dY[M,N]^T X[M,K]
+template <typename T>
+hipError_t lin_dw(gpt2_t* Mo, float* dW, const T* dY, const T* X, int M, int N, int K) {
+    GemmArgs g{};
+    g.M = N; g.N = K; g.K = M;
+    g.a = dY; g.lda = N; g.a_kcontig = false;
+    g.b = X; g.ldb = K; g.b_kcontig = false;
+    g.out = dW; g.ldo = K; g.epi = EPI_ACC_F32;
+    return gemm<T>(Mo, g);
+}
+
+template <typename T> struct Acts {
+    // per-layer activation pointers
+    T *encoded, *ln1, *qkv, *atty, *res2, *ln2, *fch, *fchg, *res3, *lnf, *logits, *dres, *dbig, *dmid;
+    float *ln1m, *ln1r, *ln2m, *ln2r, *lnfm, *lnfr, *lse, *losses;
+    size_t BTC;
+    Acts(gpt2_t* m) {
+        const Layout& L = m->L;
+        encoded = m->P<T>(L.encoded); ln1 = m->P<T>(L.ln1); qkv = m->P<T>(L.qkv); atty = m->P<T>(L.atty);
+        res2 = m->P<T>(L.res2); ln2 = m->P<T>(L.ln2); fch = m->P<T>(L.fch); fchg = m->P<T>(L.fchg);
+        res3 = m->P<T>(L.res3); lnf = m->P<T>(L.lnf); logits = m->P<T>(L.logits);
+        dres = m->P<T>(L.dres); dbig = m->P<T>(L.dbig); dmid = m->P<T>(L.dmid);
+        ln1m = m->P<float>(L.ln1_mean); ln1r = m->P<float>(L.ln1_rstd);
+        ln2m = m->P<float>(L.ln2_mean); ln2r = m->P<float>(L.ln2_rstd);
+        lnfm = m->P<float>(L.lnf_mean); lnfr = m->P<float>(L.lnf_rstd);
+        lse = m->P<float>(L.lse); losses = m->P<float>(L.losses);
+        BTC = (size_t)m->cfg.batch_size * m->cfg.seq_len * m->cfg.channels;
+    }
+};
+
+// matmul weights: the bf16 shadow in mixed mode, the fp32 master otherwise
+template <typename T> const T* weights(gpt2_t* m) {
+    if constexpr (std::is_same<T, bf16>::value) return m->P<bf16>(m->L.shadow);
+    else return m->params();
+}
+
+template <typename T> int forward_impl(gpt2_t* M, bool with_targets) {
+    const gpt2_config& c = M->cfg;
+    const int B = c.batch_size, T_ = c.seq_len, C = c.channels, NH = c.num_heads, Ly = c.num_layers;
+    const int BT = B * T_, Vp = c.padded_vocab_size, V = c.vocab_size;
+    hipStream_t s = M->stream;
+    Acts<T> a(M);
+    const float* p = M->params();
+    const T* w = weights<T>(M);
+    const size_t* po = M->L.poff;
+    const size_t BTC = a.BTC;
+    int* err = M->P<int>(M->L.err);
+    int* tok = M->P<int>(M->L.tokens);
+
+    RUN("encoder_fwd", encoder_fwd<T>(a.encoded, tok, p + po[P_WTE], p + po[P_WPE], B, T_, C, V, err, s));
+    const T* x = a.encoded;
+    for (int l = 0; l < Ly; l++) {
+        T* ln1 = a.ln1 + l * BTC;
+        T* qkv = a.qkv + l * BTC * 3;
+        T* atty = a.atty + l * BTC;
+        T* res2 = a.res2 + l * BTC;
+        T* ln2 = a.ln2 + l * BTC;
+        T* fch = a.fch + l * BTC * 4;
+        T* fchg = a.fchg + l * BTC * 4;
+        T* res3 = a.res3 + l * BTC;
+        const size_t lC = (size_t)l * C;
+        RUN("layernorm_fwd", layernorm_fwd<T>(ln1, a.ln1m + (size_t)l * BT, a.ln1r + (size_t)l * BT, x,
+                                              p + po[P_LN1W] + lC, p + po[P_LN1B] + lC, BT, C, s));
+        RUN("gemm_fwd", lin_fwd<T>(M, qkv, ln1, w + po[P_QKVW] + lC * 3 * C, p + po[P_QKVB] + lC * 3, BT, 3 * C, C,
+                                   EPI_BIAS));
+        RUN("attention_fwd", attention_fwd<T>(atty, a.lse + (size_t)l * BT * NH, qkv, B, T_, C, NH, s));
+        RUN("gemm_fwd", lin_fwd<T>(M, res2, atty, w + po[P_ATTPROJW] + lC * C, p + po[P_ATTPROJB] + lC, BT, C, C,
+                                   EPI_BIAS_RESID, x));
+        RUN("layernorm_fwd", layernorm_fwd<T>(ln2, a.ln2m + (size_t)l * BT, a.ln2r + (size_t)l * BT, res2,
+                                              p + po[P_LN2W] + lC, p + po[P_LN2B] + lC, BT, C, s));
+        RUN("gemm_fwd", lin_fwd<T>(M, fch, ln2, w + po[P_FCW] + lC * 4 * C, p + po[P_FCB] + lC * 4, BT, 4 * C, C,
+                                   EPI_BIAS_GELU, nullptr, fchg));
+        RUN("gemm_fwd", lin_fwd<T>(M, res3, fchg, w + po[P_FCPROJW] + lC * 4 * C, p + po[P_FCPROJB] + lC, BT, C,
+                                   4 * C, EPI_BIAS_RESID, res2));
+        x = res3;
+    }
+    RUN("layernorm_fwd", layernorm_fwd<T>(a.lnf, a.lnfm, a.lnfr, x, p + po[P_LNFW], p + po[P_LNFB], BT, C, s));
+    RUN("gemm_classifier_fwd", lin_fwd<T>(M, a.logits, a.lnf, w + po[P_WTE], nullptr, BT, Vp, C, EPI_STORE));
+    if (with_targets) {
+        RUN("softmax_ce", softmax_ce<T>(a.logits, a.losses, M->P<int>(M->L.targets), BT, V, Vp, 1.0f / BT, err, s));
+        RUN("loss_mean", loss_mean(M->P<float>(M->L.scalars), a.losses, BT, s));
+    }
+    return GPT2_OK;
+}
+
+template <typename T> int backward_impl(gpt2_t* M) {
+    const gpt2_config& c = M->cfg;
+    const int B = c.batch_size, T_ = c.seq_len, C = c.channels, NH = c.num_heads, Ly = c.num_layers;
+    const int BT = B * T_, Vp = c.padded_vocab_size;
+    hipStream_t s = M->stream;
+    Acts<T> a(M);
+    const float* p = M->params();
+    float* g = M->grads();
+    const T* w = weights<T>(M);
+    const size_t* po = M->L.poff;
+    const size_t BTC = a.BTC;
+    float* part = M->P<float>(M->L.partial);
+    float* attD = M->P<float>(M->L.attD);
+
+    // classifier (tied to wte): logits now hold dlogits
+    RUN("gemm_classifier_dx", lin_dx<T>(M, a.dmid, a.logits, w + po[P_WTE], BT, Vp, C, EPI_STORE));
+    RUN("gemm_classifier_dw", lin_dw<T>(M, g + po[P_WTE], a.logits, a.lnf, BT, Vp, C));
+    const T* xlast = a.res3 + (size_t)(Ly - 1) * BTC;
+    RUN("layernorm_bwd", layernorm_bwd<T>(a.dres, a.dmid, xlast, p + po[P_LNFW], a.lnfm, a.lnfr, g + po[P_LNFW],
+                                          g + po[P_LNFB], part, BT, C, true, s));
+    for (int l = Ly - 1; l >= 0; l--) {
+        const T* xin = l == 0 ? a.encoded : a.res3 + (size_t)(l - 1) * BTC;
+        const T* ln1 = a.ln1 + l * BTC;
+        const T* qkv = a.qkv + l * BTC * 3;
+        const T* atty = a.atty + l * BTC;
+        const T* res2 = a.res2 + l * BTC;
+        const T* ln2 = a.ln2 + l * BTC;
+        const T* fch = a.fch + l * BTC * 4;
+        const T* fchg = a.fchg + l * BTC * 4;
+        const size_t lC = (size_t)l * C;
+        // fcproj: res3 = res2 + fchg Wfp^T + b   (dres is d res3)
+        RUN("gemm_dx", lin_dx<T>(M, a.dbig, a.dres, w + po[P_FCPROJW] + lC * 4 * C, BT, C, 4 * C, EPI_GELU_BWD, fch));
+        RUN("gemm_dw", lin_dw<T>(M, g + po[P_FCPROJW] + lC * 4 * C, a.dres, fchg, BT, C, 4 * C));
+        RUN("colsum", colsum_accum<T>(g + po[P_FCPROJB] + lC, a.dres, BT, C, part, s));
+        // fc: fch = ln2 Wfc^T + b   (dbig is d fch)
+        RUN("gemm_dx", lin_dx<T>(M, a.dmid, a.dbig, w + po[P_FCW] + lC * 4 * C, BT, 4 * C, C, EPI_STORE));
+        RUN("gemm_dw", lin_dw<T>(M, g + po[P_FCW] + lC * 4 * C, a.dbig, ln2, BT, 4 * C, C));
+        RUN("colsum", colsum_accum<T>(g + po[P_FCB] + lC * 4, a.dbig, BT, 4 * C, part, s));
+        // ln2: dres += LN2'(dmid)  -> dres is d res2
+        RUN("layernorm_bwd", layernorm_bwd<T>(a.dres, a.dmid, res2, p + po[P_LN2W] + lC, a.ln2m + (size_t)l * BT,
+                                              a.ln2r + (size_t)l * BT, g + po[P_LN2W] + lC, g + po[P_LN2B] + lC,
+                                              part, BT, C, false, s));
+        // attproj: res2 = xin + atty Wap^T + b
+        RUN("gemm_dx", lin_dx<T>(M, a.dmid, a.dres, w + po[P_ATTPROJW] + lC * C, BT, C, C, EPI_STORE));
+        RUN("gemm_dw", lin_dw<T>(M, g + po[P_ATTPROJW] + lC * C, a.dres, atty, BT, C, C));
+        RUN("colsum", colsum_accum<T>(g + po[P_ATTPROJB] + lC, a.dres, BT, C, part, s));
+        // attention: dmid (d atty) -> dbig (d qkv)
+        RUN("attention_bwd", attention_bwd<T>(a.dbig, a.dmid, qkv, atty, a.lse + (size_t)l * BT * NH, attD, B, T_,
+                                              C, NH, s));
+        // qkv: qkv = ln1 Wqkv^T + b
+        RUN("gemm_dx", lin_dx<T>(M, a.dmid, a.dbig, w + po[P_QKVW] + lC * 3 * C, BT, 3 * C, C, EPI_STORE));
+        RUN("gemm_dw", lin_dw<T>(M, g + po[P_QKVW] + lC * 3 * C, a.dbig, ln1, BT, 3 * C, C));
+        RUN("colsum", colsum_accum<T>(g + po[P_QKVB] + lC * 3, a.dbig, BT, 3 * C, part, s));
+        // ln1: dres += LN1'(dmid) -> dres is d xin
+        RUN("layernorm_bwd", layernorm_bwd<T>(a.dres, a.dmid, xin, p + po[P_LN1W] + lC, a.ln1m + (size_t)l * BT,
+                                              a.ln1r + (size_t)l * BT, g + po[P_LN1W] + lC, g + po[P_LN1B] + lC,
+                                              part, BT, C, false, s));
+    }
+    RUN("encoder_bwd", encoder_bwd<T>(g + po[P_WTE], g + po[P_WPE], a.dres, M->P<int>(M->L.tokens), B, T_, C, s));
+    return GPT2_OK;
+}
+
+int read_scalars(gpt2_t* M, int n_floats) {
+    HIPCHK(hipMemcpyAsync(M->h_scalars, M->P<float>(M->L.scalars), 16, hipMemcpyDeviceToHost, M->stream));
+    HIPCHK(hipMemcpyAsync(M->h_scalars + 4, M->P<int>(M->L.err), 4, hipMemcpyDeviceToHost, M->stream));
+    HIPCHK(hipStreamSynchronize(M->stream));
+    (void)n_floats;
+    int errflag;
+    memcpy(&errflag, M->h_scalars + 4, 4);
+    if (errflag) {
+        HIPCHK(hipMemsetAsync(M->P<int>(M->L.err), 0, 4, M->stream));
+        return fail(GPT2_EINVAL, "token or target id outside [0, vocab_size) (flag %d); it was replaced by 0",
+                    errflag);
+    }
+    return GPT2_OK;
+}
+
+int forward_common(gpt2_t* M, bool with_targets, float* mean_loss) {
+    int rc = M->bf16mode() ? forward_impl<bf16>(M, with_targets) : forward_impl<float>(M, with_targets);
+    if (rc) return rc;
+    M->have_targets = with_targets;
+    M->logits_valid = !with_targets;
+    if (mean_loss) {
+        if (!with_targets) {
+            *mean_loss = NAN;
+            return GPT2_OK;
+        }
+        rc = read_scalars(M, 1);
+        if (rc) {
+            M->have_targets = false;
+            return rc;
+        }
+        *mean_loss = M->h_scalars[0];
+    }
+    return GPT2_OK;
+}
+
+}  // namespace
+
+// ============================================================================
+// C ABI
+// ============================================================================
+extern "C" {
+
+const char* gpt2_last_error(void) { return g_last_error.c_str(); }
+
+int gpt2_plan(const gpt2_config* cfg, size_t* device_bytes) {
+    int rc = validate(cfg);
+    if (rc) return rc;
+    if (!device_bytes) return fail(GPT2_EINVAL, "device_bytes is NULL");
+    *device_bytes = make_layout(*cfg).total;
+    return GPT2_OK;
+}
+
+int gpt2_build(const gpt2_config* cfg, uint64_t seed, void* device_buf, size_t bytes, void* hip_stream,
+               gpt2_t** out) {
+    int rc = validate(cfg);
+    if (rc) return rc;
+    if (!out) return fail(GPT2_EINVAL, "out is NULL");
+    *out = nullptr;
+    Layout L = make_layout(*cfg);
+    if (!device_buf) return fail(GPT2_EINVAL, "device_buf is NULL");
+    if ((uintptr_t)device_buf & 255) return fail(GPT2_EINVAL, "device_buf must be 256-byte aligned");
+    if (bytes < L.total) return fail(GPT2_ENOMEM, "device buffer has %zu bytes, the plan needs %zu", bytes, L.total);
+    gpt2_t* M = new gpt2_model();
+    M->cfg = *cfg;
+    M->L = L;
+    M->stream = (hipStream_t)hip_stream;
+    M->base = (char*)device_buf;
+    M->bytes = bytes;
+    size_t BT = (size_t)cfg->batch_size * cfg->seq_len;
+    if (hipHostMalloc((void**)&M->h_tok, 8 * BT, 0) != hipSuccess ||
+        hipHostMalloc((void**)&M->h_scalars, 64, 0) != hipSuccess || hipEventCreate(&M->staged) != hipSuccess) {
+        delete M;
+        return fail(GPT2_EIO, "pinned host staging allocation failed");
+    }
+    std::vector<float> host(L.N);
+    init_params_host(*cfg, L, seed, host.data());
+    hipStream_t s = M->stream;
+    hipError_t e = hipMemcpyAsync(M->params(), host.data(), 4 * L.N, hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipMemsetAsync(M->grads(), 0, 4 * L.N, s);
+    if (e == hipSuccess) e = hipMemsetAsync(M->P<float>(L.m), 0, 4 * L.N, s);
+    if (e == hipSuccess) e = hipMemsetAsync(M->P<float>(L.v), 0, 4 * L.N, s);
+    if (e == hipSuccess) e = hipMemsetAsync(M->P<int>(L.err), 0, 64, s);
+    if (e == hipSuccess) e = hipMemsetAsync(M->P<float>(L.scalars), 0, 64, s);
+    if (e == hipSuccess && M->bf16mode()) e = cast_bf16(M->P<bf16>(L.shadow), M->params(), L.N, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) {
+        gpt2_destroy(M);
+        return fail(GPT2_EIO, "gpt2_build: %s", hipGetErrorString(e));
+    }
+    *out = M;
+    return GPT2_OK;
+}
+
+int gpt2_destroy(gpt2_t* M) {
+    if (!M) return GPT2_OK;
+    (void)hipStreamSynchronize(M->stream);
+    if (M->h_tok) (void)hipHostFree(M->h_tok);
+    if (M->h_scalars) (void)hipHostFree(M->h_scalars);
+    if (M->staged) (void)hipEventDestroy(M->staged);
+    for (auto e : M->t_ev) (void)hipEventDestroy(e);
+    delete M;
+    return GPT2_OK;
+}
+
+int gpt2_forward(gpt2_t* M, const int32_t* tokens, const int32_t* targets, float* mean_loss) {
+    if (!M || !tokens) return fail(GPT2_EINVAL, "NULL model or tokens");
+    const gpt2_config& c = M->cfg;
+    size_t BT = (size_t)c.batch_size * c.seq_len;
+    for (size_t i = 0; i < BT; i++) {
+        if (tokens[i] < 0 || tokens[i] >= c.vocab_size) return fail(GPT2_EINVAL, "token %zu = %d out of range", i, tokens[i]);
+        if (targets && (targets[i] < 0 || targets[i] >= c.vocab_size))
+            return fail(GPT2_EINVAL, "target %zu = %d out of range", i, targets[i]);
+    }
+    HIPCHK(hipEventSynchronize(M->staged));  // the previous upload has left the staging buffer
+    memcpy(M->h_tok, tokens, 4 * BT);
+    if (targets) memcpy(M->h_tok + BT, targets, 4 * BT);
+    HIPCHK(hipMemcpyAsync(M->P<int>(M->L.tokens), M->h_tok, 4 * BT, hipMemcpyHostToDevice, M->stream));
+    if (targets)
+        HIPCHK(hipMemcpyAsync(M->P<int>(M->L.targets), M->h_tok + BT, 4 * BT, hipMemcpyHostToDevice, M->stream));
+    HIPCHK(hipEventRecord(M->staged, M->stream));
+    return forward_common(M, targets != nullptr, mean_loss);
+}
+
+int gpt2_forward_device(gpt2_t* M, const int32_t* d_tokens, const int32_t* d_targets, float* mean_loss) {
+    if (!M || !d_tokens) return fail(GPT2_EINVAL, "NULL model or tokens");
+    size_t BT = (size_t)M->cfg.batch_size * M->cfg.seq_len;
+    HIPCHK(hipMemcpyAsync(M->P<int>(M->L.tokens), d_tokens, 4 * BT, hipMemcpyDeviceToDevice, M->stream));
+    if (d_targets)
+        HIPCHK(hipMemcpyAsync(M->P<int>(M->L.targets), d_targets, 4 * BT, hipMemcpyDeviceToDevice, M->stream));
+    return forward_common(M, d_targets != nullptr, mean_loss);
+}
+
+int gpt2_read_loss(gpt2_t* M, float* mean_loss) {
+    if (!M || !mean_loss) return fail(GPT2_EINVAL, "NULL argument");
+    if (!M->have_targets) return fail(GPT2_EPERM, "no forward with targets since the last update");
+    int rc = read_scalars(M, 1);
+    if (rc) return rc;
+    *mean_loss = M->h_scalars[0];
+    return GPT2_OK;
+}
+
+int gpt2_zero_grad(gpt2_t* M) {
+    if (!M) return fail(GPT2_EINVAL, "NULL model");
+    HIPCHK(hipMemsetAsync(M->grads(), 0, 4 * M->L.N, M->stream));
+    return GPT2_OK;
+}
+
+int gpt2_backward(gpt2_t* M) {
+    if (!M) return fail(GPT2_EINVAL, "NULL model");
+    if (!M->have_targets) return fail(GPT2_EPERM, "gpt2_backward needs a forward with targets first");
+    int rc = M->bf16mode() ? backward_impl<bf16>(M) : backward_impl<float>(M);
+    M->have_targets = false;  // dlogits were consumed
+    return rc;
+}
+
+int gpt2_clip_grad_norm(gpt2_t* M, float max_norm, float* norm) {
+    if (!M) return fail(GPT2_EINVAL, "NULL model");
+    float* ns = M->P<float>(M->L.scalars) + 4;
+    RUN("grad_norm", grad_norm(M->P<float>(M->L.norm_partial), ns, M->grads(), M->L.N, max_norm, M->stream));
+    M->norm_bad = false;
+    M->clip_pending = true;
+    if (norm) {
+        HIPCHK(hipMemcpyAsync(M->h_scalars, ns, 8, hipMemcpyDeviceToHost, M->stream));
+        HIPCHK(hipStreamSynchronize(M->stream));
+        *norm = M->h_scalars[0];
+        if (!isfinite(*norm)) {
+            M->norm_bad = true;
+            return fail(GPT2_ERANGE, "gradient norm is not finite");
+        }
+    }
+    return GPT2_OK;
+}
+
+int gpt2_adamw_step(gpt2_t* M, float lr, float beta1, float beta2, float eps, float weight_decay, int t) {
+    if (!M) return fail(GPT2_EINVAL, "NULL model");
+    if (t < 1) return fail(GPT2_EINVAL, "AdamW step t must be >= 1 (got %d)", t);
+    if (M->norm_bad) return fail(GPT2_ERANGE, "refusing the update: the last gradient norm was not finite");
+    float c1 = (float)(1.0 - pow((double)beta1, t)), c2 = (float)(1.0 - pow((double)beta2, t));
+    float* ns = M->clip_pending ? M->P<float>(M->L.scalars) + 4 : nullptr;
+    bf16* sh = M->bf16mode() ? M->P<bf16>(M->L.shadow) : nullptr;
+    RUN("adamw", adamw(M->params(), M->grads(), M->P<float>(M->L.m), M->P<float>(M->L.v), sh, M->L.N, lr, beta1, beta2,
+                       eps, weight_decay, c1, c2, ns, M->stream));
+    M->clip_pending = false;  // a clip factor applies to one update only
+    M->have_targets = false;
+    return GPT2_OK;
+}
+
+size_t gpt2_num_params(const gpt2_t* M) { return M ? M->L.N : 0; }
+
+int gpt2_param_offsets(const gpt2_t* M, size_t offsets[16]) {
+    if (!M || !offsets) return fail(GPT2_EINVAL, "NULL argument");
+    for (int i = 0; i < NPARAM; i++) offsets[i] = M->L.poff[i];
+    return GPT2_OK;
+}
+
+int gpt2_copy_params(gpt2_t* M, float* dst) {
+    if (!M || !dst) return fail(GPT2_EINVAL, "NULL argument");
+    HIPCHK(hipMemcpyAsync(dst, M->params(), 4 * M->L.N, hipMemcpyDeviceToHost, M->stream));
+    HIPCHK(hipStreamSynchronize(M->stream));
+    return GPT2_OK;
+}
+
+int gpt2_copy_grads(gpt2_t* M, float* dst) {
+    if (!M || !dst) return fail(GPT2_EINVAL, "NULL argument");
+    HIPCHK(hipMemcpyAsync(dst, M->grads(), 4 * M->L.N, hipMemcpyDeviceToHost, M->stream));
+    HIPCHK(hipStreamSynchronize(M->stream));
+    return GPT2_OK;
+}
+
+int gpt2_copy_opt_state(gpt2_t* M, float* mdst, float* vdst) {
+    if (!M) return fail(GPT2_EINVAL, "NULL model");
+    if (mdst) HIPCHK(hipMemcpyAsync(mdst, M->P<float>(M->L.m), 4 * M->L.N, hipMemcpyDeviceToHost, M->stream));
+    if (vdst) HIPCHK(hipMemcpyAsync(vdst, M->P<float>(M->L.v), 4 * M->L.N, hipMemcpyDeviceToHost, M->stream));
+    HIPCHK(hipStreamSynchronize(M->stream));
+    return GPT2_OK;
+}
+
+int gpt2_copy_logits(gpt2_t* M, float* dst) {
+    if (!M || !dst) return fail(GPT2_EINVAL, "NULL argument");
+    if (!M->logits_valid) return fail(GPT2_EPERM, "logits are only kept by a forward without targets");
+    size_t n = (size_t)M->cfg.batch_size * M->cfg.seq_len * M->cfg.padded_vocab_size;
+    if (M->bf16mode()) {
+        // widen into the dbig/dmid activation-gradient scratch is too small; widen in chunks via dbig
+        const bf16* src = M->P<bf16>(M->L.logits);
+        float* tmp = M->P<float>(M->L.dbig);
+        size_t chunk = (size_t)M->cfg.batch_size * M->cfg.seq_len * M->cfg.channels * 2;  // floats that fit in dbig
+        for (size_t o = 0; o < n; o += chunk) {
+            size_t k = n - o < chunk ? n - o : chunk;
+            HIPCHK(widen_f32<bf16>(tmp, src + o, k, M->stream));
+            HIPCHK(hipMemcpyAsync(dst + o, tmp, 4 * k, hipMemcpyDeviceToHost, M->stream));
+            HIPCHK(hipStreamSynchronize(M->stream));
+        }
+    } else {
+        HIPCHK(hipMemcpyAsync(dst, M->P<float>(M->L.logits), 4 * n, hipMemcpyDeviceToHost, M->stream));
+        HIPCHK(hipStreamSynchronize(M->stream));
+    }
+    return GPT2_OK;
+}
+
+int gpt2_copy_losses(gpt2_t* M, float* dst) {
+    if (!M || !dst) return fail(GPT2_EINVAL, "NULL argument");
+    size_t n = (size_t)M->cfg.batch_size * M->cfg.seq_len;
+    HIPCHK(hipMemcpyAsync(dst, M->P<float>(M->L.losses), 4 * n, hipMemcpyDeviceToHost, M->stream));
+    HIPCHK(hipStreamSynchronize(M->stream));
+    return GPT2_OK;
+}
+
+int gpt2_set_params(gpt2_t* M, const float* src) {
+    if (!M || !src) return fail(GPT2_EINVAL, "NULL argument");
+    HIPCHK(hipMemcpyAsync(M->params(), src, 4 * M->L.N, hipMemcpyHostToDevice, M->stream));
+    if (M->bf16mode()) HIPCHK(cast_bf16(M->P<bf16>(M->L.shadow), M->params(), M->L.N, M->stream));
+    HIPCHK(hipStreamSynchronize(M->stream));
+    return GPT2_OK;
+}
+
+void* gpt2_device_params(gpt2_t* M) { return M ? M->params() : nullptr; }
+void* gpt2_device_grads(gpt2_t* M) { return M ? M->grads() : nullptr; }
+void* gpt2_device_shadow(gpt2_t* M) { return (M && M->bf16mode()) ? M->base + M->L.shadow : nullptr; }
+
+int gpt2_kernel_timing_enable(gpt2_t* M, const char* cls, int enable) {
+    if (!M) return fail(GPT2_EINVAL, "NULL model");
+    HIPCHK(hipStreamSynchronize(M->stream));
+    M->t_on = enable != 0;
+    M->t_cls = cls ? cls : "";
+    M->t_used = 0;
+    // pre-create events so that none is created inside a timed region
+    while (M->t_ev.size() < 4096) {
+        hipEvent_t e;
+        HIPCHK(hipEventCreate(&e));
+        M->t_ev.push_back(e);
+    }
+    return GPT2_OK;
+}
+
+int gpt2_kernel_timing_read(gpt2_t* M, int* launches, double* total_ms) {
+    if (!M || !launches || !total_ms) return fail(GPT2_EINVAL, "NULL argument");
+    HIPCHK(hipStreamSynchronize(M->stream));
+    double tot = 0;
+    size_t n = M->t_used / 2;
+    for (size_t i = 0; i < n; i++) {
+        float ms = 0;
+        HIPCHK(hipEventElapsedTime(&ms, M->t_ev[2 * i], M->t_ev[2 * i + 1]));
+        tot += ms;
+    }
+    *launches = (int)n;
+    *total_ms = tot;
+    return GPT2_OK;
+}
+
+int gpt2_test_gemm_nt(gpt2_t* M, void* out, const void* a, const void* w, const float* bias, int m, int n, int k) {
+    if (!M || !out || !a || !w) return fail(GPT2_EINVAL, "NULL argument");
+    int epi = bias ? EPI_BIAS : EPI_STORE;
+    if (M->bf16mode())
+        RUN("gemm_test", lin_fwd<bf16>(M, (bf16*)out, (const bf16*)a, (const bf16*)w, bias, m, n, k, epi));
+    else
+        RUN("gemm_test", lin_fwd<float>(M, (float*)out, (const float*)a, (const float*)w, bias, m, n, k, epi));
+    return GPT2_OK;
+}
+
+int gpt2_test_gemm_nn(gpt2_t* M, void* dx, const void* dy, const void* w, int m, int n, int k) {
+    if (!M || !dx || !dy || !w) return fail(GPT2_EINVAL, "NULL argument");
+    if (M->bf16mode())
+        RUN("gemm_test", lin_dx<bf16>(M, (bf16*)dx, (const bf16*)dy, (const bf16*)w, m, n, k, EPI_STORE));
+    else
+        RUN("gemm_test", lin_dx<float>(M, (float*)dx, (const float*)dy, (const float*)w, m, n, k, EPI_STORE));
+    return GPT2_OK;
+}
+
+int gpt2_test_gemm_tn(gpt2_t* M, float* dw, const void* dy, const void* x, int m, int n, int k) {
+    if (!M || !dw || !dy || !x) return fail(GPT2_EINVAL, "NULL argument");
+    if (M->bf16mode())
+        RUN("gemm_test", lin_dw<bf16>(M, dw, (const bf16*)dy, (const bf16*)x, m, n, k));
+    else
+        RUN("gemm_test", lin_dw<float>(M, dw, (const float*)dy, (const float*)x, m, n, k));
+    return GPT2_OK;
+}
+
+}  // extern "C"

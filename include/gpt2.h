@@ -200,6 +200,17 @@ int gpt2_test_gemm_nn(gpt2_t* m, void* dx, const void* dy, const void* w, int M,
 /* dW[N,K] (fp32) += dY[M,N]^T * X[M,K]   (the backward-weight kernel) */
 int gpt2_test_gemm_tn(gpt2_t* m, float* dw, const void* dy, const void* x, int M, int N, int K);
 
+/* Causal attention kernels on device arrays in the model's activation
+ * dtype: qkv [B,T,3C] (q|k|v, head h owns channels [h*hs,(h+1)*hs) of
+ * each), out [B,T,C], lse [B,NH,T] fp32 (natural-log sum of exp of the
+ * scaled scores of each query row), dout [B,T,C], dqkv [B,T,3C].
+ * B*NH*T may not exceed the model's batch_size*num_heads*seq_len (the
+ * backward keeps its row sums D = rowsum(dout o out) in the model's buffer).
+ * The same kernels the training step runs. */
+int gpt2_test_attention_fwd(gpt2_t* m, void* out, float* lse, const void* qkv, int B, int T, int C, int NH);
+int gpt2_test_attention_bwd(gpt2_t* m, void* dqkv, const void* dout, const void* qkv, const void* out,
+                            const float* lse, int B, int T, int C, int NH);
+
 #ifdef __cplusplus
 }
 #endif

@@ -76,3 +76,62 @@ def test_gemm_kernels_vs_oracle(prec, cases, dt, tol):
         _close(_host64(dx), rdx, tol)
         _close(dw.cpu().numpy().astype(np.float64) - dw0, rdw, 1e-5 if dt == "f32" else 2e-5)
     m.close()
+
+
+def test_gemm_split_k_weight_gradient():
+    """The weight-gradient product with a long reduction (split over several
+    workgroups, partials summed in a second kernel) against the oracle."""
+    cfg = G.make_config(1, 64, 1, 64, 64, 64, 64, 64, G.GPT2_BF16_MIXED)  # B*T = 4096 tokens
+    m = G.Model(cfg, 1)
+    rng = np.random.default_rng(1)
+    for (M, N, K) in [(2048, 192, 64), (4096, 64, 64), (1024, 128, 64)]:
+        print(f"split-k gemm M={M} N={N} K={K}", flush=True)
+        dy = _dev(rng.standard_normal((M, N)), torch.bfloat16)
+        x = _dev(rng.standard_normal((M, K)), torch.bfloat16)
+        dw0 = rng.standard_normal((N, K)).astype(np.float32)
+        dw = torch.from_numpy(dw0).cuda()
+        G.gpt2_test_gemm_tn(m.h, dw.data_ptr(), dy.data_ptr(), x.data_ptr(), M, N, K)
+        torch.cuda.synchronize()
+        _, rdw, _ = O.matmul_backward(_host64(dy), _host64(x), np.zeros((N, K)), prec="f64")
+        _close(dw.cpu().numpy().astype(np.float64) - dw0, rdw, 2e-5)
+    m.close()
+
+
+@pytest.mark.parametrize("prec,B,T,NH,hs", [
+    (G.GPT2_BF16_MIXED, 2, 320, 2, 64),   # ragged against the 128-row blocks
+    (G.GPT2_BF16_MIXED, 1, 1024, 1, 64),  # the full sequence length
+    (G.GPT2_BF16_MIXED, 3, 64, 3, 64),
+    (G.GPT2_FP32, 2, 37, 3, 16),
+    (G.GPT2_FP32, 1, 130, 2, 64),
+])
+def test_attention_vs_oracle(prec, B, T, NH, hs):
+    C = NH * hs
+    bf = prec == G.GPT2_BF16_MIXED
+    tdt = torch.bfloat16 if bf else torch.float32
+    # a model whose B*NH*T covers the case (its buffers hold the row sums D)
+    cfg = G.make_config(1, C, NH, 1024, 64, 64, B, ((T + 63) // 64) * 64, prec)
+    m = G.Model(cfg, 1)
+    print(f"attention prec={prec} B={B} T={T} NH={NH} hs={hs}", flush=True)
+    rng = np.random.default_rng(2)
+    qkv = _dev(rng.standard_normal((B, T, 3 * C)), tdt)
+    out = torch.zeros((B, T, C), dtype=tdt, device="cuda")
+    lse = torch.zeros((B, NH, T), dtype=torch.float32, device="cuda")
+    G.gpt2_test_attention_fwd(m.h, out.data_ptr(), lse.data_ptr(), qkv.data_ptr(), B, T, C, NH)
+    dout = _dev(rng.standard_normal((B, T, C)), tdt)
+    dqkv = torch.zeros_like(qkv)
+    G.gpt2_test_attention_bwd(m.h, dqkv.data_ptr(), dout.data_ptr(), qkv.data_ptr(), out.data_ptr(),
+                              lse.data_ptr(), B, T, C, NH)
+    torch.cuda.synchronize()
+    q64 = _host64(qkv)
+    ref, pre, att = O.attention_forward(q64, NH, prec="f64")
+    tol = 2e-2 if bf else 1e-5
+    _close(_host64(out), ref, tol)
+    # lse: log of the softmax normaliser of the scaled scores over t2 <= t
+    from scipy.special import logsumexp
+    mask = np.tril(np.ones((T, T), bool))
+    ref_lse = logsumexp(np.where(mask, pre, -np.inf), axis=-1)
+    np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, rtol=0, atol=2e-2 if bf else 1e-5)
+    # backward against the oracle run on the GPU's own forward output
+    rdq = O.attention_backward(_host64(dout), q64, att, NH, prec="f64")
+    _close(_host64(dqkv), rdq, 3e-2 if bf else 1e-5)
+    m.close()

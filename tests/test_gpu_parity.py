@@ -4,7 +4,7 @@ Configurations (GPT-2 training-step workloads):
   * tiny fp32: L=2, C=64, NH=4, T=32, B=4, V=512, uniform tokens; 10 AdamW
     steps (lr 1e-4, betas 0.9/0.999, eps 1e-8, wd 0);
   * GPT-2 124M fp32 at B=4, T=64, Zipf(1.1) tokens, same optimizer;
-  * GPT-2 124M bf16 mixed at B=4, T=64 with lr 6e-4, wd 0.1, clip 1.0;
+  * GPT-2 124M bf16 mixed at B=4, T=64 with lr 1e-4, wd 0.1, clip 1.0;
   * GPT-2 124M bf16 mixed at the benchmark size B=16, T=1024 (sampled rows).
 Tolerances: fp32 mode 1e-4 relative (loss; per tensor relative L2 and max
 error relative to the tensor's max); bf16 mode 1e-2 absolute on the loss
@@ -48,8 +48,26 @@ def rel_max(a, b):
     return float(np.max(np.abs(a.astype(np.float64) - b)) / (np.max(np.abs(b)) + 1e-30))
 
 
-def compare_tensors(got, ref, cfg, tol, check_max=True, what="grads"):
+def kbias_mask(cfg):
+    """Mask over qkvb selecting the key-bias slice.  A bias on k adds
+    q.b_k to every score of a query row, which the softmax cancels, so its
+    gradient is zero in exact arithmetic; AdamW then turns rounding noise
+    into +-lr steps, which no two summation orders share."""
+    msk = np.zeros((cfg["L"], 3, cfg["C"]), bool)
+    msk[:, 1, :] = True
+    return msk.reshape(-1)
+
+
+def compare_tensors(got, ref, cfg, tol, check_max=True, what="grads", kbias_steps=None):
     g, r = split(got, cfg), split(ref.astype(np.float64), cfg)
+    if kbias_steps is not None:
+        # parameters after AdamW steps: the key-bias slice only has to stay
+        # within AdamW's per-step bound on both sides; the rest is compared
+        lr, steps = kbias_steps
+        k = kbias_mask(cfg)
+        assert np.max(np.abs(g["qkvb"][k])) <= 3 * lr * steps
+        assert np.max(np.abs(r["qkvb"][k])) <= 3 * lr * steps
+        g["qkvb"], r["qkvb"] = g["qkvb"][~k], r["qkvb"][~k]
     gnorm = np.linalg.norm(ref)
     bad = []
     for name in O.PARAM_NAMES:
@@ -112,7 +130,7 @@ def gpu_run(cfg, B, T, seed, dist, steps, lr, wd, clip, prec):
     return out
 
 
-def check_fp32(o, g, cfg):
+def check_fp32(o, g, cfg, lr, steps):
     assert np.array_equal(g["init"], o["init"].astype(np.float32)), "init differs"
     assert rel_l2(g["logits"], o["logits"]) <= 1e-4 and rel_max(g["logits"], o["logits"]) <= 1e-4
     for a, b in zip(g["losses"], o["losses"]):
@@ -121,14 +139,29 @@ def check_fp32(o, g, cfg):
     compare_tensors(g["grads0"], o["grads0"], cfg, 1e-4, what="grads")
     for a, b in zip(g["norms"], o["norms"]):
         assert abs(a - b) <= 1e-4 * b
-    compare_tensors(g["params"], o["params"], cfg, 1e-4, check_max=False, what="params after 10 steps")
+    compare_tensors(g["params"], o["params"], cfg, 1e-4, check_max=False, what="params after 10 steps",
+                    kbias_steps=(lr, steps))
+
+
+def test_oracle_key_bias_gradient_vanishes():
+    """Pins the reading behind kbias_mask: in fp64 the key-bias gradient is
+    zero to rounding while the query- and value-bias gradients are not."""
+    m = O.Model(ocfg(TINY), 4, 32, "f64")
+    m.init(1337)
+    x, y = synth.batch(1337, 0, 4, 32, TINY["V"], "uniform")
+    m.forward(x, y)
+    m.zero_grad()
+    m.backward()
+    g = m.G()["qkvb"].reshape(TINY["L"], 3, TINY["C"])
+    assert np.abs(g[:, 1]).max() < 1e-15 * np.abs(g[:, 2]).max()
+    assert np.abs(g[:, 0]).max() > 1e-8
 
 
 def test_tiny_fp32_parity():
     kw = dict(seed=1337, dist="uniform", steps=10, lr=1e-4, wd=0.0, clip=0.0)
     o = oracle_run(TINY, 4, 32, **kw)
     g = gpu_run(TINY, 4, 32, prec=G.GPT2_FP32, **kw)
-    check_fp32(o, g, TINY)
+    check_fp32(o, g, TINY, kw["lr"], kw["steps"])
     assert all(b < a for a, b in zip(g["losses"], g["losses"][1:])), g["losses"]
 
 
@@ -137,12 +170,15 @@ def test_124m_fp32_parity():
     kw = dict(seed=1337, dist="zipf", steps=10, lr=1e-4, wd=0.0, clip=0.0)
     o = oracle_run(M124, 4, 64, **kw)
     g = gpu_run(M124, 4, 64, prec=G.GPT2_FP32, **kw)
-    check_fp32(o, g, M124)
+    check_fp32(o, g, M124, kw["lr"], kw["steps"])
 
 
 @pytest.mark.timeout(900)
 def test_124m_bf16_parity():
-    kw = dict(seed=1337, dist="zipf", steps=10, lr=6e-4, wd=0.1, clip=1.0)
+    # lr 1e-4 with weight decay and clipping on: at lr 6e-4 the fp32
+    # oracle's own trajectory on a repeated batch turns unstable (its loss
+    # rises at step 6), and any rounding difference then grows without bound
+    kw = dict(seed=1337, dist="zipf", steps=10, lr=1e-4, wd=0.1, clip=1.0)
     o = oracle_run(M124, 4, 64, **kw)
     g = gpu_run(M124, 4, 64, prec=G.GPT2_BF16_MIXED, **kw)
     assert np.array_equal(g["init"], o["init"].astype(np.float32)), "init differs"
@@ -153,7 +189,8 @@ def test_124m_bf16_parity():
     compare_tensors(g["grads0"], o["grads0"], M124, 5e-2, check_max=False, what="grads")
     for a, b in zip(g["norms"], o["norms"]):
         assert abs(a - b) <= 5e-2 * b
-    compare_tensors(g["params"], o["params"], M124, 5e-2, check_max=False, what="params after 10 steps")
+    compare_tensors(g["params"], o["params"], M124, 5e-2, check_max=False, what="params after 10 steps",
+                    kbias_steps=(kw["lr"], kw["steps"]))
 
 
 @pytest.mark.timeout(900)

@@ -14,7 +14,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(BUILD, "libgpt2mi.so")
-SOURCES = ["model.hip", "kernels_misc.hip", "gemm_simt.hip", "gemm_mfma.hip", "attention.hip"]
+SOURCES = ["model.hip", "kernels_misc.hip", "gemm_simt.hip", "gemm_mfma.hip", "attention.hip",
+           "attention_mfma.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-Wall", "-Wno-unused-function",

@@ -10,6 +10,8 @@
 // Two LDS buffers: the global loads of k-step t+1 are in flight while the
 // matrix cores work on step t.  Block ids are remapped so that the tiles
 // one XCD (one L2) runs are neighbours sharing operand panels.
+#include <algorithm>
+
 #include "kernels.h"
 
 namespace {
@@ -90,8 +92,14 @@ template <int R> struct MNTile {
     }
 };
 
+constexpr int EPI_PARTIAL = 100;  // split-K partial tile into g.ws[split][M][N]
+
 template <int EPI>
 DEVI void epi_store(const GemmArgs& g, int m, int n, float acc) {
+    if (EPI == EPI_PARTIAL) {
+        g.ws[((int64_t)blockIdx.y * g.M + m) * g.N + n] = acc;
+        return;
+    }
     int64_t o = (int64_t)m * g.ldo + n;
     if (EPI == EPI_ACC_F32) {
         float* out = (float*)g.out;
@@ -107,7 +115,7 @@ DEVI void epi_store(const GemmArgs& g, int m, int n, float acc) {
 }
 
 template <int BM, int BN, bool AK, bool BKC, int EPI>
-__global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs g) {
+__global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs g, int kchunk) {
     constexpr int TM = BM / 2, TN = BN / 2, FM = TM / 32, FN = TN / 32;
     __shared__ __attribute__((aligned(16))) uint16_t lds[2][(BM + BN) * LDK];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -153,13 +161,15 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs g) {
         else tb.store(buf + BM * LDK, tid, 128);
     };
 
-    const int nk = g.K / BK;
-    load(0);
+    // this workgroup's share of the reduction (the whole of it unless split)
+    const int kbeg = blockIdx.y * kchunk;
+    const int nk = (min(g.K, kbeg + kchunk) - kbeg) / BK;
+    load(kbeg);
     store(lds[0]);
     __syncthreads();
     for (int kt = 0; kt < nk; kt++) {
         const int cur = kt & 1;
-        if (kt + 1 < nk) load((kt + 1) * BK);
+        if (kt + 1 < nk) load(kbeg + (kt + 1) * BK);
         const uint16_t* As = lds[cur];
         const uint16_t* Bs = lds[cur] + BM * LDK;
 #pragma unroll
@@ -197,10 +207,41 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs g) {
 }
 
 template <int BM, int BN, bool AK, bool BKC, int EPI>
-hipError_t launch(const GemmArgs& g, hipStream_t s) {
-    unsigned blocks = cdiv(g.M, BM) * cdiv(g.N, BN);
-    gemm_mfma_kernel<BM, BN, AK, BKC, EPI><<<blocks, 256, 0, s>>>(g);
+hipError_t launch(const GemmArgs& g, hipStream_t s, int splits = 1, int kchunk = 0) {
+    dim3 grid(cdiv(g.M, BM) * cdiv(g.N, BN), splits);
+    gemm_mfma_kernel<BM, BN, AK, BKC, EPI><<<grid, 256, 0, s>>>(g, kchunk ? kchunk : g.K);
     return hipGetLastError();
+}
+
+// Split of the reduction for the weight-gradient products, whose outputs are
+// small (C x C .. 4C x C) next to their reduction over all B*T tokens:
+// enough splits to give ~512 workgroups, each at least 4 k-steps long.
+void splitk_plan(int M, int N, int K, int* splits, int* kchunk) {
+    int tiles = (int)(cdiv(M, 128) * cdiv(N, 128));
+    int S = (512 + tiles - 1) / tiles;
+    int smax = K / 256;
+    if (S > smax) S = smax;
+    if (S < 1) S = 1;
+    int kc = (int)cdiv(K / BK, S) * BK;
+    *kchunk = kc;
+    *splits = (K + kc - 1) / kc;
+}
+
+__global__ void splitk_reduce_kernel(float* out, int64_t ldo, const float* ws, int S, int M, int N) {
+    const int64_t n4 = (int64_t)M * N / 4;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x) {
+        int64_t e = i * 4;
+        int m = (int)(e / N), n = (int)(e % N);
+        float4 acc = reinterpret_cast<const float4*>(ws)[i];
+        for (int sp = 1; sp < S; sp++) {
+            float4 v = reinterpret_cast<const float4*>(ws + (int64_t)sp * M * N)[i];
+            acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+        }
+        float4* o = reinterpret_cast<float4*>(out + (int64_t)m * ldo + n);
+        float4 cur = *o;
+        cur.x += acc.x; cur.y += acc.y; cur.z += acc.z; cur.w += acc.w;
+        *o = cur;
+    }
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
@@ -227,6 +268,24 @@ hipError_t gemm_mfma_bf16(const GemmArgs& g, hipStream_t s) {
             default: return hipErrorInvalidValue;
         }
     }
-    if (!g.a_kcontig && !g.b_kcontig && g.epi == EPI_ACC_F32) return launch<128, 128, false, false, EPI_ACC_F32>(g, s);
+    if (!g.a_kcontig && !g.b_kcontig && g.epi == EPI_ACC_F32) {
+        int S, kc;
+        splitk_plan(g.M, g.N, g.K, &S, &kc);
+        if (S > 1 && g.ws && (size_t)S * g.M * g.N * 4 <= g.ws_bytes && g.N % 4 == 0 && g.ldo % 4 == 0) {
+            hipError_t e = launch<128, 128, false, false, EPI_PARTIAL>(g, s, S, kc);
+            if (e != hipSuccess) return e;
+            int64_t n4 = (int64_t)g.M * g.N / 4;
+            unsigned blocks = (unsigned)std::min<int64_t>((n4 + 255) / 256, 4096);
+            splitk_reduce_kernel<<<blocks, 256, 0, s>>>((float*)g.out, g.ldo, g.ws, S, g.M, g.N);
+            return hipGetLastError();
+        }
+        return launch<128, 128, false, false, EPI_ACC_F32>(g, s);
+    }
     return hipErrorInvalidValue;
+}
+
+size_t gemm_splitk_ws_bytes(int M, int N, int K) {
+    int S, kc;
+    splitk_plan(M, N, K, &S, &kc);
+    return S > 1 ? (size_t)S * M * N * 4 : 0;
 }

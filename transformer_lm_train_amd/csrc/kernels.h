@@ -15,6 +15,10 @@ enum GemmEpi {
     EPI_GELU_BWD = 4,    // out = acc * GELU'(aux[m][n])
     EPI_ACC_F32 = 5,     // out (fp32) += acc
 };
+// EPI_ACC_F32 may split the reduction over several workgroups: each writes
+// its fp32 partial tile to ws[split][M][N] and a second kernel adds the
+// partials, in split order, into out.  gemm_splitk_ws_bytes gives the
+// workspace that split choice needs.
 
 struct GemmArgs {
     int M, N, K;
@@ -31,7 +35,10 @@ struct GemmArgs {
     const void* aux;     // activation dtype, leading dim ldo
     void* out2;          // activation dtype, leading dim ldo
     int epi;
+    float* ws;           // split-K workspace (EPI_ACC_F32), may be NULL
+    size_t ws_bytes;
 };
+size_t gemm_splitk_ws_bytes(int M, int N, int K);
 
 // fp32-accumulating SIMT kernel for any shapes (activation dtype T).
 template <typename T> hipError_t gemm_simt(const GemmArgs& g, hipStream_t s);
@@ -83,3 +90,7 @@ hipError_t attention_fwd(T* out, float* lse, const T* qkv, int B, int T_, int C,
 template <typename T>
 hipError_t attention_bwd(T* dqkv, const T* dout, const T* qkv, const T* out, const float* lse, float* dbuf,
                          int B, int T_, int C, int NH, hipStream_t s);
+// head size 64, bf16, MFMA flash kernels (dbuf receives D = rowsum(dO o O))
+hipError_t flash_attention_fwd(bf16* out, float* lse, const bf16* qkv, int B, int T_, int C, int NH, hipStream_t s);
+hipError_t flash_attention_bwd(bf16* dqkv, const bf16* dout, const bf16* qkv, const bf16* out, const float* lse,
+                               float* dbuf, int B, int T_, int C, int NH, hipStream_t s);

@@ -166,7 +166,7 @@ hipError_t layernorm_fwd(T* out, float* mean, float* rstd, const T* x, const flo
 // dw/db sums in registers, reduces its 4 waves in LDS and writes one
 // partial row; a second kernel sums the G partials in block order.
 // ============================================================================
-constexpr int LN_BWD_G = 256;
+constexpr int LN_BWD_G = 1024;
 
 template <typename T, int MAXV>
 __global__ __launch_bounds__(256) void layernorm_bwd_kernel(T* dres, const T* dy, const T* x, const float* w,
@@ -248,16 +248,29 @@ __global__ __launch_bounds__(256) void layernorm_bwd_kernel(T* dres, const T* dy
     }
 }
 
-// out0[c] += sum_g partial[g][c]; out1[c] += sum_g partial[G+g][c] (if out1)
-__global__ void sum_partials_kernel(float* out0, float* out1, const float* partial, int G, int C) {
-    int c = blockIdx.x * blockDim.x + threadIdx.x;
-    if (c >= C) return;
+// out0[c] += sum_g partial[g][c]; out1[c] += sum_g partial[G+g][c] (if out1).
+// Block: 64 columns x 16 row lanes, each lane summing every 16th partial
+// row, then a fixed-order combine of the 16 lanes.
+__global__ __launch_bounds__(1024) void sum_partials_kernel(float* out0, float* out1, const float* partial, int G,
+                                                            int C) {
+    __shared__ float red[2][16][64];
+    const int cx = threadIdx.x & 63, ry = threadIdx.x >> 6;
+    const int c = blockIdx.x * 64 + cx;
     float s0 = 0.f, s1 = 0.f;
-    for (int g = 0; g < G; g++) s0 += partial[(int64_t)g * C + c];
-    out0[c] += s0;
-    if (out1) {
-        for (int g = 0; g < G; g++) s1 += partial[((int64_t)G + g) * C + c];
-        out1[c] += s1;
+    if (c < C) {
+        for (int g = ry; g < G; g += 16) {
+            s0 += partial[(int64_t)g * C + c];
+            if (out1) s1 += partial[((int64_t)G + g) * C + c];
+        }
+    }
+    red[0][ry][cx] = s0;
+    red[1][ry][cx] = s1;
+    __syncthreads();
+    if (ry == 0 && c < C) {
+        float a = 0.f, b = 0.f;
+        for (int i = 0; i < 16; i++) { a += red[0][i][cx]; b += red[1][i][cx]; }
+        out0[c] += a;
+        if (out1) out1[c] += b;
     }
 }
 
@@ -278,7 +291,7 @@ hipError_t layernorm_bwd(T* dres, const T* dy, const T* x, const float* w, const
         layernorm_bwd_kernel<T, 4><<<G, 256, lds, s>>>(dres, dy, x, w, mean, rstd, partial, N, C, ow);
     else
         layernorm_bwd_kernel<T, 8><<<G, 256, lds, s>>>(dres, dy, x, w, mean, rstd, partial, N, C, ow);
-    sum_partials_kernel<<<cdiv(C, 256), 256, 0, s>>>(dw, db, partial, G, C);
+    sum_partials_kernel<<<cdiv(C, 64), 1024, 0, s>>>(dw, db, partial, G, C);
     return LAUNCH_CHECK();
 }
 
@@ -324,7 +337,7 @@ hipError_t colsum_accum(float* dbias, const T* dy, int M, int N, float* partial,
     int G = COLSUM_G;
     dim3 grid(cdiv(N / VN, 64), G);
     colsum_kernel<T><<<grid, 256, 0, s>>>(partial, dy, M, N);
-    sum_partials_kernel<<<cdiv(N, 256), 256, 0, s>>>(dbias, nullptr, partial, G, N);
+    sum_partials_kernel<<<cdiv(N, 64), 1024, 0, s>>>(dbias, nullptr, partial, G, N);
     return LAUNCH_CHECK();
 }
 

@@ -12,6 +12,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <string>
 #include <thread>
 #include <type_traits>
@@ -66,7 +67,8 @@ struct Layout {
     size_t params, grads, m, v, shadow;
     size_t encoded, ln1, qkv, atty, res2, ln2, fch, fchg, res3, lnf, logits;
     size_t ln1_mean, ln1_rstd, ln2_mean, ln2_rstd, lnf_mean, lnf_rstd, lse, losses;
-    size_t dres, dbig, dmid, attD, partial, norm_partial, scalars, err, tokens, targets;
+    size_t dres, dbig, dmid, attD, partial, norm_partial, scalars, err, tokens, targets, splitk;
+    size_t splitk_bytes;
     size_t total;
 };
 
@@ -134,12 +136,19 @@ Layout make_layout(const gpt2_config& c) {
     L.dbig = add(A * BT * 4 * C);
     L.dmid = add(A * BT * C);
     L.attD = add(4 * BT * c.num_heads);
-    L.partial = add(4 * 512 * C);
+    L.partial = add(4 * 2048 * C);
     L.norm_partial = add(4 * 1024);
     L.scalars = add(64);
     L.err = add(64);
     L.tokens = add(4 * BT);
     L.targets = add(4 * BT);
+    L.splitk_bytes = 0;
+    if (c.precision == GPT2_BF16_MIXED) {
+        const int dims[5][2] = {{3 * (int)C, (int)C}, {(int)C, (int)C}, {4 * (int)C, (int)C}, {(int)C, 4 * (int)C},
+                                {c.padded_vocab_size, (int)C}};
+        for (auto& d : dims) L.splitk_bytes = std::max(L.splitk_bytes, gemm_splitk_ws_bytes(d[0], d[1], (int)BT));
+    }
+    L.splitk = add(L.splitk_bytes);
     L.total = add(0);
     return L;
 }
@@ -284,7 +293,22 @@ hipError_t lin_dw(gpt2_t* Mo, float* dW, const T* dY, const T* X, int M, int N, 
     g.a = dY; g.lda = N; g.a_kcontig = false;
     g.b = X; g.ldb = K; g.b_kcontig = false;
     g.out = dW; g.ldo = K; g.epi = EPI_ACC_F32;
+    g.ws = Mo->P<float>(Mo->L.splitk);
+    g.ws_bytes = Mo->L.splitk_bytes;
     return gemm<T>(Mo, g);
+}
+
+template <typename T>
+hipError_t attn_fwd(T* out, float* lse, const T* qkv, int B, int T_, int C, int NH, hipStream_t s) {
+    if constexpr (std::is_same<T, bf16>::value) return flash_attention_fwd(out, lse, qkv, B, T_, C, NH, s);
+    else return attention_fwd<float>(out, lse, qkv, B, T_, C, NH, s);
+}
+template <typename T>
+hipError_t attn_bwd(T* dqkv, const T* dout, const T* qkv, const T* out, const float* lse, float* dbuf, int B, int T_,
+                    int C, int NH, hipStream_t s) {
+    if constexpr (std::is_same<T, bf16>::value)
+        return flash_attention_bwd(dqkv, dout, qkv, out, lse, dbuf, B, T_, C, NH, s);
+    else return attention_bwd<float>(dqkv, dout, qkv, out, lse, dbuf, B, T_, C, NH, s);
 }
 
 template <typename T> struct Acts {
@@ -341,7 +365,7 @@ template <typename T> int forward_impl(gpt2_t* M, bool with_targets) {
                                               p + po[P_LN1W] + lC, p + po[P_LN1B] + lC, BT, C, s));
         RUN("gemm_fwd", lin_fwd<T>(M, qkv, ln1, w + po[P_QKVW] + lC * 3 * C, p + po[P_QKVB] + lC * 3, BT, 3 * C, C,
                                    EPI_BIAS));
-        RUN("attention_fwd", attention_fwd<T>(atty, a.lse + (size_t)l * BT * NH, qkv, B, T_, C, NH, s));
+        RUN("attention_fwd", attn_fwd<T>(atty, a.lse + (size_t)l * BT * NH, qkv, B, T_, C, NH, s));
         RUN("gemm_fwd", lin_fwd<T>(M, res2, atty, w + po[P_ATTPROJW] + lC * C, p + po[P_ATTPROJB] + lC, BT, C, C,
                                    EPI_BIAS_RESID, x));
         RUN("layernorm_fwd", layernorm_fwd<T>(ln2, a.ln2m + (size_t)l * BT, a.ln2r + (size_t)l * BT, res2,
@@ -408,7 +432,7 @@ template <typename T> int backward_impl(gpt2_t* M) {
         RUN("gemm_dw", lin_dw<T>(M, g + po[P_ATTPROJW] + lC * C, a.dres, atty, BT, C, C));
         RUN("colsum", colsum_accum<T>(g + po[P_ATTPROJB] + lC, a.dres, BT, C, part, s));
         // attention: dmid (d atty) -> dbig (d qkv)
-        RUN("attention_bwd", attention_bwd<T>(a.dbig, a.dmid, qkv, atty, a.lse + (size_t)l * BT * NH, attD, B, T_,
+        RUN("attention_bwd", attn_bwd<T>(a.dbig, a.dmid, qkv, atty, a.lse + (size_t)l * BT * NH, attD, B, T_,
                                               C, NH, s));
         // qkv: qkv = ln1 Wqkv^T + b
         RUN("gemm_dx", lin_dx<T>(M, a.dmid, a.dbig, w + po[P_QKVW] + lC * 3 * C, BT, 3 * C, C, EPI_STORE));
@@ -737,6 +761,32 @@ int gpt2_test_gemm_tn(gpt2_t* M, float* dw, const void* dy, const void* x, int m
         RUN("gemm_test", lin_dw<bf16>(M, dw, (const bf16*)dy, (const bf16*)x, m, n, k));
     else
         RUN("gemm_test", lin_dw<float>(M, dw, (const float*)dy, (const float*)x, m, n, k));
+    return GPT2_OK;
+}
+
+int gpt2_test_attention_fwd(gpt2_t* M, void* out, float* lse, const void* qkv, int B, int T_, int C, int NH) {
+    if (!M || !out || !lse || !qkv || B <= 0 || T_ <= 0 || NH <= 0 || C % NH) return fail(GPT2_EINVAL, "bad argument");
+    if (M->bf16mode())
+        RUN("attention_test", attn_fwd<bf16>((bf16*)out, lse, (const bf16*)qkv, B, T_, C, NH, M->stream));
+    else
+        RUN("attention_test", attn_fwd<float>((float*)out, lse, (const float*)qkv, B, T_, C, NH, M->stream));
+    return GPT2_OK;
+}
+
+int gpt2_test_attention_bwd(gpt2_t* M, void* dqkv, const void* dout, const void* qkv, const void* out,
+                            const float* lse, int B, int T_, int C, int NH) {
+    if (!M || !dqkv || !dout || !qkv || !out || !lse || B <= 0 || T_ <= 0 || NH <= 0 || C % NH)
+        return fail(GPT2_EINVAL, "bad argument");
+    const gpt2_config& c = M->cfg;
+    if ((int64_t)B * NH * T_ > (int64_t)c.batch_size * c.num_heads * c.seq_len)
+        return fail(GPT2_EINVAL, "B*NH*T exceeds the model's attention row buffer");
+    float* D = M->P<float>(M->L.attD);
+    if (M->bf16mode())
+        RUN("attention_test", attn_bwd<bf16>((bf16*)dqkv, (const bf16*)dout, (const bf16*)qkv, (const bf16*)out, lse,
+                                             D, B, T_, C, NH, M->stream));
+    else
+        RUN("attention_test", attn_bwd<float>((float*)dqkv, (const float*)dout, (const float*)qkv,
+                                              (const float*)out, lse, D, B, T_, C, NH, M->stream));
     return GPT2_OK;
 }
 

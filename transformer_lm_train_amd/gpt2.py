@@ -83,6 +83,8 @@ def lib():
         "gpt2_test_gemm_nt": ([vp, vp, vp, vp, vp, i32, i32, i32], ctypes.c_int),
         "gpt2_test_gemm_nn": ([vp, vp, vp, vp, i32, i32, i32], ctypes.c_int),
         "gpt2_test_gemm_tn": ([vp, vp, vp, vp, i32, i32, i32], ctypes.c_int),
+        "gpt2_test_attention_fwd": ([vp, vp, vp, vp, i32, i32, i32, i32], ctypes.c_int),
+        "gpt2_test_attention_bwd": ([vp, vp, vp, vp, vp, vp, i32, i32, i32, i32], ctypes.c_int),
     }
     for name, (args, res) in sigs.items():
         fn = getattr(L, name)
@@ -234,6 +236,14 @@ def gpt2_test_gemm_nn(h, dx_ptr, dy_ptr, w_ptr, M, N, K):
 
 def gpt2_test_gemm_tn(h, dw_ptr, dy_ptr, x_ptr, M, N, K):
     _check(lib().gpt2_test_gemm_tn(h, dw_ptr, dy_ptr, x_ptr, M, N, K))
+
+
+def gpt2_test_attention_fwd(h, out_ptr, lse_ptr, qkv_ptr, B, T, C, NH):
+    _check(lib().gpt2_test_attention_fwd(h, out_ptr, lse_ptr, qkv_ptr, B, T, C, NH))
+
+
+def gpt2_test_attention_bwd(h, dqkv_ptr, dout_ptr, qkv_ptr, out_ptr, lse_ptr, B, T, C, NH):
+    _check(lib().gpt2_test_attention_bwd(h, dqkv_ptr, dout_ptr, qkv_ptr, out_ptr, lse_ptr, B, T, C, NH))
 
 
 # ---- convenience wrapper: torch owns the device buffer and the stream -------

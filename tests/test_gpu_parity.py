@@ -4,7 +4,7 @@ Configurations (GPT-2 training-step workloads):
   * tiny fp32: L=2, C=64, NH=4, T=32, B=4, V=512, uniform tokens; 10 AdamW
     steps (lr 1e-4, betas 0.9/0.999, eps 1e-8, wd 0);
   * GPT-2 124M fp32 at B=4, T=64, Zipf(1.1) tokens, same optimizer;
-  * GPT-2 124M bf16 mixed at B=4, T=64 with lr 1e-4, wd 0.1, clip 1.0;
+  * GPT-2 124M bf16 mixed at B=4, T=64 with lr 3e-5, wd 0.1, clip 1.0;
   * GPT-2 124M bf16 mixed at the benchmark size B=16, T=1024 (sampled rows).
 Tolerances: fp32 mode 1e-4 relative (loss; per tensor relative L2 and max
 error relative to the tensor's max); bf16 mode 1e-2 absolute on the loss
@@ -175,10 +175,12 @@ def test_124m_fp32_parity():
 
 @pytest.mark.timeout(900)
 def test_124m_bf16_parity():
-    # lr 1e-4 with weight decay and clipping on: at lr 6e-4 the fp32
-    # oracle's own trajectory on a repeated batch turns unstable (its loss
-    # rises at step 6), and any rounding difference then grows without bound
-    kw = dict(seed=1337, dist="zipf", steps=10, lr=1e-4, wd=0.1, clip=1.0)
+    # lr 3e-5 with weight decay and clipping on.  On a repeated batch AdamW's
+    # first steps move every parameter by ~lr; from lr ~1e-4 up the fp32
+    # oracle's own loss oscillates (8.44 -> 8.85 at step 3 with lr 1e-4, a
+    # rise at step 6 with lr 6e-4) and bf16 rounding differences grow step by
+    # step.  At 3e-5 the oracle's loss falls monotonically 10.99 -> 4.83.
+    kw = dict(seed=1337, dist="zipf", steps=10, lr=3e-5, wd=0.1, clip=1.0)
     o = oracle_run(M124, 4, 64, **kw)
     g = gpu_run(M124, 4, 64, prec=G.GPT2_BF16_MIXED, **kw)
     assert np.array_equal(g["init"], o["init"].astype(np.float32)), "init differs"

@@ -55,7 +55,10 @@ template <int R> struct MNTile {
         for (int p = 0; p < PER; p++) {
             int b = t + p * 256;
             if (b < R) {
-                int kb = b / (R / 8), rb = b % (R / 8);
+                // k-block fastest: the 8 lanes of a group then write 8 different
+                // 16-byte columns of one LDS row group (distinct banks), while
+                // each row of 8 lanes still reads 128 contiguous bytes
+                int kb = b & 7, rb = b >> 3;
                 int r = r0 + rb * 8;
 #pragma unroll
                 for (int j = 0; j < 8; j++) {
@@ -73,7 +76,7 @@ template <int R> struct MNTile {
         for (int p = 0; p < PER; p++) {
             int b = t + p * 256;
             if (b < R) {
-                int kb = b / (R / 8), rb = b % (R / 8);
+                int kb = b & 7, rb = b >> 3;
                 const uint32_t* w[8];
 #pragma unroll
                 for (int j = 0; j < 8; j++) w[j] = reinterpret_cast<const uint32_t*>(&v[p][j]);
@@ -114,12 +117,14 @@ DEVI void epi_store(const GemmArgs& g, int m, int n, float acc) {
     if (EPI == EPI_BIAS_GELU) ((bf16*)g.out2)[o] = (bf16)gelu_f(y);
 }
 
-template <int BM, int BN, bool AK, bool BKC, int EPI>
+template <int BM, int BN, int WAVES_M, bool AK, bool BKC, int EPI>
 __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs g, int kchunk) {
-    constexpr int TM = BM / 2, TN = BN / 2, FM = TM / 32, FN = TN / 32;
+    constexpr int WAVES_N = 4 / WAVES_M;
+    constexpr int TM = BM / WAVES_M, TN = BN / WAVES_N, FM = TM / 32, FN = TN / 32;
+    static_assert(FM >= 1 && FN >= 1 && TM % 32 == 0 && TN % 32 == 0, "wave tile");
     __shared__ __attribute__((aligned(16))) uint16_t lds[2][(BM + BN) * LDK];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
 
     // block -> tile: XCD-contiguous ranges, then groups of 8 tile-rows
     const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
@@ -206,10 +211,10 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs g, int kchunk) 
             }
 }
 
-template <int BM, int BN, bool AK, bool BKC, int EPI>
+template <int BM, int BN, int WAVES_M, bool AK, bool BKC, int EPI>
 hipError_t launch(const GemmArgs& g, hipStream_t s, int splits = 1, int kchunk = 0) {
     dim3 grid(cdiv(g.M, BM) * cdiv(g.N, BN), splits);
-    gemm_mfma_kernel<BM, BN, AK, BKC, EPI><<<grid, 256, 0, s>>>(g, kchunk ? kchunk : g.K);
+    gemm_mfma_kernel<BM, BN, WAVES_M, AK, BKC, EPI><<<grid, 256, 0, s>>>(g, kchunk ? kchunk : g.K);
     return hipGetLastError();
 }
 
@@ -254,17 +259,17 @@ hipError_t gemm_mfma_bf16(const GemmArgs& g, hipStream_t s) {
     if (!aligned16(g.a) || !aligned16(g.b)) return hipErrorInvalidValue;
     if (g.a_kcontig && g.b_kcontig) {
         switch (g.epi) {
-            case EPI_STORE: return launch<128, 128, true, true, EPI_STORE>(g, s);
-            case EPI_BIAS: return launch<128, 128, true, true, EPI_BIAS>(g, s);
-            case EPI_BIAS_RESID: return launch<128, 128, true, true, EPI_BIAS_RESID>(g, s);
-            case EPI_BIAS_GELU: return launch<128, 128, true, true, EPI_BIAS_GELU>(g, s);
+            case EPI_STORE: return launch<128, 128, 2, true, true, EPI_STORE>(g, s);
+            case EPI_BIAS: return launch<128, 128, 2, true, true, EPI_BIAS>(g, s);
+            case EPI_BIAS_RESID: return launch<128, 128, 2, true, true, EPI_BIAS_RESID>(g, s);
+            case EPI_BIAS_GELU: return launch<128, 128, 2, true, true, EPI_BIAS_GELU>(g, s);
             default: return hipErrorInvalidValue;
         }
     }
     if (g.a_kcontig && !g.b_kcontig) {
         switch (g.epi) {
-            case EPI_STORE: return launch<128, 128, true, false, EPI_STORE>(g, s);
-            case EPI_GELU_BWD: return launch<128, 128, true, false, EPI_GELU_BWD>(g, s);
+            case EPI_STORE: return launch<128, 128, 2, true, false, EPI_STORE>(g, s);
+            case EPI_GELU_BWD: return launch<128, 128, 2, true, false, EPI_GELU_BWD>(g, s);
             default: return hipErrorInvalidValue;
         }
     }
@@ -272,14 +277,14 @@ hipError_t gemm_mfma_bf16(const GemmArgs& g, hipStream_t s) {
         int S, kc;
         splitk_plan(g.M, g.N, g.K, &S, &kc);
         if (S > 1 && g.ws && (size_t)S * g.M * g.N * 4 <= g.ws_bytes && g.N % 4 == 0 && g.ldo % 4 == 0) {
-            hipError_t e = launch<128, 128, false, false, EPI_PARTIAL>(g, s, S, kc);
+            hipError_t e = launch<128, 128, 2, false, false, EPI_PARTIAL>(g, s, S, kc);
             if (e != hipSuccess) return e;
             int64_t n4 = (int64_t)g.M * g.N / 4;
             unsigned blocks = (unsigned)std::min<int64_t>((n4 + 255) / 256, 4096);
             splitk_reduce_kernel<<<blocks, 256, 0, s>>>((float*)g.out, g.ldo, g.ws, S, g.M, g.N);
             return hipGetLastError();
         }
-        return launch<128, 128, false, false, EPI_ACC_F32>(g, s);
+        return launch<128, 128, 2, false, false, EPI_ACC_F32>(g, s);
     }
     return hipErrorInvalidValue;
 }

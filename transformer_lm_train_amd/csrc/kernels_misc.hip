@@ -299,7 +299,7 @@ hipError_t layernorm_bwd(T* dres, const T* dy, const T* x, const float* w, const
 // bias gradient: dbias[n] += sum_m dy[m][n]
 // Block: 64 column chunks x 4 row lanes; grid.y = G row groups.
 // ============================================================================
-constexpr int COLSUM_G = 64;
+constexpr int COLSUM_G = 256;
 
 template <typename T>
 __global__ __launch_bounds__(256) void colsum_kernel(float* partial, const T* dy, int M, int N) {
@@ -350,78 +350,105 @@ hipError_t colsum_accum(float* dbias, const T* dy, int M, int N, float* partial,
 // ============================================================================
 constexpr int CE_THREADS = 1024;
 
-template <typename T>
+// block-wide max / sum over CE_THREADS threads (fixed combine order)
+DEVI float block_max(float x, float* sh) {
+    x = wave_max(x);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = x;
+    __syncthreads();
+    float r = sh[0];
+    for (int i = 1; i < CE_THREADS / 64; i++) r = fmaxf(r, sh[i]);
+    return r;
+}
+DEVI float block_sum(float x, float* sh) {
+    x = wave_sum(x);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = x;
+    __syncthreads();
+    float r = 0.f;
+    for (int i = 0; i < CE_THREADS / 64; i++) r += sh[i];
+    return r;
+}
+
+// One block per row.  The row is read once into registers (MAXC 16-byte
+// chunks per thread), reduced, and written back once as dlogits.
+template <typename T, int MAXC>
 __global__ __launch_bounds__(CE_THREADS) void softmax_ce_kernel(T* logits, float* losses, const int* targets,
                                                                 int V, int Vp, float dscale, int* err) {
     constexpr int VN = Vec16<T>::N;
-    __shared__ float sm[CE_THREADS / 64], ss[CE_THREADS / 64];
-    __shared__ float s_max, s_sum;
-    int row = blockIdx.x;
+    __shared__ float sh[CE_THREADS / 64];
+    __shared__ float s_zt;
+    const int row = blockIdx.x;
     T* z = logits + (int64_t)row * Vp;
-    int chunks = Vp / VN;
-    float m = -INFINITY, s = 0.f;
-    for (int ch = threadIdx.x; ch < chunks; ch += CE_THREADS) {
-        Vec16<T> q = ld16(z + ch * VN);
-#pragma unroll
-        for (int j = 0; j < VN; j++) {
-            int v = ch * VN + j;
-            if (v < V) {
-                float x = to_f32(q.v[j]);
-                if (x > m) {
-                    s = s * __expf(m - x) + 1.f;
-                    m = x;
-                } else {
-                    s += __expf(x - m);
-                }
-            }
-        }
-    }
-    // wavefront then block combine of (m, s)
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-        float m2 = __shfl_xor(m, o, 64), s2 = __shfl_xor(s, o, 64);
-        float mn = fmaxf(m, m2);
-        s = (m == -INFINITY ? 0.f : s * __expf(m - mn)) + (m2 == -INFINITY ? 0.f : s2 * __expf(m2 - mn));
-        m = mn;
-    }
-    int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    if (lane == 0) { sm[wv] = m; ss[wv] = s; }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        float M = -INFINITY;
-        for (int i = 0; i < CE_THREADS / 64; i++) M = fmaxf(M, sm[i]);
-        float S = 0.f;
-        for (int i = 0; i < CE_THREADS / 64; i++) S += sm[i] == -INFINITY ? 0.f : ss[i] * __expf(sm[i] - M);
-        s_max = M;
-        s_sum = S;
-    }
-    __syncthreads();
-    float M = s_max, invS = 1.f / s_sum;
+    const int chunks = Vp / VN;
     int tgt = targets[row];
     if (tgt < 0 || tgt >= V) {
         if (threadIdx.x == 0) atomicOr(err, 2);
         tgt = 0;
     }
-    if (threadIdx.x == 0) losses[row] = M + logf(s_sum) - to_f32(z[tgt]);
-    __syncthreads();  // the target logit is read before any thread overwrites it
-    for (int ch = threadIdx.x; ch < chunks; ch += CE_THREADS) {
-        Vec16<T> q = ld16(z + ch * VN);
+    Vec16<T> q[MAXC];
+    float mx = -INFINITY;
 #pragma unroll
-        for (int j = 0; j < VN; j++) {
-            int v = ch * VN + j;
-            float d = 0.f;
-            if (v < V) d = (__expf(to_f32(q.v[j]) - M) * invS - (v == tgt ? 1.f : 0.f)) * dscale;
-            q.v[j] = from_f32<T>(d);
+    for (int i = 0; i < MAXC; i++) {
+        const int ch = threadIdx.x + i * CE_THREADS;
+        if (ch < chunks) {
+            q[i] = ld16(z + ch * VN);
+#pragma unroll
+            for (int j = 0; j < VN; j++) {
+                const int v = ch * VN + j;
+                const float x = to_f32(q[i].v[j]);
+                if (v < V) mx = fmaxf(mx, x);
+                if (v == tgt) s_zt = x;
+            }
         }
-        st16(z + ch * VN, q);
+    }
+    const float M = block_max(mx, sh);
+    float se = 0.f;
+#pragma unroll
+    for (int i = 0; i < MAXC; i++) {
+        const int ch = threadIdx.x + i * CE_THREADS;
+        if (ch < chunks) {
+#pragma unroll
+            for (int j = 0; j < VN; j++)
+                if (ch * VN + j < V) se += __expf(to_f32(q[i].v[j]) - M);
+        }
+    }
+    const float S = block_sum(se, sh);  // its barriers also publish s_zt
+    if (threadIdx.x == 0) losses[row] = M + logf(S) - s_zt;
+    const float invS = 1.f / S;
+#pragma unroll
+    for (int i = 0; i < MAXC; i++) {
+        const int ch = threadIdx.x + i * CE_THREADS;
+        if (ch < chunks) {
+            Vec16<T> o;
+#pragma unroll
+            for (int j = 0; j < VN; j++) {
+                const int v = ch * VN + j;
+                float d = 0.f;
+                if (v < V) d = (__expf(to_f32(q[i].v[j]) - M) * invS - (v == tgt ? 1.f : 0.f)) * dscale;
+                o.v[j] = from_f32<T>(d);
+            }
+            st16(z + ch * VN, o);
+        }
     }
 }
 
 template <typename T>
 hipError_t softmax_ce(T* logits, float* losses, const int* targets, int BT, int V, int Vp, float dscale, int* err,
                       hipStream_t s) {
-    if (Vp % Vec16<T>::N) return hipErrorInvalidValue;
-    softmax_ce_kernel<T><<<BT, CE_THREADS, 0, s>>>(logits, losses, targets, V, Vp, dscale, err);
+    constexpr int VN = Vec16<T>::N;
+    if (Vp % VN) return hipErrorInvalidValue;
+    const int per = (int)cdiv(Vp / VN, CE_THREADS);
+    if (per <= 2)
+        softmax_ce_kernel<T, 2><<<BT, CE_THREADS, 0, s>>>(logits, losses, targets, V, Vp, dscale, err);
+    else if (per <= 4)
+        softmax_ce_kernel<T, 4><<<BT, CE_THREADS, 0, s>>>(logits, losses, targets, V, Vp, dscale, err);
+    else if (per <= 8)
+        softmax_ce_kernel<T, 8><<<BT, CE_THREADS, 0, s>>>(logits, losses, targets, V, Vp, dscale, err);
+    else if (per <= 16)
+        softmax_ce_kernel<T, 16><<<BT, CE_THREADS, 0, s>>>(logits, losses, targets, V, Vp, dscale, err);
+    else
+        return hipErrorInvalidValue;  // rows above 16K chunks (Vp > 131072 bf16) are not supported
     return LAUNCH_CHECK();
 }
 
@@ -498,41 +525,53 @@ DEVI void adamw_one(float& p, float g, float& m, float& v, float lr, float b1, f
 __global__ __launch_bounds__(256) void adamw_kernel(float* p, const float* g, float* m, float* v, bf16* shadow,
                                                     size_t n, float lr, float b1, float b2, float eps, float wd,
                                                     float c1, float c2, const float* norm_scale) {
-    float sc = norm_scale ? norm_scale[1] : 1.f;
-    size_t n4 = n / 4;
-    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (size_t)gridDim.x * 256) {
-        float4 pp = reinterpret_cast<float4*>(p)[i];
-        float4 gg = reinterpret_cast<const float4*>(g)[i];
-        float4 mm = reinterpret_cast<float4*>(m)[i];
-        float4 vv = reinterpret_cast<float4*>(v)[i];
-        adamw_one(pp.x, gg.x * sc, mm.x, vv.x, lr, b1, b2, eps, wd, c1, c2);
-        adamw_one(pp.y, gg.y * sc, mm.y, vv.y, lr, b1, b2, eps, wd, c1, c2);
-        adamw_one(pp.z, gg.z * sc, mm.z, vv.z, lr, b1, b2, eps, wd, c1, c2);
-        adamw_one(pp.w, gg.w * sc, mm.w, vv.w, lr, b1, b2, eps, wd, c1, c2);
-        reinterpret_cast<float4*>(p)[i] = pp;
-        reinterpret_cast<float4*>(m)[i] = mm;
-        reinterpret_cast<float4*>(v)[i] = vv;
-        if (shadow) {
-            typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
-            bf16x4 o = {(bf16)pp.x, (bf16)pp.y, (bf16)pp.z, (bf16)pp.w};
-            reinterpret_cast<bf16x4*>(shadow)[i] = o;
+    typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    const float sc = norm_scale ? norm_scale[1] : 1.f;
+    const size_t n4 = n / 4;
+    // each thread updates two float4 groups, with all eight loads issued first
+    const size_t i0 = ((size_t)blockIdx.x * 256 + threadIdx.x) * 2;
+    float4 pp[2], gg[2], mm[2], vv[2];
+#pragma unroll
+    for (int u = 0; u < 2; u++) {
+        const size_t i = i0 + u;
+        if (i < n4) {
+            pp[u] = reinterpret_cast<const float4*>(p)[i];
+            gg[u] = reinterpret_cast<const float4*>(g)[i];
+            mm[u] = reinterpret_cast<const float4*>(m)[i];
+            vv[u] = reinterpret_cast<const float4*>(v)[i];
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < 2; u++) {
+        const size_t i = i0 + u;
+        if (i < n4) {
+            adamw_one(pp[u].x, gg[u].x * sc, mm[u].x, vv[u].x, lr, b1, b2, eps, wd, c1, c2);
+            adamw_one(pp[u].y, gg[u].y * sc, mm[u].y, vv[u].y, lr, b1, b2, eps, wd, c1, c2);
+            adamw_one(pp[u].z, gg[u].z * sc, mm[u].z, vv[u].z, lr, b1, b2, eps, wd, c1, c2);
+            adamw_one(pp[u].w, gg[u].w * sc, mm[u].w, vv[u].w, lr, b1, b2, eps, wd, c1, c2);
+            reinterpret_cast<float4*>(p)[i] = pp[u];
+            reinterpret_cast<float4*>(m)[i] = mm[u];
+            reinterpret_cast<float4*>(v)[i] = vv[u];
+            if (shadow) {
+                bf16x4 o = {(bf16)pp[u].x, (bf16)pp[u].y, (bf16)pp[u].z, (bf16)pp[u].w};
+                reinterpret_cast<bf16x4*>(shadow)[i] = o;
+            }
         }
     }
     if (blockIdx.x == 0 && threadIdx.x < (n & 3)) {
-        size_t i = n4 * 4 + threadIdx.x;
-        float pp = p[i], mm = m[i], vv = v[i];
-        adamw_one(pp, g[i] * sc, mm, vv, lr, b1, b2, eps, wd, c1, c2);
-        p[i] = pp;
-        m[i] = mm;
-        v[i] = vv;
-        if (shadow) shadow[i] = (bf16)pp;
+        const size_t i = n4 * 4 + threadIdx.x;
+        float a = p[i], b = m[i], c = v[i];
+        adamw_one(a, g[i] * sc, b, c, lr, b1, b2, eps, wd, c1, c2);
+        p[i] = a;
+        m[i] = b;
+        v[i] = c;
+        if (shadow) shadow[i] = (bf16)a;
     }
 }
 
 hipError_t adamw(float* p, const float* g, float* m, float* v, bf16* shadow, size_t n, float lr, float b1, float b2,
                  float eps, float wd, float c1, float c2, const float* norm_scale, hipStream_t s) {
-    size_t blocks = cdiv(n / 4 + 1, 256);
-    if (blocks > 8192) blocks = 8192;
+    const size_t blocks = cdiv(n / 4, 512) + 1;
     adamw_kernel<<<(unsigned)blocks, 256, 0, s>>>(p, g, m, v, shadow, n, lr, b1, b2, eps, wd, c1, c2, norm_scale);
     return LAUNCH_CHECK();
 }

@@ -16,81 +16,68 @@
 
 namespace {
 
+// native 4 x u32 vector (SROA-friendly, unlike the union-based uint4)
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 constexpr int BK = 64;
 constexpr int LDK = BK + 8;  // LDS row pitch in elements (144 bytes)
 
-// rows [r0, r0+R) x k [k0, k0+64) of X with X(r,k) = X[r*ld + k]
-template <int R> struct KTile {
-    static constexpr int PER = R * (BK / 8) / 256;
-    uint4 v[PER];
-    DEVI void load(const bf16* X, int64_t ld, int r0, int rows, int k0, int tid) {
+// ---- operand tiles: rows [r0, r0+R) x k [k0, k0+64) of X ------------------
+// Rows past the end re-read the last row (always in bounds).  They only feed
+// accumulator rows/columns past M or N, which the epilogue never stores, so
+// they need no zeroing and the loads carry no branches.
+
+// k-contiguous X (X(r,k) = X[r*ld + k]): R*8 16-byte chunks, R/32 per thread
+template <int R> struct KT {
+    static constexpr int N = R / 32;
+    static DEVI void load(u32x4 (&v)[N], const bf16* X, int64_t ld, int r0, int rows, int k0, int tid, int) {
 #pragma unroll
-        for (int i = 0; i < PER; i++) {
-            int c = tid + i * 256;
-            int row = c >> 3, kc = c & 7;
-            if (r0 + row < rows)
-                v[i] = *reinterpret_cast<const uint4*>(X + (int64_t)(r0 + row) * ld + k0 + kc * 8);
-            else
-                v[i] = make_uint4(0, 0, 0, 0);
+        for (int i = 0; i < N; i++) {
+            const int c = tid + i * 256;
+            const int rr = min(r0 + (c >> 3), rows - 1);
+            v[i] = *reinterpret_cast<const u32x4*>(X + (int64_t)rr * ld + k0 + (c & 7) * 8);
         }
     }
-    DEVI void store(uint16_t* lds, int tid) {
+    static DEVI void store(const u32x4 (&v)[N], uint16_t* lds, int tid, int) {
 #pragma unroll
-        for (int i = 0; i < PER; i++) {
-            int c = tid + i * 256;
-            int row = c >> 3, kc = c & 7;
-            *reinterpret_cast<uint4*>(lds + row * LDK + kc * 8) = v[i];
+        for (int i = 0; i < N; i++) {
+            const int c = tid + i * 256;
+            *reinterpret_cast<u32x4*>(lds + (c >> 3) * LDK + (c & 7) * 8) = v[i];
         }
     }
 };
 
-// same tile of X with X(r,k) = X[k*ld + r]: R/8 x 8 blocks of 8x8, one
-// block per thread (threads (tid+off)%256 < R work), transposed in registers.
-template <int R> struct MNTile {
-    static constexpr int PER = (R + 255) / 256;
-    uint4 v[PER][8];
-    DEVI void load(const bf16* X, int64_t ld, int r0, int rows, int k0, int tid, int off) {
-        int t = (tid + off) & 255;
+// mn-contiguous X (X(r,k) = X[k*ld + r]): 8 x R/8 blocks of 8x8, one block
+// per thread for threads (tid+off)%256 < R (R <= 256), transposed in
+// registers on the way into LDS.  The k-block index runs fastest, so the 8
+// lanes of a group write 8 different 16-byte columns of one LDS row group
+// (distinct banks) while every 8 lanes still read 128 contiguous bytes.
+template <int R> struct MNT {
+    static_assert(R <= 256, "one 8x8 block per thread");
+    static constexpr int N = 8;
+    static DEVI void load(u32x4 (&v)[N], const bf16* X, int64_t ld, int r0, int rows, int k0, int tid, int off) {
+        const int b = (tid + off) & 255;
+        if (b >= R) return;
+        const int kb = b & 7, rb = b >> 3;
+        const int rr = min(r0 + rb * 8, rows - 8);
 #pragma unroll
-        for (int p = 0; p < PER; p++) {
-            int b = t + p * 256;
-            if (b < R) {
-                // k-block fastest: the 8 lanes of a group then write 8 different
-                // 16-byte columns of one LDS row group (distinct banks), while
-                // each row of 8 lanes still reads 128 contiguous bytes
-                int kb = b & 7, rb = b >> 3;
-                int r = r0 + rb * 8;
-#pragma unroll
-                for (int j = 0; j < 8; j++) {
-                    if (r < rows)
-                        v[p][j] = *reinterpret_cast<const uint4*>(X + (int64_t)(k0 + kb * 8 + j) * ld + r);
-                    else
-                        v[p][j] = make_uint4(0, 0, 0, 0);
-                }
-            }
-        }
+        for (int j = 0; j < 8; j++) v[j] = *reinterpret_cast<const u32x4*>(X + (int64_t)(k0 + kb * 8 + j) * ld + rr);
     }
-    DEVI void store(uint16_t* lds, int tid, int off) {
-        int t = (tid + off) & 255;
+    static DEVI void store(const u32x4 (&v)[N], uint16_t* lds, int tid, int off) {
+        const int b = (tid + off) & 255;
+        if (b >= R) return;
+        const int kb = b & 7, rb = b >> 3;
 #pragma unroll
-        for (int p = 0; p < PER; p++) {
-            int b = t + p * 256;
-            if (b < R) {
-                int kb = b & 7, rb = b >> 3;
-                const uint32_t* w[8];
+        for (int i = 0; i < 8; i++) {
+            uint32_t o[4];
 #pragma unroll
-                for (int j = 0; j < 8; j++) w[j] = reinterpret_cast<const uint32_t*>(&v[p][j]);
-#pragma unroll
-                for (int i = 0; i < 8; i++) {
-                    uint32_t o[4];
-#pragma unroll
-                    for (int q = 0; q < 4; q++) {
-                        uint32_t lo = w[2 * q][i >> 1], hi = w[2 * q + 1][i >> 1];
-                        o[q] = (i & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-                    }
-                    *reinterpret_cast<uint4*>(lds + (rb * 8 + i) * LDK + kb * 8) = make_uint4(o[0], o[1], o[2], o[3]);
-                }
+            for (int q = 0; q < 4; q++) {
+                const uint32_t lo = (i & 2) ? (i & 4 ? v[2 * q].w : v[2 * q].y) : (i & 4 ? v[2 * q].z : v[2 * q].x);
+                const uint32_t hi = (i & 2) ? (i & 4 ? v[2 * q + 1].w : v[2 * q + 1].y)
+                                            : (i & 4 ? v[2 * q + 1].z : v[2 * q + 1].x);
+                o[q] = (i & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
             }
+            *reinterpret_cast<u32x4*>(lds + (rb * 8 + i) * LDK + kb * 8) = u32x4{o[0], o[1], o[2], o[3]};
         }
     }
 };
@@ -115,6 +102,39 @@ DEVI void epi_store(const GemmArgs& g, int m, int n, float acc) {
     if (EPI == EPI_GELU_BWD) y = acc * gelu_grad_f(to_f32(((const bf16*)g.aux)[o]));
     ((bf16*)g.out)[o] = (bf16)y;
     if (EPI == EPI_BIAS_GELU) ((bf16*)g.out2)[o] = (bf16)gelu_f(y);
+}
+
+// One k-step (64) of the wave's FM x FN block of 32x32 accumulators from an
+// LDS stage holding the A tile ([BM][LDK]) followed by the B tile.
+template <int BM, int FM, int FN, int TM, int TN>
+DEVI void mfma_tile(f32x16 (&acc)[FM][FN], const uint16_t* As, int wm, int wn, int lane) {
+    const uint16_t* Bs = As + BM * LDK;
+    // fragments double-buffered in registers (see mfma_swz)
+    bf16x8 a[2][FM], b[2][FN];
+    auto frag = [&](int ks, bf16x8 (&fa)[FM], bf16x8 (&fb)[FN]) {
+        const int koff = ks * 16 + (lane >> 5) * 8;
+#pragma unroll
+        for (int i = 0; i < FM; i++)
+            fa[i] = *reinterpret_cast<const bf16x8*>(As + (wm * TM + i * 32 + (lane & 31)) * LDK + koff);
+#pragma unroll
+        for (int j = 0; j < FN; j++)
+            fb[j] = *reinterpret_cast<const bf16x8*>(Bs + (wn * TN + j * 32 + (lane & 31)) * LDK + koff);
+    };
+    frag(0, a[0], b[0]);
+    __builtin_amdgcn_sched_group_barrier(0x100, FM + FN, 0);
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ks++) {
+        if (ks + 1 < BK / 16) frag(ks + 1, a[(ks + 1) & 1], b[(ks + 1) & 1]);
+#pragma unroll
+        for (int i = 0; i < FM; i++)
+#pragma unroll
+            for (int j = 0; j < FN; j++)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks & 1][i], b[ks & 1][j], acc[i][j], 0, 0, 0);
+        // keep that order through scheduling: the next sub-step's LDS reads
+        // (mask 0x100) issue ahead of this sub-step's MFMAs (mask 0x008)
+        if (ks + 1 < BK / 16) __builtin_amdgcn_sched_group_barrier(0x100, FM + FN, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, FM * FN, 0);
+    }
 }
 
 template <int BM, int BN, int WAVES_M, bool AK, bool BKC, int EPI>
@@ -150,52 +170,50 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs g, int kchunk) 
 #pragma unroll
             for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
 
-    typename std::conditional<AK, KTile<BM>, MNTile<BM>>::type ta;
-    typename std::conditional<BKC, KTile<BN>, MNTile<BN>>::type tb;
-
-    auto load = [&](int k0) {
-        if constexpr (AK) ta.load(A, g.lda, m0, g.M, k0, tid);
-        else ta.load(A, g.lda, m0, g.M, k0, tid, 0);
-        if constexpr (BKC) tb.load(B, g.ldb, n0, g.N, k0, tid);
-        else tb.load(B, g.ldb, n0, g.N, k0, tid, 128);
-    };
-    auto store = [&](uint16_t* buf) {
-        if constexpr (AK) ta.store(buf, tid);
-        else ta.store(buf, tid, 0);
-        if constexpr (BKC) tb.store(buf + BM * LDK, tid);
-        else tb.store(buf + BM * LDK, tid, 128);
-    };
-
-    // this workgroup's share of the reduction (the whole of it unless split)
-    const int kbeg = blockIdx.y * kchunk;
+    typedef typename std::conditional<AK, KT<BM>, MNT<BM>>::type TA;
+    typedef typename std::conditional<BKC, KT<BN>, MNT<BN>>::type TB;
+    // two register stages: the loads of k-step t+2 are issued while step t
+    // computes, and step t+1 (loaded one compute phase earlier) goes to LDS
+    u32x4 ra0[TA::N], ra1[TA::N], rb0[TB::N], rb1[TB::N];
+    const int kbeg = blockIdx.y * kchunk;  // this workgroup's share of the reduction
     const int nk = (min(g.K, kbeg + kchunk) - kbeg) / BK;
-    load(kbeg);
-    store(lds[0]);
+#define GEMM_LOAD(ra, rb, k0)                                   \
+    do {                                                        \
+        TA::load(ra, A, g.lda, m0, g.M, (k0), tid, 0);          \
+        TB::load(rb, B, g.ldb, n0, g.N, (k0), tid, 128);        \
+    } while (0)
+#define GEMM_STORE(ra, rb, buf)                                 \
+    do {                                                        \
+        TA::store(ra, (buf), tid, 0);                           \
+        TB::store(rb, (buf) + BM * LDK, tid, 128);              \
+    } while (0)
+
+    // Loads are issued unconditionally (the k-step index clamped to the last
+    // one; a redundant tail load is never consumed): a load under a branch
+    // makes the wait-count insertion assume the worst at the join and wait
+    // for every outstanding load, which would undo the prefetch.
+    const int klast = kbeg + (nk - 1) * BK;
+    GEMM_LOAD(ra0, rb0, kbeg);
+    GEMM_LOAD(ra1, rb1, min(kbeg + BK, klast));
+    GEMM_STORE(ra0, rb0, lds[0]);
     __syncthreads();
-    for (int kt = 0; kt < nk; kt++) {
-        const int cur = kt & 1;
-        if (kt + 1 < nk) load(kbeg + (kt + 1) * BK);
-        const uint16_t* As = lds[cur];
-        const uint16_t* Bs = lds[cur] + BM * LDK;
-#pragma unroll
-        for (int ks = 0; ks < BK / 16; ks++) {
-            bf16x8 a[FM], b[FN];
-            const int koff = ks * 16 + (lane >> 5) * 8;
-#pragma unroll
-            for (int i = 0; i < FM; i++)
-                a[i] = *reinterpret_cast<const bf16x8*>(As + (wm * TM + i * 32 + (lane & 31)) * LDK + koff);
-#pragma unroll
-            for (int j = 0; j < FN; j++)
-                b[j] = *reinterpret_cast<const bf16x8*>(Bs + (wn * TN + j * 32 + (lane & 31)) * LDK + koff);
-#pragma unroll
-            for (int i = 0; i < FM; i++)
-#pragma unroll
-                for (int j = 0; j < FN; j++)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-        }
-        if (kt + 1 < nk) store(lds[cur ^ 1]);
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+        // even step: compute buffer 0, refill register stage 0 with step kt+2
+        GEMM_LOAD(ra0, rb0, min(kbeg + (kt + 2) * BK, klast));
+        mfma_tile<BM, FM, FN, TM, TN>(acc, lds[0], wm, wn, lane);
+        GEMM_STORE(ra1, rb1, lds[1]);
+        __syncthreads();
+        // odd step: compute buffer 1, refill register stage 1 with step kt+3;
+        // buffer 0 then receives step kt+2 (unused when kt+2 == nk)
+        GEMM_LOAD(ra1, rb1, min(kbeg + (kt + 3) * BK, klast));
+        mfma_tile<BM, FM, FN, TM, TN>(acc, lds[1], wm, wn, lane);
+        GEMM_STORE(ra0, rb0, lds[0]);
         __syncthreads();
     }
+    if (kt < nk) mfma_tile<BM, FM, FN, TM, TN>(acc, lds[0], wm, wn, lane);  // odd step count: last one in buffer 0
+#undef GEMM_LOAD
+#undef GEMM_STORE
 
     // accumulator (i,j) register r of lane l holds row 8*(r/4) + 4*(l/32) + r%4,
     // column l%32 of the 32x32 block
@@ -209,6 +227,228 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs g, int kchunk) 
                 int n = n0 + wn * TN + j * 32 + (lane & 31);
                 if (m < g.M && n < g.N) epi_store<EPI>(g, m, n, acc[i][j][r]);
             }
+}
+
+// ============================================================================
+// Direct-to-LDS variant.  A k-contiguous operand tile goes from global memory
+// straight into LDS with global_load_lds_dwordx4 (no staging registers, no
+// ds_write): one instruction fills 1 KB of LDS, lane l's 16 bytes at
+// base + 16*l.  The LDS tile is unpadded ([row][64] bf16, 128-byte rows) and
+// XOR-swizzled: the 16-byte k-chunk c of row r sits in slot c ^ (r & 7), so
+// the 32 rows an MFMA fragment read touches spread over all banks.  An
+// mn-contiguous operand still goes through registers (8x8 transposes) into
+// the same swizzled layout.  NS stages, each its own __shared__ array (so
+// alias analysis keeps the reads of one stage independent of the loads in
+// flight into another); each k-step waits only for its own stage's loads
+// (explicit vmcnt) and synchronises with a raw barrier, so the loads of the
+// next NS-1 stages stay in flight across it.
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+DEVI int swz(int row, int chunk) { return row * BK + ((chunk ^ (row & 7)) << 3); }
+
+// s_waitcnt immediate (gfx9 encoding): vmcnt <= N, lgkmcnt = 0 (this wave's
+// LDS writes done before a barrier publishes them), expcnt unconstrained
+template <int N> constexpr int vmcnt_imm() { return (N & 15) | ((N >> 4) << 14) | (7 << 4); }
+
+// rows [r0, r0+R) x k [k0, k0+64) of a k-contiguous X, R/32 loads per thread
+template <int R>
+DEVI void dma_tile(uint16_t* tile, const bf16* X, int64_t ld, int r0, int rows, int k0, int wave, int lane) {
+    constexpr int NI = R / 32;
+    const int r_in = lane >> 3;                   // row within the 8-row, 1 KB block
+    const int c = (lane & 7) ^ r_in;              // global chunk that lands in this lane's slot
+#pragma unroll
+    for (int i = 0; i < NI; i++) {
+        const int blk = wave * NI + i;
+        const int rr = min(r0 + blk * 8 + r_in, rows - 1);  // past-the-end rows: clamped (never stored)
+        __builtin_amdgcn_global_load_lds((glb_void_t*)(X + (int64_t)rr * ld + k0 + c * 8),
+                                         (lds_void_t*)(tile + blk * 512), 16, 0, 0);
+    }
+}
+
+// mn-contiguous X through registers: 8x8 blocks, block b = (tid+off)%256 < R
+template <int R> struct MNS {
+    static_assert(R <= 256, "one block per thread");
+    static DEVI void load(u32x4 (&v)[8], const bf16* X, int64_t ld, int r0, int rows, int k0, int tid, int off) {
+        const int b = (tid + off) & 255;
+        if (b >= R) return;
+        const int kb = b & 7, rb = b >> 3;
+        const int rr = min(r0 + rb * 8, rows - 8);
+#pragma unroll
+        for (int j = 0; j < 8; j++) v[j] = *reinterpret_cast<const u32x4*>(X + (int64_t)(k0 + kb * 8 + j) * ld + rr);
+    }
+    static DEVI void store(const u32x4 (&v)[8], uint16_t* tile, int tid, int off) {
+        const int b = (tid + off) & 255;
+        if (b >= R) return;
+        const int kb = b & 7, rb = b >> 3;
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            uint32_t o[4];
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                const uint32_t lo = (i & 2) ? (i & 4 ? v[2 * q].w : v[2 * q].y) : (i & 4 ? v[2 * q].z : v[2 * q].x);
+                const uint32_t hi = (i & 2) ? (i & 4 ? v[2 * q + 1].w : v[2 * q + 1].y)
+                                            : (i & 4 ? v[2 * q + 1].z : v[2 * q + 1].x);
+                o[q] = (i & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+            }
+            *reinterpret_cast<u32x4*>(tile + swz(rb * 8 + i, kb)) = u32x4{o[0], o[1], o[2], o[3]};
+        }
+    }
+};
+
+template <int FM, int FN, int TM, int TN>
+DEVI void mfma_swz(f32x16 (&acc)[FM][FN], const uint16_t* As, const uint16_t* Bs, int wm, int wn, int lane) {
+    // fragments double-buffered in registers: the LDS reads of sub-step ks+1
+    // are in flight while the MFMAs of sub-step ks run
+    bf16x8 a[2][FM], b[2][FN];
+    auto frag = [&](int ks, bf16x8 (&fa)[FM], bf16x8 (&fb)[FN]) {
+        const int c = ks * 2 + (lane >> 5);
+#pragma unroll
+        for (int i = 0; i < FM; i++)
+            fa[i] = *reinterpret_cast<const bf16x8*>(As + swz(wm * TM + i * 32 + (lane & 31), c));
+#pragma unroll
+        for (int j = 0; j < FN; j++)
+            fb[j] = *reinterpret_cast<const bf16x8*>(Bs + swz(wn * TN + j * 32 + (lane & 31), c));
+    };
+    frag(0, a[0], b[0]);
+    __builtin_amdgcn_sched_group_barrier(0x100, FM + FN, 0);
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ks++) {
+        if (ks + 1 < BK / 16) frag(ks + 1, a[(ks + 1) & 1], b[(ks + 1) & 1]);
+#pragma unroll
+        for (int i = 0; i < FM; i++)
+#pragma unroll
+            for (int j = 0; j < FN; j++)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks & 1][i], b[ks & 1][j], acc[i][j], 0, 0, 0);
+        // keep that order through scheduling: the next sub-step's LDS reads
+        // (mask 0x100) issue ahead of this sub-step's MFMAs (mask 0x008)
+        if (ks + 1 < BK / 16) __builtin_amdgcn_sched_group_barrier(0x100, FM + FN, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, FM * FN, 0);
+    }
+}
+
+// A is k-contiguous (direct loads); B k-contiguous (direct) or mn-contiguous
+// (registers).
+template <int BM, int BN, int WAVES_M, int NS, bool BKC, int EPI>
+__global__ __launch_bounds__(256) void gemm_dlds_kernel(GemmArgs g, int kchunk) {
+    constexpr int WAVES_N = 4 / WAVES_M;
+    constexpr int TM = BM / WAVES_M, TN = BN / WAVES_N, FM = TM / 32, FN = TN / 32;
+    static_assert(NS >= 2 && NS <= 4, "stages");
+    __shared__ __attribute__((aligned(1024))) uint16_t sa0[BM * BK], sa1[BM * BK], sa2[NS > 2 ? BM * BK : 8],
+        sa3[NS > 3 ? BM * BK : 8];
+    __shared__ __attribute__((aligned(1024))) uint16_t sb0[BN * BK], sb1[BN * BK], sb2[NS > 2 ? BN * BK : 8],
+        sb3[NS > 3 ? BN * BK : 8];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+
+    const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
+    int bid = blockIdx.x;
+    const int total = gridDim.x;
+    if ((total & 7) == 0) bid = (bid & 7) * (total >> 3) + (bid >> 3);
+    constexpr int GM = 8;
+    const int group = bid / (GM * tiles_n);
+    const int first_m = group * GM;
+    const int gsz = min(tiles_m - first_m, GM);
+    const int in = bid % (GM * tiles_n);
+    const int m0 = (first_m + in % gsz) * BM;
+    const int n0 = (in / gsz) * BN;
+    const bf16* A = (const bf16*)g.a;
+    const bf16* B = (const bf16*)g.b;
+
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; i++)
+#pragma unroll
+        for (int j = 0; j < FN; j++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
+
+    const int kbeg = blockIdx.y * kchunk;
+    const int nk = (min(g.K, kbeg + kchunk) - kbeg) / BK;
+    const int klast = kbeg + (nk - 1) * BK;
+    // direct loads per thread per stage (what the explicit waits count)
+    constexpr int LPS = BM / 32 + (BKC ? BN / 32 : 0);
+    u32x4 rb[8];  // mn-contiguous B staging (unused when B is k-contiguous)
+
+#define DLDS_DMA(SA, SB, K0)                                                      \
+    do {                                                                          \
+        dma_tile<BM>(SA, A, g.lda, m0, g.M, (K0), wave, lane);                    \
+        if constexpr (BKC) dma_tile<BN>(SB, B, g.ldb, n0, g.N, (K0), wave, lane); \
+    } while (0)
+#define DLDS_SYNC()                                                     \
+    do {                                                                \
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm<(NS - 2) * LPS>());        \
+        __builtin_amdgcn_s_barrier();                                   \
+        asm volatile("" ::: "memory");                                  \
+    } while (0)
+    // one k-step: stage (SA,SB) computed, next DMA into (NA,NB) for step KT+NS-1,
+    // the mn-contiguous B of step KT+1 staged through registers into (XA,XB)
+#define DLDS_STEP(SA, SB, NA, NB, XB, KT)                                                    \
+    do {                                                                                     \
+        DLDS_SYNC();                                                                         \
+        if constexpr (!BKC) MNS<BN>::load(rb, B, g.ldb, n0, g.N, min(kbeg + ((KT) + 1) * BK, klast), tid, 0); \
+        DLDS_DMA(NA, NB, min(kbeg + ((KT) + NS - 1) * BK, klast));                           \
+        mfma_swz<FM, FN, TM, TN>(acc, SA, SB, wm, wn, lane);                                  \
+        if constexpr (!BKC) MNS<BN>::store(rb, XB, tid, 0);                                   \
+    } while (0)
+
+    // prologue: stages 0..NS-2 in flight (and the mn-contiguous B of step 0)
+    DLDS_DMA(sa0, sb0, kbeg);
+    if constexpr (NS > 2) DLDS_DMA(sa1, sb1, min(kbeg + BK, klast));
+    if constexpr (NS > 3) DLDS_DMA(sa2, sb2, min(kbeg + 2 * BK, klast));
+    if constexpr (!BKC) {
+        MNS<BN>::load(rb, B, g.ldb, n0, g.N, kbeg, tid, 0);
+        MNS<BN>::store(rb, sb0, tid, 0);
+    }
+    int kt = 0;
+    if constexpr (NS == 2) {
+        for (; kt + 2 <= nk; kt += 2) {
+            DLDS_STEP(sa0, sb0, sa1, sb1, sb1, kt);
+            DLDS_STEP(sa1, sb1, sa0, sb0, sb0, kt + 1);
+        }
+        if (kt < nk) DLDS_STEP(sa0, sb0, sa1, sb1, sb1, kt);
+    } else if constexpr (NS == 3) {
+        for (; kt + 3 <= nk; kt += 3) {
+            DLDS_STEP(sa0, sb0, sa2, sb2, sb1, kt);
+            DLDS_STEP(sa1, sb1, sa0, sb0, sb2, kt + 1);
+            DLDS_STEP(sa2, sb2, sa1, sb1, sb0, kt + 2);
+        }
+        if (kt < nk) { DLDS_STEP(sa0, sb0, sa2, sb2, sb1, kt); kt++; }
+        if (kt < nk) DLDS_STEP(sa1, sb1, sa0, sb0, sb2, kt);
+    } else {
+        for (; kt + 4 <= nk; kt += 4) {
+            DLDS_STEP(sa0, sb0, sa3, sb3, sb1, kt);
+            DLDS_STEP(sa1, sb1, sa0, sb0, sb2, kt + 1);
+            DLDS_STEP(sa2, sb2, sa1, sb1, sb3, kt + 2);
+            DLDS_STEP(sa3, sb3, sa2, sb2, sb0, kt + 3);
+        }
+        if (kt < nk) { DLDS_STEP(sa0, sb0, sa3, sb3, sb1, kt); kt++; }
+        if (kt < nk) { DLDS_STEP(sa1, sb1, sa0, sb0, sb2, kt); kt++; }
+        if (kt < nk) DLDS_STEP(sa2, sb2, sa1, sb1, sb3, kt);
+    }
+#undef DLDS_DMA
+#undef DLDS_SYNC
+#undef DLDS_STEP
+    // drain: no load may still be writing LDS when the workgroup exits
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
+
+#pragma unroll
+    for (int i = 0; i < FM; i++)
+#pragma unroll
+        for (int j = 0; j < FN; j++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                const int m = m0 + wm * TM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+                const int n = n0 + wn * TN + j * 32 + (lane & 31);
+                if (m < g.M && n < g.N) epi_store<EPI>(g, m, n, acc[i][j][r]);
+            }
+}
+
+template <int BM, int BN, int WAVES_M, int NS, bool BKC, int EPI>
+hipError_t launch_dlds(const GemmArgs& g, hipStream_t s) {
+    dim3 grid(cdiv(g.M, BM) * cdiv(g.N, BN), 1);
+    gemm_dlds_kernel<BM, BN, WAVES_M, NS, BKC, EPI><<<grid, 256, 0, s>>>(g, g.K);
+    return hipGetLastError();
 }
 
 template <int BM, int BN, int WAVES_M, bool AK, bool BKC, int EPI>

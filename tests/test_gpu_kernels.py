@@ -31,8 +31,10 @@ def _host64(t):
 
 # bf16 needs the reduction dimension of each product to be a multiple of 64
 # (K for NT, N for NN, M for TN) and the others multiples of 8.
+# The shapes also reach every tile configuration the dispatcher picks:
+# forward N < 1536 / >= 1536 / >= 3072, ragged against 128 and 256 tiles.
 BF16_CASES = [(256, 384, 128), (136, 72, 64), (192, 320, 128), (128, 1000, 192), (64, 64, 64),
-              (392, 264, 320), (448, 192, 576)]
+              (392, 264, 320), (448, 192, 576), (136, 1600, 64), (264, 3080, 128), (320, 3072, 192)]
 F32_CASES = [(100, 70, 33), (64, 64, 64), (5, 130, 7), (257, 19, 100)]
 
 
@@ -84,7 +86,8 @@ def test_gemm_split_k_weight_gradient():
     cfg = G.make_config(1, 64, 1, 64, 64, 64, 64, 64, G.GPT2_BF16_MIXED)  # B*T = 4096 tokens
     m = G.Model(cfg, 1)
     rng = np.random.default_rng(1)
-    for (M, N, K) in [(2048, 192, 64), (4096, 64, 64), (1024, 128, 64)]:
+    # the last case has a wide enough output (256 tiles of 256x256) to take the unsplit path
+    for (M, N, K) in [(2048, 192, 64), (4096, 64, 64), (1024, 128, 64), (128, 4096, 4096)]:
         print(f"split-k gemm M={M} N={N} K={K}", flush=True)
         dy = _dev(rng.standard_normal((M, N)), torch.bfloat16)
         x = _dev(rng.standard_normal((M, K)), torch.bfloat16)

@@ -50,14 +50,19 @@ DEVI float wave_max(float x) {
     return x;
 }
 
+// tanh(x) = 1 - 2 / (exp(2x) + 1): the hardware exp and reciprocal, exact to
+// a few fp32 ulps, and saturating cleanly to +-1 (exp overflows to inf or
+// underflows to 0; the denominator never falls below 1)
+DEVI float tanh_fast(float x) { return 1.f - __fdividef(2.f, __expf(2.f * x) + 1.f); }
+
 // GELU, tanh approximation: 0.5 u (1 + tanh(k (u + 0.044715 u^3))), k = sqrt(2/pi)
 #define GELU_K 0.7978845608028654f
 DEVI float gelu_f(float u) {
-    float t = tanhf(GELU_K * (u + 0.044715f * u * u * u));
+    float t = tanh_fast(GELU_K * (u + 0.044715f * u * u * u));
     return 0.5f * u * (1.0f + t);
 }
 DEVI float gelu_grad_f(float u) {
-    float t = tanhf(GELU_K * (u + 0.044715f * u * u * u));
+    float t = tanh_fast(GELU_K * (u + 0.044715f * u * u * u));
     return 0.5f * (1.0f + t) + 0.5f * u * (1.0f - t * t) * GELU_K * (1.0f + 3.0f * 0.044715f * u * u);
 }
 

@@ -193,25 +193,40 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs g, int kchunk) 
     // makes the wait-count insertion assume the worst at the join and wait
     // for every outstanding load, which would undo the prefetch.
     const int klast = kbeg + (nk - 1) * BK;
-    GEMM_LOAD(ra0, rb0, kbeg);
-    GEMM_LOAD(ra1, rb1, min(kbeg + BK, klast));
-    GEMM_STORE(ra0, rb0, lds[0]);
-    __syncthreads();
     int kt = 0;
-    for (; kt + 1 < nk; kt += 2) {
-        // even step: compute buffer 0, refill register stage 0 with step kt+2
-        GEMM_LOAD(ra0, rb0, min(kbeg + (kt + 2) * BK, klast));
-        mfma_tile<BM, FM, FN, TM, TN>(acc, lds[0], wm, wn, lane);
-        GEMM_STORE(ra1, rb1, lds[1]);
-        __syncthreads();
-        // odd step: compute buffer 1, refill register stage 1 with step kt+3;
-        // buffer 0 then receives step kt+2 (unused when kt+2 == nk)
-        GEMM_LOAD(ra1, rb1, min(kbeg + (kt + 3) * BK, klast));
-        mfma_tile<BM, FM, FN, TM, TN>(acc, lds[1], wm, wn, lane);
+    if constexpr (!AK && !BKC) {
+        // both operands transposed through registers (16 x 16 bytes per thread):
+        // one register stage keeps the kernel at two waves per SIMD
+        GEMM_LOAD(ra0, rb0, kbeg);
         GEMM_STORE(ra0, rb0, lds[0]);
         __syncthreads();
+        for (; kt < nk; kt++) {
+            const int cur = kt & 1;
+            GEMM_LOAD(ra0, rb0, min(kbeg + (kt + 1) * BK, klast));
+            mfma_tile<BM, FM, FN, TM, TN>(acc, lds[cur], wm, wn, lane);
+            GEMM_STORE(ra0, rb0, lds[cur ^ 1]);
+            __syncthreads();
+        }
+    } else {
+        GEMM_LOAD(ra0, rb0, kbeg);
+        GEMM_LOAD(ra1, rb1, min(kbeg + BK, klast));
+        GEMM_STORE(ra0, rb0, lds[0]);
+        __syncthreads();
+        for (; kt + 1 < nk; kt += 2) {
+            // even step: compute buffer 0, refill register stage 0 with step kt+2
+            GEMM_LOAD(ra0, rb0, min(kbeg + (kt + 2) * BK, klast));
+            mfma_tile<BM, FM, FN, TM, TN>(acc, lds[0], wm, wn, lane);
+            GEMM_STORE(ra1, rb1, lds[1]);
+            __syncthreads();
+            // odd step: compute buffer 1, refill register stage 1 with step kt+3;
+            // buffer 0 then receives step kt+2 (unused when kt+2 == nk)
+            GEMM_LOAD(ra1, rb1, min(kbeg + (kt + 3) * BK, klast));
+            mfma_tile<BM, FM, FN, TM, TN>(acc, lds[1], wm, wn, lane);
+            GEMM_STORE(ra0, rb0, lds[0]);
+            __syncthreads();
+        }
+        if (kt < nk) mfma_tile<BM, FM, FN, TM, TN>(acc, lds[0], wm, wn, lane);  // odd step count: last one in buffer 0
     }
-    if (kt < nk) mfma_tile<BM, FM, FN, TM, TN>(acc, lds[0], wm, wn, lane);  // odd step count: last one in buffer 0
 #undef GEMM_LOAD
 #undef GEMM_STORE
 
@@ -451,6 +466,186 @@ hipError_t launch_dlds(const GemmArgs& g, hipStream_t s) {
     return hipGetLastError();
 }
 
+// ============================================================================
+// Large-tile variant: every operand goes global -> LDS by direct loads, in the
+// layout it has in memory.
+//  - k-contiguous operand: LDS [row][64], 16-byte chunk c of row r in slot
+//    c ^ (r & 7); fragment = one 16-byte LDS read.
+//  - mn-contiguous operand: LDS [k][R] (R = tile rows), 16-byte chunk c of
+//    k-row k in slot c ^ ((k & 3) << 1); fragment = two ds_read_b64_tr_b16.
+//    Within each 16-lane group that instruction hands lane i element (i % 4)
+//    of the 8-byte read of lane 4e + i/4 as its element e; so when lane j
+//    reads X[k0 + j/4][m0 + 4(j%4) .. +3], lane i receives X[k0..k0+3][m0+i],
+//    four consecutive k of one row: exactly the MFMA operand fragment.
+// NW waves (2 x NW/2), each owning a (BM/2) x (BN/(NW/2)) block of 32x32
+// accumulators; NS LDS stages with explicit vmcnt waits and raw barriers.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+DEVI int mn_swz(int k) { return (k & 3) << 1; }
+
+// tile rows [r0, r0+R) x k [k0, k0+64) of X into LDS; NIW 1 KB loads per wave
+template <int R, int NW, bool KCONTIG>
+DEVI void dma_any(uint16_t* tile, const bf16* X, int64_t ld, int r0, int rows, int k0, int wave, int lane) {
+    constexpr int NIW = R / (8 * NW);
+    static_assert(NIW >= 1 && NIW * 8 * NW == R, "tile rows vs waves");
+#pragma unroll
+    for (int i = 0; i < NIW; i++) {
+        const int blk = wave * NIW + i;  // 1 KB block of the tile
+        const bf16* g;
+        if constexpr (KCONTIG) {
+            const int r = blk * 8 + (lane >> 3);
+            const int c = (lane & 7) ^ (lane >> 3);  // = slot ^ (r & 7)
+            g = X + (int64_t)min(r0 + r, rows - 1) * ld + k0 + c * 8;
+        } else {
+            constexpr int CPR = R / 8;  // chunks per k-row
+            const int p = blk * 64 + lane;
+            const int k = p / CPR;
+            const int c = (p % CPR) ^ mn_swz(k);
+            g = X + (int64_t)(k0 + k) * ld + min(r0 + c * 8, rows - 8);
+        }
+        __builtin_amdgcn_global_load_lds((glb_void_t*)g, (lds_void_t*)(tile + blk * 512), 16, 0, 0);
+    }
+}
+
+// MFMA fragment: rows row0 + (lane & 31), k = kk + (lane >> 5) * 8 + 0..7
+template <int R, bool KCONTIG>
+DEVI bf16x8 frag_any(const uint16_t* tile, int row0, int kk, int lane) {
+    if constexpr (KCONTIG) {
+        const int r = row0 + (lane & 31);
+        const int c = (kk >> 3) + (lane >> 5);
+        return *reinterpret_cast<const bf16x8*>(tile + r * BK + ((c ^ (r & 7)) << 3));
+    } else {
+        const int j = lane & 15, g = lane >> 4;
+        const int m = row0 + 16 * (g & 1) + 4 * (j & 3);
+        const int k = kk + (g >> 1) * 8 + (j >> 2);
+        const int o0 = k * R + ((((m >> 3) ^ mn_swz(k)) << 3) | (m & 7));
+        const int o1 = (k + 4) * R + ((((m >> 3) ^ mn_swz(k + 4)) << 3) | (m & 7));
+        i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + o0));
+        i16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + o1));
+        i16x4 xy[2] = {x, y};
+        return *reinterpret_cast<bf16x8*>(xy);
+    }
+}
+
+template <int BM, int BN, int FM, int FN, int TM, int TN, bool AK, bool BKC>
+DEVI void mfma_any(f32x16 (&acc)[FM][FN], const uint16_t* As, const uint16_t* Bs, int wm, int wn, int lane) {
+    bf16x8 a[2][FM], b[2][FN];
+#pragma unroll
+    for (int i = 0; i < FM; i++) a[0][i] = frag_any<BM, AK>(As, wm * TM + i * 32, 0, lane);
+#pragma unroll
+    for (int j = 0; j < FN; j++) b[0][j] = frag_any<BN, BKC>(Bs, wn * TN + j * 32, 0, lane);
+    __builtin_amdgcn_sched_group_barrier(0x100, (FM + FN) * (AK && BKC ? 1 : 2), 0);
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ks++) {
+        if (ks + 1 < BK / 16) {
+#pragma unroll
+            for (int i = 0; i < FM; i++) a[(ks + 1) & 1][i] = frag_any<BM, AK>(As, wm * TM + i * 32, (ks + 1) * 16, lane);
+#pragma unroll
+            for (int j = 0; j < FN; j++) b[(ks + 1) & 1][j] = frag_any<BN, BKC>(Bs, wn * TN + j * 32, (ks + 1) * 16, lane);
+        }
+#pragma unroll
+        for (int i = 0; i < FM; i++)
+#pragma unroll
+            for (int j = 0; j < FN; j++)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks & 1][i], b[ks & 1][j], acc[i][j], 0, 0, 0);
+        if (ks + 1 < BK / 16) __builtin_amdgcn_sched_group_barrier(0x100, (FM + FN) * (AK && BKC ? 1 : 2), 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, FM * FN, 0);
+    }
+}
+
+template <int BM, int BN, int NW, int NS, bool AK, bool BKC, int EPI>
+__global__ __launch_bounds__(NW * 64) void gemm_big_kernel(GemmArgs g, int kchunk) {
+    constexpr int WAVES_M = 2, WAVES_N = NW / 2;
+    constexpr int TM = BM / WAVES_M, TN = BN / WAVES_N, FM = TM / 32, FN = TN / 32;
+    static_assert(NS >= 2 && NS <= 3, "stages");
+    __shared__ __attribute__((aligned(1024))) uint16_t sa0[BM * BK], sa1[BM * BK], sa2[NS > 2 ? BM * BK : 8];
+    __shared__ __attribute__((aligned(1024))) uint16_t sb0[BN * BK], sb1[BN * BK], sb2[NS > 2 ? BN * BK : 8];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+
+    const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
+    int bid = blockIdx.x;
+    const int total = gridDim.x;
+    if ((total & 7) == 0) bid = (bid & 7) * (total >> 3) + (bid >> 3);
+    constexpr int GM = 8;
+    const int group = bid / (GM * tiles_n);
+    const int first_m = group * GM;
+    const int gsz = min(tiles_m - first_m, GM);
+    const int in = bid % (GM * tiles_n);
+    const int m0 = (first_m + in % gsz) * BM;
+    const int n0 = (in / gsz) * BN;
+    const bf16* A = (const bf16*)g.a;
+    const bf16* B = (const bf16*)g.b;
+
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; i++)
+#pragma unroll
+        for (int j = 0; j < FN; j++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
+
+    const int kbeg = blockIdx.y * kchunk;
+    const int nk = (min(g.K, kbeg + kchunk) - kbeg) / BK;
+    const int klast = kbeg + (nk - 1) * BK;
+    constexpr int LPS = (BM + BN) / (8 * NW);  // direct loads per thread per stage
+
+#define BIG_DMA(SA, SB, K0)                                                  \
+    do {                                                                     \
+        dma_any<BM, NW, AK>(SA, A, g.lda, m0, g.M, (K0), wave, lane);        \
+        dma_any<BN, NW, BKC>(SB, B, g.ldb, n0, g.N, (K0), wave, lane);       \
+    } while (0)
+#define BIG_STEP(SA, SB, NA, NB, KT)                                                     \
+    do {                                                                                 \
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm<(NS - 2) * LPS>());                         \
+        __builtin_amdgcn_s_barrier();                                                    \
+        asm volatile("" ::: "memory");                                                   \
+        BIG_DMA(NA, NB, min(kbeg + ((KT) + NS - 1) * BK, klast));                        \
+        mfma_any<BM, BN, FM, FN, TM, TN, AK, BKC>(acc, SA, SB, wm, wn, lane);            \
+    } while (0)
+
+    BIG_DMA(sa0, sb0, kbeg);
+    if constexpr (NS > 2) BIG_DMA(sa1, sb1, min(kbeg + BK, klast));
+    int kt = 0;
+    if constexpr (NS == 2) {
+        for (; kt + 2 <= nk; kt += 2) {
+            BIG_STEP(sa0, sb0, sa1, sb1, kt);
+            BIG_STEP(sa1, sb1, sa0, sb0, kt + 1);
+        }
+        if (kt < nk) BIG_STEP(sa0, sb0, sa1, sb1, kt);
+    } else {
+        for (; kt + 3 <= nk; kt += 3) {
+            BIG_STEP(sa0, sb0, sa2, sb2, kt);
+            BIG_STEP(sa1, sb1, sa0, sb0, kt + 1);
+            BIG_STEP(sa2, sb2, sa1, sb1, kt + 2);
+        }
+        if (kt < nk) { BIG_STEP(sa0, sb0, sa2, sb2, kt); kt++; }
+        if (kt < nk) BIG_STEP(sa1, sb1, sa0, sb0, kt);
+    }
+#undef BIG_DMA
+#undef BIG_STEP
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());  // no load may still be writing LDS at exit
+
+#pragma unroll
+    for (int i = 0; i < FM; i++)
+#pragma unroll
+        for (int j = 0; j < FN; j++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                const int m = m0 + wm * TM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+                const int n = n0 + wn * TN + j * 32 + (lane & 31);
+                if (m < g.M && n < g.N) epi_store<EPI>(g, m, n, acc[i][j][r]);
+            }
+}
+
+template <int BM, int BN, int NW, int NS, bool AK, bool BKC, int EPI>
+hipError_t launch_big(const GemmArgs& g, hipStream_t s, int splits = 1, int kchunk = 0) {
+    dim3 grid(cdiv(g.M, BM) * cdiv(g.N, BN), splits);
+    gemm_big_kernel<BM, BN, NW, NS, AK, BKC, EPI><<<grid, NW * 64, 0, s>>>(g, kchunk ? kchunk : g.K);
+    return hipGetLastError();
+}
+
 template <int BM, int BN, int WAVES_M, bool AK, bool BKC, int EPI>
 hipError_t launch(const GemmArgs& g, hipStream_t s, int splits = 1, int kchunk = 0) {
     dim3 grid(cdiv(g.M, BM) * cdiv(g.N, BN), splits);
@@ -497,34 +692,51 @@ hipError_t gemm_mfma_bf16(const GemmArgs& g, hipStream_t s) {
     if (g.M <= 0 || g.N <= 0 || g.K <= 0 || g.K % BK || g.M % 8 || g.N % 8 || g.lda % 8 || g.ldb % 8)
         return hipErrorInvalidValue;
     if (!aligned16(g.a) || !aligned16(g.b)) return hipErrorInvalidValue;
+    // Tile choice per form and width, from timings at the GPT-2 shapes:
+    // 256x256 (8 waves) for wide outputs and the backward-data products,
+    // 128x128 direct-load tiles for mid widths, the register-staged 128x128
+    // kernel for the narrow (N = C) forward products.
     if (g.a_kcontig && g.b_kcontig) {
-        switch (g.epi) {
-            case EPI_STORE: return launch<128, 128, 2, true, true, EPI_STORE>(g, s);
-            case EPI_BIAS: return launch<128, 128, 2, true, true, EPI_BIAS>(g, s);
-            case EPI_BIAS_RESID: return launch<128, 128, 2, true, true, EPI_BIAS_RESID>(g, s);
-            case EPI_BIAS_GELU: return launch<128, 128, 2, true, true, EPI_BIAS_GELU>(g, s);
-            default: return hipErrorInvalidValue;
-        }
+#define NT_CASES(BIG)                                                                                   \
+    switch (g.epi) {                                                                                    \
+        case EPI_STORE: return BIG(EPI_STORE);                                                          \
+        case EPI_BIAS: return BIG(EPI_BIAS);                                                            \
+        case EPI_BIAS_RESID: return BIG(EPI_BIAS_RESID);                                                \
+        case EPI_BIAS_GELU: return BIG(EPI_BIAS_GELU);                                                  \
+        default: return hipErrorInvalidValue;                                                           \
+    }
+#define NT_256(E) launch_big<256, 256, 8, 2, true, true, E>(g, s)
+#define NT_128(E) launch_big<128, 128, 4, 2, true, true, E>(g, s)
+#define NT_REG(E) launch<128, 128, 2, true, true, E>(g, s)
+        if (g.N >= 3072) NT_CASES(NT_256)
+        if (g.N >= 1536) NT_CASES(NT_128)
+        NT_CASES(NT_REG)
+#undef NT_CASES
+#undef NT_256
+#undef NT_128
+#undef NT_REG
     }
     if (g.a_kcontig && !g.b_kcontig) {
         switch (g.epi) {
-            case EPI_STORE: return launch<128, 128, 2, true, false, EPI_STORE>(g, s);
-            case EPI_GELU_BWD: return launch<128, 128, 2, true, false, EPI_GELU_BWD>(g, s);
+            case EPI_STORE: return launch_big<256, 256, 8, 2, true, false, EPI_STORE>(g, s);
+            case EPI_GELU_BWD: return launch_big<256, 256, 8, 2, true, false, EPI_GELU_BWD>(g, s);
             default: return hipErrorInvalidValue;
         }
     }
     if (!g.a_kcontig && !g.b_kcontig && g.epi == EPI_ACC_F32) {
+        if (cdiv(g.M, 256) * cdiv(g.N, 256) >= 256)  // wide output (the classifier): no split needed
+            return launch_big<256, 256, 8, 2, false, false, EPI_ACC_F32>(g, s);
         int S, kc;
         splitk_plan(g.M, g.N, g.K, &S, &kc);
         if (S > 1 && g.ws && (size_t)S * g.M * g.N * 4 <= g.ws_bytes && g.N % 4 == 0 && g.ldo % 4 == 0) {
-            hipError_t e = launch<128, 128, 2, false, false, EPI_PARTIAL>(g, s, S, kc);
+            hipError_t e = launch_big<128, 128, 4, 3, false, false, EPI_PARTIAL>(g, s, S, kc);
             if (e != hipSuccess) return e;
             int64_t n4 = (int64_t)g.M * g.N / 4;
             unsigned blocks = (unsigned)std::min<int64_t>((n4 + 255) / 256, 4096);
             splitk_reduce_kernel<<<blocks, 256, 0, s>>>((float*)g.out, g.ldo, g.ws, S, g.M, g.N);
             return hipGetLastError();
         }
-        return launch<128, 128, 2, false, false, EPI_ACC_F32>(g, s);
+        return launch_big<128, 128, 4, 3, false, false, EPI_ACC_F32>(g, s);
     }
     return hipErrorInvalidValue;
 }

@@ -84,24 +84,71 @@ template <int R> struct MNT {
 
 constexpr int EPI_PARTIAL = 100;  // split-K partial tile into g.ws[split][M][N]
 
+// Epilogue of 4 consecutive columns n..n+3 of row m (n % 4 == 0, N % 8 == 0,
+// so the 4 are all inside or all outside the matrix): 8-byte bf16 or 16-byte
+// fp32 accesses.
 template <int EPI>
-DEVI void epi_store(const GemmArgs& g, int m, int n, float acc) {
+DEVI void epi_store4(const GemmArgs& g, int m, int n, const float (&acc)[4]) {
+    typedef bf16 bf16x4_t __attribute__((ext_vector_type(4)));
     if (EPI == EPI_PARTIAL) {
-        g.ws[((int64_t)blockIdx.y * g.M + m) * g.N + n] = acc;
+        *reinterpret_cast<float4*>(g.ws + ((int64_t)blockIdx.y * g.M + m) * g.N + n) =
+            make_float4(acc[0], acc[1], acc[2], acc[3]);
         return;
     }
-    int64_t o = (int64_t)m * g.ldo + n;
+    const int64_t o = (int64_t)m * g.ldo + n;
     if (EPI == EPI_ACC_F32) {
-        float* out = (float*)g.out;
-        out[o] += acc;
+        float4* p = reinterpret_cast<float4*>((float*)g.out + o);
+        float4 v = *p;
+        v.x += acc[0]; v.y += acc[1]; v.z += acc[2]; v.w += acc[3];
+        *p = v;
         return;
     }
-    float b = (EPI != EPI_STORE && EPI != EPI_GELU_BWD && g.bias) ? g.bias[n] : 0.f;
-    float y = acc + b;
-    if (EPI == EPI_BIAS_RESID) y += to_f32(((const bf16*)g.resid)[o]);
-    if (EPI == EPI_GELU_BWD) y = acc * gelu_grad_f(to_f32(((const bf16*)g.aux)[o]));
-    ((bf16*)g.out)[o] = (bf16)y;
-    if (EPI == EPI_BIAS_GELU) ((bf16*)g.out2)[o] = (bf16)gelu_f(y);
+    float y[4] = {acc[0], acc[1], acc[2], acc[3]};
+    if ((EPI == EPI_BIAS || EPI == EPI_BIAS_RESID || EPI == EPI_BIAS_GELU) && g.bias) {
+        const float4 bv = *reinterpret_cast<const float4*>(g.bias + n);
+        y[0] += bv.x; y[1] += bv.y; y[2] += bv.z; y[3] += bv.w;
+    }
+    if (EPI == EPI_BIAS_RESID) {
+        const bf16x4_t r = *reinterpret_cast<const bf16x4_t*>((const bf16*)g.resid + o);
+#pragma unroll
+        for (int e = 0; e < 4; e++) y[e] += (float)r[e];
+    }
+    if (EPI == EPI_GELU_BWD) {
+        const bf16x4_t u = *reinterpret_cast<const bf16x4_t*>((const bf16*)g.aux + o);
+#pragma unroll
+        for (int e = 0; e < 4; e++) y[e] *= gelu_grad_f((float)u[e]);
+    }
+    bf16x4_t out;
+#pragma unroll
+    for (int e = 0; e < 4; e++) out[e] = (bf16)y[e];
+    *reinterpret_cast<bf16x4_t*>((bf16*)g.out + o) = out;
+    if (EPI == EPI_BIAS_GELU) {
+#pragma unroll
+        for (int e = 0; e < 4; e++) out[e] = (bf16)gelu_f(y[e]);
+        *reinterpret_cast<bf16x4_t*>((bf16*)g.out2 + o) = out;
+    }
+}
+
+// The products run the MFMA with the operands swapped, acc = B A^T: register
+// r of lane l of the 32x32 block (i, j) then holds row i*32 + l % 32 and
+// column j*32 + 8*(r/4) + 4*(l/32) + r%4, so each group of 4 registers is 4
+// consecutive columns of one row.
+template <int EPI, int FM, int FN>
+DEVI void epilogue(const GemmArgs& g, const f32x16 (&acc)[FM][FN], int mrow0, int ncol0, int lane) {
+#pragma unroll
+    for (int i = 0; i < FM; i++)
+#pragma unroll
+        for (int j = 0; j < FN; j++)
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                const int m = mrow0 + i * 32 + (lane & 31);
+                const int n = ncol0 + j * 32 + q * 8 + (lane >> 5) * 4;
+                if (m < g.M && n < g.N) {
+                    const float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                        acc[i][j][4 * q + 3]};
+                    epi_store4<EPI>(g, m, n, v);
+                }
+            }
 }
 
 // One k-step (64) of the wave's FM x FN block of 32x32 accumulators from an
@@ -129,7 +176,7 @@ DEVI void mfma_tile(f32x16 (&acc)[FM][FN], const uint16_t* As, int wm, int wn, i
         for (int i = 0; i < FM; i++)
 #pragma unroll
             for (int j = 0; j < FN; j++)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks & 1][i], b[ks & 1][j], acc[i][j], 0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[ks & 1][j], a[ks & 1][i], acc[i][j], 0, 0, 0);
         // keep that order through scheduling: the next sub-step's LDS reads
         // (mask 0x100) issue ahead of this sub-step's MFMAs (mask 0x008)
         if (ks + 1 < BK / 16) __builtin_amdgcn_sched_group_barrier(0x100, FM + FN, 0);
@@ -230,241 +277,18 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs g, int kchunk) 
 #undef GEMM_LOAD
 #undef GEMM_STORE
 
-    // accumulator (i,j) register r of lane l holds row 8*(r/4) + 4*(l/32) + r%4,
-    // column l%32 of the 32x32 block
-#pragma unroll
-    for (int i = 0; i < FM; i++)
-#pragma unroll
-        for (int j = 0; j < FN; j++)
-#pragma unroll
-            for (int r = 0; r < 16; r++) {
-                int m = m0 + wm * TM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-                int n = n0 + wn * TN + j * 32 + (lane & 31);
-                if (m < g.M && n < g.N) epi_store<EPI>(g, m, n, acc[i][j][r]);
-            }
+    epilogue<EPI>(g, acc, m0 + wm * TM, n0 + wn * TN, lane);
 }
 
 // ============================================================================
-// Direct-to-LDS variant.  A k-contiguous operand tile goes from global memory
-// straight into LDS with global_load_lds_dwordx4 (no staging registers, no
-// ds_write): one instruction fills 1 KB of LDS, lane l's 16 bytes at
-// base + 16*l.  The LDS tile is unpadded ([row][64] bf16, 128-byte rows) and
-// XOR-swizzled: the 16-byte k-chunk c of row r sits in slot c ^ (r & 7), so
-// the 32 rows an MFMA fragment read touches spread over all banks.  An
-// mn-contiguous operand still goes through registers (8x8 transposes) into
-// the same swizzled layout.  NS stages, each its own __shared__ array (so
-// alias analysis keeps the reads of one stage independent of the loads in
-// flight into another); each k-step waits only for its own stage's loads
-// (explicit vmcnt) and synchronises with a raw barrier, so the loads of the
-// next NS-1 stages stay in flight across it.
+// Machinery of the direct-to-LDS kernel below: global_load_lds_dwordx4 fills
+// 1 KB of LDS per wave instruction, lane l's 16 bytes at base + 16*l.
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
-
-DEVI int swz(int row, int chunk) { return row * BK + ((chunk ^ (row & 7)) << 3); }
 
 // s_waitcnt immediate (gfx9 encoding): vmcnt <= N, lgkmcnt = 0 (this wave's
 // LDS writes done before a barrier publishes them), expcnt unconstrained
 template <int N> constexpr int vmcnt_imm() { return (N & 15) | ((N >> 4) << 14) | (7 << 4); }
-
-// rows [r0, r0+R) x k [k0, k0+64) of a k-contiguous X, R/32 loads per thread
-template <int R>
-DEVI void dma_tile(uint16_t* tile, const bf16* X, int64_t ld, int r0, int rows, int k0, int wave, int lane) {
-    constexpr int NI = R / 32;
-    const int r_in = lane >> 3;                   // row within the 8-row, 1 KB block
-    const int c = (lane & 7) ^ r_in;              // global chunk that lands in this lane's slot
-#pragma unroll
-    for (int i = 0; i < NI; i++) {
-        const int blk = wave * NI + i;
-        const int rr = min(r0 + blk * 8 + r_in, rows - 1);  // past-the-end rows: clamped (never stored)
-        __builtin_amdgcn_global_load_lds((glb_void_t*)(X + (int64_t)rr * ld + k0 + c * 8),
-                                         (lds_void_t*)(tile + blk * 512), 16, 0, 0);
-    }
-}
-
-// mn-contiguous X through registers: 8x8 blocks, block b = (tid+off)%256 < R
-template <int R> struct MNS {
-    static_assert(R <= 256, "one block per thread");
-    static DEVI void load(u32x4 (&v)[8], const bf16* X, int64_t ld, int r0, int rows, int k0, int tid, int off) {
-        const int b = (tid + off) & 255;
-        if (b >= R) return;
-        const int kb = b & 7, rb = b >> 3;
-        const int rr = min(r0 + rb * 8, rows - 8);
-#pragma unroll
-        for (int j = 0; j < 8; j++) v[j] = *reinterpret_cast<const u32x4*>(X + (int64_t)(k0 + kb * 8 + j) * ld + rr);
-    }
-    static DEVI void store(const u32x4 (&v)[8], uint16_t* tile, int tid, int off) {
-        const int b = (tid + off) & 255;
-        if (b >= R) return;
-        const int kb = b & 7, rb = b >> 3;
-#pragma unroll
-        for (int i = 0; i < 8; i++) {
-            uint32_t o[4];
-#pragma unroll
-            for (int q = 0; q < 4; q++) {
-                const uint32_t lo = (i & 2) ? (i & 4 ? v[2 * q].w : v[2 * q].y) : (i & 4 ? v[2 * q].z : v[2 * q].x);
-                const uint32_t hi = (i & 2) ? (i & 4 ? v[2 * q + 1].w : v[2 * q + 1].y)
-                                            : (i & 4 ? v[2 * q + 1].z : v[2 * q + 1].x);
-                o[q] = (i & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-            }
-            *reinterpret_cast<u32x4*>(tile + swz(rb * 8 + i, kb)) = u32x4{o[0], o[1], o[2], o[3]};
-        }
-    }
-};
-
-template <int FM, int FN, int TM, int TN>
-DEVI void mfma_swz(f32x16 (&acc)[FM][FN], const uint16_t* As, const uint16_t* Bs, int wm, int wn, int lane) {
-    // fragments double-buffered in registers: the LDS reads of sub-step ks+1
-    // are in flight while the MFMAs of sub-step ks run
-    bf16x8 a[2][FM], b[2][FN];
-    auto frag = [&](int ks, bf16x8 (&fa)[FM], bf16x8 (&fb)[FN]) {
-        const int c = ks * 2 + (lane >> 5);
-#pragma unroll
-        for (int i = 0; i < FM; i++)
-            fa[i] = *reinterpret_cast<const bf16x8*>(As + swz(wm * TM + i * 32 + (lane & 31), c));
-#pragma unroll
-        for (int j = 0; j < FN; j++)
-            fb[j] = *reinterpret_cast<const bf16x8*>(Bs + swz(wn * TN + j * 32 + (lane & 31), c));
-    };
-    frag(0, a[0], b[0]);
-    __builtin_amdgcn_sched_group_barrier(0x100, FM + FN, 0);
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ks++) {
-        if (ks + 1 < BK / 16) frag(ks + 1, a[(ks + 1) & 1], b[(ks + 1) & 1]);
-#pragma unroll
-        for (int i = 0; i < FM; i++)
-#pragma unroll
-            for (int j = 0; j < FN; j++)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks & 1][i], b[ks & 1][j], acc[i][j], 0, 0, 0);
-        // keep that order through scheduling: the next sub-step's LDS reads
-        // (mask 0x100) issue ahead of this sub-step's MFMAs (mask 0x008)
-        if (ks + 1 < BK / 16) __builtin_amdgcn_sched_group_barrier(0x100, FM + FN, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, FM * FN, 0);
-    }
-}
-
-// A is k-contiguous (direct loads); B k-contiguous (direct) or mn-contiguous
-// (registers).
-template <int BM, int BN, int WAVES_M, int NS, bool BKC, int EPI>
-__global__ __launch_bounds__(256) void gemm_dlds_kernel(GemmArgs g, int kchunk) {
-    constexpr int WAVES_N = 4 / WAVES_M;
-    constexpr int TM = BM / WAVES_M, TN = BN / WAVES_N, FM = TM / 32, FN = TN / 32;
-    static_assert(NS >= 2 && NS <= 4, "stages");
-    __shared__ __attribute__((aligned(1024))) uint16_t sa0[BM * BK], sa1[BM * BK], sa2[NS > 2 ? BM * BK : 8],
-        sa3[NS > 3 ? BM * BK : 8];
-    __shared__ __attribute__((aligned(1024))) uint16_t sb0[BN * BK], sb1[BN * BK], sb2[NS > 2 ? BN * BK : 8],
-        sb3[NS > 3 ? BN * BK : 8];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
-
-    const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
-    int bid = blockIdx.x;
-    const int total = gridDim.x;
-    if ((total & 7) == 0) bid = (bid & 7) * (total >> 3) + (bid >> 3);
-    constexpr int GM = 8;
-    const int group = bid / (GM * tiles_n);
-    const int first_m = group * GM;
-    const int gsz = min(tiles_m - first_m, GM);
-    const int in = bid % (GM * tiles_n);
-    const int m0 = (first_m + in % gsz) * BM;
-    const int n0 = (in / gsz) * BN;
-    const bf16* A = (const bf16*)g.a;
-    const bf16* B = (const bf16*)g.b;
-
-    f32x16 acc[FM][FN];
-#pragma unroll
-    for (int i = 0; i < FM; i++)
-#pragma unroll
-        for (int j = 0; j < FN; j++)
-#pragma unroll
-            for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
-
-    const int kbeg = blockIdx.y * kchunk;
-    const int nk = (min(g.K, kbeg + kchunk) - kbeg) / BK;
-    const int klast = kbeg + (nk - 1) * BK;
-    // direct loads per thread per stage (what the explicit waits count)
-    constexpr int LPS = BM / 32 + (BKC ? BN / 32 : 0);
-    u32x4 rb[8];  // mn-contiguous B staging (unused when B is k-contiguous)
-
-#define DLDS_DMA(SA, SB, K0)                                                      \
-    do {                                                                          \
-        dma_tile<BM>(SA, A, g.lda, m0, g.M, (K0), wave, lane);                    \
-        if constexpr (BKC) dma_tile<BN>(SB, B, g.ldb, n0, g.N, (K0), wave, lane); \
-    } while (0)
-#define DLDS_SYNC()                                                     \
-    do {                                                                \
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm<(NS - 2) * LPS>());        \
-        __builtin_amdgcn_s_barrier();                                   \
-        asm volatile("" ::: "memory");                                  \
-    } while (0)
-    // one k-step: stage (SA,SB) computed, next DMA into (NA,NB) for step KT+NS-1,
-    // the mn-contiguous B of step KT+1 staged through registers into (XA,XB)
-#define DLDS_STEP(SA, SB, NA, NB, XB, KT)                                                    \
-    do {                                                                                     \
-        DLDS_SYNC();                                                                         \
-        if constexpr (!BKC) MNS<BN>::load(rb, B, g.ldb, n0, g.N, min(kbeg + ((KT) + 1) * BK, klast), tid, 0); \
-        DLDS_DMA(NA, NB, min(kbeg + ((KT) + NS - 1) * BK, klast));                           \
-        mfma_swz<FM, FN, TM, TN>(acc, SA, SB, wm, wn, lane);                                  \
-        if constexpr (!BKC) MNS<BN>::store(rb, XB, tid, 0);                                   \
-    } while (0)
-
-    // prologue: stages 0..NS-2 in flight (and the mn-contiguous B of step 0)
-    DLDS_DMA(sa0, sb0, kbeg);
-    if constexpr (NS > 2) DLDS_DMA(sa1, sb1, min(kbeg + BK, klast));
-    if constexpr (NS > 3) DLDS_DMA(sa2, sb2, min(kbeg + 2 * BK, klast));
-    if constexpr (!BKC) {
-        MNS<BN>::load(rb, B, g.ldb, n0, g.N, kbeg, tid, 0);
-        MNS<BN>::store(rb, sb0, tid, 0);
-    }
-    int kt = 0;
-    if constexpr (NS == 2) {
-        for (; kt + 2 <= nk; kt += 2) {
-            DLDS_STEP(sa0, sb0, sa1, sb1, sb1, kt);
-            DLDS_STEP(sa1, sb1, sa0, sb0, sb0, kt + 1);
-        }
-        if (kt < nk) DLDS_STEP(sa0, sb0, sa1, sb1, sb1, kt);
-    } else if constexpr (NS == 3) {
-        for (; kt + 3 <= nk; kt += 3) {
-            DLDS_STEP(sa0, sb0, sa2, sb2, sb1, kt);
-            DLDS_STEP(sa1, sb1, sa0, sb0, sb2, kt + 1);
-            DLDS_STEP(sa2, sb2, sa1, sb1, sb0, kt + 2);
-        }
-        if (kt < nk) { DLDS_STEP(sa0, sb0, sa2, sb2, sb1, kt); kt++; }
-        if (kt < nk) DLDS_STEP(sa1, sb1, sa0, sb0, sb2, kt);
-    } else {
-        for (; kt + 4 <= nk; kt += 4) {
-            DLDS_STEP(sa0, sb0, sa3, sb3, sb1, kt);
-            DLDS_STEP(sa1, sb1, sa0, sb0, sb2, kt + 1);
-            DLDS_STEP(sa2, sb2, sa1, sb1, sb3, kt + 2);
-            DLDS_STEP(sa3, sb3, sa2, sb2, sb0, kt + 3);
-        }
-        if (kt < nk) { DLDS_STEP(sa0, sb0, sa3, sb3, sb1, kt); kt++; }
-        if (kt < nk) { DLDS_STEP(sa1, sb1, sa0, sb0, sb2, kt); kt++; }
-        if (kt < nk) DLDS_STEP(sa2, sb2, sa1, sb1, sb3, kt);
-    }
-#undef DLDS_DMA
-#undef DLDS_SYNC
-#undef DLDS_STEP
-    // drain: no load may still be writing LDS when the workgroup exits
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
-
-#pragma unroll
-    for (int i = 0; i < FM; i++)
-#pragma unroll
-        for (int j = 0; j < FN; j++)
-#pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const int m = m0 + wm * TM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-                const int n = n0 + wn * TN + j * 32 + (lane & 31);
-                if (m < g.M && n < g.N) epi_store<EPI>(g, m, n, acc[i][j][r]);
-            }
-}
-
-template <int BM, int BN, int WAVES_M, int NS, bool BKC, int EPI>
-hipError_t launch_dlds(const GemmArgs& g, hipStream_t s) {
-    dim3 grid(cdiv(g.M, BM) * cdiv(g.N, BN), 1);
-    gemm_dlds_kernel<BM, BN, WAVES_M, NS, BKC, EPI><<<grid, 256, 0, s>>>(g, g.K);
-    return hipGetLastError();
-}
 
 // ============================================================================
 // Large-tile variant: every operand goes global -> LDS by direct loads, in the
@@ -548,7 +372,7 @@ DEVI void mfma_any(f32x16 (&acc)[FM][FN], const uint16_t* As, const uint16_t* Bs
         for (int i = 0; i < FM; i++)
 #pragma unroll
             for (int j = 0; j < FN; j++)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks & 1][i], b[ks & 1][j], acc[i][j], 0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[ks & 1][j], a[ks & 1][i], acc[i][j], 0, 0, 0);
         if (ks + 1 < BK / 16) __builtin_amdgcn_sched_group_barrier(0x100, (FM + FN) * (AK && BKC ? 1 : 2), 0);
         __builtin_amdgcn_sched_group_barrier(0x008, FM * FN, 0);
     }
@@ -627,16 +451,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_big_kernel(GemmArgs g, int kchun
 #undef BIG_STEP
     __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());  // no load may still be writing LDS at exit
 
-#pragma unroll
-    for (int i = 0; i < FM; i++)
-#pragma unroll
-        for (int j = 0; j < FN; j++)
-#pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const int m = m0 + wm * TM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-                const int n = n0 + wn * TN + j * 32 + (lane & 31);
-                if (m < g.M && n < g.N) epi_store<EPI>(g, m, n, acc[i][j][r]);
-            }
+    epilogue<EPI>(g, acc, m0 + wm * TM, n0 + wn * TN, lane);
 }
 
 template <int BM, int BN, int NW, int NS, bool AK, bool BKC, int EPI>

@@ -79,7 +79,7 @@ typedef struct gpt2_model gpt2_t;
  * backward needs, activation gradients and small scratch, each region
  * 256-byte aligned.  Pure host function.  GPT2_EINVAL on a bad config:
  * C % NH != 0, T > maxT, V > Vp, a non-positive size, an unknown precision,
- * or in BF16_MIXED: hs != 64, C % 64 != 0 or (B*T) % 64 != 0. */
+ * or in BF16_MIXED: hs != 64, or C, Vp or T not a multiple of 64. */
 int gpt2_plan(const gpt2_config* cfg, size_t* device_bytes);
 
 /* Carve device_buf (device memory of at least gpt2_plan() bytes, 256-byte

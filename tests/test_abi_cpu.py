@@ -63,7 +63,8 @@ def test_plan_sizes():
     (dict(V=50305), "vocab_size"),
     (dict(precision=7), "precision"),
     (dict(NH=6), "head size 64"),             # bf16 mode needs hs = 64
-    (dict(B=1, T=63), "multiples of 64"),     # bf16 mode needs B*T % 64 == 0
+    (dict(B=1, T=63), "multiples of 64"),     # bf16 mode needs T % 64 == 0
+    (dict(B=64, T=33), "multiples of 64"),    # even when B*T is one
     (dict(L=0), "positive"),
 ])
 def test_plan_rejects_bad_configs(kw, msg):

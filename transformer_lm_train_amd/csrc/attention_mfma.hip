@@ -16,6 +16,15 @@
 // exactly the B-operand shape of the next product (O^T = V^T P^T), so P
 // never leaves registers; V^T is staged in LDS key-contiguous to match.
 //
+// Tiles stream through LDS in their natural [row][64] layout (16-byte chunk c
+// of row r in slot c ^ (r & 7)), loaded by global_load_lds_dwordx4 straight
+// from global memory, NS stages deep.  A product that needs a tile
+// transposed (V^T, K^T, dO and Q as B operands) reads it with
+// ds_read_b64_tr_b16: within a 16-lane group, lane i receives element i%4 of
+// the 8-byte reads of lanes 4e + i/4 (e = 0..3), so lanes reading rows
+// k0..k0+3 at columns m0 + 4(j%4) hand lane i the column m0 + i over those
+// four rows.
+//
 // Backward is two deterministic kernels, no atomics:
 //   dq kernel (query blocks): recompute S^T and dP^T = V dO^T, dS^T =
 //     P^T (dP^T - D), dQ^T = K^T dS^T; also writes D = rowsum(dO o O).
@@ -29,14 +38,17 @@ namespace {
 constexpr int HS = 64;   // head size
 constexpr int QB = 128;  // rows (queries or keys) owned by one workgroup: 4 waves x 32
 constexpr int KB = 64;   // rows streamed per inner step
-constexpr int LP = 72;   // LDS pitch (elements) of a 64-wide bf16 row, padded
+constexpr int NS = 3;    // LDS stages
+constexpr int TILE = KB * HS;  // elements of one 64 x 64 tile
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-DEVI bf16x8 cat44(bf16x4 a, bf16x4 b) { return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7); }
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
 
 DEVI bf16x8 to_bf16x8(const f32x16& v, int base) {
     bf16x8 r;
@@ -58,61 +70,65 @@ DEVI u32x4 ld_row(const bf16* p, bool ok) {
     return ok ? *reinterpret_cast<const u32x4*>(p) : u32x4{0, 0, 0, 0};
 }
 
-// A 64-row x 64-channel block of a [*, ld] bf16 matrix in 8x8 pieces, one per
-// thread t = 0..63 (rows rb*8.., channels cb*8..).  Rows at or past `rows`
-// re-read row rows-1: every consumer masks them (their probabilities are 0),
-// so they only need to be finite.
-DEVI void blk_load(u32x4 (&v)[8], const bf16* src, int64_t ld, int r0, int rows, int t) {
-    const int rb = t >> 3, cb = t & 7;
+// s_waitcnt immediate (gfx9 encoding): vmcnt <= N, lgkmcnt = 0, expcnt free
+template <int N> constexpr int vmcnt_imm() { return (N & 15) | ((N >> 4) << 14) | (7 << 4); }
+
+// rows [r0, r0+64) x 64 channels of a [*, ld] matrix into a swizzled tile;
+// each of the 4 waves issues 2 loads of 1 KB.  Rows at or past `rows` re-read
+// row rows-1: every consumer masks them, so they only need to be finite.
+DEVI void dma_tile(bf16* tile, const bf16* src, int64_t ld, int r0, int rows, int wave, int lane) {
+    const int c = (lane & 7) ^ (lane >> 3);  // chunk landing in slot lane&7 of row lane>>3 (mod 8)
 #pragma unroll
-    for (int j = 0; j < 8; j++) {
-        const int r = min(r0 + rb * 8 + j, rows - 1);
-        v[j] = *reinterpret_cast<const u32x4*>(src + (int64_t)r * ld + cb * 8);
-    }
-}
-DEVI void blk_store_nat(const u32x4 (&v)[8], bf16* nat, int t) {
-    const int rb = t >> 3, cb = t & 7;
-#pragma unroll
-    for (int j = 0; j < 8; j++) *reinterpret_cast<u32x4*>(nat + (rb * 8 + j) * LP + cb * 8) = v[j];
-}
-// transposed copy: LDS row c holds channel c of the 64 rows (row-contiguous)
-DEVI void blk_store_tr(const u32x4 (&v)[8], bf16* tr, int t) {
-    const int rb = t >> 3, cb = t & 7;
-#pragma unroll
-    for (int i = 0; i < 8; i++) {
-        uint32_t o[4];
-#pragma unroll
-        for (int q = 0; q < 4; q++) {
-            const uint32_t lo = v[2 * q][i >> 1], hi = v[2 * q + 1][i >> 1];
-            o[q] = (i & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-        }
-        *reinterpret_cast<u32x4*>(tr + (cb * 8 + i) * LP + rb * 8) = u32x4{o[0], o[1], o[2], o[3]};
+    for (int i = 0; i < 2; i++) {
+        const int blk = wave * 2 + i;
+        const int r = min(r0 + blk * 8 + (lane >> 3), rows - 1);
+        __builtin_amdgcn_global_load_lds((glb_void_t*)(src + (int64_t)r * ld + c * 8), (lds_void_t*)(tile + blk * 512),
+                                         16, 0, 0);
     }
 }
 
-// The A operand of a 32x32x16 product whose 16 reduction slots are the rows
-// held by accumulator registers 8j..8j+7 of a lane in half hi: positions
-// t32 + 8*(2j) + 4hi + 0..3 and t32 + 8*(2j+1) + 4hi + 0..3 of a
-// row-contiguous (transposed) LDS row.
-DEVI bf16x8 a_from_tr(const bf16* row, int t32, int j, int hi) {
-    bf16x4 x = *reinterpret_cast<const bf16x4*>(row + t32 + 16 * j + 4 * hi);
-    bf16x4 y = *reinterpret_cast<const bf16x4*>(row + t32 + 16 * j + 8 + 4 * hi);
-    return cat44(x, y);
+// 8 consecutive channels chunk*8.. of tile row `row` (one 16-byte read)
+DEVI bf16x8 frag_row(const bf16* tile, int row, int chunk) {
+    return *reinterpret_cast<const bf16x8*>(tile + row * HS + ((chunk ^ (row & 7)) << 3));
+}
+
+// 4 consecutive rows krow..krow+3 of column mcol + (lane % 16), transposed
+// out of the tile (krow, mcol uniform over each 16-lane group)
+DEVI i16x4 tr4(const bf16* tile, int krow, int mcol, int lane) {
+    const int j = lane & 15;
+    const int r = krow + (j >> 2), c = mcol + 4 * (j & 3);
+    const int off = r * HS + ((((c >> 3) ^ (r & 7)) << 3) | (c & 7));
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + off));
+}
+
+// Operand of a 32x32x16 product whose 16 reduction slots are the tile rows
+// held by accumulator registers 8j..8j+7 of a lane in half hi (rows
+// t32 + 16j + 4hi + 0..3 and t32 + 16j + 8 + 4hi + 0..3) and whose 32 rows or
+// columns are channels dt*32 + lane%32: two transposing reads.
+DEVI bf16x8 frag_tr(const bf16* tile, int t32, int j, int dt, int lane) {
+    const int krow = t32 + 16 * j + 4 * (lane >> 5);
+    const int mcol = dt * 32 + 16 * ((lane >> 4) & 1);
+    i16x4 xy[2] = {tr4(tile, krow, mcol, lane), tr4(tile, krow + 8, mcol, lane)};
+    return *reinterpret_cast<bf16x8*>(xy);
 }
 
 // accumulator register r of lane half hi covers row 8*(r/4) + 4*hi + r%4
 DEVI int acc_row(int r, int hi) { return ((r >> 2) << 3) + (hi << 2) + (r & 3); }
 
-// Every kernel below streams 64-row blocks through two LDS buffers: the
-// global loads of block i+1 go to registers before block i is computed and
-// are written to the other buffer after it, so their latency overlaps the
-// matrix-core work.  The prefetch index is clamped instead of branched (the
-// last iteration re-loads its own block), keeping the wait counts tight.
+// The stages are distinct __shared__ arrays so that alias analysis keeps the
+// reads of one stage independent of the loads in flight into another; each
+// step waits only for its own stage (explicit vmcnt), then a raw barrier.
+#define STAGE_SYNC(LPS)                                       \
+    do {                                                      \
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm<(NS - 2) * (LPS)>()); \
+        __builtin_amdgcn_s_barrier();                         \
+        asm volatile("" ::: "memory");                        \
+    } while (0)
 
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void flash_fwd_kernel(bf16* out, float* lse, const bf16* qkv, int T, int C, int NH) {
-    __shared__ __attribute__((aligned(16))) bf16 Ks[2][KB * LP];
-    __shared__ __attribute__((aligned(16))) bf16 Vt[2][HS * LP];
+    __shared__ __attribute__((aligned(1024))) bf16 k0s[TILE], k1s[TILE], k2s[TILE];
+    __shared__ __attribute__((aligned(1024))) bf16 v0s[TILE], v1s[TILE], v2s[TILE];
     const int nqb = (T + QB - 1) / QB;
     const int qblk = nqb - 1 - (int)blockIdx.x;  // longest rows first
     const int h = blockIdx.y, b = blockIdx.z;
@@ -136,83 +152,73 @@ __global__ __launch_bounds__(256) void flash_fwd_kernel(bf16* out, float* lse, c
 
     const int kend = min(T, qblk * QB + QB);
     const int nkb = (kend + KB - 1) / KB;
-    u32x4 kr[2], vr[8];
-    // K block: 512 16-byte chunks, 2 per thread; V block: 8x8 pieces, threads 0..63
-    auto load = [&](int k0) {
+    const int klast = (nkb - 1) * KB;
+
+    auto step = [&](const bf16* Ks, const bf16* Vs, bf16* NK, bf16* NV, int kb) {
+        STAGE_SYNC(4);
+        const int kn = min((kb + NS - 1) * KB, klast);
+        dma_tile(NK, kbase, C3, kn, T, w, lane);
+        dma_tile(NV, vbase, C3, kn, T, w, lane);
+        const int k0 = kb * KB;
+        if (k0 > q0 + 31) return;  // every key of the block is in the future of every query of the wave
+        f32x16 s[2];
 #pragma unroll
-        for (int i = 0; i < 2; i++) {
-            const int c = tid + i * 256;
-            const int key = min(k0 + (c >> 3), T - 1);
-            kr[i] = *reinterpret_cast<const u32x4*>(kbase + (int64_t)key * C3 + (c & 7) * 8);
+        for (int t = 0; t < 2; t++) {
+            s[t] = zero16();
+#pragma unroll
+            for (int ks = 0; ks < 4; ks++) s[t] = mfma(frag_row(Ks, t * 32 + lq, ks * 2 + hi), qf[ks], s[t]);
         }
-        if (tid < 64) blk_load(vr, vbase, C3, k0, T, tid);
-    };
-    auto store = [&](int buf) {
+        float mloc = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < 2; i++) {
-            const int c = tid + i * 256;
-            *reinterpret_cast<u32x4*>(&Ks[buf][(c >> 3) * LP + (c & 7) * 8]) = kr[i];
-        }
-        if (tid < 64) blk_store_tr(vr, Vt[buf], tid);
-    };
-    load(0);
-    store(0);
-    __syncthreads();
-    for (int kb = 0; kb < nkb; kb++) {
-        const int k0 = kb * KB, cur = kb & 1;
-        load(min(kb + 1, nkb - 1) * KB);
-        if (k0 <= q0 + 31) {  // else every key of the block is in the future of every query of the wave
-            f32x16 s[2];
+        for (int t = 0; t < 2; t++)
 #pragma unroll
-            for (int t = 0; t < 2; t++) {
-                s[t] = zero16();
-#pragma unroll
-                for (int ks = 0; ks < 4; ks++) {
-                    bf16x8 a = *reinterpret_cast<const bf16x8*>(&Ks[cur][(t * 32 + lq) * LP + ks * 16 + hi * 8]);
-                    s[t] = mfma(a, qf[ks], s[t]);
-                }
+            for (int r = 0; r < 16; r++) {
+                const int key = k0 + t * 32 + acc_row(r, hi);
+                float x = s[t][r] * sc;
+                if (key > q || key >= T) x = -INFINITY;
+                s[t][r] = x;
+                mloc = fmaxf(mloc, x);
             }
-            float mloc = -INFINITY;
+        mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+        const float m_new = fmaxf(m_run, mloc);
+        const float alpha = exp2f(m_run - m_new);
+        float lsum = 0.f;
 #pragma unroll
-            for (int t = 0; t < 2; t++)
+        for (int t = 0; t < 2; t++)
 #pragma unroll
-                for (int r = 0; r < 16; r++) {
-                    const int key = k0 + t * 32 + acc_row(r, hi);
-                    float x = s[t][r] * sc;
-                    if (key > q || key >= T) x = -INFINITY;
-                    s[t][r] = x;
-                    mloc = fmaxf(mloc, x);
-                }
-            mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-            const float m_new = fmaxf(m_run, mloc);
-            const float alpha = exp2f(m_run - m_new);
-            float lsum = 0.f;
+            for (int r = 0; r < 16; r++) {
+                const float pr = exp2f(s[t][r] - m_new);
+                s[t][r] = pr;
+                lsum += pr;
+            }
+        lsum += __shfl_xor(lsum, 32, 64);
+        l_run = l_run * alpha + lsum;
+        m_run = m_new;
 #pragma unroll
-            for (int t = 0; t < 2; t++)
+        for (int r = 0; r < 16; r++) { o[0][r] *= alpha; o[1][r] *= alpha; }
 #pragma unroll
-                for (int r = 0; r < 16; r++) {
-                    const float p = exp2f(s[t][r] - m_new);
-                    s[t][r] = p;
-                    lsum += p;
-                }
-            lsum += __shfl_xor(lsum, 32, 64);
-            l_run = l_run * alpha + lsum;
-            m_run = m_new;
+        for (int t = 0; t < 2; t++)
 #pragma unroll
-            for (int r = 0; r < 16; r++) { o[0][r] *= alpha; o[1][r] *= alpha; }
+            for (int j = 0; j < 2; j++) {
+                const bf16x8 pb = to_bf16x8(s[t], 8 * j);
 #pragma unroll
-            for (int t = 0; t < 2; t++)
-#pragma unroll
-                for (int j = 0; j < 2; j++) {
-                    const bf16x8 pb = to_bf16x8(s[t], 8 * j);
-#pragma unroll
-                    for (int dt = 0; dt < 2; dt++)
-                        o[dt] = mfma(a_from_tr(&Vt[cur][(dt * 32 + lq) * LP], t * 32, j, hi), pb, o[dt]);
-                }
-        }
-        store(cur ^ 1);
-        __syncthreads();
+                for (int dt = 0; dt < 2; dt++) o[dt] = mfma(frag_tr(Vs, t * 32, j, dt, lane), pb, o[dt]);
+            }
+    };
+    dma_tile(k0s, kbase, C3, 0, T, w, lane);
+    dma_tile(v0s, vbase, C3, 0, T, w, lane);
+    dma_tile(k1s, kbase, C3, min(KB, klast), T, w, lane);
+    dma_tile(v1s, vbase, C3, min(KB, klast), T, w, lane);
+    int kb = 0;
+    for (; kb + 3 <= nkb; kb += 3) {
+        step(k0s, v0s, k2s, v2s, kb);
+        step(k1s, v1s, k0s, v0s, kb + 1);
+        step(k2s, v2s, k1s, v1s, kb + 2);
     }
+    if (kb < nkb) { step(k0s, v0s, k2s, v2s, kb); kb++; }
+    if (kb < nkb) step(k1s, v1s, k0s, v0s, kb);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());  // no load may still be writing LDS at exit
+
     if (q < T) {
         const float inv = 1.f / l_run;
         bf16* orow = out + ((int64_t)b * T + q) * C + h * HS;
@@ -232,15 +238,16 @@ __global__ __launch_bounds__(256) void flash_fwd_kernel(bf16* out, float* lse, c
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void flash_bwd_dq_kernel(bf16* dqkv, float* Dout, const bf16* dout, const bf16* qkv,
                                                            const bf16* out, const float* lse, int T, int C, int NH) {
-    __shared__ __attribute__((aligned(16))) bf16 Ks[2][KB * LP];
-    __shared__ __attribute__((aligned(16))) bf16 Kt[2][HS * LP];
-    __shared__ __attribute__((aligned(16))) bf16 Vs[2][KB * LP];
+    __shared__ __attribute__((aligned(1024))) bf16 k0s[TILE], k1s[TILE], k2s[TILE];
+    __shared__ __attribute__((aligned(1024))) bf16 v0s[TILE], v1s[TILE], v2s[TILE];
     const int nqb = (T + QB - 1) / QB;
     const int qblk = nqb - 1 - (int)blockIdx.x;
     const int h = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hi = lane >> 5, lq = lane & 31;
     const int64_t C3 = 3 * (int64_t)C;
     const bf16* base = qkv + (int64_t)b * T * C3;
+    const bf16* kbase = base + C + h * HS;
+    const bf16* vbase = base + 2 * C + h * HS;
     const int q0 = qblk * QB + w * 32;
     const int q = q0 + lq;
     const bool qok = q < T;
@@ -268,59 +275,57 @@ __global__ __launch_bounds__(256) void flash_bwd_dq_kernel(bf16* dqkv, float* Do
     f32x16 dq[2] = {zero16(), zero16()};
     const int kend = min(T, qblk * QB + QB);
     const int nkb = (kend + KB - 1) / KB;
-    u32x4 reg[8];  // threads 0..63: a K block piece; 64..127: a V block piece
-    auto load = [&](int k0) {
-        if (tid < 64) blk_load(reg, base + C + h * HS, C3, k0, T, tid);
-        else if (tid < 128) blk_load(reg, base + 2 * C + h * HS, C3, k0, T, tid - 64);
-    };
-    auto store = [&](int buf) {
-        if (tid < 64) {
-            blk_store_nat(reg, Ks[buf], tid);
-            blk_store_tr(reg, Kt[buf], tid);
-        } else if (tid < 128) {
-            blk_store_nat(reg, Vs[buf], tid - 64);
+    const int klast = (nkb - 1) * KB;
+
+    auto step = [&](const bf16* Ks, const bf16* Vs, bf16* NK, bf16* NV, int kb) {
+        STAGE_SYNC(4);
+        const int kn = min((kb + NS - 1) * KB, klast);
+        dma_tile(NK, kbase, C3, kn, T, w, lane);
+        dma_tile(NV, vbase, C3, kn, T, w, lane);
+        const int k0 = kb * KB;
+        if (k0 > q0 + 31) return;
+        f32x16 s[2], dp[2];
+#pragma unroll
+        for (int t = 0; t < 2; t++) {
+            s[t] = zero16();
+            dp[t] = zero16();
+#pragma unroll
+            for (int ks = 0; ks < 4; ks++) {
+                s[t] = mfma(frag_row(Ks, t * 32 + lq, ks * 2 + hi), qf[ks], s[t]);
+                dp[t] = mfma(frag_row(Vs, t * 32 + lq, ks * 2 + hi), dof[ks], dp[t]);
+            }
         }
-    };
-    load(0);
-    store(0);
-    __syncthreads();
-    for (int kb = 0; kb < nkb; kb++) {
-        const int k0 = kb * KB, cur = kb & 1;
-        load(min(kb + 1, nkb - 1) * KB);
-        if (k0 <= q0 + 31) {
-            f32x16 s[2], dp[2];
 #pragma unroll
-            for (int t = 0; t < 2; t++) {
-                s[t] = zero16();
-                dp[t] = zero16();
+        for (int t = 0; t < 2; t++)
 #pragma unroll
-                for (int ks = 0; ks < 4; ks++) {
-                    const int off = (t * 32 + lq) * LP + ks * 16 + hi * 8;
-                    s[t] = mfma(*reinterpret_cast<const bf16x8*>(&Ks[cur][off]), qf[ks], s[t]);
-                    dp[t] = mfma(*reinterpret_cast<const bf16x8*>(&Vs[cur][off]), dof[ks], dp[t]);
-                }
+            for (int r = 0; r < 16; r++) {
+                const int key = k0 + t * 32 + acc_row(r, hi);
+                const float pr = (key > q || key >= T || !qok) ? 0.f : exp2f(s[t][r] * sc - lse2);
+                s[t][r] = pr * (dp[t][r] - Dq);  // dS^T
             }
 #pragma unroll
-            for (int t = 0; t < 2; t++)
+        for (int t = 0; t < 2; t++)
 #pragma unroll
-                for (int r = 0; r < 16; r++) {
-                    const int key = k0 + t * 32 + acc_row(r, hi);
-                    const float p = (key > q || key >= T || !qok) ? 0.f : exp2f(s[t][r] * sc - lse2);
-                    s[t][r] = p * (dp[t][r] - Dq);  // dS^T
-                }
+            for (int j = 0; j < 2; j++) {
+                const bf16x8 dsb = to_bf16x8(s[t], 8 * j);
 #pragma unroll
-            for (int t = 0; t < 2; t++)
-#pragma unroll
-                for (int j = 0; j < 2; j++) {
-                    const bf16x8 dsb = to_bf16x8(s[t], 8 * j);
-#pragma unroll
-                    for (int dt = 0; dt < 2; dt++)
-                        dq[dt] = mfma(a_from_tr(&Kt[cur][(dt * 32 + lq) * LP], t * 32, j, hi), dsb, dq[dt]);
-                }
-        }
-        store(cur ^ 1);
-        __syncthreads();
+                for (int dt = 0; dt < 2; dt++) dq[dt] = mfma(frag_tr(Ks, t * 32, j, dt, lane), dsb, dq[dt]);
+            }
+    };
+    dma_tile(k0s, kbase, C3, 0, T, w, lane);
+    dma_tile(v0s, vbase, C3, 0, T, w, lane);
+    dma_tile(k1s, kbase, C3, min(KB, klast), T, w, lane);
+    dma_tile(v1s, vbase, C3, min(KB, klast), T, w, lane);
+    int kb = 0;
+    for (; kb + 3 <= nkb; kb += 3) {
+        step(k0s, v0s, k2s, v2s, kb);
+        step(k1s, v1s, k0s, v0s, kb + 1);
+        step(k2s, v2s, k1s, v1s, kb + 2);
     }
+    if (kb < nkb) { step(k0s, v0s, k2s, v2s, kb); kb++; }
+    if (kb < nkb) step(k1s, v1s, k0s, v0s, kb);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
+
     if (qok) {
         bf16* row = dqkv + ((int64_t)b * T + q) * C3 + h * HS;
 #pragma unroll
@@ -336,19 +341,27 @@ __global__ __launch_bounds__(256) void flash_bwd_dq_kernel(bf16* dqkv, float* Do
 }
 
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void flash_bwd_dkdv_kernel(bf16* dqkv, const float* Din, const bf16* dout,
+// Per-query statistics of a 64-query block, one 1 KB load per wave into the
+// wave's own region: lanes 0..15 bring lse[q0 .. q0+63], lanes 16..31 D[...],
+// lanes 32..63 repeat lane 0's read (unused).  Needs T % 64 == 0.
+DEVI void dma_stats(float* region, const float* lse, const float* D, int64_t rbase, int q0, int lane) {
+    const float* src = lane < 16 ? lse + rbase + q0 + 4 * lane
+                     : lane < 32 ? D + rbase + q0 + 4 * (lane - 16) : lse + rbase + q0;
+    __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)region, 16, 0, 0);
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void flash_bwd_dkdv_kernel(bf16* dqkv, const float* Din, const bf16* dout,
                                                              const bf16* qkv, const float* lse, int T, int C, int NH) {
-    __shared__ __attribute__((aligned(16))) bf16 Qs[2][KB * LP];
-    __shared__ __attribute__((aligned(16))) bf16 Qt[2][HS * LP];
-    __shared__ __attribute__((aligned(16))) bf16 Os[2][KB * LP];  // dO natural
-    __shared__ __attribute__((aligned(16))) bf16 Ot[2][HS * LP];  // dO transposed
-    __shared__ __attribute__((aligned(16))) float sl[2][KB], sd[2][KB];
+    __shared__ __attribute__((aligned(1024))) bf16 q0s[TILE], q1s[TILE], q2s[TILE];
+    __shared__ __attribute__((aligned(1024))) bf16 o0s[TILE], o1s[TILE], o2s[TILE];  // dO
+    __shared__ __attribute__((aligned(1024))) float st0[4 * 256], st1[4 * 256], st2[4 * 256];
     const int kblk = blockIdx.x;  // the first key blocks see the most queries: launched first
     const int h = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hi = lane >> 5, lq = lane & 31;
     const int64_t C3 = 3 * (int64_t)C;
     const bf16* base = qkv + (int64_t)b * T * C3;
-    const bf16* dbase = dout + (int64_t)b * T * C;
+    const bf16* qbase = base + h * HS;
+    const bf16* dbase = dout + (int64_t)b * T * C + h * HS;
     const int k0 = kblk * QB + w * 32;
     const int key = k0 + lq;
 
@@ -364,86 +377,72 @@ __global__ __launch_bounds__(256) void flash_bwd_dkdv_kernel(bf16* dqkv, const f
     f32x16 dk[2] = {zero16(), zero16()}, dv[2] = {zero16(), zero16()};
     const float sc = 0.125f * LOG2E;
     const int64_t rbase = ((int64_t)b * NH + h) * T;
-
     const int qstart = (kblk * QB / KB) * KB;
     const int nqb = (T - qstart + KB - 1) / KB;
-    u32x4 reg[8];
-    float rl = 0.f, rd = 0.f;
-    auto load = [&](int qs0) {
-        if (tid < 64) blk_load(reg, base + h * HS, C3, qs0, T, tid);
-        else if (tid < 128) blk_load(reg, dbase + h * HS, C, qs0, T, tid - 64);
-        else if (tid < 192) {
-            const int qq = min(qs0 + tid - 128, T - 1);
-            rl = lse[rbase + qq] * LOG2E;
-            rd = Din[rbase + qq];
-        }
+    const int qlast = qstart + (nqb - 1) * KB;
+
+    auto load = [&](bf16* Q, bf16* O, float* S, int qs0) {
+        dma_tile(Q, qbase, C3, qs0, T, w, lane);
+        dma_tile(O, dbase, C, qs0, T, w, lane);
+        dma_stats(S + w * 256, lse, Din, rbase, qs0, lane);
     };
-    auto store = [&](int buf) {
-        if (tid < 64) {
-            blk_store_nat(reg, Qs[buf], tid);
-            blk_store_tr(reg, Qt[buf], tid);
-        } else if (tid < 128) {
-            blk_store_nat(reg, Os[buf], tid - 64);
-            blk_store_tr(reg, Ot[buf], tid - 64);
-        } else if (tid < 192) {
-            sl[buf][tid - 128] = rl;
-            sd[buf][tid - 128] = rd;
-        }
-    };
-    load(qstart);
-    store(0);
-    __syncthreads();
-    for (int i = 0; i < nqb; i++) {
-        const int qs0 = qstart + i * KB, cur = i & 1;
-        load(qstart + min(i + 1, nqb - 1) * KB);
-        if (qs0 + KB - 1 >= k0) {  // else every query of the block precedes every key of the wave
-            f32x16 s[2], dp[2];
+    auto step = [&](const bf16* Qs, const bf16* Os, const float* S, bf16* NQ, bf16* NO, float* NS_, int i) {
+        STAGE_SYNC(5);
+        load(NQ, NO, NS_, min(qstart + (i + NS - 1) * KB, qlast));
+        const int qs0 = qstart + i * KB;
+        if (qs0 + KB - 1 < k0) return;  // every query of the block precedes every key of the wave
+        const float* sl = S + w * 256;
+        const float* sd = sl + 64;
+        // one 32-query half at a time keeps only 32 score registers live
 #pragma unroll
-            for (int t = 0; t < 2; t++) {
-                s[t] = zero16();
-                dp[t] = zero16();
+        for (int t = 0; t < 2; t++) {
+            f32x16 s = zero16(), dp = zero16();
 #pragma unroll
-                for (int ks = 0; ks < 4; ks++) {
-                    const int off = (t * 32 + lq) * LP + ks * 16 + hi * 8;
-                    s[t] = mfma(*reinterpret_cast<const bf16x8*>(&Qs[cur][off]), kf[ks], s[t]);
-                    dp[t] = mfma(*reinterpret_cast<const bf16x8*>(&Os[cur][off]), vf[ks], dp[t]);
-                }
+            for (int ks = 0; ks < 4; ks++) {
+                s = mfma(frag_row(Qs, t * 32 + lq, ks * 2 + hi), kf[ks], s);
+                dp = mfma(frag_row(Os, t * 32 + lq, ks * 2 + hi), vf[ks], dp);
             }
-            // s[t][r]: query qs0 + t*32 + acc_row(r), key `key`; registers 4g..4g+3
+            // s[r]: query qs0 + t*32 + acc_row(r), key `key`; registers 4g..4g+3
             // cover 4 consecutive queries, so their lse and D come as one float4
 #pragma unroll
-            for (int t = 0; t < 2; t++)
+            for (int g = 0; g < 4; g++) {
+                const int ql0 = t * 32 + 8 * g + 4 * hi;
+                const float4 L4 = *reinterpret_cast<const float4*>(sl + ql0);
+                const float4 D4 = *reinterpret_cast<const float4*>(sd + ql0);
+                const float Lv[4] = {L4.x, L4.y, L4.z, L4.w}, Dv[4] = {D4.x, D4.y, D4.z, D4.w};
 #pragma unroll
-                for (int g = 0; g < 4; g++) {
-                    const int ql0 = t * 32 + 8 * g + 4 * hi;
-                    const float4 L4 = *reinterpret_cast<const float4*>(&sl[cur][ql0]);
-                    const float4 D4 = *reinterpret_cast<const float4*>(&sd[cur][ql0]);
-                    const float Lv[4] = {L4.x, L4.y, L4.z, L4.w}, Dv[4] = {D4.x, D4.y, D4.z, D4.w};
-#pragma unroll
-                    for (int e = 0; e < 4; e++) {
-                        const int r = 4 * g + e;
-                        const int qq = qs0 + ql0 + e;
-                        const float p = (key > qq || qq >= T || key >= T) ? 0.f : exp2f(s[t][r] * sc - Lv[e]);
-                        s[t][r] = p;
-                        dp[t][r] = p * (dp[t][r] - Dv[e]);
-                    }
+                for (int e = 0; e < 4; e++) {
+                    const int r = 4 * g + e;
+                    const int qq = qs0 + ql0 + e;
+                    const float pr = (key > qq || key >= T) ? 0.f : exp2f(s[r] * sc - Lv[e] * LOG2E);
+                    s[r] = pr;
+                    dp[r] = pr * (dp[r] - Dv[e]);
                 }
+            }
 #pragma unroll
-            for (int t = 0; t < 2; t++)
+            for (int j = 0; j < 2; j++) {
+                const bf16x8 pa = to_bf16x8(s, 8 * j);
+                const bf16x8 da = to_bf16x8(dp, 8 * j);
 #pragma unroll
-                for (int j = 0; j < 2; j++) {
-                    const bf16x8 pa = to_bf16x8(s[t], 8 * j);
-                    const bf16x8 da = to_bf16x8(dp[t], 8 * j);
-#pragma unroll
-                    for (int dt = 0; dt < 2; dt++) {
-                        dv[dt] = mfma(pa, a_from_tr(&Ot[cur][(dt * 32 + lq) * LP], t * 32, j, hi), dv[dt]);
-                        dk[dt] = mfma(da, a_from_tr(&Qt[cur][(dt * 32 + lq) * LP], t * 32, j, hi), dk[dt]);
-                    }
+                for (int dt = 0; dt < 2; dt++) {
+                    dv[dt] = mfma(pa, frag_tr(Os, t * 32, j, dt, lane), dv[dt]);
+                    dk[dt] = mfma(da, frag_tr(Qs, t * 32, j, dt, lane), dk[dt]);
                 }
+            }
         }
-        store(cur ^ 1);
-        __syncthreads();
+    };
+    load(q0s, o0s, st0, qstart);
+    load(q1s, o1s, st1, min(qstart + KB, qlast));
+    int i = 0;
+    for (; i + 3 <= nqb; i += 3) {
+        step(q0s, o0s, st0, q2s, o2s, st2, i);
+        step(q1s, o1s, st1, q0s, o0s, st0, i + 1);
+        step(q2s, o2s, st2, q1s, o1s, st1, i + 2);
     }
+    if (i < nqb) { step(q0s, o0s, st0, q2s, o2s, st2, i); i++; }
+    if (i < nqb) step(q1s, o1s, st1, q0s, o0s, st0, i);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
+
     // dk[dt][r], dv[dt][r]: key k0 + acc_row(r), channel dt*32 + lq
 #pragma unroll
     for (int r = 0; r < 16; r++) {
@@ -459,10 +458,12 @@ __global__ __launch_bounds__(256) void flash_bwd_dkdv_kernel(bf16* dqkv, const f
     }
 }
 
+#undef STAGE_SYNC
+
 }  // namespace
 
 hipError_t flash_attention_fwd(bf16* out, float* lse, const bf16* qkv, int B, int T, int C, int NH, hipStream_t s) {
-    if (C / NH != HS || C % NH) return hipErrorInvalidValue;
+    if (C / NH != HS || C % NH || T % KB) return hipErrorInvalidValue;
     dim3 grid((T + QB - 1) / QB, NH, B);
     flash_fwd_kernel<<<grid, 256, 0, s>>>(out, lse, qkv, T, C, NH);
     return hipGetLastError();
@@ -470,7 +471,7 @@ hipError_t flash_attention_fwd(bf16* out, float* lse, const bf16* qkv, int B, in
 
 hipError_t flash_attention_bwd(bf16* dqkv, const bf16* dout, const bf16* qkv, const bf16* out, const float* lse,
                                float* dbuf, int B, int T, int C, int NH, hipStream_t s) {
-    if (C / NH != HS || C % NH) return hipErrorInvalidValue;
+    if (C / NH != HS || C % NH || T % KB) return hipErrorInvalidValue;
     dim3 grid((T + QB - 1) / QB, NH, B);
     flash_bwd_dq_kernel<<<grid, 256, 0, s>>>(dqkv, dbuf, dout, qkv, out, lse, T, C, NH);
     flash_bwd_dkdv_kernel<<<grid, 256, 0, s>>>(dqkv, dbuf, dout, qkv, lse, T, C, NH);

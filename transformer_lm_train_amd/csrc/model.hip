@@ -88,8 +88,8 @@ int validate(const gpt2_config* c) {
     if (c->channels > 4096) return fail(GPT2_EINVAL, "channels <= 4096 required");
     if (c->precision == GPT2_BF16_MIXED) {
         if (hs != 64) return fail(GPT2_EINVAL, "BF16_MIXED needs head size 64");
-        if (c->channels % 64 || c->padded_vocab_size % 64 || ((int64_t)c->batch_size * c->seq_len) % 64)
-            return fail(GPT2_EINVAL, "BF16_MIXED needs C, Vp and B*T to be multiples of 64");
+        if (c->channels % 64 || c->padded_vocab_size % 64 || c->seq_len % 64)
+            return fail(GPT2_EINVAL, "BF16_MIXED needs C, Vp and T to be multiples of 64");
     }
     return GPT2_OK;
 }

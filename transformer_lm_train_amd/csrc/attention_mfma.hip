@@ -14,7 +14,16 @@
 // the query's keys sits in lane l ^ 32: one shuffle combines them).  The
 // accumulator registers 8j..8j+7 of a lane hold 8 distinct keys, which is
 // exactly the B-operand shape of the next product (O^T = V^T P^T), so P
-// never leaves registers; V^T is staged in LDS key-contiguous to match.
+// never leaves registers.
+//
+// The softmax work per score element is what bounds these kernels (the
+// exponential runs at a quarter of the FMA rate), so each element costs the
+// minimum: one FMA into the raw v_exp_f32 (arguments are <= 0, so the
+// denormal range handling of exp2f is not needed), the causal mask only on
+// the one diagonal block of each wave, and in the forward the output is
+// rescaled only when the running max grows by more than 2^8 (the final
+// normalisation uses the same stale max for numerator and denominator, and
+// probabilities up to 256 are harmless in fp32 and bf16).
 //
 // Tiles stream through LDS in their natural [row][64] layout (16-byte chunk c
 // of row r in slot c ^ (r & 7)), loaded by global_load_lds_dwordx4 straight
@@ -41,6 +50,7 @@ constexpr int KB = 64;   // rows streamed per inner step
 constexpr int NS = 3;    // LDS stages
 constexpr int TILE = KB * HS;  // elements of one 64 x 64 tile
 constexpr float LOG2E = 1.4426950408889634f;
+constexpr float RESCALE_LOG2 = 8.f;  // lazy rescale threshold of the running max (log2 units)
 constexpr float LN2 = 0.6931471805599453f;
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -74,17 +84,19 @@ DEVI u32x4 ld_row(const bf16* p, bool ok) {
 template <int N> constexpr int vmcnt_imm() { return (N & 15) | ((N >> 4) << 14) | (7 << 4); }
 
 // rows [r0, r0+64) x 64 channels of a [*, ld] matrix into a swizzled tile;
-// each of the 4 waves issues 2 loads of 1 KB.  Rows at or past `rows` re-read
-// row rows-1: every consumer masks them, so they only need to be finite.
-DEVI void dma_tile(bf16* tile, const bf16* src, int64_t ld, int r0, int rows, int wave, int lane) {
+// each of the 4 waves issues 2 loads of 1 KB.  Callers stream whole 64-row
+// blocks of a sequence whose length is a multiple of 64, so every row read
+// exists.  `src` already points at row 0 of this wave's lanes
+// (see dma_lane_ptr); the row offset is wave-uniform.
+DEVI const bf16* dma_lane_ptr(const bf16* base, int ld, int wave, int lane) {
     const int c = (lane & 7) ^ (lane >> 3);  // chunk landing in slot lane&7 of row lane>>3 (mod 8)
+    return base + (wave * 16 + (lane >> 3)) * ld + c * 8;
+}
+DEVI void dma_tile(bf16* tile, const bf16* src, int ld, int r0, int wave) {
 #pragma unroll
-    for (int i = 0; i < 2; i++) {
-        const int blk = wave * 2 + i;
-        const int r = min(r0 + blk * 8 + (lane >> 3), rows - 1);
-        __builtin_amdgcn_global_load_lds((glb_void_t*)(src + (int64_t)r * ld + c * 8), (lds_void_t*)(tile + blk * 512),
+    for (int i = 0; i < 2; i++)
+        __builtin_amdgcn_global_load_lds((glb_void_t*)(src + (r0 + i * 8) * ld), (lds_void_t*)(tile + (wave * 2 + i) * 512),
                                          16, 0, 0);
-    }
 }
 
 // 8 consecutive channels chunk*8.. of tile row `row` (one 16-byte read)
@@ -114,6 +126,9 @@ DEVI bf16x8 frag_tr(const bf16* tile, int t32, int j, int dt, int lane) {
 
 // accumulator register r of lane half hi covers row 8*(r/4) + 4*hi + r%4
 DEVI int acc_row(int r, int hi) { return ((r >> 2) << 3) + (hi << 2) + (r & 3); }
+DEVI constexpr int acc_off(int r) { return ((r >> 2) << 3) + (r & 3); }  // acc_row less the half term
+
+DEVI float exp2_raw(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // The stages are distinct __shared__ arrays so that alias analysis keeps the
 // reads of one stage independent of the loads in flight into another; each
@@ -126,17 +141,17 @@ DEVI int acc_row(int r, int hi) { return ((r >> 2) << 3) + (hi << 2) + (r & 3); 
     } while (0)
 
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void flash_fwd_kernel(bf16* out, float* lse, const bf16* qkv, int T, int C, int NH) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void flash_fwd_kernel(bf16* out, float* lse, const bf16* qkv, int T, int C, int NH) {
     __shared__ __attribute__((aligned(1024))) bf16 k0s[TILE], k1s[TILE], k2s[TILE];
     __shared__ __attribute__((aligned(1024))) bf16 v0s[TILE], v1s[TILE], v2s[TILE];
     const int nqb = (T + QB - 1) / QB;
     const int qblk = nqb - 1 - (int)blockIdx.x;  // longest rows first
     const int h = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hi = lane >> 5, lq = lane & 31;
-    const int64_t C3 = 3 * (int64_t)C;
+    const int C3 = 3 * C;
     const bf16* base = qkv + (int64_t)b * T * C3;
-    const bf16* kbase = base + C + h * HS;
-    const bf16* vbase = base + 2 * C + h * HS;
+    const bf16* kbase = dma_lane_ptr(base + C + h * HS, C3, w, lane);
+    const bf16* vbase = dma_lane_ptr(base + 2 * C + h * HS, C3, w, lane);
     const int q0 = qblk * QB + w * 32;
     const int q = q0 + lq;
 
@@ -157,10 +172,12 @@ __global__ __launch_bounds__(256) void flash_fwd_kernel(bf16* out, float* lse, c
     auto step = [&](const bf16* Ks, const bf16* Vs, bf16* NK, bf16* NV, int kb) {
         STAGE_SYNC(4);
         const int kn = min((kb + NS - 1) * KB, klast);
-        dma_tile(NK, kbase, C3, kn, T, w, lane);
-        dma_tile(NV, vbase, C3, kn, T, w, lane);
+        dma_tile(NK, kbase, C3, kn, w);
+        dma_tile(NV, vbase, C3, kn, w);
         const int k0 = kb * KB;
-        if (k0 > q0 + 31) return;  // every key of the block is in the future of every query of the wave
+        // every key of the block is in the future of every query of the wave,
+        // or the wave's queries are all past the end of the sequence
+        if (k0 > q0 + 31 || q0 >= T) return;
         f32x16 s[2];
 #pragma unroll
         for (int t = 0; t < 2; t++) {
@@ -168,34 +185,38 @@ __global__ __launch_bounds__(256) void flash_fwd_kernel(bf16* out, float* lse, c
 #pragma unroll
             for (int ks = 0; ks < 4; ks++) s[t] = mfma(frag_row(Ks, t * 32 + lq, ks * 2 + hi), qf[ks], s[t]);
         }
-        float mloc = -INFINITY;
+        if (k0 + KB - 1 > q0) {  // the wave's diagonal block: key k0 + t*32 + acc_row(r) > q is masked
 #pragma unroll
-        for (int t = 0; t < 2; t++)
+            for (int t = 0; t < 2; t++) {
+                const int thr = q - k0 - t * 32 - 4 * hi;
 #pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const int key = k0 + t * 32 + acc_row(r, hi);
-                float x = s[t][r] * sc;
-                if (key > q || key >= T) x = -INFINITY;
-                s[t][r] = x;
-                mloc = fmaxf(mloc, x);
+                for (int r = 0; r < 16; r++)
+                    if (acc_off(r) > thr) s[t][r] = -INFINITY;
             }
-        mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-        const float m_new = fmaxf(m_run, mloc);
-        const float alpha = exp2f(m_run - m_new);
-        float lsum = 0.f;
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int t = 0; t < 2; t++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) mx = fmaxf(mx, s[t][r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * sc;
+        if (__any(mx > m_run + RESCALE_LOG2)) {
+            const float m_new = fmaxf(m_run, mx);
+            const float alpha = exp2_raw(m_run - m_new);  // 0 on the first block (m_run = -inf)
+            l_run *= alpha;
+#pragma unroll
+            for (int r = 0; r < 16; r++) { o[0][r] *= alpha; o[1][r] *= alpha; }
+            m_run = m_new;
+        }
+        const float nm = -m_run;
 #pragma unroll
         for (int t = 0; t < 2; t++)
 #pragma unroll
             for (int r = 0; r < 16; r++) {
-                const float pr = exp2f(s[t][r] - m_new);
+                const float pr = exp2_raw(fmaf(s[t][r], sc, nm));
                 s[t][r] = pr;
-                lsum += pr;
+                l_run += pr;  // this half's keys only: the halves are combined at the end
             }
-        lsum += __shfl_xor(lsum, 32, 64);
-        l_run = l_run * alpha + lsum;
-        m_run = m_new;
-#pragma unroll
-        for (int r = 0; r < 16; r++) { o[0][r] *= alpha; o[1][r] *= alpha; }
 #pragma unroll
         for (int t = 0; t < 2; t++)
 #pragma unroll
@@ -205,10 +226,10 @@ __global__ __launch_bounds__(256) void flash_fwd_kernel(bf16* out, float* lse, c
                 for (int dt = 0; dt < 2; dt++) o[dt] = mfma(frag_tr(Vs, t * 32, j, dt, lane), pb, o[dt]);
             }
     };
-    dma_tile(k0s, kbase, C3, 0, T, w, lane);
-    dma_tile(v0s, vbase, C3, 0, T, w, lane);
-    dma_tile(k1s, kbase, C3, min(KB, klast), T, w, lane);
-    dma_tile(v1s, vbase, C3, min(KB, klast), T, w, lane);
+    dma_tile(k0s, kbase, C3, 0, w);
+    dma_tile(v0s, vbase, C3, 0, w);
+    dma_tile(k1s, kbase, C3, min(KB, klast), w);
+    dma_tile(v1s, vbase, C3, min(KB, klast), w);
     int kb = 0;
     for (; kb + 3 <= nkb; kb += 3) {
         step(k0s, v0s, k2s, v2s, kb);
@@ -219,6 +240,7 @@ __global__ __launch_bounds__(256) void flash_fwd_kernel(bf16* out, float* lse, c
     if (kb < nkb) step(k1s, v1s, k0s, v0s, kb);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());  // no load may still be writing LDS at exit
 
+    l_run += __shfl_xor(l_run, 32, 64);
     if (q < T) {
         const float inv = 1.f / l_run;
         bf16* orow = out + ((int64_t)b * T + q) * C + h * HS;
@@ -231,23 +253,25 @@ __global__ __launch_bounds__(256) void flash_fwd_kernel(bf16* out, float* lse, c
                 for (int i = 0; i < 4; i++) v[i] = (bf16)(o[dt][4 * g + i] * inv);
                 *reinterpret_cast<bf16x4*>(orow + dt * 32 + 8 * g + 4 * hi) = v;
             }
-        if (hi == 0) lse[((int64_t)b * NH + h) * T + q] = (m_run + log2f(l_run)) * LN2;
+        if (hi == 0) lse[((int64_t)b * NH + h) * T + q] = (m_run + __log2f(l_run)) * LN2;
     }
 }
 
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void flash_bwd_dq_kernel(bf16* dqkv, float* Dout, const bf16* dout, const bf16* qkv,
-                                                           const bf16* out, const float* lse, int T, int C, int NH) {
+// Dout[row] = rowsum(dO o O) and Lout[row] = -lse * log2(e), for the dK/dV kernel
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void flash_bwd_dq_kernel(bf16* dqkv, float* Dout, float* Lout, const bf16* dout,
+                                                           const bf16* qkv, const bf16* out, const float* lse, int T,
+                                                           int C, int NH) {
     __shared__ __attribute__((aligned(1024))) bf16 k0s[TILE], k1s[TILE], k2s[TILE];
     __shared__ __attribute__((aligned(1024))) bf16 v0s[TILE], v1s[TILE], v2s[TILE];
     const int nqb = (T + QB - 1) / QB;
     const int qblk = nqb - 1 - (int)blockIdx.x;
     const int h = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hi = lane >> 5, lq = lane & 31;
-    const int64_t C3 = 3 * (int64_t)C;
+    const int C3 = 3 * C;
     const bf16* base = qkv + (int64_t)b * T * C3;
-    const bf16* kbase = base + C + h * HS;
-    const bf16* vbase = base + 2 * C + h * HS;
+    const bf16* kbase = dma_lane_ptr(base + C + h * HS, C3, w, lane);
+    const bf16* vbase = dma_lane_ptr(base + 2 * C + h * HS, C3, w, lane);
     const int q0 = qblk * QB + w * 32;
     const int q = q0 + lq;
     const bool qok = q < T;
@@ -268,8 +292,8 @@ __global__ __launch_bounds__(256) void flash_bwd_dq_kernel(bf16* dqkv, float* Do
     }
     const float Dq = dsum + __shfl_xor(dsum, 32, 64);
     const int64_t ri = ((int64_t)b * NH + h) * T + q;
-    if (qok && hi == 0) Dout[ri] = Dq;
-    const float lse2 = qok ? lse[ri] * LOG2E : 0.f;
+    const float nl2 = qok ? -lse[ri] * LOG2E : 0.f;
+    if (qok && hi == 0) { Dout[ri] = Dq; Lout[ri] = nl2; }
     const float sc = 0.125f * LOG2E;
 
     f32x16 dq[2] = {zero16(), zero16()};
@@ -280,10 +304,10 @@ __global__ __launch_bounds__(256) void flash_bwd_dq_kernel(bf16* dqkv, float* Do
     auto step = [&](const bf16* Ks, const bf16* Vs, bf16* NK, bf16* NV, int kb) {
         STAGE_SYNC(4);
         const int kn = min((kb + NS - 1) * KB, klast);
-        dma_tile(NK, kbase, C3, kn, T, w, lane);
-        dma_tile(NV, vbase, C3, kn, T, w, lane);
+        dma_tile(NK, kbase, C3, kn, w);
+        dma_tile(NV, vbase, C3, kn, w);
         const int k0 = kb * KB;
-        if (k0 > q0 + 31) return;
+        if (k0 > q0 + 31 || q0 >= T) return;
         f32x16 s[2], dp[2];
 #pragma unroll
         for (int t = 0; t < 2; t++) {
@@ -295,12 +319,20 @@ __global__ __launch_bounds__(256) void flash_bwd_dq_kernel(bf16* dqkv, float* Do
                 dp[t] = mfma(frag_row(Vs, t * 32 + lq, ks * 2 + hi), dof[ks], dp[t]);
             }
         }
+        if (k0 + KB - 1 > q0) {  // diagonal block
+#pragma unroll
+            for (int t = 0; t < 2; t++) {
+                const int thr = q - k0 - t * 32 - 4 * hi;
+#pragma unroll
+                for (int r = 0; r < 16; r++)
+                    if (acc_off(r) > thr) s[t][r] = -INFINITY;
+            }
+        }
 #pragma unroll
         for (int t = 0; t < 2; t++)
 #pragma unroll
             for (int r = 0; r < 16; r++) {
-                const int key = k0 + t * 32 + acc_row(r, hi);
-                const float pr = (key > q || key >= T || !qok) ? 0.f : exp2f(s[t][r] * sc - lse2);
+                const float pr = exp2_raw(fmaf(s[t][r], sc, nl2));
                 s[t][r] = pr * (dp[t][r] - Dq);  // dS^T
             }
 #pragma unroll
@@ -312,10 +344,10 @@ __global__ __launch_bounds__(256) void flash_bwd_dq_kernel(bf16* dqkv, float* Do
                 for (int dt = 0; dt < 2; dt++) dq[dt] = mfma(frag_tr(Ks, t * 32, j, dt, lane), dsb, dq[dt]);
             }
     };
-    dma_tile(k0s, kbase, C3, 0, T, w, lane);
-    dma_tile(v0s, vbase, C3, 0, T, w, lane);
-    dma_tile(k1s, kbase, C3, min(KB, klast), T, w, lane);
-    dma_tile(v1s, vbase, C3, min(KB, klast), T, w, lane);
+    dma_tile(k0s, kbase, C3, 0, w);
+    dma_tile(v0s, vbase, C3, 0, w);
+    dma_tile(k1s, kbase, C3, min(KB, klast), w);
+    dma_tile(v1s, vbase, C3, min(KB, klast), w);
     int kb = 0;
     for (; kb + 3 <= nkb; kb += 3) {
         step(k0s, v0s, k2s, v2s, kb);
@@ -342,26 +374,27 @@ __global__ __launch_bounds__(256) void flash_bwd_dq_kernel(bf16* dqkv, float* Do
 
 // ---------------------------------------------------------------------------
 // Per-query statistics of a 64-query block, one 1 KB load per wave into the
-// wave's own region: lanes 0..15 bring lse[q0 .. q0+63], lanes 16..31 D[...],
-// lanes 32..63 repeat lane 0's read (unused).  Needs T % 64 == 0.
-DEVI void dma_stats(float* region, const float* lse, const float* D, int64_t rbase, int q0, int lane) {
-    const float* src = lane < 16 ? lse + rbase + q0 + 4 * lane
-                     : lane < 32 ? D + rbase + q0 + 4 * (lane - 16) : lse + rbase + q0;
-    __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)region, 16, 0, 0);
+// wave's own region: lanes 0..15 bring L[q0 .. q0+63] (-lse log2 e), lanes
+// 16..31 D[...], lanes 32..63 repeat lane 0's read (unused).  Needs T % 64 == 0.
+DEVI const float* stats_lane_ptr(const float* L, const float* D, int64_t rbase, int lane) {
+    return lane < 16 ? L + rbase + 4 * lane : lane < 32 ? D + rbase + 4 * (lane - 16) : L + rbase;
+}
+DEVI void dma_stats(float* region, const float* src, int q0) {
+    __builtin_amdgcn_global_load_lds((glb_void_t*)(src + q0), (lds_void_t*)region, 16, 0, 0);
 }
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void flash_bwd_dkdv_kernel(bf16* dqkv, const float* Din, const bf16* dout,
-                                                             const bf16* qkv, const float* lse, int T, int C, int NH) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void flash_bwd_dkdv_kernel(
+    bf16* dqkv, const float* Din, const float* Lin, const bf16* dout, const bf16* qkv, int T, int C, int NH) {
     __shared__ __attribute__((aligned(1024))) bf16 q0s[TILE], q1s[TILE], q2s[TILE];
     __shared__ __attribute__((aligned(1024))) bf16 o0s[TILE], o1s[TILE], o2s[TILE];  // dO
     __shared__ __attribute__((aligned(1024))) float st0[4 * 256], st1[4 * 256], st2[4 * 256];
     const int kblk = blockIdx.x;  // the first key blocks see the most queries: launched first
     const int h = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hi = lane >> 5, lq = lane & 31;
-    const int64_t C3 = 3 * (int64_t)C;
+    const int C3 = 3 * C;
     const bf16* base = qkv + (int64_t)b * T * C3;
-    const bf16* qbase = base + h * HS;
-    const bf16* dbase = dout + (int64_t)b * T * C + h * HS;
+    const bf16* qbase = dma_lane_ptr(base + h * HS, C3, w, lane);
+    const bf16* dbase = dma_lane_ptr(dout + (int64_t)b * T * C + h * HS, C, w, lane);
     const int k0 = kblk * QB + w * 32;
     const int key = k0 + lq;
 
@@ -377,20 +410,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     f32x16 dk[2] = {zero16(), zero16()}, dv[2] = {zero16(), zero16()};
     const float sc = 0.125f * LOG2E;
     const int64_t rbase = ((int64_t)b * NH + h) * T;
+    const float* sbase = stats_lane_ptr(Lin, Din, rbase, lane);
     const int qstart = (kblk * QB / KB) * KB;
     const int nqb = (T - qstart + KB - 1) / KB;
     const int qlast = qstart + (nqb - 1) * KB;
 
     auto load = [&](bf16* Q, bf16* O, float* S, int qs0) {
-        dma_tile(Q, qbase, C3, qs0, T, w, lane);
-        dma_tile(O, dbase, C, qs0, T, w, lane);
-        dma_stats(S + w * 256, lse, Din, rbase, qs0, lane);
+        dma_tile(Q, qbase, C3, qs0, w);
+        dma_tile(O, dbase, C, qs0, w);
+        dma_stats(S + w * 256, sbase, qs0);
     };
     auto step = [&](const bf16* Qs, const bf16* Os, const float* S, bf16* NQ, bf16* NO, float* NS_, int i) {
         STAGE_SYNC(5);
         load(NQ, NO, NS_, min(qstart + (i + NS - 1) * KB, qlast));
         const int qs0 = qstart + i * KB;
-        if (qs0 + KB - 1 < k0) return;  // every query of the block precedes every key of the wave
+        // every query of the block precedes every key of the wave, or the
+        // wave's keys are all past the end of the sequence
+        if (qs0 + KB - 1 < k0 || k0 >= T) return;
+        const bool diag = qs0 < k0 + 31;
         const float* sl = S + w * 256;
         const float* sd = sl + 64;
         // one 32-query half at a time keeps only 32 score registers live
@@ -403,7 +440,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 dp = mfma(frag_row(Os, t * 32 + lq, ks * 2 + hi), vf[ks], dp);
             }
             // s[r]: query qs0 + t*32 + acc_row(r), key `key`; registers 4g..4g+3
-            // cover 4 consecutive queries, so their lse and D come as one float4
+            // cover 4 consecutive queries, so their L and D come as one float4
+            if (diag) {  // query qs0 + t*32 + acc_row(r) < key is masked
+                const int thr = key - qs0 - t * 32 - 4 * hi;
+#pragma unroll
+                for (int r = 0; r < 16; r++)
+                    if (acc_off(r) < thr) s[r] = -INFINITY;
+            }
 #pragma unroll
             for (int g = 0; g < 4; g++) {
                 const int ql0 = t * 32 + 8 * g + 4 * hi;
@@ -413,8 +456,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
                     const int r = 4 * g + e;
-                    const int qq = qs0 + ql0 + e;
-                    const float pr = (key > qq || key >= T) ? 0.f : exp2f(s[r] * sc - Lv[e] * LOG2E);
+                    const float pr = exp2_raw(fmaf(s[r], sc, Lv[e]));
                     s[r] = pr;
                     dp[r] = pr * (dp[r] - Dv[e]);
                 }
@@ -473,7 +515,8 @@ hipError_t flash_attention_bwd(bf16* dqkv, const bf16* dout, const bf16* qkv, co
                                float* dbuf, int B, int T, int C, int NH, hipStream_t s) {
     if (C / NH != HS || C % NH || T % KB) return hipErrorInvalidValue;
     dim3 grid((T + QB - 1) / QB, NH, B);
-    flash_bwd_dq_kernel<<<grid, 256, 0, s>>>(dqkv, dbuf, dout, qkv, out, lse, T, C, NH);
-    flash_bwd_dkdv_kernel<<<grid, 256, 0, s>>>(dqkv, dbuf, dout, qkv, lse, T, C, NH);
+    const int64_t rows = (int64_t)B * NH * T;
+    flash_bwd_dq_kernel<<<grid, 256, 0, s>>>(dqkv, dbuf, dbuf + rows, dout, qkv, out, lse, T, C, NH);
+    flash_bwd_dkdv_kernel<<<grid, 256, 0, s>>>(dqkv, dbuf, dbuf + rows, dout, qkv, T, C, NH);
     return hipGetLastError();
 }

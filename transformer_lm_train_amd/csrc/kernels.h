@@ -90,7 +90,8 @@ hipError_t attention_fwd(T* out, float* lse, const T* qkv, int B, int T_, int C,
 template <typename T>
 hipError_t attention_bwd(T* dqkv, const T* dout, const T* qkv, const T* out, const float* lse, float* dbuf,
                          int B, int T_, int C, int NH, hipStream_t s);
-// head size 64, bf16, MFMA flash kernels (dbuf receives D = rowsum(dO o O))
+// head size 64, bf16, MFMA flash kernels, T % 64 == 0; dbuf holds 2*B*NH*T
+// floats: D = rowsum(dO o O), then -lse*log2(e), one per (b, h, t)
 hipError_t flash_attention_fwd(bf16* out, float* lse, const bf16* qkv, int B, int T_, int C, int NH, hipStream_t s);
 hipError_t flash_attention_bwd(bf16* dqkv, const bf16* dout, const bf16* qkv, const bf16* out, const float* lse,
                                float* dbuf, int B, int T_, int C, int NH, hipStream_t s);

@@ -135,7 +135,7 @@ Layout make_layout(const gpt2_config& c) {
     L.dres = add(A * BT * C);
     L.dbig = add(A * BT * 4 * C);
     L.dmid = add(A * BT * C);
-    L.attD = add(4 * BT * c.num_heads);
+    L.attD = add(2 * 4 * BT * c.num_heads);  // D and the base-2 lse of every attention row
     L.partial = add(4 * 2048 * C);
     L.norm_partial = add(4 * 1024);
     L.scalars = add(64);

@@ -50,20 +50,24 @@ DEVI float wave_max(float x) {
     return x;
 }
 
-// tanh(x) = 1 - 2 / (exp(2x) + 1): the hardware exp and reciprocal, exact to
-// a few fp32 ulps, and saturating cleanly to +-1 (exp overflows to inf or
-// underflows to 0; the denominator never falls below 1)
-DEVI float tanh_fast(float x) { return 1.f - __fdividef(2.f, __expf(2.f * x) + 1.f); }
-
-// GELU, tanh approximation: 0.5 u (1 + tanh(k (u + 0.044715 u^3))), k = sqrt(2/pi)
+// GELU, tanh approximation: 0.5 u (1 + tanh(v/2)) with v = 2k (u + 0.044715 u^3),
+// k = sqrt(2/pi).  Since 0.5 (1 + tanh(v/2)) is the logistic sigmoid s(v),
+// gelu(u) = u s(v) and gelu'(u) = s + u s (1 - s) v', each from one exp2 and
+// one reciprocal: s = 1 / (1 + 2^(-v log2 e)).  At the tails 2^(..) goes to 0
+// or +inf, s to 1 or 0, and both formulas stay finite (1 - s, not e s, carries
+// the derivative's second term).
 #define GELU_K 0.7978845608028654f
-DEVI float gelu_f(float u) {
-    float t = tanh_fast(GELU_K * (u + 0.044715f * u * u * u));
-    return 0.5f * u * (1.0f + t);
+#define GELU_C 0.044715f
+DEVI float gelu_sig(float u) {
+    const float u2 = u * u;
+    const float z = u * fmaf(-2.f * GELU_K * GELU_C * 1.4426950408889634f, u2, -2.f * GELU_K * 1.4426950408889634f);
+    return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(z));
 }
+DEVI float gelu_f(float u) { return u * gelu_sig(u); }
 DEVI float gelu_grad_f(float u) {
-    float t = tanh_fast(GELU_K * (u + 0.044715f * u * u * u));
-    return 0.5f * (1.0f + t) + 0.5f * u * (1.0f - t * t) * GELU_K * (1.0f + 3.0f * 0.044715f * u * u);
+    const float s = gelu_sig(u);
+    const float dv = fmaf(6.f * GELU_K * GELU_C, u * u, 2.f * GELU_K);  // v'
+    return s * fmaf(u * dv, 1.f - s, 1.f);
 }
 
 static inline unsigned cdiv(size_t a, size_t b) { return (unsigned)((a + b - 1) / b); }

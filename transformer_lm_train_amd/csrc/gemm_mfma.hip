@@ -1,283 +1,131 @@
 // bf16 matrix products on the gfx950 matrix cores.
 //
-// Block tile BM x BN, k-step 64, 256 threads = 4 wavefronts in a 2x2 grid,
-// each wave owning a (BM/2) x (BN/2) sub-tile of 32x32 accumulators fed by
-// v_mfma_f32_32x32x16_bf16 (8 bf16 of A and of B per lane, fp32 accumulate).
-// Operand tiles are staged in LDS as [row][k] with k contiguous, so every
-// MFMA fragment is one 16-byte LDS read.  An operand stored with its row
-// index contiguous (the transposed operands of the backward products) is
-// loaded as 8x8 blocks and transposed in registers on its way into LDS.
-// Two LDS buffers: the global loads of k-step t+1 are in flight while the
-// matrix cores work on step t.  Block ids are remapped so that the tiles
-// one XCD (one L2) runs are neighbours sharing operand panels.
+// One kernel for the three operand forms of a training step (X W^T forward,
+// dY W backward-data, dY^T X backward-weight): operands go global -> LDS by
+// direct loads in the layout they have in memory (k-contiguous rows, or
+// rows contiguous along m / n for the transposed operands, read back with
+// transposing LDS reads), NS stages deep; 32x32x16 bf16 MFMAs with fp32
+// accumulators; a fused epilogue (bias, residual, GELU and its derivative,
+// fp32 gradient accumulation) that leaves through LDS so that global
+// accesses are whole row segments.  Weight gradients, whose outputs are
+// small next to their reduction over all tokens, split the reduction over
+// workgroups and add the partial tiles in a fixed order (deterministic).
+// Block ids are remapped so that the tiles one XCD (one L2) runs are
+// neighbours sharing operand panels.
 #include <algorithm>
 
 #include "kernels.h"
 
 namespace {
 
-// native 4 x u32 vector (SROA-friendly, unlike the union-based uint4)
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-constexpr int BK = 64;
-constexpr int LDK = BK + 8;  // LDS row pitch in elements (144 bytes)
-
-// ---- operand tiles: rows [r0, r0+R) x k [k0, k0+64) of X ------------------
-// Rows past the end re-read the last row (always in bounds).  They only feed
-// accumulator rows/columns past M or N, which the epilogue never stores, so
-// they need no zeroing and the loads carry no branches.
-
-// k-contiguous X (X(r,k) = X[r*ld + k]): R*8 16-byte chunks, R/32 per thread
-template <int R> struct KT {
-    static constexpr int N = R / 32;
-    static DEVI void load(u32x4 (&v)[N], const bf16* X, int64_t ld, int r0, int rows, int k0, int tid, int) {
-#pragma unroll
-        for (int i = 0; i < N; i++) {
-            const int c = tid + i * 256;
-            const int rr = min(r0 + (c >> 3), rows - 1);
-            v[i] = *reinterpret_cast<const u32x4*>(X + (int64_t)rr * ld + k0 + (c & 7) * 8);
-        }
-    }
-    static DEVI void store(const u32x4 (&v)[N], uint16_t* lds, int tid, int) {
-#pragma unroll
-        for (int i = 0; i < N; i++) {
-            const int c = tid + i * 256;
-            *reinterpret_cast<u32x4*>(lds + (c >> 3) * LDK + (c & 7) * 8) = v[i];
-        }
-    }
-};
-
-// mn-contiguous X (X(r,k) = X[k*ld + r]): 8 x R/8 blocks of 8x8, one block
-// per thread for threads (tid+off)%256 < R (R <= 256), transposed in
-// registers on the way into LDS.  The k-block index runs fastest, so the 8
-// lanes of a group write 8 different 16-byte columns of one LDS row group
-// (distinct banks) while every 8 lanes still read 128 contiguous bytes.
-template <int R> struct MNT {
-    static_assert(R <= 256, "one 8x8 block per thread");
-    static constexpr int N = 8;
-    static DEVI void load(u32x4 (&v)[N], const bf16* X, int64_t ld, int r0, int rows, int k0, int tid, int off) {
-        const int b = (tid + off) & 255;
-        if (b >= R) return;
-        const int kb = b & 7, rb = b >> 3;
-        const int rr = min(r0 + rb * 8, rows - 8);
-#pragma unroll
-        for (int j = 0; j < 8; j++) v[j] = *reinterpret_cast<const u32x4*>(X + (int64_t)(k0 + kb * 8 + j) * ld + rr);
-    }
-    static DEVI void store(const u32x4 (&v)[N], uint16_t* lds, int tid, int off) {
-        const int b = (tid + off) & 255;
-        if (b >= R) return;
-        const int kb = b & 7, rb = b >> 3;
-#pragma unroll
-        for (int i = 0; i < 8; i++) {
-            uint32_t o[4];
-#pragma unroll
-            for (int q = 0; q < 4; q++) {
-                const uint32_t lo = (i & 2) ? (i & 4 ? v[2 * q].w : v[2 * q].y) : (i & 4 ? v[2 * q].z : v[2 * q].x);
-                const uint32_t hi = (i & 2) ? (i & 4 ? v[2 * q + 1].w : v[2 * q + 1].y)
-                                            : (i & 4 ? v[2 * q + 1].z : v[2 * q + 1].x);
-                o[q] = (i & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-            }
-            *reinterpret_cast<u32x4*>(lds + (rb * 8 + i) * LDK + kb * 8) = u32x4{o[0], o[1], o[2], o[3]};
-        }
-    }
-};
+constexpr int KALIGN = 64;  // K, and every split-K chunk, is a multiple of this
 
 constexpr int EPI_PARTIAL = 100;  // split-K partial tile into g.ws[split][M][N]
-
-// Epilogue of 4 consecutive columns n..n+3 of row m (n % 4 == 0, N % 8 == 0,
-// so the 4 are all inside or all outside the matrix): 8-byte bf16 or 16-byte
-// fp32 accesses.
-template <int EPI>
-DEVI void epi_store4(const GemmArgs& g, int m, int n, const float (&acc)[4]) {
-    typedef bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-    if (EPI == EPI_PARTIAL) {
-        *reinterpret_cast<float4*>(g.ws + ((int64_t)blockIdx.y * g.M + m) * g.N + n) =
-            make_float4(acc[0], acc[1], acc[2], acc[3]);
-        return;
-    }
-    const int64_t o = (int64_t)m * g.ldo + n;
-    if (EPI == EPI_ACC_F32) {
-        float4* p = reinterpret_cast<float4*>((float*)g.out + o);
-        float4 v = *p;
-        v.x += acc[0]; v.y += acc[1]; v.z += acc[2]; v.w += acc[3];
-        *p = v;
-        return;
-    }
-    float y[4] = {acc[0], acc[1], acc[2], acc[3]};
-    if ((EPI == EPI_BIAS || EPI == EPI_BIAS_RESID || EPI == EPI_BIAS_GELU) && g.bias) {
-        const float4 bv = *reinterpret_cast<const float4*>(g.bias + n);
-        y[0] += bv.x; y[1] += bv.y; y[2] += bv.z; y[3] += bv.w;
-    }
-    if (EPI == EPI_BIAS_RESID) {
-        const bf16x4_t r = *reinterpret_cast<const bf16x4_t*>((const bf16*)g.resid + o);
-#pragma unroll
-        for (int e = 0; e < 4; e++) y[e] += (float)r[e];
-    }
-    if (EPI == EPI_GELU_BWD) {
-        const bf16x4_t u = *reinterpret_cast<const bf16x4_t*>((const bf16*)g.aux + o);
-#pragma unroll
-        for (int e = 0; e < 4; e++) y[e] *= gelu_grad_f((float)u[e]);
-    }
-    bf16x4_t out;
-#pragma unroll
-    for (int e = 0; e < 4; e++) out[e] = (bf16)y[e];
-    *reinterpret_cast<bf16x4_t*>((bf16*)g.out + o) = out;
-    if (EPI == EPI_BIAS_GELU) {
-#pragma unroll
-        for (int e = 0; e < 4; e++) out[e] = (bf16)gelu_f(y[e]);
-        *reinterpret_cast<bf16x4_t*>((bf16*)g.out2 + o) = out;
-    }
-}
 
 // The products run the MFMA with the operands swapped, acc = B A^T: register
 // r of lane l of the 32x32 block (i, j) then holds row i*32 + l % 32 and
 // column j*32 + 8*(r/4) + 4*(l/32) + r%4, so each group of 4 registers is 4
 // consecutive columns of one row.
-template <int EPI, int FM, int FN>
-DEVI void epilogue(const GemmArgs& g, const f32x16 (&acc)[FM][FN], int mrow0, int ncol0, int lane) {
-#pragma unroll
-    for (int i = 0; i < FM; i++)
-#pragma unroll
-        for (int j = 0; j < FN; j++)
-#pragma unroll
-            for (int q = 0; q < 4; q++) {
-                const int m = mrow0 + i * 32 + (lane & 31);
-                const int n = ncol0 + j * 32 + q * 8 + (lane >> 5) * 4;
-                if (m < g.M && n < g.N) {
-                    const float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                                        acc[i][j][4 * q + 3]};
-                    epi_store4<EPI>(g, m, n, v);
-                }
-            }
-}
+//
+// Row-major epilogue through LDS: the wave writes RH rows (32, or 16 when
+// its region is small) of one 32-row accumulator block into its own LDS
+// region (pitch TN + 4 floats, so the 16 rows a 16-byte access group touches
+// fall in distinct bank groups), reads them back so that each lane owns 8
+// consecutive outputs of one row, and finishes them with 16-byte bf16 /
+// 32-byte fp32 global accesses: LPR lanes cover a whole row segment, so
+// every access instruction moves full cache lines instead of 32 scattered
+// 16-byte pieces.  LDS order within one wave is
+// program order, so the region needs no synchronisation between the blocks.
+template <int RH, int TN> constexpr int red_bytes() { return RH * (TN + 4) * 4; }
 
-// One k-step (64) of the wave's FM x FN block of 32x32 accumulators from an
-// LDS stage holding the A tile ([BM][LDK]) followed by the B tile.
-template <int BM, int FM, int FN, int TM, int TN>
-DEVI void mfma_tile(f32x16 (&acc)[FM][FN], const uint16_t* As, int wm, int wn, int lane) {
-    const uint16_t* Bs = As + BM * LDK;
-    // fragments double-buffered in registers (see mfma_swz)
-    bf16x8 a[2][FM], b[2][FN];
-    auto frag = [&](int ks, bf16x8 (&fa)[FM], bf16x8 (&fb)[FN]) {
-        const int koff = ks * 16 + (lane >> 5) * 8;
+template <int EPI, int RH, int FM, int FN>
+DEVI void epilogue_rows(const GemmArgs& g, const f32x16 (&acc)[FM][FN], float* red, int mrow0, int ncol0, int lane) {
+    constexpr int TN = FN * 32, P = TN + 4;
+    constexpr int LPR = TN / 8;    // lanes per output row
+    constexpr int RPI = 64 / LPR;  // rows per access instruction
+    constexpr int NR = RH / RPI;   // row groups per pass
+    static_assert(RH == 32 || RH == 16, "rows per pass");
+    constexpr bool BIAS = EPI == EPI_BIAS || EPI == EPI_BIAS_RESID || EPI == EPI_BIAS_GELU;
+    typedef bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+    const int hi = lane >> 5, l32 = lane & 31;
+    const int cl = (lane % LPR) * 8;
+    const int n = ncol0 + cl;
+    const bool nok = n < g.N;
+    float b8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (BIAS && g.bias && nok) {
+        const float4 u = *reinterpret_cast<const float4*>(g.bias + n);
+        const float4 v = *reinterpret_cast<const float4*>(g.bias + n + 4);
+        b8[0] = u.x; b8[1] = u.y; b8[2] = u.z; b8[3] = u.w; b8[4] = v.x; b8[5] = v.y; b8[6] = v.z; b8[7] = v.w;
+    }
 #pragma unroll
-        for (int i = 0; i < FM; i++)
-            fa[i] = *reinterpret_cast<const bf16x8*>(As + (wm * TM + i * 32 + (lane & 31)) * LDK + koff);
+    for (int pass = 0; pass < FM * (32 / RH); pass++) {
+        const int i = pass / (32 / RH), h = pass % (32 / RH);  // rows h*RH .. of block i
+        // operands of this pass's outputs, requested before the LDS round trip
+        bf16x8_t r16[NR];
+        float4 r32[NR][2];
 #pragma unroll
-        for (int j = 0; j < FN; j++)
-            fb[j] = *reinterpret_cast<const bf16x8*>(Bs + (wn * TN + j * 32 + (lane & 31)) * LDK + koff);
-    };
-    frag(0, a[0], b[0]);
-    __builtin_amdgcn_sched_group_barrier(0x100, FM + FN, 0);
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ks++) {
-        if (ks + 1 < BK / 16) frag(ks + 1, a[(ks + 1) & 1], b[(ks + 1) & 1]);
-#pragma unroll
-        for (int i = 0; i < FM; i++)
+        for (int rr = 0; rr < NR; rr++) {
+            const int m = mrow0 + i * 32 + h * RH + rr * RPI + lane / LPR;
+            const bool ok = m < g.M && nok;
+            const int64_t o = (int64_t)m * g.ldo + n;
+            if constexpr (EPI == EPI_BIAS_RESID)
+                r16[rr] = ok ? *reinterpret_cast<const bf16x8_t*>((const bf16*)g.resid + o) : bf16x8_t{};
+            if constexpr (EPI == EPI_GELU_BWD)
+                r16[rr] = ok ? *reinterpret_cast<const bf16x8_t*>((const bf16*)g.aux + o) : bf16x8_t{};
+            if constexpr (EPI == EPI_ACC_F32) {
+                r32[rr][0] = ok ? *reinterpret_cast<const float4*>((const float*)g.out + o) : make_float4(0.f, 0.f, 0.f, 0.f);
+                r32[rr][1] = ok ? *reinterpret_cast<const float4*>((const float*)g.out + o + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+        }
+        if (RH == 32 || (l32 >> 4) == h) {
+            const int wr = l32 % RH;
 #pragma unroll
             for (int j = 0; j < FN; j++)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[ks & 1][j], a[ks & 1][i], acc[i][j], 0, 0, 0);
-        // keep that order through scheduling: the next sub-step's LDS reads
-        // (mask 0x100) issue ahead of this sub-step's MFMAs (mask 0x008)
-        if (ks + 1 < BK / 16) __builtin_amdgcn_sched_group_barrier(0x100, FM + FN, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, FM * FN, 0);
-    }
-}
-
-template <int BM, int BN, int WAVES_M, bool AK, bool BKC, int EPI>
-__global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs g, int kchunk) {
-    constexpr int WAVES_N = 4 / WAVES_M;
-    constexpr int TM = BM / WAVES_M, TN = BN / WAVES_N, FM = TM / 32, FN = TN / 32;
-    static_assert(FM >= 1 && FN >= 1 && TM % 32 == 0 && TN % 32 == 0, "wave tile");
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2][(BM + BN) * LDK];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
-
-    // block -> tile: XCD-contiguous ranges, then groups of 8 tile-rows
-    const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
-    int bid = blockIdx.x;
-    const int total = gridDim.x;
-    if ((total & 7) == 0) bid = (bid & 7) * (total >> 3) + (bid >> 3);
-    constexpr int GM = 8;
-    int group = bid / (GM * tiles_n);
-    int first_m = group * GM;
-    int gsz = min(tiles_m - first_m, GM);
-    int in = bid % (GM * tiles_n);
-    const int m0 = (first_m + in % gsz) * BM;
-    const int n0 = (in / gsz) * BN;
-
-    const bf16* A = (const bf16*)g.a;
-    const bf16* B = (const bf16*)g.b;
-
-    f32x16 acc[FM][FN];
 #pragma unroll
-    for (int i = 0; i < FM; i++)
-#pragma unroll
-        for (int j = 0; j < FN; j++)
-#pragma unroll
-            for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
-
-    typedef typename std::conditional<AK, KT<BM>, MNT<BM>>::type TA;
-    typedef typename std::conditional<BKC, KT<BN>, MNT<BN>>::type TB;
-    // two register stages: the loads of k-step t+2 are issued while step t
-    // computes, and step t+1 (loaded one compute phase earlier) goes to LDS
-    u32x4 ra0[TA::N], ra1[TA::N], rb0[TB::N], rb1[TB::N];
-    const int kbeg = blockIdx.y * kchunk;  // this workgroup's share of the reduction
-    const int nk = (min(g.K, kbeg + kchunk) - kbeg) / BK;
-#define GEMM_LOAD(ra, rb, k0)                                   \
-    do {                                                        \
-        TA::load(ra, A, g.lda, m0, g.M, (k0), tid, 0);          \
-        TB::load(rb, B, g.ldb, n0, g.N, (k0), tid, 128);        \
-    } while (0)
-#define GEMM_STORE(ra, rb, buf)                                 \
-    do {                                                        \
-        TA::store(ra, (buf), tid, 0);                           \
-        TB::store(rb, (buf) + BM * LDK, tid, 128);              \
-    } while (0)
-
-    // Loads are issued unconditionally (the k-step index clamped to the last
-    // one; a redundant tail load is never consumed): a load under a branch
-    // makes the wait-count insertion assume the worst at the join and wait
-    // for every outstanding load, which would undo the prefetch.
-    const int klast = kbeg + (nk - 1) * BK;
-    int kt = 0;
-    if constexpr (!AK && !BKC) {
-        // both operands transposed through registers (16 x 16 bytes per thread):
-        // one register stage keeps the kernel at two waves per SIMD
-        GEMM_LOAD(ra0, rb0, kbeg);
-        GEMM_STORE(ra0, rb0, lds[0]);
-        __syncthreads();
-        for (; kt < nk; kt++) {
-            const int cur = kt & 1;
-            GEMM_LOAD(ra0, rb0, min(kbeg + (kt + 1) * BK, klast));
-            mfma_tile<BM, FM, FN, TM, TN>(acc, lds[cur], wm, wn, lane);
-            GEMM_STORE(ra0, rb0, lds[cur ^ 1]);
-            __syncthreads();
+                for (int q = 0; q < 4; q++)
+                    *reinterpret_cast<float4*>(red + wr * P + j * 32 + q * 8 + hi * 4) =
+                        make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
         }
-    } else {
-        GEMM_LOAD(ra0, rb0, kbeg);
-        GEMM_LOAD(ra1, rb1, min(kbeg + BK, klast));
-        GEMM_STORE(ra0, rb0, lds[0]);
-        __syncthreads();
-        for (; kt + 1 < nk; kt += 2) {
-            // even step: compute buffer 0, refill register stage 0 with step kt+2
-            GEMM_LOAD(ra0, rb0, min(kbeg + (kt + 2) * BK, klast));
-            mfma_tile<BM, FM, FN, TM, TN>(acc, lds[0], wm, wn, lane);
-            GEMM_STORE(ra1, rb1, lds[1]);
-            __syncthreads();
-            // odd step: compute buffer 1, refill register stage 1 with step kt+3;
-            // buffer 0 then receives step kt+2 (unused when kt+2 == nk)
-            GEMM_LOAD(ra1, rb1, min(kbeg + (kt + 3) * BK, klast));
-            mfma_tile<BM, FM, FN, TM, TN>(acc, lds[1], wm, wn, lane);
-            GEMM_STORE(ra0, rb0, lds[0]);
-            __syncthreads();
+#pragma unroll
+        for (int rr = 0; rr < NR; rr++) {
+            const int row = rr * RPI + lane / LPR;
+            const int m = mrow0 + i * 32 + h * RH + row;
+            const float4 u = *reinterpret_cast<const float4*>(red + row * P + cl);
+            const float4 v = *reinterpret_cast<const float4*>(red + row * P + cl + 4);
+            float y[8] = {u.x, u.y, u.z, u.w, v.x, v.y, v.z, v.w};
+            if (m >= g.M || !nok) continue;
+            const int64_t o = (int64_t)m * g.ldo + n;
+            if constexpr (EPI == EPI_PARTIAL) {
+                float* w = g.ws + ((int64_t)blockIdx.y * g.M + m) * g.N + n;
+                *reinterpret_cast<float4*>(w) = u;
+                *reinterpret_cast<float4*>(w + 4) = v;
+                continue;
+            }
+            if constexpr (EPI == EPI_ACC_F32) {
+                float* w = (float*)g.out + o;
+                *reinterpret_cast<float4*>(w) =
+                    make_float4(r32[rr][0].x + y[0], r32[rr][0].y + y[1], r32[rr][0].z + y[2], r32[rr][0].w + y[3]);
+                *reinterpret_cast<float4*>(w + 4) =
+                    make_float4(r32[rr][1].x + y[4], r32[rr][1].y + y[5], r32[rr][1].z + y[6], r32[rr][1].w + y[7]);
+                continue;
+            }
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+                if constexpr (BIAS) y[e] += b8[e];
+                if constexpr (EPI == EPI_BIAS_RESID) y[e] += (float)r16[rr][e];
+                if constexpr (EPI == EPI_GELU_BWD) y[e] *= gelu_grad_f((float)r16[rr][e]);
+            }
+            bf16x8_t out;
+#pragma unroll
+            for (int e = 0; e < 8; e++) out[e] = (bf16)y[e];
+            *reinterpret_cast<bf16x8_t*>((bf16*)g.out + o) = out;
+            if constexpr (EPI == EPI_BIAS_GELU) {
+#pragma unroll
+                for (int e = 0; e < 8; e++) out[e] = (bf16)gelu_f(y[e]);
+                *reinterpret_cast<bf16x8_t*>((bf16*)g.out2 + o) = out;
+            }
         }
-        if (kt < nk) mfma_tile<BM, FM, FN, TM, TN>(acc, lds[0], wm, wn, lane);  // odd step count: last one in buffer 0
     }
-#undef GEMM_LOAD
-#undef GEMM_STORE
-
-    epilogue<EPI>(g, acc, m0 + wm * TM, n0 + wn * TN, lane);
 }
 
 // ============================================================================
@@ -291,60 +139,81 @@ typedef __attribute__((address_space(1))) void glb_void_t;
 template <int N> constexpr int vmcnt_imm() { return (N & 15) | ((N >> 4) << 14) | (7 << 4); }
 
 // ============================================================================
-// Large-tile variant: every operand goes global -> LDS by direct loads, in the
-// layout it has in memory.
-//  - k-contiguous operand: LDS [row][64], 16-byte chunk c of row r in slot
-//    c ^ (r & 7); fragment = one 16-byte LDS read.
-//  - mn-contiguous operand: LDS [k][R] (R = tile rows), 16-byte chunk c of
-//    k-row k in slot c ^ ((k & 3) << 1); fragment = two ds_read_b64_tr_b16.
-//    Within each 16-lane group that instruction hands lane i element (i % 4)
-//    of the 8-byte read of lane 4e + i/4 as its element e; so when lane j
-//    reads X[k0 + j/4][m0 + 4(j%4) .. +3], lane i receives X[k0..k0+3][m0+i],
-//    four consecutive k of one row: exactly the MFMA operand fragment.
-// NW waves (2 x NW/2), each owning a (BM/2) x (BN/(NW/2)) block of 32x32
-// accumulators; NS LDS stages with explicit vmcnt waits and raw barriers.
+// Direct-to-LDS kernel: every operand goes global -> LDS by
+// global_load_lds_dwordx4, in the layout it has in memory, NS stages deep with
+// explicit vmcnt waits and raw barriers, k-step KB (32 or 64).
+// LDS has 64 banks of 4 bytes, so a conflict-free read instruction must spread
+// each group of lanes served together over all 256 bytes of a bank window:
+//  - k-contiguous operand: LDS [row][KB]; the 16-byte chunk c of row r sits in
+//    slot c ^ kswz(r), which puts the 16 rows read by 16 lanes (one chunk
+//    each) in 16 distinct 16-byte bank groups.  Fragment = one ds_read_b128.
+//  - mn-contiguous operand: LDS [k][R] (R = tile rows); chunk c of k-row k sits
+//    in slot c ^ ((k & 3) << 2), so the four k-rows a transposing read touches
+//    at once land in four distinct 64-byte quarters.  Fragment = two
+//    ds_read_b64_tr_b16: within each 16-lane group that instruction hands
+//    lane i element (i % 4) of the 8-byte read of lane 4e + i/4 as its element
+//    e; so when lane j reads X[k0 + j/4][m0 + 4(j%4) .. +3], lane i receives
+//    X[k0..k0+3][m0+i], four consecutive k of one row: the MFMA fragment.
+// WAVES_M x (NW / WAVES_M) waves, each owning a TM x TN block of 32x32
+// accumulators.
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-DEVI int mn_swz(int k) { return (k & 3) << 1; }
-
-// tile rows [r0, r0+R) x k [k0, k0+64) of X into LDS; NIW 1 KB loads per wave
-template <int R, int NW, bool KCONTIG>
-DEVI void dma_any(uint16_t* tile, const bf16* X, int64_t ld, int r0, int rows, int k0, int wave, int lane) {
-    constexpr int NIW = R / (8 * NW);
-    static_assert(NIW >= 1 && NIW * 8 * NW == R, "tile rows vs waves");
-#pragma unroll
-    for (int i = 0; i < NIW; i++) {
-        const int blk = wave * NIW + i;  // 1 KB block of the tile
-        const bf16* g;
-        if constexpr (KCONTIG) {
-            const int r = blk * 8 + (lane >> 3);
-            const int c = (lane & 7) ^ (lane >> 3);  // = slot ^ (r & 7)
-            g = X + (int64_t)min(r0 + r, rows - 1) * ld + k0 + c * 8;
-        } else {
-            constexpr int CPR = R / 8;  // chunks per k-row
-            const int p = blk * 64 + lane;
-            const int k = p / CPR;
-            const int c = (p % CPR) ^ mn_swz(k);
-            g = X + (int64_t)(k0 + k) * ld + min(r0 + c * 8, rows - 8);
-        }
-        __builtin_amdgcn_global_load_lds((glb_void_t*)g, (lds_void_t*)(tile + blk * 512), 16, 0, 0);
-    }
+template <int KB> DEVI int kswz(int r) {
+    if constexpr (KB == 64) return (r >> 1) & 7;  // 2 rows of 128 B per bank window
+    else return (r >> 2) & 3;                     // 4 rows of 64 B per bank window
 }
+DEVI int mnswz(int k) { return (k & 3) << 2; }
+
+// Per-lane element offsets of the NIW direct loads one wave issues per stage
+// for tile rows [r0, r0+R) of X; the k-step only adds a uniform offset.
+// Rows past the end re-read the last row (in bounds); they only feed
+// accumulators the epilogue never stores.
+template <int R, int NW, int KB, bool KCONTIG>
+struct Dma {
+    static constexpr int NIW = R * KB / (512 * NW);
+    static_assert(NIW >= 1 && NIW * 512 * NW == R * KB, "tile vs waves");
+    uint32_t off[NIW];
+    DEVI void init(int ld, int r0, int rows, int wave, int lane) {
+#pragma unroll
+        for (int i = 0; i < NIW; i++) {
+            const int p = (wave * NIW + i) * 64 + lane;  // 16-byte chunk position in the tile
+            if constexpr (KCONTIG) {
+                constexpr int CPR = KB / 8;
+                const int r = p / CPR;
+                const int c = (p % CPR) ^ kswz<KB>(r);
+                off[i] = (uint32_t)(min(r0 + r, rows - 1) * ld + c * 8);
+            } else {
+                constexpr int CPR = R / 8;
+                const int k = p / CPR;
+                const int c = (p % CPR) ^ mnswz(k);
+                off[i] = (uint32_t)(k * ld + min(r0 + c * 8, rows - 8));
+            }
+        }
+    }
+    // kofs: k0 (k-contiguous) or k0 * ld (mn-contiguous)
+    DEVI void issue(uint16_t* tile, const bf16* X, int64_t kofs, int wave) const {
+        const bf16* base = X + kofs;
+#pragma unroll
+        for (int i = 0; i < NIW; i++)
+            __builtin_amdgcn_global_load_lds((glb_void_t*)(base + off[i]), (lds_void_t*)(tile + (wave * NIW + i) * 512),
+                                             16, 0, 0);
+    }
+};
 
 // MFMA fragment: rows row0 + (lane & 31), k = kk + (lane >> 5) * 8 + 0..7
-template <int R, bool KCONTIG>
+template <int R, int KB, bool KCONTIG>
 DEVI bf16x8 frag_any(const uint16_t* tile, int row0, int kk, int lane) {
     if constexpr (KCONTIG) {
         const int r = row0 + (lane & 31);
         const int c = (kk >> 3) + (lane >> 5);
-        return *reinterpret_cast<const bf16x8*>(tile + r * BK + ((c ^ (r & 7)) << 3));
+        return *reinterpret_cast<const bf16x8*>(tile + r * KB + ((c ^ kswz<KB>(r)) << 3));
     } else {
         const int j = lane & 15, g = lane >> 4;
         const int m = row0 + 16 * (g & 1) + 4 * (j & 3);
         const int k = kk + (g >> 1) * 8 + (j >> 2);
-        const int o0 = k * R + ((((m >> 3) ^ mn_swz(k)) << 3) | (m & 7));
-        const int o1 = (k + 4) * R + ((((m >> 3) ^ mn_swz(k + 4)) << 3) | (m & 7));
+        const int o0 = k * R + ((((m >> 3) ^ mnswz(k)) << 3) | (m & 7));
+        const int o1 = (k + 4) * R + ((((m >> 3) ^ mnswz(k + 4)) << 3) | (m & 7));
         i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + o0));
         i16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + o1));
         i16x4 xy[2] = {x, y};
@@ -352,46 +221,52 @@ DEVI bf16x8 frag_any(const uint16_t* tile, int row0, int kk, int lane) {
     }
 }
 
-template <int BM, int BN, int FM, int FN, int TM, int TN, bool AK, bool BKC>
+template <int BM, int BN, int KB, int FM, int FN, int TM, int TN, bool AK, bool BKC>
 DEVI void mfma_any(f32x16 (&acc)[FM][FN], const uint16_t* As, const uint16_t* Bs, int wm, int wn, int lane) {
     bf16x8 a[2][FM], b[2][FN];
+    constexpr int NRD = FM * (AK ? 1 : 2) + FN * (BKC ? 1 : 2);  // LDS read instructions per sub-step
 #pragma unroll
-    for (int i = 0; i < FM; i++) a[0][i] = frag_any<BM, AK>(As, wm * TM + i * 32, 0, lane);
+    for (int i = 0; i < FM; i++) a[0][i] = frag_any<BM, KB, AK>(As, wm * TM + i * 32, 0, lane);
 #pragma unroll
-    for (int j = 0; j < FN; j++) b[0][j] = frag_any<BN, BKC>(Bs, wn * TN + j * 32, 0, lane);
-    __builtin_amdgcn_sched_group_barrier(0x100, (FM + FN) * (AK && BKC ? 1 : 2), 0);
+    for (int j = 0; j < FN; j++) b[0][j] = frag_any<BN, KB, BKC>(Bs, wn * TN + j * 32, 0, lane);
+    __builtin_amdgcn_sched_group_barrier(0x100, NRD, 0);
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ks++) {
-        if (ks + 1 < BK / 16) {
+    for (int ks = 0; ks < KB / 16; ks++) {
+        if (ks + 1 < KB / 16) {
 #pragma unroll
-            for (int i = 0; i < FM; i++) a[(ks + 1) & 1][i] = frag_any<BM, AK>(As, wm * TM + i * 32, (ks + 1) * 16, lane);
+            for (int i = 0; i < FM; i++)
+                a[(ks + 1) & 1][i] = frag_any<BM, KB, AK>(As, wm * TM + i * 32, (ks + 1) * 16, lane);
 #pragma unroll
-            for (int j = 0; j < FN; j++) b[(ks + 1) & 1][j] = frag_any<BN, BKC>(Bs, wn * TN + j * 32, (ks + 1) * 16, lane);
+            for (int j = 0; j < FN; j++)
+                b[(ks + 1) & 1][j] = frag_any<BN, KB, BKC>(Bs, wn * TN + j * 32, (ks + 1) * 16, lane);
         }
 #pragma unroll
         for (int i = 0; i < FM; i++)
 #pragma unroll
             for (int j = 0; j < FN; j++)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[ks & 1][j], a[ks & 1][i], acc[i][j], 0, 0, 0);
-        if (ks + 1 < BK / 16) __builtin_amdgcn_sched_group_barrier(0x100, (FM + FN) * (AK && BKC ? 1 : 2), 0);
+        // keep the next sub-step's LDS reads (mask 0x100) ahead of this
+        // sub-step's MFMAs (mask 0x008) through scheduling
+        if (ks + 1 < KB / 16) __builtin_amdgcn_sched_group_barrier(0x100, NRD, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, FM * FN, 0);
     }
 }
 
-template <int BM, int BN, int NW, int NS, bool AK, bool BKC, int EPI>
-__global__ __launch_bounds__(NW * 64) void gemm_big_kernel(GemmArgs g, int kchunk) {
-    constexpr int WAVES_M = 2, WAVES_N = NW / 2;
+template <int BM, int BN, int NW, int WAVES_M, int KB, int NS, bool AK, bool BKC, int EPI>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_big_kernel(GemmArgs g, int kchunk) {
+    constexpr int WAVES_N = NW / WAVES_M;
     constexpr int TM = BM / WAVES_M, TN = BN / WAVES_N, FM = TM / 32, FN = TN / 32;
-    static_assert(NS >= 2 && NS <= 3, "stages");
-    __shared__ __attribute__((aligned(1024))) uint16_t sa0[BM * BK], sa1[BM * BK], sa2[NS > 2 ? BM * BK : 8];
-    __shared__ __attribute__((aligned(1024))) uint16_t sb0[BN * BK], sb1[BN * BK], sb2[NS > 2 ? BN * BK : 8];
+    static_assert(NS >= 2 && NS <= 4, "stages");
+    constexpr int SA = BM * KB, SB = BN * KB;
+    __shared__ __attribute__((aligned(1024))) uint16_t sa0[SA], sa1[SA], sa2[NS > 2 ? SA : 8], sa3[NS > 3 ? SA : 8];
+    __shared__ __attribute__((aligned(1024))) uint16_t sb0[SB], sb1[SB], sb2[NS > 2 ? SB : 8], sb3[NS > 3 ? SB : 8];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WAVES_N, wn = wave % WAVES_N;
 
     const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
     int bid = blockIdx.x;
     const int total = gridDim.x;
-    if ((total & 7) == 0) bid = (bid & 7) * (total >> 3) + (bid >> 3);
+    if ((total & 7) == 0) bid = (bid & 7) * (total >> 3) + (bid >> 3);  // neighbouring tiles on one XCD
     constexpr int GM = 8;
     const int group = bid / (GM * tiles_n);
     const int first_m = group * GM;
@@ -411,73 +286,99 @@ __global__ __launch_bounds__(NW * 64) void gemm_big_kernel(GemmArgs g, int kchun
             for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
 
     const int kbeg = blockIdx.y * kchunk;
-    const int nk = (min(g.K, kbeg + kchunk) - kbeg) / BK;
-    const int klast = kbeg + (nk - 1) * BK;
-    constexpr int LPS = (BM + BN) / (8 * NW);  // direct loads per thread per stage
+    const int nk = (min(g.K, kbeg + kchunk) - kbeg) / KB;
+    const int klast = kbeg + (nk - 1) * KB;
+    Dma<BM, NW, KB, AK> da;
+    Dma<BN, NW, KB, BKC> db;
+    da.init(g.lda, m0, g.M, wave, lane);
+    db.init(g.ldb, n0, g.N, wave, lane);
+    constexpr int LPS = Dma<BM, NW, KB, AK>::NIW + Dma<BN, NW, KB, BKC>::NIW;  // loads per thread per stage
 
-#define BIG_DMA(SA, SB, K0)                                                  \
-    do {                                                                     \
-        dma_any<BM, NW, AK>(SA, A, g.lda, m0, g.M, (K0), wave, lane);        \
-        dma_any<BN, NW, BKC>(SB, B, g.ldb, n0, g.N, (K0), wave, lane);       \
-    } while (0)
-#define BIG_STEP(SA, SB, NA, NB, KT)                                                     \
-    do {                                                                                 \
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm<(NS - 2) * LPS>());                         \
-        __builtin_amdgcn_s_barrier();                                                    \
-        asm volatile("" ::: "memory");                                                   \
-        BIG_DMA(NA, NB, min(kbeg + ((KT) + NS - 1) * BK, klast));                        \
-        mfma_any<BM, BN, FM, FN, TM, TN, AK, BKC>(acc, SA, SB, wm, wn, lane);            \
-    } while (0)
+    auto dma = [&](uint16_t* ta, uint16_t* tb, int k0) {
+        da.issue(ta, A, AK ? (int64_t)k0 : (int64_t)k0 * g.lda, wave);
+        db.issue(tb, B, BKC ? (int64_t)k0 : (int64_t)k0 * g.ldb, wave);
+    };
+    // stage kt landed for every wave, and every wave is done with the stage
+    // the next load overwrites; then load k-step kt + NS - 1 and compute kt
+    auto step = [&](const uint16_t* ca, const uint16_t* cb, uint16_t* na, uint16_t* nb, int kt) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm<(NS - 2) * LPS>());
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        dma(na, nb, min(kbeg + (kt + NS - 1) * KB, klast));
+        mfma_any<BM, BN, KB, FM, FN, TM, TN, AK, BKC>(acc, ca, cb, wm, wn, lane);
+    };
 
-    BIG_DMA(sa0, sb0, kbeg);
-    if constexpr (NS > 2) BIG_DMA(sa1, sb1, min(kbeg + BK, klast));
+    dma(sa0, sb0, kbeg);
+    if constexpr (NS > 2) dma(sa1, sb1, min(kbeg + KB, klast));
+    if constexpr (NS > 3) dma(sa2, sb2, min(kbeg + 2 * KB, klast));
     int kt = 0;
     if constexpr (NS == 2) {
         for (; kt + 2 <= nk; kt += 2) {
-            BIG_STEP(sa0, sb0, sa1, sb1, kt);
-            BIG_STEP(sa1, sb1, sa0, sb0, kt + 1);
+            step(sa0, sb0, sa1, sb1, kt);
+            step(sa1, sb1, sa0, sb0, kt + 1);
         }
-        if (kt < nk) BIG_STEP(sa0, sb0, sa1, sb1, kt);
-    } else {
+        if (kt < nk) step(sa0, sb0, sa1, sb1, kt);
+    } else if constexpr (NS == 3) {
         for (; kt + 3 <= nk; kt += 3) {
-            BIG_STEP(sa0, sb0, sa2, sb2, kt);
-            BIG_STEP(sa1, sb1, sa0, sb0, kt + 1);
-            BIG_STEP(sa2, sb2, sa1, sb1, kt + 2);
+            step(sa0, sb0, sa2, sb2, kt);
+            step(sa1, sb1, sa0, sb0, kt + 1);
+            step(sa2, sb2, sa1, sb1, kt + 2);
         }
-        if (kt < nk) { BIG_STEP(sa0, sb0, sa2, sb2, kt); kt++; }
-        if (kt < nk) BIG_STEP(sa1, sb1, sa0, sb0, kt);
+        if (kt < nk) { step(sa0, sb0, sa2, sb2, kt); kt++; }
+        if (kt < nk) step(sa1, sb1, sa0, sb0, kt);
+    } else {
+        for (; kt + 4 <= nk; kt += 4) {
+            step(sa0, sb0, sa3, sb3, kt);
+            step(sa1, sb1, sa0, sb0, kt + 1);
+            step(sa2, sb2, sa1, sb1, kt + 2);
+            step(sa3, sb3, sa2, sb2, kt + 3);
+        }
+        if (kt < nk) { step(sa0, sb0, sa3, sb3, kt); kt++; }
+        if (kt < nk) { step(sa1, sb1, sa0, sb0, kt); kt++; }
+        if (kt < nk) step(sa2, sb2, sa1, sb1, kt);
     }
-#undef BIG_DMA
-#undef BIG_STEP
     __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());  // no load may still be writing LDS at exit
 
-    epilogue<EPI>(g, acc, m0 + wm * TM, n0 + wn * TN, lane);
+    // The stage buffers become the epilogue's per-wave regions once every
+    // wave is past its last LDS read.
+    constexpr int RBYTES = 2 * (BN < BM ? BN : BM) * KB;  // smallest stage array
+    constexpr int RH = red_bytes<32, TN>() <= RBYTES ? 32 : 16;
+    static_assert(NW <= 2 * NS && red_bytes<RH, TN>() <= RBYTES, "epilogue regions must fit the stage buffers");
+    {
+        __syncthreads();
+        uint16_t* region;
+        switch (wave) {
+            case 0: region = sa0; break;
+            case 1: region = sb0; break;
+            case 2: region = sa1; break;
+            case 3: region = sb1; break;
+            case 4: region = sa2; break;
+            case 5: region = sb2; break;
+            case 6: region = sa3; break;
+            default: region = sb3; break;
+        }
+        epilogue_rows<EPI, RH>(g, acc, reinterpret_cast<float*>(region), m0 + wm * TM, n0 + wn * TN, lane);
+    }
 }
 
-template <int BM, int BN, int NW, int NS, bool AK, bool BKC, int EPI>
+template <int BM, int BN, int NW, int WAVES_M, int KB, int NS, bool AK, bool BKC, int EPI>
 hipError_t launch_big(const GemmArgs& g, hipStream_t s, int splits = 1, int kchunk = 0) {
     dim3 grid(cdiv(g.M, BM) * cdiv(g.N, BN), splits);
-    gemm_big_kernel<BM, BN, NW, NS, AK, BKC, EPI><<<grid, NW * 64, 0, s>>>(g, kchunk ? kchunk : g.K);
-    return hipGetLastError();
-}
-
-template <int BM, int BN, int WAVES_M, bool AK, bool BKC, int EPI>
-hipError_t launch(const GemmArgs& g, hipStream_t s, int splits = 1, int kchunk = 0) {
-    dim3 grid(cdiv(g.M, BM) * cdiv(g.N, BN), splits);
-    gemm_mfma_kernel<BM, BN, WAVES_M, AK, BKC, EPI><<<grid, 256, 0, s>>>(g, kchunk ? kchunk : g.K);
+    gemm_big_kernel<BM, BN, NW, WAVES_M, KB, NS, AK, BKC, EPI><<<grid, NW * 64, 0, s>>>(g, kchunk ? kchunk : g.K);
     return hipGetLastError();
 }
 
 // Split of the reduction for the weight-gradient products, whose outputs are
 // small (C x C .. 4C x C) next to their reduction over all B*T tokens:
 // enough splits to give ~512 workgroups, each at least 4 k-steps long.
-void splitk_plan(int M, int N, int K, int* splits, int* kchunk) {
-    int tiles = (int)(cdiv(M, 128) * cdiv(N, 128));
+constexpr int SK_TM = 128, SK_TN = 128;  // tile of the split weight-gradient products
+void splitk_plan(int M, int N, int K, int tm, int tn, int* splits, int* kchunk) {
+    int tiles = (int)(cdiv(M, tm) * cdiv(N, tn));
     int S = (512 + tiles - 1) / tiles;
     int smax = K / 256;
     if (S > smax) S = smax;
     if (S < 1) S = 1;
-    int kc = (int)cdiv(K / BK, S) * BK;
+    int kc = (int)cdiv(K / KALIGN, S) * KALIGN;
     *kchunk = kc;
     *splits = (K + kc - 1) / kc;
 }
@@ -504,60 +405,54 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 }  // namespace
 
 hipError_t gemm_mfma_bf16(const GemmArgs& g, hipStream_t s) {
-    if (g.M <= 0 || g.N <= 0 || g.K <= 0 || g.K % BK || g.M % 8 || g.N % 8 || g.lda % 8 || g.ldb % 8)
+    if (g.M <= 0 || g.N <= 0 || g.K <= 0 || g.K % KALIGN || g.M % 8 || g.N % 8 || g.lda % 8 || g.ldb % 8)
         return hipErrorInvalidValue;
     if (!aligned16(g.a) || !aligned16(g.b)) return hipErrorInvalidValue;
-    // Tile choice per form and width, from timings at the GPT-2 shapes:
-    // 256x256 (8 waves) for wide outputs and the backward-data products,
-    // 128x128 direct-load tiles for mid widths, the register-staged 128x128
-    // kernel for the narrow (N = C) forward products.
+    // per-lane operand offsets are 32-bit element counts
+    const int64_t amax = g.a_kcontig ? (int64_t)(g.M - 1) * g.lda + g.K : (int64_t)(g.K - 1) * g.lda + g.M;
+    const int64_t bmax = g.b_kcontig ? (int64_t)(g.N - 1) * g.ldb + g.K : (int64_t)(g.K - 1) * g.ldb + g.N;
+    if (amax >= (int64_t)1 << 31 || bmax >= (int64_t)1 << 31) return hipErrorInvalidValue;
+    // Tile choice from timings at the GPT-2 shapes on gfx950: the 256 x 256
+    // tile (8 waves of 128 x 64, k-step 32, 4 LDS stages) leads or ties in
+    // every forward and backward-data product.
+#define BIG256(AKC, BKCC, E) launch_big<256, 256, 8, 2, 32, 4, AKC, BKCC, E>(g, s)
     if (g.a_kcontig && g.b_kcontig) {
-#define NT_CASES(BIG)                                                                                   \
-    switch (g.epi) {                                                                                    \
-        case EPI_STORE: return BIG(EPI_STORE);                                                          \
-        case EPI_BIAS: return BIG(EPI_BIAS);                                                            \
-        case EPI_BIAS_RESID: return BIG(EPI_BIAS_RESID);                                                \
-        case EPI_BIAS_GELU: return BIG(EPI_BIAS_GELU);                                                  \
-        default: return hipErrorInvalidValue;                                                           \
-    }
-#define NT_256(E) launch_big<256, 256, 8, 2, true, true, E>(g, s)
-#define NT_128(E) launch_big<128, 128, 4, 2, true, true, E>(g, s)
-#define NT_REG(E) launch<128, 128, 2, true, true, E>(g, s)
-        if (g.N >= 3072) NT_CASES(NT_256)
-        if (g.N >= 1536) NT_CASES(NT_128)
-        NT_CASES(NT_REG)
-#undef NT_CASES
-#undef NT_256
-#undef NT_128
-#undef NT_REG
+        switch (g.epi) {
+            case EPI_STORE: return BIG256(true, true, EPI_STORE);
+            case EPI_BIAS: return BIG256(true, true, EPI_BIAS);
+            case EPI_BIAS_RESID: return BIG256(true, true, EPI_BIAS_RESID);
+            case EPI_BIAS_GELU: return BIG256(true, true, EPI_BIAS_GELU);
+            default: return hipErrorInvalidValue;
+        }
     }
     if (g.a_kcontig && !g.b_kcontig) {
         switch (g.epi) {
-            case EPI_STORE: return launch_big<256, 256, 8, 2, true, false, EPI_STORE>(g, s);
-            case EPI_GELU_BWD: return launch_big<256, 256, 8, 2, true, false, EPI_GELU_BWD>(g, s);
+            case EPI_STORE: return BIG256(true, false, EPI_STORE);
+            case EPI_GELU_BWD: return BIG256(true, false, EPI_GELU_BWD);
             default: return hipErrorInvalidValue;
         }
     }
     if (!g.a_kcontig && !g.b_kcontig && g.epi == EPI_ACC_F32) {
         if (cdiv(g.M, 256) * cdiv(g.N, 256) >= 256)  // wide output (the classifier): no split needed
-            return launch_big<256, 256, 8, 2, false, false, EPI_ACC_F32>(g, s);
+            return BIG256(false, false, EPI_ACC_F32);
         int S, kc;
-        splitk_plan(g.M, g.N, g.K, &S, &kc);
+        splitk_plan(g.M, g.N, g.K, SK_TM, SK_TN, &S, &kc);
         if (S > 1 && g.ws && (size_t)S * g.M * g.N * 4 <= g.ws_bytes && g.N % 4 == 0 && g.ldo % 4 == 0) {
-            hipError_t e = launch_big<128, 128, 4, 3, false, false, EPI_PARTIAL>(g, s, S, kc);
+            hipError_t e = launch_big<128, 128, 4, 2, 32, 4, false, false, EPI_PARTIAL>(g, s, S, kc);
             if (e != hipSuccess) return e;
             int64_t n4 = (int64_t)g.M * g.N / 4;
             unsigned blocks = (unsigned)std::min<int64_t>((n4 + 255) / 256, 4096);
             splitk_reduce_kernel<<<blocks, 256, 0, s>>>((float*)g.out, g.ldo, g.ws, S, g.M, g.N);
             return hipGetLastError();
         }
-        return launch_big<128, 128, 4, 3, false, false, EPI_ACC_F32>(g, s);
+        return launch_big<128, 128, 4, 2, 32, 4, false, false, EPI_ACC_F32>(g, s);
     }
+#undef BIG256
     return hipErrorInvalidValue;
 }
 
 size_t gemm_splitk_ws_bytes(int M, int N, int K) {
     int S, kc;
-    splitk_plan(M, N, K, &S, &kc);
+    splitk_plan(M, N, K, SK_TM, SK_TN, &S, &kc);
     return S > 1 ? (size_t)S * M * N * 4 : 0;
 }

@@ -249,16 +249,17 @@ __global__ __launch_bounds__(256) void layernorm_bwd_kernel(T* dres, const T* dy
 }
 
 // out0[c] += sum_g partial[g][c]; out1[c] += sum_g partial[G+g][c] (if out1).
-// Block: 64 columns x 16 row lanes, each lane summing every 16th partial
-// row, then a fixed-order combine of the 16 lanes.
+// Block: 16 columns x 64 row lanes; lane r sums partial rows r, r+64, ...
+// (all its loads independent, so the whole array is in flight at once), then
+// the 64 lane sums of a column are combined in a fixed order.
 __global__ __launch_bounds__(1024) void sum_partials_kernel(float* out0, float* out1, const float* partial, int G,
                                                             int C) {
-    __shared__ float red[2][16][64];
-    const int cx = threadIdx.x & 63, ry = threadIdx.x >> 6;
-    const int c = blockIdx.x * 64 + cx;
+    __shared__ float red[2][64][17];
+    const int cx = threadIdx.x & 15, ry = threadIdx.x >> 4;
+    const int c = blockIdx.x * 16 + cx;
     float s0 = 0.f, s1 = 0.f;
     if (c < C) {
-        for (int g = ry; g < G; g += 16) {
+        for (int g = ry; g < G; g += 64) {
             s0 += partial[(int64_t)g * C + c];
             if (out1) s1 += partial[((int64_t)G + g) * C + c];
         }
@@ -266,11 +267,14 @@ __global__ __launch_bounds__(1024) void sum_partials_kernel(float* out0, float* 
     red[0][ry][cx] = s0;
     red[1][ry][cx] = s1;
     __syncthreads();
-    if (ry == 0 && c < C) {
-        float a = 0.f, b = 0.f;
-        for (int i = 0; i < 16; i++) { a += red[0][i][cx]; b += red[1][i][cx]; }
-        out0[c] += a;
-        if (out1) out1[c] += b;
+    if (threadIdx.x < 32) {
+        const int k = threadIdx.x >> 4;  // 0: out0, 1: out1
+        const int cc = blockIdx.x * 16 + cx;
+        if (cc < C && (k == 0 || out1)) {
+            float t = 0.f;
+            for (int i = 0; i < 64; i++) t += red[k][i][cx];
+            (k == 0 ? out0 : out1)[cc] += t;
+        }
     }
 }
 
@@ -291,7 +295,7 @@ hipError_t layernorm_bwd(T* dres, const T* dy, const T* x, const float* w, const
         layernorm_bwd_kernel<T, 4><<<G, 256, lds, s>>>(dres, dy, x, w, mean, rstd, partial, N, C, ow);
     else
         layernorm_bwd_kernel<T, 8><<<G, 256, lds, s>>>(dres, dy, x, w, mean, rstd, partial, N, C, ow);
-    sum_partials_kernel<<<cdiv(C, 64), 1024, 0, s>>>(dw, db, partial, G, C);
+    sum_partials_kernel<<<cdiv(C, 16), 1024, 0, s>>>(dw, db, partial, G, C);
     return LAUNCH_CHECK();
 }
 
@@ -337,7 +341,7 @@ hipError_t colsum_accum(float* dbias, const T* dy, int M, int N, float* partial,
     int G = COLSUM_G;
     dim3 grid(cdiv(N / VN, 64), G);
     colsum_kernel<T><<<grid, 256, 0, s>>>(partial, dy, M, N);
-    sum_partials_kernel<<<cdiv(N, 64), 1024, 0, s>>>(dbias, nullptr, partial, G, N);
+    sum_partials_kernel<<<cdiv(N, 16), 1024, 0, s>>>(dbias, nullptr, partial, G, N);
     return LAUNCH_CHECK();
 }
 
@@ -348,35 +352,47 @@ hipError_t colsum_accum(float* dbias, const T* dy, int M, int N, float* partial,
 // thread over the real columns v < V, pass 2 rewrites the row in place as
 // (softmax - onehot(target)) * dscale and zeros the padded columns.
 // ============================================================================
-constexpr int CE_THREADS = 1024;
-
-// block-wide max / sum over CE_THREADS threads (fixed combine order)
-DEVI float block_max(float x, float* sh) {
+// block-wide max / sum over NT threads (fixed combine order)
+template <int NT> DEVI float block_max(float x, float* sh) {
     x = wave_max(x);
-    __syncthreads();
     if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = x;
     __syncthreads();
     float r = sh[0];
-    for (int i = 1; i < CE_THREADS / 64; i++) r = fmaxf(r, sh[i]);
+#pragma unroll
+    for (int i = 1; i < NT / 64; i++) r = fmaxf(r, sh[i]);
+    __syncthreads();  // sh is reused by the next reduction
     return r;
 }
-DEVI float block_sum(float x, float* sh) {
+template <int NT> DEVI float block_sum(float x, float* sh) {
     x = wave_sum(x);
-    __syncthreads();
     if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = x;
     __syncthreads();
     float r = 0.f;
-    for (int i = 0; i < CE_THREADS / 64; i++) r += sh[i];
+#pragma unroll
+    for (int i = 0; i < NT / 64; i++) r += sh[i];
     return r;
 }
 
-// One block per row.  The row is read once into registers (MAXC 16-byte
-// chunks per thread), reduced, and written back once as dlogits.
-template <typename T, int MAXC>
-__global__ __launch_bounds__(CE_THREADS) void softmax_ce_kernel(T* logits, float* losses, const int* targets,
-                                                                int V, int Vp, float dscale, int* err) {
+// Makes the packed chunk opaque to the compiler, so that each pass widens it
+// again instead of keeping every widened value live across passes.
+template <typename T> DEVI void keep_packed(Vec16<T>& q) {
+    typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+    u32x4_t r;
+    __builtin_memcpy(&r, &q, 16);
+    asm volatile("" : "+v"(r));
+    __builtin_memcpy(&q, &r, 16);
+}
+
+// One block of NT threads per row.  The row is read once into registers
+// (MAXC 16-byte chunks per thread), reduced, and written back once as
+// dlogits.  NT is small (4 waves for bf16) so that several rows are in flight
+// per CU and the block reductions are short.
+template <typename T, int NT, int MAXC>
+__global__ __launch_bounds__(NT) void softmax_ce_kernel(T* logits, float* losses, const int* targets, int V, int Vp,
+                                                        float dscale, int* err) {
     constexpr int VN = Vec16<T>::N;
-    __shared__ float sh[CE_THREADS / 64];
+    constexpr float L2E = 1.4426950408889634f;
+    __shared__ float sh[NT / 64];
     __shared__ float s_zt;
     const int row = blockIdx.x;
     T* z = logits + (int64_t)row * Vp;
@@ -387,45 +403,52 @@ __global__ __launch_bounds__(CE_THREADS) void softmax_ce_kernel(T* logits, float
         tgt = 0;
     }
     Vec16<T> q[MAXC];
+#pragma unroll
+    for (int i = 0; i < MAXC; i++) {
+        const int ch = threadIdx.x + i * NT;
+        if (ch < chunks) q[i] = ld16(z + ch * VN);
+    }
     float mx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < MAXC; i++) {
-        const int ch = threadIdx.x + i * CE_THREADS;
+        const int ch = threadIdx.x + i * NT;
         if (ch < chunks) {
-            q[i] = ld16(z + ch * VN);
 #pragma unroll
             for (int j = 0; j < VN; j++) {
-                const int v = ch * VN + j;
                 const float x = to_f32(q[i].v[j]);
-                if (v < V) mx = fmaxf(mx, x);
-                if (v == tgt) s_zt = x;
+                if (ch * VN + j < V) mx = fmaxf(mx, x);
+                if (ch * VN + j == tgt) s_zt = x;  // static index: the row stays in registers
             }
         }
     }
-    const float M = block_max(mx, sh);
+    const float M2 = block_max<NT>(mx, sh) * L2E;  // row max, log2 units
+#pragma unroll
+    for (int i = 0; i < MAXC; i++) keep_packed(q[i]);
     float se = 0.f;
 #pragma unroll
     for (int i = 0; i < MAXC; i++) {
-        const int ch = threadIdx.x + i * CE_THREADS;
+        const int ch = threadIdx.x + i * NT;
         if (ch < chunks) {
 #pragma unroll
             for (int j = 0; j < VN; j++)
-                if (ch * VN + j < V) se += __expf(to_f32(q[i].v[j]) - M);
+                if (ch * VN + j < V) se += __builtin_amdgcn_exp2f(fmaf(to_f32(q[i].v[j]), L2E, -M2));
         }
     }
-    const float S = block_sum(se, sh);  // its barriers also publish s_zt
-    if (threadIdx.x == 0) losses[row] = M + logf(S) - s_zt;
-    const float invS = 1.f / S;
+    const float S = block_sum<NT>(se, sh);  // its barrier also publishes s_zt
+    if (threadIdx.x == 0) losses[row] = (M2 + __log2f(S)) * 0.6931471805599453f - s_zt;
+    const float ps = dscale / S;  // softmax scale folded with the loss-mean factor
+#pragma unroll
+    for (int i = 0; i < MAXC; i++) keep_packed(q[i]);
 #pragma unroll
     for (int i = 0; i < MAXC; i++) {
-        const int ch = threadIdx.x + i * CE_THREADS;
+        const int ch = threadIdx.x + i * NT;
         if (ch < chunks) {
             Vec16<T> o;
 #pragma unroll
             for (int j = 0; j < VN; j++) {
                 const int v = ch * VN + j;
-                float d = 0.f;
-                if (v < V) d = (__expf(to_f32(q[i].v[j]) - M) * invS - (v == tgt ? 1.f : 0.f)) * dscale;
+                float d = v < V ? __builtin_amdgcn_exp2f(fmaf(to_f32(q[i].v[j]), L2E, -M2)) * ps : 0.f;
+                if (v == tgt) d -= dscale;
                 o.v[j] = from_f32<T>(d);
             }
             st16(z + ch * VN, o);
@@ -433,23 +456,27 @@ __global__ __launch_bounds__(CE_THREADS) void softmax_ce_kernel(T* logits, float
     }
 }
 
+template <typename T, int NT>
+hipError_t softmax_ce_nt(T* logits, float* losses, const int* targets, int BT, int V, int Vp, float dscale, int* err,
+                         hipStream_t s) {
+    constexpr int VN = Vec16<T>::N;
+    const int per = (int)cdiv(Vp / VN, NT);
+    if (per <= 4) softmax_ce_kernel<T, NT, 4><<<BT, NT, 0, s>>>(logits, losses, targets, V, Vp, dscale, err);
+    else if (per <= 8) softmax_ce_kernel<T, NT, 8><<<BT, NT, 0, s>>>(logits, losses, targets, V, Vp, dscale, err);
+    else if (per <= 16) softmax_ce_kernel<T, NT, 16><<<BT, NT, 0, s>>>(logits, losses, targets, V, Vp, dscale, err);
+    else if (per <= 25) softmax_ce_kernel<T, NT, 25><<<BT, NT, 0, s>>>(logits, losses, targets, V, Vp, dscale, err);
+    else if (per <= 32) softmax_ce_kernel<T, NT, 32><<<BT, NT, 0, s>>>(logits, losses, targets, V, Vp, dscale, err);
+    else return hipErrorInvalidValue;
+    return LAUNCH_CHECK();
+}
+
 template <typename T>
 hipError_t softmax_ce(T* logits, float* losses, const int* targets, int BT, int V, int Vp, float dscale, int* err,
                       hipStream_t s) {
-    constexpr int VN = Vec16<T>::N;
-    if (Vp % VN) return hipErrorInvalidValue;
-    const int per = (int)cdiv(Vp / VN, CE_THREADS);
-    if (per <= 2)
-        softmax_ce_kernel<T, 2><<<BT, CE_THREADS, 0, s>>>(logits, losses, targets, V, Vp, dscale, err);
-    else if (per <= 4)
-        softmax_ce_kernel<T, 4><<<BT, CE_THREADS, 0, s>>>(logits, losses, targets, V, Vp, dscale, err);
-    else if (per <= 8)
-        softmax_ce_kernel<T, 8><<<BT, CE_THREADS, 0, s>>>(logits, losses, targets, V, Vp, dscale, err);
-    else if (per <= 16)
-        softmax_ce_kernel<T, 16><<<BT, CE_THREADS, 0, s>>>(logits, losses, targets, V, Vp, dscale, err);
-    else
-        return hipErrorInvalidValue;  // rows above 16K chunks (Vp > 131072 bf16) are not supported
-    return LAUNCH_CHECK();
+    if (Vp % Vec16<T>::N) return hipErrorInvalidValue;
+    // 256 threads per bf16 row, 512 per fp32 row: rows up to 65536 (bf16) or 65536 (fp32) columns
+    if constexpr (std::is_same<T, bf16>::value) return softmax_ce_nt<T, 256>(logits, losses, targets, BT, V, Vp, dscale, err, s);
+    else return softmax_ce_nt<T, 512>(logits, losses, targets, BT, V, Vp, dscale, err, s);
 }
 
 // mean of n losses, summed in a fixed order in double by one block
@@ -514,26 +541,29 @@ hipError_t grad_norm(float* partial, float* norm_scale, const float* g, size_t n
 // AdamW (decoupled weight decay, bias-corrected; c1 = 1-b1^t, c2 = 1-b2^t),
 // gradient times the clip factor norm_scale[1]; refreshes the bf16 shadow.
 // ============================================================================
+// ic1 = 1 / (1 - b1^t), ic2 = 1 / (1 - b2^t)
 DEVI void adamw_one(float& p, float g, float& m, float& v, float lr, float b1, float b2, float eps, float wd,
-                    float c1, float c2) {
-    m = b1 * m + (1.f - b1) * g;
-    v = b2 * v + (1.f - b2) * g * g;
-    float mh = m / c1, vh = v / c2;
-    p = p - lr * (mh / (sqrtf(vh) + eps) + wd * p);
+                    float ic1, float ic2) {
+    m = fmaf(b1, m, (1.f - b1) * g);
+    v = fmaf(b2, v, (1.f - b2) * g * g);
+    const float mh = m * ic1, vh = v * ic2;
+    p = p - lr * (mh * __builtin_amdgcn_rcpf(sqrtf(vh) + eps) + wd * p);
 }
 
+// Each block updates ADAM_U x 256 float4 groups; group u of a block sits at
+// (block * ADAM_U + u) * 256 + thread, so every load and store instruction
+// covers 4 KB contiguously.  All loads of a thread are issued first.
+constexpr int ADAM_U = 4;
 __global__ __launch_bounds__(256) void adamw_kernel(float* p, const float* g, float* m, float* v, bf16* shadow,
                                                     size_t n, float lr, float b1, float b2, float eps, float wd,
-                                                    float c1, float c2, const float* norm_scale) {
+                                                    float ic1, float ic2, const float* norm_scale) {
     typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
     const float sc = norm_scale ? norm_scale[1] : 1.f;
     const size_t n4 = n / 4;
-    // each thread updates two float4 groups, with all eight loads issued first
-    const size_t i0 = ((size_t)blockIdx.x * 256 + threadIdx.x) * 2;
-    float4 pp[2], gg[2], mm[2], vv[2];
+    float4 pp[ADAM_U], gg[ADAM_U], mm[ADAM_U], vv[ADAM_U];
 #pragma unroll
-    for (int u = 0; u < 2; u++) {
-        const size_t i = i0 + u;
+    for (int u = 0; u < ADAM_U; u++) {
+        const size_t i = ((size_t)blockIdx.x * ADAM_U + u) * 256 + threadIdx.x;
         if (i < n4) {
             pp[u] = reinterpret_cast<const float4*>(p)[i];
             gg[u] = reinterpret_cast<const float4*>(g)[i];
@@ -542,13 +572,13 @@ __global__ __launch_bounds__(256) void adamw_kernel(float* p, const float* g, fl
         }
     }
 #pragma unroll
-    for (int u = 0; u < 2; u++) {
-        const size_t i = i0 + u;
+    for (int u = 0; u < ADAM_U; u++) {
+        const size_t i = ((size_t)blockIdx.x * ADAM_U + u) * 256 + threadIdx.x;
         if (i < n4) {
-            adamw_one(pp[u].x, gg[u].x * sc, mm[u].x, vv[u].x, lr, b1, b2, eps, wd, c1, c2);
-            adamw_one(pp[u].y, gg[u].y * sc, mm[u].y, vv[u].y, lr, b1, b2, eps, wd, c1, c2);
-            adamw_one(pp[u].z, gg[u].z * sc, mm[u].z, vv[u].z, lr, b1, b2, eps, wd, c1, c2);
-            adamw_one(pp[u].w, gg[u].w * sc, mm[u].w, vv[u].w, lr, b1, b2, eps, wd, c1, c2);
+            adamw_one(pp[u].x, gg[u].x * sc, mm[u].x, vv[u].x, lr, b1, b2, eps, wd, ic1, ic2);
+            adamw_one(pp[u].y, gg[u].y * sc, mm[u].y, vv[u].y, lr, b1, b2, eps, wd, ic1, ic2);
+            adamw_one(pp[u].z, gg[u].z * sc, mm[u].z, vv[u].z, lr, b1, b2, eps, wd, ic1, ic2);
+            adamw_one(pp[u].w, gg[u].w * sc, mm[u].w, vv[u].w, lr, b1, b2, eps, wd, ic1, ic2);
             reinterpret_cast<float4*>(p)[i] = pp[u];
             reinterpret_cast<float4*>(m)[i] = mm[u];
             reinterpret_cast<float4*>(v)[i] = vv[u];
@@ -561,7 +591,7 @@ __global__ __launch_bounds__(256) void adamw_kernel(float* p, const float* g, fl
     if (blockIdx.x == 0 && threadIdx.x < (n & 3)) {
         const size_t i = n4 * 4 + threadIdx.x;
         float a = p[i], b = m[i], c = v[i];
-        adamw_one(a, g[i] * sc, b, c, lr, b1, b2, eps, wd, c1, c2);
+        adamw_one(a, g[i] * sc, b, c, lr, b1, b2, eps, wd, ic1, ic2);
         p[i] = a;
         m[i] = b;
         v[i] = c;
@@ -571,8 +601,9 @@ __global__ __launch_bounds__(256) void adamw_kernel(float* p, const float* g, fl
 
 hipError_t adamw(float* p, const float* g, float* m, float* v, bf16* shadow, size_t n, float lr, float b1, float b2,
                  float eps, float wd, float c1, float c2, const float* norm_scale, hipStream_t s) {
-    const size_t blocks = cdiv(n / 4, 512) + 1;
-    adamw_kernel<<<(unsigned)blocks, 256, 0, s>>>(p, g, m, v, shadow, n, lr, b1, b2, eps, wd, c1, c2, norm_scale);
+    const size_t blocks = cdiv(n / 4, 256 * ADAM_U) + 1;
+    adamw_kernel<<<(unsigned)blocks, 256, 0, s>>>(p, g, m, v, shadow, n, lr, b1, b2, eps, wd, 1.f / c1, 1.f / c2,
+                                                  norm_scale);
     return LAUNCH_CHECK();
 }
 

@@ -130,6 +130,21 @@ DEVI constexpr int acc_off(int r) { return ((r >> 2) << 3) + (r & 3); }  // acc_
 
 DEVI float exp2_raw(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Block placement on a 1-D grid of nblk blocks per (batch, head): workgroup
+// L runs on XCD L % 8, so when the grid size is a multiple of 8 each XCD
+// takes a contiguous range of work, i.e. all blocks of a few heads, whose
+// K/V (or Q/dO) re-reads then hit that XCD's L2.  Returns the block index
+// within the head (0 = first launched) and the head's (b, h).
+DEVI int place_block(int nblk, int NH, int* h, int* b) {
+    const int total = gridDim.x;
+    int w = blockIdx.x;
+    if ((total & 7) == 0) w = (w & 7) * (total >> 3) + (w >> 3);
+    const int bh = w / nblk;
+    *h = bh % NH;
+    *b = bh / NH;
+    return w % nblk;
+}
+
 // The stages are distinct __shared__ arrays so that alias analysis keeps the
 // reads of one stage independent of the loads in flight into another; each
 // step waits only for its own stage (explicit vmcnt), then a raw barrier.
@@ -145,8 +160,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     __shared__ __attribute__((aligned(1024))) bf16 k0s[TILE], k1s[TILE], k2s[TILE];
     __shared__ __attribute__((aligned(1024))) bf16 v0s[TILE], v1s[TILE], v2s[TILE];
     const int nqb = (T + QB - 1) / QB;
-    const int qblk = nqb - 1 - (int)blockIdx.x;  // longest rows first
-    const int h = blockIdx.y, b = blockIdx.z;
+    int h, b;
+    const int qblk = nqb - 1 - place_block(nqb, NH, &h, &b);  // longest rows first
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hi = lane >> 5, lq = lane & 31;
     const int C3 = 3 * C;
     const bf16* base = qkv + (int64_t)b * T * C3;
@@ -265,8 +280,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     __shared__ __attribute__((aligned(1024))) bf16 k0s[TILE], k1s[TILE], k2s[TILE];
     __shared__ __attribute__((aligned(1024))) bf16 v0s[TILE], v1s[TILE], v2s[TILE];
     const int nqb = (T + QB - 1) / QB;
-    const int qblk = nqb - 1 - (int)blockIdx.x;
-    const int h = blockIdx.y, b = blockIdx.z;
+    int h, b;
+    const int qblk = nqb - 1 - place_block(nqb, NH, &h, &b);
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hi = lane >> 5, lq = lane & 31;
     const int C3 = 3 * C;
     const bf16* base = qkv + (int64_t)b * T * C3;
@@ -388,8 +403,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     __shared__ __attribute__((aligned(1024))) bf16 q0s[TILE], q1s[TILE], q2s[TILE];
     __shared__ __attribute__((aligned(1024))) bf16 o0s[TILE], o1s[TILE], o2s[TILE];  // dO
     __shared__ __attribute__((aligned(1024))) float st0[4 * 256], st1[4 * 256], st2[4 * 256];
-    const int kblk = blockIdx.x;  // the first key blocks see the most queries: launched first
-    const int h = blockIdx.y, b = blockIdx.z;
+    int h, b;
+    const int kblk = place_block((T + QB - 1) / QB, NH, &h, &b);  // the first key blocks see the most queries
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hi = lane >> 5, lq = lane & 31;
     const int C3 = 3 * C;
     const bf16* base = qkv + (int64_t)b * T * C3;
@@ -506,7 +521,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
 hipError_t flash_attention_fwd(bf16* out, float* lse, const bf16* qkv, int B, int T, int C, int NH, hipStream_t s) {
     if (C / NH != HS || C % NH || T % KB) return hipErrorInvalidValue;
-    dim3 grid((T + QB - 1) / QB, NH, B);
+    const unsigned grid = (unsigned)((T + QB - 1) / QB * NH * B);
     flash_fwd_kernel<<<grid, 256, 0, s>>>(out, lse, qkv, T, C, NH);
     return hipGetLastError();
 }
@@ -514,7 +529,7 @@ hipError_t flash_attention_fwd(bf16* out, float* lse, const bf16* qkv, int B, in
 hipError_t flash_attention_bwd(bf16* dqkv, const bf16* dout, const bf16* qkv, const bf16* out, const float* lse,
                                float* dbuf, int B, int T, int C, int NH, hipStream_t s) {
     if (C / NH != HS || C % NH || T % KB) return hipErrorInvalidValue;
-    dim3 grid((T + QB - 1) / QB, NH, B);
+    const unsigned grid = (unsigned)((T + QB - 1) / QB * NH * B);
     const int64_t rows = (int64_t)B * NH * T;
     flash_bwd_dq_kernel<<<grid, 256, 0, s>>>(dqkv, dbuf, dbuf + rows, dout, qkv, out, lse, T, C, NH);
     flash_bwd_dkdv_kernel<<<grid, 256, 0, s>>>(dqkv, dbuf, dbuf + rows, dout, qkv, T, C, NH);

@@ -39,7 +39,8 @@ constexpr int EPI_PARTIAL = 100;  // split-K partial tile into g.ws[split][M][N]
 template <int RH, int TN> constexpr int red_bytes() { return RH * (TN + 4) * 4; }
 
 template <int EPI, int RH, int FM, int FN>
-DEVI void epilogue_rows(const GemmArgs& g, const f32x16 (&acc)[FM][FN], float* red, int mrow0, int ncol0, int lane) {
+DEVI void epilogue_rows(const GemmArgs& g, const f32x16 (&acc)[FM][FN], float* red, int mrow0, int ncol0, int split,
+                        int lane) {
     constexpr int TN = FN * 32, P = TN + 4;
     constexpr int LPR = TN / 8;    // lanes per output row
     constexpr int RPI = 64 / LPR;  // rows per access instruction
@@ -96,7 +97,7 @@ DEVI void epilogue_rows(const GemmArgs& g, const f32x16 (&acc)[FM][FN], float* r
             if (m >= g.M || !nok) continue;
             const int64_t o = (int64_t)m * g.ldo + n;
             if constexpr (EPI == EPI_PARTIAL) {
-                float* w = g.ws + ((int64_t)blockIdx.y * g.M + m) * g.N + n;
+                float* w = g.ws + ((int64_t)split * g.M + m) * g.N + n;
                 *reinterpret_cast<float4*>(w) = u;
                 *reinterpret_cast<float4*>(w + 4) = v;
                 continue;
@@ -264,9 +265,16 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const int wm = wave / WAVES_N, wn = wave % WAVES_N;
 
     const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
-    int bid = blockIdx.x;
-    const int total = gridDim.x;
-    if ((total & 7) == 0) bid = (bid & 7) * (total >> 3) + (bid >> 3);  // neighbouring tiles on one XCD
+    // Workgroup L (linear id, x fastest) runs on XCD L % 8.  Give each XCD a
+    // contiguous range of (split, tile) work in split-major order, so that
+    // the tiles sharing operand panels (same split, neighbouring tiles) share
+    // one L2.
+    const int tiles = gridDim.x;
+    int work = blockIdx.x + blockIdx.y * tiles;
+    const int total = tiles * gridDim.y;
+    if ((total & 7) == 0) work = (work & 7) * (total >> 3) + (work >> 3);
+    const int split = work / tiles;
+    int bid = work % tiles;
     constexpr int GM = 8;
     const int group = bid / (GM * tiles_n);
     const int first_m = group * GM;
@@ -285,7 +293,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
             for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
 
-    const int kbeg = blockIdx.y * kchunk;
+    const int kbeg = split * kchunk;
     const int nk = (min(g.K, kbeg + kchunk) - kbeg) / KB;
     const int klast = kbeg + (nk - 1) * KB;
     Dma<BM, NW, KB, AK> da;
@@ -357,7 +365,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
             case 6: region = sa3; break;
             default: region = sb3; break;
         }
-        epilogue_rows<EPI, RH>(g, acc, reinterpret_cast<float*>(region), m0 + wm * TM, n0 + wn * TN, lane);
+        epilogue_rows<EPI, RH>(g, acc, reinterpret_cast<float*>(region), m0 + wm * TM, n0 + wn * TN, split, lane);
     }
 }
 
@@ -378,6 +386,9 @@ void splitk_plan(int M, int N, int K, int tm, int tn, int* splits, int* kchunk) 
     int smax = K / 256;
     if (S > smax) S = smax;
     if (S < 1) S = 1;
+    // a grid that is a multiple of 8 lets the kernel keep each split on one XCD
+    for (int t = S; t <= smax && t < 2 * S; t++)
+        if ((tiles * t) % 8 == 0) { S = t; break; }
     int kc = (int)cdiv(K / KALIGN, S) * KALIGN;
     *kchunk = kc;
     *splits = (K + kc - 1) / kc;

@@ -92,7 +92,7 @@ def main():
     ap.add_argument("--config", default="124m", choices=sorted(CONFIGS))
     ap.add_argument("--seed", type=int, default=1337)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample", default="2x256", help="BxT of the oracle sample")
+    ap.add_argument("--cpu-sample", default="4x512", help="BxT of the oracle sample")
     ap.add_argument("--timing-class", default="auto")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -179,6 +179,9 @@ def main():
         achieved = per_launch / (avg_ms / 1e3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
+    from transformer_lm_train_amd import pmc_traffic
+    traffic = pmc_traffic.recorded(dom)  # bytes per launch from the committed counter runs, if still current
+    roof["traffic"] = traffic
     roof["kernel"] = dom
     roof["avg_launch_ms"] = round(avg_ms, 4)
     roof["launches"] = launches

@@ -13,12 +13,28 @@
 // Block ids are remapped so that the tiles one XCD (one L2) runs are
 // neighbours sharing operand panels.
 #include <algorithm>
+#include <type_traits>
 
 #include "kernels.h"
 
 namespace {
 
 constexpr int KALIGN = 64;  // K, and every split-K chunk, is a multiple of this
+
+// LDS stages and schedule of the two tile shapes in use (256x256 for the
+// forward and backward-data products, 128x128 for split weight gradients).
+#ifndef GEMM_BIG_NS
+#define GEMM_BIG_NS 4
+#endif
+#ifndef GEMM_BIG_XPF
+#define GEMM_BIG_XPF false
+#endif
+#ifndef GEMM_SPLIT_NS
+#define GEMM_SPLIT_NS 5
+#endif
+#ifndef GEMM_SPLIT_XPF
+#define GEMM_SPLIT_XPF true
+#endif
 
 constexpr int EPI_PARTIAL = 100;  // split-K partial tile into g.ws[split][M][N]
 
@@ -222,45 +238,101 @@ DEVI bf16x8 frag_any(const uint16_t* tile, int row0, int kk, int lane) {
     }
 }
 
-template <int BM, int BN, int KB, int FM, int FN, int TM, int TN, bool AK, bool BKC>
-DEVI void mfma_any(f32x16 (&acc)[FM][FN], const uint16_t* As, const uint16_t* Bs, int wm, int wn, int lane) {
-    bf16x8 a[2][FM], b[2][FN];
+// Scheduling order of one sub-step: its NM MFMAs alternate with the NR LDS
+// reads of the next sub-step (mask 0x008: MFMA, 0x100: DS read), so reads
+// trickle out while the matrix core is busy and few are outstanding at once.
+template <int NM, int NR, int Q = 0> DEVI void interleave_mfma_reads() {
+    if constexpr (Q < NM || Q < NR) {
+        if constexpr (Q < NM) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if constexpr (Q < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        interleave_mfma_reads<NM, NR, Q + 1>();
+    }
+}
+
+// One k-step of the wave's FM x FN block of 32x32 accumulators.  The
+// fragments of sub-step s+1 are read while the MFMAs of sub-step s run.
+// XPF: fa / fb hold the fragments of sub-step 0 on entry, and the last
+// sub-step reads sub-step 0 of the next stage (nA / nB) into them, so the next
+// k-step can start its MFMAs right after its barrier.  Otherwise sub-step 0
+// is read here, after the barrier.
+template <int BM, int BN, int KB, int FM, int FN, int TM, int TN, bool AK, bool BKC, bool XPF>
+DEVI void mfma_step(f32x16 (&acc)[FM][FN], bf16x8 (&fa)[FM], bf16x8 (&fb)[FN], const uint16_t* As,
+                    const uint16_t* Bs, const uint16_t* nA, const uint16_t* nB, int wm, int wn, int lane) {
+    constexpr int KS = KB / 16;
+    static_assert(KS % 2 == 0, "sub-steps come in pairs");
     constexpr int NRD = FM * (AK ? 1 : 2) + FN * (BKC ? 1 : 2);  // LDS read instructions per sub-step
+    bf16x8 a[2][FM], b[2][FN];
+    // fragment reads in the order of first use by the i-major MFMA loop
+    // (a0, b0 .. b[FN-1], a1 .. a[FM-1]), so the next sub-step's first MFMAs
+    // wait only for reads issued several MFMAs earlier
+    auto read_frags = [&](bf16x8 (&ra)[FM], bf16x8 (&rb)[FN], const uint16_t* ta, const uint16_t* tb, int kk) {
+        ra[0] = frag_any<BM, KB, AK>(ta, wm * TM, kk, lane);
 #pragma unroll
-    for (int i = 0; i < FM; i++) a[0][i] = frag_any<BM, KB, AK>(As, wm * TM + i * 32, 0, lane);
+        for (int j = 0; j < FN; j++) rb[j] = frag_any<BN, KB, BKC>(tb, wn * TN + j * 32, kk, lane);
 #pragma unroll
-    for (int j = 0; j < FN; j++) b[0][j] = frag_any<BN, KB, BKC>(Bs, wn * TN + j * 32, 0, lane);
-    __builtin_amdgcn_sched_group_barrier(0x100, NRD, 0);
+        for (int i = 1; i < FM; i++) ra[i] = frag_any<BM, KB, AK>(ta, wm * TM + i * 32, kk, lane);
+    };
+    if constexpr (XPF) {
 #pragma unroll
-    for (int ks = 0; ks < KB / 16; ks++) {
-        if (ks + 1 < KB / 16) {
+        for (int i = 0; i < FM; i++) a[0][i] = fa[i];
 #pragma unroll
-            for (int i = 0; i < FM; i++)
-                a[(ks + 1) & 1][i] = frag_any<BM, KB, AK>(As, wm * TM + i * 32, (ks + 1) * 16, lane);
+        for (int j = 0; j < FN; j++) b[0][j] = fb[j];
+    } else {
+        read_frags(a[0], b[0], As, Bs, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, NRD, 0);
+    }
 #pragma unroll
-            for (int j = 0; j < FN; j++)
-                b[(ks + 1) & 1][j] = frag_any<BN, KB, BKC>(Bs, wn * TN + j * 32, (ks + 1) * 16, lane);
-        }
+    for (int ks = 0; ks < KS; ks++) {
+        const uint16_t* ta = ks + 1 < KS ? As : nA;
+        const uint16_t* tb = ks + 1 < KS ? Bs : nB;
+        const int kk = ks + 1 < KS ? (ks + 1) * 16 : 0;
+        if (XPF || ks + 1 < KS) read_frags(a[(ks + 1) & 1], b[(ks + 1) & 1], ta, tb, kk);
 #pragma unroll
         for (int i = 0; i < FM; i++)
 #pragma unroll
             for (int j = 0; j < FN; j++)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[ks & 1][j], a[ks & 1][i], acc[i][j], 0, 0, 0);
-        // keep the next sub-step's LDS reads (mask 0x100) ahead of this
-        // sub-step's MFMAs (mask 0x008) through scheduling
-        if (ks + 1 < KB / 16) __builtin_amdgcn_sched_group_barrier(0x100, NRD, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, FM * FN, 0);
+        if (XPF || ks + 1 < KS) interleave_mfma_reads<FM * FN, NRD>();
+        else __builtin_amdgcn_sched_group_barrier(0x008, FM * FN, 0);
+    }
+    if constexpr (XPF) {
+#pragma unroll
+        for (int i = 0; i < FM; i++) fa[i] = a[0][i];
+#pragma unroll
+        for (int j = 0; j < FN; j++) fb[j] = b[0][j];
     }
 }
 
-template <int BM, int BN, int NW, int WAVES_M, int KB, int NS, bool AK, bool BKC, int EPI>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_big_kernel(GemmArgs g, int kchunk) {
+// OCC: waves per SIMD the register allocation targets (2: up to 256
+// registers; 1: up to 512, accumulators in AGPRs)
+template <int BM, int BN, int NW, int WAVES_M, int KB, int NS, bool XPF, bool AK, bool BKC, int EPI, int OCC = 2>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void gemm_big_kernel(GemmArgs g, int kchunk) {
     constexpr int WAVES_N = NW / WAVES_M;
     constexpr int TM = BM / WAVES_M, TN = BN / WAVES_N, FM = TM / 32, FN = TN / 32;
-    static_assert(NS >= 2 && NS <= 4, "stages");
+    static_assert(NS >= 3 && NS <= 5, "stages");
     constexpr int SA = BM * KB, SB = BN * KB;
-    __shared__ __attribute__((aligned(1024))) uint16_t sa0[SA], sa1[SA], sa2[NS > 2 ? SA : 8], sa3[NS > 3 ? SA : 8];
-    __shared__ __attribute__((aligned(1024))) uint16_t sb0[SB], sb1[SB], sb2[NS > 2 ? SB : 8], sb3[NS > 3 ? SB : 8];
+    // one array per stage (alias analysis then keeps the reads of one stage
+    // independent of the loads in flight into another)
+    __shared__ __attribute__((aligned(1024))) uint16_t sa0[SA], sa1[SA], sa2[SA], sa3[NS > 3 ? SA : 8],
+        sa4[NS > 4 ? SA : 8];
+    __shared__ __attribute__((aligned(1024))) uint16_t sb0[SB], sb1[SB], sb2[SB], sb3[NS > 3 ? SB : 8],
+        sb4[NS > 4 ? SB : 8];
+    auto stA = [&](auto J) -> uint16_t* {
+        constexpr int j = decltype(J)::value % NS;
+        if constexpr (j == 0) return sa0;
+        else if constexpr (j == 1) return sa1;
+        else if constexpr (j == 2) return sa2;
+        else if constexpr (j == 3) return sa3;
+        else return sa4;
+    };
+    auto stB = [&](auto J) -> uint16_t* {
+        constexpr int j = decltype(J)::value % NS;
+        if constexpr (j == 0) return sb0;
+        else if constexpr (j == 1) return sb1;
+        else if constexpr (j == 2) return sb2;
+        else if constexpr (j == 3) return sb3;
+        else return sb4;
+    };
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WAVES_N, wn = wave % WAVES_N;
 
@@ -306,52 +378,63 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         da.issue(ta, A, AK ? (int64_t)k0 : (int64_t)k0 * g.lda, wave);
         db.issue(tb, B, BKC ? (int64_t)k0 : (int64_t)k0 * g.ldb, wave);
     };
-    // stage kt landed for every wave, and every wave is done with the stage
-    // the next load overwrites; then load k-step kt + NS - 1 and compute kt
-    auto step = [&](const uint16_t* ca, const uint16_t* cb, uint16_t* na, uint16_t* nb, int kt) {
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm<(NS - 2) * LPS>());
+    // Step kt (stage kt % NS): wait for this wave's loads of k-step kt + 1
+    // (XPF) or kt, barrier (that k-step is then in LDS for every wave, and
+    // every wave is done with k-step kt - 1), load k-step kt + NS - 1 over
+    // k-step kt - 1, then the MFMAs of k-step kt.  XPF starts them from
+    // fragments already in registers and reads the first fragments of k-step
+    // kt + 1 at the end, at the price of one k-step less of load latency cover.
+    static_assert(!XPF || NS >= 3, "cross-barrier prefetch needs 3 stages");
+    bf16x8 fa[FM], fb[FN];
+    auto step = [&](auto J, int kt) {
+        constexpr int j = decltype(J)::value;
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm<(XPF ? NS - 3 : NS - 2) * LPS>());
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        dma(na, nb, min(kbeg + (kt + NS - 1) * KB, klast));
-        mfma_any<BM, BN, KB, FM, FN, TM, TN, AK, BKC>(acc, ca, cb, wm, wn, lane);
+        dma(stA(std::integral_constant<int, j + NS - 1>{}), stB(std::integral_constant<int, j + NS - 1>{}),
+            min(kbeg + (kt + NS - 1) * KB, klast));
+        mfma_step<BM, BN, KB, FM, FN, TM, TN, AK, BKC, XPF>(acc, fa, fb, stA(J), stB(J),
+                                                       stA(std::integral_constant<int, j + 1>{}),
+                                                       stB(std::integral_constant<int, j + 1>{}), wm, wn, lane);
     };
+    typedef std::integral_constant<int, 0> I0;
+    typedef std::integral_constant<int, 1> I1;
+    typedef std::integral_constant<int, 2> I2;
+    typedef std::integral_constant<int, 3> I3;
+    typedef std::integral_constant<int, 4> I4;
 
     dma(sa0, sb0, kbeg);
-    if constexpr (NS > 2) dma(sa1, sb1, min(kbeg + KB, klast));
+    dma(sa1, sb1, min(kbeg + KB, klast));
     if constexpr (NS > 3) dma(sa2, sb2, min(kbeg + 2 * KB, klast));
-    int kt = 0;
-    if constexpr (NS == 2) {
-        for (; kt + 2 <= nk; kt += 2) {
-            step(sa0, sb0, sa1, sb1, kt);
-            step(sa1, sb1, sa0, sb0, kt + 1);
-        }
-        if (kt < nk) step(sa0, sb0, sa1, sb1, kt);
-    } else if constexpr (NS == 3) {
-        for (; kt + 3 <= nk; kt += 3) {
-            step(sa0, sb0, sa2, sb2, kt);
-            step(sa1, sb1, sa0, sb0, kt + 1);
-            step(sa2, sb2, sa1, sb1, kt + 2);
-        }
-        if (kt < nk) { step(sa0, sb0, sa2, sb2, kt); kt++; }
-        if (kt < nk) step(sa1, sb1, sa0, sb0, kt);
-    } else {
-        for (; kt + 4 <= nk; kt += 4) {
-            step(sa0, sb0, sa3, sb3, kt);
-            step(sa1, sb1, sa0, sb0, kt + 1);
-            step(sa2, sb2, sa1, sb1, kt + 2);
-            step(sa3, sb3, sa2, sb2, kt + 3);
-        }
-        if (kt < nk) { step(sa0, sb0, sa3, sb3, kt); kt++; }
-        if (kt < nk) { step(sa1, sb1, sa0, sb0, kt); kt++; }
-        if (kt < nk) step(sa2, sb2, sa1, sb1, kt);
+    if constexpr (NS > 4) dma(sa3, sb3, min(kbeg + 3 * KB, klast));
+    if constexpr (XPF) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm<(NS - 2) * LPS>());  // k-step 0
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int i = 0; i < FM; i++) fa[i] = frag_any<BM, KB, AK>(sa0, wm * TM + i * 32, 0, lane);
+#pragma unroll
+        for (int jj = 0; jj < FN; jj++) fb[jj] = frag_any<BN, KB, BKC>(sb0, wn * TN + jj * 32, 0, lane);
     }
+    int kt = 0;
+    for (; kt + NS <= nk; kt += NS) {
+        step(I0{}, kt);
+        step(I1{}, kt + 1);
+        step(I2{}, kt + 2);
+        if constexpr (NS > 3) step(I3{}, kt + 3);
+        if constexpr (NS > 4) step(I4{}, kt + 4);
+    }
+    if (kt < nk) { step(I0{}, kt); kt++; }
+    if (kt < nk) { step(I1{}, kt); kt++; }
+    if constexpr (NS > 3) if (kt < nk) { step(I2{}, kt); kt++; }
+    if constexpr (NS > 4) if (kt < nk) { step(I3{}, kt); kt++; }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());  // no load may still be writing LDS at exit
 
     // The stage buffers become the epilogue's per-wave regions once every
     // wave is past its last LDS read.
     constexpr int RBYTES = 2 * (BN < BM ? BN : BM) * KB;  // smallest stage array
     constexpr int RH = red_bytes<32, TN>() <= RBYTES ? 32 : 16;
-    static_assert(NW <= 2 * NS && red_bytes<RH, TN>() <= RBYTES, "epilogue regions must fit the stage buffers");
+    static_assert(NW <= 8 && NW <= 2 * NS && red_bytes<RH, TN>() <= RBYTES, "epilogue regions must fit the stage buffers");
     {
         __syncthreads();
         uint16_t* region;
@@ -369,10 +452,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     }
 }
 
-template <int BM, int BN, int NW, int WAVES_M, int KB, int NS, bool AK, bool BKC, int EPI>
+template <int BM, int BN, int NW, int WAVES_M, int KB, int NS, bool XPF, bool AK, bool BKC, int EPI, int OCC = 2>
 hipError_t launch_big(const GemmArgs& g, hipStream_t s, int splits = 1, int kchunk = 0) {
     dim3 grid(cdiv(g.M, BM) * cdiv(g.N, BN), splits);
-    gemm_big_kernel<BM, BN, NW, WAVES_M, KB, NS, AK, BKC, EPI><<<grid, NW * 64, 0, s>>>(g, kchunk ? kchunk : g.K);
+    gemm_big_kernel<BM, BN, NW, WAVES_M, KB, NS, XPF, AK, BKC, EPI, OCC>
+        <<<grid, NW * 64, 0, s>>>(g, kchunk ? kchunk : g.K);
     return hipGetLastError();
 }
 
@@ -426,7 +510,7 @@ hipError_t gemm_mfma_bf16(const GemmArgs& g, hipStream_t s) {
     // Tile choice from timings at the GPT-2 shapes on gfx950: the 256 x 256
     // tile (8 waves of 128 x 64, k-step 32, 4 LDS stages) leads or ties in
     // every forward and backward-data product.
-#define BIG256(AKC, BKCC, E) launch_big<256, 256, 8, 2, 32, 4, AKC, BKCC, E>(g, s)
+#define BIG256(AKC, BKCC, E) launch_big<256, 256, 8, 2, 32, GEMM_BIG_NS, GEMM_BIG_XPF, AKC, BKCC, E>(g, s)
     if (g.a_kcontig && g.b_kcontig) {
         switch (g.epi) {
             case EPI_STORE: return BIG256(true, true, EPI_STORE);
@@ -449,14 +533,15 @@ hipError_t gemm_mfma_bf16(const GemmArgs& g, hipStream_t s) {
         int S, kc;
         splitk_plan(g.M, g.N, g.K, SK_TM, SK_TN, &S, &kc);
         if (S > 1 && g.ws && (size_t)S * g.M * g.N * 4 <= g.ws_bytes && g.N % 4 == 0 && g.ldo % 4 == 0) {
-            hipError_t e = launch_big<128, 128, 4, 2, 32, 4, false, false, EPI_PARTIAL>(g, s, S, kc);
+            hipError_t e =
+                launch_big<128, 128, 4, 2, 32, GEMM_SPLIT_NS, GEMM_SPLIT_XPF, false, false, EPI_PARTIAL>(g, s, S, kc);
             if (e != hipSuccess) return e;
             int64_t n4 = (int64_t)g.M * g.N / 4;
             unsigned blocks = (unsigned)std::min<int64_t>((n4 + 255) / 256, 4096);
             splitk_reduce_kernel<<<blocks, 256, 0, s>>>((float*)g.out, g.ldo, g.ws, S, g.M, g.N);
             return hipGetLastError();
         }
-        return launch_big<128, 128, 4, 2, 32, 4, false, false, EPI_ACC_F32>(g, s);
+        return launch_big<128, 128, 4, 2, 32, GEMM_SPLIT_NS, GEMM_SPLIT_XPF, false, false, EPI_ACC_F32>(g, s);
     }
 #undef BIG256
     return hipErrorInvalidValue;

@@ -80,6 +80,37 @@ def test_gemm_kernels_vs_oracle(prec, cases, dt, tol):
     m.close()
 
 
+def test_gemm_tile_widths_at_scale():
+    """Forward (NT) and backward-data (NN) products with M = 16384 rows, at
+    output widths that select the 256-wide tile (3072) and the 192-wide tile
+    (768), checked on sampled rows (first, last, random) against the oracle
+    run on those rows alone (each output row depends only on its input row)."""
+    m = _model(G.GPT2_BF16_MIXED)
+    rng = np.random.default_rng(2)
+    M, R = 16384, 64
+    rows = np.unique(np.concatenate([np.arange(64), np.arange(M - 64, M), rng.integers(0, M, 128)]))
+    for N in (3072, 768):
+        print(f"gemm tile width N={N}", flush=True)
+        # forward: out[M,N] = x[M,R] W[N,R]^T + b
+        x = _dev(rng.standard_normal((M, R)), torch.bfloat16)
+        w = _dev(rng.standard_normal((N, R)) * 0.1, torch.bfloat16)
+        bias = torch.from_numpy(rng.standard_normal(N).astype(np.float32)).cuda()
+        out = torch.zeros((M, N), dtype=torch.bfloat16, device="cuda")
+        G.gpt2_test_gemm_nt(m.h, out.data_ptr(), x.data_ptr(), w.data_ptr(), bias.data_ptr(), M, N, R)
+        torch.cuda.synchronize()
+        ref = O.matmul_forward(_host64(x)[rows], _host64(w), bias.cpu().numpy().astype(np.float64), prec="f64")
+        _close(_host64(out)[rows], ref, 8e-3)
+        # backward data: dX[M,N] = dY[M,R] W2[R,N]  (output width N, reduction R)
+        dy = _dev(rng.standard_normal((M, R)), torch.bfloat16)
+        w2 = _dev(rng.standard_normal((R, N)) * 0.1, torch.bfloat16)
+        dx = torch.zeros((M, N), dtype=torch.bfloat16, device="cuda")
+        G.gpt2_test_gemm_nn(m.h, dx.data_ptr(), dy.data_ptr(), w2.data_ptr(), M, R, N)
+        torch.cuda.synchronize()
+        rdx, _, _ = O.matmul_backward(_host64(dy)[rows], np.zeros((rows.size, N)), _host64(w2), prec="f64")
+        _close(_host64(dx)[rows], rdx, 8e-3)
+    m.close()
+
+
 def test_gemm_split_k_weight_gradient():
     """The weight-gradient product with a long reduction (split over several
     workgroups, partials summed in a second kernel) against the oracle."""

@@ -58,42 +58,53 @@ template <int EPI, int RH, int FM, int FN>
 DEVI void epilogue_rows(const GemmArgs& g, const f32x16 (&acc)[FM][FN], float* red, int mrow0, int ncol0, int split,
                         int lane) {
     constexpr int TN = FN * 32, P = TN + 4;
-    constexpr int LPR = TN / 8;    // lanes per output row
+    constexpr int CG = TN % 64 == 0 ? 64 : 32;  // columns read back per group
+    constexpr int NCG = TN / CG;
+    constexpr int LPR = CG / 8;    // lanes per output row segment
     constexpr int RPI = 64 / LPR;  // rows per access instruction
     constexpr int NR = RH / RPI;   // row groups per pass
     static_assert(RH == 32 || RH == 16, "rows per pass");
     constexpr bool BIAS = EPI == EPI_BIAS || EPI == EPI_BIAS_RESID || EPI == EPI_BIAS_GELU;
     typedef bf16 bf16x8_t __attribute__((ext_vector_type(8)));
     const int hi = lane >> 5, l32 = lane & 31;
-    const int cl = (lane % LPR) * 8;
-    const int n = ncol0 + cl;
-    const bool nok = n < g.N;
-    float b8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if (BIAS && g.bias && nok) {
-        const float4 u = *reinterpret_cast<const float4*>(g.bias + n);
-        const float4 v = *reinterpret_cast<const float4*>(g.bias + n + 4);
-        b8[0] = u.x; b8[1] = u.y; b8[2] = u.z; b8[3] = u.w; b8[4] = v.x; b8[5] = v.y; b8[6] = v.z; b8[7] = v.w;
+    float b8[NCG][8];
+#pragma unroll
+    for (int cg = 0; cg < NCG; cg++) {
+        const int n = ncol0 + cg * CG + (lane % LPR) * 8;
+#pragma unroll
+        for (int e = 0; e < 8; e++) b8[cg][e] = 0.f;
+        if (BIAS && g.bias && n < g.N) {
+            const float4 u = *reinterpret_cast<const float4*>(g.bias + n);
+            const float4 v = *reinterpret_cast<const float4*>(g.bias + n + 4);
+            b8[cg][0] = u.x; b8[cg][1] = u.y; b8[cg][2] = u.z; b8[cg][3] = u.w;
+            b8[cg][4] = v.x; b8[cg][5] = v.y; b8[cg][6] = v.z; b8[cg][7] = v.w;
+        }
     }
 #pragma unroll
     for (int pass = 0; pass < FM * (32 / RH); pass++) {
         const int i = pass / (32 / RH), h = pass % (32 / RH);  // rows h*RH .. of block i
         // operands of this pass's outputs, requested before the LDS round trip
-        bf16x8_t r16[NR];
-        float4 r32[NR][2];
+        bf16x8_t r16[NCG][NR];
+        float4 r32[NCG][NR][2];
 #pragma unroll
-        for (int rr = 0; rr < NR; rr++) {
-            const int m = mrow0 + i * 32 + h * RH + rr * RPI + lane / LPR;
-            const bool ok = m < g.M && nok;
-            const int64_t o = (int64_t)m * g.ldo + n;
-            if constexpr (EPI == EPI_BIAS_RESID)
-                r16[rr] = ok ? *reinterpret_cast<const bf16x8_t*>((const bf16*)g.resid + o) : bf16x8_t{};
-            if constexpr (EPI == EPI_GELU_BWD)
-                r16[rr] = ok ? *reinterpret_cast<const bf16x8_t*>((const bf16*)g.aux + o) : bf16x8_t{};
-            if constexpr (EPI == EPI_ACC_F32) {
-                r32[rr][0] = ok ? *reinterpret_cast<const float4*>((const float*)g.out + o) : make_float4(0.f, 0.f, 0.f, 0.f);
-                r32[rr][1] = ok ? *reinterpret_cast<const float4*>((const float*)g.out + o + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int cg = 0; cg < NCG; cg++)
+#pragma unroll
+            for (int rr = 0; rr < NR; rr++) {
+                const int m = mrow0 + i * 32 + h * RH + rr * RPI + lane / LPR;
+                const int n = ncol0 + cg * CG + (lane % LPR) * 8;
+                const bool ok = m < g.M && n < g.N;
+                const int64_t o = (int64_t)m * g.ldo + n;
+                if constexpr (EPI == EPI_BIAS_RESID)
+                    r16[cg][rr] = ok ? *reinterpret_cast<const bf16x8_t*>((const bf16*)g.resid + o) : bf16x8_t{};
+                if constexpr (EPI == EPI_GELU_BWD)
+                    r16[cg][rr] = ok ? *reinterpret_cast<const bf16x8_t*>((const bf16*)g.aux + o) : bf16x8_t{};
+                if constexpr (EPI == EPI_ACC_F32) {
+                    r32[cg][rr][0] = ok ? *reinterpret_cast<const float4*>((const float*)g.out + o)
+                                        : make_float4(0.f, 0.f, 0.f, 0.f);
+                    r32[cg][rr][1] = ok ? *reinterpret_cast<const float4*>((const float*)g.out + o + 4)
+                                        : make_float4(0.f, 0.f, 0.f, 0.f);
+                }
             }
-        }
         if (RH == 32 || (l32 >> 4) == h) {
             const int wr = l32 % RH;
 #pragma unroll
@@ -104,44 +115,47 @@ DEVI void epilogue_rows(const GemmArgs& g, const f32x16 (&acc)[FM][FN], float* r
                         make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
         }
 #pragma unroll
-        for (int rr = 0; rr < NR; rr++) {
-            const int row = rr * RPI + lane / LPR;
-            const int m = mrow0 + i * 32 + h * RH + row;
-            const float4 u = *reinterpret_cast<const float4*>(red + row * P + cl);
-            const float4 v = *reinterpret_cast<const float4*>(red + row * P + cl + 4);
-            float y[8] = {u.x, u.y, u.z, u.w, v.x, v.y, v.z, v.w};
-            if (m >= g.M || !nok) continue;
-            const int64_t o = (int64_t)m * g.ldo + n;
-            if constexpr (EPI == EPI_PARTIAL) {
-                float* w = g.ws + ((int64_t)split * g.M + m) * g.N + n;
-                *reinterpret_cast<float4*>(w) = u;
-                *reinterpret_cast<float4*>(w + 4) = v;
-                continue;
-            }
-            if constexpr (EPI == EPI_ACC_F32) {
-                float* w = (float*)g.out + o;
-                *reinterpret_cast<float4*>(w) =
-                    make_float4(r32[rr][0].x + y[0], r32[rr][0].y + y[1], r32[rr][0].z + y[2], r32[rr][0].w + y[3]);
-                *reinterpret_cast<float4*>(w + 4) =
-                    make_float4(r32[rr][1].x + y[4], r32[rr][1].y + y[5], r32[rr][1].z + y[6], r32[rr][1].w + y[7]);
-                continue;
-            }
+        for (int cg = 0; cg < NCG; cg++)
 #pragma unroll
-            for (int e = 0; e < 8; e++) {
-                if constexpr (BIAS) y[e] += b8[e];
-                if constexpr (EPI == EPI_BIAS_RESID) y[e] += (float)r16[rr][e];
-                if constexpr (EPI == EPI_GELU_BWD) y[e] *= gelu_grad_f((float)r16[rr][e]);
-            }
-            bf16x8_t out;
+            for (int rr = 0; rr < NR; rr++) {
+                const int row = rr * RPI + lane / LPR;
+                const int cl = cg * CG + (lane % LPR) * 8;
+                const int m = mrow0 + i * 32 + h * RH + row;
+                const int n = ncol0 + cl;
+                const float4 u = *reinterpret_cast<const float4*>(red + row * P + cl);
+                const float4 v = *reinterpret_cast<const float4*>(red + row * P + cl + 4);
+                float y[8] = {u.x, u.y, u.z, u.w, v.x, v.y, v.z, v.w};
+                if (m >= g.M || n >= g.N) continue;
+                const int64_t o = (int64_t)m * g.ldo + n;
+                if constexpr (EPI == EPI_PARTIAL) {
+                    float* w = g.ws + ((int64_t)split * g.M + m) * g.N + n;
+                    *reinterpret_cast<float4*>(w) = u;
+                    *reinterpret_cast<float4*>(w + 4) = v;
+                    continue;
+                }
+                if constexpr (EPI == EPI_ACC_F32) {
+                    const float4 a0 = r32[cg][rr][0], a1 = r32[cg][rr][1];
+                    float* w = (float*)g.out + o;
+                    *reinterpret_cast<float4*>(w) = make_float4(a0.x + y[0], a0.y + y[1], a0.z + y[2], a0.w + y[3]);
+                    *reinterpret_cast<float4*>(w + 4) = make_float4(a1.x + y[4], a1.y + y[5], a1.z + y[6], a1.w + y[7]);
+                    continue;
+                }
 #pragma unroll
-            for (int e = 0; e < 8; e++) out[e] = (bf16)y[e];
-            *reinterpret_cast<bf16x8_t*>((bf16*)g.out + o) = out;
-            if constexpr (EPI == EPI_BIAS_GELU) {
+                for (int e = 0; e < 8; e++) {
+                    if constexpr (BIAS) y[e] += b8[cg][e];
+                    if constexpr (EPI == EPI_BIAS_RESID) y[e] += (float)r16[cg][rr][e];
+                    if constexpr (EPI == EPI_GELU_BWD) y[e] *= gelu_grad_f((float)r16[cg][rr][e]);
+                }
+                bf16x8_t out;
 #pragma unroll
-                for (int e = 0; e < 8; e++) out[e] = (bf16)gelu_f(y[e]);
-                *reinterpret_cast<bf16x8_t*>((bf16*)g.out2 + o) = out;
+                for (int e = 0; e < 8; e++) out[e] = (bf16)y[e];
+                *reinterpret_cast<bf16x8_t*>((bf16*)g.out + o) = out;
+                if constexpr (EPI == EPI_BIAS_GELU) {
+#pragma unroll
+                    for (int e = 0; e < 8; e++) out[e] = (bf16)gelu_f(y[e]);
+                    *reinterpret_cast<bf16x8_t*>((bf16*)g.out2 + o) = out;
+                }
             }
-        }
     }
 }
 
@@ -304,11 +318,16 @@ DEVI void mfma_step(f32x16 (&acc)[FM][FN], bf16x8 (&fa)[FM], bf16x8 (&fb)[FN], c
 }
 
 // OCC: waves per SIMD the register allocation targets (2: up to 256
-// registers; 1: up to 512, accumulators in AGPRs)
-template <int BM, int BN, int NW, int WAVES_M, int KB, int NS, bool XPF, bool AK, bool BKC, int EPI, int OCC = 2>
+// registers; 1: up to 512, accumulators in AGPRs).  BNV: output columns per
+// tile when fewer than BN; the B operand is still staged BN rows wide (same
+// load geometry, every wave issues the same loads), the rows past BNV land in
+// LDS that no fragment reads.
+template <int BM, int BN, int NW, int WAVES_M, int KB, int NS, bool XPF, bool AK, bool BKC, int EPI, int OCC = 2,
+          int BNV = BN>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void gemm_big_kernel(GemmArgs g, int kchunk) {
     constexpr int WAVES_N = NW / WAVES_M;
-    constexpr int TM = BM / WAVES_M, TN = BN / WAVES_N, FM = TM / 32, FN = TN / 32;
+    constexpr int TM = BM / WAVES_M, TN = BNV / WAVES_N, FM = TM / 32, FN = TN / 32;
+    static_assert(BNV <= BN && TN % 32 == 0, "tile width");
     static_assert(NS >= 3 && NS <= 5, "stages");
     constexpr int SA = BM * KB, SB = BN * KB;
     // one array per stage (alias analysis then keeps the reads of one stage
@@ -336,7 +355,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WAVES_N, wn = wave % WAVES_N;
 
-    const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
+    const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BNV - 1) / BNV;
     // Workgroup L (linear id, x fastest) runs on XCD L % 8.  Give each XCD a
     // contiguous range of (split, tile) work in split-major order, so that
     // the tiles sharing operand panels (same split, neighbouring tiles) share
@@ -353,7 +372,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
     const int gsz = min(tiles_m - first_m, GM);
     const int in = bid % (GM * tiles_n);
     const int m0 = (first_m + in % gsz) * BM;
-    const int n0 = (in / gsz) * BN;
+    const int n0 = (in / gsz) * BNV;
     const bf16* A = (const bf16*)g.a;
     const bf16* B = (const bf16*)g.b;
 
@@ -452,10 +471,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
     }
 }
 
-template <int BM, int BN, int NW, int WAVES_M, int KB, int NS, bool XPF, bool AK, bool BKC, int EPI, int OCC = 2>
+template <int BM, int BN, int NW, int WAVES_M, int KB, int NS, bool XPF, bool AK, bool BKC, int EPI, int OCC = 2,
+          int BNV = BN>
 hipError_t launch_big(const GemmArgs& g, hipStream_t s, int splits = 1, int kchunk = 0) {
-    dim3 grid(cdiv(g.M, BM) * cdiv(g.N, BN), splits);
-    gemm_big_kernel<BM, BN, NW, WAVES_M, KB, NS, XPF, AK, BKC, EPI, OCC>
+    dim3 grid(cdiv(g.M, BM) * cdiv(g.N, BNV), splits);
+    gemm_big_kernel<BM, BN, NW, WAVES_M, KB, NS, XPF, AK, BKC, EPI, OCC, BNV>
         <<<grid, NW * 64, 0, s>>>(g, kchunk ? kchunk : g.K);
     return hipGetLastError();
 }
@@ -497,6 +517,16 @@ __global__ void splitk_reduce_kernel(float* out, int64_t ldo, const float* ws, i
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
+// Whether 192-wide tiles finish in fewer (tile-size weighted) rounds of one
+// workgroup per CU than 256-wide ones, by at least 10%.
+bool use_192(int M, int N) {
+    constexpr int CUS = 256;
+    const int64_t tm = cdiv(M, 256);
+    const int64_t r256 = (tm * cdiv(N, 256) + CUS - 1) / CUS;
+    const int64_t r192 = (tm * cdiv(N, 192) + CUS - 1) / CUS;
+    return 10 * 3 * r192 <= 9 * 4 * r256;
+}
+
 }  // namespace
 
 hipError_t gemm_mfma_bf16(const GemmArgs& g, hipStream_t s) {
@@ -511,22 +541,29 @@ hipError_t gemm_mfma_bf16(const GemmArgs& g, hipStream_t s) {
     // tile (8 waves of 128 x 64, k-step 32, 4 LDS stages) leads or ties in
     // every forward and backward-data product.
 #define BIG256(AKC, BKCC, E) launch_big<256, 256, 8, 2, 32, GEMM_BIG_NS, GEMM_BIG_XPF, AKC, BKCC, E>(g, s)
+    // 192 output columns per tile (8 waves of 64 x 96) when that saves whole
+    // rounds of workgroups: N = 768 gives 256 tiles instead of 192 for 256
+    // CUs, N = 2304 three full rounds instead of 2.25.
+#define BIG192(AKC, BKCC, E) launch_big<256, 256, 8, 4, 32, GEMM_BIG_NS, GEMM_BIG_XPF, AKC, BKCC, E, 2, 192>(g, s)
+    const bool w192 = use_192(g.M, g.N);
     if (g.a_kcontig && g.b_kcontig) {
         switch (g.epi) {
-            case EPI_STORE: return BIG256(true, true, EPI_STORE);
-            case EPI_BIAS: return BIG256(true, true, EPI_BIAS);
-            case EPI_BIAS_RESID: return BIG256(true, true, EPI_BIAS_RESID);
-            case EPI_BIAS_GELU: return BIG256(true, true, EPI_BIAS_GELU);
+            case EPI_STORE: return w192 ? BIG192(true, true, EPI_STORE) : BIG256(true, true, EPI_STORE);
+            case EPI_BIAS: return w192 ? BIG192(true, true, EPI_BIAS) : BIG256(true, true, EPI_BIAS);
+            case EPI_BIAS_RESID:
+                return w192 ? BIG192(true, true, EPI_BIAS_RESID) : BIG256(true, true, EPI_BIAS_RESID);
+            case EPI_BIAS_GELU: return w192 ? BIG192(true, true, EPI_BIAS_GELU) : BIG256(true, true, EPI_BIAS_GELU);
             default: return hipErrorInvalidValue;
         }
     }
     if (g.a_kcontig && !g.b_kcontig) {
         switch (g.epi) {
-            case EPI_STORE: return BIG256(true, false, EPI_STORE);
-            case EPI_GELU_BWD: return BIG256(true, false, EPI_GELU_BWD);
+            case EPI_STORE: return w192 ? BIG192(true, false, EPI_STORE) : BIG256(true, false, EPI_STORE);
+            case EPI_GELU_BWD: return w192 ? BIG192(true, false, EPI_GELU_BWD) : BIG256(true, false, EPI_GELU_BWD);
             default: return hipErrorInvalidValue;
         }
     }
+#undef BIG192
     if (!g.a_kcontig && !g.b_kcontig && g.epi == EPI_ACC_F32) {
         if (cdiv(g.M, 256) * cdiv(g.N, 256) >= 256)  // wide output (the classifier): no split needed
             return BIG256(false, false, EPI_ACC_F32);

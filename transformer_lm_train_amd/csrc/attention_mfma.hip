@@ -274,9 +274,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
 // ---------------------------------------------------------------------------
 // Dout[row] = rowsum(dO o O) and Lout[row] = -lse * log2(e), for the dK/dV kernel
+// bpart (optional): per-(batch, 128-row block) column sums of the dq / dk / dv
+// written, one row [3C] per block: the partials of the qkv bias gradient.
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void flash_bwd_dq_kernel(bf16* dqkv, float* Dout, float* Lout, const bf16* dout,
                                                            const bf16* qkv, const bf16* out, const float* lse, int T,
-                                                           int C, int NH) {
+                                                           int C, int NH, float* bpart) {
     __shared__ __attribute__((aligned(1024))) bf16 k0s[TILE], k1s[TILE], k2s[TILE];
     __shared__ __attribute__((aligned(1024))) bf16 v0s[TILE], v1s[TILE], v2s[TILE];
     const int nqb = (T + QB - 1) / QB;
@@ -385,6 +387,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 *reinterpret_cast<bf16x4*>(row + dt * 32 + 8 * g + 4 * hi) = v;
             }
     }
+    if (bpart) {
+        // sum of the stored dq over the block's queries.  Each wave transposes
+        // its 32 queries x 64 channels through its own 8 KB stage array (free
+        // once every wave is past the loop): row q, float4 slot c4 ^ (q & 15),
+        // so 16 lanes writing one column hit 16 distinct bank groups; then
+        // lane c sums column c over the 32 rows and the 4 waves are added in
+        // a fixed order.
+        __shared__ float cred[4][HS];
+        __syncthreads();
+        float* tq = reinterpret_cast<float*>(w == 0 ? k0s : w == 1 ? k1s : w == 2 ? k2s : v0s);
+#pragma unroll
+        for (int dt = 0; dt < 2; dt++)
+#pragma unroll
+            for (int g = 0; g < 4; g++) {
+                const int c4 = dt * 8 + 2 * g + hi;  // channels dt*32 + 8g + 4hi .. +3
+                float4 v;
+                v.x = qok ? (float)(bf16)(dq[dt][4 * g + 0] * 0.125f) : 0.f;
+                v.y = qok ? (float)(bf16)(dq[dt][4 * g + 1] * 0.125f) : 0.f;
+                v.z = qok ? (float)(bf16)(dq[dt][4 * g + 2] * 0.125f) : 0.f;
+                v.w = qok ? (float)(bf16)(dq[dt][4 * g + 3] * 0.125f) : 0.f;
+                *reinterpret_cast<float4*>(tq + lq * HS + ((c4 ^ (lq & 15)) << 2)) = v;
+            }
+        float t = 0.f;
+#pragma unroll
+        for (int qq = 0; qq < 32; qq++) t += tq[qq * HS + ((((lane >> 2) ^ (qq & 15)) << 2) | (lane & 3))];
+        cred[w][lane] = t;
+        __syncthreads();
+        if (tid < HS)
+            bpart[((int64_t)b * nqb + qblk) * C3 + h * HS + tid] = cred[0][tid] + cred[1][tid] + cred[2][tid] + cred[3][tid];
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -399,7 +431,8 @@ DEVI void dma_stats(float* region, const float* src, int q0) {
 }
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void flash_bwd_dkdv_kernel(
-    bf16* dqkv, const float* Din, const float* Lin, const bf16* dout, const bf16* qkv, int T, int C, int NH) {
+    bf16* dqkv, const float* Din, const float* Lin, const bf16* dout, const bf16* qkv, int T, int C, int NH,
+    float* bpart) {
     __shared__ __attribute__((aligned(1024))) bf16 q0s[TILE], q1s[TILE], q2s[TILE];
     __shared__ __attribute__((aligned(1024))) bf16 o0s[TILE], o1s[TILE], o2s[TILE];  // dO
     __shared__ __attribute__((aligned(1024))) float st0[4 * 256], st1[4 * 256], st2[4 * 256];
@@ -513,6 +546,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             }
         }
     }
+    if (bpart) {
+        // sums of the stored dk, dv over the block's keys: the 16 registers
+        // and two halves of a lane's channel, then the 4 waves
+        __shared__ float kred[4][HS], vred[4][HS];
+#pragma unroll
+        for (int dt = 0; dt < 2; dt++) {
+            float tk = 0.f, tv = 0.f;
+#pragma unroll
+            for (int r = 0; r < 16; r++)
+                if (k0 + acc_row(r, hi) < T) {
+                    tk += (float)(bf16)(dk[dt][r] * 0.125f);
+                    tv += (float)(bf16)dv[dt][r];
+                }
+            tk += __shfl_xor(tk, 32, 64);
+            tv += __shfl_xor(tv, 32, 64);
+            if (hi == 0) {
+                kred[w][dt * 32 + lq] = tk;
+                vred[w][dt * 32 + lq] = tv;
+            }
+        }
+        __syncthreads();
+        if (tid < HS) {
+            float* prow = bpart + ((int64_t)b * ((T + QB - 1) / QB) + kblk) * C3 + h * HS + tid;
+            prow[C] = kred[0][tid] + kred[1][tid] + kred[2][tid] + kred[3][tid];
+            prow[2 * C] = vred[0][tid] + vred[1][tid] + vred[2][tid] + vred[3][tid];
+        }
+    }
 }
 
 #undef STAGE_SYNC
@@ -527,11 +587,14 @@ hipError_t flash_attention_fwd(bf16* out, float* lse, const bf16* qkv, int B, in
 }
 
 hipError_t flash_attention_bwd(bf16* dqkv, const bf16* dout, const bf16* qkv, const bf16* out, const float* lse,
-                               float* dbuf, int B, int T, int C, int NH, hipStream_t s) {
+                               float* dbuf, int B, int T, int C, int NH, float* dbias, float* bpart,
+                               hipStream_t s) {
     if (C / NH != HS || C % NH || T % KB) return hipErrorInvalidValue;
     const unsigned grid = (unsigned)((T + QB - 1) / QB * NH * B);
     const int64_t rows = (int64_t)B * NH * T;
-    flash_bwd_dq_kernel<<<grid, 256, 0, s>>>(dqkv, dbuf, dbuf + rows, dout, qkv, out, lse, T, C, NH);
-    flash_bwd_dkdv_kernel<<<grid, 256, 0, s>>>(dqkv, dbuf, dbuf + rows, dout, qkv, T, C, NH);
+    float* bp = dbias ? bpart : nullptr;
+    flash_bwd_dq_kernel<<<grid, 256, 0, s>>>(dqkv, dbuf, dbuf + rows, dout, qkv, out, lse, T, C, NH, bp);
+    flash_bwd_dkdv_kernel<<<grid, 256, 0, s>>>(dqkv, dbuf, dbuf + rows, dout, qkv, T, C, NH, bp);
+    if (dbias) return sum_partials(dbias, nullptr, nullptr, bpart, B * ((T + QB - 1) / QB), 3 * C, s);
     return hipGetLastError();
 }

@@ -56,7 +56,7 @@ template <int RH, int TN> constexpr int red_bytes() { return RH * (TN + 4) * 4; 
 
 template <int EPI, int RH, int FM, int FN>
 DEVI void epilogue_rows(const GemmArgs& g, const f32x16 (&acc)[FM][FN], float* red, int mrow0, int ncol0, int split,
-                        int lane) {
+                        int prow, int lane) {
     constexpr int TN = FN * 32, P = TN + 4;
     constexpr int CG = TN % 64 == 0 ? 64 : 32;  // columns read back per group
     constexpr int NCG = TN / CG;
@@ -67,6 +67,12 @@ DEVI void epilogue_rows(const GemmArgs& g, const f32x16 (&acc)[FM][FN], float* r
     constexpr bool BIAS = EPI == EPI_BIAS || EPI == EPI_BIAS_RESID || EPI == EPI_BIAS_GELU;
     typedef bf16 bf16x8_t __attribute__((ext_vector_type(8)));
     const int hi = lane >> 5, l32 = lane & 31;
+    constexpr bool CSUM = EPI == EPI_GELU_BWD;  // column sums of the outputs, if g.colsum
+    float cs[NCG][8];
+#pragma unroll
+    for (int cg = 0; cg < NCG; cg++)
+#pragma unroll
+        for (int e = 0; e < 8; e++) cs[cg][e] = 0.f;
     float b8[NCG][8];
 #pragma unroll
     for (int cg = 0; cg < NCG; cg++) {
@@ -150,12 +156,43 @@ DEVI void epilogue_rows(const GemmArgs& g, const f32x16 (&acc)[FM][FN], float* r
 #pragma unroll
                 for (int e = 0; e < 8; e++) out[e] = (bf16)y[e];
                 *reinterpret_cast<bf16x8_t*>((bf16*)g.out + o) = out;
+                if constexpr (CSUM) {
+#pragma unroll
+                    for (int e = 0; e < 8; e++) cs[cg][e] += (float)out[e];
+                }
                 if constexpr (EPI == EPI_BIAS_GELU) {
 #pragma unroll
                     for (int e = 0; e < 8; e++) out[e] = (bf16)gelu_f(y[e]);
                     *reinterpret_cast<bf16x8_t*>((bf16*)g.out2 + o) = out;
                 }
             }
+    }
+    if constexpr (CSUM) {
+        if (g.colsum) {
+            // lanes l, l + LPR, l + 2 LPR, ... hold the same columns: combine
+            // them (fixed butterfly order), then lanes 0 .. LPR-1 write the
+            // wave's partial row
+#pragma unroll
+            for (int cg = 0; cg < NCG; cg++)
+#pragma unroll
+                for (int e = 0; e < 8; e++) {
+                    float t = cs[cg][e];
+#pragma unroll
+                    for (int off = LPR; off < 64; off <<= 1) t += __shfl_xor(t, off, 64);
+                    cs[cg][e] = t;
+                }
+            if (lane < LPR) {
+#pragma unroll
+                for (int cg = 0; cg < NCG; cg++) {
+                    const int n = ncol0 + cg * CG + lane * 8;
+                    if (n < g.N) {
+                        float* w = g.colsum_ws + (int64_t)prow * g.N + n;
+                        *reinterpret_cast<float4*>(w) = make_float4(cs[cg][0], cs[cg][1], cs[cg][2], cs[cg][3]);
+                        *reinterpret_cast<float4*>(w + 4) = make_float4(cs[cg][4], cs[cg][5], cs[cg][6], cs[cg][7]);
+                    }
+                }
+            }
+        }
     }
 }
 
@@ -467,7 +504,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
             case 6: region = sa3; break;
             default: region = sb3; break;
         }
-        epilogue_rows<EPI, RH>(g, acc, reinterpret_cast<float*>(region), m0 + wm * TM, n0 + wn * TN, split, lane);
+        epilogue_rows<EPI, RH>(g, acc, reinterpret_cast<float*>(region), m0 + wm * TM, n0 + wn * TN, split,
+                               (m0 / BM) * WAVES_M + wm, lane);
     }
 }
 
@@ -559,7 +597,13 @@ hipError_t gemm_mfma_bf16(const GemmArgs& g, hipStream_t s) {
     if (g.a_kcontig && !g.b_kcontig) {
         switch (g.epi) {
             case EPI_STORE: return w192 ? BIG192(true, false, EPI_STORE) : BIG256(true, false, EPI_STORE);
-            case EPI_GELU_BWD: return w192 ? BIG192(true, false, EPI_GELU_BWD) : BIG256(true, false, EPI_GELU_BWD);
+            case EPI_GELU_BWD: {
+                hipError_t e = w192 ? BIG192(true, false, EPI_GELU_BWD) : BIG256(true, false, EPI_GELU_BWD);
+                if (e != hipSuccess || !g.colsum) return e;
+                // one partial row per wave row block: 4 per 256-row tile (192-wide tiles), else 2
+                const int G = (int)cdiv(g.M, 256) * (w192 ? 4 : 2);
+                return sum_partials(g.colsum, nullptr, nullptr, g.colsum_ws, G, g.N, s);
+            }
             default: return hipErrorInvalidValue;
         }
     }

@@ -37,6 +37,11 @@ struct GemmArgs {
     int epi;
     float* ws;           // split-K workspace (EPI_ACC_F32), may be NULL
     size_t ws_bytes;
+    // EPI_GELU_BWD, bf16 MFMA path: colsum[n] += sum_m out[m][n] (the bias
+    // gradient of the layer whose output gradient this product produces),
+    // through per-wave partial rows in colsum_ws (fixed-order sum).  NULL: off.
+    float* colsum;
+    float* colsum_ws;
 };
 size_t gemm_splitk_ws_bytes(int M, int N, int K);
 
@@ -58,11 +63,14 @@ template <typename T>
 hipError_t layernorm_fwd(T* out, float* mean, float* rstd, const T* x, const float* w, const float* b,
                          int N, int C, hipStream_t s);
 // dres (+)= LN backward of dy; per-block partial dw/db go to partial[2][G][C]
-// and are then summed in block order into dw, db.
+// and are then summed in block order into dw, db.  G <= 1024.
 template <typename T>
 hipError_t layernorm_bwd(T* dres, const T* dy, const T* x, const float* w, const float* mean,
                          const float* rstd, float* dw, float* db, float* partial, int N, int C,
                          bool overwrite, hipStream_t s);
+// out_k[c] += sum_g partial[k*G + g][c] for the non-null out_k, k < 3, in a
+// fixed order.
+hipError_t sum_partials(float* out0, float* out1, float* out2, const float* partial, int G, int C, hipStream_t s);
 // dbias[n] += sum_m dy[m][n] (deterministic two-stage sum via partial).
 template <typename T>
 hipError_t colsum_accum(float* dbias, const T* dy, int M, int N, float* partial, hipStream_t s);
@@ -91,7 +99,11 @@ template <typename T>
 hipError_t attention_bwd(T* dqkv, const T* dout, const T* qkv, const T* out, const float* lse, float* dbuf,
                          int B, int T_, int C, int NH, hipStream_t s);
 // head size 64, bf16, MFMA flash kernels, T % 64 == 0; dbuf holds 2*B*NH*T
-// floats: D = rowsum(dO o O), then -lse*log2(e), one per (b, h, t)
+// floats: D = rowsum(dO o O), then -lse*log2(e), one per (b, h, t).  With
+// dbias, the backward also adds the column sums of dqkv to dbias [3C] (the
+// qkv bias gradient), through bpart [B * ceil(T/128)][3C].
+
 hipError_t flash_attention_fwd(bf16* out, float* lse, const bf16* qkv, int B, int T_, int C, int NH, hipStream_t s);
 hipError_t flash_attention_bwd(bf16* dqkv, const bf16* dout, const bf16* qkv, const bf16* out, const float* lse,
-                               float* dbuf, int B, int T_, int C, int NH, hipStream_t s);
+                               float* dbuf, int B, int T_, int C, int NH, float* dbias, float* bpart,
+                               hipStream_t s);

@@ -173,7 +173,8 @@ __global__ __launch_bounds__(256) void layernorm_bwd_kernel(T* dres, const T* dy
                                                             const float* mean, const float* rstd,
                                                             float* partial, int N, int C, int overwrite) {
     constexpr int VN = Vec16<T>::N;
-    extern __shared__ float smem[];  // [4][2][C]
+    constexpr int NP = 2;            // partial sums per channel (dw, db)
+    extern __shared__ float smem[];  // [4][NP][C]
     int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     int chunks = C / VN;
     float aw[MAXV][VN], ab[MAXV][VN];
@@ -231,51 +232,58 @@ __global__ __launch_bounds__(256) void layernorm_bwd_kernel(T* dres, const T* dy
         if (ch < chunks) {
 #pragma unroll
             for (int j = 0; j < VN; j++) {
-                smem[(wv * 2 + 0) * C + ch * VN + j] = aw[i][j];
-                smem[(wv * 2 + 1) * C + ch * VN + j] = ab[i][j];
+                smem[(wv * NP + 0) * C + ch * VN + j] = aw[i][j];
+                smem[(wv * NP + 1) * C + ch * VN + j] = ab[i][j];
             }
         }
     }
     __syncthreads();
     for (int c = threadIdx.x; c < C; c += 256) {
-        float sw = 0.f, sb = 0.f;
-        for (int q = 0; q < 4; q++) {
-            sw += smem[(q * 2 + 0) * C + c];
-            sb += smem[(q * 2 + 1) * C + c];
+#pragma unroll
+        for (int k = 0; k < NP; k++) {
+            float t = 0.f;
+            for (int q = 0; q < 4; q++) t += smem[(q * NP + k) * C + c];
+            partial[((int64_t)k * gridDim.x + blockIdx.x) * C + c] = t;
         }
-        partial[(int64_t)blockIdx.x * C + c] = sw;
-        partial[((int64_t)gridDim.x + blockIdx.x) * C + c] = sb;
     }
 }
 
-// out0[c] += sum_g partial[g][c]; out1[c] += sum_g partial[G+g][c] (if out1).
+// out_k[c] += sum_g partial[k*G + g][c] for each non-null out_k (k < 3).
 // Block: 16 columns x 64 row lanes; lane r sums partial rows r, r+64, ...
 // (all its loads independent, so the whole array is in flight at once), then
 // the 64 lane sums of a column are combined in a fixed order.
-__global__ __launch_bounds__(1024) void sum_partials_kernel(float* out0, float* out1, const float* partial, int G,
-                                                            int C) {
-    __shared__ float red[2][64][17];
+__global__ __launch_bounds__(1024) void sum_partials_kernel(float* out0, float* out1, float* out2,
+                                                            const float* partial, int G, int C) {
+    __shared__ float red[3][64][17];
     const int cx = threadIdx.x & 15, ry = threadIdx.x >> 4;
     const int c = blockIdx.x * 16 + cx;
-    float s0 = 0.f, s1 = 0.f;
-    if (c < C) {
-        for (int g = ry; g < G; g += 64) {
-            s0 += partial[(int64_t)g * C + c];
-            if (out1) s1 += partial[((int64_t)G + g) * C + c];
+    float* outs[3] = {out0, out1, out2};
+    const int nk = out2 ? 3 : out1 ? 2 : 1;  // out0 is always given
+    float t0 = 0.f, t1 = 0.f, t2 = 0.f;
+    if (c < C)
+        for (int g = ry; g < G; g += 64) {  // the nk loads of a row are independent
+            const float* pr = partial + (int64_t)g * C + c;
+            t0 += pr[0];
+            if (nk > 1) t1 += pr[(int64_t)G * C];
+            if (nk > 2) t2 += pr[2 * (int64_t)G * C];
         }
-    }
-    red[0][ry][cx] = s0;
-    red[1][ry][cx] = s1;
+    red[0][ry][cx] = t0;
+    red[1][ry][cx] = t1;
+    red[2][ry][cx] = t2;
     __syncthreads();
-    if (threadIdx.x < 32) {
-        const int k = threadIdx.x >> 4;  // 0: out0, 1: out1
-        const int cc = blockIdx.x * 16 + cx;
-        if (cc < C && (k == 0 || out1)) {
+    if (threadIdx.x < 48) {
+        const int k = threadIdx.x >> 4;
+        if (c < C && outs[k]) {
             float t = 0.f;
             for (int i = 0; i < 64; i++) t += red[k][i][cx];
-            (k == 0 ? out0 : out1)[cc] += t;
+            outs[k][c] += t;
         }
     }
+}
+
+hipError_t sum_partials(float* out0, float* out1, float* out2, const float* partial, int G, int C, hipStream_t s) {
+    sum_partials_kernel<<<cdiv(C, 16), 1024, 0, s>>>(out0, out1, out2, partial, G, C);
+    return hipGetLastError();
 }
 
 template <typename T>
@@ -295,7 +303,7 @@ hipError_t layernorm_bwd(T* dres, const T* dy, const T* x, const float* w, const
         layernorm_bwd_kernel<T, 4><<<G, 256, lds, s>>>(dres, dy, x, w, mean, rstd, partial, N, C, ow);
     else
         layernorm_bwd_kernel<T, 8><<<G, 256, lds, s>>>(dres, dy, x, w, mean, rstd, partial, N, C, ow);
-    sum_partials_kernel<<<cdiv(C, 16), 1024, 0, s>>>(dw, db, partial, G, C);
+    sum_partials_kernel<<<cdiv(C, 16), 1024, 0, s>>>(dw, db, nullptr, partial, G, C);
     return LAUNCH_CHECK();
 }
 
@@ -341,7 +349,7 @@ hipError_t colsum_accum(float* dbias, const T* dy, int M, int N, float* partial,
     int G = COLSUM_G;
     dim3 grid(cdiv(N / VN, 64), G);
     colsum_kernel<T><<<grid, 256, 0, s>>>(partial, dy, M, N);
-    sum_partials_kernel<<<cdiv(N, 16), 1024, 0, s>>>(dbias, nullptr, partial, G, N);
+    sum_partials_kernel<<<cdiv(N, 16), 1024, 0, s>>>(dbias, nullptr, nullptr, partial, G, N);
     return LAUNCH_CHECK();
 }
 

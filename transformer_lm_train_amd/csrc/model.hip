@@ -136,7 +136,18 @@ Layout make_layout(const gpt2_config& c) {
     L.dbig = add(A * BT * 4 * C);
     L.dmid = add(A * BT * C);
     L.attD = add(2 * 4 * BT * c.num_heads);  // D and the base-2 lse of every attention row
-    L.partial = add(4 * 2048 * C);
+    {
+        // partial sums of the fixed-order reductions; the largest of: LN
+        // backward (2 per channel, up to 1024 rows), the fused bias column
+        // sums of the GELU' product (4 rows per 256 tokens, 4C wide) and of
+        // attention (one row per 128-token block, 3C wide), the stand-alone
+        // column sums (256 rows, up to 4C wide)
+        const size_t ln = 2 * 1024 * (size_t)C;
+        const size_t ge = cdiv(BT, 256) * 4 * 4 * (size_t)C;
+        const size_t at = (size_t)c.batch_size * cdiv(c.seq_len, 128) * 3 * C;
+        const size_t cs = 256 * 4 * (size_t)C;
+        L.partial = add(4 * std::max(std::max(ln, ge), std::max(at, cs)));
+    }
     L.norm_partial = add(4 * 1024);
     L.scalars = add(64);
     L.err = add(64);
@@ -276,13 +287,17 @@ hipError_t lin_fwd(gpt2_t* Mo, T* out, const T* X, const T* W, const float* bias
     return gemm<T>(Mo, g);
 }
 // dX[M,K] = dY[M,N] W[N,K]  (+ GELU' epilogue with aux)
+// With colsum (bf16 GELU' path only), colsum[k] += sum_m dX[m][k] as well.
 template <typename T>
-hipError_t lin_dx(gpt2_t* Mo, T* dX, const T* dY, const T* W, int M, int N, int K, int epi, const T* aux = nullptr) {
+hipError_t lin_dx(gpt2_t* Mo, T* dX, const T* dY, const T* W, int M, int N, int K, int epi, const T* aux = nullptr,
+                  float* colsum = nullptr) {
     GemmArgs g{};
     g.M = M; g.N = K; g.K = N;
     g.a = dY; g.lda = N; g.a_kcontig = true;
     g.b = W; g.ldb = K; g.b_kcontig = false;
     g.out = dX; g.ldo = K; g.aux = aux; g.epi = epi;
+    g.colsum = colsum;
+    g.colsum_ws = colsum ? Mo->P<float>(Mo->L.partial) : nullptr;
     return gemm<T>(Mo, g);
 }
 // dW[N,K] += dY[M,N]^T X[M,K]
@@ -303,11 +318,12 @@ hipError_t attn_fwd(T* out, float* lse, const T* qkv, int B, int T_, int C, int 
     if constexpr (std::is_same<T, bf16>::value) return flash_attention_fwd(out, lse, qkv, B, T_, C, NH, s);
     else return attention_fwd<float>(out, lse, qkv, B, T_, C, NH, s);
 }
+// dbias (bf16 path): qkv bias gradient from the kernels' own column sums
 template <typename T>
 hipError_t attn_bwd(T* dqkv, const T* dout, const T* qkv, const T* out, const float* lse, float* dbuf, int B, int T_,
-                    int C, int NH, hipStream_t s) {
+                    int C, int NH, float* dbias, float* bpart, hipStream_t s) {
     if constexpr (std::is_same<T, bf16>::value)
-        return flash_attention_bwd(dqkv, dout, qkv, out, lse, dbuf, B, T_, C, NH, s);
+        return flash_attention_bwd(dqkv, dout, qkv, out, lse, dbuf, B, T_, C, NH, dbias, bpart, s);
     else return attention_bwd<float>(dqkv, dout, qkv, out, lse, dbuf, B, T_, C, NH, s);
 }
 
@@ -403,6 +419,11 @@ template <typename T> int backward_impl(gpt2_t* M) {
     RUN("gemm_classifier_dx", lin_dx<T>(M, a.dmid, a.logits, w + po[P_WTE], BT, Vp, C, EPI_STORE));
     RUN("gemm_classifier_dw", lin_dw<T>(M, g + po[P_WTE], a.logits, a.lnf, BT, Vp, C));
     const T* xlast = a.res3 + (size_t)(Ly - 1) * BTC;
+    // Bias gradients are column sums of the output gradients.  In bf16 mode
+    // the kernel that produces the gradient also takes its column sums for
+    // fc (the GELU' product) and qkv (the attention backward); the others
+    // (and all of them in fp32 mode) get a column-sum pass.
+    constexpr bool fused = std::is_same<T, bf16>::value;
     RUN("layernorm_bwd", layernorm_bwd<T>(a.dres, a.dmid, xlast, p + po[P_LNFW], a.lnfm, a.lnfr, g + po[P_LNFW],
                                           g + po[P_LNFB], part, BT, C, true, s));
     for (int l = Ly - 1; l >= 0; l--) {
@@ -416,13 +437,14 @@ template <typename T> int backward_impl(gpt2_t* M) {
         const T* fchg = a.fchg + l * BTC * 4;
         const size_t lC = (size_t)l * C;
         // fcproj: res3 = res2 + fchg Wfp^T + b   (dres is d res3)
-        RUN("gemm_dx", lin_dx<T>(M, a.dbig, a.dres, w + po[P_FCPROJW] + lC * 4 * C, BT, C, 4 * C, EPI_GELU_BWD, fch));
+        RUN("gemm_dx", lin_dx<T>(M, a.dbig, a.dres, w + po[P_FCPROJW] + lC * 4 * C, BT, C, 4 * C, EPI_GELU_BWD, fch,
+                                 fused ? g + po[P_FCB] + lC * 4 : nullptr));
         RUN("gemm_dw", lin_dw<T>(M, g + po[P_FCPROJW] + lC * 4 * C, a.dres, fchg, BT, C, 4 * C));
         RUN("colsum", colsum_accum<T>(g + po[P_FCPROJB] + lC, a.dres, BT, C, part, s));
         // fc: fch = ln2 Wfc^T + b   (dbig is d fch)
         RUN("gemm_dx", lin_dx<T>(M, a.dmid, a.dbig, w + po[P_FCW] + lC * 4 * C, BT, 4 * C, C, EPI_STORE));
         RUN("gemm_dw", lin_dw<T>(M, g + po[P_FCW] + lC * 4 * C, a.dbig, ln2, BT, 4 * C, C));
-        RUN("colsum", colsum_accum<T>(g + po[P_FCB] + lC * 4, a.dbig, BT, 4 * C, part, s));
+        if (!fused) RUN("colsum", colsum_accum<T>(g + po[P_FCB] + lC * 4, a.dbig, BT, 4 * C, part, s));
         // ln2: dres += LN2'(dmid)  -> dres is d res2
         RUN("layernorm_bwd", layernorm_bwd<T>(a.dres, a.dmid, res2, p + po[P_LN2W] + lC, a.ln2m + (size_t)l * BT,
                                               a.ln2r + (size_t)l * BT, g + po[P_LN2W] + lC, g + po[P_LN2B] + lC,
@@ -433,11 +455,11 @@ template <typename T> int backward_impl(gpt2_t* M) {
         RUN("colsum", colsum_accum<T>(g + po[P_ATTPROJB] + lC, a.dres, BT, C, part, s));
         // attention: dmid (d atty) -> dbig (d qkv)
         RUN("attention_bwd", attn_bwd<T>(a.dbig, a.dmid, qkv, atty, a.lse + (size_t)l * BT * NH, attD, B, T_,
-                                              C, NH, s));
+                                              C, NH, fused ? g + po[P_QKVB] + lC * 3 : nullptr, part, s));
         // qkv: qkv = ln1 Wqkv^T + b
         RUN("gemm_dx", lin_dx<T>(M, a.dmid, a.dbig, w + po[P_QKVW] + lC * 3 * C, BT, 3 * C, C, EPI_STORE));
         RUN("gemm_dw", lin_dw<T>(M, g + po[P_QKVW] + lC * 3 * C, a.dbig, ln1, BT, 3 * C, C));
-        RUN("colsum", colsum_accum<T>(g + po[P_QKVB] + lC * 3, a.dbig, BT, 3 * C, part, s));
+        if (!fused) RUN("colsum", colsum_accum<T>(g + po[P_QKVB] + lC * 3, a.dbig, BT, 3 * C, part, s));
         // ln1: dres += LN1'(dmid) -> dres is d xin
         RUN("layernorm_bwd", layernorm_bwd<T>(a.dres, a.dmid, xin, p + po[P_LN1W] + lC, a.ln1m + (size_t)l * BT,
                                               a.ln1r + (size_t)l * BT, g + po[P_LN1W] + lC, g + po[P_LN1B] + lC,
@@ -783,10 +805,10 @@ int gpt2_test_attention_bwd(gpt2_t* M, void* dqkv, const void* dout, const void*
     float* D = M->P<float>(M->L.attD);
     if (M->bf16mode())
         RUN("attention_test", attn_bwd<bf16>((bf16*)dqkv, (const bf16*)dout, (const bf16*)qkv, (const bf16*)out, lse,
-                                             D, B, T_, C, NH, M->stream));
+                                             D, B, T_, C, NH, nullptr, nullptr, M->stream));
     else
         RUN("attention_test", attn_bwd<float>((float*)dqkv, (const float*)dout, (const float*)qkv,
-                                              (const float*)out, lse, D, B, T_, C, NH, M->stream));
+                                              (const float*)out, lse, D, B, T_, C, NH, nullptr, nullptr, M->stream));
     return GPT2_OK;
 }
 

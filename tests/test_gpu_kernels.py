@@ -134,6 +134,7 @@ def test_gemm_split_k_weight_gradient():
 @pytest.mark.parametrize("prec,B,T,NH,hs", [
     (G.GPT2_BF16_MIXED, 2, 320, 2, 64),   # ragged against the 128-row blocks
     (G.GPT2_BF16_MIXED, 1, 1024, 1, 64),  # the full sequence length
+    (G.GPT2_BF16_MIXED, 2, 1024, 4, 64),  # 64 blocks: whole heads per XCD, blocks issued longest first
     (G.GPT2_BF16_MIXED, 3, 64, 3, 64),
     (G.GPT2_FP32, 2, 37, 3, 16),
     (G.GPT2_FP32, 1, 130, 2, 64),

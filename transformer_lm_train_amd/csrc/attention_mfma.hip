@@ -26,7 +26,7 @@
 // probabilities up to 256 are harmless in fp32 and bf16).
 //
 // Tiles stream through LDS in their natural [row][64] layout (16-byte chunk c
-// of row r in slot c ^ (r & 7)), loaded by global_load_lds_dwordx4 straight
+// of row r in slot c ^ aswz(r), see below), loaded by global_load_lds_dwordx4 straight
 // from global memory, NS stages deep.  A product that needs a tile
 // transposed (V^T, K^T, dO and Q as B operands) reads it with
 // ds_read_b64_tr_b16: within a 16-lane group, lane i receives element i%4 of
@@ -83,25 +83,46 @@ DEVI u32x4 ld_row(const bf16* p, bool ok) {
 // s_waitcnt immediate (gfx9 encoding): vmcnt <= N, lgkmcnt = 0, expcnt free
 template <int N> constexpr int vmcnt_imm() { return (N & 15) | ((N >> 4) << 14) | (7 << 4); }
 
-// rows [r0, r0+64) x 64 channels of a [*, ld] matrix into a swizzled tile;
-// each of the 4 waves issues 2 loads of 1 KB.  Callers stream whole 64-row
-// blocks of a sequence whose length is a multiple of 64, so every row read
-// exists.  `src` already points at row 0 of this wave's lanes
-// (see dma_lane_ptr); the row offset is wave-uniform.
-DEVI const bf16* dma_lane_ptr(const bf16* base, int ld, int wave, int lane) {
-    const int c = (lane & 7) ^ (lane >> 3);  // chunk landing in slot lane&7 of row lane>>3 (mod 8)
-    return base + (wave * 16 + (lane >> 3)) * ld + c * 8;
+// LDS swizzle of the [row][64] tiles (64 banks of 4 bytes: two 128-byte rows
+// per bank window): chunk c of row r sits in slot c ^ aswz(r), aswz(r) =
+// rot(r/2 mod 8) with rot moving bit 0 to bit 2.  Sixteen rows read at one
+// chunk (a 16-byte fragment read) then cover all 16 bank groups, and so do
+// the four rows x four-chunk groups a transposing read touches at once
+// (rows two apart differ in bit 2 of the swizzle).
+DEVI int aswz(int r) {
+    const int x = (r >> 1) & 7;
+    return ((x & 1) << 2) | (x >> 1);
 }
-DEVI void dma_tile(bf16* tile, const bf16* src, int ld, int r0, int wave) {
+
+// rows [r0, r0+64) x 64 channels of a [*, ld] matrix into a swizzled tile;
+// each of the 4 waves issues 2 loads of 1 KB (8 rows each).  Callers stream
+// whole 64-row blocks of a sequence whose length is a multiple of 64, so
+// every row read exists.  The per-lane source addresses of the two loads are
+// computed once (row 0 of the wave's 8-row blocks); the row offset r0 is
+// wave-uniform.
+struct LanePtr {
+    const bf16* p[2];
+};
+DEVI LanePtr dma_lane_ptr(const bf16* base, int ld, int wave, int lane) {
+    LanePtr lp;
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+        const int row = wave * 16 + i * 8 + (lane >> 3);  // tile row this lane lands in
+        const int c = (lane & 7) ^ aswz(row);             // chunk landing in slot lane & 7
+        lp.p[i] = base + row * ld + c * 8;
+    }
+    return lp;
+}
+DEVI void dma_tile(bf16* tile, const LanePtr& src, int ld, int r0, int wave) {
 #pragma unroll
     for (int i = 0; i < 2; i++)
-        __builtin_amdgcn_global_load_lds((glb_void_t*)(src + (r0 + i * 8) * ld), (lds_void_t*)(tile + (wave * 2 + i) * 512),
+        __builtin_amdgcn_global_load_lds((glb_void_t*)(src.p[i] + r0 * ld), (lds_void_t*)(tile + (wave * 2 + i) * 512),
                                          16, 0, 0);
 }
 
 // 8 consecutive channels chunk*8.. of tile row `row` (one 16-byte read)
 DEVI bf16x8 frag_row(const bf16* tile, int row, int chunk) {
-    return *reinterpret_cast<const bf16x8*>(tile + row * HS + ((chunk ^ (row & 7)) << 3));
+    return *reinterpret_cast<const bf16x8*>(tile + row * HS + ((chunk ^ aswz(row)) << 3));
 }
 
 // 4 consecutive rows krow..krow+3 of column mcol + (lane % 16), transposed
@@ -109,7 +130,7 @@ DEVI bf16x8 frag_row(const bf16* tile, int row, int chunk) {
 DEVI i16x4 tr4(const bf16* tile, int krow, int mcol, int lane) {
     const int j = lane & 15;
     const int r = krow + (j >> 2), c = mcol + 4 * (j & 3);
-    const int off = r * HS + ((((c >> 3) ^ (r & 7)) << 3) | (c & 7));
+    const int off = r * HS + ((((c >> 3) ^ aswz(r)) << 3) | (c & 7));
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + off));
 }
 
@@ -130,19 +151,30 @@ DEVI constexpr int acc_off(int r) { return ((r >> 2) << 3) + (r & 3); }  // acc_
 
 DEVI float exp2_raw(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Block placement on a 1-D grid of nblk blocks per (batch, head): workgroup
-// L runs on XCD L % 8, so when the grid size is a multiple of 8 each XCD
-// takes a contiguous range of work, i.e. all blocks of a few heads, whose
-// K/V (or Q/dO) re-reads then hit that XCD's L2.  Returns the block index
-// within the head (0 = first launched) and the head's (b, h).
+// Block placement on a 1-D grid of nblk blocks per (batch, head).
+// Workgroup L runs on XCD L % 8.  When the grid splits evenly, each XCD
+// takes a contiguous range of heads (their K/V or Q/dO re-reads then hit
+// that XCD's L2), and within it the blocks go out rank-major: rank 0 of
+// every head first, then rank 1, ...; callers give rank 0 to their longest
+// block, so the short blocks fill the tail of the launch.  Returns the rank
+// and the head's (b, h).
 DEVI int place_block(int nblk, int NH, int* h, int* b) {
     const int total = gridDim.x;
-    int w = blockIdx.x;
-    if ((total & 7) == 0) w = (w & 7) * (total >> 3) + (w >> 3);
-    const int bh = w / nblk;
+    const int L = blockIdx.x;
+    int bh, rank;
+    const int per_xcd = total >> 3;
+    if ((total & 7) == 0 && per_xcd % nblk == 0) {
+        const int heads = per_xcd / nblk;  // heads per XCD
+        const int pos = L >> 3;
+        rank = pos / heads;
+        bh = (L & 7) * heads + pos % heads;
+    } else {
+        bh = L / nblk;
+        rank = L % nblk;
+    }
     *h = bh % NH;
     *b = bh / NH;
-    return w % nblk;
+    return rank;
 }
 
 // The stages are distinct __shared__ arrays so that alias analysis keeps the
@@ -165,8 +197,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hi = lane >> 5, lq = lane & 31;
     const int C3 = 3 * C;
     const bf16* base = qkv + (int64_t)b * T * C3;
-    const bf16* kbase = dma_lane_ptr(base + C + h * HS, C3, w, lane);
-    const bf16* vbase = dma_lane_ptr(base + 2 * C + h * HS, C3, w, lane);
+    const LanePtr kbase = dma_lane_ptr(base + C + h * HS, C3, w, lane);
+    const LanePtr vbase = dma_lane_ptr(base + 2 * C + h * HS, C3, w, lane);
     const int q0 = qblk * QB + w * 32;
     const int q = q0 + lq;
 
@@ -287,8 +319,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hi = lane >> 5, lq = lane & 31;
     const int C3 = 3 * C;
     const bf16* base = qkv + (int64_t)b * T * C3;
-    const bf16* kbase = dma_lane_ptr(base + C + h * HS, C3, w, lane);
-    const bf16* vbase = dma_lane_ptr(base + 2 * C + h * HS, C3, w, lane);
+    const LanePtr kbase = dma_lane_ptr(base + C + h * HS, C3, w, lane);
+    const LanePtr vbase = dma_lane_ptr(base + 2 * C + h * HS, C3, w, lane);
     const int q0 = qblk * QB + w * 32;
     const int q = q0 + lq;
     const bool qok = q < T;
@@ -441,8 +473,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hi = lane >> 5, lq = lane & 31;
     const int C3 = 3 * C;
     const bf16* base = qkv + (int64_t)b * T * C3;
-    const bf16* qbase = dma_lane_ptr(base + h * HS, C3, w, lane);
-    const bf16* dbase = dma_lane_ptr(dout + (int64_t)b * T * C + h * HS, C, w, lane);
+    const LanePtr qbase = dma_lane_ptr(base + h * HS, C3, w, lane);
+    const LanePtr dbase = dma_lane_ptr(dout + (int64_t)b * T * C + h * HS, C, w, lane);
     const int k0 = kblk * QB + w * 32;
     const int key = k0 + lq;
 

@@ -188,7 +188,7 @@ DEVI int place_block(int nblk, int NH, int* h, int* b) {
     } while (0)
 
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void flash_fwd_kernel(bf16* out, float* lse, const bf16* qkv, int T, int C, int NH) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void flash_fwd_kernel(bf16* out, float* lse, const bf16* qkv, int T, int C, int NH) {
     __shared__ __attribute__((aligned(1024))) bf16 k0s[TILE], k1s[TILE], k2s[TILE];
     __shared__ __attribute__((aligned(1024))) bf16 v0s[TILE], v1s[TILE], v2s[TILE];
     const int nqb = (T + QB - 1) / QB;

@@ -618,15 +618,14 @@ hipError_t flash_attention_fwd(bf16* out, float* lse, const bf16* qkv, int B, in
     return hipGetLastError();
 }
 
+int flash_attention_bias_rows(int B, int T) { return B * ((T + QB - 1) / QB); }
+
 hipError_t flash_attention_bwd(bf16* dqkv, const bf16* dout, const bf16* qkv, const bf16* out, const float* lse,
-                               float* dbuf, int B, int T, int C, int NH, float* dbias, float* bpart,
-                               hipStream_t s) {
+                               float* dbuf, int B, int T, int C, int NH, float* bpart, hipStream_t s) {
     if (C / NH != HS || C % NH || T % KB) return hipErrorInvalidValue;
     const unsigned grid = (unsigned)((T + QB - 1) / QB * NH * B);
     const int64_t rows = (int64_t)B * NH * T;
-    float* bp = dbias ? bpart : nullptr;
-    flash_bwd_dq_kernel<<<grid, 256, 0, s>>>(dqkv, dbuf, dbuf + rows, dout, qkv, out, lse, T, C, NH, bp);
-    flash_bwd_dkdv_kernel<<<grid, 256, 0, s>>>(dqkv, dbuf, dbuf + rows, dout, qkv, T, C, NH, bp);
-    if (dbias) return sum_partials(dbias, nullptr, nullptr, bpart, B * ((T + QB - 1) / QB), 3 * C, s);
+    flash_bwd_dq_kernel<<<grid, 256, 0, s>>>(dqkv, dbuf, dbuf + rows, dout, qkv, out, lse, T, C, NH, bpart);
+    flash_bwd_dkdv_kernel<<<grid, 256, 0, s>>>(dqkv, dbuf, dbuf + rows, dout, qkv, T, C, NH, bpart);
     return hipGetLastError();
 }

@@ -67,7 +67,7 @@ DEVI void epilogue_rows(const GemmArgs& g, const f32x16 (&acc)[FM][FN], float* r
     constexpr bool BIAS = EPI == EPI_BIAS || EPI == EPI_BIAS_RESID || EPI == EPI_BIAS_GELU;
     typedef bf16 bf16x8_t __attribute__((ext_vector_type(8)));
     const int hi = lane >> 5, l32 = lane & 31;
-    constexpr bool CSUM = EPI == EPI_GELU_BWD;  // column sums of the outputs, if g.colsum
+    constexpr bool CSUM = EPI == EPI_GELU_BWD;  // column sums of the outputs, if g.colsum_ws
     float cs[NCG][8];
 #pragma unroll
     for (int cg = 0; cg < NCG; cg++)
@@ -168,7 +168,7 @@ DEVI void epilogue_rows(const GemmArgs& g, const f32x16 (&acc)[FM][FN], float* r
             }
     }
     if constexpr (CSUM) {
-        if (g.colsum) {
+        if (g.colsum_ws) {
             // lanes l, l + LPR, l + 2 LPR, ... hold the same columns: combine
             // them (fixed butterfly order), then lanes 0 .. LPR-1 write the
             // wave's partial row
@@ -597,13 +597,7 @@ hipError_t gemm_mfma_bf16(const GemmArgs& g, hipStream_t s) {
     if (g.a_kcontig && !g.b_kcontig) {
         switch (g.epi) {
             case EPI_STORE: return w192 ? BIG192(true, false, EPI_STORE) : BIG256(true, false, EPI_STORE);
-            case EPI_GELU_BWD: {
-                hipError_t e = w192 ? BIG192(true, false, EPI_GELU_BWD) : BIG256(true, false, EPI_GELU_BWD);
-                if (e != hipSuccess || !g.colsum) return e;
-                // one partial row per wave row block: 4 per 256-row tile (192-wide tiles), else 2
-                const int G = (int)cdiv(g.M, 256) * (w192 ? 4 : 2);
-                return sum_partials(g.colsum, nullptr, nullptr, g.colsum_ws, G, g.N, s);
-            }
+            case EPI_GELU_BWD: return w192 ? BIG192(true, false, EPI_GELU_BWD) : BIG256(true, false, EPI_GELU_BWD);
             default: return hipErrorInvalidValue;
         }
     }
@@ -627,6 +621,9 @@ hipError_t gemm_mfma_bf16(const GemmArgs& g, hipStream_t s) {
 #undef BIG256
     return hipErrorInvalidValue;
 }
+
+// one partial row per wave row block: 4 per 256-row tile (192-wide tiles), else 2
+int gemm_colsum_rows(int M, int N) { return (int)cdiv(M, 256) * (use_192(M, N) ? 4 : 2); }
 
 size_t gemm_splitk_ws_bytes(int M, int N, int K) {
     int S, kc;

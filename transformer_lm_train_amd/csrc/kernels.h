@@ -37,13 +37,14 @@ struct GemmArgs {
     int epi;
     float* ws;           // split-K workspace (EPI_ACC_F32), may be NULL
     size_t ws_bytes;
-    // EPI_GELU_BWD, bf16 MFMA path: colsum[n] += sum_m out[m][n] (the bias
+    // EPI_GELU_BWD, bf16 MFMA path: partial column sums of out (the bias
     // gradient of the layer whose output gradient this product produces),
-    // through per-wave partial rows in colsum_ws (fixed-order sum).  NULL: off.
-    float* colsum;
+    // one row per wave row block: colsum_ws [gemm_colsum_rows(M, N)][N].
+    // The caller sums them (sum_partials_batch).  NULL: off.
     float* colsum_ws;
 };
 size_t gemm_splitk_ws_bytes(int M, int N, int K);
+int gemm_colsum_rows(int M, int N);
 
 // fp32-accumulating SIMT kernel for any shapes (activation dtype T).
 template <typename T> hipError_t gemm_simt(const GemmArgs& g, hipStream_t s);
@@ -62,14 +63,24 @@ hipError_t encoder_bwd(float* dwte, float* dwpe, const T* dx, const int* tokens,
 template <typename T>
 hipError_t layernorm_fwd(T* out, float* mean, float* rstd, const T* x, const float* w, const float* b,
                          int N, int C, hipStream_t s);
-// dres (+)= LN backward of dy; per-block partial dw/db go to partial[2][G][C]
-// and are then summed in block order into dw, db.  G <= 1024.
+// dres (+)= LN backward of dy.  Per-block partial sums go to partial[NP][G][C]
+// with G = layernorm_bwd_blocks(N) <= 1024: dw, db and, if dsum (NP = 3), the
+// column sums of the new dres.  The caller adds them to their outputs with
+// sum_partials_batch ({dw, db, dsum-target}, partial, G, C).
+int layernorm_bwd_blocks(int N);
 template <typename T>
 hipError_t layernorm_bwd(T* dres, const T* dy, const T* x, const float* w, const float* mean,
-                         const float* rstd, float* dw, float* db, float* partial, int N, int C,
-                         bool overwrite, hipStream_t s);
-// out_k[c] += sum_g partial[k*G + g][c] for the non-null out_k, k < 3, in a
-// fixed order.
+                         const float* rstd, float* partial, int N, int C, bool overwrite, bool dsum, hipStream_t s);
+// A fixed-order column sum of partial rows: out[k][c] += sum_g partial[k*G + g][c]
+// for each non-null out[k], k < 3 (out[0] required).
+struct SumJob {
+    float* out[3];
+    const float* partial;
+    int G, C;
+};
+constexpr int SUM_JOBS_MAX = 6;
+// Runs up to SUM_JOBS_MAX jobs in one launch.
+hipError_t sum_partials_batch(const SumJob* jobs, int n, hipStream_t s);
 hipError_t sum_partials(float* out0, float* out1, float* out2, const float* partial, int G, int C, hipStream_t s);
 // dbias[n] += sum_m dy[m][n] (deterministic two-stage sum via partial).
 template <typename T>
@@ -100,10 +111,11 @@ hipError_t attention_bwd(T* dqkv, const T* dout, const T* qkv, const T* out, con
                          int B, int T_, int C, int NH, hipStream_t s);
 // head size 64, bf16, MFMA flash kernels, T % 64 == 0; dbuf holds 2*B*NH*T
 // floats: D = rowsum(dO o O), then -lse*log2(e), one per (b, h, t).  With
-// dbias, the backward also adds the column sums of dqkv to dbias [3C] (the
-// qkv bias gradient), through bpart [B * ceil(T/128)][3C].
+// bpart, the backward also writes partial column sums of dqkv (the qkv bias
+// gradient) to bpart [flash_attention_bias_rows(B, T)][3C], one row per
+// (batch, 128-query block); the caller sums them (sum_partials_batch).
+int flash_attention_bias_rows(int B, int T_);
 
 hipError_t flash_attention_fwd(bf16* out, float* lse, const bf16* qkv, int B, int T_, int C, int NH, hipStream_t s);
 hipError_t flash_attention_bwd(bf16* dqkv, const bf16* dout, const bf16* qkv, const bf16* out, const float* lse,
-                               float* dbuf, int B, int T_, int C, int NH, float* dbias, float* bpart,
-                               hipStream_t s);
+                               float* dbuf, int B, int T_, int C, int NH, float* bpart, hipStream_t s);

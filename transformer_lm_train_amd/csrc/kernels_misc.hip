@@ -161,80 +161,104 @@ hipError_t layernorm_fwd(T* out, float* mean, float* rstd, const T* x, const flo
 // ============================================================================
 // LayerNorm backward.  With xhat = (x-mean)*rstd and g = dy*w:
 //   dx = rstd * (g - mean_c(g) - xhat * mean_c(g*xhat)),  dres (+)= dx;
-//   dw += sum_rows dy*xhat,  db += sum_rows dy.
-// Each block handles rows blk*4+wave, stepping by 4*G, keeps per-channel
-// dw/db sums in registers, reduces its 4 waves in LDS and writes one
-// partial row; a second kernel sums the G partials in block order.
+//   dw += sum_rows dy*xhat,  db += sum_rows dy,
+// and, with NP = 3, the column sums of the new dres as well: that is the
+// gradient of the bias of the projection whose output joined the residual
+// stream at this point.  Each block handles rows blk*4+wave, stepping by 4*G
+// (the next row's operands are requested before the current row is worked),
+// keeps its per-channel sums in registers, reduces its 4 waves in LDS and
+// writes one partial row per sum; sum_partials_batch adds the G partials in
+// block order.
 // ============================================================================
 constexpr int LN_BWD_G = 1024;
 
-template <typename T, int MAXV>
+int layernorm_bwd_blocks(int N) { return (int)std::min<int64_t>(cdiv(N, 4), LN_BWD_G); }
+
+template <typename T, int MAXV, int NP>
 __global__ __launch_bounds__(256) void layernorm_bwd_kernel(T* dres, const T* dy, const T* x, const float* w,
                                                             const float* mean, const float* rstd,
                                                             float* partial, int N, int C, int overwrite) {
     constexpr int VN = Vec16<T>::N;
-    constexpr int NP = 2;            // partial sums per channel (dw, db)
     extern __shared__ float smem[];  // [4][NP][C]
-    int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    int chunks = C / VN;
-    float aw[MAXV][VN], ab[MAXV][VN];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int chunks = C / VN;
+    const int step = gridDim.x * 4;
+    float acc[NP][MAXV][VN];
 #pragma unroll
-    for (int i = 0; i < MAXV; i++)
+    for (int k = 0; k < NP; k++)
 #pragma unroll
-        for (int j = 0; j < VN; j++) { aw[i][j] = 0.f; ab[i][j] = 0.f; }
-    for (int row = blockIdx.x * 4 + wv; row < N; row += gridDim.x * 4) {
-        float mu = mean[row], rs = rstd[row];
-        const T* xr = x + (int64_t)row * C;
-        const T* dr = dy + (int64_t)row * C;
+        for (int i = 0; i < MAXV; i++)
+#pragma unroll
+            for (int j = 0; j < VN; j++) acc[k][i][j] = 0.f;
+    Vec16<T> xv[MAXV], dv[MAXV], ov[MAXV];
+    float mu = 0.f, rs = 0.f;
+    auto load = [&](int r) {
+        const int64_t o = (int64_t)r * C;
+#pragma unroll
+        for (int i = 0; i < MAXV; i++) {
+            const int ch = lane + i * 64;
+            if (ch < chunks) {
+                xv[i] = ld16(x + o + ch * VN);
+                dv[i] = ld16(dy + o + ch * VN);
+                if (!overwrite) ov[i] = ld16(dres + o + ch * VN);
+            }
+        }
+        mu = mean[r];
+        rs = rstd[r];
+    };
+    int row = blockIdx.x * 4 + wv;
+    if (row < N) load(row);
+    for (; row < N; row += step) {
+        const float rmu = mu, rrs = rs;
         float xh[MAXV][VN], gg[MAXV][VN];
+        Vec16<T> o[MAXV];
         float sg = 0.f, sgx = 0.f;
 #pragma unroll
         for (int i = 0; i < MAXV; i++) {
-            int ch = lane + i * 64;
+            const int ch = lane + i * 64;
             if (ch < chunks) {
-                Vec16<T> xv = ld16(xr + ch * VN);
-                Vec16<T> dv = ld16(dr + ch * VN);
+                o[i] = ov[i];
 #pragma unroll
                 for (int j = 0; j < VN; j++) {
-                    int c = ch * VN + j;
-                    float d = to_f32(dv.v[j]);
-                    xh[i][j] = (to_f32(xv.v[j]) - mu) * rs;
+                    const int c = ch * VN + j;
+                    const float d = to_f32(dv[i].v[j]);
+                    xh[i][j] = (to_f32(xv[i].v[j]) - rmu) * rrs;
                     gg[i][j] = d * w[c];
                     sg += gg[i][j];
                     sgx += gg[i][j] * xh[i][j];
-                    aw[i][j] += d * xh[i][j];
-                    ab[i][j] += d;
+                    acc[0][i][j] += d * xh[i][j];
+                    acc[1][i][j] += d;
                 }
             }
         }
+        if (row + step < N) load(row + step);
         sg = wave_sum(sg) / C;
         sgx = wave_sum(sgx) / C;
         T* orow = dres + (int64_t)row * C;
 #pragma unroll
         for (int i = 0; i < MAXV; i++) {
-            int ch = lane + i * 64;
+            const int ch = lane + i * 64;
             if (ch < chunks) {
-                Vec16<T> o;
-                if (!overwrite) o = ld16(orow + ch * VN);
 #pragma unroll
                 for (int j = 0; j < VN; j++) {
-                    float dx = rs * (gg[i][j] - sg - xh[i][j] * sgx);
-                    o.v[j] = from_f32<T>(overwrite ? dx : to_f32(o.v[j]) + dx);
+                    const float dx = rrs * (gg[i][j] - sg - xh[i][j] * sgx);
+                    const T r = from_f32<T>(overwrite ? dx : to_f32(o[i].v[j]) + dx);
+                    o[i].v[j] = r;
+                    if constexpr (NP == 3) acc[2][i][j] += to_f32(r);
                 }
-                st16(orow + ch * VN, o);
+                st16(orow + ch * VN, o[i]);
             }
         }
     }
     // block reduction of the per-channel sums over the 4 waves
 #pragma unroll
     for (int i = 0; i < MAXV; i++) {
-        int ch = lane + i * 64;
+        const int ch = lane + i * 64;
         if (ch < chunks) {
 #pragma unroll
-            for (int j = 0; j < VN; j++) {
-                smem[(wv * NP + 0) * C + ch * VN + j] = aw[i][j];
-                smem[(wv * NP + 1) * C + ch * VN + j] = ab[i][j];
-            }
+            for (int k = 0; k < NP; k++)
+#pragma unroll
+                for (int j = 0; j < VN; j++) smem[(wv * NP + k) * C + ch * VN + j] = acc[k][i][j];
         }
     }
     __syncthreads();
@@ -248,17 +272,27 @@ __global__ __launch_bounds__(256) void layernorm_bwd_kernel(T* dres, const T* dy
     }
 }
 
-// out_k[c] += sum_g partial[k*G + g][c] for each non-null out_k (k < 3).
-// Block: 16 columns x 64 row lanes; lane r sums partial rows r, r+64, ...
-// (all its loads independent, so the whole array is in flight at once), then
-// the 64 lane sums of a column are combined in a fixed order.
-__global__ __launch_bounds__(1024) void sum_partials_kernel(float* out0, float* out1, float* out2,
-                                                            const float* partial, int G, int C) {
+// For each job, out_k[c] += sum_g partial[k*G + g][c] for its non-null out_k
+// (k < 3).  Block: 16 columns x 64 row lanes of one job (the jobs' blocks are
+// laid end to end); lane r sums partial rows r, r+64, ... (all its loads
+// independent, so the whole array is in flight at once), then the 64 lane
+// sums of a column are combined in a fixed order.
+struct SumBatch {
+    SumJob job[SUM_JOBS_MAX];
+    int start[SUM_JOBS_MAX + 1];  // first block of each job
+    int n;
+};
+
+__global__ __launch_bounds__(1024) void sum_partials_kernel(SumBatch bt) {
     __shared__ float red[3][64][17];
+    int k = 0;
+    while (k + 1 < bt.n && (int)blockIdx.x >= bt.start[k + 1]) k++;
+    const SumJob& jb = bt.job[k];
+    const int G = jb.G, C = jb.C;
+    const float* partial = jb.partial;
     const int cx = threadIdx.x & 15, ry = threadIdx.x >> 4;
-    const int c = blockIdx.x * 16 + cx;
-    float* outs[3] = {out0, out1, out2};
-    const int nk = out2 ? 3 : out1 ? 2 : 1;  // out0 is always given
+    const int c = ((int)blockIdx.x - bt.start[k]) * 16 + cx;
+    const int nk = jb.out[2] ? 3 : jb.out[1] ? 2 : 1;  // out[0] is always given
     float t0 = 0.f, t1 = 0.f, t2 = 0.f;
     if (c < C)
         for (int g = ry; g < G; g += 64) {  // the nk loads of a row are independent
@@ -272,38 +306,53 @@ __global__ __launch_bounds__(1024) void sum_partials_kernel(float* out0, float* 
     red[2][ry][cx] = t2;
     __syncthreads();
     if (threadIdx.x < 48) {
-        const int k = threadIdx.x >> 4;
-        if (c < C && outs[k]) {
+        const int q = threadIdx.x >> 4;
+        float* out = q == 0 ? jb.out[0] : q == 1 ? jb.out[1] : jb.out[2];
+        if (c < C && out) {
             float t = 0.f;
-            for (int i = 0; i < 64; i++) t += red[k][i][cx];
-            outs[k][c] += t;
+            for (int i = 0; i < 64; i++) t += red[q][i][cx];
+            out[c] += t;
         }
     }
 }
 
-hipError_t sum_partials(float* out0, float* out1, float* out2, const float* partial, int G, int C, hipStream_t s) {
-    sum_partials_kernel<<<cdiv(C, 16), 1024, 0, s>>>(out0, out1, out2, partial, G, C);
+hipError_t sum_partials_batch(const SumJob* jobs, int n, hipStream_t s) {
+    if (n < 0 || n > SUM_JOBS_MAX) return hipErrorInvalidValue;
+    if (n == 0) return hipSuccess;
+    SumBatch bt{};
+    bt.n = n;
+    bt.start[0] = 0;
+    for (int i = 0; i < n; i++) {
+        if (!jobs[i].out[0] || !jobs[i].partial || jobs[i].G <= 0 || jobs[i].C <= 0) return hipErrorInvalidValue;
+        bt.job[i] = jobs[i];
+        bt.start[i + 1] = bt.start[i] + (int)cdiv(jobs[i].C, 16);
+    }
+    sum_partials_kernel<<<bt.start[n], 1024, 0, s>>>(bt);
     return hipGetLastError();
+}
+
+hipError_t sum_partials(float* out0, float* out1, float* out2, const float* partial, int G, int C, hipStream_t s) {
+    const SumJob j{{out0, out1, out2}, partial, G, C};
+    return sum_partials_batch(&j, 1, s);
 }
 
 template <typename T>
 hipError_t layernorm_bwd(T* dres, const T* dy, const T* x, const float* w, const float* mean, const float* rstd,
-                         float* dw, float* db, float* partial, int N, int C, bool overwrite, hipStream_t s) {
-    if (C % Vec16<T>::N || C / Vec16<T>::N > LN_MAXV * 64) return hipErrorInvalidValue;
-    int G = (int)cdiv(N, 4);
-    if (G > LN_BWD_G) G = LN_BWD_G;
-    size_t lds = sizeof(float) * 8 * C;
-    int per_lane = (int)cdiv(C / Vec16<T>::N, 64);
-    int ow = overwrite ? 1 : 0;
-    if (per_lane <= 1)
-        layernorm_bwd_kernel<T, 1><<<G, 256, lds, s>>>(dres, dy, x, w, mean, rstd, partial, N, C, ow);
-    else if (per_lane <= 2)
-        layernorm_bwd_kernel<T, 2><<<G, 256, lds, s>>>(dres, dy, x, w, mean, rstd, partial, N, C, ow);
-    else if (per_lane <= 4)
-        layernorm_bwd_kernel<T, 4><<<G, 256, lds, s>>>(dres, dy, x, w, mean, rstd, partial, N, C, ow);
-    else
-        layernorm_bwd_kernel<T, 8><<<G, 256, lds, s>>>(dres, dy, x, w, mean, rstd, partial, N, C, ow);
-    sum_partials_kernel<<<cdiv(C, 16), 1024, 0, s>>>(dw, db, nullptr, partial, G, C);
+                         float* partial, int N, int C, bool overwrite, bool dsum, hipStream_t s) {
+    if (C % Vec16<T>::N || C / Vec16<T>::N > LN_MAXV * 64 || N <= 0) return hipErrorInvalidValue;
+    const int G = layernorm_bwd_blocks(N);
+    const int NP = dsum ? 3 : 2;
+    const size_t lds = sizeof(float) * 4 * NP * C;
+    const int per_lane = (int)cdiv(C / Vec16<T>::N, 64);
+    const int ow = overwrite ? 1 : 0;
+#define LN_BWD(V)                                                                                             \
+    (dsum ? layernorm_bwd_kernel<T, V, 3><<<G, 256, lds, s>>>(dres, dy, x, w, mean, rstd, partial, N, C, ow)  \
+          : layernorm_bwd_kernel<T, V, 2><<<G, 256, lds, s>>>(dres, dy, x, w, mean, rstd, partial, N, C, ow))
+    if (per_lane <= 1) LN_BWD(1);
+    else if (per_lane <= 2) LN_BWD(2);
+    else if (per_lane <= 4) LN_BWD(4);
+    else LN_BWD(8);
+#undef LN_BWD
     return LAUNCH_CHECK();
 }
 
@@ -349,8 +398,8 @@ hipError_t colsum_accum(float* dbias, const T* dy, int M, int N, float* partial,
     int G = COLSUM_G;
     dim3 grid(cdiv(N / VN, 64), G);
     colsum_kernel<T><<<grid, 256, 0, s>>>(partial, dy, M, N);
-    sum_partials_kernel<<<cdiv(N, 16), 1024, 0, s>>>(dbias, nullptr, nullptr, partial, G, N);
-    return LAUNCH_CHECK();
+    hipError_t e = LAUNCH_CHECK();
+    return e != hipSuccess ? e : sum_partials(dbias, nullptr, nullptr, partial, G, N, s);
 }
 
 // ============================================================================
@@ -645,7 +694,7 @@ template <typename T> hipError_t widen_f32(float* dst, const T* src, size_t n, h
     template hipError_t layernorm_fwd<T>(T*, float*, float*, const T*, const float*, const float*, int, int, \
                                          hipStream_t);                                                       \
     template hipError_t layernorm_bwd<T>(T*, const T*, const T*, const float*, const float*, const float*,   \
-                                         float*, float*, float*, int, int, bool, hipStream_t);               \
+                                         float*, int, int, bool, bool, hipStream_t);                         \
     template hipError_t colsum_accum<T>(float*, const T*, int, int, float*, hipStream_t);                    \
     template hipError_t softmax_ce<T>(T*, float*, const int*, int, int, int, float, int*, hipStream_t);      \
     template hipError_t widen_f32<T>(float*, const T*, size_t, hipStream_t);

@@ -67,7 +67,7 @@ struct Layout {
     size_t params, grads, m, v, shadow;
     size_t encoded, ln1, qkv, atty, res2, ln2, fch, fchg, res3, lnf, logits;
     size_t ln1_mean, ln1_rstd, ln2_mean, ln2_rstd, lnf_mean, lnf_rstd, lse, losses;
-    size_t dres, dbig, dmid, attD, partial, norm_partial, scalars, err, tokens, targets, splitk;
+    size_t dres, dbig, dmid, attD, part_fin, part_ln2, part_ln1, part_fc, part_qkv, norm_partial, scalars, err, tokens, targets, splitk;
     size_t splitk_bytes;
     size_t total;
 };
@@ -137,16 +137,21 @@ Layout make_layout(const gpt2_config& c) {
     L.dmid = add(A * BT * C);
     L.attD = add(2 * 4 * BT * c.num_heads);  // D and the base-2 lse of every attention row
     {
-        // partial sums of the fixed-order reductions; the largest of: LN
-        // backward (2 per channel, up to 1024 rows), the fused bias column
-        // sums of the GELU' product (4 rows per 256 tokens, 4C wide) and of
-        // attention (one row per 128-token block, 3C wide), the stand-alone
-        // column sums (256 rows, up to 4C wide)
-        const size_t ln = 2 * 1024 * (size_t)C;
-        const size_t ge = cdiv(BT, 256) * 4 * 4 * (size_t)C;
-        const size_t at = (size_t)c.batch_size * cdiv(c.seq_len, 128) * 3 * C;
-        const size_t cs = 256 * 4 * (size_t)C;
-        L.partial = add(4 * std::max(std::max(ln, ge), std::max(at, cs)));
+        // Partial rows of the fixed-order column sums of the backward pass,
+        // one region per producer so that a layer's sums can run as one
+        // batch at its end: the final LN and the two LNs of a block (3 sums
+        // per channel, up to 1024 rows), the fc bias (the GELU' product's 4
+        // rows per 256 tokens, 4C wide, or the stand-alone column sums' 256
+        // rows in fp32 mode) and the qkv bias (attention's row per
+        // 128-token block, 3C wide, or the stand-alone column sums).
+        const size_t ln = 3 * 1024 * (size_t)C;
+        const size_t fc = std::max<size_t>(cdiv(BT, 256) * 4, 256) * 4 * C;
+        const size_t qk = std::max<size_t>((size_t)c.batch_size * cdiv(c.seq_len, 128), 256) * 3 * C;
+        L.part_fin = add(4 * ln);
+        L.part_ln2 = add(4 * ln);
+        L.part_ln1 = add(4 * ln);
+        L.part_fc = add(4 * fc);
+        L.part_qkv = add(4 * qk);
     }
     L.norm_partial = add(4 * 1024);
     L.scalars = add(64);
@@ -287,17 +292,17 @@ hipError_t lin_fwd(gpt2_t* Mo, T* out, const T* X, const T* W, const float* bias
     return gemm<T>(Mo, g);
 }
 // dX[M,K] = dY[M,N] W[N,K]  (+ GELU' epilogue with aux)
-// With colsum (bf16 GELU' path only), colsum[k] += sum_m dX[m][k] as well.
+// With colsum_ws (bf16 GELU' path only), partial column sums of dX as well:
+// gemm_colsum_rows(M, K) rows of K.
 template <typename T>
 hipError_t lin_dx(gpt2_t* Mo, T* dX, const T* dY, const T* W, int M, int N, int K, int epi, const T* aux = nullptr,
-                  float* colsum = nullptr) {
+                  float* colsum_ws = nullptr) {
     GemmArgs g{};
     g.M = M; g.N = K; g.K = N;
     g.a = dY; g.lda = N; g.a_kcontig = true;
     g.b = W; g.ldb = K; g.b_kcontig = false;
     g.out = dX; g.ldo = K; g.aux = aux; g.epi = epi;
-    g.colsum = colsum;
-    g.colsum_ws = colsum ? Mo->P<float>(Mo->L.partial) : nullptr;
+    g.colsum_ws = colsum_ws;
     return gemm<T>(Mo, g);
 }
 // dW[N,K] += dY[M,N]^T X[M,K]
@@ -318,12 +323,12 @@ hipError_t attn_fwd(T* out, float* lse, const T* qkv, int B, int T_, int C, int 
     if constexpr (std::is_same<T, bf16>::value) return flash_attention_fwd(out, lse, qkv, B, T_, C, NH, s);
     else return attention_fwd<float>(out, lse, qkv, B, T_, C, NH, s);
 }
-// dbias (bf16 path): qkv bias gradient from the kernels' own column sums
+// bpart (bf16 path): partial column sums of dqkv, the qkv bias gradient
 template <typename T>
 hipError_t attn_bwd(T* dqkv, const T* dout, const T* qkv, const T* out, const float* lse, float* dbuf, int B, int T_,
-                    int C, int NH, float* dbias, float* bpart, hipStream_t s) {
+                    int C, int NH, float* bpart, hipStream_t s) {
     if constexpr (std::is_same<T, bf16>::value)
-        return flash_attention_bwd(dqkv, dout, qkv, out, lse, dbuf, B, T_, C, NH, dbias, bpart, s);
+        return flash_attention_bwd(dqkv, dout, qkv, out, lse, dbuf, B, T_, C, NH, bpart, s);
     else return attention_bwd<float>(dqkv, dout, qkv, out, lse, dbuf, B, T_, C, NH, s);
 }
 
@@ -412,20 +417,28 @@ template <typename T> int backward_impl(gpt2_t* M) {
     const T* w = weights<T>(M);
     const size_t* po = M->L.poff;
     const size_t BTC = a.BTC;
-    float* part = M->P<float>(M->L.partial);
+    float* pfin = M->P<float>(M->L.part_fin);
+    float* pln2 = M->P<float>(M->L.part_ln2);
+    float* pln1 = M->P<float>(M->L.part_ln1);
+    float* pfc = M->P<float>(M->L.part_fc);
+    float* pqkv = M->P<float>(M->L.part_qkv);
     float* attD = M->P<float>(M->L.attD);
+    const int Gln = layernorm_bwd_blocks(BT);
 
     // classifier (tied to wte): logits now hold dlogits
     RUN("gemm_classifier_dx", lin_dx<T>(M, a.dmid, a.logits, w + po[P_WTE], BT, Vp, C, EPI_STORE));
     RUN("gemm_classifier_dw", lin_dw<T>(M, g + po[P_WTE], a.logits, a.lnf, BT, Vp, C));
     const T* xlast = a.res3 + (size_t)(Ly - 1) * BTC;
-    // Bias gradients are column sums of the output gradients.  In bf16 mode
-    // the kernel that produces the gradient also takes its column sums for
-    // fc (the GELU' product) and qkv (the attention backward); the others
-    // (and all of them in fp32 mode) get a column-sum pass.
+    // Bias gradients are column sums of the output gradients, taken as
+    // partial rows by the kernel that produces each gradient and summed in a
+    // fixed order, one batched launch per layer: attproj and fcproj from the
+    // LN backward that writes the residual-stream gradient they see (LN2 of
+    // the block, and the final LN or LN1 of the block above); in bf16 mode fc
+    // from the GELU' product and qkv from the attention backward (fp32 mode:
+    // a column-sum pass each).
     constexpr bool fused = std::is_same<T, bf16>::value;
-    RUN("layernorm_bwd", layernorm_bwd<T>(a.dres, a.dmid, xlast, p + po[P_LNFW], a.lnfm, a.lnfr, g + po[P_LNFW],
-                                          g + po[P_LNFB], part, BT, C, true, s));
+    RUN("layernorm_bwd", layernorm_bwd<T>(a.dres, a.dmid, xlast, p + po[P_LNFW], a.lnfm, a.lnfr, pfin, BT, C, true,
+                                          true, s));
     for (int l = Ly - 1; l >= 0; l--) {
         const T* xin = l == 0 ? a.encoded : a.res3 + (size_t)(l - 1) * BTC;
         const T* ln1 = a.ln1 + l * BTC;
@@ -436,34 +449,40 @@ template <typename T> int backward_impl(gpt2_t* M) {
         const T* fch = a.fch + l * BTC * 4;
         const T* fchg = a.fchg + l * BTC * 4;
         const size_t lC = (size_t)l * C;
+        SumJob jobs[SUM_JOBS_MAX];
+        int nj = 0;
+        if (l == Ly - 1) jobs[nj++] = SumJob{{g + po[P_LNFW], g + po[P_LNFB], g + po[P_FCPROJB] + lC}, pfin, Gln, C};
         // fcproj: res3 = res2 + fchg Wfp^T + b   (dres is d res3)
         RUN("gemm_dx", lin_dx<T>(M, a.dbig, a.dres, w + po[P_FCPROJW] + lC * 4 * C, BT, C, 4 * C, EPI_GELU_BWD, fch,
-                                 fused ? g + po[P_FCB] + lC * 4 : nullptr));
+                                 fused ? pfc : nullptr));
+        if (fused) jobs[nj++] = SumJob{{g + po[P_FCB] + lC * 4}, pfc, gemm_colsum_rows(BT, 4 * C), 4 * C};
         RUN("gemm_dw", lin_dw<T>(M, g + po[P_FCPROJW] + lC * 4 * C, a.dres, fchg, BT, C, 4 * C));
-        RUN("colsum", colsum_accum<T>(g + po[P_FCPROJB] + lC, a.dres, BT, C, part, s));
         // fc: fch = ln2 Wfc^T + b   (dbig is d fch)
         RUN("gemm_dx", lin_dx<T>(M, a.dmid, a.dbig, w + po[P_FCW] + lC * 4 * C, BT, 4 * C, C, EPI_STORE));
         RUN("gemm_dw", lin_dw<T>(M, g + po[P_FCW] + lC * 4 * C, a.dbig, ln2, BT, 4 * C, C));
-        if (!fused) RUN("colsum", colsum_accum<T>(g + po[P_FCB] + lC * 4, a.dbig, BT, 4 * C, part, s));
+        if (!fused) RUN("colsum", colsum_accum<T>(g + po[P_FCB] + lC * 4, a.dbig, BT, 4 * C, pfc, s));
         // ln2: dres += LN2'(dmid)  -> dres is d res2
         RUN("layernorm_bwd", layernorm_bwd<T>(a.dres, a.dmid, res2, p + po[P_LN2W] + lC, a.ln2m + (size_t)l * BT,
-                                              a.ln2r + (size_t)l * BT, g + po[P_LN2W] + lC, g + po[P_LN2B] + lC,
-                                              part, BT, C, false, s));
+                                              a.ln2r + (size_t)l * BT, pln2, BT, C, false, true, s));
+        jobs[nj++] = SumJob{{g + po[P_LN2W] + lC, g + po[P_LN2B] + lC, g + po[P_ATTPROJB] + lC}, pln2, Gln, C};
         // attproj: res2 = xin + atty Wap^T + b
         RUN("gemm_dx", lin_dx<T>(M, a.dmid, a.dres, w + po[P_ATTPROJW] + lC * C, BT, C, C, EPI_STORE));
         RUN("gemm_dw", lin_dw<T>(M, g + po[P_ATTPROJW] + lC * C, a.dres, atty, BT, C, C));
-        RUN("colsum", colsum_accum<T>(g + po[P_ATTPROJB] + lC, a.dres, BT, C, part, s));
         // attention: dmid (d atty) -> dbig (d qkv)
         RUN("attention_bwd", attn_bwd<T>(a.dbig, a.dmid, qkv, atty, a.lse + (size_t)l * BT * NH, attD, B, T_,
-                                              C, NH, fused ? g + po[P_QKVB] + lC * 3 : nullptr, part, s));
+                                              C, NH, fused ? pqkv : nullptr, s));
+        if (fused) jobs[nj++] = SumJob{{g + po[P_QKVB] + lC * 3}, pqkv, flash_attention_bias_rows(B, T_), 3 * C};
         // qkv: qkv = ln1 Wqkv^T + b
         RUN("gemm_dx", lin_dx<T>(M, a.dmid, a.dbig, w + po[P_QKVW] + lC * 3 * C, BT, 3 * C, C, EPI_STORE));
         RUN("gemm_dw", lin_dw<T>(M, g + po[P_QKVW] + lC * 3 * C, a.dbig, ln1, BT, 3 * C, C));
-        if (!fused) RUN("colsum", colsum_accum<T>(g + po[P_QKVB] + lC * 3, a.dbig, BT, 3 * C, part, s));
-        // ln1: dres += LN1'(dmid) -> dres is d xin
+        if (!fused) RUN("colsum", colsum_accum<T>(g + po[P_QKVB] + lC * 3, a.dbig, BT, 3 * C, pqkv, s));
+        // ln1: dres += LN1'(dmid) -> dres is d xin, whose column sums are the
+        // fcproj bias gradient of the block below
         RUN("layernorm_bwd", layernorm_bwd<T>(a.dres, a.dmid, xin, p + po[P_LN1W] + lC, a.ln1m + (size_t)l * BT,
-                                              a.ln1r + (size_t)l * BT, g + po[P_LN1W] + lC, g + po[P_LN1B] + lC,
-                                              part, BT, C, false, s));
+                                              a.ln1r + (size_t)l * BT, pln1, BT, C, false, l > 0, s));
+        jobs[nj++] = SumJob{{g + po[P_LN1W] + lC, g + po[P_LN1B] + lC, l > 0 ? g + po[P_FCPROJB] + lC - C : nullptr},
+                            pln1, Gln, C};
+        RUN("bias_sums", sum_partials_batch(jobs, nj, s));
     }
     RUN("encoder_bwd", encoder_bwd<T>(g + po[P_WTE], g + po[P_WPE], a.dres, M->P<int>(M->L.tokens), B, T_, C, s));
     return GPT2_OK;
@@ -805,10 +824,10 @@ int gpt2_test_attention_bwd(gpt2_t* M, void* dqkv, const void* dout, const void*
     float* D = M->P<float>(M->L.attD);
     if (M->bf16mode())
         RUN("attention_test", attn_bwd<bf16>((bf16*)dqkv, (const bf16*)dout, (const bf16*)qkv, (const bf16*)out, lse,
-                                             D, B, T_, C, NH, nullptr, nullptr, M->stream));
+                                             D, B, T_, C, NH, nullptr, M->stream));
     else
         RUN("attention_test", attn_bwd<float>((float*)dqkv, (const float*)dout, (const float*)qkv,
-                                              (const float*)out, lse, D, B, T_, C, NH, nullptr, nullptr, M->stream));
+                                              (const float*)out, lse, D, B, T_, C, NH, nullptr, M->stream));
     return GPT2_OK;
 }
 

@@ -38,16 +38,30 @@ template <typename T> DEVI void st16(T* p, const Vec16<T>& r) {
     *reinterpret_cast<uint4*>(p) = *reinterpret_cast<const uint4*>(&r);
 }
 
-// ---- wavefront reductions (64 lanes) --------------------------------------
+// ---- wavefront reductions (64 lanes, all active) ---------------------------
+// Within each 16-lane row through DPP lane moves (quad_perm [1,0,3,2] and
+// [2,3,0,1], then row_ror 4 and 8), then the four row results, read out of
+// lanes 0, 16, 32 and 48, are combined in a fixed order: the result is the
+// same in every lane and from run to run.
+template <int CTRL> DEVI float dpp_mov(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
+DEVI float lane_value(float x, int l) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
+}
 DEVI float wave_sum(float x) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
-    return x;
+    x += dpp_mov<0xB1>(x);   // lane ^ 1
+    x += dpp_mov<0x4E>(x);   // lane ^ 2: each lane holds its quad's sum
+    x += dpp_mov<0x124>(x);  // + the quad 4 lanes round the row
+    x += dpp_mov<0x128>(x);  // + the other two quads: lane 16r holds row r's sum
+    return (lane_value(x, 0) + lane_value(x, 16)) + (lane_value(x, 32) + lane_value(x, 48));
 }
 DEVI float wave_max(float x) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
-    return x;
+    x = fmaxf(x, dpp_mov<0xB1>(x));
+    x = fmaxf(x, dpp_mov<0x4E>(x));
+    x = fmaxf(x, dpp_mov<0x124>(x));
+    x = fmaxf(x, dpp_mov<0x128>(x));
+    return fmaxf(fmaxf(lane_value(x, 0), lane_value(x, 16)), fmaxf(lane_value(x, 32), lane_value(x, 48)));
 }
 
 // GELU, tanh approximation: 0.5 u (1 + tanh(v/2)) with v = 2k (u + 0.044715 u^3),

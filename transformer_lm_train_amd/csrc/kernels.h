@@ -64,7 +64,7 @@ template <typename T>
 hipError_t layernorm_fwd(T* out, float* mean, float* rstd, const T* x, const float* w, const float* b,
                          int N, int C, hipStream_t s);
 // dres (+)= LN backward of dy.  Per-block partial sums go to partial[NP][G][C]
-// with G = layernorm_bwd_blocks(N) <= 1024: dw, db and, if dsum (NP = 3), the
+// with G = layernorm_bwd_blocks(N) <= 512: dw, db and, if dsum (NP = 3), the
 // column sums of the new dres.  The caller adds them to their outputs with
 // sum_partials_batch ({dw, db, dsum-target}, partial, G, C).
 int layernorm_bwd_blocks(int N);

@@ -86,59 +86,74 @@ hipError_t encoder_bwd(float* dwte, float* dwpe, const T* dx, const int* tokens,
 // LayerNorm forward: mean, biased variance, rstd = 1/sqrt(var + 1e-5);
 // y = (x - mean) * rstd * w + b; mean and rstd saved for the backward
 // (origin-of-llm.c transcript, "Pure C").  One wavefront per row, the row
-// held in registers (up to MAXV 16-byte chunks per lane).
+// held in registers (up to MAXV 16-byte chunks per lane); each wave takes R
+// rows (stride 4 rows apart) and requests all of them before any arithmetic.
 // ============================================================================
 constexpr int LN_MAXV = 8;
 
-template <typename T, int MAXV>
+template <typename T, int MAXV, int R>
 __global__ __launch_bounds__(256) void layernorm_fwd_kernel(T* out, float* mean, float* rstd, const T* x,
                                                             const float* w, const float* b, int N, int C) {
     constexpr int VN = Vec16<T>::N;
-    int lane = threadIdx.x & 63;
-    int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= N) return;
-    int chunks = C / VN;
-    const T* xr = x + (int64_t)row * C;
-    float v[MAXV][VN];
-    float s = 0.f;
+    const int lane = threadIdx.x & 63;
+    const int row0 = blockIdx.x * 4 * R + (threadIdx.x >> 6);
+    const int chunks = C / VN;
+    Vec16<T> q[R][MAXV];
 #pragma unroll
-    for (int i = 0; i < MAXV; i++) {
-        int ch = lane + i * 64;
-        if (ch < chunks) {
-            Vec16<T> q = ld16(xr + ch * VN);
+    for (int r = 0; r < R; r++) {
+        const int row = row0 + 4 * r;
 #pragma unroll
-            for (int j = 0; j < VN; j++) { v[i][j] = to_f32(q.v[j]); s += v[i][j]; }
+        for (int i = 0; i < MAXV; i++) {
+            const int ch = lane + i * 64;
+            if (row < N && ch < chunks) q[r][i] = ld16(x + (int64_t)row * C + ch * VN);
         }
     }
-    float mu = wave_sum(s) / C;
-    float ss = 0.f;
+    float mu[R], rs[R];
 #pragma unroll
-    for (int i = 0; i < MAXV; i++) {
-        int ch = lane + i * 64;
-        if (ch < chunks) {
+    for (int r = 0; r < R; r++) {
+        float s = 0.f;
 #pragma unroll
-            for (int j = 0; j < VN; j++) { float d = v[i][j] - mu; ss += d * d; }
-        }
+        for (int i = 0; i < MAXV; i++)
+            if (lane + i * 64 < chunks)
+#pragma unroll
+                for (int j = 0; j < VN; j++) s += to_f32(q[r][i].v[j]);
+        mu[r] = wave_sum(s) / C;
     }
-    float var = wave_sum(ss) / C;
-    float rs = rsqrtf(var + 1e-5f);
-    T* orow = out + (int64_t)row * C;
 #pragma unroll
-    for (int i = 0; i < MAXV; i++) {
-        int ch = lane + i * 64;
-        if (ch < chunks) {
-            Vec16<T> o;
+    for (int r = 0; r < R; r++) {
+        float ss = 0.f;
 #pragma unroll
-            for (int j = 0; j < VN; j++) {
-                int c = ch * VN + j;
-                o.v[j] = from_f32<T>((v[i][j] - mu) * rs * w[c] + b[c]);
+        for (int i = 0; i < MAXV; i++)
+            if (lane + i * 64 < chunks)
+#pragma unroll
+                for (int j = 0; j < VN; j++) {
+                    const float d = to_f32(q[r][i].v[j]) - mu[r];
+                    ss += d * d;
+                }
+        rs[r] = rsqrtf(wave_sum(ss) / C + 1e-5f);
+    }
+#pragma unroll
+    for (int r = 0; r < R; r++) {
+        const int row = row0 + 4 * r;
+        if (row >= N) break;
+        T* orow = out + (int64_t)row * C;
+#pragma unroll
+        for (int i = 0; i < MAXV; i++) {
+            const int ch = lane + i * 64;
+            if (ch < chunks) {
+                Vec16<T> o;
+#pragma unroll
+                for (int j = 0; j < VN; j++) {
+                    const int c = ch * VN + j;
+                    o.v[j] = from_f32<T>((to_f32(q[r][i].v[j]) - mu[r]) * rs[r] * w[c] + b[c]);
+                }
+                st16(orow + ch * VN, o);
             }
-            st16(orow + ch * VN, o);
         }
-    }
-    if (lane == 0) {
-        mean[row] = mu;
-        rstd[row] = rs;
+        if (lane == 0) {
+            mean[row] = mu[r];
+            rstd[row] = rs[r];
+        }
     }
 }
 
@@ -146,15 +161,14 @@ template <typename T>
 hipError_t layernorm_fwd(T* out, float* mean, float* rstd, const T* x, const float* w, const float* b, int N,
                          int C, hipStream_t s) {
     if (C % Vec16<T>::N || C / Vec16<T>::N > LN_MAXV * 64) return hipErrorInvalidValue;
-    int per_lane = (int)cdiv(C / Vec16<T>::N, 64);
-    if (per_lane <= 1)
-        layernorm_fwd_kernel<T, 1><<<cdiv(N, 4), 256, 0, s>>>(out, mean, rstd, x, w, b, N, C);
-    else if (per_lane <= 2)
-        layernorm_fwd_kernel<T, 2><<<cdiv(N, 4), 256, 0, s>>>(out, mean, rstd, x, w, b, N, C);
-    else if (per_lane <= 4)
-        layernorm_fwd_kernel<T, 4><<<cdiv(N, 4), 256, 0, s>>>(out, mean, rstd, x, w, b, N, C);
-    else
-        layernorm_fwd_kernel<T, 8><<<cdiv(N, 4), 256, 0, s>>>(out, mean, rstd, x, w, b, N, C);
+    const int per_lane = (int)cdiv(C / Vec16<T>::N, 64);
+    // rows per wave: 4 while the row chunks fit 2 per lane, then fewer
+#define LN_FWD(V, R) layernorm_fwd_kernel<T, V, R><<<cdiv(N, 4 * R), 256, 0, s>>>(out, mean, rstd, x, w, b, N, C)
+    if (per_lane <= 1) LN_FWD(1, 4);
+    else if (per_lane <= 2) LN_FWD(2, 4);
+    else if (per_lane <= 4) LN_FWD(4, 2);
+    else LN_FWD(8, 1);
+#undef LN_FWD
     return LAUNCH_CHECK();
 }
 
@@ -164,89 +178,121 @@ hipError_t layernorm_fwd(T* out, float* mean, float* rstd, const T* x, const flo
 //   dw += sum_rows dy*xhat,  db += sum_rows dy,
 // and, with NP = 3, the column sums of the new dres as well: that is the
 // gradient of the bias of the projection whose output joined the residual
-// stream at this point.  Each block handles rows blk*4+wave, stepping by 4*G
-// (the next row's operands are requested before the current row is worked),
+// stream at this point.  Each block handles rows blk*4+wave, stepping by 4*G,
+// R rows at a time (the next R rows' operands are requested before the
+// current ones are worked),
 // keeps its per-channel sums in registers, reduces its 4 waves in LDS and
 // writes one partial row per sum; sum_partials_batch adds the G partials in
 // block order.
 // ============================================================================
-constexpr int LN_BWD_G = 1024;
+constexpr int LN_BWD_G = 512;
 
 int layernorm_bwd_blocks(int N) { return (int)std::min<int64_t>(cdiv(N, 4), LN_BWD_G); }
 
-template <typename T, int MAXV, int NP>
-__global__ __launch_bounds__(256) void layernorm_bwd_kernel(T* dres, const T* dy, const T* x, const float* w,
-                                                            const float* mean, const float* rstd,
-                                                            float* partial, int N, int C, int overwrite) {
+template <typename T, int MAXV, int NP, int R>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void layernorm_bwd_kernel(T* dres, const T* dy, const T* x, const float* w, const float* mean, const float* rstd,
+                          float* partial, int N, int C, int overwrite) {
     constexpr int VN = Vec16<T>::N;
     extern __shared__ float smem[];  // [4][NP][C]
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int chunks = C / VN;
-    const int step = gridDim.x * 4;
+    const int step = gridDim.x * 4;  // a wave's rows: row0, row0 + step, ...
+    const int row0 = blockIdx.x * 4 + wv;
     float acc[NP][MAXV][VN];
+    float wr[MAXV][VN];
 #pragma unroll
-    for (int k = 0; k < NP; k++)
+    for (int i = 0; i < MAXV; i++) {
+        const int ch = lane + i * 64;
 #pragma unroll
-        for (int i = 0; i < MAXV; i++)
+        for (int j = 0; j < VN; j++) {
+            wr[i][j] = ch < chunks ? w[ch * VN + j] : 0.f;
 #pragma unroll
-            for (int j = 0; j < VN; j++) acc[k][i][j] = 0.f;
-    Vec16<T> xv[MAXV], dv[MAXV], ov[MAXV];
-    float mu = 0.f, rs = 0.f;
-    auto load = [&](int r) {
-        const int64_t o = (int64_t)r * C;
+            for (int k = 0; k < NP; k++) acc[k][i][j] = 0.f;
+        }
+    }
+    // operands of the R rows being worked (c) and of the next R (n)
+    Vec16<T> xc[R][MAXV], dc[R][MAXV], oc[R][MAXV], xn[R][MAXV], dn[R][MAXV], on[R][MAXV];
+    float mun[R], rsn[R];
+    auto load = [&](int k0) {
 #pragma unroll
-        for (int i = 0; i < MAXV; i++) {
-            const int ch = lane + i * 64;
-            if (ch < chunks) {
-                xv[i] = ld16(x + o + ch * VN);
-                dv[i] = ld16(dy + o + ch * VN);
-                if (!overwrite) ov[i] = ld16(dres + o + ch * VN);
+        for (int r = 0; r < R; r++) {
+            const int row = row0 + (k0 + r) * step;
+            if (row < N) {
+                const int64_t o = (int64_t)row * C;
+#pragma unroll
+                for (int i = 0; i < MAXV; i++) {
+                    const int ch = lane + i * 64;
+                    if (ch < chunks) {
+                        xn[r][i] = ld16(x + o + ch * VN);
+                        dn[r][i] = ld16(dy + o + ch * VN);
+                        if (!overwrite) on[r][i] = ld16(dres + o + ch * VN);
+                    }
+                }
+                mun[r] = mean[row];
+                rsn[r] = rstd[row];
             }
         }
-        mu = mean[r];
-        rs = rstd[r];
     };
-    int row = blockIdx.x * 4 + wv;
-    if (row < N) load(row);
-    for (; row < N; row += step) {
-        const float rmu = mu, rrs = rs;
-        float xh[MAXV][VN], gg[MAXV][VN];
-        Vec16<T> o[MAXV];
-        float sg = 0.f, sgx = 0.f;
+    load(0);
+    for (int k0 = 0; row0 + k0 * step < N; k0 += R) {
+        float mu[R], rs[R];
 #pragma unroll
-        for (int i = 0; i < MAXV; i++) {
-            const int ch = lane + i * 64;
-            if (ch < chunks) {
-                o[i] = ov[i];
+        for (int r = 0; r < R; r++) {
+            mu[r] = mun[r];
+            rs[r] = rsn[r];
 #pragma unroll
-                for (int j = 0; j < VN; j++) {
-                    const int c = ch * VN + j;
-                    const float d = to_f32(dv[i].v[j]);
-                    xh[i][j] = (to_f32(xv[i].v[j]) - rmu) * rrs;
-                    gg[i][j] = d * w[c];
-                    sg += gg[i][j];
-                    sgx += gg[i][j] * xh[i][j];
-                    acc[0][i][j] += d * xh[i][j];
-                    acc[1][i][j] += d;
+            for (int i = 0; i < MAXV; i++) { xc[r][i] = xn[r][i]; dc[r][i] = dn[r][i]; oc[r][i] = on[r][i]; }
+        }
+        if (row0 + (k0 + R) * step < N) load(k0 + R);
+        float sg[R], sgx[R];
+#pragma unroll
+        for (int r = 0; r < R; r++) {
+            sg[r] = 0.f;
+            sgx[r] = 0.f;
+            if (row0 + (k0 + r) * step >= N) continue;
+#pragma unroll
+            for (int i = 0; i < MAXV; i++) {
+                if (lane + i * 64 < chunks) {
+#pragma unroll
+                    for (int j = 0; j < VN; j++) {
+                        const float d = to_f32(dc[r][i].v[j]);
+                        const float xh = (to_f32(xc[r][i].v[j]) - mu[r]) * rs[r];
+                        const float gg = d * wr[i][j];
+                        sg[r] += gg;
+                        sgx[r] += gg * xh;
+                        acc[0][i][j] += d * xh;
+                        acc[1][i][j] += d;
+                    }
                 }
             }
         }
-        if (row + step < N) load(row + step);
-        sg = wave_sum(sg) / C;
-        sgx = wave_sum(sgx) / C;
-        T* orow = dres + (int64_t)row * C;
 #pragma unroll
-        for (int i = 0; i < MAXV; i++) {
-            const int ch = lane + i * 64;
-            if (ch < chunks) {
+        for (int r = 0; r < R; r++) {
+            sg[r] = wave_sum(sg[r]) / C;
+            sgx[r] = wave_sum(sgx[r]) / C;
+        }
 #pragma unroll
-                for (int j = 0; j < VN; j++) {
-                    const float dx = rrs * (gg[i][j] - sg - xh[i][j] * sgx);
-                    const T r = from_f32<T>(overwrite ? dx : to_f32(o[i].v[j]) + dx);
-                    o[i].v[j] = r;
-                    if constexpr (NP == 3) acc[2][i][j] += to_f32(r);
+        for (int r = 0; r < R; r++) {
+            const int row = row0 + (k0 + r) * step;
+            if (row >= N) continue;
+            T* orow = dres + (int64_t)row * C;
+#pragma unroll
+            for (int i = 0; i < MAXV; i++) {
+                const int ch = lane + i * 64;
+                if (ch < chunks) {
+                    Vec16<T> o;
+#pragma unroll
+                    for (int j = 0; j < VN; j++) {
+                        const float xh = (to_f32(xc[r][i].v[j]) - mu[r]) * rs[r];
+                        const float gg = to_f32(dc[r][i].v[j]) * wr[i][j];
+                        const float dx = rs[r] * (gg - sg[r] - xh * sgx[r]);
+                        const T v = from_f32<T>(overwrite ? dx : to_f32(oc[r][i].v[j]) + dx);
+                        o.v[j] = v;
+                        if constexpr (NP == 3) acc[2][i][j] += to_f32(v);
+                    }
+                    st16(orow + ch * VN, o);
                 }
-                st16(orow + ch * VN, o[i]);
             }
         }
     }
@@ -293,13 +339,26 @@ __global__ __launch_bounds__(1024) void sum_partials_kernel(SumBatch bt) {
     const int cx = threadIdx.x & 15, ry = threadIdx.x >> 4;
     const int c = ((int)blockIdx.x - bt.start[k]) * 16 + cx;
     const int nk = jb.out[2] ? 3 : jb.out[1] ? 2 : 1;  // out[0] is always given
+    // rows ry, ry + 64, ... in that order, U rows' loads issued before their adds
+    constexpr int U = 8;
     float t0 = 0.f, t1 = 0.f, t2 = 0.f;
     if (c < C)
-        for (int g = ry; g < G; g += 64) {  // the nk loads of a row are independent
-            const float* pr = partial + (int64_t)g * C + c;
-            t0 += pr[0];
-            if (nk > 1) t1 += pr[(int64_t)G * C];
-            if (nk > 2) t2 += pr[2 * (int64_t)G * C];
+        for (int g0 = ry; g0 < G; g0 += 64 * U) {
+            float v0[U], v1[U], v2[U];
+#pragma unroll
+            for (int u = 0; u < U; u++) {
+                const int g = g0 + 64 * u;
+                const float* pr = partial + (int64_t)g * C + c;
+                v0[u] = g < G ? pr[0] : 0.f;
+                v1[u] = nk > 1 && g < G ? pr[(int64_t)G * C] : 0.f;
+                v2[u] = nk > 2 && g < G ? pr[2 * (int64_t)G * C] : 0.f;
+            }
+#pragma unroll
+            for (int u = 0; u < U; u++) {
+                t0 += v0[u];
+                t1 += v1[u];
+                t2 += v2[u];
+            }
         }
     red[0][ry][cx] = t0;
     red[1][ry][cx] = t1;
@@ -345,13 +404,13 @@ hipError_t layernorm_bwd(T* dres, const T* dy, const T* x, const float* w, const
     const size_t lds = sizeof(float) * 4 * NP * C;
     const int per_lane = (int)cdiv(C / Vec16<T>::N, 64);
     const int ow = overwrite ? 1 : 0;
-#define LN_BWD(V)                                                                                             \
-    (dsum ? layernorm_bwd_kernel<T, V, 3><<<G, 256, lds, s>>>(dres, dy, x, w, mean, rstd, partial, N, C, ow)  \
-          : layernorm_bwd_kernel<T, V, 2><<<G, 256, lds, s>>>(dres, dy, x, w, mean, rstd, partial, N, C, ow))
-    if (per_lane <= 1) LN_BWD(1);
-    else if (per_lane <= 2) LN_BWD(2);
-    else if (per_lane <= 4) LN_BWD(4);
-    else LN_BWD(8);
+#define LN_BWD(V, R)                                                                                              \
+    (dsum ? layernorm_bwd_kernel<T, V, 3, R><<<G, 256, lds, s>>>(dres, dy, x, w, mean, rstd, partial, N, C, ow)   \
+          : layernorm_bwd_kernel<T, V, 2, R><<<G, 256, lds, s>>>(dres, dy, x, w, mean, rstd, partial, N, C, ow))
+    if (per_lane <= 1) LN_BWD(1, 2);
+    else if (per_lane <= 2) LN_BWD(2, 2);
+    else if (per_lane <= 4) LN_BWD(4, 1);
+    else LN_BWD(8, 1);
 #undef LN_BWD
     return LAUNCH_CHECK();
 }

@@ -140,11 +140,11 @@ Layout make_layout(const gpt2_config& c) {
         // Partial rows of the fixed-order column sums of the backward pass,
         // one region per producer so that a layer's sums can run as one
         // batch at its end: the final LN and the two LNs of a block (3 sums
-        // per channel, up to 1024 rows), the fc bias (the GELU' product's 4
+        // per channel, up to 512 rows), the fc bias (the GELU' product's 4
         // rows per 256 tokens, 4C wide, or the stand-alone column sums' 256
         // rows in fp32 mode) and the qkv bias (attention's row per
         // 128-token block, 3C wide, or the stand-alone column sums).
-        const size_t ln = 3 * 1024 * (size_t)C;
+        const size_t ln = 3 * (size_t)layernorm_bwd_blocks((int)BT) * C;
         const size_t fc = std::max<size_t>(cdiv(BT, 256) * 4, 256) * 4 * C;
         const size_t qk = std::max<size_t>((size_t)c.batch_size * cdiv(c.seq_len, 128), 256) * 3 * C;
         L.part_fin = add(4 * ln);

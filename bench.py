@@ -52,10 +52,10 @@ def class_work(c):
     return {
         "gemm_classifier_fwd": (2 * BT * C * V, "flop", 1),
         "gemm_classifier_dx": (2 * BT * C * V, "flop", 1),
-        "gemm_classifier_dw": (2 * BT * C * V, "flop", 1),
         "gemm_fwd": (lin, "flop", 4 * L),
         "gemm_dx": (lin, "flop", 4 * L),
-        "gemm_dw": (lin, "flop", 4 * L),
+        # every weight gradient, the classifier's included, in one grouped launch
+        "gemm_dw": (lin + 2 * BT * C * V, "flop", 1),
         "attention_fwd": (att, "flop", L),
         "attention_bwd": (2 * att, "flop", L),
         "softmax_ce": (2 * BT * Vp * 2, "byte", 1),

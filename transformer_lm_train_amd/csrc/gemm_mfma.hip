@@ -359,9 +359,13 @@ DEVI void mfma_step(f32x16 (&acc)[FM][FN], bf16x8 (&fa)[FM], bf16x8 (&fb)[FN], c
 // tile when fewer than BN; the B operand is still staged BN rows wide (same
 // load geometry, every wave issues the same loads), the rows past BNV land in
 // LDS that no fragment reads.
+// GROUPED: one launch over the tiles of several problems; tile_list[w]
+// holds (problem << 22 | tile row << 11 | tile column), or ~0 for padding,
+// and group[problem] the problem's arguments.
 template <int BM, int BN, int NW, int WAVES_M, int KB, int NS, bool XPF, bool AK, bool BKC, int EPI, int OCC = 2,
-          int BNV = BN>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void gemm_big_kernel(GemmArgs g, int kchunk) {
+          int BNV = BN, bool GROUPED = false>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void gemm_big_kernel(
+    GemmArgs garg, int kchunk, const GemmArgs* __restrict__ group, const uint32_t* __restrict__ tile_list) {
     constexpr int WAVES_N = NW / WAVES_M;
     constexpr int TM = BM / WAVES_M, TN = BNV / WAVES_N, FM = TM / 32, FN = TN / 32;
     static_assert(BNV <= BN && TN % 32 == 0, "tile width");
@@ -392,24 +396,39 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WAVES_N, wn = wave % WAVES_N;
 
-    const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BNV - 1) / BNV;
     // Workgroup L (linear id, x fastest) runs on XCD L % 8.  Give each XCD a
-    // contiguous range of (split, tile) work in split-major order, so that
-    // the tiles sharing operand panels (same split, neighbouring tiles) share
-    // one L2.
-    const int tiles = gridDim.x;
-    int work = blockIdx.x + blockIdx.y * tiles;
-    const int total = tiles * gridDim.y;
-    if ((total & 7) == 0) work = (work & 7) * (total >> 3) + (work >> 3);
-    const int split = work / tiles;
-    int bid = work % tiles;
-    constexpr int GM = 8;
-    const int group = bid / (GM * tiles_n);
-    const int first_m = group * GM;
-    const int gsz = min(tiles_m - first_m, GM);
-    const int in = bid % (GM * tiles_n);
-    const int m0 = (first_m + in % gsz) * BM;
-    const int n0 = (in / gsz) * BNV;
+    // contiguous range of the work list (split-major (split, tile) pairs, or
+    // the grouped tile list), so that the tiles sharing operand panels (same
+    // split, neighbouring tiles) share one L2.
+    GemmArgs g;
+    int m0, n0, split;
+    if constexpr (GROUPED) {
+        const int total = gridDim.x;  // a multiple of 8
+        const int work = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
+        const uint32_t t = tile_list[work];
+        if (t == ~0u) return;
+        g = group[t >> 22];
+        m0 = (int)((t >> 11) & 0x7FF) * BM;
+        n0 = (int)(t & 0x7FF) * BNV;
+        split = 0;
+        kchunk = g.K;
+    } else {
+        g = garg;
+        const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BNV - 1) / BNV;
+        const int tiles = gridDim.x;
+        int work = blockIdx.x + blockIdx.y * tiles;
+        const int total = tiles * gridDim.y;
+        if ((total & 7) == 0) work = (work & 7) * (total >> 3) + (work >> 3);
+        split = work / tiles;
+        const int bid = work % tiles;
+        constexpr int GM = 8;
+        const int gi = bid / (GM * tiles_n);
+        const int first_m = gi * GM;
+        const int gsz = min(tiles_m - first_m, GM);
+        const int in = bid % (GM * tiles_n);
+        m0 = (first_m + in % gsz) * BM;
+        n0 = (in / gsz) * BNV;
+    }
     const bf16* A = (const bf16*)g.a;
     const bf16* B = (const bf16*)g.b;
 
@@ -514,7 +533,7 @@ template <int BM, int BN, int NW, int WAVES_M, int KB, int NS, bool XPF, bool AK
 hipError_t launch_big(const GemmArgs& g, hipStream_t s, int splits = 1, int kchunk = 0) {
     dim3 grid(cdiv(g.M, BM) * cdiv(g.N, BNV), splits);
     gemm_big_kernel<BM, BN, NW, WAVES_M, KB, NS, XPF, AK, BKC, EPI, OCC, BNV>
-        <<<grid, NW * 64, 0, s>>>(g, kchunk ? kchunk : g.K);
+        <<<grid, NW * 64, 0, s>>>(g, kchunk ? kchunk : g.K, nullptr, nullptr);
     return hipGetLastError();
 }
 
@@ -565,16 +584,60 @@ bool use_192(int M, int N) {
     return 10 * 3 * r192 <= 9 * 4 * r256;
 }
 
-}  // namespace
-
-hipError_t gemm_mfma_bf16(const GemmArgs& g, hipStream_t s) {
+// Shapes and operands the direct-to-LDS kernel takes.
+bool shape_ok(const GemmArgs& g) {
     if (g.M <= 0 || g.N <= 0 || g.K <= 0 || g.K % KALIGN || g.M % 8 || g.N % 8 || g.lda % 8 || g.ldb % 8)
-        return hipErrorInvalidValue;
-    if (!aligned16(g.a) || !aligned16(g.b)) return hipErrorInvalidValue;
+        return false;
+    if (!aligned16(g.a) || !aligned16(g.b)) return false;
     // per-lane operand offsets are 32-bit element counts
     const int64_t amax = g.a_kcontig ? (int64_t)(g.M - 1) * g.lda + g.K : (int64_t)(g.K - 1) * g.lda + g.M;
     const int64_t bmax = g.b_kcontig ? (int64_t)(g.N - 1) * g.ldb + g.K : (int64_t)(g.K - 1) * g.ldb + g.N;
-    if (amax >= (int64_t)1 << 31 || bmax >= (int64_t)1 << 31) return hipErrorInvalidValue;
+    return amax < (int64_t)1 << 31 && bmax < (int64_t)1 << 31;
+}
+
+// The grouped weight-gradient products: 256 x 256 tiles, the whole reduction
+// in each workgroup, out (fp32) += acc.
+#define GROUPED_DW_KERNEL \
+    gemm_big_kernel<256, 256, 8, 2, 32, GEMM_BIG_NS, GEMM_BIG_XPF, false, false, EPI_ACC_F32, 2, 256, true>
+constexpr int GROUP_TILE = 256;
+
+}  // namespace
+
+int gemm_grouped_tiles(const GemmArgs* probs, int n, uint32_t* tiles, int cap) {
+    if (n <= 0 || n > 1024) return -1;
+    int cnt = 0;
+    for (int p = 0; p < n; p++) {
+        const GemmArgs& g = probs[p];
+        if (!shape_ok(g) || g.a_kcontig || g.b_kcontig || g.epi != EPI_ACC_F32 || g.ldo % 4 ||
+            ((uintptr_t)g.out & 15))
+            return -1;
+        const int tm = (int)cdiv(g.M, GROUP_TILE), tn = (int)cdiv(g.N, GROUP_TILE);
+        if (tm > 2047 || tn > 2047) return -1;
+        // row groups of 8 tiles, column by column within a group (as the
+        // single-problem launch orders its tiles)
+        constexpr int GM = 8;
+        for (int bid = 0; bid < tm * tn; bid++) {
+            const int first_m = bid / (GM * tn) * GM, gsz = std::min(tm - first_m, GM), in = bid % (GM * tn);
+            if (tiles && cnt >= cap) return -1;
+            if (tiles) tiles[cnt] = (uint32_t)p << 22 | (uint32_t)(first_m + in % gsz) << 11 | (uint32_t)(in / gsz);
+            cnt++;
+        }
+    }
+    for (; cnt % 8; cnt++) {
+        if (tiles && cnt >= cap) return -1;
+        if (tiles) tiles[cnt] = ~0u;
+    }
+    return cnt;
+}
+
+hipError_t gemm_grouped_bf16(const GemmArgs* d_probs, const uint32_t* d_tiles, int ntiles, hipStream_t s) {
+    if (ntiles <= 0 || ntiles % 8 || !d_probs || !d_tiles) return hipErrorInvalidValue;
+    GROUPED_DW_KERNEL<<<ntiles, 512, 0, s>>>(GemmArgs{}, 0, d_probs, d_tiles);
+    return hipGetLastError();
+}
+
+hipError_t gemm_mfma_bf16(const GemmArgs& g, hipStream_t s) {
+    if (!shape_ok(g)) return hipErrorInvalidValue;
     // Tile choice from timings at the GPT-2 shapes on gfx950: the 256 x 256
     // tile (8 waves of 128 x 64, k-step 32, 4 LDS stages) leads or ties in
     // every forward and backward-data product.

@@ -45,6 +45,15 @@ struct GemmArgs {
 };
 size_t gemm_splitk_ws_bytes(int M, int N, int K);
 int gemm_colsum_rows(int M, int N);
+// Grouped weight-gradient products (bf16): one launch over the 256 x 256
+// tiles of n problems, each mn-contiguous x mn-contiguous with EPI_ACC_F32
+// and its whole reduction in one workgroup.  gemm_grouped_tiles validates the
+// problems and writes their tile list (padded to a multiple of 8; tiles may
+// be NULL to count), returning its length, or -1 when a problem does not fit
+// or cap is too small.  gemm_grouped_bf16 runs the list against the device
+// copies of the problems and the list.
+int gemm_grouped_tiles(const GemmArgs* probs, int n, uint32_t* tiles, int cap);
+hipError_t gemm_grouped_bf16(const GemmArgs* d_probs, const uint32_t* d_tiles, int ntiles, hipStream_t s);
 
 // fp32-accumulating SIMT kernel for any shapes (activation dtype T).
 template <typename T> hipError_t gemm_simt(const GemmArgs& g, hipStream_t s);
@@ -63,14 +72,15 @@ hipError_t encoder_bwd(float* dwte, float* dwpe, const T* dx, const int* tokens,
 template <typename T>
 hipError_t layernorm_fwd(T* out, float* mean, float* rstd, const T* x, const float* w, const float* b,
                          int N, int C, hipStream_t s);
-// dres (+)= LN backward of dy.  Per-block partial sums go to partial[NP][G][C]
-// with G = layernorm_bwd_blocks(N) <= 512: dw, db and, if dsum (NP = 3), the
-// column sums of the new dres.  The caller adds them to their outputs with
+// dout = din + LN backward of dy (din NULL: dout = the LN backward alone;
+// din may equal dout).  Per-block partial sums go to partial[NP][G][C] with
+// G = layernorm_bwd_blocks(N) <= 512: dw, db and, if dsum (NP = 3), the
+// column sums of dout.  The caller adds them to their outputs with
 // sum_partials_batch ({dw, db, dsum-target}, partial, G, C).
 int layernorm_bwd_blocks(int N);
 template <typename T>
-hipError_t layernorm_bwd(T* dres, const T* dy, const T* x, const float* w, const float* mean,
-                         const float* rstd, float* partial, int N, int C, bool overwrite, bool dsum, hipStream_t s);
+hipError_t layernorm_bwd(T* dout, const T* din, const T* dy, const T* x, const float* w, const float* mean,
+                         const float* rstd, float* partial, int N, int C, bool dsum, hipStream_t s);
 // A fixed-order column sum of partial rows: out[k][c] += sum_g partial[k*G + g][c]
 // for each non-null out[k], k < 3 (out[0] required).
 struct SumJob {

@@ -174,16 +174,16 @@ hipError_t layernorm_fwd(T* out, float* mean, float* rstd, const T* x, const flo
 
 // ============================================================================
 // LayerNorm backward.  With xhat = (x-mean)*rstd and g = dy*w:
-//   dx = rstd * (g - mean_c(g) - xhat * mean_c(g*xhat)),  dres (+)= dx;
+//   dx = rstd * (g - mean_c(g) - xhat * mean_c(g*xhat)),  dout = din + dx
+//   (the residual-stream gradient, written out of place),
 //   dw += sum_rows dy*xhat,  db += sum_rows dy,
-// and, with NP = 3, the column sums of the new dres as well: that is the
-// gradient of the bias of the projection whose output joined the residual
-// stream at this point.  Each block handles rows blk*4+wave, stepping by 4*G,
-// R rows at a time (the next R rows' operands are requested before the
-// current ones are worked),
-// keeps its per-channel sums in registers, reduces its 4 waves in LDS and
-// writes one partial row per sum; sum_partials_batch adds the G partials in
-// block order.
+// and, with NP = 3, the column sums of dout as well: that is the gradient of
+// the bias of the projection whose output joined the residual stream at this
+// point.  Each block handles rows blk*4+wave, stepping by 4*G, R rows at a
+// time (the next R rows' operands are requested before the current ones are
+// worked), keeps its per-channel sums in registers, reduces its 4 waves in
+// LDS and writes one partial row per sum; sum_partials_batch adds the G
+// partials in block order.
 // ============================================================================
 constexpr int LN_BWD_G = 512;
 
@@ -191,8 +191,8 @@ int layernorm_bwd_blocks(int N) { return (int)std::min<int64_t>(cdiv(N, 4), LN_B
 
 template <typename T, int MAXV, int NP, int R>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void layernorm_bwd_kernel(T* dres, const T* dy, const T* x, const float* w, const float* mean, const float* rstd,
-                          float* partial, int N, int C, int overwrite) {
+void layernorm_bwd_kernel(T* dout, const T* din, const T* dy, const T* x, const float* w, const float* mean,
+                          const float* rstd, float* partial, int N, int C) {
     constexpr int VN = Vec16<T>::N;
     extern __shared__ float smem[];  // [4][NP][C]
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -226,7 +226,7 @@ void layernorm_bwd_kernel(T* dres, const T* dy, const T* x, const float* w, cons
                     if (ch < chunks) {
                         xn[r][i] = ld16(x + o + ch * VN);
                         dn[r][i] = ld16(dy + o + ch * VN);
-                        if (!overwrite) on[r][i] = ld16(dres + o + ch * VN);
+                        if (din) on[r][i] = ld16(din + o + ch * VN);
                     }
                 }
                 mun[r] = mean[row];
@@ -276,7 +276,7 @@ void layernorm_bwd_kernel(T* dres, const T* dy, const T* x, const float* w, cons
         for (int r = 0; r < R; r++) {
             const int row = row0 + (k0 + r) * step;
             if (row >= N) continue;
-            T* orow = dres + (int64_t)row * C;
+            T* orow = dout + (int64_t)row * C;
 #pragma unroll
             for (int i = 0; i < MAXV; i++) {
                 const int ch = lane + i * 64;
@@ -287,7 +287,7 @@ void layernorm_bwd_kernel(T* dres, const T* dy, const T* x, const float* w, cons
                         const float xh = (to_f32(xc[r][i].v[j]) - mu[r]) * rs[r];
                         const float gg = to_f32(dc[r][i].v[j]) * wr[i][j];
                         const float dx = rs[r] * (gg - sg[r] - xh * sgx[r]);
-                        const T v = from_f32<T>(overwrite ? dx : to_f32(oc[r][i].v[j]) + dx);
+                        const T v = from_f32<T>(din ? to_f32(oc[r][i].v[j]) + dx : dx);
                         o.v[j] = v;
                         if constexpr (NP == 3) acc[2][i][j] += to_f32(v);
                     }
@@ -396,17 +396,16 @@ hipError_t sum_partials(float* out0, float* out1, float* out2, const float* part
 }
 
 template <typename T>
-hipError_t layernorm_bwd(T* dres, const T* dy, const T* x, const float* w, const float* mean, const float* rstd,
-                         float* partial, int N, int C, bool overwrite, bool dsum, hipStream_t s) {
+hipError_t layernorm_bwd(T* dout, const T* din, const T* dy, const T* x, const float* w, const float* mean,
+                         const float* rstd, float* partial, int N, int C, bool dsum, hipStream_t s) {
     if (C % Vec16<T>::N || C / Vec16<T>::N > LN_MAXV * 64 || N <= 0) return hipErrorInvalidValue;
     const int G = layernorm_bwd_blocks(N);
     const int NP = dsum ? 3 : 2;
     const size_t lds = sizeof(float) * 4 * NP * C;
     const int per_lane = (int)cdiv(C / Vec16<T>::N, 64);
-    const int ow = overwrite ? 1 : 0;
-#define LN_BWD(V, R)                                                                                              \
-    (dsum ? layernorm_bwd_kernel<T, V, 3, R><<<G, 256, lds, s>>>(dres, dy, x, w, mean, rstd, partial, N, C, ow)   \
-          : layernorm_bwd_kernel<T, V, 2, R><<<G, 256, lds, s>>>(dres, dy, x, w, mean, rstd, partial, N, C, ow))
+#define LN_BWD(V, R)                                                                                               \
+    (dsum ? layernorm_bwd_kernel<T, V, 3, R><<<G, 256, lds, s>>>(dout, din, dy, x, w, mean, rstd, partial, N, C)  \
+          : layernorm_bwd_kernel<T, V, 2, R><<<G, 256, lds, s>>>(dout, din, dy, x, w, mean, rstd, partial, N, C))
     if (per_lane <= 1) LN_BWD(1, 2);
     else if (per_lane <= 2) LN_BWD(2, 2);
     else if (per_lane <= 4) LN_BWD(4, 1);
@@ -752,8 +751,8 @@ template <typename T> hipError_t widen_f32(float* dst, const T* src, size_t n, h
     template hipError_t encoder_bwd<T>(float*, float*, const T*, const int*, int, int, int, hipStream_t);    \
     template hipError_t layernorm_fwd<T>(T*, float*, float*, const T*, const float*, const float*, int, int, \
                                          hipStream_t);                                                       \
-    template hipError_t layernorm_bwd<T>(T*, const T*, const T*, const float*, const float*, const float*,   \
-                                         float*, int, int, bool, bool, hipStream_t);                         \
+    template hipError_t layernorm_bwd<T>(T*, const T*, const T*, const T*, const float*, const float*,      \
+                                         const float*, float*, int, int, bool, hipStream_t);                 \
     template hipError_t colsum_accum<T>(float*, const T*, int, int, float*, hipStream_t);                    \
     template hipError_t softmax_ce<T>(T*, float*, const int*, int, int, int, float, int*, hipStream_t);      \
     template hipError_t widen_f32<T>(float*, const T*, size_t, hipStream_t);

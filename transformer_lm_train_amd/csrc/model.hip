@@ -67,8 +67,10 @@ struct Layout {
     size_t params, grads, m, v, shadow;
     size_t encoded, ln1, qkv, atty, res2, ln2, fch, fchg, res3, lnf, logits;
     size_t ln1_mean, ln1_rstd, ln2_mean, ln2_rstd, lnf_mean, lnf_rstd, lse, losses;
-    size_t dres, dbig, dmid, attD, part_fin, part_ln2, part_ln1, part_fc, part_qkv, norm_partial, scalars, err, tokens, targets, splitk;
+    size_t gres3, gres2, gfch, gqkv, dmid, attD, part_fin, part_ln2, part_ln1, part_fc, part_qkv, norm_partial,
+        scalars, err, tokens, targets, splitk, dw_probs, dw_tiles;
     size_t splitk_bytes;
+    int dw_n, dw_ntiles;  // weight-gradient products and their grouped tile list
     size_t total;
 };
 
@@ -93,6 +95,8 @@ int validate(const gpt2_config* c) {
     }
     return GPT2_OK;
 }
+
+void dw_problems(const gpt2_config& c, const Layout& L, char* base, GemmArgs* out);
 
 Layout make_layout(const gpt2_config& c) {
     Layout L{};
@@ -132,8 +136,13 @@ Layout make_layout(const gpt2_config& c) {
     L.lnf_rstd = add(4 * BT);
     L.lse = add(4 * Ly * BT * c.num_heads);
     L.losses = add(4 * BT);
-    L.dres = add(A * BT * C);
-    L.dbig = add(A * BT * 4 * C);
+    // Output gradients of every layer, kept until the weight-gradient
+    // products at the end of the backward: d res3 (index l + 1 for block l,
+    // index 0 the gradient of the embedding output), d res2, d fch, d qkv.
+    L.gres3 = add(A * (Ly + 1) * BT * C);
+    L.gres2 = add(A * Ly * BT * C);
+    L.gfch = add(A * Ly * BT * 4 * C);
+    L.gqkv = add(A * Ly * BT * 3 * C);
     L.dmid = add(A * BT * C);
     L.attD = add(2 * 4 * BT * c.num_heads);  // D and the base-2 lse of every attention row
     {
@@ -165,8 +174,49 @@ Layout make_layout(const gpt2_config& c) {
         for (auto& d : dims) L.splitk_bytes = std::max(L.splitk_bytes, gemm_splitk_ws_bytes(d[0], d[1], (int)BT));
     }
     L.splitk = add(L.splitk_bytes);
+    L.dw_n = 4 * c.num_layers + 1;
+    L.dw_probs = add(sizeof(GemmArgs) * L.dw_n);
+    L.dw_ntiles = 0;
+    if (c.precision == GPT2_BF16_MIXED) {
+        // tile count of the grouped launch, from the problems placed at a
+        // stand-in base address with the buffer's alignment
+        std::vector<GemmArgs> pr(L.dw_n);
+        dw_problems(c, L, reinterpret_cast<char*>((uintptr_t)1 << 20), pr.data());
+        L.dw_ntiles = std::max(0, gemm_grouped_tiles(pr.data(), L.dw_n, nullptr, 0));
+    }
+    L.dw_tiles = add(4 * (size_t)L.dw_ntiles);
     L.total = add(0);
     return L;
+}
+
+// The weight-gradient products of one step, dW[N, K] += dY[BT, N]^T X[BT, K]:
+// the tied classifier, then fcproj, fc, attproj and qkv of each block, from
+// the output gradients kept by the backward and the forward's activations.
+void dw_problems(const gpt2_config& c, const Layout& L, char* base, GemmArgs* out) {
+    const size_t A = c.precision == GPT2_BF16_MIXED ? 2 : 4;
+    const size_t C = c.channels, BT = (size_t)c.batch_size * c.seq_len, BTC = BT * C;
+    float* g = reinterpret_cast<float*>(base + L.grads);
+    auto act = [&](size_t off, size_t idx) { return base + off + A * idx; };
+    auto prob = [&](float* dW, const char* dY, const char* X, size_t N, size_t K) {
+        GemmArgs a{};
+        a.M = (int)N; a.N = (int)K; a.K = (int)BT;
+        a.a = dY; a.lda = (int64_t)N; a.a_kcontig = false;
+        a.b = X; a.ldb = (int64_t)K; a.b_kcontig = false;
+        a.out = dW; a.ldo = (int64_t)K; a.epi = EPI_ACC_F32;
+        a.ws = reinterpret_cast<float*>(base + L.splitk);
+        a.ws_bytes = L.splitk_bytes;
+        return a;
+    };
+    int n = 0;
+    out[n++] = prob(g + L.poff[P_WTE], act(L.logits, 0), act(L.lnf, 0), c.padded_vocab_size, C);
+    for (int l = c.num_layers - 1; l >= 0; l--) {
+        const size_t lC = (size_t)l * C;
+        out[n++] = prob(g + L.poff[P_FCPROJW] + lC * 4 * C, act(L.gres3, (l + 1) * BTC), act(L.fchg, l * BTC * 4), C,
+                        4 * C);
+        out[n++] = prob(g + L.poff[P_FCW] + lC * 4 * C, act(L.gfch, l * BTC * 4), act(L.ln2, l * BTC), 4 * C, C);
+        out[n++] = prob(g + L.poff[P_ATTPROJW] + lC * C, act(L.gres2, l * BTC), act(L.atty, l * BTC), C, C);
+        out[n++] = prob(g + L.poff[P_QKVW] + lC * 3 * C, act(L.gqkv, l * BTC * 3), act(L.ln1, l * BTC), 3 * C, C);
+    }
 }
 
 // ---- init: SplitMix64 (Steele, Lea & Flood 2014) + Box-Muller -------------
@@ -235,6 +285,7 @@ struct gpt2_model {
     bool logits_valid = false;
     bool norm_bad = false;
     bool clip_pending = false;  // gpt2_clip_grad_norm ran since the last update
+    std::vector<GemmArgs> dw;   // the weight-gradient products (device copy at L.dw_probs)
     // kernel timing
     std::string t_cls;
     bool t_on = false;
@@ -334,7 +385,7 @@ hipError_t attn_bwd(T* dqkv, const T* dout, const T* qkv, const T* out, const fl
 
 template <typename T> struct Acts {
     // per-layer activation pointers
-    T *encoded, *ln1, *qkv, *atty, *res2, *ln2, *fch, *fchg, *res3, *lnf, *logits, *dres, *dbig, *dmid;
+    T *encoded, *ln1, *qkv, *atty, *res2, *ln2, *fch, *fchg, *res3, *lnf, *logits, *gres3, *gres2, *gfch, *gqkv, *dmid;
     float *ln1m, *ln1r, *ln2m, *ln2r, *lnfm, *lnfr, *lse, *losses;
     size_t BTC;
     Acts(gpt2_t* m) {
@@ -342,7 +393,8 @@ template <typename T> struct Acts {
         encoded = m->P<T>(L.encoded); ln1 = m->P<T>(L.ln1); qkv = m->P<T>(L.qkv); atty = m->P<T>(L.atty);
         res2 = m->P<T>(L.res2); ln2 = m->P<T>(L.ln2); fch = m->P<T>(L.fch); fchg = m->P<T>(L.fchg);
         res3 = m->P<T>(L.res3); lnf = m->P<T>(L.lnf); logits = m->P<T>(L.logits);
-        dres = m->P<T>(L.dres); dbig = m->P<T>(L.dbig); dmid = m->P<T>(L.dmid);
+        gres3 = m->P<T>(L.gres3); gres2 = m->P<T>(L.gres2); gfch = m->P<T>(L.gfch); gqkv = m->P<T>(L.gqkv);
+        dmid = m->P<T>(L.dmid);
         ln1m = m->P<float>(L.ln1_mean); ln1r = m->P<float>(L.ln1_rstd);
         ln2m = m->P<float>(L.ln2_mean); ln2r = m->P<float>(L.ln2_rstd);
         lnfm = m->P<float>(L.lnf_mean); lnfr = m->P<float>(L.lnf_rstd);
@@ -406,6 +458,23 @@ template <typename T> int forward_impl(gpt2_t* M, bool with_targets) {
     return GPT2_OK;
 }
 
+// All weight gradients of the step: in bf16 mode one grouped launch over the
+// tiles of every product (each workgroup takes a whole 256 x 256 tile over
+// all B*T tokens, so no split of the reduction is needed), else one product
+// at a time.
+template <typename T> hipError_t weight_grads(gpt2_t* M) {
+    if constexpr (std::is_same<T, bf16>::value) {
+        if (M->L.dw_ntiles > 0)
+            return gemm_grouped_bf16(M->P<GemmArgs>(M->L.dw_probs), M->P<uint32_t>(M->L.dw_tiles), M->L.dw_ntiles,
+                                     M->stream);
+    }
+    for (const GemmArgs& g : M->dw) {
+        hipError_t e = gemm<T>(M, g);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
 template <typename T> int backward_impl(gpt2_t* M) {
     const gpt2_config& c = M->cfg;
     const int B = c.batch_size, T_ = c.seq_len, C = c.channels, NH = c.num_heads, Ly = c.num_layers;
@@ -424,10 +493,14 @@ template <typename T> int backward_impl(gpt2_t* M) {
     float* pqkv = M->P<float>(M->L.part_qkv);
     float* attD = M->P<float>(M->L.attD);
     const int Gln = layernorm_bwd_blocks(BT);
+    // output gradients kept for the weight-gradient products
+    auto G3 = [&](int l) { return a.gres3 + (size_t)(l + 1) * BTC; };  // d res3 of block l (l = -1: d encoded)
+    auto G2 = [&](int l) { return a.gres2 + (size_t)l * BTC; };        // d res2
+    auto GF = [&](int l) { return a.gfch + (size_t)l * BTC * 4; };     // d fch
+    auto GQ = [&](int l) { return a.gqkv + (size_t)l * BTC * 3; };     // d qkv
 
     // classifier (tied to wte): logits now hold dlogits
     RUN("gemm_classifier_dx", lin_dx<T>(M, a.dmid, a.logits, w + po[P_WTE], BT, Vp, C, EPI_STORE));
-    RUN("gemm_classifier_dw", lin_dw<T>(M, g + po[P_WTE], a.logits, a.lnf, BT, Vp, C));
     const T* xlast = a.res3 + (size_t)(Ly - 1) * BTC;
     // Bias gradients are column sums of the output gradients, taken as
     // partial rows by the kernel that produces each gradient and summed in a
@@ -435,56 +508,51 @@ template <typename T> int backward_impl(gpt2_t* M) {
     // LN backward that writes the residual-stream gradient they see (LN2 of
     // the block, and the final LN or LN1 of the block above); in bf16 mode fc
     // from the GELU' product and qkv from the attention backward (fp32 mode:
-    // a column-sum pass each).
+    // a column-sum pass each).  The weight gradients, which nothing in the
+    // backward reads, are all taken at its end from the kept gradients.
     constexpr bool fused = std::is_same<T, bf16>::value;
-    RUN("layernorm_bwd", layernorm_bwd<T>(a.dres, a.dmid, xlast, p + po[P_LNFW], a.lnfm, a.lnfr, pfin, BT, C, true,
-                                          true, s));
+    RUN("layernorm_bwd", layernorm_bwd<T>(G3(Ly - 1), nullptr, a.dmid, xlast, p + po[P_LNFW], a.lnfm, a.lnfr, pfin,
+                                          BT, C, true, s));
     for (int l = Ly - 1; l >= 0; l--) {
         const T* xin = l == 0 ? a.encoded : a.res3 + (size_t)(l - 1) * BTC;
-        const T* ln1 = a.ln1 + l * BTC;
         const T* qkv = a.qkv + l * BTC * 3;
         const T* atty = a.atty + l * BTC;
         const T* res2 = a.res2 + l * BTC;
-        const T* ln2 = a.ln2 + l * BTC;
         const T* fch = a.fch + l * BTC * 4;
-        const T* fchg = a.fchg + l * BTC * 4;
         const size_t lC = (size_t)l * C;
         SumJob jobs[SUM_JOBS_MAX];
         int nj = 0;
         if (l == Ly - 1) jobs[nj++] = SumJob{{g + po[P_LNFW], g + po[P_LNFB], g + po[P_FCPROJB] + lC}, pfin, Gln, C};
-        // fcproj: res3 = res2 + fchg Wfp^T + b   (dres is d res3)
-        RUN("gemm_dx", lin_dx<T>(M, a.dbig, a.dres, w + po[P_FCPROJW] + lC * 4 * C, BT, C, 4 * C, EPI_GELU_BWD, fch,
+        // fcproj: res3 = res2 + fchg Wfp^T + b  ->  d fch = (d res3 Wfp) * GELU'(fch)
+        RUN("gemm_dx", lin_dx<T>(M, GF(l), G3(l), w + po[P_FCPROJW] + lC * 4 * C, BT, C, 4 * C, EPI_GELU_BWD, fch,
                                  fused ? pfc : nullptr));
         if (fused) jobs[nj++] = SumJob{{g + po[P_FCB] + lC * 4}, pfc, gemm_colsum_rows(BT, 4 * C), 4 * C};
-        RUN("gemm_dw", lin_dw<T>(M, g + po[P_FCPROJW] + lC * 4 * C, a.dres, fchg, BT, C, 4 * C));
-        // fc: fch = ln2 Wfc^T + b   (dbig is d fch)
-        RUN("gemm_dx", lin_dx<T>(M, a.dmid, a.dbig, w + po[P_FCW] + lC * 4 * C, BT, 4 * C, C, EPI_STORE));
-        RUN("gemm_dw", lin_dw<T>(M, g + po[P_FCW] + lC * 4 * C, a.dbig, ln2, BT, 4 * C, C));
-        if (!fused) RUN("colsum", colsum_accum<T>(g + po[P_FCB] + lC * 4, a.dbig, BT, 4 * C, pfc, s));
-        // ln2: dres += LN2'(dmid)  -> dres is d res2
-        RUN("layernorm_bwd", layernorm_bwd<T>(a.dres, a.dmid, res2, p + po[P_LN2W] + lC, a.ln2m + (size_t)l * BT,
-                                              a.ln2r + (size_t)l * BT, pln2, BT, C, false, true, s));
+        // fc: fch = ln2 Wfc^T + b  ->  d ln2
+        RUN("gemm_dx", lin_dx<T>(M, a.dmid, GF(l), w + po[P_FCW] + lC * 4 * C, BT, 4 * C, C, EPI_STORE));
+        if (!fused) RUN("colsum", colsum_accum<T>(g + po[P_FCB] + lC * 4, GF(l), BT, 4 * C, pfc, s));
+        // ln2: d res2 = d res3 + LN2'(d ln2)
+        RUN("layernorm_bwd", layernorm_bwd<T>(G2(l), G3(l), a.dmid, res2, p + po[P_LN2W] + lC, a.ln2m + (size_t)l * BT,
+                                              a.ln2r + (size_t)l * BT, pln2, BT, C, true, s));
         jobs[nj++] = SumJob{{g + po[P_LN2W] + lC, g + po[P_LN2B] + lC, g + po[P_ATTPROJB] + lC}, pln2, Gln, C};
-        // attproj: res2 = xin + atty Wap^T + b
-        RUN("gemm_dx", lin_dx<T>(M, a.dmid, a.dres, w + po[P_ATTPROJW] + lC * C, BT, C, C, EPI_STORE));
-        RUN("gemm_dw", lin_dw<T>(M, g + po[P_ATTPROJW] + lC * C, a.dres, atty, BT, C, C));
-        // attention: dmid (d atty) -> dbig (d qkv)
-        RUN("attention_bwd", attn_bwd<T>(a.dbig, a.dmid, qkv, atty, a.lse + (size_t)l * BT * NH, attD, B, T_,
-                                              C, NH, fused ? pqkv : nullptr, s));
+        // attproj: res2 = xin + atty Wap^T + b  ->  d atty
+        RUN("gemm_dx", lin_dx<T>(M, a.dmid, G2(l), w + po[P_ATTPROJW] + lC * C, BT, C, C, EPI_STORE));
+        // attention: d atty -> d qkv
+        RUN("attention_bwd", attn_bwd<T>(GQ(l), a.dmid, qkv, atty, a.lse + (size_t)l * BT * NH, attD, B, T_, C, NH,
+                                         fused ? pqkv : nullptr, s));
         if (fused) jobs[nj++] = SumJob{{g + po[P_QKVB] + lC * 3}, pqkv, flash_attention_bias_rows(B, T_), 3 * C};
-        // qkv: qkv = ln1 Wqkv^T + b
-        RUN("gemm_dx", lin_dx<T>(M, a.dmid, a.dbig, w + po[P_QKVW] + lC * 3 * C, BT, 3 * C, C, EPI_STORE));
-        RUN("gemm_dw", lin_dw<T>(M, g + po[P_QKVW] + lC * 3 * C, a.dbig, ln1, BT, 3 * C, C));
-        if (!fused) RUN("colsum", colsum_accum<T>(g + po[P_QKVB] + lC * 3, a.dbig, BT, 3 * C, pqkv, s));
-        // ln1: dres += LN1'(dmid) -> dres is d xin, whose column sums are the
-        // fcproj bias gradient of the block below
-        RUN("layernorm_bwd", layernorm_bwd<T>(a.dres, a.dmid, xin, p + po[P_LN1W] + lC, a.ln1m + (size_t)l * BT,
-                                              a.ln1r + (size_t)l * BT, pln1, BT, C, false, l > 0, s));
+        // qkv: qkv = ln1 Wqkv^T + b  ->  d ln1
+        RUN("gemm_dx", lin_dx<T>(M, a.dmid, GQ(l), w + po[P_QKVW] + lC * 3 * C, BT, 3 * C, C, EPI_STORE));
+        if (!fused) RUN("colsum", colsum_accum<T>(g + po[P_QKVB] + lC * 3, GQ(l), BT, 3 * C, pqkv, s));
+        // ln1: d xin = d res2 + LN1'(d ln1), whose column sums are the fcproj
+        // bias gradient of the block below
+        RUN("layernorm_bwd", layernorm_bwd<T>(G3(l - 1), G2(l), a.dmid, xin, p + po[P_LN1W] + lC,
+                                              a.ln1m + (size_t)l * BT, a.ln1r + (size_t)l * BT, pln1, BT, C, l > 0, s));
         jobs[nj++] = SumJob{{g + po[P_LN1W] + lC, g + po[P_LN1B] + lC, l > 0 ? g + po[P_FCPROJB] + lC - C : nullptr},
                             pln1, Gln, C};
         RUN("bias_sums", sum_partials_batch(jobs, nj, s));
     }
-    RUN("encoder_bwd", encoder_bwd<T>(g + po[P_WTE], g + po[P_WPE], a.dres, M->P<int>(M->L.tokens), B, T_, C, s));
+    RUN("gemm_dw", weight_grads<T>(M));
+    RUN("encoder_bwd", encoder_bwd<T>(g + po[P_WTE], g + po[P_WPE], G3(-1), M->P<int>(M->L.tokens), B, T_, C, s));
     return GPT2_OK;
 }
 
@@ -572,6 +640,15 @@ int gpt2_build(const gpt2_config* cfg, uint64_t seed, void* device_buf, size_t b
     if (e == hipSuccess) e = hipMemsetAsync(M->P<int>(L.err), 0, 64, s);
     if (e == hipSuccess) e = hipMemsetAsync(M->P<float>(L.scalars), 0, 64, s);
     if (e == hipSuccess && M->bf16mode()) e = cast_bf16(M->P<bf16>(L.shadow), M->params(), L.N, s);
+    M->dw.resize(L.dw_n);
+    dw_problems(*cfg, L, M->base, M->dw.data());
+    std::vector<uint32_t> tiles(L.dw_ntiles);
+    if (L.dw_ntiles > 0 && gemm_grouped_tiles(M->dw.data(), L.dw_n, tiles.data(), L.dw_ntiles) != L.dw_ntiles)
+        e = hipErrorInvalidValue;
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(M->P<GemmArgs>(L.dw_probs), M->dw.data(), sizeof(GemmArgs) * L.dw_n, hipMemcpyHostToDevice, s);
+    if (e == hipSuccess && L.dw_ntiles > 0)
+        e = hipMemcpyAsync(M->P<uint32_t>(L.dw_tiles), tiles.data(), 4 * (size_t)L.dw_ntiles, hipMemcpyHostToDevice, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     if (e != hipSuccess) {
         gpt2_destroy(M);
@@ -710,10 +787,11 @@ int gpt2_copy_logits(gpt2_t* M, float* dst) {
     if (!M->logits_valid) return fail(GPT2_EPERM, "logits are only kept by a forward without targets");
     size_t n = (size_t)M->cfg.batch_size * M->cfg.seq_len * M->cfg.padded_vocab_size;
     if (M->bf16mode()) {
-        // widen into the dbig/dmid activation-gradient scratch is too small; widen in chunks via dbig
+        // widen in chunks through the d fch region of the kept gradients (its
+        // first block alone holds B*T*4C bf16 = B*T*2C floats)
         const bf16* src = M->P<bf16>(M->L.logits);
-        float* tmp = M->P<float>(M->L.dbig);
-        size_t chunk = (size_t)M->cfg.batch_size * M->cfg.seq_len * M->cfg.channels * 2;  // floats that fit in dbig
+        float* tmp = M->P<float>(M->L.gfch);
+        size_t chunk = (size_t)M->cfg.batch_size * M->cfg.seq_len * M->cfg.channels * 2;
         for (size_t o = 0; o < n; o += chunk) {
             size_t k = n - o < chunk ? n - o : chunk;
             HIPCHK(widen_f32<bf16>(tmp, src + o, k, M->stream));

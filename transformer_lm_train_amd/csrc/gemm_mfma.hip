@@ -7,11 +7,13 @@
 // transposing LDS reads), NS stages deep; 32x32x16 bf16 MFMAs with fp32
 // accumulators; a fused epilogue (bias, residual, GELU and its derivative,
 // fp32 gradient accumulation) that leaves through LDS so that global
-// accesses are whole row segments.  Weight gradients, whose outputs are
-// small next to their reduction over all tokens, split the reduction over
-// workgroups and add the partial tiles in a fixed order (deterministic).
-// Block ids are remapped so that the tiles one XCD (one L2) runs are
-// neighbours sharing operand panels.
+// accesses are whole row segments.  The weight gradients of a training step,
+// whose outputs are small next to their reduction over all tokens, run as
+// one grouped launch over the tiles of every product, each tile over the
+// whole reduction; a single weight-gradient product may instead split the
+// reduction over workgroups and add the partial tiles in a fixed order
+// (deterministic).  Block ids are remapped so that the tiles one XCD (one
+// L2) runs are neighbours sharing operand panels.
 #include <algorithm>
 #include <type_traits>
 
@@ -21,13 +23,20 @@ namespace {
 
 constexpr int KALIGN = 64;  // K, and every split-K chunk, is a multiple of this
 
-// LDS stages and schedule of the two tile shapes in use (256x256 for the
-// forward and backward-data products, 128x128 for split weight gradients).
+// LDS stages and schedule of the tile shapes in use (256x256 for the forward
+// and backward-data products and the grouped weight gradients, 128x128 for
+// split weight gradients).
 #ifndef GEMM_BIG_NS
 #define GEMM_BIG_NS 4
 #endif
 #ifndef GEMM_BIG_XPF
 #define GEMM_BIG_XPF false
+#endif
+#ifndef GEMM_GROUP_NS
+#define GEMM_GROUP_NS 4
+#endif
+#ifndef GEMM_GROUP_XPF
+#define GEMM_GROUP_XPF false
 #endif
 #ifndef GEMM_SPLIT_NS
 #define GEMM_SPLIT_NS 5
@@ -598,7 +607,7 @@ bool shape_ok(const GemmArgs& g) {
 // The grouped weight-gradient products: 256 x 256 tiles, the whole reduction
 // in each workgroup, out (fp32) += acc.
 #define GROUPED_DW_KERNEL \
-    gemm_big_kernel<256, 256, 8, 2, 32, GEMM_BIG_NS, GEMM_BIG_XPF, false, false, EPI_ACC_F32, 2, 256, true>
+    gemm_big_kernel<256, 256, 8, 2, 32, GEMM_GROUP_NS, GEMM_GROUP_XPF, false, false, EPI_ACC_F32, 2, 256, true>
 constexpr int GROUP_TILE = 256;
 
 }  // namespace

@@ -116,7 +116,11 @@ int gpt2_forward_device(gpt2_t* m, const int32_t* d_tokens, const int32_t* d_tar
 int gpt2_read_loss(gpt2_t* m, float* mean_loss);
 
 /* Parameter gradients <- 0.  (Activation gradients are overwritten by every
- * backward, never accumulated.) */
+ * backward, never accumulated.)  In BF16_MIXED mode the clear is deferred:
+ * the next gpt2_backward stores into every gradient element instead of
+ * adding, and a gradient reader that comes first (clip, AdamW, copy,
+ * gpt2_device_grads) queues the clear before it reads.  Either way every
+ * later observer sees zeros plus what backward added. */
 int gpt2_zero_grad(gpt2_t* m);
 
 /* Backward pass of the last forward-with-targets: the forward's layers in
@@ -173,7 +177,9 @@ int gpt2_copy_losses(gpt2_t* m, float* host_dst);
 int gpt2_set_params(gpt2_t* m, const float* host_src);
 
 /* Device pointer of the planned buffer region holding the fp32 master
- * parameters, gradients and the bf16 weight shadow (NULL in FP32 mode). */
+ * parameters, gradients and the bf16 weight shadow (NULL in FP32 mode).
+ * gpt2_device_grads first queues a deferred gpt2_zero_grad clear, if one is
+ * pending, on the model's stream. */
 void* gpt2_device_params(gpt2_t* m);
 void* gpt2_device_grads(gpt2_t* m);
 void* gpt2_device_shadow(gpt2_t* m);

@@ -284,3 +284,42 @@ def test_determinism_fp32_and_bf16():
                 assert rel_l2(g0[name], g1[name].astype(np.float64)) < 1e-6
             else:
                 assert np.array_equal(g0[name], g1[name]), name
+
+
+def test_zero_grad_deferred_store_and_accumulation():
+    """gpt2_zero_grad in bf16 mode defers the clear: a gradient read before
+    the next backward sees zeros; that backward stores every gradient element
+    (bitwise what it would add to an explicit clear, apart from the token
+    embedding rows, which take fp32 atomic adds in any order); the next
+    backward adds on top; wpe rows at and past T stay zero."""
+    d = dict(L=2, C=128, NH=2, maxT=128, V=1000, Vp=1024)
+    B, T = 2, 64
+    print(f"deferred zero_grad B={B} T={T} maxT={d['maxT']}", flush=True)
+    m = G.Model(gcfg(d, B, T, G.GPT2_BF16_MIXED), 7, device="cuda:0")
+    x, y = synth.batch(5, 0, B, T, d["V"], "uniform")
+    m.forward(x, y)
+    m.backward()                       # gradients now non-zero
+    assert np.any(m.grads() != 0)
+    m.zero_grad()
+    assert not np.any(m.grads())       # a read before the backward clears first
+    m.forward(x, y)
+    m.backward()                       # explicit clear above, so this one adds onto zeros
+    g_add = m.grads()
+    m.zero_grad()
+    m.forward(x, y)
+    m.backward()                       # deferred clear: this one stores
+    g_store = m.grads()
+    m.forward(x, y)
+    m.backward()                       # and this one accumulates
+    g_two = m.grads()
+    m.close()
+    ga, gs, g2 = split(g_add, d), split(g_store, d), split(g_two, d)
+    for name in O.PARAM_NAMES:
+        if name == "wte":
+            np.testing.assert_allclose(gs[name], ga[name], rtol=1e-5, atol=1e-7)
+            np.testing.assert_allclose(g2[name], 2 * gs[name], rtol=1e-5, atol=1e-7)
+        else:
+            assert np.array_equal(gs[name], ga[name]), name
+            assert np.array_equal(g2[name], 2 * gs[name]), name
+    assert np.any(gs["wpe"][:T * d["C"]] != 0)
+    assert not np.any(gs["wpe"][T * d["C"]:]) and not np.any(g2["wpe"][T * d["C"]:])

@@ -114,9 +114,10 @@ DEVI void epilogue_rows(const GemmArgs& g, const f32x16 (&acc)[FM][FN], float* r
                 if constexpr (EPI == EPI_GELU_BWD)
                     r16[cg][rr] = ok ? *reinterpret_cast<const bf16x8_t*>((const bf16*)g.aux + o) : bf16x8_t{};
                 if constexpr (EPI == EPI_ACC_F32) {
-                    r32[cg][rr][0] = ok ? *reinterpret_cast<const float4*>((const float*)g.out + o)
+                    const bool rd = ok && !g.acc_overwrite;
+                    r32[cg][rr][0] = rd ? *reinterpret_cast<const float4*>((const float*)g.out + o)
                                         : make_float4(0.f, 0.f, 0.f, 0.f);
-                    r32[cg][rr][1] = ok ? *reinterpret_cast<const float4*>((const float*)g.out + o + 4)
+                    r32[cg][rr][1] = rd ? *reinterpret_cast<const float4*>((const float*)g.out + o + 4)
                                         : make_float4(0.f, 0.f, 0.f, 0.f);
                 }
             }
@@ -370,11 +371,13 @@ DEVI void mfma_step(f32x16 (&acc)[FM][FN], bf16x8 (&fa)[FM], bf16x8 (&fb)[FN], c
 // LDS that no fragment reads.
 // GROUPED: one launch over the tiles of several problems; tile_list[w]
 // holds (problem << 22 | tile row << 11 | tile column), or ~0 for padding,
-// and group[problem] the problem's arguments.
+// group[problem] the problem's arguments, and overwrite sets their
+// acc_overwrite.
 template <int BM, int BN, int NW, int WAVES_M, int KB, int NS, bool XPF, bool AK, bool BKC, int EPI, int OCC = 2,
           int BNV = BN, bool GROUPED = false>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void gemm_big_kernel(
-    GemmArgs garg, int kchunk, const GemmArgs* __restrict__ group, const uint32_t* __restrict__ tile_list) {
+    GemmArgs garg, int kchunk, const GemmArgs* __restrict__ group, const uint32_t* __restrict__ tile_list,
+    int overwrite) {
     constexpr int WAVES_N = NW / WAVES_M;
     constexpr int TM = BM / WAVES_M, TN = BNV / WAVES_N, FM = TM / 32, FN = TN / 32;
     static_assert(BNV <= BN && TN % 32 == 0, "tile width");
@@ -417,6 +420,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
         const uint32_t t = tile_list[work];
         if (t == ~0u) return;
         g = group[t >> 22];
+        g.acc_overwrite = overwrite != 0;
         m0 = (int)((t >> 11) & 0x7FF) * BM;
         n0 = (int)(t & 0x7FF) * BNV;
         split = 0;
@@ -542,7 +546,7 @@ template <int BM, int BN, int NW, int WAVES_M, int KB, int NS, bool XPF, bool AK
 hipError_t launch_big(const GemmArgs& g, hipStream_t s, int splits = 1, int kchunk = 0) {
     dim3 grid(cdiv(g.M, BM) * cdiv(g.N, BNV), splits);
     gemm_big_kernel<BM, BN, NW, WAVES_M, KB, NS, XPF, AK, BKC, EPI, OCC, BNV>
-        <<<grid, NW * 64, 0, s>>>(g, kchunk ? kchunk : g.K, nullptr, nullptr);
+        <<<grid, NW * 64, 0, s>>>(g, kchunk ? kchunk : g.K, nullptr, nullptr, 0);
     return hipGetLastError();
 }
 
@@ -564,7 +568,7 @@ void splitk_plan(int M, int N, int K, int tm, int tn, int* splits, int* kchunk) 
     *splits = (K + kc - 1) / kc;
 }
 
-__global__ void splitk_reduce_kernel(float* out, int64_t ldo, const float* ws, int S, int M, int N) {
+__global__ void splitk_reduce_kernel(float* out, int64_t ldo, const float* ws, int S, int M, int N, int overwrite) {
     const int64_t n4 = (int64_t)M * N / 4;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x) {
         int64_t e = i * 4;
@@ -575,9 +579,11 @@ __global__ void splitk_reduce_kernel(float* out, int64_t ldo, const float* ws, i
             acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
         }
         float4* o = reinterpret_cast<float4*>(out + (int64_t)m * ldo + n);
-        float4 cur = *o;
-        cur.x += acc.x; cur.y += acc.y; cur.z += acc.z; cur.w += acc.w;
-        *o = cur;
+        if (!overwrite) {
+            const float4 cur = *o;
+            acc.x += cur.x; acc.y += cur.y; acc.z += cur.z; acc.w += cur.w;
+        }
+        *o = acc;
     }
 }
 
@@ -639,9 +645,10 @@ int gemm_grouped_tiles(const GemmArgs* probs, int n, uint32_t* tiles, int cap) {
     return cnt;
 }
 
-hipError_t gemm_grouped_bf16(const GemmArgs* d_probs, const uint32_t* d_tiles, int ntiles, hipStream_t s) {
+hipError_t gemm_grouped_bf16(const GemmArgs* d_probs, const uint32_t* d_tiles, int ntiles, bool overwrite,
+                             hipStream_t s) {
     if (ntiles <= 0 || ntiles % 8 || !d_probs || !d_tiles) return hipErrorInvalidValue;
-    GROUPED_DW_KERNEL<<<ntiles, 512, 0, s>>>(GemmArgs{}, 0, d_probs, d_tiles);
+    GROUPED_DW_KERNEL<<<ntiles, 512, 0, s>>>(GemmArgs{}, 0, d_probs, d_tiles, overwrite ? 1 : 0);
     return hipGetLastError();
 }
 
@@ -685,7 +692,7 @@ hipError_t gemm_mfma_bf16(const GemmArgs& g, hipStream_t s) {
             if (e != hipSuccess) return e;
             int64_t n4 = (int64_t)g.M * g.N / 4;
             unsigned blocks = (unsigned)std::min<int64_t>((n4 + 255) / 256, 4096);
-            splitk_reduce_kernel<<<blocks, 256, 0, s>>>((float*)g.out, g.ldo, g.ws, S, g.M, g.N);
+            splitk_reduce_kernel<<<blocks, 256, 0, s>>>((float*)g.out, g.ldo, g.ws, S, g.M, g.N, g.acc_overwrite);
             return hipGetLastError();
         }
         return launch_big<128, 128, 4, 2, 32, GEMM_SPLIT_NS, GEMM_SPLIT_XPF, false, false, EPI_ACC_F32>(g, s);

@@ -37,6 +37,7 @@ struct GemmArgs {
     int epi;
     float* ws;           // split-K workspace (EPI_ACC_F32), may be NULL
     size_t ws_bytes;
+    bool acc_overwrite;  // EPI_ACC_F32: out = acc (out's old contents are not read)
     // EPI_GELU_BWD, bf16 MFMA path: partial column sums of out (the bias
     // gradient of the layer whose output gradient this product produces),
     // one row per wave row block: colsum_ws [gemm_colsum_rows(M, N)][N].
@@ -51,9 +52,11 @@ int gemm_colsum_rows(int M, int N);
 // problems and writes their tile list (padded to a multiple of 8; tiles may
 // be NULL to count), returning its length, or -1 when a problem does not fit
 // or cap is too small.  gemm_grouped_bf16 runs the list against the device
-// copies of the problems and the list.
+// copies of the problems and the list; overwrite: out = acc for every
+// problem (instead of out += acc).
 int gemm_grouped_tiles(const GemmArgs* probs, int n, uint32_t* tiles, int cap);
-hipError_t gemm_grouped_bf16(const GemmArgs* d_probs, const uint32_t* d_tiles, int ntiles, hipStream_t s);
+hipError_t gemm_grouped_bf16(const GemmArgs* d_probs, const uint32_t* d_tiles, int ntiles, bool overwrite,
+                             hipStream_t s);
 
 // fp32-accumulating SIMT kernel for any shapes (activation dtype T).
 template <typename T> hipError_t gemm_simt(const GemmArgs& g, hipStream_t s);
@@ -67,8 +70,8 @@ template <typename T>
 hipError_t encoder_fwd(T* out, int* tokens, const float* wte, const float* wpe, int B, int T_,
                        int C, int V, int* err_flag, hipStream_t s);
 template <typename T>
-hipError_t encoder_bwd(float* dwte, float* dwpe, const T* dx, const int* tokens, int B, int T_, int C,
-                       hipStream_t s);
+hipError_t encoder_bwd(float* dwte, float* dwpe, const T* dx, const int* tokens, int B, int T_, int maxT, int C,
+                       bool overwrite, hipStream_t s);
 template <typename T>
 hipError_t layernorm_fwd(T* out, float* mean, float* rstd, const T* x, const float* w, const float* b,
                          int N, int C, hipStream_t s);
@@ -89,8 +92,8 @@ struct SumJob {
     int G, C;
 };
 constexpr int SUM_JOBS_MAX = 6;
-// Runs up to SUM_JOBS_MAX jobs in one launch.
-hipError_t sum_partials_batch(const SumJob* jobs, int n, hipStream_t s);
+// Runs up to SUM_JOBS_MAX jobs in one launch; overwrite: out[k][c] = the sum.
+hipError_t sum_partials_batch(const SumJob* jobs, int n, bool overwrite, hipStream_t s);
 hipError_t sum_partials(float* out0, float* out1, float* out2, const float* partial, int G, int C, hipStream_t s);
 // dbias[n] += sum_m dy[m][n] (deterministic two-stage sum via partial).
 template <typename T>

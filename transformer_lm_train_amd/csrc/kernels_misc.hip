@@ -63,22 +63,26 @@ __global__ void encoder_bwd_wte_kernel(float* dwte, const T* dx, const int* toke
     int row = (int)(i / C), c = (int)(i % C);
     atomicAdd(dwte + (int64_t)tokens[row] * C + c, to_f32(dx[i]));
 }
+// dwpe[t][c] (+)= sum_b dx[b][t][c] over all maxT positions (0 for t >= T_,
+// so that overwrite also clears the positions the batch does not reach).
 template <typename T>
-__global__ void encoder_bwd_wpe_kernel(float* dwpe, const T* dx, int B, int T_, int C) {
+__global__ void encoder_bwd_wpe_kernel(float* dwpe, const T* dx, int B, int T_, int maxT, int C, int overwrite) {
     int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= (int64_t)T_ * C) return;
+    if (i >= (int64_t)maxT * C) return;
     int t = (int)(i / C), c = (int)(i % C);
     float acc = 0.f;
-    for (int b = 0; b < B; b++) acc += to_f32(dx[((int64_t)b * T_ + t) * C + c]);
-    dwpe[i] += acc;
+    if (t < T_)
+        for (int b = 0; b < B; b++) acc += to_f32(dx[((int64_t)b * T_ + t) * C + c]);
+    dwpe[i] = overwrite ? acc : dwpe[i] + acc;
 }
 
 template <typename T>
-hipError_t encoder_bwd(float* dwte, float* dwpe, const T* dx, const int* tokens, int B, int T_, int C,
-                       hipStream_t s) {
+hipError_t encoder_bwd(float* dwte, float* dwpe, const T* dx, const int* tokens, int B, int T_, int maxT, int C,
+                       bool overwrite, hipStream_t s) {
+    if (T_ > maxT) return hipErrorInvalidValue;
     int64_t n = (int64_t)B * T_ * C;
     encoder_bwd_wte_kernel<T><<<cdiv(n, 256), 256, 0, s>>>(dwte, dx, tokens, C, B * T_);
-    encoder_bwd_wpe_kernel<T><<<cdiv((int64_t)T_ * C, 256), 256, 0, s>>>(dwpe, dx, B, T_, C);
+    encoder_bwd_wpe_kernel<T><<<cdiv((int64_t)maxT * C, 256), 256, 0, s>>>(dwpe, dx, B, T_, maxT, C, overwrite);
     return LAUNCH_CHECK();
 }
 
@@ -327,6 +331,7 @@ struct SumBatch {
     SumJob job[SUM_JOBS_MAX];
     int start[SUM_JOBS_MAX + 1];  // first block of each job
     int n;
+    int overwrite;  // out = sum instead of out += sum
 };
 
 __global__ __launch_bounds__(1024) void sum_partials_kernel(SumBatch bt) {
@@ -370,16 +375,17 @@ __global__ __launch_bounds__(1024) void sum_partials_kernel(SumBatch bt) {
         if (c < C && out) {
             float t = 0.f;
             for (int i = 0; i < 64; i++) t += red[q][i][cx];
-            out[c] += t;
+            out[c] = bt.overwrite ? t : out[c] + t;
         }
     }
 }
 
-hipError_t sum_partials_batch(const SumJob* jobs, int n, hipStream_t s) {
+hipError_t sum_partials_batch(const SumJob* jobs, int n, bool overwrite, hipStream_t s) {
     if (n < 0 || n > SUM_JOBS_MAX) return hipErrorInvalidValue;
     if (n == 0) return hipSuccess;
     SumBatch bt{};
     bt.n = n;
+    bt.overwrite = overwrite ? 1 : 0;
     bt.start[0] = 0;
     for (int i = 0; i < n; i++) {
         if (!jobs[i].out[0] || !jobs[i].partial || jobs[i].G <= 0 || jobs[i].C <= 0) return hipErrorInvalidValue;
@@ -392,7 +398,7 @@ hipError_t sum_partials_batch(const SumJob* jobs, int n, hipStream_t s) {
 
 hipError_t sum_partials(float* out0, float* out1, float* out2, const float* partial, int G, int C, hipStream_t s) {
     const SumJob j{{out0, out1, out2}, partial, G, C};
-    return sum_partials_batch(&j, 1, s);
+    return sum_partials_batch(&j, 1, false, s);
 }
 
 template <typename T>
@@ -595,21 +601,35 @@ hipError_t softmax_ce(T* logits, float* losses, const int* targets, int BT, int 
 }
 
 // mean of n losses, summed in a fixed order in double by one block
-__global__ __launch_bounds__(256) void loss_mean_kernel(float* out, const float* losses, int n) {
-    __shared__ double red[256];
+// Fixed-order fp64 sum of x[0 .. n) by one block of 1024 threads: thread t
+// adds x[t], x[t + 1024], ... (its loads issued 4 at a time, independent of
+// one another), then a pairwise tree over the 1024 thread sums.
+DEVI double block_sum_f64(const float* x, int n, double* red) {
     double s = 0.0;
-    for (int i = threadIdx.x; i < n; i += 256) s += losses[i];
+    for (int i0 = threadIdx.x; i0 < n; i0 += 4 * 1024) {
+        float v[4];
+#pragma unroll
+        for (int u = 0; u < 4; u++) v[u] = i0 + u * 1024 < n ? x[i0 + u * 1024] : 0.f;
+#pragma unroll
+        for (int u = 0; u < 4; u++) s += v[u];
+    }
     red[threadIdx.x] = s;
     __syncthreads();
-    for (int o = 128; o >= 1; o >>= 1) {
-        if (threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+    for (int o = 512; o >= 1; o >>= 1) {
+        if ((int)threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
         __syncthreads();
     }
-    if (threadIdx.x == 0) out[0] = (float)(red[0] / n);
+    return red[0];
+}
+
+__global__ __launch_bounds__(1024) void loss_mean_kernel(float* out, const float* losses, int n) {
+    __shared__ double red[1024];
+    const double s = block_sum_f64(losses, n, red);
+    if (threadIdx.x == 0) out[0] = (float)(s / n);
 }
 
 hipError_t loss_mean(float* out, const float* losses, int n, hipStream_t s) {
-    loss_mean_kernel<<<1, 256, 0, s>>>(out, losses, n);
+    loss_mean_kernel<<<1, 1024, 0, s>>>(out, losses, n);
     return LAUNCH_CHECK();
 }
 
@@ -637,18 +657,20 @@ __global__ __launch_bounds__(256) void sumsq_kernel(float* partial, const float*
     if (threadIdx.x == 0) partial[blockIdx.x] = red[0] + red[1] + red[2] + red[3];
 }
 
-__global__ void norm_final_kernel(float* norm_scale, const float* partial, int G, float max_norm) {
-    if (threadIdx.x != 0) return;
-    double s = 0.0;
-    for (int i = 0; i < G; i++) s += partial[i];
-    float n = (float)sqrt(s);
-    norm_scale[0] = n;
-    norm_scale[1] = (max_norm > 0.f && n > max_norm) ? max_norm / n : 1.f;
+__global__ __launch_bounds__(1024) void norm_final_kernel(float* norm_scale, const float* partial, int G,
+                                                          float max_norm) {
+    __shared__ double red[1024];
+    const double s = block_sum_f64(partial, G, red);
+    if (threadIdx.x == 0) {
+        const float n = (float)sqrt(s);
+        norm_scale[0] = n;
+        norm_scale[1] = (max_norm > 0.f && n > max_norm) ? max_norm / n : 1.f;
+    }
 }
 
 hipError_t grad_norm(float* partial, float* norm_scale, const float* g, size_t n, float max_norm, hipStream_t s) {
     sumsq_kernel<<<NORM_G, 256, 0, s>>>(partial, g, n);
-    norm_final_kernel<<<1, 64, 0, s>>>(norm_scale, partial, NORM_G, max_norm);
+    norm_final_kernel<<<1, 1024, 0, s>>>(norm_scale, partial, NORM_G, max_norm);
     return LAUNCH_CHECK();
 }
 
@@ -748,7 +770,8 @@ template <typename T> hipError_t widen_f32(float* dst, const T* src, size_t n, h
 #define INST(T)                                                                                              \
     template hipError_t encoder_fwd<T>(T*, int*, const float*, const float*, int, int, int, int, int*,       \
                                        hipStream_t);                                                         \
-    template hipError_t encoder_bwd<T>(float*, float*, const T*, const int*, int, int, int, hipStream_t);    \
+    template hipError_t encoder_bwd<T>(float*, float*, const T*, const int*, int, int, int, int, bool,        \
+                                        hipStream_t);                                                        \
     template hipError_t layernorm_fwd<T>(T*, float*, float*, const T*, const float*, const float*, int, int, \
                                          hipStream_t);                                                       \
     template hipError_t layernorm_bwd<T>(T*, const T*, const T*, const T*, const float*, const float*,      \

@@ -286,6 +286,11 @@ struct gpt2_model {
     bool norm_bad = false;
     bool clip_pending = false;  // gpt2_clip_grad_norm ran since the last update
     std::vector<GemmArgs> dw;   // the weight-gradient products (device copy at L.dw_probs)
+    // bf16 mode: gpt2_zero_grad only sets this; the next backward then
+    // writes every gradient element instead of adding to it (each element
+    // has exactly one first writer), and any earlier reader of the gradient
+    // gets it cleared first (materialize_zero_grad).
+    bool grads_zero = false;
     // kernel timing
     std::string t_cls;
     bool t_on = false;
@@ -462,13 +467,14 @@ template <typename T> int forward_impl(gpt2_t* M, bool with_targets) {
 // tiles of every product (each workgroup takes a whole 256 x 256 tile over
 // all B*T tokens, so no split of the reduction is needed), else one product
 // at a time.
-template <typename T> hipError_t weight_grads(gpt2_t* M) {
+template <typename T> hipError_t weight_grads(gpt2_t* M, bool overwrite) {
     if constexpr (std::is_same<T, bf16>::value) {
         if (M->L.dw_ntiles > 0)
             return gemm_grouped_bf16(M->P<GemmArgs>(M->L.dw_probs), M->P<uint32_t>(M->L.dw_tiles), M->L.dw_ntiles,
-                                     M->stream);
+                                     overwrite, M->stream);
     }
-    for (const GemmArgs& g : M->dw) {
+    for (GemmArgs g : M->dw) {
+        g.acc_overwrite = overwrite;
         hipError_t e = gemm<T>(M, g);
         if (e != hipSuccess) return e;
     }
@@ -511,6 +517,8 @@ template <typename T> int backward_impl(gpt2_t* M) {
     // a column-sum pass each).  The weight gradients, which nothing in the
     // backward reads, are all taken at its end from the kept gradients.
     constexpr bool fused = std::is_same<T, bf16>::value;
+    // first backward since gpt2_zero_grad: every gradient's one first writer stores
+    const bool ow = M->grads_zero;
     RUN("layernorm_bwd", layernorm_bwd<T>(G3(Ly - 1), nullptr, a.dmid, xlast, p + po[P_LNFW], a.lnfm, a.lnfr, pfin,
                                           BT, C, true, s));
     for (int l = Ly - 1; l >= 0; l--) {
@@ -549,10 +557,12 @@ template <typename T> int backward_impl(gpt2_t* M) {
                                               a.ln1m + (size_t)l * BT, a.ln1r + (size_t)l * BT, pln1, BT, C, l > 0, s));
         jobs[nj++] = SumJob{{g + po[P_LN1W] + lC, g + po[P_LN1B] + lC, l > 0 ? g + po[P_FCPROJB] + lC - C : nullptr},
                             pln1, Gln, C};
-        RUN("bias_sums", sum_partials_batch(jobs, nj, s));
+        RUN("bias_sums", sum_partials_batch(jobs, nj, ow, s));
     }
-    RUN("gemm_dw", weight_grads<T>(M));
-    RUN("encoder_bwd", encoder_bwd<T>(g + po[P_WTE], g + po[P_WPE], G3(-1), M->P<int>(M->L.tokens), B, T_, C, s));
+    RUN("gemm_dw", weight_grads<T>(M, ow));  // the classifier's product writes every wte row first
+    RUN("encoder_bwd", encoder_bwd<T>(g + po[P_WTE], g + po[P_WPE], G3(-1), M->P<int>(M->L.tokens), B, T_,
+                                      c.max_seq_len, C, ow, s));
+    M->grads_zero = false;
     return GPT2_OK;
 }
 
@@ -587,6 +597,16 @@ int forward_common(gpt2_t* M, bool with_targets, float* mean_loss) {
             return rc;
         }
         *mean_loss = M->h_scalars[0];
+    }
+    return GPT2_OK;
+}
+
+// The deferred clear of gpt2_zero_grad, for a reader that comes before the
+// next backward.
+int materialize_zero_grad(gpt2_t* M) {
+    if (M->grads_zero) {
+        HIPCHK(hipMemsetAsync(M->grads(), 0, 4 * M->L.N, M->stream));
+        M->grads_zero = false;
     }
     return GPT2_OK;
 }
@@ -708,7 +728,8 @@ int gpt2_read_loss(gpt2_t* M, float* mean_loss) {
 
 int gpt2_zero_grad(gpt2_t* M) {
     if (!M) return fail(GPT2_EINVAL, "NULL model");
-    HIPCHK(hipMemsetAsync(M->grads(), 0, 4 * M->L.N, M->stream));
+    if (M->bf16mode()) M->grads_zero = true;
+    else HIPCHK(hipMemsetAsync(M->grads(), 0, 4 * M->L.N, M->stream));
     return GPT2_OK;
 }
 
@@ -722,6 +743,7 @@ int gpt2_backward(gpt2_t* M) {
 
 int gpt2_clip_grad_norm(gpt2_t* M, float max_norm, float* norm) {
     if (!M) return fail(GPT2_EINVAL, "NULL model");
+    if (int rc = materialize_zero_grad(M)) return rc;
     float* ns = M->P<float>(M->L.scalars) + 4;
     RUN("grad_norm", grad_norm(M->P<float>(M->L.norm_partial), ns, M->grads(), M->L.N, max_norm, M->stream));
     M->norm_bad = false;
@@ -742,6 +764,7 @@ int gpt2_adamw_step(gpt2_t* M, float lr, float beta1, float beta2, float eps, fl
     if (!M) return fail(GPT2_EINVAL, "NULL model");
     if (t < 1) return fail(GPT2_EINVAL, "AdamW step t must be >= 1 (got %d)", t);
     if (M->norm_bad) return fail(GPT2_ERANGE, "refusing the update: the last gradient norm was not finite");
+    if (int rc = materialize_zero_grad(M)) return rc;
     float c1 = (float)(1.0 - pow((double)beta1, t)), c2 = (float)(1.0 - pow((double)beta2, t));
     float* ns = M->clip_pending ? M->P<float>(M->L.scalars) + 4 : nullptr;
     bf16* sh = M->bf16mode() ? M->P<bf16>(M->L.shadow) : nullptr;
@@ -769,6 +792,7 @@ int gpt2_copy_params(gpt2_t* M, float* dst) {
 
 int gpt2_copy_grads(gpt2_t* M, float* dst) {
     if (!M || !dst) return fail(GPT2_EINVAL, "NULL argument");
+    if (int rc = materialize_zero_grad(M)) return rc;
     HIPCHK(hipMemcpyAsync(dst, M->grads(), 4 * M->L.N, hipMemcpyDeviceToHost, M->stream));
     HIPCHK(hipStreamSynchronize(M->stream));
     return GPT2_OK;
@@ -822,7 +846,10 @@ int gpt2_set_params(gpt2_t* M, const float* src) {
 }
 
 void* gpt2_device_params(gpt2_t* M) { return M ? M->params() : nullptr; }
-void* gpt2_device_grads(gpt2_t* M) { return M ? M->grads() : nullptr; }
+void* gpt2_device_grads(gpt2_t* M) {
+    if (!M || materialize_zero_grad(M)) return nullptr;
+    return M->grads();
+}
 void* gpt2_device_shadow(gpt2_t* M) { return (M && M->bf16mode()) ? M->base + M->L.shadow : nullptr; }
 
 int gpt2_kernel_timing_enable(gpt2_t* M, const char* cls, int enable) {

@@ -369,15 +369,11 @@ DEVI void mfma_step(f32x16 (&acc)[FM][FN], bf16x8 (&fa)[FM], bf16x8 (&fb)[FN], c
 // tile when fewer than BN; the B operand is still staged BN rows wide (same
 // load geometry, every wave issues the same loads), the rows past BNV land in
 // LDS that no fragment reads.
-// GROUPED: one launch over the tiles of several problems; tile_list[w]
-// holds (problem << 22 | tile row << 11 | tile column), or ~0 for padding,
-// group[problem] the problem's arguments, and overwrite sets their
-// acc_overwrite.
+// GROUPED: one launch over the tiles of several problems (see GroupSched).
 template <int BM, int BN, int NW, int WAVES_M, int KB, int NS, bool XPF, bool AK, bool BKC, int EPI, int OCC = 2,
           int BNV = BN, bool GROUPED = false>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void gemm_big_kernel(
-    GemmArgs garg, int kchunk, const GemmArgs* __restrict__ group, const uint32_t* __restrict__ tile_list,
-    int overwrite) {
+    GemmArgs garg, int kchunk, GroupSched gs) {
     constexpr int WAVES_N = NW / WAVES_M;
     constexpr int TM = BM / WAVES_M, TN = BNV / WAVES_N, FM = TM / 32, FN = TN / 32;
     static_assert(BNV <= BN && TN % 32 == 0, "tile width");
@@ -414,17 +410,23 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
     // split, neighbouring tiles) share one L2.
     GemmArgs g;
     int m0, n0, split;
+    int half_slot = -1;  // grouped: workspace slot of a half-reduction tile
     if constexpr (GROUPED) {
-        const int total = gridDim.x;  // a multiple of 8
-        const int work = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
-        const uint32_t t = tile_list[work];
+        const int xcd = blockIdx.x & 7, pos = blockIdx.x >> 3;
+        const uint32_t t = gs.tiles[xcd * (gs.full + 2 * gs.split) + pos];
         if (t == ~0u) return;
-        g = group[t >> 22];
-        g.acc_overwrite = overwrite != 0;
+        g = gs.probs[t >> 22];
+        g.acc_overwrite = gs.overwrite != 0;
         m0 = (int)((t >> 11) & 0x7FF) * BM;
         n0 = (int)(t & 0x7FF) * BNV;
         split = 0;
         kchunk = g.K;
+        if (pos >= gs.full) {  // the XCD's last round: each tile in two halves of the reduction
+            const int q = pos - gs.full;
+            split = q & 1;
+            kchunk = g.K / 2;
+            half_slot = 2 * (xcd * gs.split + (q >> 1)) + split;
+        }
     } else {
         g = garg;
         const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BNV - 1) / BNV;
@@ -536,8 +538,19 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
             case 6: region = sa3; break;
             default: region = sb3; break;
         }
-        epilogue_rows<EPI, RH>(g, acc, reinterpret_cast<float*>(region), m0 + wm * TM, n0 + wn * TN, split,
-                               (m0 / BM) * WAVES_M + wm, lane);
+        if (GROUPED && half_slot >= 0) {
+            // a half-reduction tile leaves its fp32 partial in its own slot
+            GemmArgs h = g;
+            h.out = gs.ws + (int64_t)half_slot * (BM * BNV);
+            h.ldo = BNV;
+            h.M = min(BM, g.M - m0);
+            h.N = min(BNV, g.N - n0);
+            h.acc_overwrite = true;
+            epilogue_rows<EPI, RH>(h, acc, reinterpret_cast<float*>(region), wm * TM, wn * TN, 0, 0, lane);
+        } else {
+            epilogue_rows<EPI, RH>(g, acc, reinterpret_cast<float*>(region), m0 + wm * TM, n0 + wn * TN, split,
+                                   (m0 / BM) * WAVES_M + wm, lane);
+        }
     }
 }
 
@@ -546,7 +559,7 @@ template <int BM, int BN, int NW, int WAVES_M, int KB, int NS, bool XPF, bool AK
 hipError_t launch_big(const GemmArgs& g, hipStream_t s, int splits = 1, int kchunk = 0) {
     dim3 grid(cdiv(g.M, BM) * cdiv(g.N, BNV), splits);
     gemm_big_kernel<BM, BN, NW, WAVES_M, KB, NS, XPF, AK, BKC, EPI, OCC, BNV>
-        <<<grid, NW * 64, 0, s>>>(g, kchunk ? kchunk : g.K, nullptr, nullptr, 0);
+        <<<grid, NW * 64, 0, s>>>(g, kchunk ? kchunk : g.K, GroupSched{});
     return hipGetLastError();
 }
 
@@ -645,10 +658,69 @@ int gemm_grouped_tiles(const GemmArgs* probs, int n, uint32_t* tiles, int cap) {
     return cnt;
 }
 
-hipError_t gemm_grouped_bf16(const GemmArgs* d_probs, const uint32_t* d_tiles, int ntiles, bool overwrite,
-                             hipStream_t s) {
-    if (ntiles <= 0 || ntiles % 8 || !d_probs || !d_tiles) return hipErrorInvalidValue;
-    GROUPED_DW_KERNEL<<<ntiles, 512, 0, s>>>(GemmArgs{}, 0, d_probs, d_tiles, overwrite ? 1 : 0);
+int gemm_grouped_schedule(const uint32_t* tiles, int n, int cus_per_xcd, uint32_t* sched, int cap,
+                          uint32_t* split_tiles, int* full, int* split) {
+    if (n <= 0 || n % 8) return -1;
+    const int chunk = n / 8;
+    int t = cus_per_xcd > 0 ? chunk % cus_per_xcd : 0;  // no CU count: no split
+    if (2 * t > cus_per_xcd || t > GROUP_SPLIT_MAX) t = 0;
+    const int F = chunk - t, len = 8 * (F + 2 * t);
+    if (len > cap) return -1;
+    for (int x = 0; x < 8; x++) {
+        uint32_t* o = sched + x * (F + 2 * t);
+        for (int i = 0; i < F; i++) o[i] = tiles[x * chunk + i];
+        for (int q = 0; q < t; q++) {
+            const uint32_t e = tiles[x * chunk + F + q];
+            o[F + 2 * q] = o[F + 2 * q + 1] = e;
+            split_tiles[x * t + q] = e;
+        }
+    }
+    *full = F;
+    *split = t;
+    return len;
+}
+
+namespace {
+// out[tile] (+)= P0 + P1 for each half-reduced tile j: block (j, 16-row group)
+__global__ __launch_bounds__(256) void grouped_fixup_kernel(const GemmArgs* __restrict__ probs,
+                                                            const uint32_t* __restrict__ split_tiles,
+                                                            const float* __restrict__ ws, int overwrite) {
+    constexpr int TS = GROUP_TILE;
+    const int j = blockIdx.x;
+    const uint32_t e = split_tiles[j];
+    if (e == ~0u) return;
+    const GemmArgs& g = probs[e >> 22];
+    const int m0 = (int)((e >> 11) & 0x7FF) * TS, n0 = (int)(e & 0x7FF) * TS;
+    const int mv = min(TS, g.M - m0), nv = min(TS, g.N - n0);
+    const float* p0 = ws + (int64_t)(2 * j) * TS * TS;
+    const float* p1 = p0 + TS * TS;
+    float* out = (float*)g.out;
+    for (int i = threadIdx.x; i < 16 * (TS / 4); i += 256) {
+        const int r = blockIdx.y * 16 + i / (TS / 4), c = (i % (TS / 4)) * 4;
+        if (r >= mv || c >= nv) continue;
+        const float4 a = *reinterpret_cast<const float4*>(p0 + r * TS + c);
+        const float4 b = *reinterpret_cast<const float4*>(p1 + r * TS + c);
+        float4* o = reinterpret_cast<float4*>(out + (int64_t)(m0 + r) * g.ldo + n0 + c);
+        float4 v = make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+        if (!overwrite) {
+            const float4 cur = *o;
+            v = make_float4(cur.x + v.x, cur.y + v.y, cur.z + v.z, cur.w + v.w);
+        }
+        *o = v;
+    }
+}
+}  // namespace
+
+hipError_t gemm_grouped_bf16(const GemmArgs* d_probs, const uint32_t* d_sched, int nsched, int full, int split,
+                             const uint32_t* d_split_tiles, float* ws, bool overwrite, hipStream_t s) {
+    if (nsched <= 0 || nsched % 8 || !d_probs || !d_sched || full < 0 || split < 0 ||
+        nsched != 8 * (full + 2 * split) || (split > 0 && (!ws || !d_split_tiles)))
+        return hipErrorInvalidValue;
+    GroupSched gs{d_probs, d_sched, ws, full, split, overwrite ? 1 : 0};
+    GROUPED_DW_KERNEL<<<nsched, 512, 0, s>>>(GemmArgs{}, 0, gs);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || split == 0) return e;
+    grouped_fixup_kernel<<<dim3(8 * split, GROUP_TILE / 16), 256, 0, s>>>(d_probs, d_split_tiles, ws, overwrite);
     return hipGetLastError();
 }
 

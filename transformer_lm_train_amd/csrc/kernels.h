@@ -47,16 +47,37 @@ struct GemmArgs {
 size_t gemm_splitk_ws_bytes(int M, int N, int K);
 int gemm_colsum_rows(int M, int N);
 // Grouped weight-gradient products (bf16): one launch over the 256 x 256
-// tiles of n problems, each mn-contiguous x mn-contiguous with EPI_ACC_F32
-// and its whole reduction in one workgroup.  gemm_grouped_tiles validates the
-// problems and writes their tile list (padded to a multiple of 8; tiles may
-// be NULL to count), returning its length, or -1 when a problem does not fit
-// or cap is too small.  gemm_grouped_bf16 runs the list against the device
-// copies of the problems and the list; overwrite: out = acc for every
-// problem (instead of out += acc).
+// tiles of n problems, each mn-contiguous x mn-contiguous with EPI_ACC_F32.
+// gemm_grouped_tiles validates the problems and writes their tile list
+// (problem << 22 | tile row << 11 | tile column, padded with ~0 to a multiple
+// of 8; tiles may be NULL to count), returning its length, or -1 when a
+// problem does not fit or cap is too small.
 int gemm_grouped_tiles(const GemmArgs* probs, int n, uint32_t* tiles, int cap);
-hipError_t gemm_grouped_bf16(const GemmArgs* d_probs, const uint32_t* d_tiles, int ntiles, bool overwrite,
-                             hipStream_t s);
+// Workgroup L runs on XCD L % 8 and takes, in order, the entries of its
+// eighth of the list; each XCD's 32 CUs (cus_per_xcd) run them in rounds of
+// one workgroup per CU.  gemm_grouped_schedule gives each XCD's last, partial
+// round (up to GROUP_SPLIT_MAX tiles, at most half the CUs) to twice as many
+// workgroups, each taking half of a tile's reduction: per XCD, `full` whole
+// tiles, then `split` tiles listed twice (halves 0 and 1), also collected in
+// split_tiles [8 * split] (cus_per_xcd <= 0: no split).  Returns the
+// schedule's length (8 * (full + 2 * split)) or -1.
+constexpr int GROUP_SPLIT_MAX = 16;
+int gemm_grouped_schedule(const uint32_t* tiles, int n, int cus_per_xcd, uint32_t* sched, int cap,
+                          uint32_t* split_tiles, int* full, int* split);
+// Runs a schedule against the device copies of the problems, the schedule
+// and split_tiles; the half tiles leave fp32 partials in ws [8 * split][2]
+// [256 x 256] that a second kernel adds, in a fixed order, to their outputs.
+// overwrite: out = acc for every problem (instead of out += acc).
+hipError_t gemm_grouped_bf16(const GemmArgs* d_probs, const uint32_t* d_sched, int nsched, int full, int split,
+                             const uint32_t* d_split_tiles, float* ws, bool overwrite, hipStream_t s);
+// What a grouped launch's workgroups read: the problems, the schedule, the
+// partial-tile workspace and the schedule's shape.
+struct GroupSched {
+    const GemmArgs* probs;
+    const uint32_t* tiles;
+    float* ws;
+    int full, split, overwrite;
+};
 
 // fp32-accumulating SIMT kernel for any shapes (activation dtype T).
 template <typename T> hipError_t gemm_simt(const GemmArgs& g, hipStream_t s);

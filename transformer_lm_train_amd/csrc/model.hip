@@ -68,9 +68,9 @@ struct Layout {
     size_t encoded, ln1, qkv, atty, res2, ln2, fch, fchg, res3, lnf, logits;
     size_t ln1_mean, ln1_rstd, ln2_mean, ln2_rstd, lnf_mean, lnf_rstd, lse, losses;
     size_t gres3, gres2, gfch, gqkv, dmid, attD, part_fin, part_ln2, part_ln1, part_fc, part_qkv, norm_partial,
-        scalars, err, tokens, targets, splitk, dw_probs, dw_tiles;
+        scalars, err, tokens, targets, splitk, dw_probs, dw_tiles, dw_split_tiles, dw_ws;
     size_t splitk_bytes;
-    int dw_n, dw_ntiles;  // weight-gradient products and their grouped tile list
+    int dw_n, dw_ntiles;  // weight-gradient products and their grouped tile list (before scheduling)
     size_t total;
 };
 
@@ -184,7 +184,11 @@ Layout make_layout(const gpt2_config& c) {
         dw_problems(c, L, reinterpret_cast<char*>((uintptr_t)1 << 20), pr.data());
         L.dw_ntiles = std::max(0, gemm_grouped_tiles(pr.data(), L.dw_n, nullptr, 0));
     }
-    L.dw_tiles = add(4 * (size_t)L.dw_ntiles);
+    // the schedule (the tile list with up to GROUP_SPLIT_MAX tiles per XCD
+    // listed twice), the split tiles and their fp32 half-reduction partials
+    L.dw_tiles = add(4 * ((size_t)L.dw_ntiles + 8 * GROUP_SPLIT_MAX));
+    L.dw_split_tiles = add(4 * 8 * GROUP_SPLIT_MAX);
+    L.dw_ws = L.dw_ntiles > 0 ? add(4 * (size_t)8 * GROUP_SPLIT_MAX * 2 * 256 * 256) : 0;
     L.total = add(0);
     return L;
 }
@@ -286,6 +290,7 @@ struct gpt2_model {
     bool norm_bad = false;
     bool clip_pending = false;  // gpt2_clip_grad_norm ran since the last update
     std::vector<GemmArgs> dw;   // the weight-gradient products (device copy at L.dw_probs)
+    int dw_nsched = 0, dw_full = 0, dw_split = 0;  // their grouped schedule
     // bf16 mode: gpt2_zero_grad only sets this; the next backward then
     // writes every gradient element instead of adding to it (each element
     // has exactly one first writer), and any earlier reader of the gradient
@@ -470,7 +475,9 @@ template <typename T> int forward_impl(gpt2_t* M, bool with_targets) {
 template <typename T> hipError_t weight_grads(gpt2_t* M, bool overwrite) {
     if constexpr (std::is_same<T, bf16>::value) {
         if (M->L.dw_ntiles > 0)
-            return gemm_grouped_bf16(M->P<GemmArgs>(M->L.dw_probs), M->P<uint32_t>(M->L.dw_tiles), M->L.dw_ntiles,
+            return gemm_grouped_bf16(M->P<GemmArgs>(M->L.dw_probs), M->P<uint32_t>(M->L.dw_tiles), M->dw_nsched,
+                                     M->dw_full, M->dw_split, M->P<uint32_t>(M->L.dw_split_tiles),
+                                     M->P<float>(M->L.dw_ws),
                                      overwrite, M->stream);
     }
     for (GemmArgs g : M->dw) {
@@ -662,13 +669,27 @@ int gpt2_build(const gpt2_config* cfg, uint64_t seed, void* device_buf, size_t b
     if (e == hipSuccess && M->bf16mode()) e = cast_bf16(M->P<bf16>(L.shadow), M->params(), L.N, s);
     M->dw.resize(L.dw_n);
     dw_problems(*cfg, L, M->base, M->dw.data());
-    std::vector<uint32_t> tiles(L.dw_ntiles);
-    if (L.dw_ntiles > 0 && gemm_grouped_tiles(M->dw.data(), L.dw_n, tiles.data(), L.dw_ntiles) != L.dw_ntiles)
-        e = hipErrorInvalidValue;
+    std::vector<uint32_t> tiles(L.dw_ntiles), sched(L.dw_ntiles + 8 * GROUP_SPLIT_MAX),
+        split_tiles(8 * GROUP_SPLIT_MAX, ~0u);
+    if (L.dw_ntiles > 0) {
+        // each XCD's last round of tiles in halves, for this device's CUs per XCD
+        int dev = 0, cus = 0;
+        if (e == hipSuccess) e = hipGetDevice(&dev);
+        if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (gemm_grouped_tiles(M->dw.data(), L.dw_n, tiles.data(), L.dw_ntiles) != L.dw_ntiles) e = hipErrorInvalidValue;
+        if (e == hipSuccess) {
+            M->dw_nsched = gemm_grouped_schedule(tiles.data(), L.dw_ntiles, cus % 8 ? 0 : cus / 8, sched.data(),
+                                                 (int)sched.size(), split_tiles.data(), &M->dw_full, &M->dw_split);
+            if (M->dw_nsched <= 0) e = hipErrorInvalidValue;
+        }
+    }
     if (e == hipSuccess)
         e = hipMemcpyAsync(M->P<GemmArgs>(L.dw_probs), M->dw.data(), sizeof(GemmArgs) * L.dw_n, hipMemcpyHostToDevice, s);
     if (e == hipSuccess && L.dw_ntiles > 0)
-        e = hipMemcpyAsync(M->P<uint32_t>(L.dw_tiles), tiles.data(), 4 * (size_t)L.dw_ntiles, hipMemcpyHostToDevice, s);
+        e = hipMemcpyAsync(M->P<uint32_t>(L.dw_tiles), sched.data(), 4 * (size_t)M->dw_nsched, hipMemcpyHostToDevice, s);
+    if (e == hipSuccess && L.dw_ntiles > 0)
+        e = hipMemcpyAsync(M->P<uint32_t>(L.dw_split_tiles), split_tiles.data(), 4 * split_tiles.size(),
+                           hipMemcpyHostToDevice, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     if (e != hipSuccess) {
         gpt2_destroy(M);

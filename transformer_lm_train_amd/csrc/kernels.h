@@ -90,9 +90,13 @@ hipError_t gemm_mfma_bf16(const GemmArgs& g, hipStream_t s);
 template <typename T>
 hipError_t encoder_fwd(T* out, int* tokens, const float* wte, const float* wpe, int B, int T_,
                        int C, int V, int* err_flag, hipStream_t s);
+// dwte[tokens[i]] += dx[i] for every position (sorted by token and summed in
+// position order: deterministic), dwpe[t] (+)= sum_b dx[b][t] (overwrite:
+// =, all maxT positions).  ws: encoder_bwd_ws_bytes(B*T, V, C) bytes.
+size_t encoder_bwd_ws_bytes(int BT, int V, int C);
 template <typename T>
 hipError_t encoder_bwd(float* dwte, float* dwpe, const T* dx, const int* tokens, int B, int T_, int maxT, int C,
-                       bool overwrite, hipStream_t s);
+                       int V, void* ws, bool overwrite, hipStream_t s);
 template <typename T>
 hipError_t layernorm_fwd(T* out, float* mean, float* rstd, const T* x, const float* w, const float* b,
                          int N, int C, hipStream_t s);

@@ -54,15 +54,216 @@ hipError_t encoder_fwd(T* out, int* tokens, const float* wte, const float* wpe, 
     return LAUNCH_CHECK();
 }
 
-// dwte[tok] += dx (fp32 atomics: a token id may repeat within the batch);
-// dwpe[t] += sum_b dx[b,t] (each (t, c) summed over b in order).
-template <typename T>
-__global__ void encoder_bwd_wte_kernel(float* dwte, const T* dx, const int* tokens, int C, int BT) {
-    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= (int64_t)BT * C) return;
-    int row = (int)(i / C), c = (int)(i % C);
-    atomicAdd(dwte + (int64_t)tokens[row] * C + c, to_f32(dx[i]));
+// dwte[tok] += dx, deterministically (no float atomics; a token may repeat
+// within the batch, Zipf-hot ones thousands of times): the positions are
+// sorted by token id, stably, by a counting sort, and each id's rows are
+// summed in position order.
+//   rank:    per block of ENC_B positions, each position's rank among the
+//            earlier positions of its block with the same id, and the
+//            block's count of each id (written by the id's first position).
+//   offsets: the total count of every id and its exclusive prefix sum, in
+//            two levels (within groups of 1024 ids, then over the groups),
+//            and, in place of the block counts, each block's exclusive
+//            prefix of them (the count of the id in the earlier blocks).
+//   scatter: position i goes to sorted slot base[id] + (count of id in the
+//            earlier blocks) + rank.
+//   chunks:  per ENC_S consecutive sorted slots, one partial row per run of
+//            equal ids, summed in slot order, stored at the run's first slot.
+//   segments: at each id's first slot, its pieces (that slot, then every
+//            chunk start inside the id's range) are added in order into dwte.
+// Ids outside [0, V) (already flagged by the forward) go to a last bin, V,
+// which is dropped.
+constexpr int ENC_B = 256, ENC_S = 32, ENC_G = 1024;
+
+struct EncWs {
+    int *H, *R, *tot, *lbase, *goff, *perm, *sid;
+    float* Q;
+};
+// carve the workspace: H [NB][V+1], R [BT], tot, lbase [V+1], goff [groups],
+// perm, sid [BT], Q [BT][C]
+static size_t enc_ws_layout(int BT, int V, int C, char* p, EncWs* w) {
+    const size_t NB = cdiv(BT, ENC_B), NG = cdiv(V + 1, ENC_G);
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off = (off + bytes + 255) & ~(size_t)255;
+        return p ? p + o : nullptr;
+    };
+    EncWs e;
+    e.H = (int*)take(4 * NB * (V + 1));
+    e.R = (int*)take(4 * (size_t)BT);
+    e.tot = (int*)take(4 * (size_t)(V + 1));
+    e.lbase = (int*)take(4 * (size_t)(V + 1));
+    e.goff = (int*)take(4 * NG);
+    e.perm = (int*)take(4 * (size_t)BT);
+    e.sid = (int*)take(4 * (size_t)BT);
+    e.Q = (float*)take(4 * (size_t)BT * C);
+    if (w) *w = e;
+    return off;
 }
+size_t encoder_bwd_ws_bytes(int BT, int V, int C) { return enc_ws_layout(BT, V, C, nullptr, nullptr); }
+
+__global__ void fill_i32_kernel(int* p, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = 0;
+}
+
+DEVI int enc_bin(int t, int V) { return t >= 0 && t < V ? t : V; }
+
+__global__ __launch_bounds__(ENC_B) void enc_rank_kernel(const int* tokens, int BT, int V, int* H, int* R) {
+    __shared__ int tk[ENC_B];
+    const int i = blockIdx.x * ENC_B + threadIdx.x;
+    const int id = i < BT ? enc_bin(tokens[i], V) : -1;
+    tk[threadIdx.x] = id;
+    __syncthreads();
+    if (i >= BT) return;
+    int r = 0, cnt = 0;
+    for (int j = 0; j < ENC_B; j++) {
+        const bool eq = tk[j] == id;
+        cnt += eq;
+        r += eq && j < (int)threadIdx.x;
+    }
+    R[i] = r;
+    if (r == 0) H[(int64_t)blockIdx.x * (V + 1) + id] = cnt;
+}
+
+// per group of ENC_G ids: totals over the NB blocks (the block counts are
+// replaced by their exclusive prefix over the blocks), the totals'
+// exclusive scan within the group (lbase) and the group's sum (gsum)
+__global__ __launch_bounds__(ENC_G) void enc_group_kernel(int* H, int NB, int V, int* tot, int* lbase, int* gsum) {
+    __shared__ int sc[ENC_G];
+    const int id = blockIdx.x * ENC_G + threadIdx.x;
+    int t = 0;
+    if (id <= V) {
+        constexpr int U = 16;
+        for (int b0 = 0; b0 < NB; b0 += U) {
+            int h[U];
+#pragma unroll
+            for (int u = 0; u < U; u++) h[u] = b0 + u < NB ? H[(int64_t)(b0 + u) * (V + 1) + id] : 0;
+#pragma unroll
+            for (int u = 0; u < U; u++)
+                if (b0 + u < NB) {
+                    H[(int64_t)(b0 + u) * (V + 1) + id] = t;
+                    t += h[u];
+                }
+        }
+    }
+    sc[threadIdx.x] = t;
+    __syncthreads();
+    for (int o = 1; o < ENC_G; o <<= 1) {  // inclusive scan (Hillis-Steele)
+        const int v = (int)threadIdx.x >= o ? sc[threadIdx.x - o] : 0;
+        __syncthreads();
+        sc[threadIdx.x] += v;
+        __syncthreads();
+    }
+    if (id <= V) {
+        tot[id] = t;
+        lbase[id] = sc[threadIdx.x] - t;
+    }
+    if (threadIdx.x == ENC_G - 1) gsum[blockIdx.x] = sc[ENC_G - 1];
+}
+
+// each block first scans the NG group sums in LDS (NG <= ENC_B)
+__global__ __launch_bounds__(ENC_B) void enc_scatter_kernel(const int* tokens, int BT, int V, const int* Hpre,
+                                                           const int* R, const int* lbase, const int* gsum, int NG,
+                                                           int* perm, int* sid) {
+    __shared__ int go[ENC_B];
+    go[threadIdx.x] = (int)threadIdx.x < NG ? gsum[threadIdx.x] : 0;
+    __syncthreads();
+    for (int o = 1; o < ENC_B; o <<= 1) {
+        const int v = (int)threadIdx.x >= o ? go[threadIdx.x - o] : 0;
+        __syncthreads();
+        go[threadIdx.x] += v;
+        __syncthreads();
+    }
+    const int i = blockIdx.x * ENC_B + threadIdx.x;
+    if (i >= BT) return;
+    const int id = enc_bin(tokens[i], V);
+    const int g = id / ENC_G;
+    const int dst = (g > 0 ? go[g - 1] : 0) + lbase[id] + Hpre[(int64_t)blockIdx.x * (V + 1) + id] + R[i];
+    perm[dst] = i;
+    sid[dst] = id;
+}
+
+// one block per ENC_S sorted slots, one thread per 4 channels; the slots'
+// rows are all requested before the runs are summed
+template <typename T>
+__global__ __launch_bounds__(1024) void enc_chunk_kernel(const T* dx, const int* perm, const int* sid, int BT, int C,
+                                                         float* Q) {
+    __shared__ int sp[ENC_S], si[ENC_S];
+    const int k0 = blockIdx.x * ENC_S, n = min(BT - k0, ENC_S);
+    if ((int)threadIdx.x < n) {
+        sp[threadIdx.x] = perm[k0 + threadIdx.x];
+        si[threadIdx.x] = sid[k0 + threadIdx.x];
+    }
+    __syncthreads();
+    const int c = threadIdx.x * 4;
+    if (c >= C) return;
+    float v[ENC_S][4];
+    if (n == ENC_S) {  // every chunk but the last: all loads unconditional
+#pragma unroll
+        for (int k = 0; k < ENC_S; k++) {
+            const T* r = dx + (int64_t)sp[k] * C + c;
+#pragma unroll
+            for (int e = 0; e < 4; e++) v[k][e] = to_f32(r[e]);
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < ENC_S; k++)
+            if (k < n) {
+                const T* r = dx + (int64_t)sp[k] * C + c;
+#pragma unroll
+                for (int e = 0; e < 4; e++) v[k][e] = to_f32(r[e]);
+            }
+    }
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+    int run = 0;
+#pragma unroll
+    for (int k = 0; k < ENC_S; k++) {
+        if (k >= n) break;
+        if (k > 0 && si[k] != si[k - 1]) {
+            *reinterpret_cast<float4*>(Q + (int64_t)(k0 + run) * C + c) = make_float4(a0, a1, a2, a3);
+            a0 = a1 = a2 = a3 = 0.f;
+            run = k;
+        }
+        a0 += v[k][0];
+        a1 += v[k][1];
+        a2 += v[k][2];
+        a3 += v[k][3];
+    }
+    *reinterpret_cast<float4*>(Q + (int64_t)(k0 + run) * C + c) = make_float4(a0, a1, a2, a3);
+}
+
+// one wave per sorted slot; at an id's first slot, its pieces go into dwte
+__global__ __launch_bounds__(256) void enc_segment_kernel(const int* sid, const int* tot, const float* Q, int BT,
+                                                          int V, int C, float* dwte) {
+    const int k = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+    if (k >= BT) return;
+    const int id = sid[k];
+    if (id >= V || (k > 0 && sid[k - 1] == id)) return;
+    const int end = k + tot[id];
+    for (int c = lane * 4; c < C; c += 256) {
+        float4 a = *reinterpret_cast<const float4*>(Q + (int64_t)k * C + c);
+        // the pieces in order, 8 requested at a time
+        constexpr int U = 8;
+        for (int m0 = (k / ENC_S + 1) * ENC_S; m0 < end; m0 += U * ENC_S) {
+            float4 q[U];
+#pragma unroll
+            for (int u = 0; u < U; u++) {
+                const int m = m0 + u * ENC_S;
+                q[u] = m < end ? *reinterpret_cast<const float4*>(Q + (int64_t)m * C + c)
+                               : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+#pragma unroll
+            for (int u = 0; u < U; u++)
+                if (m0 + u * ENC_S < end) { a.x += q[u].x; a.y += q[u].y; a.z += q[u].z; a.w += q[u].w; }
+        }
+        float4* o = reinterpret_cast<float4*>(dwte + (int64_t)id * C + c);
+        const float4 cur = *o;
+        *o = make_float4(cur.x + a.x, cur.y + a.y, cur.z + a.z, cur.w + a.w);
+    }
+}
+
 // dwpe[t][c] (+)= sum_b dx[b][t][c] over all maxT positions (0 for t >= T_,
 // so that overwrite also clears the positions the batch does not reach).
 template <typename T>
@@ -78,10 +279,21 @@ __global__ void encoder_bwd_wpe_kernel(float* dwpe, const T* dx, int B, int T_, 
 
 template <typename T>
 hipError_t encoder_bwd(float* dwte, float* dwpe, const T* dx, const int* tokens, int B, int T_, int maxT, int C,
-                       bool overwrite, hipStream_t s) {
-    if (T_ > maxT) return hipErrorInvalidValue;
-    int64_t n = (int64_t)B * T_ * C;
-    encoder_bwd_wte_kernel<T><<<cdiv(n, 256), 256, 0, s>>>(dwte, dx, tokens, C, B * T_);
+                       int V, void* ws, bool overwrite, hipStream_t s) {
+    const int BT = B * T_;
+    if (T_ > maxT || BT <= 0 || C % 4 || C > 4096 || V <= 0 || !ws) return hipErrorInvalidValue;
+    EncWs w;
+    enc_ws_layout(BT, V, C, (char*)ws, &w);
+    const int NB = (int)cdiv(BT, ENC_B), NG = (int)cdiv(V + 1, ENC_G);
+    if (NG > ENC_B) return hipErrorInvalidValue;  // V < 256 * 1024
+    const int64_t nh = (int64_t)NB * (V + 1);
+    fill_i32_kernel<<<(unsigned)std::min<int64_t>(cdiv(nh, 256), 4096), 256, 0, s>>>(w.H, nh);
+    enc_rank_kernel<<<NB, ENC_B, 0, s>>>(tokens, BT, V, w.H, w.R);
+    enc_group_kernel<<<NG, ENC_G, 0, s>>>(w.H, NB, V, w.tot, w.lbase, w.goff);
+    enc_scatter_kernel<<<NB, ENC_B, 0, s>>>(tokens, BT, V, w.H, w.R, w.lbase, w.goff, NG, w.perm, w.sid);
+    const int nt = (int)cdiv(C / 4, 64) * 64;
+    enc_chunk_kernel<T><<<(unsigned)cdiv(BT, ENC_S), nt, 0, s>>>(dx, w.perm, w.sid, BT, C, w.Q);
+    enc_segment_kernel<<<(unsigned)cdiv(BT, 4), 256, 0, s>>>(w.sid, w.tot, w.Q, BT, V, C, dwte);
     encoder_bwd_wpe_kernel<T><<<cdiv((int64_t)maxT * C, 256), 256, 0, s>>>(dwpe, dx, B, T_, maxT, C, overwrite);
     return LAUNCH_CHECK();
 }
@@ -770,8 +982,8 @@ template <typename T> hipError_t widen_f32(float* dst, const T* src, size_t n, h
 #define INST(T)                                                                                              \
     template hipError_t encoder_fwd<T>(T*, int*, const float*, const float*, int, int, int, int, int*,       \
                                        hipStream_t);                                                         \
-    template hipError_t encoder_bwd<T>(float*, float*, const T*, const int*, int, int, int, int, bool,        \
-                                        hipStream_t);                                                        \
+    template hipError_t encoder_bwd<T>(float*, float*, const T*, const int*, int, int, int, int, int, void*,  \
+                                        bool, hipStream_t);                                                  \
     template hipError_t layernorm_fwd<T>(T*, float*, float*, const T*, const float*, const float*, int, int, \
                                          hipStream_t);                                                       \
     template hipError_t layernorm_bwd<T>(T*, const T*, const T*, const T*, const float*, const float*,      \

@@ -68,7 +68,7 @@ struct Layout {
     size_t encoded, ln1, qkv, atty, res2, ln2, fch, fchg, res3, lnf, logits;
     size_t ln1_mean, ln1_rstd, ln2_mean, ln2_rstd, lnf_mean, lnf_rstd, lse, losses;
     size_t gres3, gres2, gfch, gqkv, dmid, attD, part_fin, part_ln2, part_ln1, part_fc, part_qkv, norm_partial,
-        scalars, err, tokens, targets, splitk, dw_probs, dw_tiles, dw_split_tiles, dw_ws;
+        scalars, err, tokens, targets, splitk, dw_probs, dw_tiles, dw_split_tiles, dw_ws, encws;
     size_t splitk_bytes;
     int dw_n, dw_ntiles;  // weight-gradient products and their grouped tile list (before scheduling)
     size_t total;
@@ -88,6 +88,7 @@ int validate(const gpt2_config* c) {
     int hs = c->channels / c->num_heads;
     if (c->seq_len > 1024 || hs > 128) return fail(GPT2_EINVAL, "seq_len <= 1024 and head size <= 128 required");
     if (c->channels > 4096) return fail(GPT2_EINVAL, "channels <= 4096 required");
+    if (c->vocab_size >= 256 * 1024 - 1) return fail(GPT2_EINVAL, "vocab_size < 262143 required");
     if (c->precision == GPT2_BF16_MIXED) {
         if (hs != 64) return fail(GPT2_EINVAL, "BF16_MIXED needs head size 64");
         if (c->channels % 64 || c->padded_vocab_size % 64 || c->seq_len % 64)
@@ -174,6 +175,9 @@ Layout make_layout(const gpt2_config& c) {
         for (auto& d : dims) L.splitk_bytes = std::max(L.splitk_bytes, gemm_splitk_ws_bytes(d[0], d[1], (int)BT));
     }
     L.splitk = add(L.splitk_bytes);
+    // the token-sorted embedding backward: per-block counts, ranks, offsets,
+    // the sorted positions and one fp32 partial row per sorted position
+    L.encws = add(encoder_bwd_ws_bytes((int)BT, c.vocab_size, (int)C));
     L.dw_n = 4 * c.num_layers + 1;
     L.dw_probs = add(sizeof(GemmArgs) * L.dw_n);
     L.dw_ntiles = 0;
@@ -568,7 +572,7 @@ template <typename T> int backward_impl(gpt2_t* M) {
     }
     RUN("gemm_dw", weight_grads<T>(M, ow));  // the classifier's product writes every wte row first
     RUN("encoder_bwd", encoder_bwd<T>(g + po[P_WTE], g + po[P_WPE], G3(-1), M->P<int>(M->L.tokens), B, T_,
-                                      c.max_seq_len, C, ow, s));
+                                      c.max_seq_len, C, c.vocab_size, M->base + M->L.encws, ow, s));
     M->grads_zero = false;
     return GPT2_OK;
 }

@@ -513,6 +513,70 @@ void orc_adamw_update(REAL* params, const REAL* grads, REAL* m, REAL* v, size_t 
 }
 
 /* ------------------------------------------------------------------------ */
+/* bf16 parameters with stochastic rounding ("llm.c's Origin and the Future */
+/* of LLM Compilers", section "Avengers": stochastic rounding)               */
+/* ------------------------------------------------------------------------ */
+
+/* The 16-bit draw of flat parameter index i at AdamW step t: the top 16 bits
+ * of SplitMix64 drawn at (k, i + 1), where k is SplitMix64 drawn at
+ * (seed, 2^62 + t).  A counter-based stream: every (t, i) has its own draw. */
+uint32_t orc_sr_draw(uint64_t seed, int t, uint64_t i) {
+    uint64_t k = sm64_draw(seed, ((uint64_t)1 << 62) + (uint64_t)t);
+    return (uint32_t)(sm64_draw(k, i + 1) >> 48);
+}
+
+/* Stochastic rounding of the fp32 value x to bf16 with the draw u in
+ * [0, 65536).  bf16 keeps the top 16 bits of the fp32 pattern, so the two
+ * bf16 neighbours of x are lo (its pattern with the low 16 bits cleared, x
+ * truncated toward zero) and hi (the next bf16 value away from zero), and
+ * f = (low 16 bits of x) / 65536 is where x sits between them.  The result
+ * is hi when u >= 65536 - f*65536 (probability f), else lo, so its
+ * expectation over u is x.  Exact values (f = 0) and non-finite x are
+ * returned unchanged.  The result is returned widened to float. */
+float orc_sr_bf16(float x, uint32_t u) {
+    uint32_t b;
+    memcpy(&b, &x, 4);
+    if ((b & 0x7F800000u) == 0x7F800000u) return x;  /* inf, NaN */
+    uint32_t frac = b & 0xFFFFu;
+    if (frac == 0) return x;
+    uint32_t lo = b & 0xFFFF0000u;
+    uint32_t hi = lo + 0x10000u; /* next magnitude (the exponent carries at a binade end) */
+    uint32_t r = (u >= 65536u - frac) ? hi : lo;
+    float y;
+    memcpy(&y, &r, 4);
+    return y;
+}
+
+/* Array forms of the two functions above (for the tests). */
+void orc_sr_draws(uint64_t seed, int t, uint64_t i0, size_t n, uint32_t* out) {
+    for (size_t j = 0; j < n; j++) out[j] = orc_sr_draw(seed, t, i0 + j);
+}
+void orc_sr_bf16_array(const float* x, const uint32_t* u, size_t n, float* out) {
+    for (size_t j = 0; j < n; j++) out[j] = orc_sr_bf16(x[j], u[j]);
+}
+
+/* AdamW as orc_adamw_update on parameters that are bf16 values (stored as
+ * float): the updated value is computed in double, rounded to fp32, then
+ * rounded to bf16 by orc_sr_bf16 with the draw orc_sr_draw(seed, t, i). */
+void orc_adamw_sr_update(float* params, const float* grads, float* m, float* v, size_t n,
+                         double lr, double b1, double b2, double eps, double wd, int t,
+                         double grad_scale, uint64_t seed) {
+    ACC c1 = 1.0 - pow(b1, t), c2 = 1.0 - pow(b2, t);
+    #pragma omp parallel for
+    for (size_t i = 0; i < n; i++) {
+        ACC g = (ACC)grads[i] * grad_scale;
+        ACC mi = b1 * (ACC)m[i] + (1.0 - b1) * g;
+        ACC vi = b2 * (ACC)v[i] + (1.0 - b2) * g * g;
+        ACC mh = mi / c1, vh = vi / c2;
+        ACC th = params[i];
+        float x = (float)(th - lr * (mh / (sqrt(vh) + eps) + wd * th));
+        params[i] = orc_sr_bf16(x, orc_sr_draw(seed, t, i));
+        m[i] = (float)mi;
+        v[i] = (float)vi;
+    }
+}
+
+/* ------------------------------------------------------------------------ */
 /* the model: one allocation for params, grads, m, v, acts, act grads       */
 /* ------------------------------------------------------------------------ */
 
@@ -713,6 +777,15 @@ double orc_clip_grad_norm(orc_model* M, double max_norm) {
 int orc_adamw(orc_model* M, double lr, double b1, double b2, double eps, double wd, int t) {
     if (t < 1) return -1;
     orc_adamw_update(M->params, M->grads, M->m, M->v, M->np, lr, b1, b2, eps, wd, t, 1.0);
+    return 0;
+}
+
+/* The stochastic-rounding update on the model (fp32 build only: the
+ * parameters are bf16 values held in float). */
+int orc_adamw_sr(orc_model* M, double lr, double b1, double b2, double eps, double wd, int t, uint64_t seed) {
+    if (t < 1 || sizeof(REAL) != sizeof(float)) return -1;
+    orc_adamw_sr_update((float*)M->params, (const float*)M->grads, (float*)M->m, (float*)M->v, M->np, lr, b1, b2,
+                        eps, wd, t, 1.0, seed);
     return 0;
 }
 

@@ -89,6 +89,18 @@ def _lib(precision="f32"):
     lib.orc_global_norm.argtypes = [R, sz]
     lib.orc_global_norm.restype = ctypes.c_double
     lib.orc_adamw_update.argtypes = [R, R, R, R, sz, d, d, d, d, d, ctypes.c_int, d]
+    F = ctypes.POINTER(ctypes.c_float)
+    u64 = ctypes.c_uint64
+    lib.orc_sr_draw.argtypes = [u64, ctypes.c_int, u64]
+    lib.orc_sr_draw.restype = ctypes.c_uint32
+    lib.orc_sr_bf16.argtypes = [ctypes.c_float, ctypes.c_uint32]
+    lib.orc_sr_bf16.restype = ctypes.c_float
+    U = ctypes.POINTER(ctypes.c_uint32)
+    lib.orc_sr_draws.argtypes = [u64, ctypes.c_int, u64, sz, U]
+    lib.orc_sr_bf16_array.argtypes = [F, U, sz, F]
+    lib.orc_adamw_sr_update.argtypes = [F, F, F, F, sz, d, d, d, d, d, ctypes.c_int, d, u64]
+    lib.orc_adamw_sr.argtypes = [vp, d, d, d, d, d, ctypes.c_int, u64]
+    lib.orc_adamw_sr.restype = ctypes.c_int
     lib.orc_num_threads.restype = ctypes.c_int
     lib.orc_set_num_threads.argtypes = [ctypes.c_int]
     _LIBS[precision] = lib
@@ -221,6 +233,12 @@ class Model:
         rc = self.lib.orc_adamw(self.h, lr, beta1, beta2, eps, weight_decay, t)
         if rc != 0:
             raise ValueError("t must be >= 1")
+
+    def adamw_sr(self, lr, beta1, beta2, eps, weight_decay, t, seed):
+        """AdamW on bf16-valued parameters with stochastic rounding (fp32 oracle only)."""
+        rc = self.lib.orc_adamw_sr(self.h, lr, beta1, beta2, eps, weight_decay, t, ctypes.c_uint64(seed))
+        if rc != 0:
+            raise ValueError("t must be >= 1 and the oracle the fp32 one")
 
     def logits(self):
         return self.A()["logits"].reshape(self.B * self.T, self.cfg.Vp)
@@ -357,6 +375,46 @@ def softmax_ce_backward(probs, targets, dlosses, V, prec="f32"):
 def global_norm(g, prec="f32"):
     g = _arr(g, prec)
     return float(_lib(prec).orc_global_norm(_ptr(g, prec), g.size))
+
+
+def sr_draws(seed, t, i0, n):
+    """The 16-bit stochastic-rounding draws of flat indices i0 .. i0+n-1 at AdamW step t."""
+    out = np.zeros(n, dtype=np.uint32)
+    _lib("f32").orc_sr_draws(ctypes.c_uint64(seed), t, ctypes.c_uint64(i0), n,
+                             out.ctypes.data_as(ctypes.POINTER(ctypes.c_uint32)))
+    return out
+
+
+def sr_bf16(x, u):
+    """Stochastic rounding of fp32 values x to bf16 with draws u (elementwise), widened to float32."""
+    x = np.ascontiguousarray(np.ravel(x), dtype=np.float32)
+    u = np.ascontiguousarray(np.broadcast_to(np.asarray(u, dtype=np.uint32), x.shape))
+    out = np.zeros_like(x)
+    F = ctypes.POINTER(ctypes.c_float)
+    _lib("f32").orc_sr_bf16_array(x.ctypes.data_as(F), u.ctypes.data_as(ctypes.POINTER(ctypes.c_uint32)), x.size,
+                                  out.ctypes.data_as(F))
+    return out
+
+
+def bf16_rne(x):
+    """Round fp32 values to the nearest bf16 value (ties to even), widened to float32: the
+    rounding a bf16 conversion of an fp32 value makes (finite values only)."""
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    keep = b >> 16
+    rest = b & 0xFFFF
+    up = (rest > 0x8000) | ((rest == 0x8000) & ((keep & 1) == 1))
+    return ((keep + up) << 16).astype(np.uint32).view(np.float32)
+
+
+def adamw_sr_update(params, grads, m, v, lr, b1, b2, eps, wd, t, seed, grad_scale=1.0):
+    """AdamW on bf16-valued float32 params with stochastic rounding, in place (params, m, v)."""
+    for a in (params, m, v):
+        assert a.dtype == np.float32 and a.flags.c_contiguous
+    grads = _arr(grads, "f32")
+    F = ctypes.POINTER(ctypes.c_float)
+    c = lambda a: a.ctypes.data_as(F)
+    _lib("f32").orc_adamw_sr_update(c(params), c(grads), c(m), c(v), params.size, lr, b1, b2, eps, wd, t,
+                                    grad_scale, ctypes.c_uint64(seed))
 
 
 def adamw_update(params, grads, m, v, lr, b1, b2, eps, wd, t, grad_scale=1.0, prec="f32"):

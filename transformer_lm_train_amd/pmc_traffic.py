@@ -84,9 +84,17 @@ def reduce(cls, launches, fetch_dir, write_dir, cal_fetch, cal_write, sources, p
     print(json.dumps(data[cls]))
 
 
-def recorded(cls):
-    """Bytes per launch recorded for cls, or None when absent or when the
-    kernel sources have changed since the counters were taken."""
+# the bench configuration every recorded entry was taken on (the counter runs
+# use bench.py's default: GPT-2 124M, B=16, T=1024)
+RECORDED_CONFIG = "124m"
+
+
+def recorded(cls, config=RECORDED_CONFIG):
+    """Bytes per launch recorded for cls, or None when absent, when the
+    kernel sources have changed since the counters were taken, or for another
+    model configuration than the one they were taken on."""
+    if config != RECORDED_CONFIG:
+        return None
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:

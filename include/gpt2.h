@@ -151,8 +151,9 @@ int gpt2_clip_grad_norm(gpt2_t* m, float max_norm, float* norm);
  * function at state seed + (2^62 + t)*gamma (seed: the build seed), the bf16
  * result is the top half of bits(x) + u, i.e. x moves away from zero to the
  * next bf16 value with probability (low 16 bits of x) / 65536 (unbiased).
- * The fp32 region then holds float(bf16) for the LayerNorm and bias tensors
- * (the kernels read those in fp32) and is not kept for the others.
+ * The fp32 region then holds float(bf16) of the LayerNorm and bias tensors
+ * (the kernels read those in fp32); there is no fp32 copy of the others
+ * (gpt2_plan leaves it out: 4 bytes less per matrix parameter).
  * GPT2_EINVAL if t < 1. */
 int gpt2_adamw_step(gpt2_t* m, float lr, float beta1, float beta2, float eps,
                     float weight_decay, int t);
@@ -173,8 +174,7 @@ int gpt2_param_offsets(const gpt2_t* m, size_t offsets[16]);
 
 /* Copy fp32 master parameters / gradients / AdamW m and v to host arrays of
  * N floats; m_dst or v_dst may be NULL.  In BF16_SR mode the parameters are
- * the bf16 values widened (exact); the copy also refreshes the device fp32
- * region with them. */
+ * the bf16 values widened (exact). */
 int gpt2_copy_params(gpt2_t* m, float* host_dst);
 int gpt2_copy_grads(gpt2_t* m, float* host_dst);
 int gpt2_copy_opt_state(gpt2_t* m, float* m_dst, float* v_dst);
@@ -188,14 +188,15 @@ int gpt2_copy_logits(gpt2_t* m, float* host_dst);
 int gpt2_copy_losses(gpt2_t* m, float* host_dst);
 
 /* Overwrite the fp32 master parameters from a host array of N floats and
- * refresh the bf16 shadow.  In BF16_SR mode the values are rounded to bf16
- * (nearest-even) and the fp32 region is set to the rounded values. */
+ * refresh the bf16 shadow.  In BF16_SR mode the bf16 parameters are set to
+ * the values rounded to nearest-even, and the fp32 copies to those. */
 int gpt2_set_params(gpt2_t* m, const float* host_src);
 
 /* Device pointer of the planned buffer region holding the fp32 master
  * parameters, gradients and the bf16 weight shadow (NULL in FP32 mode).
- * In BF16_SR mode the shadow holds the parameters and the fp32 region is
- * current only for the LayerNorm and bias tensors.
+ * In BF16_SR mode the shadow holds the parameters and the fp32 region holds
+ * only the LayerNorm and bias tensors (ln1w, ln1b, qkvb, attprojb, ln2w,
+ * ln2b, fcb, fcprojb, lnfw, lnfb), packed in that order.
  * gpt2_device_grads first queues a deferred gpt2_zero_grad clear, if one is
  * pending, on the model's stream. */
 void* gpt2_device_params(gpt2_t* m);

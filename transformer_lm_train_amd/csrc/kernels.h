@@ -139,16 +139,16 @@ hipError_t grad_norm(float* partial, float* norm_scale, const float* g, size_t n
 hipError_t adamw(float* p, const float* g, float* m, float* v, bf16* shadow, size_t n, float lr, float b1,
                  float b2, float eps, float wd, float c1, float c2, const float* norm_scale, hipStream_t s);
 // Flat parameter ranges [lo, hi) whose fp32 copy the stochastic-rounding
-// AdamW keeps (as float of the new bf16 value).
+// AdamW keeps (as float of the new bf16 value), at p32[dst + (i - lo)].
 constexpr int SR_RANGES_MAX = 16;
 struct SrRanges {
-    uint64_t lo[SR_RANGES_MAX], hi[SR_RANGES_MAX];
+    uint64_t lo[SR_RANGES_MAX], hi[SR_RANGES_MAX], dst[SR_RANGES_MAX];
     int n;
 };
 // AdamW over bf16 parameters w[0..n) with stochastic rounding of each fp32
 // result (draw: top 16 bits of SplitMix64's output function at state
-// key + (i+1) * 0x9E3779B97F4A7C15); p32[i] = float(w[i]) inside the
-// ranges.  n must be a multiple of 4 and every range boundary too.
+// key + (i+1) * 0x9E3779B97F4A7C15); p32[dst + i - lo] = float(w[i]) inside
+// the ranges.  n, every range boundary and every dst must be multiples of 4.
 hipError_t adamw_sr(bf16* w, float* p32, const float* g, float* m, float* v, size_t n, float lr, float b1, float b2,
                     float eps, float wd, float c1, float c2, const float* norm_scale, uint64_t key,
                     const SrRanges& mirror, hipStream_t s);

@@ -1001,7 +1001,7 @@ DEVI bf16 sr_round_bf16(float x, uint32_t u) {
 
 // Each thread updates ADAM_U groups of 4 parameters, laid out as in
 // adamw_kernel; every range boundary is a multiple of 4, so a group is
-// wholly inside or outside the mirrored ranges.
+// wholly inside or outside each mirrored range.
 __global__ __launch_bounds__(256) void adamw_sr_kernel(bf16* w, float* p32, const float* g, float* m, float* v,
                                                        size_t n, float lr, float b1, float b2, float eps, float wd,
                                                        float ic1, float ic2, const float* norm_scale, uint64_t key,
@@ -1036,10 +1036,10 @@ __global__ __launch_bounds__(256) void adamw_sr_kernel(bf16* w, float* p32, cons
             reinterpret_cast<bf16x4*>(w)[i] = o;
             reinterpret_cast<float4*>(m)[i] = mm[u];
             reinterpret_cast<float4*>(v)[i] = vv[u];
-            bool mirror = false;
-            for (int r = 0; r < mr.n; r++) mirror |= 4 * i >= mr.lo[r] && 4 * i < mr.hi[r];
-            if (mirror)
-                reinterpret_cast<float4*>(p32)[i] = make_float4((float)o[0], (float)o[1], (float)o[2], (float)o[3]);
+            for (int r = 0; r < mr.n; r++)
+                if (4 * i >= mr.lo[r] && 4 * i < mr.hi[r])
+                    *reinterpret_cast<float4*>(p32 + mr.dst[r] + (4 * i - mr.lo[r])) =
+                        make_float4((float)o[0], (float)o[1], (float)o[2], (float)o[3]);
         }
     }
 }
@@ -1049,7 +1049,8 @@ hipError_t adamw_sr(bf16* w, float* p32, const float* g, float* m, float* v, siz
                     const SrRanges& mirror, hipStream_t s) {
     if (n % 4 || mirror.n < 0 || mirror.n > SR_RANGES_MAX) return hipErrorInvalidValue;
     for (int r = 0; r < mirror.n; r++)
-        if (mirror.lo[r] % 4 || mirror.hi[r] % 4 || mirror.lo[r] > mirror.hi[r] || mirror.hi[r] > n)
+        if (mirror.lo[r] % 4 || mirror.hi[r] % 4 || mirror.dst[r] % 4 || mirror.lo[r] > mirror.hi[r] ||
+            mirror.hi[r] > n)
             return hipErrorInvalidValue;
     const size_t blocks = cdiv(n / 4, 256 * ADAM_U);
     adamw_sr_kernel<<<(unsigned)blocks, 256, 0, s>>>(w, p32, g, m, v, n, lr, b1, b2, eps, wd, 1.f / c1, 1.f / c2,

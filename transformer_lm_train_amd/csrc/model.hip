@@ -64,6 +64,11 @@ void param_sizes(const gpt2_config& c, size_t s[NPARAM]) {
 // Byte offsets of every region of the single device buffer.
 struct Layout {
     size_t N, poff[NPARAM];
+    // fp32 parameter copy: the full layout (poff32 == poff, N32 == N), or in
+    // the stochastic-rounding mode only the tensors the kernels read in fp32
+    // (LayerNorm gains and biases, linear biases), packed in tensor order;
+    // poff32 is SIZE_MAX for the others
+    size_t N32, poff32[NPARAM];
     size_t params, grads, m, v, shadow;
     size_t encoded, ln1, qkv, atty, res2, ln2, fch, fchg, res3, lnf, logits;
     size_t ln1_mean, ln1_rstd, ln2_mean, ln2_rstd, lnf_mean, lnf_rstd, lse, losses;
@@ -77,6 +82,13 @@ struct Layout {
 // bf16 activations and MFMA products (with fp32 masters, or bf16 parameters
 // updated by stochastic rounding)
 inline bool is_bf16(int precision) { return precision == GPT2_BF16_MIXED || precision == GPT2_BF16_SR; }
+
+// The parameter tensors every kernel reads in fp32 (LayerNorm gains and
+// biases, linear biases); the matrices are read from the bf16 copy in the
+// bf16 modes.
+inline bool fp32_read(int i) {
+    return !(i == P_WTE || i == P_WPE || i == P_QKVW || i == P_ATTPROJW || i == P_FCW || i == P_FCPROJW);
+}
 
 int validate(const gpt2_config* c) {
     if (!c) return fail(GPT2_EINVAL, "config is NULL");
@@ -110,6 +122,15 @@ Layout make_layout(const gpt2_config& c) {
     param_sizes(c, s);
     L.N = 0;
     for (int i = 0; i < NPARAM; i++) { L.poff[i] = L.N; L.N += s[i]; }
+    L.N32 = 0;
+    for (int i = 0; i < NPARAM; i++) {
+        if (c.precision == GPT2_BF16_SR && !fp32_read(i)) {
+            L.poff32[i] = SIZE_MAX;
+            continue;
+        }
+        L.poff32[i] = L.N32;
+        L.N32 += s[i];
+    }
     size_t total = 0;
     auto add = [&](size_t bytes) {
         size_t off = (total + 255) & ~(size_t)255;
@@ -118,7 +139,7 @@ Layout make_layout(const gpt2_config& c) {
     };
     const size_t A = is_bf16(c.precision) ? 2 : 4;  // activation bytes
     const size_t Ly = c.num_layers, C = c.channels, BT = (size_t)c.batch_size * c.seq_len;
-    L.params = add(4 * L.N);
+    L.params = add(4 * L.N32);
     L.grads = add(4 * L.N);
     L.m = add(4 * L.N);
     L.v = add(4 * L.N);
@@ -439,7 +460,8 @@ template <typename T> int forward_impl(gpt2_t* M, bool with_targets) {
     Acts<T> a(M);
     const float* p = M->params();
     const T* w = weights<T>(M);
-    const size_t* po = M->L.poff;
+    const size_t* po = M->L.poff;    // parameter offsets (gradients, bf16 copy)
+    const size_t* pf = M->L.poff32;  // offsets of the fp32 copy
     const size_t BTC = a.BTC;
     int* err = M->P<int>(M->L.err);
     int* tok = M->P<int>(M->L.tokens);
@@ -448,10 +470,10 @@ template <typename T> int forward_impl(gpt2_t* M, bool with_targets) {
         if (M->srmode()) {  // the bf16 tables are the parameters
             RUN("encoder_fwd", encoder_fwd<T>(a.encoded, tok, w + po[P_WTE], w + po[P_WPE], B, T_, C, V, err, s));
         } else {
-            RUN("encoder_fwd", encoder_fwd<T>(a.encoded, tok, p + po[P_WTE], p + po[P_WPE], B, T_, C, V, err, s));
+            RUN("encoder_fwd", encoder_fwd<T>(a.encoded, tok, p + pf[P_WTE], p + pf[P_WPE], B, T_, C, V, err, s));
         }
     } else {
-        RUN("encoder_fwd", encoder_fwd<T>(a.encoded, tok, p + po[P_WTE], p + po[P_WPE], B, T_, C, V, err, s));
+        RUN("encoder_fwd", encoder_fwd<T>(a.encoded, tok, p + pf[P_WTE], p + pf[P_WPE], B, T_, C, V, err, s));
     }
     const T* x = a.encoded;
     for (int l = 0; l < Ly; l++) {
@@ -465,21 +487,21 @@ template <typename T> int forward_impl(gpt2_t* M, bool with_targets) {
         T* res3 = a.res3 + l * BTC;
         const size_t lC = (size_t)l * C;
         RUN("layernorm_fwd", layernorm_fwd<T>(ln1, a.ln1m + (size_t)l * BT, a.ln1r + (size_t)l * BT, x,
-                                              p + po[P_LN1W] + lC, p + po[P_LN1B] + lC, BT, C, s));
-        RUN("gemm_fwd", lin_fwd<T>(M, qkv, ln1, w + po[P_QKVW] + lC * 3 * C, p + po[P_QKVB] + lC * 3, BT, 3 * C, C,
+                                              p + pf[P_LN1W] + lC, p + pf[P_LN1B] + lC, BT, C, s));
+        RUN("gemm_fwd", lin_fwd<T>(M, qkv, ln1, w + po[P_QKVW] + lC * 3 * C, p + pf[P_QKVB] + lC * 3, BT, 3 * C, C,
                                    EPI_BIAS));
         RUN("attention_fwd", attn_fwd<T>(atty, a.lse + (size_t)l * BT * NH, qkv, B, T_, C, NH, s));
-        RUN("gemm_fwd", lin_fwd<T>(M, res2, atty, w + po[P_ATTPROJW] + lC * C, p + po[P_ATTPROJB] + lC, BT, C, C,
+        RUN("gemm_fwd", lin_fwd<T>(M, res2, atty, w + po[P_ATTPROJW] + lC * C, p + pf[P_ATTPROJB] + lC, BT, C, C,
                                    EPI_BIAS_RESID, x));
         RUN("layernorm_fwd", layernorm_fwd<T>(ln2, a.ln2m + (size_t)l * BT, a.ln2r + (size_t)l * BT, res2,
-                                              p + po[P_LN2W] + lC, p + po[P_LN2B] + lC, BT, C, s));
-        RUN("gemm_fwd", lin_fwd<T>(M, fch, ln2, w + po[P_FCW] + lC * 4 * C, p + po[P_FCB] + lC * 4, BT, 4 * C, C,
+                                              p + pf[P_LN2W] + lC, p + pf[P_LN2B] + lC, BT, C, s));
+        RUN("gemm_fwd", lin_fwd<T>(M, fch, ln2, w + po[P_FCW] + lC * 4 * C, p + pf[P_FCB] + lC * 4, BT, 4 * C, C,
                                    EPI_BIAS_GELU, nullptr, fchg));
-        RUN("gemm_fwd", lin_fwd<T>(M, res3, fchg, w + po[P_FCPROJW] + lC * 4 * C, p + po[P_FCPROJB] + lC, BT, C,
+        RUN("gemm_fwd", lin_fwd<T>(M, res3, fchg, w + po[P_FCPROJW] + lC * 4 * C, p + pf[P_FCPROJB] + lC, BT, C,
                                    4 * C, EPI_BIAS_RESID, res2));
         x = res3;
     }
-    RUN("layernorm_fwd", layernorm_fwd<T>(a.lnf, a.lnfm, a.lnfr, x, p + po[P_LNFW], p + po[P_LNFB], BT, C, s));
+    RUN("layernorm_fwd", layernorm_fwd<T>(a.lnf, a.lnfm, a.lnfr, x, p + pf[P_LNFW], p + pf[P_LNFB], BT, C, s));
     RUN("gemm_classifier_fwd", lin_fwd<T>(M, a.logits, a.lnf, w + po[P_WTE], nullptr, BT, Vp, C, EPI_STORE));
     if (with_targets) {
         RUN("softmax_ce", softmax_ce<T>(a.logits, a.losses, M->P<int>(M->L.targets), BT, V, Vp, 1.0f / BT, err, s));
@@ -517,7 +539,8 @@ template <typename T> int backward_impl(gpt2_t* M) {
     const float* p = M->params();
     float* g = M->grads();
     const T* w = weights<T>(M);
-    const size_t* po = M->L.poff;
+    const size_t* po = M->L.poff;    // parameter offsets (gradients, bf16 copy)
+    const size_t* pf = M->L.poff32;  // offsets of the fp32 copy
     const size_t BTC = a.BTC;
     float* pfin = M->P<float>(M->L.part_fin);
     float* pln2 = M->P<float>(M->L.part_ln2);
@@ -546,7 +569,7 @@ template <typename T> int backward_impl(gpt2_t* M) {
     constexpr bool fused = std::is_same<T, bf16>::value;
     // first backward since gpt2_zero_grad: every gradient's one first writer stores
     const bool ow = M->grads_zero;
-    RUN("layernorm_bwd", layernorm_bwd<T>(G3(Ly - 1), nullptr, a.dmid, xlast, p + po[P_LNFW], a.lnfm, a.lnfr, pfin,
+    RUN("layernorm_bwd", layernorm_bwd<T>(G3(Ly - 1), nullptr, a.dmid, xlast, p + pf[P_LNFW], a.lnfm, a.lnfr, pfin,
                                           BT, C, true, s));
     for (int l = Ly - 1; l >= 0; l--) {
         const T* xin = l == 0 ? a.encoded : a.res3 + (size_t)(l - 1) * BTC;
@@ -566,7 +589,7 @@ template <typename T> int backward_impl(gpt2_t* M) {
         RUN("gemm_dx", lin_dx<T>(M, a.dmid, GF(l), w + po[P_FCW] + lC * 4 * C, BT, 4 * C, C, EPI_STORE));
         if (!fused) RUN("colsum", colsum_accum<T>(g + po[P_FCB] + lC * 4, GF(l), BT, 4 * C, pfc, s));
         // ln2: d res2 = d res3 + LN2'(d ln2)
-        RUN("layernorm_bwd", layernorm_bwd<T>(G2(l), G3(l), a.dmid, res2, p + po[P_LN2W] + lC, a.ln2m + (size_t)l * BT,
+        RUN("layernorm_bwd", layernorm_bwd<T>(G2(l), G3(l), a.dmid, res2, p + pf[P_LN2W] + lC, a.ln2m + (size_t)l * BT,
                                               a.ln2r + (size_t)l * BT, pln2, BT, C, true, s));
         jobs[nj++] = SumJob{{g + po[P_LN2W] + lC, g + po[P_LN2B] + lC, g + po[P_ATTPROJB] + lC}, pln2, Gln, C};
         // attproj: res2 = xin + atty Wap^T + b  ->  d atty
@@ -580,7 +603,7 @@ template <typename T> int backward_impl(gpt2_t* M) {
         if (!fused) RUN("colsum", colsum_accum<T>(g + po[P_QKVB] + lC * 3, GQ(l), BT, 3 * C, pqkv, s));
         // ln1: d xin = d res2 + LN1'(d ln1), whose column sums are the fcproj
         // bias gradient of the block below
-        RUN("layernorm_bwd", layernorm_bwd<T>(G3(l - 1), G2(l), a.dmid, xin, p + po[P_LN1W] + lC,
+        RUN("layernorm_bwd", layernorm_bwd<T>(G3(l - 1), G2(l), a.dmid, xin, p + pf[P_LN1W] + lC,
                                               a.ln1m + (size_t)l * BT, a.ln1r + (size_t)l * BT, pln1, BT, C, l > 0, s));
         jobs[nj++] = SumJob{{g + po[P_LN1W] + lC, g + po[P_LN1B] + lC, l > 0 ? g + po[P_FCPROJB] + lC - C : nullptr},
                             pln1, Gln, C};
@@ -655,6 +678,45 @@ int gpt2_plan(const gpt2_config* cfg, size_t* device_bytes) {
     return GPT2_OK;
 }
 
+namespace {
+// Staging for parameter copies in chunks: the d fch region of the kept output
+// gradients (only used inside gpt2_backward), whose first block alone holds
+// B*T*4C activations = B*T*2C floats or more.
+size_t staging_chunk(const gpt2_t* M) {
+    return (size_t)M->cfg.batch_size * M->cfg.seq_len * M->cfg.channels * 2;
+}
+
+// Set the parameters from N host floats: fp32 copy (and its bf16 rounding in
+// bf16 mixed mode); in the stochastic-rounding mode the bf16 parameters are
+// the nearest-even rounding (staged in chunks) and the packed fp32 copy their
+// widened values.  Synchronises the stream (the host array may go away).
+hipError_t upload_params(gpt2_t* M, const float* host) {
+    const Layout& L = M->L;
+    hipStream_t s = M->stream;
+    hipError_t e = hipSuccess;
+    if (!M->srmode()) {
+        e = hipMemcpyAsync(M->params(), host, 4 * L.N, hipMemcpyHostToDevice, s);
+        if (e == hipSuccess && M->bf16mode()) e = cast_bf16(M->P<bf16>(L.shadow), M->params(), L.N, s);
+    } else {
+        float* tmp = M->P<float>(L.gfch);
+        bf16* w = M->P<bf16>(L.shadow);
+        const size_t chunk = staging_chunk(M);
+        for (size_t o = 0; o < L.N && e == hipSuccess; o += chunk) {
+            const size_t k = std::min(chunk, L.N - o);
+            e = hipMemcpyAsync(tmp, host + o, 4 * k, hipMemcpyHostToDevice, s);
+            if (e == hipSuccess) e = cast_bf16(w + o, tmp, k, s);
+        }
+        size_t sz[NPARAM];
+        param_sizes(M->cfg, sz);
+        for (int i = 0; i < NPARAM && e == hipSuccess; i++)
+            if (fp32_read(i)) e = widen_f32<bf16>(M->params() + L.poff32[i], w + L.poff[i], sz[i], s);
+    }
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    return e;
+}
+
+}  // namespace
+
 int gpt2_build(const gpt2_config* cfg, uint64_t seed, void* device_buf, size_t bytes, void* hip_stream,
                gpt2_t** out) {
     int rc = validate(cfg);
@@ -680,14 +742,12 @@ int gpt2_build(const gpt2_config* cfg, uint64_t seed, void* device_buf, size_t b
     std::vector<float> host(L.N);
     init_params_host(*cfg, L, seed, host.data());
     hipStream_t s = M->stream;
-    hipError_t e = hipMemcpyAsync(M->params(), host.data(), 4 * L.N, hipMemcpyHostToDevice, s);
-    if (e == hipSuccess) e = hipMemsetAsync(M->grads(), 0, 4 * L.N, s);
+    hipError_t e = hipMemsetAsync(M->grads(), 0, 4 * L.N, s);
     if (e == hipSuccess) e = hipMemsetAsync(M->P<float>(L.m), 0, 4 * L.N, s);
     if (e == hipSuccess) e = hipMemsetAsync(M->P<float>(L.v), 0, 4 * L.N, s);
     if (e == hipSuccess) e = hipMemsetAsync(M->P<int>(L.err), 0, 64, s);
     if (e == hipSuccess) e = hipMemsetAsync(M->P<float>(L.scalars), 0, 64, s);
-    if (e == hipSuccess && M->bf16mode()) e = cast_bf16(M->P<bf16>(L.shadow), M->params(), L.N, s);
-    if (e == hipSuccess && M->srmode()) e = widen_f32<bf16>(M->params(), M->P<bf16>(L.shadow), L.N, s);
+    if (e == hipSuccess) e = upload_params(M, host.data());
     M->seed = seed;
     M->dw.resize(L.dw_n);
     dw_problems(*cfg, L, M->base, M->dw.data());
@@ -804,18 +864,18 @@ int gpt2_clip_grad_norm(gpt2_t* M, float max_norm, float* norm) {
 }
 
 namespace {
-// The parameter tensors the kernels read in fp32 (LayerNorm gains and
-// biases, linear biases): in the stochastic-rounding mode their fp32 copy
-// mirrors the bf16 parameters; adjacent tensors are merged.
+// The parameter tensors the kernels read in fp32: in the stochastic-rounding
+// mode their packed fp32 copy mirrors the bf16 parameters (flat range
+// [lo, hi) to packed offset dst; adjacent tensors are merged).
 SrRanges mirror_ranges(const gpt2_t* M) {
     size_t s[NPARAM];
     param_sizes(M->cfg, s);
     SrRanges r{};
     for (int i = 0; i < NPARAM; i++) {
-        if (i == P_WTE || i == P_WPE || i == P_QKVW || i == P_ATTPROJW || i == P_FCW || i == P_FCPROJW) continue;
-        const uint64_t lo = M->L.poff[i], hi = lo + s[i];
-        if (r.n > 0 && r.hi[r.n - 1] == lo) r.hi[r.n - 1] = hi;
-        else if (r.n < SR_RANGES_MAX) { r.lo[r.n] = lo; r.hi[r.n] = hi; r.n++; }
+        if (!fp32_read(i)) continue;
+        const uint64_t lo = M->L.poff[i], hi = lo + s[i], dst = M->L.poff32[i];
+        if (r.n > 0 && r.hi[r.n - 1] == lo && r.dst[r.n - 1] + (lo - r.lo[r.n - 1]) == dst) r.hi[r.n - 1] = hi;
+        else if (r.n < SR_RANGES_MAX) { r.lo[r.n] = lo; r.hi[r.n] = hi; r.dst[r.n] = dst; r.n++; }
     }
     return r;
 }
@@ -853,7 +913,19 @@ int gpt2_param_offsets(const gpt2_t* M, size_t offsets[16]) {
 
 int gpt2_copy_params(gpt2_t* M, float* dst) {
     if (!M || !dst) return fail(GPT2_EINVAL, "NULL argument");
-    if (M->srmode()) HIPCHK(widen_f32<bf16>(M->params(), M->P<bf16>(M->L.shadow), M->L.N, M->stream));
+    if (M->srmode()) {
+        // the bf16 parameters widened, staged in chunks
+        float* tmp = M->P<float>(M->L.gfch);
+        const bf16* w = M->P<bf16>(M->L.shadow);
+        const size_t chunk = staging_chunk(M);
+        for (size_t o = 0; o < M->L.N; o += chunk) {
+            const size_t k = std::min(chunk, M->L.N - o);
+            HIPCHK(widen_f32<bf16>(tmp, w + o, k, M->stream));
+            HIPCHK(hipMemcpyAsync(dst + o, tmp, 4 * k, hipMemcpyDeviceToHost, M->stream));
+            HIPCHK(hipStreamSynchronize(M->stream));
+        }
+        return GPT2_OK;
+    }
     HIPCHK(hipMemcpyAsync(dst, M->params(), 4 * M->L.N, hipMemcpyDeviceToHost, M->stream));
     HIPCHK(hipStreamSynchronize(M->stream));
     return GPT2_OK;
@@ -908,10 +980,7 @@ int gpt2_copy_losses(gpt2_t* M, float* dst) {
 
 int gpt2_set_params(gpt2_t* M, const float* src) {
     if (!M || !src) return fail(GPT2_EINVAL, "NULL argument");
-    HIPCHK(hipMemcpyAsync(M->params(), src, 4 * M->L.N, hipMemcpyHostToDevice, M->stream));
-    if (M->bf16mode()) HIPCHK(cast_bf16(M->P<bf16>(M->L.shadow), M->params(), M->L.N, M->stream));
-    if (M->srmode()) HIPCHK(widen_f32<bf16>(M->params(), M->P<bf16>(M->L.shadow), M->L.N, M->stream));
-    HIPCHK(hipStreamSynchronize(M->stream));
+    HIPCHK(upload_params(M, src));
     return GPT2_OK;
 }
 

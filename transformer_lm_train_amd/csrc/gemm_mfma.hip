@@ -243,19 +243,30 @@ template <int KB> DEVI int kswz(int r) {
 }
 DEVI int mnswz(int k) { return (k & 3) << 2; }
 
-// Per-lane element offsets of the NIW direct loads one wave issues per stage
-// for tile rows [r0, r0+R) of X; the k-step only adds a uniform offset.
-// Rows past the end re-read the last row (in bounds); they only feed
-// accumulators the epilogue never stores.
-template <int R, int NW, int KB, bool KCONTIG>
+// Per-lane element offsets of the direct loads one wave issues per stage for
+// tile rows [r0, r0+ROWS) of X (ROWS <= R, the staged tile's rows); the
+// k-step only adds a uniform offset.  A stage takes NIT wave instructions of
+// 1 KB.  When they split evenly over the waves, wave w issues instructions
+// w*NIW .. w*NIW+NIW-1; otherwise (a k-contiguous operand loaded for fewer
+// rows than staged: the 192-wide tiles' B) instruction q goes to wave q % NW,
+// so the first NIT % NW waves issue one more (count()).  Rows past the end
+// re-read the last row (in bounds); they only feed accumulators the epilogue
+// never stores.
+template <int R, int NW, int KB, bool KCONTIG, int ROWS = R>
 struct Dma {
-    static constexpr int NIW = R * KB / (512 * NW);
-    static_assert(NIW >= 1 && NIW * 512 * NW == R * KB, "tile vs waves");
+    static constexpr int NIT = ROWS * KB / 512;
+    static_assert(NIT >= 1 && NIT * 512 == ROWS * KB && ROWS <= R, "tile vs waves");
+    static constexpr bool EVEN = NIT % NW == 0;
+    static_assert(EVEN || KCONTIG, "partial row loads need a k-contiguous operand");
+    static constexpr int NIW = (NIT + NW - 1) / NW;  // most instructions one wave issues
+    static DEVI int slot(int wave, int i) { return EVEN ? wave * NIW + i : wave + NW * i; }
+    // instructions wave issues (uniform value)
+    static DEVI int count(int wave) { return EVEN ? NIW : (wave < NIT % NW ? NIW : NIW - 1); }
     uint32_t off[NIW];
     DEVI void init(int ld, int r0, int rows, int wave, int lane) {
 #pragma unroll
         for (int i = 0; i < NIW; i++) {
-            const int p = (wave * NIW + i) * 64 + lane;  // 16-byte chunk position in the tile
+            const int p = min(slot(wave, i), NIT - 1) * 64 + lane;  // 16-byte chunk position in the tile
             if constexpr (KCONTIG) {
                 constexpr int CPR = KB / 8;
                 const int r = p / CPR;
@@ -269,12 +280,16 @@ struct Dma {
             }
         }
     }
-    // kofs: k0 (k-contiguous) or k0 * ld (mn-contiguous)
-    DEVI void issue(uint16_t* tile, const bf16* X, int64_t kofs, int wave) const {
+    // kofs: k0 (k-contiguous) or k0 * ld (mn-contiguous).  CNT = count(wave),
+    // known at compile time in the caller's copy of the loop, so that no load
+    // sits under a branch (the compiler then keeps track of which stage array
+    // each direct load writes, and LDS reads of the others need not wait).
+    template <int CNT> DEVI void issue(uint16_t* tile, const bf16* X, int64_t kofs, int wave) const {
+        static_assert(CNT == NIW || (!EVEN && CNT == NIW - 1), "load count");
         const bf16* base = X + kofs;
 #pragma unroll
-        for (int i = 0; i < NIW; i++)
-            __builtin_amdgcn_global_load_lds((glb_void_t*)(base + off[i]), (lds_void_t*)(tile + (wave * NIW + i) * 512),
+        for (int i = 0; i < CNT; i++)
+            __builtin_amdgcn_global_load_lds((glb_void_t*)(base + off[i]), (lds_void_t*)(tile + slot(wave, i) * 512),
                                              16, 0, 0);
     }
 };
@@ -401,7 +416,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
         else if constexpr (j == 3) return sb3;
         else return sb4;
     };
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: per-wave load counts branch on it
     const int wm = wave / WAVES_N, wn = wave % WAVES_N;
 
     // Workgroup L (linear id, x fastest) runs on XCD L % 8.  Give each XCD a
@@ -458,66 +474,82 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
     const int kbeg = split * kchunk;
     const int nk = (min(g.K, kbeg + kchunk) - kbeg) / KB;
     const int klast = kbeg + (nk - 1) * KB;
-    Dma<BM, NW, KB, AK> da;
-    Dma<BN, NW, KB, BKC> db;
+    // a k-contiguous B is loaded for the BNV rows the tile uses; an
+    // mn-contiguous one for all BN (its k-rows are BN wide in LDS)
+    constexpr int BROWS = BKC ? BNV : BN;
+    typedef Dma<BM, NW, KB, AK> DmaA;
+    typedef Dma<BN, NW, KB, BKC, BROWS> DmaB;
+    DmaA da;
+    DmaB db;
     da.init(g.lda, m0, g.M, wave, lane);
     db.init(g.ldb, n0, g.N, wave, lane);
-    constexpr int LPS = Dma<BM, NW, KB, AK>::NIW + Dma<BN, NW, KB, BKC>::NIW;  // loads per thread per stage
-
-    auto dma = [&](uint16_t* ta, uint16_t* tb, int k0) {
-        da.issue(ta, A, AK ? (int64_t)k0 : (int64_t)k0 * g.lda, wave);
-        db.issue(tb, B, BKC ? (int64_t)k0 : (int64_t)k0 * g.ldb, wave);
-    };
-    // Step kt (stage kt % NS): wait for this wave's loads of k-step kt + 1
-    // (XPF) or kt, barrier (that k-step is then in LDS for every wave, and
-    // every wave is done with k-step kt - 1), load k-step kt + NS - 1 over
-    // k-step kt - 1, then the MFMAs of k-step kt.  XPF starts them from
-    // fragments already in registers and reads the first fragments of k-step
-    // kt + 1 at the end, at the price of one k-step less of load latency cover.
-    static_assert(!XPF || NS >= 3, "cross-barrier prefetch needs 3 stages");
+    // The main loop, for a wave that issues CB loads of B per stage (all
+    // waves issue DmaA::NIW of A).  Where the waves' B counts differ, each
+    // count gets its own copy of the loop (same barriers in both).
     bf16x8 fa[FM], fb[FN];
-    auto step = [&](auto J, int kt) {
-        constexpr int j = decltype(J)::value;
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm<(XPF ? NS - 3 : NS - 2) * LPS>());
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-        dma(stA(std::integral_constant<int, j + NS - 1>{}), stB(std::integral_constant<int, j + NS - 1>{}),
-            min(kbeg + (kt + NS - 1) * KB, klast));
-        mfma_step<BM, BN, KB, FM, FN, TM, TN, AK, BKC, XPF>(acc, fa, fb, stA(J), stB(J),
-                                                       stA(std::integral_constant<int, j + 1>{}),
-                                                       stB(std::integral_constant<int, j + 1>{}), wm, wn, lane);
-    };
-    typedef std::integral_constant<int, 0> I0;
-    typedef std::integral_constant<int, 1> I1;
-    typedef std::integral_constant<int, 2> I2;
-    typedef std::integral_constant<int, 3> I3;
-    typedef std::integral_constant<int, 4> I4;
+    auto main_loop = [&](auto CB_) {
+        constexpr int CB = decltype(CB_)::value;
+        constexpr int LPS = DmaA::NIW + CB;  // this wave's loads per stage
+        auto dma = [&](uint16_t* ta, uint16_t* tb, int k0) {
+            da.template issue<DmaA::NIW>(ta, A, AK ? (int64_t)k0 : (int64_t)k0 * g.lda, wave);
+            db.template issue<CB>(tb, B, BKC ? (int64_t)k0 : (int64_t)k0 * g.ldb, wave);
+        };
+        // Step kt (stage kt % NS): wait for this wave's loads of k-step kt + 1
+        // (XPF) or kt, barrier (that k-step is then in LDS for every wave, and
+        // every wave is done with k-step kt - 1), load k-step kt + NS - 1 over
+        // k-step kt - 1, then the MFMAs of k-step kt.  XPF starts them from
+        // fragments already in registers and reads the first fragments of k-step
+        // kt + 1 at the end, at the price of one k-step less of load latency cover.
+        static_assert(!XPF || NS >= 3, "cross-barrier prefetch needs 3 stages");
+        auto step = [&](auto J, int kt) {
+            constexpr int j = decltype(J)::value;
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm<(XPF ? NS - 3 : NS - 2) * LPS>());
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            dma(stA(std::integral_constant<int, j + NS - 1>{}), stB(std::integral_constant<int, j + NS - 1>{}),
+                min(kbeg + (kt + NS - 1) * KB, klast));
+            mfma_step<BM, BN, KB, FM, FN, TM, TN, AK, BKC, XPF>(acc, fa, fb, stA(J), stB(J),
+                                                           stA(std::integral_constant<int, j + 1>{}),
+                                                           stB(std::integral_constant<int, j + 1>{}), wm, wn, lane);
+        };
+        typedef std::integral_constant<int, 0> I0;
+        typedef std::integral_constant<int, 1> I1;
+        typedef std::integral_constant<int, 2> I2;
+        typedef std::integral_constant<int, 3> I3;
+        typedef std::integral_constant<int, 4> I4;
 
-    dma(sa0, sb0, kbeg);
-    dma(sa1, sb1, min(kbeg + KB, klast));
-    if constexpr (NS > 3) dma(sa2, sb2, min(kbeg + 2 * KB, klast));
-    if constexpr (NS > 4) dma(sa3, sb3, min(kbeg + 3 * KB, klast));
-    if constexpr (XPF) {
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm<(NS - 2) * LPS>());  // k-step 0
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
+        dma(sa0, sb0, kbeg);
+        dma(sa1, sb1, min(kbeg + KB, klast));
+        if constexpr (NS > 3) dma(sa2, sb2, min(kbeg + 2 * KB, klast));
+        if constexpr (NS > 4) dma(sa3, sb3, min(kbeg + 3 * KB, klast));
+        if constexpr (XPF) {
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm<(NS - 2) * LPS>());  // k-step 0
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
 #pragma unroll
-        for (int i = 0; i < FM; i++) fa[i] = frag_any<BM, KB, AK>(sa0, wm * TM + i * 32, 0, lane);
+            for (int i = 0; i < FM; i++) fa[i] = frag_any<BM, KB, AK>(sa0, wm * TM + i * 32, 0, lane);
 #pragma unroll
-        for (int jj = 0; jj < FN; jj++) fb[jj] = frag_any<BN, KB, BKC>(sb0, wn * TN + jj * 32, 0, lane);
+            for (int jj = 0; jj < FN; jj++) fb[jj] = frag_any<BN, KB, BKC>(sb0, wn * TN + jj * 32, 0, lane);
+        }
+        int kt = 0;
+        for (; kt + NS <= nk; kt += NS) {
+            step(I0{}, kt);
+            step(I1{}, kt + 1);
+            step(I2{}, kt + 2);
+            if constexpr (NS > 3) step(I3{}, kt + 3);
+            if constexpr (NS > 4) step(I4{}, kt + 4);
+        }
+        if (kt < nk) { step(I0{}, kt); kt++; }
+        if (kt < nk) { step(I1{}, kt); kt++; }
+        if constexpr (NS > 3) if (kt < nk) { step(I2{}, kt); kt++; }
+        if constexpr (NS > 4) if (kt < nk) { step(I3{}, kt); kt++; }
+    };
+    if constexpr (DmaB::EVEN) {
+        main_loop(std::integral_constant<int, DmaB::NIW>{});
+    } else {
+        if (DmaB::count(wave) == DmaB::NIW) main_loop(std::integral_constant<int, DmaB::NIW>{});
+        else main_loop(std::integral_constant<int, DmaB::NIW - 1>{});
     }
-    int kt = 0;
-    for (; kt + NS <= nk; kt += NS) {
-        step(I0{}, kt);
-        step(I1{}, kt + 1);
-        step(I2{}, kt + 2);
-        if constexpr (NS > 3) step(I3{}, kt + 3);
-        if constexpr (NS > 4) step(I4{}, kt + 4);
-    }
-    if (kt < nk) { step(I0{}, kt); kt++; }
-    if (kt < nk) { step(I1{}, kt); kt++; }
-    if constexpr (NS > 3) if (kt < nk) { step(I2{}, kt); kt++; }
-    if constexpr (NS > 4) if (kt < nk) { step(I3{}, kt); kt++; }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());  // no load may still be writing LDS at exit
 
     // The stage buffers become the epilogue's per-wave regions once every

@@ -252,7 +252,24 @@ DEVI int mnswz(int k) { return (k & 3) << 2; }
 // so the first NIT % NW waves issue one more (count()).  Rows past the end
 // re-read the last row (in bounds); they only feed accumulators the epilogue
 // never stores.
-template <int R, int NW, int KB, bool KCONTIG, int ROWS = R>
+// One 16-byte direct load per lane through a buffer resource over the
+// operand (base: the operand at the stage's k offset; byte_off: the lane's
+// offset).  The k offset then lives in the resource's scalar base and the
+// lanes carry 32-bit offsets instead of 64-bit addresses.  dword3 0x00020000:
+// raw 32-bit data format, no swizzle; num_records at its maximum (every
+// offset here is in bounds).  The builtins exist only in the device pass.
+DEVI void buffer_load_lds16(const bf16* base, uint32_t byte_off, uint16_t* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(base), (short)0, -1, 0x00020000);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)lds, 16, byte_off, 0, 0, 0);
+#endif
+}
+
+// BUF: buffer loads (buffer_load_lds16) instead of global ones; measured per
+// operand form in the training step: faster for both operands of the forward
+// products and for every mn-contiguous operand, slower for the k-contiguous
+// A of the backward-data products, which keeps global loads.
+template <int R, int NW, int KB, bool KCONTIG, int ROWS = R, bool BUF = false>
 struct Dma {
     static constexpr int NIT = ROWS * KB / 512;
     static_assert(NIT >= 1 && NIT * 512 == ROWS * KB && ROWS <= R, "tile vs waves");
@@ -288,9 +305,13 @@ struct Dma {
         static_assert(CNT == NIW || (!EVEN && CNT == NIW - 1), "load count");
         const bf16* base = X + kofs;
 #pragma unroll
-        for (int i = 0; i < CNT; i++)
-            __builtin_amdgcn_global_load_lds((glb_void_t*)(base + off[i]), (lds_void_t*)(tile + slot(wave, i) * 512),
-                                             16, 0, 0);
+        for (int i = 0; i < CNT; i++) {
+            if constexpr (BUF)
+                buffer_load_lds16(base, off[i] * 2u, tile + slot(wave, i) * 512);
+            else
+                __builtin_amdgcn_global_load_lds((glb_void_t*)(base + off[i]),
+                                                 (lds_void_t*)(tile + slot(wave, i) * 512), 16, 0, 0);
+        }
     }
 };
 
@@ -477,8 +498,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
     // a k-contiguous B is loaded for the BNV rows the tile uses; an
     // mn-contiguous one for all BN (its k-rows are BN wide in LDS)
     constexpr int BROWS = BKC ? BNV : BN;
-    typedef Dma<BM, NW, KB, AK> DmaA;
-    typedef Dma<BN, NW, KB, BKC, BROWS> DmaB;
+    typedef Dma<BM, NW, KB, AK, BM, !(AK && !BKC)> DmaA;  // global loads for the A of dY W only
+    typedef Dma<BN, NW, KB, BKC, BROWS, true> DmaB;
     DmaA da;
     DmaB db;
     da.init(g.lda, m0, g.M, wave, lane);

@@ -97,27 +97,36 @@ DEVI int aswz(int r) {
 // rows [r0, r0+64) x 64 channels of a [*, ld] matrix into a swizzled tile;
 // each of the 4 waves issues 2 loads of 1 KB (8 rows each).  Callers stream
 // whole 64-row blocks of a sequence whose length is a multiple of 64, so
-// every row read exists.  The per-lane source addresses of the two loads are
-// computed once (row 0 of the wave's 8-row blocks); the row offset r0 is
-// wave-uniform.
+// every row read exists.  The loads go through a buffer resource whose base
+// is the matrix at row r0 (wave-uniform), and each lane carries the 32-bit
+// byte offsets of its two 16-byte chunks, computed once (row 0 of the wave's
+// 8-row blocks): measured faster than per-lane 64-bit addresses (forward
+// 3%, backward 2%).  dword3 0x00020000: raw 32-bit data format;
+// num_records at its maximum (every offset here is in bounds).
 struct LanePtr {
-    const bf16* p[2];
+    const bf16* base;
+    uint32_t off[2];  // bytes from base
 };
 DEVI LanePtr dma_lane_ptr(const bf16* base, int ld, int wave, int lane) {
     LanePtr lp;
+    lp.base = base;
 #pragma unroll
     for (int i = 0; i < 2; i++) {
         const int row = wave * 16 + i * 8 + (lane >> 3);  // tile row this lane lands in
         const int c = (lane & 7) ^ aswz(row);             // chunk landing in slot lane & 7
-        lp.p[i] = base + row * ld + c * 8;
+        lp.off[i] = (uint32_t)(row * ld + c * 8) * 2u;
     }
     return lp;
 }
 DEVI void dma_tile(bf16* tile, const LanePtr& src, int ld, int r0, int wave) {
+#if defined(__HIP_DEVICE_COMPILE__)  // the buffer builtins exist only in the device pass
+    __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(src.base + (int64_t)r0 * ld), (short)0, -1, 0x00020000);
 #pragma unroll
     for (int i = 0; i < 2; i++)
-        __builtin_amdgcn_global_load_lds((glb_void_t*)(src.p[i] + r0 * ld), (lds_void_t*)(tile + (wave * 2 + i) * 512),
-                                         16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(tile + (wave * 2 + i) * 512), 16, src.off[i], 0, 0,
+                                                 0);
+#endif
 }
 
 // 8 consecutive channels chunk*8.. of tile row `row` (one 16-byte read)

@@ -246,7 +246,7 @@ __global__ __launch_bounds__(1024) void enc_chunk_kernel(const T* dx, const int*
 // one wave per sorted slot; at an id's first slot, its pieces go into dwte
 __global__ __launch_bounds__(256) void enc_segment_kernel(const int* sid, const int* tot, const float* Q, int BT,
                                                           int V, int C, float* dwte) {
-    const int k = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int k = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     if (k >= BT) return;
     const int id = sid[k];
     if (id >= V || (k > 0 && sid[k - 1] == id)) return;
@@ -321,7 +321,9 @@ __global__ __launch_bounds__(256) void layernorm_fwd_kernel(T* out, float* mean,
                                                             const float* w, const float* b, int N, int C) {
     constexpr int VN = Vec16<T>::N;
     const int lane = threadIdx.x & 63;
-    const int row0 = blockIdx.x * 4 * R + (threadIdx.x >> 6);
+    // the wave index read into a scalar register: row addresses are then a
+    // scalar base plus small lane offsets
+    const int row0 = blockIdx.x * 4 * R + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int chunks = C / VN;
     Vec16<T> q[R][MAXV];
 #pragma unroll
@@ -427,7 +429,7 @@ void layernorm_bwd_kernel(T* dout, const T* din, const T* dy, const T* x, const 
                           const float* rstd, float* partial, int N, int C) {
     constexpr int VN = Vec16<T>::N;
     extern __shared__ float smem[];  // [4][NP][C]
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform
     const int chunks = C / VN;
     const int step = gridDim.x * 4;  // a wave's rows: row0, row0 + step, ...
     const int row0 = blockIdx.x * 4 + wv;

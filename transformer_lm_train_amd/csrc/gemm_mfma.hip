@@ -226,8 +226,8 @@ template <int N> constexpr int vmcnt_imm() { return (N & 15) | ((N >> 4) << 14) 
 //    slot c ^ kswz(r), which puts the 16 rows read by 16 lanes (one chunk
 //    each) in 16 distinct 16-byte bank groups.  Fragment = one ds_read_b128.
 //  - mn-contiguous operand: LDS [k][R] (R = tile rows); chunk c of k-row k sits
-//    in slot c ^ ((k & 3) << 2), so the four k-rows a transposing read touches
-//    at once land in four distinct 64-byte quarters.  Fragment = two
+//    in slot mn_slot<R>(c, k), which puts the four k-rows a transposing read
+//    touches at once in four distinct 64-byte quarters.  Fragment = two
 //    ds_read_b64_tr_b16: within each 16-lane group that instruction hands
 //    lane i element (i % 4) of the 8-byte read of lane 4e + i/4 as its element
 //    e; so when lane j reads X[k0 + j/4][m0 + 4(j%4) .. +3], lane i receives
@@ -242,16 +242,30 @@ template <int KB> DEVI int kswz(int r) {
     else return (r >> 2) & 3;                     // 4 rows of 64 B per bank window
 }
 DEVI int mnswz(int k) { return (k & 3) << 2; }
+// Slot of 16-byte chunk c of k-row k in an mn-contiguous tile R elements wide.
+// R a multiple of 128 (rows a multiple of 256 bytes): c ^ ((k & 3) << 2), the
+// four k-rows a transposing read touches at once in four distinct 64-byte
+// quarters.
+// R = 192 (24 chunks, 384-byte rows, which already put k-rows k and k+1 128
+// bytes apart in the 256-byte bank window): chunks rotated by 4 when bit 1 of
+// k is set, which moves k-rows k+2, k+3 by another 64 bytes; the four rows
+// land at 0, 128, 64, 192 (or, past the wrap, 0, 128, 192, 64) bytes.
+template <int R> DEVI int mn_slot(int c, int k) {
+    static_assert(R % 128 == 0 || R == 192, "mn-contiguous tile width");
+    if constexpr (R != 192) return c ^ mnswz(k);
+    else {
+        const int s = c + ((k & 2) << 1);
+        return s >= 24 ? s - 24 : s;
+    }
+}
+template <int R> DEVI int mn_chunk(int s, int k) {  // inverse of mn_slot
+    if constexpr (R != 192) return s ^ mnswz(k);
+    else {
+        const int c = s - ((k & 2) << 1);
+        return c < 0 ? c + 24 : c;
+    }
+}
 
-// Per-lane element offsets of the direct loads one wave issues per stage for
-// tile rows [r0, r0+ROWS) of X (ROWS <= R, the staged tile's rows); the
-// k-step only adds a uniform offset.  A stage takes NIT wave instructions of
-// 1 KB.  When they split evenly over the waves, wave w issues instructions
-// w*NIW .. w*NIW+NIW-1; otherwise (a k-contiguous operand loaded for fewer
-// rows than staged: the 192-wide tiles' B) instruction q goes to wave q % NW,
-// so the first NIT % NW waves issue one more (count()).  Rows past the end
-// re-read the last row (in bounds); they only feed accumulators the epilogue
-// never stores.
 // One 16-byte direct load per lane through a buffer resource over the
 // operand (base: the operand at the stage's k offset; byte_off: the lane's
 // offset).  The k offset then lives in the resource's scalar base and the
@@ -265,6 +279,15 @@ DEVI void buffer_load_lds16(const bf16* base, uint32_t byte_off, uint16_t* lds) 
 #endif
 }
 
+// Per-lane element offsets of the direct loads one wave issues per stage for
+// tile rows [r0, r0+ROWS) of X; the k-step only adds a uniform offset.  A
+// k-contiguous tile is [row][KB] (R rows staged, ROWS <= R loaded); an
+// mn-contiguous one [k][R] (ROWS == R: its k-rows are R wide in LDS).  A
+// stage takes NIT wave instructions of 1 KB.  When they split evenly over the
+// waves, wave w issues instructions w*NIW .. w*NIW+NIW-1; otherwise (the
+// 192-wide tiles' B) instruction q goes to wave q % NW, so the first NIT % NW
+// waves issue one more (count()).  Rows past the end re-read the last row (in
+// bounds); they only feed accumulators the epilogue never stores.
 // BUF: buffer loads (buffer_load_lds16) instead of global ones; measured per
 // operand form in the training step: faster for both operands of the forward
 // products and for every mn-contiguous operand, slower for the k-contiguous
@@ -272,9 +295,9 @@ DEVI void buffer_load_lds16(const bf16* base, uint32_t byte_off, uint16_t* lds) 
 template <int R, int NW, int KB, bool KCONTIG, int ROWS = R, bool BUF = false>
 struct Dma {
     static constexpr int NIT = ROWS * KB / 512;
-    static_assert(NIT >= 1 && NIT * 512 == ROWS * KB && ROWS <= R, "tile vs waves");
+    static_assert(NIT >= 1 && NIT * 512 == ROWS * KB && ROWS <= R && (KCONTIG || ROWS == R), "tile vs waves");
     static constexpr bool EVEN = NIT % NW == 0;
-    static_assert(EVEN || KCONTIG, "partial row loads need a k-contiguous operand");
+
     static constexpr int NIW = (NIT + NW - 1) / NW;  // most instructions one wave issues
     static DEVI int slot(int wave, int i) { return EVEN ? wave * NIW + i : wave + NW * i; }
     // instructions wave issues (uniform value)
@@ -292,7 +315,7 @@ struct Dma {
             } else {
                 constexpr int CPR = R / 8;
                 const int k = p / CPR;
-                const int c = (p % CPR) ^ mnswz(k);
+                const int c = mn_chunk<R>(p % CPR, k);
                 off[i] = (uint32_t)(k * ld + min(r0 + c * 8, rows - 8));
             }
         }
@@ -326,8 +349,8 @@ DEVI bf16x8 frag_any(const uint16_t* tile, int row0, int kk, int lane) {
         const int j = lane & 15, g = lane >> 4;
         const int m = row0 + 16 * (g & 1) + 4 * (j & 3);
         const int k = kk + (g >> 1) * 8 + (j >> 2);
-        const int o0 = k * R + ((((m >> 3) ^ mnswz(k)) << 3) | (m & 7));
-        const int o1 = (k + 4) * R + ((((m >> 3) ^ mnswz(k + 4)) << 3) | (m & 7));
+        const int o0 = k * R + ((mn_slot<R>(m >> 3, k) << 3) | (m & 7));
+        const int o1 = (k + 4) * R + ((mn_slot<R>(m >> 3, k + 4) << 3) | (m & 7));
         i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + o0));
         i16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + o1));
         i16x4 xy[2] = {x, y};
@@ -495,11 +518,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
     const int kbeg = split * kchunk;
     const int nk = (min(g.K, kbeg + kchunk) - kbeg) / KB;
     const int klast = kbeg + (nk - 1) * KB;
-    // a k-contiguous B is loaded for the BNV rows the tile uses; an
-    // mn-contiguous one for all BN (its k-rows are BN wide in LDS)
-    constexpr int BROWS = BKC ? BNV : BN;
+    // B is loaded for the BNV rows (columns) the tile uses: k-contiguous into
+    // the [BN][KB] stage, mn-contiguous as [KB][BNV] (pitch BPITCH)
+    constexpr int BPITCH = BKC ? BN : BNV;
     typedef Dma<BM, NW, KB, AK, BM, !(AK && !BKC)> DmaA;  // global loads for the A of dY W only
-    typedef Dma<BN, NW, KB, BKC, BROWS, true> DmaB;
+    typedef Dma<BPITCH, NW, KB, BKC, BNV, true> DmaB;
     DmaA da;
     DmaB db;
     da.init(g.lda, m0, g.M, wave, lane);
@@ -529,7 +552,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
             asm volatile("" ::: "memory");
             dma(stA(std::integral_constant<int, j + NS - 1>{}), stB(std::integral_constant<int, j + NS - 1>{}),
                 min(kbeg + (kt + NS - 1) * KB, klast));
-            mfma_step<BM, BN, KB, FM, FN, TM, TN, AK, BKC, XPF>(acc, fa, fb, stA(J), stB(J),
+            mfma_step<BM, BPITCH, KB, FM, FN, TM, TN, AK, BKC, XPF>(acc, fa, fb, stA(J), stB(J),
                                                            stA(std::integral_constant<int, j + 1>{}),
                                                            stB(std::integral_constant<int, j + 1>{}), wm, wn, lane);
         };
@@ -550,7 +573,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
 #pragma unroll
             for (int i = 0; i < FM; i++) fa[i] = frag_any<BM, KB, AK>(sa0, wm * TM + i * 32, 0, lane);
 #pragma unroll
-            for (int jj = 0; jj < FN; jj++) fb[jj] = frag_any<BN, KB, BKC>(sb0, wn * TN + jj * 32, 0, lane);
+            for (int jj = 0; jj < FN; jj++) fb[jj] = frag_any<BPITCH, KB, BKC>(sb0, wn * TN + jj * 32, 0, lane);
         }
         int kt = 0;
         for (; kt + NS <= nk; kt += NS) {

@@ -644,8 +644,11 @@ hipError_t layernorm_bwd(T* dout, const T* din, const T* dy, const T* x, const f
 #define LN_BWD(V, R)                                                                                               \
     (dsum ? layernorm_bwd_kernel<T, V, 3, R><<<G, 256, lds, s>>>(dout, din, dy, x, w, mean, rstd, partial, N, C)  \
           : layernorm_bwd_kernel<T, V, 2, R><<<G, 256, lds, s>>>(dout, din, dy, x, w, mean, rstd, partial, N, C))
+    // two chunks per lane (C = 768 in bf16): one row at a time, its successor
+    // requested first, measured ~5% faster than two (more waves per SIMD or a
+    // larger grid gain nothing and add partial rows)
     if (per_lane <= 1) LN_BWD(1, 2);
-    else if (per_lane <= 2) LN_BWD(2, 2);
+    else if (per_lane <= 2) LN_BWD(2, 1);
     else if (per_lane <= 4) LN_BWD(4, 2);
     else LN_BWD(8, 1);
 #undef LN_BWD

@@ -118,8 +118,8 @@ struct SumJob {
     const float* partial;
     int G, C;
 };
-constexpr int SUM_JOBS_MAX = 6;
-// Runs up to SUM_JOBS_MAX jobs in one launch; overwrite: out[k][c] = the sum.
+constexpr int SUM_JOBS_MAX = 64;
+// Runs n jobs, up to SUM_JOBS_MAX per launch; overwrite: out[k][c] = the sum.
 hipError_t sum_partials_batch(const SumJob* jobs, int n, bool overwrite, hipStream_t s);
 hipError_t sum_partials(float* out0, float* out1, float* out2, const float* partial, int G, int C, hipStream_t s);
 // dbias[n] += sum_m dy[m][n] (deterministic two-stage sum via partial).

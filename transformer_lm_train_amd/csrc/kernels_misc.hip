@@ -568,8 +568,10 @@ struct SumBatch {
 
 __global__ __launch_bounds__(1024) void sum_partials_kernel(SumBatch bt) {
     __shared__ float red[3][64][17];
+    // the job whose block range holds this block: the last k with start[k] <= blockIdx.x
     int k = 0;
-    while (k + 1 < bt.n && (int)blockIdx.x >= bt.start[k + 1]) k++;
+    for (int w = SUM_JOBS_MAX / 2; w >= 1; w >>= 1)
+        if (k + w < bt.n && (int)blockIdx.x >= bt.start[k + w]) k += w;
     const SumJob& jb = bt.job[k];
     const int G = jb.G, C = jb.C;
     const float* partial = jb.partial;
@@ -613,19 +615,24 @@ __global__ __launch_bounds__(1024) void sum_partials_kernel(SumBatch bt) {
 }
 
 hipError_t sum_partials_batch(const SumJob* jobs, int n, bool overwrite, hipStream_t s) {
-    if (n < 0 || n > SUM_JOBS_MAX) return hipErrorInvalidValue;
-    if (n == 0) return hipSuccess;
-    SumBatch bt{};
-    bt.n = n;
-    bt.overwrite = overwrite ? 1 : 0;
-    bt.start[0] = 0;
-    for (int i = 0; i < n; i++) {
+    if (n < 0) return hipErrorInvalidValue;
+    for (int i = 0; i < n; i++)
         if (!jobs[i].out[0] || !jobs[i].partial || jobs[i].G <= 0 || jobs[i].C <= 0) return hipErrorInvalidValue;
-        bt.job[i] = jobs[i];
-        bt.start[i + 1] = bt.start[i] + (int)cdiv(jobs[i].C, 16);
+    for (int j0 = 0; j0 < n; j0 += SUM_JOBS_MAX) {
+        const int m = std::min(n - j0, SUM_JOBS_MAX);
+        SumBatch bt{};
+        bt.n = m;
+        bt.overwrite = overwrite ? 1 : 0;
+        bt.start[0] = 0;
+        for (int i = 0; i < m; i++) {
+            bt.job[i] = jobs[j0 + i];
+            bt.start[i + 1] = bt.start[i] + (int)cdiv(jobs[j0 + i].C, 16);
+        }
+        sum_partials_kernel<<<bt.start[m], 1024, 0, s>>>(bt);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
     }
-    sum_partials_kernel<<<bt.start[n], 1024, 0, s>>>(bt);
-    return hipGetLastError();
+    return hipSuccess;
 }
 
 hipError_t sum_partials(float* out0, float* out1, float* out2, const float* partial, int G, int C, hipStream_t s) {

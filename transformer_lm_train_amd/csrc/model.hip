@@ -75,6 +75,7 @@ struct Layout {
     size_t gres3, gres2, gfch, gqkv, dmid, attD, part_fin, part_ln2, part_ln1, part_fc, part_qkv, norm_partial,
         scalars, err, tokens, targets, splitk, dw_probs, dw_tiles, dw_split_tiles, dw_ws, encws;
     size_t splitk_bytes;
+    size_t part_stride_ln, part_stride_fc, part_stride_qkv;  // floats between blocks' partial sets
     int dw_n, dw_ntiles;  // weight-gradient products and their grouped tile list (before scheduling)
     size_t total;
 };
@@ -174,8 +175,8 @@ Layout make_layout(const gpt2_config& c) {
     L.attD = add(2 * 4 * BT * c.num_heads);  // D and the base-2 lse of every attention row
     {
         // Partial rows of the fixed-order column sums of the backward pass,
-        // one region per producer so that a layer's sums can run as one
-        // batch at its end: the final LN and the two LNs of a block (3 sums
+        // one region per producer and block, so that every block's sums run
+        // in one batch after the block loop: the final LN and the two LNs of a block (3 sums
         // per channel, up to 512 rows), the fc bias (the GELU' product's 4
         // rows per 256 tokens, 4C wide, or the stand-alone column sums' 256
         // rows in fp32 mode) and the qkv bias (attention's row per
@@ -184,10 +185,13 @@ Layout make_layout(const gpt2_config& c) {
         const size_t fc = std::max<size_t>(cdiv(BT, 256) * 4, 256) * 4 * C;
         const size_t qk = std::max<size_t>((size_t)c.batch_size * cdiv(c.seq_len, 128), 256) * 3 * C;
         L.part_fin = add(4 * ln);
-        L.part_ln2 = add(4 * ln);
-        L.part_ln1 = add(4 * ln);
-        L.part_fc = add(4 * fc);
-        L.part_qkv = add(4 * qk);
+        L.part_ln2 = add(4 * ln * Ly);
+        L.part_ln1 = add(4 * ln * Ly);
+        L.part_fc = add(4 * fc * Ly);
+        L.part_qkv = add(4 * qk * Ly);
+        L.part_stride_ln = ln;
+        L.part_stride_fc = fc;
+        L.part_stride_qkv = qk;
     }
     L.norm_partial = add(4 * 1024);
     L.scalars = add(64);
@@ -543,10 +547,10 @@ template <typename T> int backward_impl(gpt2_t* M) {
     const size_t* pf = M->L.poff32;  // offsets of the fp32 copy
     const size_t BTC = a.BTC;
     float* pfin = M->P<float>(M->L.part_fin);
-    float* pln2 = M->P<float>(M->L.part_ln2);
-    float* pln1 = M->P<float>(M->L.part_ln1);
-    float* pfc = M->P<float>(M->L.part_fc);
-    float* pqkv = M->P<float>(M->L.part_qkv);
+    float* pln2_all = M->P<float>(M->L.part_ln2);
+    float* pln1_all = M->P<float>(M->L.part_ln1);
+    float* pfc_all = M->P<float>(M->L.part_fc);
+    float* pqkv_all = M->P<float>(M->L.part_qkv);
     float* attD = M->P<float>(M->L.attD);
     const int Gln = layernorm_bwd_blocks(BT);
     // output gradients kept for the weight-gradient products
@@ -560,7 +564,7 @@ template <typename T> int backward_impl(gpt2_t* M) {
     const T* xlast = a.res3 + (size_t)(Ly - 1) * BTC;
     // Bias gradients are column sums of the output gradients, taken as
     // partial rows by the kernel that produces each gradient and summed in a
-    // fixed order, one batched launch per layer: attproj and fcproj from the
+    // fixed order, in one batch after the block loop: attproj and fcproj from the
     // LN backward that writes the residual-stream gradient they see (LN2 of
     // the block, and the final LN or LN1 of the block above); in bf16 mode fc
     // from the GELU' product and qkv from the attention backward (fp32 mode:
@@ -569,6 +573,8 @@ template <typename T> int backward_impl(gpt2_t* M) {
     constexpr bool fused = std::is_same<T, bf16>::value;
     // first backward since gpt2_zero_grad: every gradient's one first writer stores
     const bool ow = M->grads_zero;
+    std::vector<SumJob> jobs;  // every block's sums, run in one batch after the block loop
+    jobs.reserve(4 * (size_t)Ly + 1);
     RUN("layernorm_bwd", layernorm_bwd<T>(G3(Ly - 1), nullptr, a.dmid, xlast, p + pf[P_LNFW], a.lnfm, a.lnfr, pfin,
                                           BT, C, true, s));
     for (int l = Ly - 1; l >= 0; l--) {
@@ -578,26 +584,28 @@ template <typename T> int backward_impl(gpt2_t* M) {
         const T* res2 = a.res2 + l * BTC;
         const T* fch = a.fch + l * BTC * 4;
         const size_t lC = (size_t)l * C;
-        SumJob jobs[SUM_JOBS_MAX];
-        int nj = 0;
-        if (l == Ly - 1) jobs[nj++] = SumJob{{g + po[P_LNFW], g + po[P_LNFB], g + po[P_FCPROJB] + lC}, pfin, Gln, C};
+        float* pln2 = pln2_all + l * M->L.part_stride_ln;
+        float* pln1 = pln1_all + l * M->L.part_stride_ln;
+        float* pfc = pfc_all + l * M->L.part_stride_fc;
+        float* pqkv = pqkv_all + l * M->L.part_stride_qkv;
+        if (l == Ly - 1) jobs.push_back(SumJob{{g + po[P_LNFW], g + po[P_LNFB], g + po[P_FCPROJB] + lC}, pfin, Gln, C});
         // fcproj: res3 = res2 + fchg Wfp^T + b  ->  d fch = (d res3 Wfp) * GELU'(fch)
         RUN("gemm_dx", lin_dx<T>(M, GF(l), G3(l), w + po[P_FCPROJW] + lC * 4 * C, BT, C, 4 * C, EPI_GELU_BWD, fch,
                                  fused ? pfc : nullptr));
-        if (fused) jobs[nj++] = SumJob{{g + po[P_FCB] + lC * 4}, pfc, gemm_colsum_rows(BT, 4 * C), 4 * C};
+        if (fused) jobs.push_back(SumJob{{g + po[P_FCB] + lC * 4}, pfc, gemm_colsum_rows(BT, 4 * C), 4 * C});
         // fc: fch = ln2 Wfc^T + b  ->  d ln2
         RUN("gemm_dx", lin_dx<T>(M, a.dmid, GF(l), w + po[P_FCW] + lC * 4 * C, BT, 4 * C, C, EPI_STORE));
         if (!fused) RUN("colsum", colsum_accum<T>(g + po[P_FCB] + lC * 4, GF(l), BT, 4 * C, pfc, s));
         // ln2: d res2 = d res3 + LN2'(d ln2)
         RUN("layernorm_bwd", layernorm_bwd<T>(G2(l), G3(l), a.dmid, res2, p + pf[P_LN2W] + lC, a.ln2m + (size_t)l * BT,
                                               a.ln2r + (size_t)l * BT, pln2, BT, C, true, s));
-        jobs[nj++] = SumJob{{g + po[P_LN2W] + lC, g + po[P_LN2B] + lC, g + po[P_ATTPROJB] + lC}, pln2, Gln, C};
+        jobs.push_back(SumJob{{g + po[P_LN2W] + lC, g + po[P_LN2B] + lC, g + po[P_ATTPROJB] + lC}, pln2, Gln, C});
         // attproj: res2 = xin + atty Wap^T + b  ->  d atty
         RUN("gemm_dx", lin_dx<T>(M, a.dmid, G2(l), w + po[P_ATTPROJW] + lC * C, BT, C, C, EPI_STORE));
         // attention: d atty -> d qkv
         RUN("attention_bwd", attn_bwd<T>(GQ(l), a.dmid, qkv, atty, a.lse + (size_t)l * BT * NH, attD, B, T_, C, NH,
                                          fused ? pqkv : nullptr, s));
-        if (fused) jobs[nj++] = SumJob{{g + po[P_QKVB] + lC * 3}, pqkv, flash_attention_bias_rows(B, T_), 3 * C};
+        if (fused) jobs.push_back(SumJob{{g + po[P_QKVB] + lC * 3}, pqkv, flash_attention_bias_rows(B, T_), 3 * C});
         // qkv: qkv = ln1 Wqkv^T + b  ->  d ln1
         RUN("gemm_dx", lin_dx<T>(M, a.dmid, GQ(l), w + po[P_QKVW] + lC * 3 * C, BT, 3 * C, C, EPI_STORE));
         if (!fused) RUN("colsum", colsum_accum<T>(g + po[P_QKVB] + lC * 3, GQ(l), BT, 3 * C, pqkv, s));
@@ -605,10 +613,10 @@ template <typename T> int backward_impl(gpt2_t* M) {
         // bias gradient of the block below
         RUN("layernorm_bwd", layernorm_bwd<T>(G3(l - 1), G2(l), a.dmid, xin, p + pf[P_LN1W] + lC,
                                               a.ln1m + (size_t)l * BT, a.ln1r + (size_t)l * BT, pln1, BT, C, l > 0, s));
-        jobs[nj++] = SumJob{{g + po[P_LN1W] + lC, g + po[P_LN1B] + lC, l > 0 ? g + po[P_FCPROJB] + lC - C : nullptr},
-                            pln1, Gln, C};
-        RUN("bias_sums", sum_partials_batch(jobs, nj, ow, s));
+        jobs.push_back(SumJob{{g + po[P_LN1W] + lC, g + po[P_LN1B] + lC, l > 0 ? g + po[P_FCPROJB] + lC - C : nullptr},
+                              pln1, Gln, C});
     }
+    RUN("bias_sums", sum_partials_batch(jobs.data(), (int)jobs.size(), ow, s));
     RUN("gemm_dw", weight_grads<T>(M, ow));  // the classifier's product writes every wte row first
     RUN("encoder_bwd", encoder_bwd<T>(g + po[P_WTE], g + po[P_WPE], G3(-1), M->P<int>(M->L.tokens), B, T_,
                                       c.max_seq_len, C, c.vocab_size, M->base + M->L.encws, ow, s));

@@ -38,6 +38,27 @@ template <typename T> DEVI void st16(T* p, const Vec16<T>& r) {
     *reinterpret_cast<uint4*>(p) = *reinterpret_cast<const uint4*>(&r);
 }
 
+// ---- streaming (non-temporal) accesses -------------------------------------
+// For arrays read or written once per pass and far larger than the caches
+// (optimizer state, gradients in the update): the accesses carry the
+// non-temporal hint, so they neither keep nor evict other lines.
+typedef float f32x4_nt __attribute__((ext_vector_type(4)));
+typedef bf16 bf16x4_nt __attribute__((ext_vector_type(4)));
+DEVI float4 ld_stream(const float* p, size_t i) {  // 16 bytes at p + 4 i
+    const f32x4_nt t = __builtin_nontemporal_load(reinterpret_cast<const f32x4_nt*>(p) + i);
+    return make_float4(t.x, t.y, t.z, t.w);
+}
+DEVI void st_stream(float* p, size_t i, const float4& q) {
+    const f32x4_nt t = {q.x, q.y, q.z, q.w};
+    __builtin_nontemporal_store(t, reinterpret_cast<f32x4_nt*>(p) + i);
+}
+DEVI bf16x4_nt ld_stream(const bf16* p, size_t i) {  // 8 bytes at p + 4 i
+    return __builtin_nontemporal_load(reinterpret_cast<const bf16x4_nt*>(p) + i);
+}
+DEVI void st_stream(bf16* p, size_t i, const bf16x4_nt& q) {
+    __builtin_nontemporal_store(q, reinterpret_cast<bf16x4_nt*>(p) + i);
+}
+
 // ---- wavefront reductions (64 lanes, all active) ---------------------------
 // Within each 16-lane row through DPP lane moves (quad_perm [1,0,3,2] and
 // [2,3,0,1], then row_ror 4 and 8), then the four row results, read out of

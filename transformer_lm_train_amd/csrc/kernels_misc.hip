@@ -931,12 +931,13 @@ DEVI void adamw_one(float& p, float g, float& m, float& v, float lr, float b1, f
 
 // Each block updates ADAM_U x 256 float4 groups; group u of a block sits at
 // (block * ADAM_U + u) * 256 + thread, so every load and store instruction
-// covers 4 KB contiguously.  All loads of a thread are issued first.
+// covers 4 KB contiguously.  All loads of a thread are issued first.  The
+// arrays are streamed with non-temporal accesses (3.7 GB per step at 124M:
+// 0.674 -> 0.618 ms against plain loads and stores).
 constexpr int ADAM_U = 4;
 __global__ __launch_bounds__(256) void adamw_kernel(float* p, const float* g, float* m, float* v, bf16* shadow,
                                                     size_t n, float lr, float b1, float b2, float eps, float wd,
                                                     float ic1, float ic2, const float* norm_scale) {
-    typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
     const float sc = norm_scale ? norm_scale[1] : 1.f;
     const size_t n4 = n / 4;
     float4 pp[ADAM_U], gg[ADAM_U], mm[ADAM_U], vv[ADAM_U];
@@ -944,10 +945,10 @@ __global__ __launch_bounds__(256) void adamw_kernel(float* p, const float* g, fl
     for (int u = 0; u < ADAM_U; u++) {
         const size_t i = ((size_t)blockIdx.x * ADAM_U + u) * 256 + threadIdx.x;
         if (i < n4) {
-            pp[u] = reinterpret_cast<const float4*>(p)[i];
-            gg[u] = reinterpret_cast<const float4*>(g)[i];
-            mm[u] = reinterpret_cast<const float4*>(m)[i];
-            vv[u] = reinterpret_cast<const float4*>(v)[i];
+            pp[u] = ld_stream(p, i);
+            gg[u] = ld_stream(g, i);
+            mm[u] = ld_stream(m, i);
+            vv[u] = ld_stream(v, i);
         }
     }
 #pragma unroll
@@ -958,13 +959,10 @@ __global__ __launch_bounds__(256) void adamw_kernel(float* p, const float* g, fl
             adamw_one(pp[u].y, gg[u].y * sc, mm[u].y, vv[u].y, lr, b1, b2, eps, wd, ic1, ic2);
             adamw_one(pp[u].z, gg[u].z * sc, mm[u].z, vv[u].z, lr, b1, b2, eps, wd, ic1, ic2);
             adamw_one(pp[u].w, gg[u].w * sc, mm[u].w, vv[u].w, lr, b1, b2, eps, wd, ic1, ic2);
-            reinterpret_cast<float4*>(p)[i] = pp[u];
-            reinterpret_cast<float4*>(m)[i] = mm[u];
-            reinterpret_cast<float4*>(v)[i] = vv[u];
-            if (shadow) {
-                bf16x4 o = {(bf16)pp[u].x, (bf16)pp[u].y, (bf16)pp[u].z, (bf16)pp[u].w};
-                reinterpret_cast<bf16x4*>(shadow)[i] = o;
-            }
+            st_stream(p, i, pp[u]);
+            st_stream(m, i, mm[u]);
+            st_stream(v, i, vv[u]);
+            if (shadow) st_stream(shadow, i, bf16x4_nt{(bf16)pp[u].x, (bf16)pp[u].y, (bf16)pp[u].z, (bf16)pp[u].w});
         }
     }
     if (blockIdx.x == 0 && threadIdx.x < (n & 3)) {
@@ -1029,10 +1027,10 @@ __global__ __launch_bounds__(256) void adamw_sr_kernel(bf16* w, float* p32, cons
     for (int u = 0; u < ADAM_U; u++) {
         const size_t i = ((size_t)blockIdx.x * ADAM_U + u) * 256 + threadIdx.x;
         if (i < n4) {
-            ww[u] = reinterpret_cast<const bf16x4*>(w)[i];
-            gg[u] = reinterpret_cast<const float4*>(g)[i];
-            mm[u] = reinterpret_cast<const float4*>(m)[i];
-            vv[u] = reinterpret_cast<const float4*>(v)[i];
+            ww[u] = ld_stream(w, i);
+            gg[u] = ld_stream(g, i);
+            mm[u] = ld_stream(m, i);
+            vv[u] = ld_stream(v, i);
         }
     }
 #pragma unroll
@@ -1047,9 +1045,9 @@ __global__ __launch_bounds__(256) void adamw_sr_kernel(bf16* w, float* p32, cons
             bf16x4 o;
 #pragma unroll
             for (int e = 0; e < 4; e++) o[e] = sr_round_bf16(x[e], sr_draw16(key, 4 * i + e));
-            reinterpret_cast<bf16x4*>(w)[i] = o;
-            reinterpret_cast<float4*>(m)[i] = mm[u];
-            reinterpret_cast<float4*>(v)[i] = vv[u];
+            st_stream(w, i, o);
+            st_stream(m, i, mm[u]);
+            st_stream(v, i, vv[u]);
             for (int r = 0; r < mr.n; r++)
                 if (4 * i >= mr.lo[r] && 4 * i < mr.hi[r])
                     *reinterpret_cast<float4*>(p32 + mr.dst[r] + (4 * i - mr.lo[r])) =

@@ -40,8 +40,9 @@ template <typename T> DEVI void st16(T* p, const Vec16<T>& r) {
 
 // ---- streaming (non-temporal) accesses -------------------------------------
 // For arrays read or written once per pass and far larger than the caches
-// (optimizer state, gradients in the update): the accesses carry the
-// non-temporal hint, so they neither keep nor evict other lines.
+// (optimizer state and gradients in the update, logits in the loss): the
+// accesses carry the non-temporal hint, so they neither keep nor evict other
+// lines.
 typedef float f32x4_nt __attribute__((ext_vector_type(4)));
 typedef bf16 bf16x4_nt __attribute__((ext_vector_type(4)));
 DEVI float4 ld_stream(const float* p, size_t i) {  // 16 bytes at p + 4 i
@@ -57,6 +58,15 @@ DEVI bf16x4_nt ld_stream(const bf16* p, size_t i) {  // 8 bytes at p + 4 i
 }
 DEVI void st_stream(bf16* p, size_t i, const bf16x4_nt& q) {
     __builtin_nontemporal_store(q, reinterpret_cast<bf16x4_nt*>(p) + i);
+}
+typedef unsigned u32x4_nt __attribute__((ext_vector_type(4)));
+template <typename T> DEVI Vec16<T> ld16_stream(const T* p) {
+    Vec16<T> r;
+    *reinterpret_cast<u32x4_nt*>(&r) = __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt*>(p));
+    return r;
+}
+template <typename T> DEVI void st16_stream(T* p, const Vec16<T>& r) {
+    __builtin_nontemporal_store(*reinterpret_cast<const u32x4_nt*>(&r), reinterpret_cast<u32x4_nt*>(p));
 }
 
 // ---- wavefront reductions (64 lanes, all active) ---------------------------

@@ -749,7 +749,9 @@ template <typename T> DEVI void keep_packed(Vec16<T>& q) {
 // One block of NT threads per row.  The row is read once into registers
 // (MAXC 16-byte chunks per thread), reduced, and written back once as
 // dlogits.  NT is small (4 waves for bf16) so that several rows are in flight
-// per CU and the block reductions are short.
+// per CU and the block reductions are short.  Rows are streamed with
+// non-temporal loads and stores (3.3 GB per step at 124M, far above the
+// caches: 0.66 -> 0.61 ms against plain accesses).
 template <typename T, int NT, int MAXC>
 __global__ __launch_bounds__(NT) void softmax_ce_kernel(T* logits, float* losses, const int* targets, int V, int Vp,
                                                         float dscale, int* err) {
@@ -769,7 +771,7 @@ __global__ __launch_bounds__(NT) void softmax_ce_kernel(T* logits, float* losses
 #pragma unroll
     for (int i = 0; i < MAXC; i++) {
         const int ch = threadIdx.x + i * NT;
-        if (ch < chunks) q[i] = ld16(z + ch * VN);
+        if (ch < chunks) q[i] = ld16_stream(z + ch * VN);
     }
     float mx = -INFINITY;
 #pragma unroll
@@ -814,7 +816,7 @@ __global__ __launch_bounds__(NT) void softmax_ce_kernel(T* logits, float* losses
                 if (v == tgt) d -= dscale;
                 o.v[j] = from_f32<T>(d);
             }
-            st16(z + ch * VN, o);
+            st16_stream(z + ch * VN, o);
         }
     }
 }

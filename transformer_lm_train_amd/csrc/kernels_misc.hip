@@ -935,8 +935,9 @@ DEVI void adamw_one(float& p, float g, float& m, float& v, float lr, float b1, f
 // (block * ADAM_U + u) * 256 + thread, so every load and store instruction
 // covers 4 KB contiguously.  All loads of a thread are issued first.  The
 // arrays are streamed with non-temporal accesses (3.7 GB per step at 124M:
-// 0.674 -> 0.618 ms against plain loads and stores).
-constexpr int ADAM_U = 4;
+// 0.674 -> 0.618 ms against plain loads and stores).  Two groups per thread
+// measured ~1.5% faster than four, eight slower.
+constexpr int ADAM_U = 2;
 __global__ __launch_bounds__(256) void adamw_kernel(float* p, const float* g, float* m, float* v, bf16* shadow,
                                                     size_t n, float lr, float b1, float b2, float eps, float wd,
                                                     float ic1, float ic2, const float* norm_scale) {

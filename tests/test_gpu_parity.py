@@ -168,6 +168,41 @@ def test_tiny_fp32_parity():
     assert all(b < a for a, b in zip(g["losses"], g["losses"][1:])), g["losses"]
 
 
+# Deep and narrow: the backward's partial sums of every block run as one
+# batch of jobs after the block loop, at most 64 per launch.  fp32 mode sends
+# 2 jobs per block + 1 through it (the LayerNorm parameters with the
+# projection biases): 33 blocks need two launches.  bf16 mode adds the fc and
+# qkv biases (4 per block + 1): 17 blocks need two.
+DEEP32 = dict(L=33, C=64, NH=4, maxT=32, V=512, Vp=512)
+DEEP16 = dict(L=17, C=64, NH=1, maxT=64, V=512, Vp=512)
+SUMMED = ("ln1w", "ln1b", "ln2w", "ln2b", "attprojb", "fcprojb", "fcb", "qkvb")
+
+
+def test_deep_fp32_parity_batched_sums():
+    kw = dict(seed=7, dist="uniform", steps=2, lr=1e-4, wd=0.0, clip=0.0)
+    o = oracle_run(DEEP32, 2, 32, **kw)
+    g = gpu_run(DEEP32, 2, 32, prec=G.GPT2_FP32, **kw)
+    check_fp32(o, g, DEEP32, kw["lr"], kw["steps"])
+    # and block by block, so that no launch's share of the jobs hides in a
+    # tensor-wide norm (the key-bias slice vanishes in exact arithmetic:
+    # compared against the whole tensor's norm)
+    gg, rr = split(g["grads0"], DEEP32), split(o["grads0"].astype(np.float64), DEEP32)
+    for name in SUMMED:
+        gl, rl = gg[name].reshape(DEEP32["L"], -1), rr[name].reshape(DEEP32["L"], -1)
+        scale = np.linalg.norm(rl)
+        for l in range(DEEP32["L"]):
+            e = np.linalg.norm(gl[l] - rl[l]) / max(np.linalg.norm(rl[l]), 1e-3 * scale)
+            assert e <= 1e-4, (name, l, e)
+
+
+def test_deep_bf16_parity_batched_sums():
+    kw = dict(seed=7, dist="uniform", steps=1, lr=3e-5, wd=0.1, clip=1.0)
+    o = oracle_run(DEEP16, 2, 64, **kw)
+    g = gpu_run(DEEP16, 2, 64, prec=G.GPT2_BF16_MIXED, **kw)
+    assert abs(g["losses"][0] - o["losses"][0]) <= 1e-2
+    compare_tensors(g["grads0"], o["grads0"], DEEP16, 5e-2, check_max=False, what="grads")
+
+
 @pytest.mark.timeout(900)
 def test_124m_fp32_parity():
     kw = dict(seed=1337, dist="zipf", steps=10, lr=1e-4, wd=0.0, clip=0.0)

@@ -330,6 +330,7 @@ struct gpt2_model {
     // has exactly one first writer), and any earlier reader of the gradient
     // gets it cleared first (materialize_zero_grad).
     bool grads_zero = false;
+    std::vector<SumJob> sum_jobs;  // the backward's batched partial sums (kept: no allocation per step)
     // kernel timing
     std::string t_cls;
     bool t_on = false;
@@ -573,7 +574,8 @@ template <typename T> int backward_impl(gpt2_t* M) {
     constexpr bool fused = std::is_same<T, bf16>::value;
     // first backward since gpt2_zero_grad: every gradient's one first writer stores
     const bool ow = M->grads_zero;
-    std::vector<SumJob> jobs;  // every block's sums, run in one batch after the block loop
+    std::vector<SumJob>& jobs = M->sum_jobs;  // every block's sums, run in one batch after the block loop
+    jobs.clear();
     jobs.reserve(4 * (size_t)Ly + 1);
     RUN("layernorm_bwd", layernorm_bwd<T>(G3(Ly - 1), nullptr, a.dmid, xlast, p + pf[P_LNFW], a.lnfm, a.lnfr, pfin,
                                           BT, C, true, s));

@@ -567,48 +567,54 @@ struct SumBatch {
 };
 
 __global__ __launch_bounds__(1024) void sum_partials_kernel(SumBatch bt) {
-    __shared__ float red[3][64][17];
+    __shared__ float red[3][64][68];
     // the job whose block range holds this block: the last k with start[k] <= blockIdx.x
     int k = 0;
     for (int w = SUM_JOBS_MAX / 2; w >= 1; w >>= 1)
         if (k + w < bt.n && (int)blockIdx.x >= bt.start[k + w]) k += w;
     const SumJob& jb = bt.job[k];
-    const int G = jb.G, C = jb.C;
+    const int G = jb.G, C = jb.C;  // C % 4 == 0 (checked by the caller)
     const float* partial = jb.partial;
+    // a block takes 64 columns: lane cx of row lane ry holds columns
+    // c0 .. c0 + 3, so 16 lanes read 256 contiguous bytes of a partial row
     const int cx = threadIdx.x & 15, ry = threadIdx.x >> 4;
-    const int c = ((int)blockIdx.x - bt.start[k]) * 16 + cx;
+    const int cb = ((int)blockIdx.x - bt.start[k]) * 64;
+    const int c0 = cb + cx * 4;
     const int nk = jb.out[2] ? 3 : jb.out[1] ? 2 : 1;  // out[0] is always given
-    // rows ry, ry + 64, ... in that order, U rows' loads issued before their adds
-    constexpr int U = 8;
-    float t0 = 0.f, t1 = 0.f, t2 = 0.f;
-    if (c < C)
+    // rows ry, ry + 64, ... in that order, U rows' loads issued before their
+    // adds (U = 4: three operands of 4 x float4 fit 128 registers)
+    constexpr int U = 4;
+    const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+    float4 t0 = z4, t1 = z4, t2 = z4;
+    auto add4 = [](float4& t, const float4& v) { t.x += v.x; t.y += v.y; t.z += v.z; t.w += v.w; };
+    if (c0 < C)
         for (int g0 = ry; g0 < G; g0 += 64 * U) {
-            float v0[U], v1[U], v2[U];
+            float4 v0[U], v1[U], v2[U];
 #pragma unroll
             for (int u = 0; u < U; u++) {
                 const int g = g0 + 64 * u;
-                const float* pr = partial + (int64_t)g * C + c;
-                v0[u] = g < G ? pr[0] : 0.f;
-                v1[u] = nk > 1 && g < G ? pr[(int64_t)G * C] : 0.f;
-                v2[u] = nk > 2 && g < G ? pr[2 * (int64_t)G * C] : 0.f;
+                const float* pr = partial + (int64_t)g * C + c0;
+                v0[u] = g < G ? *reinterpret_cast<const float4*>(pr) : z4;
+                v1[u] = nk > 1 && g < G ? *reinterpret_cast<const float4*>(pr + (int64_t)G * C) : z4;
+                v2[u] = nk > 2 && g < G ? *reinterpret_cast<const float4*>(pr + 2 * (int64_t)G * C) : z4;
             }
 #pragma unroll
             for (int u = 0; u < U; u++) {
-                t0 += v0[u];
-                t1 += v1[u];
-                t2 += v2[u];
+                add4(t0, v0[u]);
+                add4(t1, v1[u]);
+                add4(t2, v2[u]);
             }
         }
-    red[0][ry][cx] = t0;
-    red[1][ry][cx] = t1;
-    red[2][ry][cx] = t2;
+    *reinterpret_cast<float4*>(&red[0][ry][cx * 4]) = t0;
+    *reinterpret_cast<float4*>(&red[1][ry][cx * 4]) = t1;
+    *reinterpret_cast<float4*>(&red[2][ry][cx * 4]) = t2;
     __syncthreads();
-    if (threadIdx.x < 48) {
-        const int q = threadIdx.x >> 4;
+    if (threadIdx.x < 192) {
+        const int q = threadIdx.x >> 6, col = threadIdx.x & 63, c = cb + col;
         float* out = q == 0 ? jb.out[0] : q == 1 ? jb.out[1] : jb.out[2];
         if (c < C && out) {
             float t = 0.f;
-            for (int i = 0; i < 64; i++) t += red[q][i][cx];
+            for (int i = 0; i < 64; i++) t += red[q][i][col];
             out[c] = bt.overwrite ? t : out[c] + t;
         }
     }
@@ -616,8 +622,10 @@ __global__ __launch_bounds__(1024) void sum_partials_kernel(SumBatch bt) {
 
 hipError_t sum_partials_batch(const SumJob* jobs, int n, bool overwrite, hipStream_t s) {
     if (n < 0) return hipErrorInvalidValue;
-    for (int i = 0; i < n; i++)
-        if (!jobs[i].out[0] || !jobs[i].partial || jobs[i].G <= 0 || jobs[i].C <= 0) return hipErrorInvalidValue;
+    for (int i = 0; i < n; i++)  // whole float4 groups of columns: C % 4 == 0, 16-byte aligned partial rows
+        if (!jobs[i].out[0] || !jobs[i].partial || jobs[i].G <= 0 || jobs[i].C <= 0 || jobs[i].C % 4 ||
+            (uintptr_t)jobs[i].partial % 16)
+            return hipErrorInvalidValue;
     for (int j0 = 0; j0 < n; j0 += SUM_JOBS_MAX) {
         const int m = std::min(n - j0, SUM_JOBS_MAX);
         SumBatch bt{};
@@ -626,7 +634,7 @@ hipError_t sum_partials_batch(const SumJob* jobs, int n, bool overwrite, hipStre
         bt.start[0] = 0;
         for (int i = 0; i < m; i++) {
             bt.job[i] = jobs[j0 + i];
-            bt.start[i + 1] = bt.start[i] + (int)cdiv(jobs[j0 + i].C, 16);
+            bt.start[i + 1] = bt.start[i] + (int)cdiv(jobs[j0 + i].C, 64);
         }
         sum_partials_kernel<<<bt.start[m], 1024, 0, s>>>(bt);
         const hipError_t e = hipGetLastError();

@@ -116,8 +116,21 @@ int gpt2_forward(gpt2_t* m, const int32_t* tokens, const int32_t* targets, float
 int gpt2_forward_device(gpt2_t* m, const int32_t* d_tokens, const int32_t* d_targets,
                         float* mean_loss);
 
-/* Mean loss of the last forward with targets (blocks on the stream). */
+/* Mean loss of the last forward with targets (blocks on the stream).  Like
+ * every call that reads a value back, it also reports a device-side
+ * condition raised since the last report (see gpt2_sync): the loss is still
+ * written when the report is GPT2_ERANGE. */
 int gpt2_read_loss(gpt2_t* m, float* mean_loss);
+
+/* Block until all queued work is done and report, then clear, the
+ * conditions the kernels raise on the device (they cannot return an error
+ * themselves): GPT2_EINVAL if a device token or target id was outside
+ * [0,V) (gpt2_forward_device), else GPT2_ERANGE if an AdamW update was
+ * refused because the gradient norm was not finite (gpt2_adamw_step after
+ * gpt2_clip_grad_norm with norm == NULL); 0 otherwise.  The global-norm
+ * clipping and its outlier guard follow the pyshine.com tour of llm.c
+ * (global-norm header). */
+int gpt2_sync(gpt2_t* m);
 
 /* Parameter gradients <- 0.  (Activation gradients are overwritten by every
  * backward, never accumulated.)  In the bf16 modes the clear is deferred:
@@ -137,7 +150,10 @@ int gpt2_backward(gpt2_t* m);
  * gpt2_adamw_step uses g * max_norm/n (the gradients in memory are not
  * rewritten).  max_norm <= 0 only measures.  If norm != NULL, *norm = n
  * (one stream sync); a non-finite n returns GPT2_ERANGE and makes the next
- * gpt2_adamw_step refuse to update. */
+ * gpt2_adamw_step refuse to update.  With norm == NULL nothing is read back:
+ * a non-finite n is caught on the device instead, where the next AdamW
+ * kernel leaves every parameter, m and v (and the bf16 copy) unchanged and
+ * raises the condition gpt2_sync and the next read-back report. */
 int gpt2_clip_grad_norm(gpt2_t* m, float max_norm, float* norm);
 
 /* AdamW (decoupled weight decay, bias-corrected, step t >= 1) over all N
@@ -186,6 +202,11 @@ int gpt2_copy_logits(gpt2_t* m, float* host_dst);
 
 /* Copy the per-position losses [B*T] of the last forward with targets. */
 int gpt2_copy_losses(gpt2_t* m, float* host_dst);
+
+/* Overwrite the parameter gradients from a host array of N floats (a
+ * pending deferred clear is dropped).  For tests of the update and of the
+ * non-finite guard. */
+int gpt2_set_grads(gpt2_t* m, const float* host_src);
 
 /* Overwrite the fp32 master parameters from a host array of N floats and
  * refresh the bf16 shadow.  In BF16_SR mode the bf16 parameters are set to

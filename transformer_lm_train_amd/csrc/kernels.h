@@ -132,12 +132,15 @@ template <typename T>
 hipError_t softmax_ce(T* logits, float* losses, const int* targets, int BT, int V, int Vp, float dscale,
                       int* err_flag, hipStream_t s);
 hipError_t loss_mean(float* out, const float* losses, int n, hipStream_t s);
-// norm_scale[0] = ||g||, norm_scale[1] = clip factor (1 if no clip).
-// adamw multiplies g by norm_scale[1], or by 1 when norm_scale is NULL.
+// norm_scale[0] = ||g||, norm_scale[1] = clip factor (1 if no clip; NaN if
+// the norm is not finite).  adamw multiplies g by norm_scale[1], or by 1 when
+// norm_scale is NULL; on a non-finite factor it writes nothing and sets
+// refused[0] = 1 (refused is required with norm_scale).
 hipError_t grad_norm(float* partial, float* norm_scale, const float* g, size_t n, float max_norm,
                      hipStream_t s);
 hipError_t adamw(float* p, const float* g, float* m, float* v, bf16* shadow, size_t n, float lr, float b1,
-                 float b2, float eps, float wd, float c1, float c2, const float* norm_scale, hipStream_t s);
+                 float b2, float eps, float wd, float c1, float c2, const float* norm_scale, int* refused,
+                 hipStream_t s);
 // Flat parameter ranges [lo, hi) whose fp32 copy the stochastic-rounding
 // AdamW keeps (as float of the new bf16 value), at p32[dst + (i - lo)].
 constexpr int SR_RANGES_MAX = 16;
@@ -151,7 +154,7 @@ struct SrRanges {
 // the ranges.  n, every range boundary and every dst must be multiples of 4.
 hipError_t adamw_sr(bf16* w, float* p32, const float* g, float* m, float* v, size_t n, float lr, float b1, float b2,
                     float eps, float wd, float c1, float c2, const float* norm_scale, uint64_t key,
-                    const SrRanges& mirror, hipStream_t s);
+                    const SrRanges& mirror, int* refused, hipStream_t s);
 hipError_t cast_bf16(bf16* dst, const float* src, size_t n, hipStream_t s);
 template <typename T> hipError_t widen_f32(float* dst, const T* src, size_t n, hipStream_t s);
 

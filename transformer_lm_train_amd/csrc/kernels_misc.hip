@@ -555,10 +555,11 @@ void layernorm_bwd_kernel(T* dout, const T* din, const T* dy, const T* x, const 
 }
 
 // For each job, out_k[c] += sum_g partial[k*G + g][c] for its non-null out_k
-// (k < 3).  Block: 16 columns x 64 row lanes of one job (the jobs' blocks are
-// laid end to end); lane r sums partial rows r, r+64, ... (all its loads
-// independent, so the whole array is in flight at once), then the 64 lane
-// sums of a column are combined in a fixed order.
+// (k < 3).  Block: 64 columns x 64 row lanes of one job (the jobs' blocks are
+// laid end to end); each lane holds 4 consecutive columns (16 lanes read 256
+// contiguous bytes of a partial row), row lane r sums partial rows r, r+64,
+// ... in that order, U rows' loads issued before their adds, then the 64
+// row-lane sums of a column are combined in a fixed order.
 struct SumBatch {
     SumJob job[SUM_JOBS_MAX];
     int start[SUM_JOBS_MAX + 1];  // first block of each job
@@ -567,7 +568,7 @@ struct SumBatch {
 };
 
 __global__ __launch_bounds__(1024) void sum_partials_kernel(SumBatch bt) {
-    __shared__ float red[3][64][68];
+    __shared__ __attribute__((aligned(16))) float red[3][64][68];  // read and written as float4
     // the job whose block range holds this block: the last k with start[k] <= blockIdx.x
     int k = 0;
     for (int w = SUM_JOBS_MAX / 2; w >= 1; w >>= 1)
@@ -916,7 +917,10 @@ __global__ __launch_bounds__(1024) void norm_final_kernel(float* norm_scale, con
     if (threadIdx.x == 0) {
         const float n = (float)sqrt(s);
         norm_scale[0] = n;
-        norm_scale[1] = (max_norm > 0.f && n > max_norm) ? max_norm / n : 1.f;
+        // a non-finite norm (a NaN or inf gradient, or a sum of squares past
+        // the float range) leaves a NaN factor: the AdamW kernels refuse to
+        // update on it
+        norm_scale[1] = !isfinite(n) ? __builtin_nanf("") : (max_norm > 0.f && n > max_norm) ? max_norm / n : 1.f;
     }
 }
 
@@ -948,8 +952,12 @@ DEVI void adamw_one(float& p, float g, float& m, float& v, float lr, float b1, f
 constexpr int ADAM_U = 2;
 __global__ __launch_bounds__(256) void adamw_kernel(float* p, const float* g, float* m, float* v, bf16* shadow,
                                                     size_t n, float lr, float b1, float b2, float eps, float wd,
-                                                    float ic1, float ic2, const float* norm_scale) {
+                                                    float ic1, float ic2, const float* norm_scale, int* refused) {
     const float sc = norm_scale ? norm_scale[1] : 1.f;
+    if (!isfinite(sc)) {  // the same for every workgroup: nothing is written
+        if (blockIdx.x == 0 && threadIdx.x == 0) refused[0] = 1;
+        return;
+    }
     const size_t n4 = n / 4;
     float4 pp[ADAM_U], gg[ADAM_U], mm[ADAM_U], vv[ADAM_U];
 #pragma unroll
@@ -988,10 +996,11 @@ __global__ __launch_bounds__(256) void adamw_kernel(float* p, const float* g, fl
 }
 
 hipError_t adamw(float* p, const float* g, float* m, float* v, bf16* shadow, size_t n, float lr, float b1, float b2,
-                 float eps, float wd, float c1, float c2, const float* norm_scale, hipStream_t s) {
+                 float eps, float wd, float c1, float c2, const float* norm_scale, int* refused, hipStream_t s) {
+    if (norm_scale && !refused) return hipErrorInvalidValue;
     const size_t blocks = cdiv(n / 4, 256 * ADAM_U) + 1;
     adamw_kernel<<<(unsigned)blocks, 256, 0, s>>>(p, g, m, v, shadow, n, lr, b1, b2, eps, wd, 1.f / c1, 1.f / c2,
-                                                  norm_scale);
+                                                  norm_scale, refused);
     return LAUNCH_CHECK();
 }
 
@@ -1028,9 +1037,13 @@ DEVI bf16 sr_round_bf16(float x, uint32_t u) {
 __global__ __launch_bounds__(256) void adamw_sr_kernel(bf16* w, float* p32, const float* g, float* m, float* v,
                                                        size_t n, float lr, float b1, float b2, float eps, float wd,
                                                        float ic1, float ic2, const float* norm_scale, uint64_t key,
-                                                       SrRanges mr) {
+                                                       SrRanges mr, int* refused) {
     typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
     const float sc = norm_scale ? norm_scale[1] : 1.f;
+    if (!isfinite(sc)) {  // the same for every workgroup: nothing is written
+        if (blockIdx.x == 0 && threadIdx.x == 0) refused[0] = 1;
+        return;
+    }
     const size_t n4 = n / 4;
     bf16x4 ww[ADAM_U];
     float4 gg[ADAM_U], mm[ADAM_U], vv[ADAM_U];
@@ -1069,15 +1082,16 @@ __global__ __launch_bounds__(256) void adamw_sr_kernel(bf16* w, float* p32, cons
 
 hipError_t adamw_sr(bf16* w, float* p32, const float* g, float* m, float* v, size_t n, float lr, float b1, float b2,
                     float eps, float wd, float c1, float c2, const float* norm_scale, uint64_t key,
-                    const SrRanges& mirror, hipStream_t s) {
+                    const SrRanges& mirror, int* refused, hipStream_t s) {
     if (n % 4 || mirror.n < 0 || mirror.n > SR_RANGES_MAX) return hipErrorInvalidValue;
+    if (norm_scale && !refused) return hipErrorInvalidValue;
     for (int r = 0; r < mirror.n; r++)
         if (mirror.lo[r] % 4 || mirror.hi[r] % 4 || mirror.dst[r] % 4 || mirror.lo[r] > mirror.hi[r] ||
             mirror.hi[r] > n)
             return hipErrorInvalidValue;
     const size_t blocks = cdiv(n / 4, 256 * ADAM_U);
     adamw_sr_kernel<<<(unsigned)blocks, 256, 0, s>>>(w, p32, g, m, v, n, lr, b1, b2, eps, wd, 1.f / c1, 1.f / c2,
-                                                     norm_scale, key, mirror);
+                                                     norm_scale, key, mirror, refused);
     return LAUNCH_CHECK();
 }
 

@@ -626,19 +626,32 @@ template <typename T> int backward_impl(gpt2_t* M) {
     return GPT2_OK;
 }
 
-int read_scalars(gpt2_t* M, int n_floats) {
-    HIPCHK(hipMemcpyAsync(M->h_scalars, M->P<float>(M->L.scalars), 16, hipMemcpyDeviceToHost, M->stream));
-    HIPCHK(hipMemcpyAsync(M->h_scalars + 4, M->P<int>(M->L.err), 4, hipMemcpyDeviceToHost, M->stream));
-    HIPCHK(hipStreamSynchronize(M->stream));
-    (void)n_floats;
-    int errflag;
-    memcpy(&errflag, M->h_scalars + 4, 4);
-    if (errflag) {
+// Device-side conditions, in the err region: [0] a token or target id was
+// out of range (replaced by 0), [1] an AdamW update was refused because the
+// gradient norm was not finite.  Both are reported, and cleared, by the next
+// call that reads a value back.
+int report_flags(gpt2_t* M, const int flags[2]) {
+    if (flags[0]) {
         HIPCHK(hipMemsetAsync(M->P<int>(M->L.err), 0, 4, M->stream));
         return fail(GPT2_EINVAL, "token or target id outside [0, vocab_size) (flag %d); it was replaced by 0",
-                    errflag);
+                    flags[0]);
+    }
+    if (flags[1]) {
+        HIPCHK(hipMemsetAsync(M->P<int>(M->L.err) + 1, 0, 4, M->stream));
+        return fail(GPT2_ERANGE, "an AdamW update was refused on the device: the gradient norm was not finite "
+                                 "(parameters and optimizer state were left unchanged)");
     }
     return GPT2_OK;
+}
+
+// Loss (and the other small scalars) plus the device flags, one sync.
+int read_scalars(gpt2_t* M) {
+    HIPCHK(hipMemcpyAsync(M->h_scalars, M->P<float>(M->L.scalars), 16, hipMemcpyDeviceToHost, M->stream));
+    HIPCHK(hipMemcpyAsync(M->h_scalars + 4, M->P<int>(M->L.err), 8, hipMemcpyDeviceToHost, M->stream));
+    HIPCHK(hipStreamSynchronize(M->stream));
+    int flags[2];
+    memcpy(flags, M->h_scalars + 4, 8);
+    return report_flags(M, flags);
 }
 
 int forward_common(gpt2_t* M, bool with_targets, float* mean_loss) {
@@ -651,12 +664,13 @@ int forward_common(gpt2_t* M, bool with_targets, float* mean_loss) {
             *mean_loss = NAN;
             return GPT2_OK;
         }
-        rc = read_scalars(M, 1);
-        if (rc) {
+        rc = read_scalars(M);
+        if (rc && rc != GPT2_ERANGE) {
             M->have_targets = false;
             return rc;
         }
-        *mean_loss = M->h_scalars[0];
+        *mean_loss = M->h_scalars[0];  // valid: an earlier refused update is reported alongside
+        if (rc) return rc;
     }
     return GPT2_OK;
 }
@@ -833,10 +847,19 @@ int gpt2_forward_device(gpt2_t* M, const int32_t* d_tokens, const int32_t* d_tar
 int gpt2_read_loss(gpt2_t* M, float* mean_loss) {
     if (!M || !mean_loss) return fail(GPT2_EINVAL, "NULL argument");
     if (!M->have_targets) return fail(GPT2_EPERM, "no forward with targets since the last update");
-    int rc = read_scalars(M, 1);
-    if (rc) return rc;
+    int rc = read_scalars(M);
+    if (rc && rc != GPT2_ERANGE) return rc;
     *mean_loss = M->h_scalars[0];
-    return GPT2_OK;
+    return rc;
+}
+
+int gpt2_sync(gpt2_t* M) {
+    if (!M) return fail(GPT2_EINVAL, "NULL model");
+    HIPCHK(hipMemcpyAsync(M->h_scalars + 4, M->P<int>(M->L.err), 8, hipMemcpyDeviceToHost, M->stream));
+    HIPCHK(hipStreamSynchronize(M->stream));
+    int flags[2];
+    memcpy(flags, M->h_scalars + 4, 8);
+    return report_flags(M, flags);
 }
 
 int gpt2_zero_grad(gpt2_t* M) {
@@ -899,14 +922,16 @@ int gpt2_adamw_step(gpt2_t* M, float lr, float beta1, float beta2, float eps, fl
     float c1 = (float)(1.0 - pow((double)beta1, t)), c2 = (float)(1.0 - pow((double)beta2, t));
     float* ns = M->clip_pending ? M->P<float>(M->L.scalars) + 4 : nullptr;
     bf16* sh = M->bf16mode() ? M->P<bf16>(M->L.shadow) : nullptr;
+    int* refused = M->P<int>(M->L.err) + 1;  // set by the kernel if the clip factor is not finite
     if (M->srmode()) {
         // the draws of step t: SplitMix64 keyed by the build seed (state 2^62 + t)
         const uint64_t key = splitmix64_at(M->seed, ((uint64_t)1 << 62) + (uint64_t)t);
         RUN("adamw", adamw_sr(sh, M->params(), M->grads(), M->P<float>(M->L.m), M->P<float>(M->L.v), M->L.N, lr,
-                              beta1, beta2, eps, weight_decay, c1, c2, ns, key, mirror_ranges(M), M->stream));
+                              beta1, beta2, eps, weight_decay, c1, c2, ns, key, mirror_ranges(M), refused,
+                              M->stream));
     } else {
         RUN("adamw", adamw(M->params(), M->grads(), M->P<float>(M->L.m), M->P<float>(M->L.v), sh, M->L.N, lr, beta1,
-                           beta2, eps, weight_decay, c1, c2, ns, M->stream));
+                           beta2, eps, weight_decay, c1, c2, ns, refused, M->stream));
     }
     M->clip_pending = false;  // a clip factor applies to one update only
     M->have_targets = false;
@@ -985,6 +1010,14 @@ int gpt2_copy_losses(gpt2_t* M, float* dst) {
     size_t n = (size_t)M->cfg.batch_size * M->cfg.seq_len;
     HIPCHK(hipMemcpyAsync(dst, M->P<float>(M->L.losses), 4 * n, hipMemcpyDeviceToHost, M->stream));
     HIPCHK(hipStreamSynchronize(M->stream));
+    return GPT2_OK;
+}
+
+int gpt2_set_grads(gpt2_t* M, const float* src) {
+    if (!M || !src) return fail(GPT2_EINVAL, "NULL argument");
+    HIPCHK(hipMemcpyAsync(M->grads(), src, 4 * M->L.N, hipMemcpyHostToDevice, M->stream));
+    HIPCHK(hipStreamSynchronize(M->stream));
+    M->grads_zero = false;  // the values just set replace any pending clear
     return GPT2_OK;
 }
 

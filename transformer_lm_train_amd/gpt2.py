@@ -61,6 +61,7 @@ def lib():
         "gpt2_forward": ([vp, ip, ip, fp], ctypes.c_int),
         "gpt2_forward_device": ([vp, vp, vp, fp], ctypes.c_int),
         "gpt2_read_loss": ([vp, fp], ctypes.c_int),
+        "gpt2_sync": ([vp], ctypes.c_int),
         "gpt2_zero_grad": ([vp], ctypes.c_int),
         "gpt2_backward": ([vp], ctypes.c_int),
         "gpt2_clip_grad_norm": ([vp, f32, fp], ctypes.c_int),
@@ -75,6 +76,7 @@ def lib():
         "gpt2_copy_logits": ([vp, fp], ctypes.c_int),
         "gpt2_copy_losses": ([vp, fp], ctypes.c_int),
         "gpt2_set_params": ([vp, fp], ctypes.c_int),
+        "gpt2_set_grads": ([vp, fp], ctypes.c_int),
         "gpt2_device_params": ([vp], vp),
         "gpt2_device_grads": ([vp], vp),
         "gpt2_device_shadow": ([vp], vp),
@@ -148,6 +150,10 @@ def gpt2_read_loss(h):
     return loss.value
 
 
+def gpt2_sync(h):
+    _check(lib().gpt2_sync(h))
+
+
 def gpt2_zero_grad(h):
     _check(lib().gpt2_zero_grad(h))
 
@@ -214,6 +220,12 @@ def gpt2_copy_losses(h, rows):
 def gpt2_set_params(h, params):
     params = np.ascontiguousarray(params, dtype=np.float32)
     _check(lib().gpt2_set_params(h, _fptr(params)))
+
+
+def gpt2_set_grads(h, grads):
+    grads = np.ascontiguousarray(grads, dtype=np.float32)
+    assert grads.size == gpt2_num_params(h)
+    _check(lib().gpt2_set_grads(h, _fptr(grads)))
 
 
 def gpt2_kernel_timing_enable(h, cls, enable=True):
@@ -315,6 +327,12 @@ class Model:
 
     def set_params(self, p):
         gpt2_set_params(self.h, p)
+
+    def set_grads(self, g):
+        gpt2_set_grads(self.h, g)
+
+    def sync(self):
+        gpt2_sync(self.h)
 
     def param_offsets(self):
         return gpt2_param_offsets(self.h)

@@ -184,7 +184,7 @@ def main():
         achieved = per_launch / (avg_ms / 1e3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
-    from transformer_lm_train_amd import pmc_traffic
+    import pmc_traffic
     # bytes per launch from the committed counter runs, if still current and of this configuration
     traffic = pmc_traffic.recorded(dom, args.config)
     roof["traffic"] = traffic

@@ -4,7 +4,12 @@ Configurations (GPT-2 training-step workloads):
   * tiny fp32: L=2, C=64, NH=4, T=32, B=4, V=512, uniform tokens; 10 AdamW
     steps (lr 1e-4, betas 0.9/0.999, eps 1e-8, wd 0);
   * GPT-2 124M fp32 at B=4, T=64, Zipf(1.1) tokens, same optimizer;
-  * GPT-2 124M bf16 mixed at B=4, T=64 with lr 3e-5, wd 0.1, clip 1.0;
+  * GPT-2 124M bf16 mixed at B=4, T=64: 10 steps with lr 3e-5, and 3 steps
+    with the benchmark's lr 6e-4 (wd 0.1, clip 1.0 both), parameters and the
+    update theta_k - theta_0 per tensor;
+  * bf16 gradients at the benchmark's token count B*T = 16384 (a narrow
+    two-block model, one block of the 124M width), the whole 124M model at
+    B=1, T=1024 and one block of the 1.6B width;
   * GPT-2 124M bf16 mixed at the benchmark size B=16, T=1024, and the 350M
     (B=16) and 1.6B (B=8) bf16 workloads at T=1024 (sampled rows).
 Tolerances: fp32 mode 1e-4 relative (loss; per tensor relative L2 and max
@@ -72,25 +77,30 @@ def compare_tensors(got, ref, cfg, tol, check_max=True, what="grads", kbias_step
         assert np.max(np.abs(r["qkvb"][k])) <= 3 * lr * steps
         g["qkvb"], r["qkvb"] = g["qkvb"][~k], r["qkvb"][~k]
     gnorm = np.linalg.norm(ref)
-    bad = []
+    bad, errs = [], {}
     for name in O.PARAM_NAMES:
         rn = np.linalg.norm(r[name])
         if rn < 1e-6 * gnorm:
             # (near-)zero reference tensor: measure against the global norm
             e = float(np.linalg.norm(g[name] - r[name]) / gnorm)
+            errs[name] = e
             if e > tol:
                 bad.append((name, e))
             continue
         e = rel_l2(g[name], r[name])
         m = rel_max(g[name], r[name]) if check_max else 0.0
+        errs[name] = max(e, m)
         if e > tol or m > tol:
             bad.append((name, e, m))
+    print(f"{what}: " + ", ".join(f"{n} {v:.2g}" for n, v in errs.items()), flush=True)
     assert not bad, f"{what}: {bad}"
 
 
-def oracle_run(cfg, B, T, seed, dist, steps, lr, wd, clip):
+def oracle_run(cfg, B, T, seed, dist, steps, lr, wd, clip, final_loss=False, init_rounded=False):
     m = O.Model(ocfg(cfg), B, T)
     m.init(seed)
+    if init_rounded:  # the initial parameters rounded to the nearest bf16 values
+        m.params[:] = O.bf16_rne(m.params)
     init = m.params.copy()
     x, y = synth.batch(seed, 0, B, T, cfg["V"], dist)
     m.forward(x)
@@ -106,11 +116,13 @@ def oracle_run(cfg, B, T, seed, dist, steps, lr, wd, clip):
             grads0 = m.grads.copy()
         norms.append(m.clip_grad_norm(clip))
         m.adamw(lr, 0.9, 0.999, 1e-8, wd, t)
+    if final_loss:
+        losses.append(m.forward(x, y))
     return dict(init=init, logits=logits, losses=losses, per_pos=per_pos, grads0=grads0,
                 params=m.params.copy(), norms=norms, x=x, y=y)
 
 
-def gpu_run(cfg, B, T, seed, dist, steps, lr, wd, clip, prec):
+def gpu_run(cfg, B, T, seed, dist, steps, lr, wd, clip, prec, final_loss=False):
     m = G.Model(gcfg(cfg, B, T, prec), seed)
     init = m.params()
     x, y = synth.batch(seed, 0, B, T, cfg["V"], dist)
@@ -127,6 +139,8 @@ def gpu_run(cfg, B, T, seed, dist, steps, lr, wd, clip, prec):
             grads0 = m.grads()
         norms.append(m.clip_grad_norm(clip))
         m.adamw_step(lr, 0.9, 0.999, 1e-8, wd, t)
+    if final_loss:
+        losses.append(m.forward(x, y))
     out = dict(init=init, logits=logits, losses=losses, per_pos=per_pos, grads0=grads0, params=m.params(),
                norms=norms)
     m.close()
@@ -144,20 +158,6 @@ def check_fp32(o, g, cfg, lr, steps):
         assert abs(a - b) <= 1e-4 * b
     compare_tensors(g["params"], o["params"], cfg, 1e-4, check_max=False, what="params after 10 steps",
                     kbias_steps=(lr, steps))
-
-
-def test_oracle_key_bias_gradient_vanishes():
-    """Pins the reading behind kbias_mask: in fp64 the key-bias gradient is
-    zero to rounding while the query- and value-bias gradients are not."""
-    m = O.Model(ocfg(TINY), 4, 32, "f64")
-    m.init(1337)
-    x, y = synth.batch(1337, 0, 4, 32, TINY["V"], "uniform")
-    m.forward(x, y)
-    m.zero_grad()
-    m.backward()
-    g = m.G()["qkvb"].reshape(TINY["L"], 3, TINY["C"])
-    assert np.abs(g[:, 1]).max() < 1e-15 * np.abs(g[:, 2]).max()
-    assert np.abs(g[:, 0]).max() > 1e-8
 
 
 def test_tiny_fp32_parity():
@@ -203,6 +203,78 @@ def test_deep_bf16_parity_batched_sums():
     compare_tensors(g["grads0"], o["grads0"], DEEP16, 5e-2, check_max=False, what="grads")
 
 
+def compare_blocks(got, ref, cfg, tol, names=SUMMED):
+    """Per-block relative L2 of the per-layer tensors whose gradients are
+    fixed-order sums of partial rows, so that no block's share hides in a
+    tensor-wide norm (a block whose own norm is tiny is measured against
+    1e-3 of the tensor's)."""
+    gg, rr = split(got, cfg), split(ref.astype(np.float64), cfg)
+    bad = []
+    for name in names:
+        gl, rl = gg[name].reshape(cfg["L"], -1), rr[name].reshape(cfg["L"], -1)
+        scale = np.linalg.norm(rl)
+        for l in range(cfg["L"]):
+            e = np.linalg.norm(gl[l] - rl[l]) / max(np.linalg.norm(rl[l]), 1e-3 * scale)
+            if e > tol:
+                bad.append((name, l, float(e)))
+    assert not bad, bad
+
+
+# bf16 gradients at the benchmark's token count and shapes, every tensor
+# against the oracle (5e-2 relative L2, per tensor and per block):
+#  * narrow: B*T = 16384 tokens (LayerNorm backward waves take 8 rows each,
+#    8 query blocks of qkv-bias rows per sequence, 64 tile rows of GELU'
+#    column sums, 512 partial rows per sum, a 16384-token weight-gradient
+#    reduction) on two thin blocks;
+#  * width 768: one block of the 124M width at B=16, T=1024, so the LayerNorm,
+#    attention and product kernels are the benchmark's own instantiations;
+#  * 124M at B=1, T=1024: the whole benchmark model at its sequence length;
+#  * width 1600 (the 1.6B width, 25 heads): the LayerNorm kernels for rows
+#    over 1024 bf16 channels, with 4 rows per backward wave.
+FULL = {
+    "narrow": (dict(L=2, C=128, NH=2, maxT=1024, V=1024, Vp=1024), 16, 1024),
+    "w768": (dict(L=1, C=768, NH=12, maxT=1024, V=2048, Vp=2048), 16, 1024),
+    "124m_b1": (M124, 1, 1024),
+    "w1600": (dict(L=1, C=1600, NH=25, maxT=256, V=1000, Vp=1024), 32, 256),
+}
+
+
+@pytest.mark.timeout(1200)
+@pytest.mark.parametrize("name", list(FULL))
+def test_bf16_gradients_full_token_count(name):
+    cfg, B, T = FULL[name]
+    seed = 1337
+    print(f"bf16 gradients {name}: L={cfg['L']} C={cfg['C']} NH={cfg['NH']} V={cfg['V']} B={B} T={T}", flush=True)
+    x, y = synth.batch(seed, 0, B, T, cfg["V"], "zipf")
+    m = G.Model(gcfg(cfg, B, T, G.GPT2_BF16_MIXED), seed)
+    loss = m.forward(x, y)
+    per_pos = m.losses()
+    m.zero_grad()
+    m.backward()
+    norm = m.clip_grad_norm(1.0)
+    g = m.grads()
+    m.close()
+    print("oracle step", flush=True)
+    om = O.Model(ocfg(cfg), B, T)
+    om.init(seed)
+    oloss = om.forward(x, y)
+    oper = om.A()["losses"].copy()
+    om.zero_grad()
+    om.backward()
+    ref = om.grads.copy()
+    onorm = om.clip_grad_norm(1.0)  # (the oracle's clip rescales its gradients in place)
+    del om
+    print(f"loss {loss:.5f} oracle {oloss:.5f}; norm {norm:.5f} oracle {onorm:.5f}", flush=True)
+    assert abs(loss - oloss) <= 1e-2
+    assert np.max(np.abs(per_pos - oper)) <= 5e-2
+    assert abs(norm - onorm) <= 5e-2 * onorm
+    compare_tensors(g, ref, cfg, 5e-2, check_max=False, what=f"grads {name}")
+    compare_blocks(g, ref, cfg, 5e-2)
+    gg = split(g, cfg)
+    assert not gg["wte"][cfg["V"] * cfg["C"]:].any()       # pad rows of wte
+    assert not gg["wpe"][T * cfg["C"]:].any()              # positions past T
+
+
 @pytest.mark.timeout(900)
 def test_124m_fp32_parity():
     kw = dict(seed=1337, dist="zipf", steps=10, lr=1e-4, wd=0.0, clip=0.0)
@@ -231,6 +303,55 @@ def test_124m_bf16_parity():
         assert abs(a - b) <= 5e-2 * b
     compare_tensors(g["params"], o["params"], M124, 5e-2, check_max=False, what="params after 10 steps",
                     kbias_steps=(kw["lr"], kw["steps"]))
+    # the update itself: theta_10 - theta_0 per tensor (the parameters of
+    # most matrices move by under 5% of their norm in 10 steps, so the check
+    # above alone could not see a missing update)
+    dg, do = g["params"] - g["init"], o["params"] - o["init"].astype(np.float64)
+    sg, so = split(dg, M124), split(do, M124)
+    print("update rel-L2: " + ", ".join(f"{n} {rel_l2(sg[n], so[n]):.3g}" for n in O.PARAM_NAMES), flush=True)
+    compare_tensors(dg, do, M124, 5e-2, check_max=False, what="theta_10 - theta_0",
+                    kbias_steps=(kw["lr"], kw["steps"]))
+
+
+@pytest.mark.timeout(900)
+def test_124m_bf16_parity_lr6e4():
+    """The benchmark's own optimizer settings (lr 6e-4, wd 0.1, clip 1.0) at
+    the 124M model, B=4, T=64: four losses (before each of three updates and
+    after the last), the gradients and norms, the parameters after three
+    updates and the update itself.  On the fp32 oracle alone, rounding the
+    initial parameters to bf16 moves the loss by up to 3e-3 over these four
+    forwards and by 0.1 at the fifth (the CPU conditioning test), so three
+    updates is as far as this rate can be compared at 1e-2."""
+    kw = dict(seed=1337, dist="zipf", steps=3, lr=6e-4, wd=0.1, clip=1.0, final_loss=True)
+    o = oracle_run(M124, 4, 64, **kw)
+    g = gpu_run(M124, 4, 64, prec=G.GPT2_BF16_MIXED, **kw)
+    print(f"losses {np.round(g['losses'], 4)} oracle {np.round(o['losses'], 4)}", flush=True)
+    for a, b in zip(g["losses"], o["losses"]):
+        assert abs(a - b) <= 1e-2, (g["losses"], o["losses"])
+    compare_tensors(g["grads0"], o["grads0"], M124, 5e-2, check_max=False, what="grads")
+    for a, b in zip(g["norms"], o["norms"]):
+        assert abs(a - b) <= 5e-2 * b
+    # Parameters after the three updates.  AdamW's first steps move each
+    # parameter by about lr times the sign of its gradient, so wherever a
+    # gradient is near zero the direction is decided by rounding.  The bound
+    # per tensor is therefore 5e-2 relative L2, or twice what the oracle
+    # itself shows when only its initial parameters are rounded to bf16 (a
+    # third, CPU-only run; 3-4% for the bias tensors at this rate, and 5-8%
+    # after one step), whichever is larger.  Gains, weights and embeddings
+    # sit far inside 5e-2.
+    o2 = oracle_run(M124, 4, 64, init_rounded=True, **kw)
+    sg, so, s2 = split(g["params"], M124), split(o["params"].astype(np.float64), M124), split(o2["params"], M124)
+    k = kbias_mask(M124)
+    for d in (sg, so, s2):
+        assert np.max(np.abs(d["qkvb"][k])) <= 3 * kw["lr"] * kw["steps"]
+        d["qkvb"] = d["qkvb"][~k]
+    bad = []
+    for n in O.PARAM_NAMES:
+        e, self_e = rel_l2(sg[n], so[n]), rel_l2(s2[n], so[n])
+        print(f"params after 3 steps {n}: {e:.3g} (oracle from rounded init: {self_e:.3g})", flush=True)
+        if e > max(5e-2, 2 * self_e):
+            bad.append((n, e, self_e))
+    assert not bad, bad
 
 
 @pytest.mark.timeout(1200)

@@ -322,6 +322,23 @@ def test_model_gradients_fd(cfg):
     assert np.all(G["wpe"][T * cfg.C:] == 0)
 
 
+def test_key_bias_gradient_vanishes():
+    """A bias on the keys adds q.b_k to every score of a query row, which the
+    softmax cancels: in the fp64 oracle the key-bias slice of the qkv-bias
+    gradient is zero to rounding, while the query- and value-bias slices are
+    not (the reading behind the key-bias carve-out of the GPU parameter
+    comparisons after AdamW steps)."""
+    m = O.Model(TINY, 4, 32, "f64")
+    m.init(1337)
+    x, y = synth.batch(1337, 0, 4, 32, TINY.V, "uniform")
+    m.forward(x, y)
+    m.zero_grad()
+    m.backward()
+    g = m.G()["qkvb"].reshape(TINY.L, 3, TINY.C)
+    assert np.abs(g[:, 1]).max() < 1e-15 * np.abs(g[:, 2]).max()
+    assert np.abs(g[:, 0]).max() > 1e-8
+
+
 def test_backward_accumulates_and_zero_grad_clears():
     m = _randomized_model(TINY, 2, 8, 3, "f64")
     x, y = synth.batch(1, 0, 2, 8, TINY.V, "uniform")

@@ -10,8 +10,9 @@ stream synchronisations, timed with HIP events on the library's stream.
 
 Prints one JSON line: tokens/s (value), MFU against the bf16 dense MFMA peak,
 the roofline of the dominant kernel class (timed live with HIP events around
-each of its launches inside the timed region) and the CPU oracle timed on a
-bounded sample of the same workload.
+each of its launches inside the timed region), the roofline of every class
+(one step each before the timed region) and the CPU oracle timed on bounded
+samples of the same model.
 """
 import argparse
 import json
@@ -67,23 +68,59 @@ def class_work(c, sr=False):
     }
 
 
-def cpu_baseline(c, sample_B, sample_T, seed):
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_step_s(c, B, T, seed, steps=1):
+    """Seconds per fp32 oracle training step (forward, backward, clip 1.0,
+    AdamW) of model c at B x T on Zipf(1.1) tokens."""
     from oracle import oracle as O
     from transformer_lm_train_amd import synth
     cfg = O.Config(L=c["L"], C=c["C"], NH=c["NH"], maxT=c["maxT"], V=c["V"], Vp=c["Vp"])
-    m = O.Model(cfg, sample_B, sample_T)
+    m = O.Model(cfg, B, T)
     m.init(seed)
-    x, y = synth.batch(seed, 0, sample_B, sample_T, c["V"], "zipf")
+    x, y = synth.batch(seed, 0, B, T, c["V"], "zipf")
     t0 = time.perf_counter()
-    m.forward(x, y)
-    m.zero_grad()
-    m.backward()
-    m.clip_grad_norm(1.0)
-    m.adamw(6e-4, 0.9, 0.999, 1e-8, 0.1, 1)
-    dt = time.perf_counter() - t0
-    return {"value": sample_B * sample_T / dt, "unit": "tokens/s", "cores": O.num_threads(), "kind": "oracle",
-            "sample": f"one fp32 oracle training step (forward, backward, clip, AdamW) of the same model at "
-                      f"B={sample_B}, T={sample_T} on Zipf(1.1) tokens: {dt:.2f} s"}
+    for t in range(1, steps + 1):
+        m.forward(x, y)
+        m.zero_grad()
+        m.backward()
+        m.clip_grad_norm(1.0)
+        m.adamw(6e-4, 0.9, 0.999, 1e-8, 0.1, t)
+    return (time.perf_counter() - t0) / steps
+
+
+def cpu_baseline(c, seed):
+    """The fp32 oracle on the host's cores, on bounded samples of the same
+    model: one step at B=1 and the benchmark's T (the headline value, tokens
+    per second), and the 124M-shape step at B=4, T=64 the pages time on a
+    laptop CPU, at all cores and at one thread."""
+    from oracle import oracle as O
+    cores = O.num_threads()
+    print(f"cpu baseline: oracle B=1 T={c['T']} on {cores} threads", flush=True)
+    s1 = _oracle_step_s(c, 1, c["T"], seed)
+    print(f"cpu baseline: oracle B=4 T=64, {cores} threads then 1", flush=True)
+    s_all = _oracle_step_s(c, 4, 64, seed, steps=2)
+    O.set_num_threads(1)
+    try:
+        s_one = _oracle_step_s(c, 4, 64, seed)
+    finally:
+        O.set_num_threads(cores)
+    return {"value": round(c["T"] / s1, 1), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"one fp32 oracle training step (forward, backward, clip, AdamW) of the same model at B=1, "
+                      f"T={c['T']} on Zipf(1.1) tokens: {s1:.2f} s, i.e. per-token throughput of a B=1 step "
+                      f"(the B={c['B']} step would need ~{c['B']}x the activation memory)",
+            "cpu_model": _cpu_model(),
+            "B4_T64": {"s_per_step": round(s_all, 3), "tokens_per_s": round(256 / s_all, 1), "threads": cores},
+            "B4_T64_one_thread": {"s_per_step": round(s_one, 3), "tokens_per_s": round(256 / s_one, 1),
+                                  "threads": 1}}
 
 
 def main():
@@ -94,7 +131,6 @@ def main():
     ap.add_argument("--config", default="124m", choices=sorted(CONFIGS))
     ap.add_argument("--seed", type=int, default=1337)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample", default="4x512", help="BxT of the oracle sample")
     ap.add_argument("--timing-class", default="auto")
     ap.add_argument("--sr", action="store_true",
                     help="bf16 parameters updated by stochastic rounding (no fp32 master) instead of fp32 masters")
@@ -139,9 +175,9 @@ def main():
         print(f"warmup step {i} loss {loss:.4f}", flush=True)
 
     work = class_work(c, args.sr)
+    per_class = {}
     # choose the dominant kernel class: one untimed-region step per class
     if args.timing_class == "auto":
-        per_class = {}
         for k, cls in enumerate(work):
             G.gpt2_kernel_timing_enable(m.h, cls, True)
             step(args.warmup + k % 8)
@@ -191,13 +227,28 @@ def main():
     roof["kernel"] = dom
     roof["avg_launch_ms"] = round(avg_ms, 4)
     roof["launches"] = launches
+    # every class's roofline, from its step of the class selection (HIP events
+    # around each of its launches, outside the timed region)
+    classes = {}
+    for cls, ms in per_class.items():
+        amount_c, unit_c, nl = work[cls]
+        if ms <= 0:
+            continue
+        if unit_c == "flop":
+            a = amount_c / (ms / 1e3) / 1e12
+            classes[cls] = {"bound": "mfma", "ms_per_step": round(ms, 4), "achieved": round(a, 1), "unit": "TFLOP/s",
+                            "frac": round(a / PEAK_BF16_TFLOPS, 4)}
+        else:
+            a = amount_c / (ms / 1e3) / 1e9
+            classes[cls] = {"bound": "hbm", "ms_per_step": round(ms, 4), "achieved": round(a, 1), "unit": "GB/s",
+                            "frac": round(a / PEAK_HBM_GBS, 4)}
+        classes[cls]["launches_per_step"] = nl
+        classes[cls]["traffic"] = pmc_traffic.recorded(cls, args.config)
     m.close()
 
     cpu = None
     if not args.no_cpu_baseline:
-        sb, st = (int(v) for v in args.cpu_sample.split("x"))
-        print(f"cpu baseline: oracle B={sb} T={st}", flush=True)
-        cpu = cpu_baseline(c, sb, st, args.seed)
+        cpu = cpu_baseline(c, args.seed)
 
     out = {
         "metric": "train tokens/s + MFU % for GPT-2 124M bf16 B=16 T=1024 on 1 MI355X",
@@ -219,6 +270,7 @@ def main():
                                + "Zipf(1.1) synthetic tokens", "batch": B, "seq_len": T,
                    "flop_per_token": fpt, "parallelism": "single GPU"},
         "roofline": roof,
+        "roofline_classes": classes,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

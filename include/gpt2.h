@@ -257,6 +257,21 @@ int gpt2_test_attention_fwd(gpt2_t* m, void* out, float* lse, const void* qkv, i
 int gpt2_test_attention_bwd(gpt2_t* m, void* dqkv, const void* dout, const void* qkv, const void* out,
                             const float* lse, int B, int T, int C, int NH);
 
+/* ---- allocation-free variant ------------------------------------------ */
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the causal
+ * attention backward of gpt2_test_attention_bwd (bf16 flash kernels, head
+ * size 64, T a multiple of 64; same arguments and layouts) without a model.
+ * Its per-row scratch (2*B*NH*T floats) is a static device array of the
+ * library, 8 MiB per GPU, held until the process ends: B*NH*T may not exceed
+ * 1048576 (GPT2_EINVAL otherwise).  Runs on hip_stream (a hipStream_t of the
+ * current device; NULL = the default stream) and allocates nothing.  Every
+ * call on one GPU shares that array, so calls that overlap on one GPU (other
+ * streams, other threads) race; calls in one stream are ordered. */
+int gpt2_attention_bwd_noalloc(void* hip_stream, void* dqkv, const void* dout, const void* qkv, const void* out,
+                               const float* lse, int B, int T, int C, int NH);
+
 #ifdef __cplusplus
 }
 #endif

@@ -3,6 +3,9 @@
 #pragma once
 #include "common.h"
 
+// Sets the calling thread's gpt2_last_error() message and returns code.
+int gpt2_report_error(int code, const char* msg);
+
 // ---- matrix products --------------------------------------------------------
 // acc[m][n] = sum_k A(m,k) * B(n,k); an operand is "k-contiguous" when
 // A(m,k) = a[m*lda + k] and "mn-contiguous" when A(m,k) = a[k*lda + m]
@@ -176,3 +179,5 @@ int flash_attention_bias_rows(int B, int T_);
 hipError_t flash_attention_fwd(bf16* out, float* lse, const bf16* qkv, int B, int T_, int C, int NH, hipStream_t s);
 hipError_t flash_attention_bwd(bf16* dqkv, const bf16* dout, const bf16* qkv, const bf16* out, const float* lse,
                                float* dbuf, int B, int T_, int C, int NH, float* bpart, hipStream_t s);
+// floats of dbuf the backward needs
+inline size_t flash_attention_bwd_ws_floats(int B, int T_, int NH) { return 2 * (size_t)B * NH * T_; }

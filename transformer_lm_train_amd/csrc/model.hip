@@ -35,6 +35,14 @@ int fail(int code, const char* fmt, ...) {
     return code;
 }
 
+}  // namespace
+
+// The error message of the calling thread, for the other sources of the
+// library (their C entry points report through gpt2_last_error too).
+int gpt2_report_error(int code, const char* msg) { return fail(code, "%s", msg); }
+
+namespace {
+
 #define HIPCHK(expr)                                                                                     \
     do {                                                                                                 \
         hipError_t e_ = (expr);                                                                          \

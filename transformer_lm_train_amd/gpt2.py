@@ -88,6 +88,7 @@ def lib():
         "gpt2_test_gemm_tn": ([vp, vp, vp, vp, i32, i32, i32], ctypes.c_int),
         "gpt2_test_attention_fwd": ([vp, vp, vp, vp, i32, i32, i32, i32], ctypes.c_int),
         "gpt2_test_attention_bwd": ([vp, vp, vp, vp, vp, vp, i32, i32, i32, i32], ctypes.c_int),
+        "gpt2_attention_bwd_noalloc": ([vp, vp, vp, vp, vp, vp, i32, i32, i32, i32], ctypes.c_int),
     }
     for name, (args, res) in sigs.items():
         fn = getattr(L, name)
@@ -257,6 +258,10 @@ def gpt2_test_attention_fwd(h, out_ptr, lse_ptr, qkv_ptr, B, T, C, NH):
 
 def gpt2_test_attention_bwd(h, dqkv_ptr, dout_ptr, qkv_ptr, out_ptr, lse_ptr, B, T, C, NH):
     _check(lib().gpt2_test_attention_bwd(h, dqkv_ptr, dout_ptr, qkv_ptr, out_ptr, lse_ptr, B, T, C, NH))
+
+
+def gpt2_attention_bwd_noalloc(stream_ptr, dqkv_ptr, dout_ptr, qkv_ptr, out_ptr, lse_ptr, B, T, C, NH):
+    _check(lib().gpt2_attention_bwd_noalloc(stream_ptr, dqkv_ptr, dout_ptr, qkv_ptr, out_ptr, lse_ptr, B, T, C, NH))
 
 
 # ---- convenience wrapper: torch owns the device buffer and the stream -------

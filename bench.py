@@ -42,24 +42,48 @@ def flops_per_token(c):
     return 3 * (L * (24 * C * C + 2 * C * (T + 1)) + 2 * C * V)
 
 
-def class_work(c, sr=False):
-    """Algorithmic work per step of each timed kernel class: (amount, unit)."""
+def class_work(c, sr=False, fused=False):
+    """Algorithmic work per step of each timed kernel class: (amount, unit,
+    launches per step).  With the fused classifier the logits are recomputed
+    in the backward (a class of its own, counted at the classifier's FLOPs)
+    in chunks of up to 4096 rows, each with its dX and dwte products, and the
+    loss pass only combines the per-row statistics."""
     L, C, T, V, B, NH = c["L"], c["C"], c["T"], c["V"], c["B"], c["NH"]
     BT = B * T
     lin = L * 2 * BT * 12 * C * C
     att = L * 2 * C * (T + 1) * BT  # causal QK^T + PV forward
     N = c["Vp"] * C + c["maxT"] * C + L * (12 * C * C + 13 * C) + 2 * C
     Vp = c["Vp"]
+    cls = 2 * BT * C * V
+    if fused:
+        chunks = -(-BT // 4096)
+        head = {
+            "gemm_classifier_fwd": (cls, "flop", 1),
+            "gemm_classifier_recompute": (cls, "flop", chunks),
+            "gemm_classifier_dx": (cls, "flop", chunks),
+            "gemm_classifier_dw": (cls, "flop", chunks),
+            "gemm_fwd": (lin, "flop", 4 * L),
+            "gemm_dx": (lin, "flop", 4 * L),
+            "gemm_dw": (lin, "flop", 1),
+            "attention_fwd": (att, "flop", L),
+            "attention_bwd": (2 * att, "flop", L),
+            # read the (max, sum) pairs and the target logits, write loss and lse
+            "softmax_ce": (8 * BT * (Vp // 64) + 4 * BT + 8 * BT, "byte", 1),
+        }
+    else:
+        head = {
+            "gemm_classifier_fwd": (cls, "flop", 1),
+            "gemm_classifier_dx": (cls, "flop", 1),
+            "gemm_fwd": (lin, "flop", 4 * L),
+            "gemm_dx": (lin, "flop", 4 * L),
+            # every weight gradient, the classifier's included, in one grouped launch
+            "gemm_dw": (lin + cls, "flop", 1),
+            "attention_fwd": (att, "flop", L),
+            "attention_bwd": (2 * att, "flop", L),
+            "softmax_ce": (2 * BT * Vp * 2, "byte", 1),
+        }
     return {
-        "gemm_classifier_fwd": (2 * BT * C * V, "flop", 1),
-        "gemm_classifier_dx": (2 * BT * C * V, "flop", 1),
-        "gemm_fwd": (lin, "flop", 4 * L),
-        "gemm_dx": (lin, "flop", 4 * L),
-        # every weight gradient, the classifier's included, in one grouped launch
-        "gemm_dw": (lin + 2 * BT * C * V, "flop", 1),
-        "attention_fwd": (att, "flop", L),
-        "attention_bwd": (2 * att, "flop", L),
-        "softmax_ce": (2 * BT * Vp * 2, "byte", 1),
+        **head,
         # fp32 master: read theta, g, m, v, write theta, m, v, bf16 copy; stochastic
         # rounding: read bf16 theta, g, m, v, write bf16 theta, m, v
         "adamw": ((24 if sr else 30) * N, "byte", 1),
@@ -132,6 +156,9 @@ def main():
     ap.add_argument("--seed", type=int, default=1337)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--timing-class", default="auto")
+    ap.add_argument("--fused-classifier", action="store_true",
+                    help="classifier product fused with the softmax cross-entropy: no logits stored, the backward "
+                         "recomputes them in chunks")
     ap.add_argument("--sr", action="store_true",
                     help="bf16 parameters updated by stochastic rounding (no fp32 master) instead of fp32 masters")
     args = ap.parse_args()
@@ -147,7 +174,8 @@ def main():
     c = CONFIGS[args.config]
     torch.cuda.set_device(0)
     prec = G.GPT2_BF16_SR if args.sr else G.GPT2_BF16_MIXED
-    cfg = G.make_config(c["L"], c["C"], c["NH"], c["maxT"], c["V"], c["Vp"], c["B"], c["T"], prec)
+    cfg = G.make_config(c["L"], c["C"], c["NH"], c["maxT"], c["V"], c["Vp"], c["B"], c["T"], prec,
+                        args.fused_classifier)
     m = G.Model(cfg, args.seed, device="cuda:0")
     B, T = c["B"], c["T"]
     nb = args.warmup + args.steps + 16
@@ -174,7 +202,7 @@ def main():
         loss = step(i)
         print(f"warmup step {i} loss {loss:.4f}", flush=True)
 
-    work = class_work(c, args.sr)
+    work = class_work(c, args.sr, args.fused_classifier)
     per_class = {}
     # choose the dominant kernel class: one untimed-region step per class
     if args.timing_class == "auto":
@@ -267,6 +295,8 @@ def main():
         "config": {"workload": f"GPT-2 {args.config} training step, "
                                + ("bf16 parameters with stochastic-rounding AdamW (fp32 m/v), " if args.sr else
                                   "bf16 mixed (fp32 master/AdamW), ")
+                               + ("classifier fused with the softmax cross-entropy (logits recomputed in the "
+                                  "backward), " if args.fused_classifier else "")
                                + "Zipf(1.1) synthetic tokens", "batch": B, "seq_len": T,
                    "flop_per_token": fpt, "parallelism": "single GPU"},
         "roofline": roof,

@@ -74,6 +74,15 @@ typedef struct {
     int32_t batch_size;        /* B */
     int32_t seq_len;           /* T <= maxT */
     int32_t precision;         /* GPT2_FP32, GPT2_BF16_MIXED or GPT2_BF16_SR */
+    int32_t fused_classifier;  /* 0: the logits are stored, then the softmax cross-entropy pass turns
+                                  them into dlogits in place (B*T*Vp activations).  1 (bf16 modes
+                                  only): the classifier product computes each row's softmax
+                                  statistics in its epilogue and the logits are never stored; the
+                                  backward recomputes them in chunks of at most 4096 rows, turning
+                                  each tile into dlogits as it leaves the product (the pyshine.com
+                                  tour's fused classifier; "llm.c's Origin and the Future of LLM
+                                  Compilers", "Avengers": recompute during the backward).  Uses
+                                  less memory, adds one classifier product. */
 } gpt2_config;
 
 typedef struct gpt2_model gpt2_t;
@@ -197,7 +206,9 @@ int gpt2_copy_opt_state(gpt2_t* m, float* m_dst, float* v_dst);
 
 /* Copy the last forward's logits [B*T, Vp] to host as fp32.  Only valid
  * after a forward with targets == NULL (a forward with targets overwrites
- * them with dlogits); GPT2_EPERM otherwise. */
+ * them with dlogits); GPT2_EPERM otherwise, and always with the fused
+ * classifier (which keeps no logits; its forward without targets stops
+ * after the final LayerNorm). */
 int gpt2_copy_logits(gpt2_t* m, float* host_dst);
 
 /* Copy the per-position losses [B*T] of the last forward with targets. */

@@ -38,10 +38,11 @@ def test_binding_covers_the_abi():
 
 
 def _cfg(**kw):
-    base = dict(L=12, C=768, NH=12, maxT=1024, V=50257, Vp=50304, B=16, T=1024, precision=G.GPT2_BF16_MIXED)
+    base = dict(L=12, C=768, NH=12, maxT=1024, V=50257, Vp=50304, B=16, T=1024, precision=G.GPT2_BF16_MIXED,
+                fused=False)
     base.update(kw)
     return G.make_config(base["L"], base["C"], base["NH"], base["maxT"], base["V"], base["Vp"], base["B"],
-                         base["T"], base["precision"])
+                         base["T"], base["precision"], base["fused"])
 
 
 def test_plan_sizes():
@@ -85,3 +86,17 @@ def test_plan_stochastic_rounding_mode():
     with pytest.raises(G.GPT2Error) as e:
         G.gpt2_plan(_cfg(NH=6, precision=G.GPT2_BF16_SR))
     assert e.value.code == G.GPT2_EINVAL and "head size 64" in str(e.value)
+
+
+def test_plan_fused_classifier():
+    # no B*T x Vp logits: one 4096-row chunk of dlogits plus 8 bytes per row
+    # and 64-column group of softmax statistics and 8 per row of target logit
+    # and log-sum-exp
+    BT, Vp = 16 * 1024, 50304
+    stats = 8 * BT * (Vp // 64) + 8 * BT
+    saved = G.gpt2_plan(_cfg()) - G.gpt2_plan(_cfg(fused=True))
+    # (plus the classifier's entries in the weight-gradient tile list: a few KB)
+    assert 0 <= saved - (2 * BT * Vp - 2 * 4096 * Vp - stats) <= 8192
+    with pytest.raises(G.GPT2Error) as e:
+        G.gpt2_plan(_cfg(B=4, T=64, precision=G.GPT2_FP32, fused=True))
+    assert e.value.code == G.GPT2_EINVAL and "bf16" in str(e.value)

@@ -39,8 +39,8 @@ def ocfg(d):
     return O.Config(L=d["L"], C=d["C"], NH=d["NH"], maxT=d["maxT"], V=d["V"], Vp=d["Vp"])
 
 
-def gcfg(d, B, T, prec):
-    return G.make_config(d["L"], d["C"], d["NH"], d["maxT"], d["V"], d["Vp"], B, T, prec)
+def gcfg(d, B, T, prec, fused=False):
+    return G.make_config(d["L"], d["C"], d["NH"], d["maxT"], d["V"], d["Vp"], B, T, prec, fused)
 
 
 def split(flat, cfg):
@@ -239,14 +239,22 @@ FULL = {
 }
 
 
+# The fused classifier (logits never stored; the backward recomputes them in
+# chunks of up to 4096 rows) on the narrow model (B*T = 16384: four chunks)
+# and the whole 124M model (the full vocabulary, one chunk).
+FUSED = ["narrow", "124m_b1"]
+
+
 @pytest.mark.timeout(1200)
-@pytest.mark.parametrize("name", list(FULL))
-def test_bf16_gradients_full_token_count(name):
+@pytest.mark.parametrize("name,fused", [(n, False) for n in FULL] + [(n, True) for n in FUSED],
+                         ids=list(FULL) + [n + "_fused_classifier" for n in FUSED])
+def test_bf16_gradients_full_token_count(name, fused):
     cfg, B, T = FULL[name]
     seed = 1337
-    print(f"bf16 gradients {name}: L={cfg['L']} C={cfg['C']} NH={cfg['NH']} V={cfg['V']} B={B} T={T}", flush=True)
+    print(f"bf16 gradients {name}: L={cfg['L']} C={cfg['C']} NH={cfg['NH']} V={cfg['V']} B={B} T={T} "
+          f"fused classifier {fused}", flush=True)
     x, y = synth.batch(seed, 0, B, T, cfg["V"], "zipf")
-    m = G.Model(gcfg(cfg, B, T, G.GPT2_BF16_MIXED), seed)
+    m = G.Model(gcfg(cfg, B, T, G.GPT2_BF16_MIXED, fused), seed)
     loss = m.forward(x, y)
     per_pos = m.losses()
     m.zero_grad()
@@ -431,6 +439,55 @@ def test_api_errors_on_gpu():
         G.gpt2_build(cfg, 1, buf.data_ptr(), need - 256, torch.cuda.current_stream().cuda_stream)
     assert e.value.code == G.GPT2_ENOMEM
     m.close()
+
+
+@pytest.mark.timeout(900)
+def test_fused_classifier_training_steps():
+    """Three clipped AdamW steps in the fused-classifier mode against the
+    oracle (losses within 1e-2 at each of four forwards, parameters after the
+    steps within 5e-2 per tensor, key-bias slice bounded) and against the
+    unfused mode on the GPU; no logits can be copied in that mode."""
+    d = dict(L=2, C=128, NH=2, maxT=1024, V=1000, Vp=1024)
+    B, T = 8, 1024  # 8192 rows: two backward chunks
+    kw = dict(seed=21, dist="zipf", steps=3, lr=3e-4, wd=0.1, clip=1.0, final_loss=True)
+    print(f"fused classifier training B={B} T={T}", flush=True)
+    o = oracle_run(d, B, T, **kw)
+    gf = gpu_run_mode(d, B, T, fused=True, **kw)
+    gu = gpu_run_mode(d, B, T, fused=False, **kw)
+    print(f"losses fused {np.round(gf['losses'], 5)} unfused {np.round(gu['losses'], 5)} "
+          f"oracle {np.round(o['losses'], 5)}", flush=True)
+    for a, b, c in zip(gf["losses"], o["losses"], gu["losses"]):
+        assert abs(a - b) <= 1e-2 and abs(a - c) <= 1e-2
+    compare_tensors(gf["grads0"], o["grads0"], d, 5e-2, check_max=False, what="grads")
+    compare_tensors(gf["params"], o["params"], d, 5e-2, check_max=False, what="params after 3 steps",
+                    kbias_steps=(kw["lr"], kw["steps"]))
+    m = G.Model(gcfg(d, B, T, G.GPT2_BF16_MIXED, True), 21)
+    x, _ = synth.batch(21, 0, B, T, d["V"], "zipf")
+    m.forward(x)
+    with pytest.raises(G.GPT2Error) as e:
+        m.logits()
+    assert e.value.code == G.GPT2_EPERM
+    m.close()
+
+
+def gpu_run_mode(cfg, B, T, fused, **kw):
+    """gpu_run in bf16 mixed mode with or without the fused classifier (no logits read)."""
+    m = G.Model(gcfg(cfg, B, T, G.GPT2_BF16_MIXED, fused), kw["seed"])
+    x, y = synth.batch(kw["seed"], 0, B, T, cfg["V"], kw["dist"])
+    losses, grads0 = [], None
+    for t in range(1, kw["steps"] + 1):
+        losses.append(m.forward(x, y))
+        m.zero_grad()
+        m.backward()
+        if t == 1:
+            grads0 = m.grads()
+        m.clip_grad_norm(kw["clip"])
+        m.adamw_step(kw["lr"], 0.9, 0.999, 1e-8, kw["wd"], t)
+    if kw.get("final_loss"):
+        losses.append(m.forward(x, y))
+    out = dict(losses=losses, grads0=grads0, params=m.params())
+    m.close()
+    return out
 
 
 def test_determinism_fp32_and_bf16():

@@ -141,7 +141,52 @@ DEVI void epilogue_rows(const GemmArgs& g, const f32x16 (&acc)[FM][FN], float* r
                 const float4 u = *reinterpret_cast<const float4*>(red + row * P + cl);
                 const float4 v = *reinterpret_cast<const float4*>(red + row * P + cl + 4);
                 float y[8] = {u.x, u.y, u.z, u.w, v.x, v.y, v.z, v.w};
+                if constexpr (EPI == EPI_CE_STATS) {
+                    // the LPR lanes of a row segment hold its CG columns: their
+                    // max (log2 units) and sum of 2^(z log2 e - max) over the
+                    // columns of the real vocabulary, combined in a fixed
+                    // butterfly order; every lane takes part in the shuffles
+                    constexpr float L2E = 1.4426950408889634f;
+                    float mx = -INFINITY;
+#pragma unroll
+                    for (int e = 0; e < 8; e++)
+                        if (n + e < g.ce_V) mx = fmaxf(mx, y[e] * L2E);
+#pragma unroll
+                    for (int off = 1; off < LPR; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+                    float se = 0.f;
+                    if (mx != -INFINITY) {
+#pragma unroll
+                        for (int e = 0; e < 8; e++)
+                            if (n + e < g.ce_V) se += __builtin_amdgcn_exp2f(fmaf(y[e], L2E, -mx));
+                    }
+#pragma unroll
+                    for (int off = 1; off < LPR; off <<= 1) se += __shfl_xor(se, off, 64);
+                    if (m < g.M) {
+                        // (the last tile column's waves past N hold no group)
+                        if (lane % LPR == 0 && ncol0 + cg * CG < g.N)
+                            g.ce_stats[(int64_t)m * g.ce_ld + (ncol0 + cg * CG) / CG] = make_float2(mx, se);
+                        const int t = g.ce_targets[m];
+#pragma unroll
+                        for (int e = 0; e < 8; e++)
+                            if (n + e == t) g.ce_zt[m] = y[e];
+                    }
+                    continue;
+                }
                 if (m >= g.M || n >= g.N) continue;
+                if constexpr (EPI == EPI_CE_GRAD) {
+                    constexpr float L2E = 1.4426950408889634f;
+                    const int t = g.ce_targets[m];
+                    const float l2 = g.ce_lse2[m];
+                    bf16x8_t d;
+#pragma unroll
+                    for (int e = 0; e < 8; e++) {
+                        float x = n + e < g.ce_V ? __builtin_amdgcn_exp2f(fmaf(y[e], L2E, -l2)) * g.ce_scale : 0.f;
+                        if (n + e == t) x -= g.ce_scale;
+                        d[e] = (bf16)x;
+                    }
+                    *reinterpret_cast<bf16x8_t*>((bf16*)g.out + (int64_t)m * g.ldo + n) = d;
+                    continue;
+                }
                 const int64_t o = (int64_t)m * g.ldo + n;
                 if constexpr (EPI == EPI_PARTIAL) {
                     float* w = g.ws + ((int64_t)split * g.M + m) * g.N + n;
@@ -683,6 +728,44 @@ __global__ void splitk_reduce_kernel(float* out, int64_t ldo, const float* ws, i
     }
 }
 
+// bf16 out = sum over the S fp32 partial tiles ws[s][M][N], in split order
+__global__ void splitk_reduce_bf16_kernel(bf16* out, int64_t ldo, const float* ws, int S, int M, int N) {
+    const int64_t n4 = (int64_t)M * N / 4;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t e = i * 4;
+        const int m = (int)(e / N), n = (int)(e % N);
+        float4 acc = reinterpret_cast<const float4*>(ws)[i];
+        for (int sp = 1; sp < S; sp++) {
+            const float4 v = reinterpret_cast<const float4*>(ws + (int64_t)sp * M * N)[i];
+            acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+        }
+        typedef bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+        *reinterpret_cast<bf16x4_t*>(out + (int64_t)m * ldo + n) = bf16x4_t{(bf16)acc.x, (bf16)acc.y, (bf16)acc.z, (bf16)acc.w};
+    }
+}
+
+// Split of the reduction for a backward-data product with a plain store whose
+// 192-wide tiles fill under one round of the 256 CUs (the fused classifier's
+// chunks: 4096 rows x C outputs over a K of Vp): the split count S <= 8 that
+// minimises rounds(tiles * S) / S, the fewest on a tie, each split at least
+// 16 k-steps long.
+void nn_split_plan(int M, int N, int K, int* splits, int* kchunk) {
+    constexpr int CUS = 256;
+    const int tiles = (int)(cdiv(M, 256) * cdiv(N, 192));
+    int S = 1;
+    if (tiles < CUS) {
+        const int smax = std::min(8, std::max(1, K / (16 * 32)));
+        double best = 1.0;
+        for (int t = 2; t <= smax; t++) {
+            const double cost = (double)((tiles * t + CUS - 1) / CUS) / t;
+            if (cost < best - 1e-9) { best = cost; S = t; }
+        }
+    }
+    const int kc = (int)cdiv(K / KALIGN, S) * KALIGN;
+    *kchunk = kc;
+    *splits = (K + kc - 1) / kc;
+}
+
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
 // Whether 192-wide tiles finish in fewer (tile-size weighted) rounds of one
@@ -825,10 +908,31 @@ hipError_t gemm_mfma_bf16(const GemmArgs& g, hipStream_t s) {
             case EPI_BIAS_RESID:
                 return w192 ? BIG192(true, true, EPI_BIAS_RESID) : BIG256(true, true, EPI_BIAS_RESID);
             case EPI_BIAS_GELU: return w192 ? BIG192(true, true, EPI_BIAS_GELU) : BIG256(true, true, EPI_BIAS_GELU);
+            // the fused classifier: 256-wide tiles, whose waves' 64-column
+            // groups are the statistics' column groups
+            case EPI_CE_STATS:
+                if (!g.ce_targets || !g.ce_stats || !g.ce_zt || g.ce_ld != (int)cdiv(g.N, 64)) return hipErrorInvalidValue;
+                return BIG256(true, true, EPI_CE_STATS);
+            case EPI_CE_GRAD:
+                if (!g.ce_targets || !g.ce_lse2 || !g.out) return hipErrorInvalidValue;
+                return BIG256(true, true, EPI_CE_GRAD);
             default: return hipErrorInvalidValue;
         }
     }
     if (g.a_kcontig && !g.b_kcontig) {
+        if (g.epi == EPI_STORE && g.ws && g.N % 4 == 0 && g.ldo % 4 == 0) {
+            int S, kc;
+            nn_split_plan(g.M, g.N, g.K, &S, &kc);
+            if (S > 1 && (size_t)S * g.M * g.N * 4 <= g.ws_bytes) {
+                hipError_t e =
+                    launch_big<256, 256, 8, 4, 32, GEMM_BIG_NS, GEMM_BIG_XPF, true, false, EPI_PARTIAL, 2, 192>(g, s, S, kc);
+                if (e != hipSuccess) return e;
+                const int64_t n4 = (int64_t)g.M * g.N / 4;
+                const unsigned blocks = (unsigned)std::min<int64_t>((n4 + 255) / 256, 4096);
+                splitk_reduce_bf16_kernel<<<blocks, 256, 0, s>>>((bf16*)g.out, g.ldo, g.ws, S, g.M, g.N);
+                return hipGetLastError();
+            }
+        }
         switch (g.epi) {
             case EPI_STORE: return w192 ? BIG192(true, false, EPI_STORE) : BIG256(true, false, EPI_STORE);
             case EPI_GELU_BWD: return w192 ? BIG192(true, false, EPI_GELU_BWD) : BIG256(true, false, EPI_GELU_BWD);
@@ -858,6 +962,12 @@ hipError_t gemm_mfma_bf16(const GemmArgs& g, hipStream_t s) {
 
 // one partial row per wave row block: 4 per 256-row tile (192-wide tiles), else 2
 int gemm_colsum_rows(int M, int N) { return (int)cdiv(M, 256) * (use_192(M, N) ? 4 : 2); }
+
+size_t gemm_nn_splitk_ws_bytes(int M, int N, int K) {
+    int S, kc;
+    nn_split_plan(M, N, K, &S, &kc);
+    return S > 1 ? (size_t)S * M * N * 4 : 0;
+}
 
 size_t gemm_splitk_ws_bytes(int M, int N, int K) {
     int S, kc;

@@ -17,6 +17,13 @@ enum GemmEpi {
     EPI_BIAS_GELU = 3,   // out = acc + bias[n] (pre-activation); out2 = GELU(that)
     EPI_GELU_BWD = 4,    // out = acc * GELU'(aux[m][n])
     EPI_ACC_F32 = 5,     // out (fp32) += acc
+    // The classifier fused with the softmax cross-entropy (acc = logits z of
+    // row m, column n; columns n >= ce_V are padding):
+    EPI_CE_STATS = 6,    // nothing stored as output: for each row m and each 64-column group q of the
+                         // tile, ce_stats[m][q] = (max z over the group's columns n < ce_V, in log2
+                         // units, and sum of 2^(z log2 e - that max)); ce_zt[m] = z at n = targets[m]
+    EPI_CE_GRAD = 7,     // out (bf16) = (softmax - onehot(targets[m])) * ce_scale, i.e.
+                         // (2^(z log2 e - ce_lse2[m]) - [n == targets[m]]) * ce_scale, 0 for n >= ce_V
 };
 // EPI_ACC_F32 may split the reduction over several workgroups: each writes
 // its fp32 partial tile to ws[split][M][N] and a second kernel adds the
@@ -46,8 +53,22 @@ struct GemmArgs {
     // one row per wave row block: colsum_ws [gemm_colsum_rows(M, N)][N].
     // The caller sums them (sum_partials_batch).  NULL: off.
     float* colsum_ws;
+    // EPI_CE_STATS / EPI_CE_GRAD: row targets (row m of this product), the
+    // real vocabulary, the per-row statistics [M][ce_ld] (float2), the target
+    // logits [M], the rows' log-sum-exp in log2 units [M] and the gradient scale
+    const int* ce_targets;
+    int ce_V;
+    int ce_ld;
+    float2* ce_stats;
+    float* ce_zt;
+    const float* ce_lse2;
+    float ce_scale;
 };
 size_t gemm_splitk_ws_bytes(int M, int N, int K);
+// A backward-data product (dY W, plain store) that fills under half the CUs
+// splits its reduction when GemmArgs.ws holds this many bytes: fp32 partial
+// tiles summed in split order into the bf16 output.
+size_t gemm_nn_splitk_ws_bytes(int M, int N, int K);
 int gemm_colsum_rows(int M, int N);
 // Grouped weight-gradient products (bf16): one launch over the 256 x 256
 // tiles of n problems, each mn-contiguous x mn-contiguous with EPI_ACC_F32.
@@ -92,8 +113,10 @@ hipError_t gemm_mfma_bf16(const GemmArgs& g, hipStream_t s);
 // ---- element-wise and row kernels ------------------------------------------
 // W: the type of the wte / wpe tables (fp32 masters, or the bf16 parameters
 // of the stochastic-rounding mode)
+// Ids outside [0, V) (tokens, and targets when not NULL) are replaced by 0
+// in place and flagged in err_flag (1: a token, 2: a target).
 template <typename T, typename W>
-hipError_t encoder_fwd(T* out, int* tokens, const W* wte, const W* wpe, int B, int T_,
+hipError_t encoder_fwd(T* out, int* tokens, int* targets, const W* wte, const W* wpe, int B, int T_,
                        int C, int V, int* err_flag, hipStream_t s);
 // dwte[tokens[i]] += dx[i] for every position (sorted by token and summed in
 // position order: deterministic), dwpe[t] (+)= sum_b dx[b][t] (overwrite:
@@ -135,6 +158,11 @@ template <typename T>
 hipError_t softmax_ce(T* logits, float* losses, const int* targets, int BT, int V, int Vp, float dscale,
                       int* err_flag, hipStream_t s);
 hipError_t loss_mean(float* out, const float* losses, int n, hipStream_t s);
+// The fused classifier's loss: per row, the G partial (max, sum) pairs of
+// stats [BT][G] (log2 units) combined into the log-sum-exp (lse2, log2
+// units) and loss = lse - z_target.
+hipError_t ce_combine(float* losses, float* lse2, const float2* stats, const float* zt, int BT, int G,
+                      hipStream_t s);
 // norm_scale[0] = ||g||, norm_scale[1] = clip factor (1 if no clip; NaN if
 // the norm is not finite).  adamw multiplies g by norm_scale[1], or by 1 when
 // norm_scale is NULL; on a non-finite factor it writes nothing and sets

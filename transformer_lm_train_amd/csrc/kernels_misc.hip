@@ -14,7 +14,7 @@
 // encoder_forward, token + position embedding)
 // ============================================================================
 template <typename T, typename W>
-__global__ void encoder_fwd_kernel(T* out, int* tokens, const W* wte, const W* wpe, int T_,
+__global__ void encoder_fwd_kernel(T* out, int* tokens, int* targets, const W* wte, const W* wpe, int T_,
                                    int C, int V, int BT, int* err) {
     constexpr int VN = Vec16<T>::N;
     int chunks = C / VN;
@@ -22,6 +22,14 @@ __global__ void encoder_fwd_kernel(T* out, int* tokens, const W* wte, const W* w
     if (i >= (int64_t)BT * chunks) return;
     int row = (int)(i / chunks), ch = (int)(i % chunks);
     int t = row % T_;
+    if (targets && ch == 0) {
+        // targets (when given) are checked here as well, before any reader
+        const int y = targets[row];
+        if (y < 0 || y >= V) {
+            atomicOr(err, 2);
+            targets[row] = 0;
+        }
+    }
     int tok = tokens[row];
     if (tok < 0 || tok >= V) {
         // flag it and replace it by 0 in the model's own token copy, so the
@@ -55,11 +63,11 @@ __global__ void encoder_fwd_kernel(T* out, int* tokens, const W* wte, const W* w
 }
 
 template <typename T, typename W>
-hipError_t encoder_fwd(T* out, int* tokens, const W* wte, const W* wpe, int B, int T_, int C,
+hipError_t encoder_fwd(T* out, int* tokens, int* targets, const W* wte, const W* wpe, int B, int T_, int C,
                        int V, int* err, hipStream_t s) {
     int BT = B * T_;
     int64_t n = (int64_t)BT * (C / Vec16<T>::N);
-    encoder_fwd_kernel<T, W><<<cdiv(n, 256), 256, 0, s>>>(out, tokens, wte, wpe, T_, C, V, BT, err);
+    encoder_fwd_kernel<T, W><<<cdiv(n, 256), 256, 0, s>>>(out, tokens, targets, wte, wpe, T_, C, V, BT, err);
     return LAUNCH_CHECK();
 }
 
@@ -875,6 +883,40 @@ DEVI double block_sum_f64(const float* x, int n, double* red) {
     return red[0];
 }
 
+// The fused classifier's loss, one wave per row: the row's G partial (max,
+// sum) pairs (log2 units; a group with no real column has max -inf and sum 0)
+// combined as M = max of the maxima, S = sum of sum_q 2^(max_q - M), each lane
+// taking groups lane, lane + 64, ... in order and the lanes combined by the
+// fixed-order wave reductions; lse2 = M + log2 S, loss = lse2 ln 2 - z_target.
+__global__ __launch_bounds__(256) void ce_combine_kernel(float* losses, float* lse2, const float2* stats,
+                                                         const float* zt, int BT, int G) {
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (row >= BT) return;  // uniform over the wave
+    const float2* st = stats + (int64_t)row * G;
+    float mx = -INFINITY;
+    for (int q = lane; q < G; q += 64) mx = fmaxf(mx, st[q].x);
+    const float M = wave_max(mx);
+    float se = 0.f;
+    for (int q = lane; q < G; q += 64) {
+        const float2 p = st[q];
+        if (p.x != -INFINITY) se += p.y * __builtin_amdgcn_exp2f(p.x - M);
+    }
+    const float S = wave_sum(se);
+    if (lane == 0) {
+        const float l2 = M + __log2f(S);
+        lse2[row] = l2;
+        losses[row] = l2 * 0.6931471805599453f - zt[row];
+    }
+}
+
+hipError_t ce_combine(float* losses, float* lse2, const float2* stats, const float* zt, int BT, int G,
+                      hipStream_t s) {
+    if (BT <= 0 || G <= 0) return hipErrorInvalidValue;
+    ce_combine_kernel<<<cdiv(BT, 4), 256, 0, s>>>(losses, lse2, stats, zt, BT, G);
+    return LAUNCH_CHECK();
+}
+
 __global__ __launch_bounds__(1024) void loss_mean_kernel(float* out, const float* losses, int n) {
     __shared__ double red[1024];
     const double s = block_sum_f64(losses, n, red);
@@ -1119,8 +1161,8 @@ template <typename T> hipError_t widen_f32(float* dst, const T* src, size_t n, h
 
 // ---- explicit instantiations ------------------------------------------------
 #define INST(T)                                                                                              \
-    template hipError_t encoder_fwd<T, float>(T*, int*, const float*, const float*, int, int, int, int, int*, \
-                                              hipStream_t);                                                  \
+    template hipError_t encoder_fwd<T, float>(T*, int*, int*, const float*, const float*, int, int, int, int,  \
+                                              int*, hipStream_t);                                            \
     template hipError_t encoder_bwd<T>(float*, float*, const T*, const int*, int, int, int, int, int, void*,  \
                                         bool, hipStream_t);                                                  \
     template hipError_t layernorm_fwd<T>(T*, float*, float*, const T*, const float*, const float*, int, int, \
@@ -1132,5 +1174,5 @@ template <typename T> hipError_t widen_f32(float* dst, const T* src, size_t n, h
     template hipError_t widen_f32<T>(float*, const T*, size_t, hipStream_t);
 INST(float)
 INST(bf16)
-template hipError_t encoder_fwd<bf16, bf16>(bf16*, int*, const bf16*, const bf16*, int, int, int, int, int*,
+template hipError_t encoder_fwd<bf16, bf16>(bf16*, int*, int*, const bf16*, const bf16*, int, int, int, int, int*,
                                             hipStream_t);

@@ -79,6 +79,8 @@ struct Layout {
     size_t N32, poff32[NPARAM];
     size_t params, grads, m, v, shadow;
     size_t encoded, ln1, qkv, atty, res2, ln2, fch, fchg, res3, lnf, logits;
+    size_t ce_stats, ce_zt, ce_lse2;  // fused classifier: per-row softmax statistics
+    int ce_rows;                      // fused classifier: rows of the logits region (one backward chunk)
     size_t ln1_mean, ln1_rstd, ln2_mean, ln2_rstd, lnf_mean, lnf_rstd, lse, losses;
     size_t gres3, gres2, gfch, gqkv, dmid, attD, part_fin, part_ln2, part_ln1, part_fc, part_qkv, norm_partial,
         scalars, err, tokens, targets, splitk, dw_probs, dw_tiles, dw_split_tiles, dw_ws, encws;
@@ -115,6 +117,9 @@ int validate(const gpt2_config* c) {
     if (c->seq_len > 1024 || hs > 128) return fail(GPT2_EINVAL, "seq_len <= 1024 and head size <= 128 required");
     if (c->channels > 4096) return fail(GPT2_EINVAL, "channels <= 4096 required");
     if (c->vocab_size >= 256 * 1024 - 1) return fail(GPT2_EINVAL, "vocab_size < 262143 required");
+    if (c->fused_classifier != 0 && c->fused_classifier != 1) return fail(GPT2_EINVAL, "fused_classifier must be 0 or 1");
+    if (c->fused_classifier && !is_bf16(c->precision))
+        return fail(GPT2_EINVAL, "the fused classifier needs a bf16 mode");
     if (is_bf16(c->precision)) {
         if (hs != 64) return fail(GPT2_EINVAL, "the bf16 modes need head size 64");
         if (c->channels % 64 || c->padded_vocab_size % 64 || c->seq_len % 64)
@@ -163,7 +168,18 @@ Layout make_layout(const gpt2_config& c) {
     L.fchg = add(A * Ly * BT * 4 * C);
     L.res3 = add(A * Ly * BT * C);
     L.lnf = add(A * BT * C);
-    L.logits = add(A * BT * c.padded_vocab_size);
+    if (c.fused_classifier) {
+        // no logits are kept: the region holds one backward chunk of dlogits,
+        // and the forward leaves (max, sum) per row and 64-column group
+        L.ce_rows = (int)std::min<size_t>(BT, 4096);
+        L.logits = add(A * (size_t)L.ce_rows * c.padded_vocab_size);
+        L.ce_stats = add(8 * BT * cdiv(c.padded_vocab_size, 64));
+        L.ce_zt = add(4 * BT);
+        L.ce_lse2 = add(4 * BT);
+    } else {
+        L.ce_rows = 0;
+        L.logits = add(A * BT * c.padded_vocab_size);
+    }
     L.ln1_mean = add(4 * Ly * BT);
     L.ln1_rstd = add(4 * Ly * BT);
     L.ln2_mean = add(4 * Ly * BT);
@@ -211,12 +227,14 @@ Layout make_layout(const gpt2_config& c) {
         const int dims[5][2] = {{3 * (int)C, (int)C}, {(int)C, (int)C}, {4 * (int)C, (int)C}, {(int)C, 4 * (int)C},
                                 {c.padded_vocab_size, (int)C}};
         for (auto& d : dims) L.splitk_bytes = std::max(L.splitk_bytes, gemm_splitk_ws_bytes(d[0], d[1], (int)BT));
+        if (c.fused_classifier)  // the chunks' backward-data product
+            L.splitk_bytes = std::max(L.splitk_bytes, gemm_nn_splitk_ws_bytes(L.ce_rows, (int)C, c.padded_vocab_size));
     }
     L.splitk = add(L.splitk_bytes);
     // the token-sorted embedding backward: per-block counts, ranks, offsets,
     // the sorted positions and one fp32 partial row per sorted position
     L.encws = add(encoder_bwd_ws_bytes((int)BT, c.vocab_size, (int)C));
-    L.dw_n = 4 * c.num_layers + 1;
+    L.dw_n = 4 * c.num_layers + (c.fused_classifier ? 0 : 1);  // the fused classifier's runs in its chunks
     L.dw_probs = add(sizeof(GemmArgs) * L.dw_n);
     L.dw_ntiles = 0;
     if (is_bf16(c.precision)) {
@@ -254,7 +272,7 @@ void dw_problems(const gpt2_config& c, const Layout& L, char* base, GemmArgs* ou
         return a;
     };
     int n = 0;
-    out[n++] = prob(g + L.poff[P_WTE], act(L.logits, 0), act(L.lnf, 0), c.padded_vocab_size, C);
+    if (!c.fused_classifier) out[n++] = prob(g + L.poff[P_WTE], act(L.logits, 0), act(L.lnf, 0), c.padded_vocab_size, C);
     for (int l = c.num_layers - 1; l >= 0; l--) {
         const size_t lC = (size_t)l * C;
         out[n++] = prob(g + L.poff[P_FCPROJW] + lC * 4 * C, act(L.gres3, (l + 1) * BTC), act(L.fchg, l * BTC * 4), C,
@@ -465,6 +483,21 @@ template <typename T> const T* weights(gpt2_t* m) {
     else return m->params();
 }
 
+// The tied classifier's product over rows of the final LayerNorm output:
+// out[rows, Vp] = X[rows, C] wte[Vp, C]^T with the fused softmax epilogues.
+template <typename T>
+GemmArgs classifier_args(gpt2_t* Mo, const T* X, const T* wte, int rows, int epi) {
+    const gpt2_config& c = Mo->cfg;
+    GemmArgs g{};
+    g.M = rows; g.N = c.padded_vocab_size; g.K = c.channels;
+    g.a = X; g.lda = c.channels; g.a_kcontig = true;
+    g.b = wte; g.ldb = c.channels; g.b_kcontig = true;
+    g.ldo = c.padded_vocab_size;
+    g.epi = epi;
+    g.ce_V = c.vocab_size;
+    return g;
+}
+
 template <typename T> int forward_impl(gpt2_t* M, bool with_targets) {
     const gpt2_config& c = M->cfg;
     const int B = c.batch_size, T_ = c.seq_len, C = c.channels, NH = c.num_heads, Ly = c.num_layers;
@@ -478,15 +511,16 @@ template <typename T> int forward_impl(gpt2_t* M, bool with_targets) {
     const size_t BTC = a.BTC;
     int* err = M->P<int>(M->L.err);
     int* tok = M->P<int>(M->L.tokens);
+    int* tgt = with_targets ? M->P<int>(M->L.targets) : nullptr;
 
     if constexpr (std::is_same<T, bf16>::value) {
         if (M->srmode()) {  // the bf16 tables are the parameters
-            RUN("encoder_fwd", encoder_fwd<T>(a.encoded, tok, w + po[P_WTE], w + po[P_WPE], B, T_, C, V, err, s));
+            RUN("encoder_fwd", encoder_fwd<T>(a.encoded, tok, tgt, w + po[P_WTE], w + po[P_WPE], B, T_, C, V, err, s));
         } else {
-            RUN("encoder_fwd", encoder_fwd<T>(a.encoded, tok, p + pf[P_WTE], p + pf[P_WPE], B, T_, C, V, err, s));
+            RUN("encoder_fwd", encoder_fwd<T>(a.encoded, tok, tgt, p + pf[P_WTE], p + pf[P_WPE], B, T_, C, V, err, s));
         }
     } else {
-        RUN("encoder_fwd", encoder_fwd<T>(a.encoded, tok, p + pf[P_WTE], p + pf[P_WPE], B, T_, C, V, err, s));
+        RUN("encoder_fwd", encoder_fwd<T>(a.encoded, tok, tgt, p + pf[P_WTE], p + pf[P_WPE], B, T_, C, V, err, s));
     }
     const T* x = a.encoded;
     for (int l = 0; l < Ly; l++) {
@@ -515,6 +549,22 @@ template <typename T> int forward_impl(gpt2_t* M, bool with_targets) {
         x = res3;
     }
     RUN("layernorm_fwd", layernorm_fwd<T>(a.lnf, a.lnfm, a.lnfr, x, p + pf[P_LNFW], p + pf[P_LNFB], BT, C, s));
+    if (c.fused_classifier) {
+        if constexpr (std::is_same<T, bf16>::value) {
+            if (!with_targets) return GPT2_OK;  // no logits are kept: nothing more to compute
+            // logits = lnf wte^T, each row's softmax statistics taken in the
+            // product's epilogue, then combined into the loss
+            GemmArgs g = classifier_args<T>(M, a.lnf, w + po[P_WTE], BT, EPI_CE_STATS);
+            g.ce_targets = tgt;
+            g.ce_ld = (int)cdiv(Vp, 64);
+            g.ce_stats = M->P<float2>(M->L.ce_stats);
+            g.ce_zt = M->P<float>(M->L.ce_zt);
+            RUN("gemm_classifier_fwd", gemm<T>(M, g));
+            RUN("softmax_ce", ce_combine(a.losses, M->P<float>(M->L.ce_lse2), g.ce_stats, g.ce_zt, BT, g.ce_ld, s));
+            RUN("loss_mean", loss_mean(M->P<float>(M->L.scalars), a.losses, BT, s));
+            return GPT2_OK;
+        }
+    }
     RUN("gemm_classifier_fwd", lin_fwd<T>(M, a.logits, a.lnf, w + po[P_WTE], nullptr, BT, Vp, C, EPI_STORE));
     if (with_targets) {
         RUN("softmax_ce", softmax_ce<T>(a.logits, a.losses, M->P<int>(M->L.targets), BT, V, Vp, 1.0f / BT, err, s));
@@ -568,8 +618,46 @@ template <typename T> int backward_impl(gpt2_t* M) {
     auto GF = [&](int l) { return a.gfch + (size_t)l * BTC * 4; };     // d fch
     auto GQ = [&](int l) { return a.gqkv + (size_t)l * BTC * 3; };     // d qkv
 
-    // classifier (tied to wte): logits now hold dlogits
-    RUN("gemm_classifier_dx", lin_dx<T>(M, a.dmid, a.logits, w + po[P_WTE], BT, Vp, C, EPI_STORE));
+    // first backward since gpt2_zero_grad: every gradient's one first writer stores
+    const bool ow = M->grads_zero;
+    if (c.fused_classifier) {
+        if constexpr (std::is_same<T, bf16>::value) {
+            // the logits were never stored: per chunk of rows, recompute them
+            // and leave the product as dlogits, then the chunk's dX rows and its
+            // share of dwte (the first chunk stores after gpt2_zero_grad)
+            const int R = M->L.ce_rows;
+            for (int r0 = 0, ck = 0; r0 < BT; r0 += R, ck++) {
+                const int rows = std::min(R, BT - r0);
+                GemmArgs cr = classifier_args<T>(M, a.lnf + (size_t)r0 * C, w + po[P_WTE], rows, EPI_CE_GRAD);
+                cr.out = a.logits;
+                cr.ce_targets = M->P<int>(M->L.targets) + r0;
+                cr.ce_lse2 = M->P<float>(M->L.ce_lse2) + r0;
+                cr.ce_scale = 1.0f / BT;
+                RUN("gemm_classifier_recompute", gemm<T>(M, cr));
+                {
+                    // dX rows of the chunk (4096 x C outputs over K = Vp: split reduction)
+                    GemmArgs dx{};
+                    dx.M = rows; dx.N = C; dx.K = Vp;
+                    dx.a = a.logits; dx.lda = Vp; dx.a_kcontig = true;
+                    dx.b = w + po[P_WTE]; dx.ldb = C; dx.b_kcontig = false;
+                    dx.out = a.dmid + (size_t)r0 * C; dx.ldo = C; dx.epi = EPI_STORE;
+                    dx.ws = M->P<float>(M->L.splitk);
+                    dx.ws_bytes = M->L.splitk_bytes;
+                    RUN("gemm_classifier_dx", gemm<T>(M, dx));
+                }
+                GemmArgs d{};
+                d.M = Vp; d.N = C; d.K = rows;
+                d.a = a.logits; d.lda = Vp; d.a_kcontig = false;
+                d.b = a.lnf + (size_t)r0 * C; d.ldb = C; d.b_kcontig = false;
+                d.out = g + po[P_WTE]; d.ldo = C; d.epi = EPI_ACC_F32;
+                d.acc_overwrite = ow && ck == 0;
+                RUN("gemm_classifier_dw", gemm<T>(M, d));
+            }
+        }
+    } else {
+        // classifier (tied to wte): logits now hold dlogits
+        RUN("gemm_classifier_dx", lin_dx<T>(M, a.dmid, a.logits, w + po[P_WTE], BT, Vp, C, EPI_STORE));
+    }
     const T* xlast = a.res3 + (size_t)(Ly - 1) * BTC;
     // Bias gradients are column sums of the output gradients, taken as
     // partial rows by the kernel that produces each gradient and summed in a
@@ -580,8 +668,6 @@ template <typename T> int backward_impl(gpt2_t* M) {
     // a column-sum pass each).  The weight gradients, which nothing in the
     // backward reads, are all taken at its end from the kept gradients.
     constexpr bool fused = std::is_same<T, bf16>::value;
-    // first backward since gpt2_zero_grad: every gradient's one first writer stores
-    const bool ow = M->grads_zero;
     std::vector<SumJob>& jobs = M->sum_jobs;  // every block's sums, run in one batch after the block loop
     jobs.clear();
     jobs.reserve(4 * (size_t)Ly + 1);
@@ -627,7 +713,7 @@ template <typename T> int backward_impl(gpt2_t* M) {
                               pln1, Gln, C});
     }
     RUN("bias_sums", sum_partials_batch(jobs.data(), (int)jobs.size(), ow, s));
-    RUN("gemm_dw", weight_grads<T>(M, ow));  // the classifier's product writes every wte row first
+    RUN("gemm_dw", weight_grads<T>(M, ow));  // the classifier's product (or chunks) wrote every wte row first
     RUN("encoder_bwd", encoder_bwd<T>(g + po[P_WTE], g + po[P_WPE], G3(-1), M->P<int>(M->L.tokens), B, T_,
                                       c.max_seq_len, C, c.vocab_size, M->base + M->L.encws, ow, s));
     M->grads_zero = false;
@@ -992,6 +1078,7 @@ int gpt2_copy_opt_state(gpt2_t* M, float* mdst, float* vdst) {
 
 int gpt2_copy_logits(gpt2_t* M, float* dst) {
     if (!M || !dst) return fail(GPT2_EINVAL, "NULL argument");
+    if (M->cfg.fused_classifier) return fail(GPT2_EPERM, "the fused classifier keeps no logits");
     if (!M->logits_valid) return fail(GPT2_EPERM, "logits are only kept by a forward without targets");
     size_t n = (size_t)M->cfg.batch_size * M->cfg.seq_len * M->cfg.padded_vocab_size;
     if (M->bf16mode()) {

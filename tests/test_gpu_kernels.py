@@ -81,16 +81,19 @@ def test_gemm_kernels_vs_oracle(prec, cases, dt, tol):
 
 
 def test_gemm_tile_widths_at_scale():
-    """Forward (NT) and backward-data (NN) products with M = 16384 rows, at
+    """Forward (NT) and backward-data (NN) products with thousands of rows, at
     output widths that select the 256-wide tile (3072) and the 192-wide tile
-    (768), checked on sampled rows (first, last, random) against the oracle
-    run on those rows alone (each output row depends only on its input row)."""
+    (768, 2304), in one round of tiles (768) or as the persistent schedule
+    over several (3072, 2304, and a ragged 8200 x 2056: 297 tiles, not a
+    multiple of the 8 XCDs), checked on sampled rows (first, last, random)
+    against the oracle run on those rows alone (each output row depends only
+    on its input row)."""
     m = _model(G.GPT2_BF16_MIXED)
     rng = np.random.default_rng(2)
-    M, R = 16384, 64
-    rows = np.unique(np.concatenate([np.arange(64), np.arange(M - 64, M), rng.integers(0, M, 128)]))
-    for N in (3072, 768):
-        print(f"gemm tile width N={N}", flush=True)
+    R = 64
+    for M, N in ((16384, 3072), (16384, 768), (16384, 2304), (8200, 2056)):
+        rows = np.unique(np.concatenate([np.arange(64), np.arange(M - 64, M), rng.integers(0, M, 128)]))
+        print(f"gemm tile width M={M} N={N}", flush=True)
         # forward: out[M,N] = x[M,R] W[N,R]^T + b
         x = _dev(rng.standard_normal((M, R)), torch.bfloat16)
         w = _dev(rng.standard_normal((N, R)) * 0.1, torch.bfloat16)

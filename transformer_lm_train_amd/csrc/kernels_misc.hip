@@ -392,6 +392,86 @@ __global__ __launch_bounds__(256) void layernorm_fwd_kernel(T* out, float* mean,
     }
 }
 
+// The same LayerNorm with each wave taking rows row0, row0 + step, ...
+// (step = 4 x the grid): the lane's gains and biases are read once into
+// registers, and the next row's chunks are requested before the current row
+// is worked.  Per-lane sums run over the chunks in the same order as above,
+// so the results are the same bit for bit.
+template <typename T, int MAXV>
+__global__ __launch_bounds__(256) void layernorm_fwd_rows_kernel(T* out, float* mean, float* rstd, const T* x,
+                                                                 const float* w, const float* b, int N, int C) {
+    constexpr int VN = Vec16<T>::N;
+    const int lane = threadIdx.x & 63;
+    const int step = gridDim.x * 4;
+    int row = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int chunks = C / VN;
+    float wr[MAXV][VN], br[MAXV][VN];
+#pragma unroll
+    for (int i = 0; i < MAXV; i++) {
+        const int ch = lane + i * 64;
+#pragma unroll
+        for (int j = 0; j < VN; j += 4) {
+            float4 u = make_float4(0.f, 0.f, 0.f, 0.f), v = u;
+            if (ch < chunks) {
+                u = *reinterpret_cast<const float4*>(w + ch * VN + j);
+                v = *reinterpret_cast<const float4*>(b + ch * VN + j);
+            }
+            wr[i][j] = u.x; wr[i][j + 1] = u.y; wr[i][j + 2] = u.z; wr[i][j + 3] = u.w;
+            br[i][j] = v.x; br[i][j + 1] = v.y; br[i][j + 2] = v.z; br[i][j + 3] = v.w;
+        }
+    }
+    Vec16<T> q[MAXV], qn[MAXV];
+    auto load = [&](Vec16<T>(&dst)[MAXV], int r) {
+#pragma unroll
+        for (int i = 0; i < MAXV; i++) {
+            const int ch = lane + i * 64;
+            if (ch < chunks) dst[i] = ld16(x + (int64_t)r * C + ch * VN);
+        }
+    };
+    if (row < N) load(q, row);
+    for (; row < N; row += step) {
+        if (row + step < N) load(qn, row + step);
+        float s = 0.f;
+#pragma unroll
+        for (int i = 0; i < MAXV; i++)
+            if (lane + i * 64 < chunks)
+#pragma unroll
+                for (int j = 0; j < VN; j++) s += to_f32(q[i].v[j]);
+        const float mu = wave_sum(s) / C;
+        float ss = 0.f;
+#pragma unroll
+        for (int i = 0; i < MAXV; i++)
+            if (lane + i * 64 < chunks)
+#pragma unroll
+                for (int j = 0; j < VN; j++) {
+                    const float d = to_f32(q[i].v[j]) - mu;
+                    ss += d * d;
+                }
+        const float rs = rsqrtf(wave_sum(ss) / C + 1e-5f);
+        T* orow = out + (int64_t)row * C;
+#pragma unroll
+        for (int i = 0; i < MAXV; i++) {
+            const int ch = lane + i * 64;
+            if (ch < chunks) {
+                Vec16<T> o;
+#pragma unroll
+                for (int j = 0; j < VN; j++) o.v[j] = from_f32<T>((to_f32(q[i].v[j]) - mu) * rs * wr[i][j] + br[i][j]);
+                st16(orow + ch * VN, o);
+            }
+        }
+        if (lane == 0) {
+            mean[row] = mu;
+            rstd[row] = rs;
+        }
+#pragma unroll
+        for (int i = 0; i < MAXV; i++) q[i] = qn[i];
+    }
+}
+
+#ifndef LN_FWD_ROWS_PER_WAVE
+#define LN_FWD_ROWS_PER_WAVE 4
+#endif
+
 template <typename T>
 hipError_t layernorm_fwd(T* out, float* mean, float* rstd, const T* x, const float* w, const float* b, int N,
                          int C, hipStream_t s) {
@@ -401,11 +481,14 @@ hipError_t layernorm_fwd(T* out, float* mean, float* rstd, const T* x, const flo
     // lane (C = 768 in bf16: more, shorter waves overlap one block's stores
     // with another's loads, ~3% faster than 4 rows per wave), two beyond
 #define LN_FWD(V, R) layernorm_fwd_kernel<T, V, R><<<cdiv(N, 4 * R), 256, 0, s>>>(out, mean, rstd, x, w, b, N, C)
+#define LN_FWD_ROWS(V)                                                                                            \
+    layernorm_fwd_rows_kernel<T, V><<<cdiv(N, 4 * LN_FWD_ROWS_PER_WAVE), 256, 0, s>>>(out, mean, rstd, x, w, b, N, C)
     if (per_lane <= 1) LN_FWD(1, 4);
-    else if (per_lane <= 2) LN_FWD(2, 1);
-    else if (per_lane <= 4) LN_FWD(4, 2);
+    else if (per_lane <= 2) LN_FWD_ROWS(2);
+    else if (per_lane <= 4) LN_FWD_ROWS(4);
     else LN_FWD(8, 1);
 #undef LN_FWD
+#undef LN_FWD_ROWS
     return LAUNCH_CHECK();
 }
 

@@ -314,7 +314,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
 }
 
 // ---------------------------------------------------------------------------
-// Dout[row] = rowsum(dO o O) and Lout[row] = -lse * log2(e), for the dK/dV kernel
+// Dout[row] = -rowsum(dO o O) and Lout[row] = -lse * log2(e), for the dK/dV kernel
 // bpart (optional): per-(batch, 128-row block) column sums of the dq / dk / dv
 // written, one row [3C] per block: the partials of the qkv bias gradient.
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void flash_bwd_dq_kernel(bf16* dqkv, float* Dout, float* Lout, const bf16* dout,
@@ -351,7 +351,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const float Dq = dsum + __shfl_xor(dsum, 32, 64);
     const int64_t ri = ((int64_t)b * NH + h) * T + q;
     const float nl2 = qok ? -lse[ri] * LOG2E : 0.f;
-    if (qok && hi == 0) { Dout[ri] = Dq; Lout[ri] = nl2; }
+    if (qok && hi == 0) { Dout[ri] = -Dq; Lout[ri] = nl2; }
+    // dP^T - D straight out of the matrix core: its accumulators start at -D
+    // (the query's, the same in every register of the lane)
+    f32x16 negD;
+#pragma unroll
+    for (int r = 0; r < 16; r++) negD[r] = -Dq;
     const float sc = 0.125f * LOG2E;
 
     f32x16 dq[2] = {zero16(), zero16()};
@@ -370,7 +375,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
         for (int t = 0; t < 2; t++) {
             s[t] = zero16();
-            dp[t] = zero16();
+            dp[t] = negD;
 #pragma unroll
             for (int ks = 0; ks < 4; ks++) {
                 s[t] = mfma(frag_row(Ks, t * 32 + lq, ks * 2 + hi), qf[ks], s[t]);
@@ -391,7 +396,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
             for (int r = 0; r < 16; r++) {
                 const float pr = exp2_raw(fmaf(s[t][r], sc, nl2));
-                s[t][r] = pr * (dp[t][r] - Dq);  // dS^T
+                s[t][r] = pr * dp[t][r];  // dS^T = P^T (dP^T - D)
             }
 #pragma unroll
         for (int t = 0; t < 2; t++)
@@ -463,7 +468,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // ---------------------------------------------------------------------------
 // Per-query statistics of a 64-query block, one 1 KB load per wave into the
 // wave's own region: lanes 0..15 bring L[q0 .. q0+63] (-lse log2 e), lanes
-// 16..31 D[...], lanes 32..63 repeat lane 0's read (unused).  Needs T % 64 == 0.
+// 16..31 -D[...], lanes 32..63 repeat lane 0's read (unused).  Needs T % 64 == 0.
 DEVI const float* stats_lane_ptr(const float* L, const float* D, int64_t rbase, int lane) {
     return lane < 16 ? L + rbase + 4 * lane : lane < 32 ? D + rbase + 4 * (lane - 16) : L + rbase;
 }
@@ -522,7 +527,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         // one 32-query half at a time keeps only 32 score registers live
 #pragma unroll
         for (int t = 0; t < 2; t++) {
-            f32x16 s = zero16(), dp = zero16();
+            // dP - D straight out of the matrix core: the accumulators start at
+            // -D of each register's query (registers 4g..4g+3 cover 4
+            // consecutive queries: one float4 of the stats each)
+            f32x16 s = zero16(), dp;
+#pragma unroll
+            for (int g = 0; g < 4; g++) {
+                const float4 D4 = *reinterpret_cast<const float4*>(sd + t * 32 + 8 * g + 4 * hi);
+                dp[4 * g] = D4.x; dp[4 * g + 1] = D4.y; dp[4 * g + 2] = D4.z; dp[4 * g + 3] = D4.w;
+            }
 #pragma unroll
             for (int ks = 0; ks < 4; ks++) {
                 s = mfma(frag_row(Qs, t * 32 + lq, ks * 2 + hi), kf[ks], s);
@@ -540,14 +553,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             for (int g = 0; g < 4; g++) {
                 const int ql0 = t * 32 + 8 * g + 4 * hi;
                 const float4 L4 = *reinterpret_cast<const float4*>(sl + ql0);
-                const float4 D4 = *reinterpret_cast<const float4*>(sd + ql0);
-                const float Lv[4] = {L4.x, L4.y, L4.z, L4.w}, Dv[4] = {D4.x, D4.y, D4.z, D4.w};
+                const float Lv[4] = {L4.x, L4.y, L4.z, L4.w};
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
                     const int r = 4 * g + e;
                     const float pr = exp2_raw(fmaf(s[r], sc, Lv[e]));
                     s[r] = pr;
-                    dp[r] = pr * (dp[r] - Dv[e]);
+                    dp[r] = pr * dp[r];  // dS = P (dP - D)
                 }
             }
 #pragma unroll

@@ -198,7 +198,7 @@ template <typename T>
 hipError_t attention_bwd(T* dqkv, const T* dout, const T* qkv, const T* out, const float* lse, float* dbuf,
                          int B, int T_, int C, int NH, hipStream_t s);
 // head size 64, bf16, MFMA flash kernels, T % 64 == 0; dbuf holds 2*B*NH*T
-// floats: D = rowsum(dO o O), then -lse*log2(e), one per (b, h, t).  With
+// floats: -D = -rowsum(dO o O), then -lse*log2(e), one per (b, h, t).  With
 // bpart, the backward also writes partial column sums of dqkv (the qkv bias
 // gradient) to bpart [flash_attention_bias_rows(B, T)][3C], one row per
 // (batch, 128-query block); the caller sums them (sum_partials_batch).

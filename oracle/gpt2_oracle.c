@@ -186,41 +186,40 @@ void orc_init_params(const orc_config* g, uint64_t seed, REAL* params) {
 /* layer functions (forward / backward pairs of [P5] section 2)             */
 /* ------------------------------------------------------------------------ */
 
-/* out[b,t,:] = wte[inp[b,t],:] + wpe[t,:] */
-void orc_encoder_forward(REAL* out, const int* inp, const REAL* wte, const REAL* wpe,
-                         int B, int T, int C) {
+/* Token plus position embedding: x[b,t,:] = wte[tok[b,t],:] + wpe[t,:]. */
+void orc_embed_fwd(const int* tok, const REAL* wte, const REAL* wpe, int B, int T, int C, REAL* x) {
     #pragma omp parallel for collapse(2)
     for (int b = 0; b < B; b++)
         for (int t = 0; t < T; t++) {
-            REAL* o = out + ((size_t)b * T + t) * C;
-            const REAL* we = wte + (size_t)inp[b * T + t] * C;
+            REAL* o = x + ((size_t)b * T + t) * C;
+            const REAL* we = wte + (size_t)tok[b * T + t] * C;
             const REAL* pe = wpe + (size_t)t * C;
             for (int c = 0; c < C; c++) o[c] = we[c] + pe[c];
         }
 }
 
-/* dwte[inp[b,t],:] += dout[b,t,:]; dwpe[t,:] += dout[b,t,:].  Parallel over
- * channels only, each channel summed over (b,t) in order. */
-void orc_encoder_backward(REAL* dwte, REAL* dwpe, const REAL* dout, const int* inp,
-                          int B, int T, int C) {
+/* Its gradient: dwte[tok[b,t],:] += dx[b,t,:]; dwpe[t,:] += dx[b,t,:].
+ * Parallel over channels only, each channel summed over (b,t) in order. */
+void orc_embed_bwd(const REAL* dx, const int* tok, int B, int T, int C, REAL* dwte, REAL* dwpe) {
     #pragma omp parallel for
     for (int c = 0; c < C; c++) {
         for (int b = 0; b < B; b++)
             for (int t = 0; t < T; t++) {
-                REAL d = dout[((size_t)b * T + t) * C + c];
-                dwte[(size_t)inp[b * T + t] * C + c] += d;
+                REAL d = dx[((size_t)b * T + t) * C + c];
+                dwte[(size_t)tok[b * T + t] * C + c] += d;
                 dwpe[(size_t)t * C + c] += d;
             }
     }
 }
 
-/* LayerNorm over the last dim of N rows: biased variance, eps = 1e-5;
- * saves mean and rstd = 1/sqrt(var+eps) for the backward ([P1] "Pure C"). */
-void orc_layernorm_forward(REAL* out, REAL* mean, REAL* rstd, const REAL* inp,
-                           const REAL* w, const REAL* b, int N, int C) {
+/* Layer normalisation of each of `rows` rows of width C: biased variance,
+ * eps = 1e-5, y = (x - mu) * rs * gain + shift with rs = 1/sqrt(var+eps);
+ * mu and rs are kept for the backward ([P1] "Pure C"). */
+void orc_norm_fwd(const REAL* xin, const REAL* gain, const REAL* shift, int rows, int C,
+                  REAL* y, REAL* mu, REAL* rs) {
     #pragma omp parallel for
-    for (int n = 0; n < N; n++) {
-        const REAL* x = inp + (size_t)n * C;
+    for (int n = 0; n < rows; n++) {
+        const REAL* x = xin + (size_t)n * C;
         ACC m = 0;
         for (int c = 0; c < C; c++) m += x[c];
         m /= C;
@@ -228,103 +227,101 @@ void orc_layernorm_forward(REAL* out, REAL* mean, REAL* rstd, const REAL* inp,
         for (int c = 0; c < C; c++) { ACC d = x[c] - m; v += d * d; }
         v /= C;
         ACC r = 1.0 / sqrt(v + 1e-5);
-        REAL* o = out + (size_t)n * C;
-        for (int c = 0; c < C; c++) o[c] = (REAL)(((x[c] - m) * r) * w[c] + b[c]);
-        mean[n] = (REAL)m;
-        rstd[n] = (REAL)r;
+        REAL* o = y + (size_t)n * C;
+        for (int c = 0; c < C; c++) o[c] = (REAL)(((x[c] - m) * r) * gain[c] + shift[c]);
+        mu[n] = (REAL)m;
+        rs[n] = (REAL)r;
     }
 }
 
-/* With xhat = (x-mean)*rstd and g = dout*w:
- *   dinp += rstd * (g - mean_c(g) - xhat * mean_c(g*xhat))
- *   dw   += sum_rows dout*xhat,   db += sum_rows dout. */
-void orc_layernorm_backward(REAL* dinp, REAL* dw, REAL* db, const REAL* dout,
-                            const REAL* inp, const REAL* w, const REAL* mean,
-                            const REAL* rstd, int N, int C) {
+/* Its gradient, with xhat = (x-mu)*rs and g = dy*gain:
+ *   dx     += rs * (g - mean_c(g) - xhat * mean_c(g*xhat))
+ *   dgain  += sum_rows dy*xhat,   dshift += sum_rows dy. */
+void orc_norm_bwd(const REAL* dyin, const REAL* xin, const REAL* gain, const REAL* mu, const REAL* rs,
+                  int rows, int C, REAL* dxout, REAL* dgain, REAL* dshift) {
     #pragma omp parallel for
-    for (int n = 0; n < N; n++) {
-        const REAL* x = inp + (size_t)n * C;
-        const REAL* dy = dout + (size_t)n * C;
-        ACC m = mean[n], r = rstd[n];
+    for (int n = 0; n < rows; n++) {
+        const REAL* x = xin + (size_t)n * C;
+        const REAL* dy = dyin + (size_t)n * C;
+        ACC m = mu[n], r = rs[n];
         ACC sg = 0, sgx = 0;
         for (int c = 0; c < C; c++) {
             ACC xh = (x[c] - m) * r;
-            ACC gg = (ACC)dy[c] * w[c];
+            ACC gg = (ACC)dy[c] * gain[c];
             sg += gg;
             sgx += gg * xh;
         }
         sg /= C;
         sgx /= C;
-        REAL* dx = dinp + (size_t)n * C;
+        REAL* dx = dxout + (size_t)n * C;
         for (int c = 0; c < C; c++) {
             ACC xh = (x[c] - m) * r;
-            ACC gg = (ACC)dy[c] * w[c];
+            ACC gg = (ACC)dy[c] * gain[c];
             dx[c] = (REAL)(dx[c] + r * (gg - sg - xh * sgx));
         }
     }
     #pragma omp parallel for
     for (int c = 0; c < C; c++) {
         ACC aw = 0, ab = 0;
-        for (int n = 0; n < N; n++) {
-            ACC xh = (inp[(size_t)n * C + c] - (ACC)mean[n]) * rstd[n];
-            ACC d = dout[(size_t)n * C + c];
+        for (int n = 0; n < rows; n++) {
+            ACC xh = (xin[(size_t)n * C + c] - (ACC)mu[n]) * rs[n];
+            ACC d = dyin[(size_t)n * C + c];
             aw += d * xh;
             ab += d;
         }
-        dw[c] = (REAL)(dw[c] + aw);
-        db[c] = (REAL)(db[c] + ab);
+        dgain[c] = (REAL)(dgain[c] + aw);
+        dshift[c] = (REAL)(dshift[c] + ab);
     }
 }
 
-/* Linear layer y = x W^T + b on N rows: inp (N,C), w (OC,C), bias (OC) or
- * NULL, out (N,OC).  ([P5] section 2: matmul_forward(out, inp, w, b, ...)) */
-void orc_matmul_forward(REAL* out, const REAL* inp, const REAL* w, const REAL* bias,
-                        int N, int C, int OC) {
+/* Affine map y = x W^T + bias on `rows` rows: x (rows,in), W (out,in)
+ * row-major, bias (out) or NULL, y (rows,out). */
+void orc_linear_fwd(const REAL* xin, const REAL* W, const REAL* bias, int rows, int in, int out, REAL* y) {
     #pragma omp parallel for
-    for (int n = 0; n < N; n++) {
-        const REAL* x = inp + (size_t)n * C;
-        for (int o = 0; o < OC; o++) {
-            const REAL* wr = w + (size_t)o * C;
+    for (int n = 0; n < rows; n++) {
+        const REAL* x = xin + (size_t)n * in;
+        for (int o = 0; o < out; o++) {
+            const REAL* wr = W + (size_t)o * in;
             ACC acc = bias ? (ACC)bias[o] : 0.0;
             #pragma omp simd reduction(+:acc)
-            for (int c = 0; c < C; c++) acc += (ACC)x[c] * wr[c];
-            out[(size_t)n * OC + o] = (REAL)acc;
+            for (int c = 0; c < in; c++) acc += (ACC)x[c] * wr[c];
+            y[(size_t)n * out + o] = (REAL)acc;
         }
     }
 }
 
-/* Backward of the linear layer, each forward "out += inp*w" read in reverse:
- *   dinp += dout W,  dw += dout^T inp,  dbias += sum_rows dout. */
-void orc_matmul_backward(REAL* dinp, REAL* dw, REAL* dbias, const REAL* dout,
-                         const REAL* inp, const REAL* w, int N, int C, int OC) {
+/* Its gradient, every product of the forward taken in reverse:
+ *   dx += dy W,  dW += dy^T x,  dbias += sum_rows dy  (dbias may be NULL). */
+void orc_linear_bwd(const REAL* dy, const REAL* xin, const REAL* W, int rows, int in, int out,
+                    REAL* dx, REAL* dW, REAL* dbias) {
     #pragma omp parallel
     {
-        ACC* acc = (ACC*)malloc(sizeof(ACC) * (size_t)C);
+        ACC* acc = (ACC*)malloc(sizeof(ACC) * (size_t)in);
         #pragma omp for
-        for (int n = 0; n < N; n++) {
-            for (int c = 0; c < C; c++) acc[c] = 0;
-            for (int o = 0; o < OC; o++) {
-                ACC d = dout[(size_t)n * OC + o];
-                const REAL* wr = w + (size_t)o * C;
+        for (int n = 0; n < rows; n++) {
+            for (int c = 0; c < in; c++) acc[c] = 0;
+            for (int o = 0; o < out; o++) {
+                ACC d = dy[(size_t)n * out + o];
+                const REAL* wr = W + (size_t)o * in;
                 #pragma omp simd
-                for (int c = 0; c < C; c++) acc[c] += d * wr[c];
+                for (int c = 0; c < in; c++) acc[c] += d * wr[c];
             }
-            REAL* dx = dinp + (size_t)n * C;
-            for (int c = 0; c < C; c++) dx[c] = (REAL)(dx[c] + acc[c]);
+            REAL* dxr = dx + (size_t)n * in;
+            for (int c = 0; c < in; c++) dxr[c] = (REAL)(dxr[c] + acc[c]);
         }
         #pragma omp for
-        for (int o = 0; o < OC; o++) {
-            for (int c = 0; c < C; c++) acc[c] = 0;
+        for (int o = 0; o < out; o++) {
+            for (int c = 0; c < in; c++) acc[c] = 0;
             ACC ab = 0;
-            for (int n = 0; n < N; n++) {
-                ACC d = dout[(size_t)n * OC + o];
-                const REAL* x = inp + (size_t)n * C;
+            for (int n = 0; n < rows; n++) {
+                ACC d = dy[(size_t)n * out + o];
+                const REAL* x = xin + (size_t)n * in;
                 ab += d;
                 #pragma omp simd
-                for (int c = 0; c < C; c++) acc[c] += d * x[c];
+                for (int c = 0; c < in; c++) acc[c] += d * x[c];
             }
-            REAL* dwr = dw + (size_t)o * C;
-            for (int c = 0; c < C; c++) dwr[c] = (REAL)(dwr[c] + acc[c]);
+            REAL* dwr = dW + (size_t)o * in;
+            for (int c = 0; c < in; c++) dwr[c] = (REAL)(dwr[c] + acc[c]);
             if (dbias) dbias[o] = (REAL)(dbias[o] + ab);
         }
         free(acc);
@@ -332,11 +329,12 @@ void orc_matmul_backward(REAL* dinp, REAL* dw, REAL* dbias, const REAL* dout,
 }
 
 /* Causal multi-head self-attention on qkv (B,T,3C) packed q|k|v, head h
- * owning channels [h*hs, (h+1)*hs) of each block.  For t2 <= t:
- * preatt = q_t . k_t2 / sqrt(hs); att = softmax over t2 <= t (max
- * subtracted); out_t = sum_t2 att * v_t2.  Entries with t2 > t are 0. */
-void orc_attention_forward(REAL* out, REAL* preatt, REAL* att, const REAL* qkv,
-                           int B, int T, int C, int NH) {
+ * owning channels [h*hs, (h+1)*hs) of each third.  For keys t2 <= t:
+ * score = q_t . k_t2 / sqrt(hs); weight = softmax of the scores over t2 <= t
+ * (the row maximum subtracted first); y_t = sum_t2 weight * v_t2.  The
+ * scores go to pre and the weights to att, both (B,NH,T,T), with 0 where
+ * t2 > t. */
+void orc_attn_fwd(const REAL* qkv, int B, int T, int C, int NH, REAL* y, REAL* preatt, REAL* att) {
     int hs = C / NH;
     ACC scale = 1.0 / sqrt((ACC)hs);
     size_t C3 = 3 * (size_t)C;
@@ -362,26 +360,25 @@ void orc_attention_forward(REAL* out, REAL* preatt, REAL* att, const REAL* qkv,
                     if (t2 <= t) a[t2] = (REAL)(exp((ACC)pre[t2] - mx) / den);
                     else { a[t2] = 0; pre[t2] = 0; }
                 }
-                REAL* o = out + ((size_t)b * T + t) * C + (size_t)h * hs;
+                REAL* o = y + ((size_t)b * T + t) * C + (size_t)h * hs;
                 for (int i = 0; i < hs; i++) {
-                    ACC y = 0;
+                    ACC acc = 0;
                     for (int t2 = 0; t2 <= t; t2++) {
                         const REAL* v = qkv + ((size_t)b * T + t2) * C3 + 2 * (size_t)C + (size_t)h * hs;
-                        y += (ACC)a[t2] * v[i];
+                        acc += (ACC)a[t2] * v[i];
                     }
-                    o[i] = (REAL)y;
+                    o[i] = (REAL)acc;
                 }
             }
 }
 
-/* Attention backward ([P5] section 2: "out += att*value" becomes
- * datt += value*dout and dvalue += att*dout):
- *   datt_t2 = v_t2 . dout_t;  dv_t2 += att_t2 dout_t;
+/* Its gradient ([P5] section 2: each product of the forward sends gradient
+ * to both of its factors), accumulated into dqkv:
+ *   datt_t2 = v_t2 . dy_t;  dv_t2 += att_t2 dy_t;
  *   dpre_t2 = att_t2 (datt_t2 - sum_t3 att_t3 datt_t3);
  *   dq_t += dpre_t2 k_t2 / sqrt(hs);  dk_t2 += dpre_t2 q_t / sqrt(hs).
  * One (b,h) pair owns every row it writes, so (b,h) is the parallel loop. */
-void orc_attention_backward(REAL* dqkv, const REAL* dout, const REAL* qkv,
-                            const REAL* att, int B, int T, int C, int NH) {
+void orc_attn_bwd(const REAL* dyin, const REAL* qkv, const REAL* att, int B, int T, int C, int NH, REAL* dqkv) {
     int hs = C / NH;
     ACC scale = 1.0 / sqrt((ACC)hs);
     size_t C3 = 3 * (size_t)C;
@@ -394,7 +391,7 @@ void orc_attention_backward(REAL* dqkv, const REAL* dout, const REAL* qkv,
             for (int h = 0; h < NH; h++) {
                 for (int t = 0; t < T; t++) {
                     const REAL* a = att + (((size_t)b * NH + h) * T + t) * T;
-                    const REAL* dy = dout + ((size_t)b * T + t) * C + (size_t)h * hs;
+                    const REAL* dy = dyin + ((size_t)b * T + t) * C + (size_t)h * hs;
                     const REAL* q = qkv + ((size_t)b * T + t) * C3 + (size_t)h * hs;
                     REAL* dq = dqkv + ((size_t)b * T + t) * C3 + (size_t)h * hs;
                     for (int t2 = 0; t2 <= t; t2++) {
@@ -430,34 +427,34 @@ void orc_attention_backward(REAL* dqkv, const REAL* dout, const REAL* qkv,
  * k = sqrt(2/pi). */
 static ACC gelu_k(void) { return sqrt(2.0 / 3.14159265358979323846); }
 
-void orc_gelu_forward(REAL* out, const REAL* inp, size_t n) {
+void orc_gelu_fwd(const REAL* uin, size_t n, REAL* y) {
     ACC k = gelu_k();
     #pragma omp parallel for
     for (size_t i = 0; i < n; i++) {
-        ACC u = inp[i];
-        out[i] = (REAL)(0.5 * u * (1.0 + tanh(k * (u + 0.044715 * u * u * u))));
+        ACC u = uin[i];
+        y[i] = (REAL)(0.5 * u * (1.0 + tanh(k * (u + 0.044715 * u * u * u))));
     }
 }
 
-/* d/du of the above: 0.5(1+tau) + 0.5 u (1-tau^2) k (1 + 3*0.044715 u^2). */
-void orc_gelu_backward(REAL* dinp, const REAL* inp, const REAL* dout, size_t n) {
+/* Its gradient, accumulated into du: with tau = tanh(k (u + 0.044715 u^3)),
+ * d/du = 0.5(1+tau) + 0.5 u (1-tau^2) k (1 + 3*0.044715 u^2). */
+void orc_gelu_bwd(const REAL* dy, const REAL* uin, size_t n, REAL* du) {
     ACC k = gelu_k();
     #pragma omp parallel for
     for (size_t i = 0; i < n; i++) {
-        ACC u = inp[i];
+        ACC u = uin[i];
         ACC tau = tanh(k * (u + 0.044715 * u * u * u));
         ACC d = 0.5 * (1.0 + tau) + 0.5 * u * (1.0 - tau * tau) * k * (1.0 + 3.0 * 0.044715 * u * u);
-        dinp[i] = (REAL)(dinp[i] + d * dout[i]);
+        du[i] = (REAL)(du[i] + d * dy[i]);
     }
 }
 
-/* Softmax over the real vocabulary v < V of each of N rows of width Vp
+/* Softmax over the real vocabulary v < V of each of `rows` rows of width Vp
  * (padded columns excluded, their probability set to 0), and the
- * cross-entropy loss_n = logsumexp - logit[target]. */
-void orc_softmax_ce_forward(REAL* losses, REAL* probs, const REAL* logits,
-                            const int* targets, int N, int V, int Vp) {
+ * cross-entropy loss_n = logsumexp - logit[target] when targets is given. */
+void orc_xent_fwd(const REAL* logits, const int* targets, int rows, int V, int Vp, REAL* probs, REAL* losses) {
     #pragma omp parallel for
-    for (int n = 0; n < N; n++) {
+    for (int n = 0; n < rows; n++) {
         const REAL* z = logits + (size_t)n * Vp;
         REAL* p = probs + (size_t)n * Vp;
         ACC mx = -INFINITY;
@@ -469,12 +466,12 @@ void orc_softmax_ce_forward(REAL* losses, REAL* probs, const REAL* logits,
     }
 }
 
-/* dlogits[n,v] = (probs[n,v] - [v == target]) * dloss[n] for v < V; 0 for
- * the padded columns. */
-void orc_softmax_ce_backward(REAL* dlogits, const REAL* dlosses, const REAL* probs,
-                             const int* targets, int N, int V, int Vp) {
+/* Its gradient, accumulated into dlogits: (probs[n,v] - [v == target]) *
+ * dloss[n] for v < V; the padded columns receive nothing. */
+void orc_xent_bwd(const REAL* dlosses, const REAL* probs, const int* targets, int rows, int V, int Vp,
+                  REAL* dlogits) {
     #pragma omp parallel for
-    for (int n = 0; n < N; n++) {
+    for (int n = 0; n < rows; n++) {
         REAL* d = dlogits + (size_t)n * Vp;
         const REAL* p = probs + (size_t)n * Vp;
         for (int v = 0; v < Vp; v++) {
@@ -635,10 +632,110 @@ REAL* orc_act_grads(orc_model* M) { return M->gacts; }
 size_t orc_model_num_params(orc_model* M) { return M->np; }
 size_t orc_model_num_acts(orc_model* M) { return M->na; }
 
-/* Forward pass ([P5] section 2: gpt2_forward calls each layer in order; per
- * layer LN1 -> qkv -> attention -> attproj -> residual -> LN2 -> fc -> GELU
- * -> fcproj -> residual).  Returns the mean loss over the B*T positions, or
- * NaN when targets is NULL (then only logits and probs are produced). */
+/* Views of block l's slices of the flat buffers: its parameters (or their
+ * gradients), and below its saved activations (or their gradients). */
+typedef struct {
+    REAL *norm1_gain, *norm1_shift, *Wqkv, *bqkv, *Wo, *bo;
+    REAL *norm2_gain, *norm2_shift, *Wup, *bup, *Wdown, *bdown;
+} orc_block_params;
+
+/* The two normalisations read the block input and mid; out is the block's
+ * output and the next block's input. */
+typedef struct {
+    REAL *n1, *n1_mu, *n1_rs, *qkv, *heads, *scores, *weights, *attn_out, *mid;
+    REAL *n2, *n2_mu, *n2_rs, *up, *up_act, *down, *out;
+} orc_block_acts;
+
+static orc_block_params block_params(REAL** T, size_t l, size_t C) {
+    orc_block_params w;
+    w.norm1_gain = T[2] + l * C;
+    w.norm1_shift = T[3] + l * C;
+    w.Wqkv = T[4] + l * 3 * C * C;
+    w.bqkv = T[5] + l * 3 * C;
+    w.Wo = T[6] + l * C * C;
+    w.bo = T[7] + l * C;
+    w.norm2_gain = T[8] + l * C;
+    w.norm2_shift = T[9] + l * C;
+    w.Wup = T[10] + l * 4 * C * C;
+    w.bup = T[11] + l * 4 * C;
+    w.Wdown = T[12] + l * 4 * C * C;
+    w.bdown = T[13] + l * C;
+    return w;
+}
+
+static orc_block_acts block_acts(REAL** X, size_t l, size_t BT, size_t C, size_t BHTT) {
+    size_t n = BT * C;
+    orc_block_acts a;
+    a.n1 = X[1] + l * n;
+    a.n1_mu = X[2] + l * BT;
+    a.n1_rs = X[3] + l * BT;
+    a.qkv = X[4] + l * 3 * n;
+    a.heads = X[5] + l * n;
+    a.scores = X[6] + l * BHTT;
+    a.weights = X[7] + l * BHTT;
+    a.attn_out = X[8] + l * n;
+    a.mid = X[9] + l * n;
+    a.n2 = X[10] + l * n;
+    a.n2_mu = X[11] + l * BT;
+    a.n2_rs = X[12] + l * BT;
+    a.up = X[13] + l * 4 * n;
+    a.up_act = X[14] + l * 4 * n;
+    a.down = X[15] + l * n;
+    a.out = X[16] + l * n;
+    return a;
+}
+
+/* Residual join out = a + b, and its gradient: d(out) reaches both terms. */
+static void residual_fwd(const REAL* a, const REAL* b, size_t n, REAL* out) {
+    for (size_t i = 0; i < n; i++) out[i] = a[i] + b[i];
+}
+static void residual_bwd(const REAL* dout, size_t n, REAL* da, REAL* db) {
+    for (size_t i = 0; i < n; i++) { da[i] += dout[i]; db[i] += dout[i]; }
+}
+
+/* A pre-norm block ([P5] section 2 gives the layer order):
+ *   mid = x + Wo attn(Wqkv norm1(x))
+ *   out = mid + Wdown gelu(Wup norm2(mid)). */
+static void block_fwd(const REAL* x, const orc_block_params* w, int B, int T, int C, int NH,
+                      const orc_block_acts* a) {
+    int BT = B * T;
+    size_t n = (size_t)BT * C;
+    orc_norm_fwd(x, w->norm1_gain, w->norm1_shift, BT, C, a->n1, a->n1_mu, a->n1_rs);
+    orc_linear_fwd(a->n1, w->Wqkv, w->bqkv, BT, C, 3 * C, a->qkv);
+    orc_attn_fwd(a->qkv, B, T, C, NH, a->heads, a->scores, a->weights);
+    orc_linear_fwd(a->heads, w->Wo, w->bo, BT, C, C, a->attn_out);
+    residual_fwd(x, a->attn_out, n, a->mid);
+    orc_norm_fwd(a->mid, w->norm2_gain, w->norm2_shift, BT, C, a->n2, a->n2_mu, a->n2_rs);
+    orc_linear_fwd(a->n2, w->Wup, w->bup, BT, C, 4 * C, a->up);
+    orc_gelu_fwd(a->up, n * 4, a->up_act);
+    orc_linear_fwd(a->up_act, w->Wdown, w->bdown, BT, 4 * C, C, a->down);
+    residual_fwd(a->mid, a->down, n, a->out);
+}
+
+/* Its gradient, from d(out) already in da->out: every step of block_fwd in
+ * reverse.  Parameter gradients accumulate into dw; the gradient of the
+ * block input accumulates into dx. */
+static void block_bwd(const REAL* x, const orc_block_params* w, const orc_block_acts* a, int B, int T, int C,
+                      int NH, const orc_block_params* dw, const orc_block_acts* da, REAL* dx) {
+    int BT = B * T;
+    size_t n = (size_t)BT * C;
+    residual_bwd(da->out, n, da->mid, da->down);
+    orc_linear_bwd(da->down, a->up_act, w->Wdown, BT, 4 * C, C, da->up_act, dw->Wdown, dw->bdown);
+    orc_gelu_bwd(da->up_act, a->up, n * 4, da->up);
+    orc_linear_bwd(da->up, a->n2, w->Wup, BT, C, 4 * C, da->n2, dw->Wup, dw->bup);
+    orc_norm_bwd(da->n2, a->mid, w->norm2_gain, a->n2_mu, a->n2_rs, BT, C, da->mid, dw->norm2_gain,
+                 dw->norm2_shift);
+    residual_bwd(da->mid, n, dx, da->attn_out);
+    orc_linear_bwd(da->attn_out, a->heads, w->Wo, BT, C, C, da->heads, dw->Wo, dw->bo);
+    orc_attn_bwd(da->heads, a->qkv, a->weights, B, T, C, NH, da->qkv);
+    orc_linear_bwd(da->qkv, a->n1, w->Wqkv, BT, C, 3 * C, da->n1, dw->Wqkv, dw->bqkv);
+    orc_norm_bwd(da->n1, x, w->norm1_gain, a->n1_mu, a->n1_rs, BT, C, dx, dw->norm1_gain, dw->norm1_shift);
+}
+
+/* Forward pass: embedding, the L blocks, the final normalisation, the tied
+ * classifier (logits = lnf wte^T) and softmax cross-entropy.  Returns the
+ * mean loss over the B*T positions, or NaN when targets is NULL (then only
+ * logits and probs are produced). */
 double orc_forward(orc_model* M, const int* inputs, const int* targets) {
     const orc_config* g = &M->cfg;
     int B = M->B, T = M->T, C = g->C, L = g->L, NH = g->NH, V = g->V, Vp = g->Vp;
@@ -648,41 +745,18 @@ double orc_forward(orc_model* M, const int* inputs, const int* targets) {
     if (targets) memcpy(M->targets, targets, sizeof(int) * (size_t)BT);
     REAL** P = M->P;
     REAL** A = M->A;
-    size_t BTC = (size_t)BT * C;
-    orc_encoder_forward(A[0], M->inputs, P[0], P[1], B, T, C);
-    const REAL* residual = A[0];
+    size_t BHTT = (size_t)B * NH * T * T;
+    orc_embed_fwd(M->inputs, P[0], P[1], B, T, C, A[0]);
+    const REAL* x = A[0];
     for (int l = 0; l < L; l++) {
-        REAL* ln1 = A[1] + l * BTC;
-        REAL* ln1m = A[2] + (size_t)l * BT;
-        REAL* ln1r = A[3] + (size_t)l * BT;
-        REAL* qkv = A[4] + l * BTC * 3;
-        REAL* atty = A[5] + l * BTC;
-        REAL* pre = A[6] + (size_t)l * B * NH * T * T;
-        REAL* att = A[7] + (size_t)l * B * NH * T * T;
-        REAL* attproj = A[8] + l * BTC;
-        REAL* res2 = A[9] + l * BTC;
-        REAL* ln2 = A[10] + l * BTC;
-        REAL* ln2m = A[11] + (size_t)l * BT;
-        REAL* ln2r = A[12] + (size_t)l * BT;
-        REAL* fch = A[13] + l * BTC * 4;
-        REAL* fchg = A[14] + l * BTC * 4;
-        REAL* fcproj = A[15] + l * BTC;
-        REAL* res3 = A[16] + l * BTC;
-        orc_layernorm_forward(ln1, ln1m, ln1r, residual, P[2] + (size_t)l * C, P[3] + (size_t)l * C, BT, C);
-        orc_matmul_forward(qkv, ln1, P[4] + (size_t)l * 3 * C * C, P[5] + (size_t)l * 3 * C, BT, C, 3 * C);
-        orc_attention_forward(atty, pre, att, qkv, B, T, C, NH);
-        orc_matmul_forward(attproj, atty, P[6] + (size_t)l * C * C, P[7] + (size_t)l * C, BT, C, C);
-        for (size_t i = 0; i < BTC; i++) res2[i] = residual[i] + attproj[i];
-        orc_layernorm_forward(ln2, ln2m, ln2r, res2, P[8] + (size_t)l * C, P[9] + (size_t)l * C, BT, C);
-        orc_matmul_forward(fch, ln2, P[10] + (size_t)l * 4 * C * C, P[11] + (size_t)l * 4 * C, BT, C, 4 * C);
-        orc_gelu_forward(fchg, fch, BTC * 4);
-        orc_matmul_forward(fcproj, fchg, P[12] + (size_t)l * 4 * C * C, P[13] + (size_t)l * C, BT, 4 * C, C);
-        for (size_t i = 0; i < BTC; i++) res3[i] = res2[i] + fcproj[i];
-        residual = res3;
+        orc_block_params w = block_params(P, l, C);
+        orc_block_acts a = block_acts(A, l, BT, C, BHTT);
+        block_fwd(x, &w, B, T, C, NH, &a);
+        x = a.out;
     }
-    orc_layernorm_forward(A[17], A[18], A[19], residual, P[14], P[15], BT, C);
-    orc_matmul_forward(A[20], A[17], P[0], NULL, BT, C, Vp);
-    orc_softmax_ce_forward(A[22], A[21], A[20], targets ? M->targets : NULL, BT, V, Vp);
+    orc_norm_fwd(x, P[14], P[15], BT, C, A[17], A[18], A[19]);
+    orc_linear_fwd(A[17], P[0], NULL, BT, C, Vp, A[20]);
+    orc_xent_fwd(A[20], targets ? M->targets : NULL, BT, V, Vp, A[21], A[22]);
     if (!targets) return NAN;
     ACC s = 0;
     for (int i = 0; i < BT; i++) s += A[22][i];
@@ -694,71 +768,34 @@ void orc_zero_grad(orc_model* M) {
     M->grad_scale = 1.0;
 }
 
-/* Backward pass: the forward list in reverse, seeding dloss = 1/(B*T) per
- * position ([P5] section 2).  Parameter gradients accumulate (+=);
- * activation gradients are recomputed from zero on every call. */
+/* Backward pass: the forward in reverse, seeded with d(loss_n) = 1/(B*T) for
+ * every position (the loss is their mean).  Parameter gradients accumulate
+ * (+=); activation gradients start from zero on every call. */
 int orc_backward(orc_model* M) {
     if (!M->have_targets) return -1;
     const orc_config* g = &M->cfg;
     int B = M->B, T = M->T, C = g->C, L = g->L, NH = g->NH, V = g->V, Vp = g->Vp;
     int BT = B * T;
-    size_t BTC = (size_t)BT * C;
+    size_t BHTT = (size_t)B * NH * T * T;
     REAL** P = M->P;
     REAL** G = M->G;
     REAL** A = M->A;
     REAL** D = M->GA;
     memset(M->gacts, 0, sizeof(REAL) * M->na);
     for (int i = 0; i < BT; i++) D[22][i] = (REAL)(1.0 / BT);
-    orc_softmax_ce_backward(D[20], D[22], A[21], M->targets, BT, V, Vp);
-    orc_matmul_backward(D[17], G[0], NULL, D[20], A[17], P[0], BT, C, Vp);
-    const REAL* residual = A[16] + (size_t)(L - 1) * BTC;
-    REAL* dresidual = D[16] + (size_t)(L - 1) * BTC;
-    orc_layernorm_backward(dresidual, G[14], G[15], D[17], residual, P[14], A[18], A[19], BT, C);
+    orc_xent_bwd(D[22], A[21], M->targets, BT, V, Vp, D[20]);
+    orc_linear_bwd(D[20], A[17], P[0], BT, C, Vp, D[17], G[0], NULL);
+    orc_block_acts top = block_acts(A, L - 1, BT, C, BHTT);
+    orc_block_acts dtop = block_acts(D, L - 1, BT, C, BHTT);
+    orc_norm_bwd(D[17], top.out, P[14], A[18], A[19], BT, C, dtop.out, G[14], G[15]);
     for (int l = L - 1; l >= 0; l--) {
-        const REAL* res_in = l == 0 ? A[0] : A[16] + (size_t)(l - 1) * BTC;
-        REAL* dres_in = l == 0 ? D[0] : D[16] + (size_t)(l - 1) * BTC;
-        REAL* dres3 = D[16] + (size_t)l * BTC;
-        REAL* ln1 = A[1] + l * BTC;
-        REAL* ln1m = A[2] + (size_t)l * BT;
-        REAL* ln1r = A[3] + (size_t)l * BT;
-        REAL* qkv = A[4] + l * BTC * 3;
-        REAL* atty = A[5] + l * BTC;
-        REAL* att = A[7] + (size_t)l * B * NH * T * T;
-        REAL* res2 = A[9] + l * BTC;
-        REAL* ln2 = A[10] + l * BTC;
-        REAL* ln2m = A[11] + (size_t)l * BT;
-        REAL* ln2r = A[12] + (size_t)l * BT;
-        REAL* fch = A[13] + l * BTC * 4;
-        REAL* fchg = A[14] + l * BTC * 4;
-        REAL* dln1 = D[1] + l * BTC;
-        REAL* dqkv = D[4] + l * BTC * 3;
-        REAL* datty = D[5] + l * BTC;
-        REAL* dattproj = D[8] + l * BTC;
-        REAL* dres2 = D[9] + l * BTC;
-        REAL* dln2 = D[10] + l * BTC;
-        REAL* dfch = D[13] + l * BTC * 4;
-        REAL* dfchg = D[14] + l * BTC * 4;
-        REAL* dfcproj = D[15] + l * BTC;
-        /* res3 = res2 + fcproj: the gradient flows unchanged to both */
-        for (size_t i = 0; i < BTC; i++) { dres2[i] += dres3[i]; dfcproj[i] += dres3[i]; }
-        orc_matmul_backward(dfchg, G[12] + (size_t)l * 4 * C * C, G[13] + (size_t)l * C, dfcproj, fchg,
-                            P[12] + (size_t)l * 4 * C * C, BT, 4 * C, C);
-        orc_gelu_backward(dfch, fch, dfchg, BTC * 4);
-        orc_matmul_backward(dln2, G[10] + (size_t)l * 4 * C * C, G[11] + (size_t)l * 4 * C, dfch, ln2,
-                            P[10] + (size_t)l * 4 * C * C, BT, C, 4 * C);
-        orc_layernorm_backward(dres2, G[8] + (size_t)l * C, G[9] + (size_t)l * C, dln2, res2,
-                               P[8] + (size_t)l * C, ln2m, ln2r, BT, C);
-        /* res2 = res_in + attproj */
-        for (size_t i = 0; i < BTC; i++) { dres_in[i] += dres2[i]; dattproj[i] += dres2[i]; }
-        orc_matmul_backward(datty, G[6] + (size_t)l * C * C, G[7] + (size_t)l * C, dattproj, atty,
-                            P[6] + (size_t)l * C * C, BT, C, C);
-        orc_attention_backward(dqkv, datty, qkv, att, B, T, C, NH);
-        orc_matmul_backward(dln1, G[4] + (size_t)l * 3 * C * C, G[5] + (size_t)l * 3 * C, dqkv, ln1,
-                            P[4] + (size_t)l * 3 * C * C, BT, C, 3 * C);
-        orc_layernorm_backward(dres_in, G[2] + (size_t)l * C, G[3] + (size_t)l * C, dln1, res_in,
-                               P[2] + (size_t)l * C, ln1m, ln1r, BT, C);
+        orc_block_params w = block_params(P, l, C), dw = block_params(G, l, C);
+        orc_block_acts a = block_acts(A, l, BT, C, BHTT), da = block_acts(D, l, BT, C, BHTT);
+        const REAL* x = l == 0 ? A[0] : block_acts(A, l - 1, BT, C, BHTT).out;
+        REAL* dx = l == 0 ? D[0] : block_acts(D, l - 1, BT, C, BHTT).out;
+        block_bwd(x, &w, &a, B, T, C, NH, &dw, &da, dx);
     }
-    orc_encoder_backward(G[0], G[1], D[0], M->inputs, B, T, C);
+    orc_embed_bwd(D[0], M->inputs, B, T, C, G[0], G[1]);
     return 0;
 }
 

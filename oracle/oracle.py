@@ -74,18 +74,19 @@ def _lib(precision="f32"):
     d = ctypes.c_double
     lib.orc_adamw.argtypes = [vp, d, d, d, d, d, ctypes.c_int]
     lib.orc_adamw.restype = ctypes.c_int
-    lib.orc_encoder_forward.argtypes = [R, I, R, R, ctypes.c_int, ctypes.c_int, ctypes.c_int]
-    lib.orc_encoder_backward.argtypes = [R, R, R, I, ctypes.c_int, ctypes.c_int, ctypes.c_int]
-    lib.orc_layernorm_forward.argtypes = [R, R, R, R, R, R, ctypes.c_int, ctypes.c_int]
-    lib.orc_layernorm_backward.argtypes = [R, R, R, R, R, R, R, R, ctypes.c_int, ctypes.c_int]
-    lib.orc_matmul_forward.argtypes = [R, R, R, R, ctypes.c_int, ctypes.c_int, ctypes.c_int]
-    lib.orc_matmul_backward.argtypes = [R, R, R, R, R, R, ctypes.c_int, ctypes.c_int, ctypes.c_int]
-    lib.orc_attention_forward.argtypes = [R, R, R, R] + [ctypes.c_int] * 4
-    lib.orc_attention_backward.argtypes = [R, R, R, R] + [ctypes.c_int] * 4
-    lib.orc_gelu_forward.argtypes = [R, R, sz]
-    lib.orc_gelu_backward.argtypes = [R, R, R, sz]
-    lib.orc_softmax_ce_forward.argtypes = [R, R, R, I, ctypes.c_int, ctypes.c_int, ctypes.c_int]
-    lib.orc_softmax_ce_backward.argtypes = [R, R, R, I, ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    i32 = ctypes.c_int
+    lib.orc_embed_fwd.argtypes = [I, R, R, i32, i32, i32, R]
+    lib.orc_embed_bwd.argtypes = [R, I, i32, i32, i32, R, R]
+    lib.orc_norm_fwd.argtypes = [R, R, R, i32, i32, R, R, R]
+    lib.orc_norm_bwd.argtypes = [R, R, R, R, R, i32, i32, R, R, R]
+    lib.orc_linear_fwd.argtypes = [R, R, R, i32, i32, i32, R]
+    lib.orc_linear_bwd.argtypes = [R, R, R, i32, i32, i32, R, R, R]
+    lib.orc_attn_fwd.argtypes = [R, i32, i32, i32, i32, R, R, R]
+    lib.orc_attn_bwd.argtypes = [R, R, R, i32, i32, i32, i32, R]
+    lib.orc_gelu_fwd.argtypes = [R, sz, R]
+    lib.orc_gelu_bwd.argtypes = [R, R, sz, R]
+    lib.orc_xent_fwd.argtypes = [R, I, i32, i32, i32, R, R]
+    lib.orc_xent_bwd.argtypes = [R, R, I, i32, i32, i32, R]
     lib.orc_global_norm.argtypes = [R, sz]
     lib.orc_global_norm.restype = ctypes.c_double
     lib.orc_adamw_update.argtypes = [R, R, R, R, sz, d, d, d, d, d, ctypes.c_int, d]
@@ -255,7 +256,7 @@ def encoder_forward(inp, wte, wpe, prec="f32"):
     C = wte.shape[1]
     wte, wpe = _arr(wte, prec), _arr(wpe, prec)
     out = np.zeros((B, T, C), _NP[prec])
-    _lib(prec).orc_encoder_forward(_ptr(out, prec), _iptr(inp), _ptr(wte, prec), _ptr(wpe, prec), B, T, C)
+    _lib(prec).orc_embed_fwd(_iptr(inp), _ptr(wte, prec), _ptr(wpe, prec), B, T, C, _ptr(out, prec))
     return out
 
 
@@ -264,7 +265,7 @@ def encoder_backward(dwte, dwpe, dout, inp, prec="f32"):
     B, T = inp.shape
     C = dout.shape[-1]
     dout = _arr(dout, prec)
-    _lib(prec).orc_encoder_backward(_ptr(dwte, prec), _ptr(dwpe, prec), _ptr(dout, prec), _iptr(inp), B, T, C)
+    _lib(prec).orc_embed_bwd(_ptr(dout, prec), _iptr(inp), B, T, C, _ptr(dwte, prec), _ptr(dwpe, prec))
 
 
 def layernorm_forward(x, w, b, prec="f32"):
@@ -273,8 +274,8 @@ def layernorm_forward(x, w, b, prec="f32"):
     out = np.zeros_like(x)
     mean = np.zeros(N, _NP[prec])
     rstd = np.zeros(N, _NP[prec])
-    _lib(prec).orc_layernorm_forward(_ptr(out, prec), _ptr(mean, prec), _ptr(rstd, prec), _ptr(x, prec),
-                                     _ptr(w, prec), _ptr(b, prec), N, C)
+    _lib(prec).orc_norm_fwd(_ptr(x, prec), _ptr(w, prec), _ptr(b, prec), N, C, _ptr(out, prec), _ptr(mean, prec),
+                            _ptr(rstd, prec))
     return out, mean, rstd
 
 
@@ -284,8 +285,8 @@ def layernorm_backward(dout, x, w, mean, rstd, prec="f32"):
     dx = np.zeros_like(x)
     dw = np.zeros(C, _NP[prec])
     db = np.zeros(C, _NP[prec])
-    _lib(prec).orc_layernorm_backward(_ptr(dx, prec), _ptr(dw, prec), _ptr(db, prec), _ptr(dout, prec),
-                                      _ptr(x, prec), _ptr(w, prec), _ptr(mean, prec), _ptr(rstd, prec), N, C)
+    _lib(prec).orc_norm_bwd(_ptr(dout, prec), _ptr(x, prec), _ptr(w, prec), _ptr(mean, prec), _ptr(rstd, prec),
+                            N, C, _ptr(dx, prec), _ptr(dw, prec), _ptr(db, prec))
     return dx, dw, db
 
 
@@ -298,7 +299,7 @@ def matmul_forward(x, w, bias=None, prec="f32"):
     if bias is not None:
         bias = _arr(bias, prec)
         bp = _ptr(bias, prec)
-    _lib(prec).orc_matmul_forward(_ptr(out, prec), _ptr(x, prec), _ptr(w, prec), bp, N, C, OC)
+    _lib(prec).orc_linear_fwd(_ptr(x, prec), _ptr(w, prec), bp, N, C, OC, _ptr(out, prec))
     return out
 
 
@@ -309,8 +310,8 @@ def matmul_backward(dout, x, w, prec="f32"):
     dx = np.zeros_like(x)
     dw = np.zeros_like(w)
     db = np.zeros(OC, _NP[prec])
-    _lib(prec).orc_matmul_backward(_ptr(dx, prec), _ptr(dw, prec), _ptr(db, prec), _ptr(dout, prec),
-                                   _ptr(x, prec), _ptr(w, prec), N, C, OC)
+    _lib(prec).orc_linear_bwd(_ptr(dout, prec), _ptr(x, prec), _ptr(w, prec), N, C, OC, _ptr(dx, prec),
+                              _ptr(dw, prec), _ptr(db, prec))
     return dx, dw, db
 
 
@@ -321,8 +322,7 @@ def attention_forward(qkv, NH, prec="f32"):
     out = np.zeros((B, T, C), _NP[prec])
     pre = np.zeros((B, NH, T, T), _NP[prec])
     att = np.zeros((B, NH, T, T), _NP[prec])
-    _lib(prec).orc_attention_forward(_ptr(out, prec), _ptr(pre, prec), _ptr(att, prec), _ptr(qkv, prec),
-                                     B, T, C, NH)
+    _lib(prec).orc_attn_fwd(_ptr(qkv, prec), B, T, C, NH, _ptr(out, prec), _ptr(pre, prec), _ptr(att, prec))
     return out, pre, att
 
 
@@ -330,22 +330,22 @@ def attention_backward(dout, qkv, att, NH, prec="f32"):
     dout, qkv, att = _arr(dout, prec), _arr(qkv, prec), _arr(att, prec)
     B, T, C3 = qkv.shape
     dqkv = np.zeros_like(qkv)
-    _lib(prec).orc_attention_backward(_ptr(dqkv, prec), _ptr(dout, prec), _ptr(qkv, prec), _ptr(att, prec),
-                                      B, T, C3 // 3, NH)
+    _lib(prec).orc_attn_bwd(_ptr(dout, prec), _ptr(qkv, prec), _ptr(att, prec), B, T, C3 // 3, NH,
+                            _ptr(dqkv, prec))
     return dqkv
 
 
 def gelu_forward(x, prec="f32"):
     x = _arr(x, prec)
     out = np.zeros_like(x)
-    _lib(prec).orc_gelu_forward(_ptr(out, prec), _ptr(x, prec), x.size)
+    _lib(prec).orc_gelu_fwd(_ptr(x, prec), x.size, _ptr(out, prec))
     return out
 
 
 def gelu_backward(x, dout, prec="f32"):
     x, dout = _arr(x, prec), _arr(dout, prec)
     dx = np.zeros_like(x)
-    _lib(prec).orc_gelu_backward(_ptr(dx, prec), _ptr(x, prec), _ptr(dout, prec), x.size)
+    _lib(prec).orc_gelu_bwd(_ptr(dout, prec), _ptr(x, prec), x.size, _ptr(dx, prec))
     return dx
 
 
@@ -358,7 +358,7 @@ def softmax_ce_forward(logits, targets, V, prec="f32"):
     if targets is not None:
         targets = np.ascontiguousarray(targets, dtype=np.int32)
         tp = _iptr(targets)
-    _lib(prec).orc_softmax_ce_forward(_ptr(losses, prec), _ptr(probs, prec), _ptr(logits, prec), tp, N, V, Vp)
+    _lib(prec).orc_xent_fwd(_ptr(logits, prec), tp, N, V, Vp, _ptr(probs, prec), _ptr(losses, prec))
     return losses, probs
 
 
@@ -367,8 +367,7 @@ def softmax_ce_backward(probs, targets, dlosses, V, prec="f32"):
     targets = np.ascontiguousarray(targets, dtype=np.int32)
     N, Vp = probs.shape
     d = np.zeros_like(probs)
-    _lib(prec).orc_softmax_ce_backward(_ptr(d, prec), _ptr(dlosses, prec), _ptr(probs, prec), _iptr(targets),
-                                       N, V, Vp)
+    _lib(prec).orc_xent_bwd(_ptr(dlosses, prec), _ptr(probs, prec), _iptr(targets), N, V, Vp, _ptr(d, prec))
     return d
 
 

@@ -83,11 +83,10 @@ def test_gemm_kernels_vs_oracle(prec, cases, dt, tol):
 def test_gemm_tile_widths_at_scale():
     """Forward (NT) and backward-data (NN) products with thousands of rows, at
     output widths that select the 256-wide tile (3072) and the 192-wide tile
-    (768, 2304), in one round of tiles (768) or as the persistent schedule
-    over several (3072, 2304, and a ragged 8200 x 2056: 297 tiles, not a
-    multiple of the 8 XCDs), checked on sampled rows (first, last, random)
-    against the oracle run on those rows alone (each output row depends only
-    on its input row)."""
+    (768, 2304), in one round of tiles (768) or over several rounds (3072,
+    2304, and a ragged 8200 x 2056: 297 tiles, not a multiple of the 8 XCDs),
+    checked on sampled rows (first, last, random) against the oracle run on
+    those rows alone (each output row depends only on its input row)."""
     m = _model(G.GPT2_BF16_MIXED)
     rng = np.random.default_rng(2)
     R = 64
@@ -111,6 +110,30 @@ def test_gemm_tile_widths_at_scale():
         torch.cuda.synchronize()
         rdx, _, _ = O.matmul_backward(_host64(dy)[rows], np.zeros((rows.size, N)), _host64(w2), prec="f64")
         _close(_host64(dx)[rows], rdx, 8e-3)
+    m.close()
+
+
+def test_gemm_plain_store_persistent():
+    """Plain-store forward products (no bias) over at least two rounds of
+    256 x 256 tiles, which run the persistent kernel with register-staged
+    64-deep k-steps: a ragged output width (32776 = 128 tiles + 8 columns)
+    over two k-steps, ragged rows (4104) over an odd five, and the
+    classifier's width and depth (50304 x 768) at 1024 rows; sampled rows
+    against the oracle on those rows alone."""
+    m = _model(G.GPT2_BF16_MIXED)
+    rng = np.random.default_rng(5)
+    for M, N, K, nr in ((4096, 32776, 128, 128), (4104, 8192, 320, 128), (1024, 50304, 768, 48)):
+        rows = np.unique(np.concatenate([np.arange(8), np.arange(M - 8, M), rng.integers(0, M, nr)]))
+        print(f"plain-store gemm M={M} N={N} K={K}", flush=True)
+        x = _dev(rng.standard_normal((M, K)), torch.bfloat16)
+        w = _dev(rng.standard_normal((N, K)) * 0.1, torch.bfloat16)
+        out = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+        G.gpt2_test_gemm_nt(m.h, out.data_ptr(), x.data_ptr(), w.data_ptr(), None, M, N, K)
+        torch.cuda.synchronize()
+        # every element written (the NaN fill would survive an unwritten tile)
+        assert not torch.isnan(out).any().item()
+        ref = O.matmul_forward(_host64(x)[rows], _host64(w), None, prec="f64")
+        _close(_host64(out)[rows], ref, 8e-3)
     m.close()
 
 

@@ -13,7 +13,9 @@
 // whole reduction; a single weight-gradient product may instead split the
 // reduction over workgroups and add the partial tiles in a fixed order
 // (deterministic).  Block ids are remapped so that the tiles one XCD (one
-// L2) runs are neighbours sharing operand panels.
+// L2) runs are neighbours sharing operand panels.  Wide single products with a
+// plain store (the classifier's logits) instead run a persistent schedule
+// whose k-contiguous operands move through registers in 64-deep k-steps.
 #include <algorithm>
 #include <type_traits>
 
@@ -390,6 +392,60 @@ struct Dma {
     }
 };
 
+// Register-staged loads of a k-contiguous operand, k-step 64: each wave
+// instruction reads 8 rows x 128 bytes (8 lanes per row, one whole L2 line
+// per row) into registers; store() then writes them into the stage tile
+// [row][64] with chunk c of row r in slot c ^ kswz<64>(r).  ROWS rows of the
+// stage are loaded; instruction i of wave w covers tile rows
+// 8 (w NIW + i) .. +7.  The loads go through a buffer resource over the
+// operand's rows, so rows past its end read as zero (they only feed
+// accumulators the epilogue never stores); each lane keeps one byte offset,
+// and the instruction and k offsets are uniform.
+template <int NW, int ROWS>
+struct RegDma {
+    static constexpr int KB = 64;
+    static constexpr int NIT = ROWS * KB / 512;
+    static_assert(NIT % NW == 0, "register loads split evenly over the waves");
+    static constexpr int NIW = NIT / NW;
+#if defined(__HIP_DEVICE_COMPILE__)
+    __amdgpu_buffer_rsrc_t rs;
+#endif
+    uint32_t goff;      // lane byte offset in the wave's first instruction
+    uint32_t rstep;     // bytes between instructions (8 rows)
+    uint32_t loff[2];   // lane LDS element offset in an even / odd instruction
+    int q0;             // the wave's first instruction index
+    bf16x8 v[NIW];
+    DEVI void init(const bf16* X, int64_t ld, int r0, int rows, int wave, int lane) {
+        const int l = lane >> 3, c = lane & 7;
+        q0 = wave * NIW;
+#if defined(__HIP_DEVICE_COMPILE__)
+        rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(X), (short)0, (int)(rows * ld * 2), 0x00020000);
+#endif
+        goff = (uint32_t)(((int64_t)(r0 + q0 * 8 + l) * ld + c * 8) * 2);
+        rstep = (uint32_t)(8 * ld * 2);
+        // kswz<64>(8q + l) = ((8q + l) >> 1) & 7 = 4 (q & 1) + (l >> 1)
+        loff[0] = (uint32_t)(l * KB + ((c ^ (l >> 1)) << 3));
+        loff[1] = (uint32_t)(l * KB + ((c ^ (4 + (l >> 1))) << 3));
+    }
+    DEVI void load(int k0) {
+#if defined(__HIP_DEVICE_COMPILE__)
+#pragma unroll
+        for (int i = 0; i < NIW; i++) {
+            typedef int i32x4 __attribute__((ext_vector_type(4)));
+            const i32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rs, goff, (int)(i * rstep + k0 * 2), 0);
+            v[i] = *reinterpret_cast<const bf16x8*>(&x);
+        }
+#endif
+    }
+    DEVI void store(uint16_t* tile) const {
+#pragma unroll
+        for (int i = 0; i < NIW; i++) {
+            const int q = q0 + i;
+            *reinterpret_cast<bf16x8*>(tile + q * 512 + loff[q & 1]) = v[i];
+        }
+    }
+};
+
 // MFMA fragment: rows row0 + (lane & 31), k = kk + (lane >> 5) * 8 + 0..7
 template <int R, int KB, bool KCONTIG>
 DEVI bf16x8 frag_any(const uint16_t* tile, int row0, int kk, int lane) {
@@ -482,19 +538,19 @@ DEVI void mfma_step(f32x16 (&acc)[FM][FN], bf16x8 (&fa)[FM], bf16x8 (&fb)[FN], c
 // LDS that no fragment reads.
 // GROUPED: one launch over the tiles of several problems (see GroupSched).
 template <int BM, int BN, int NW, int WAVES_M, int KB, int NS, bool XPF, bool AK, bool BKC, int EPI, int OCC = 2,
-          int BNV = BN, bool GROUPED = false>
+          int BNV = BN, bool GROUPED = false, bool RL = false, bool PERS = false>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void gemm_big_kernel(
     GemmArgs garg, int kchunk, GroupSched gs) {
     constexpr int WAVES_N = NW / WAVES_M;
     constexpr int TM = BM / WAVES_M, TN = BNV / WAVES_N, FM = TM / 32, FN = TN / 32;
     static_assert(BNV <= BN && TN % 32 == 0, "tile width");
-    static_assert(NS >= 3 && NS <= 5, "stages");
+    static_assert(RL ? (NS == 2 && KB == 64 && AK && BKC && !XPF && !GROUPED) : (NS >= 3 && NS <= 5), "stages");
     constexpr int SA = BM * KB, SB = BN * KB;
     // one array per stage (alias analysis then keeps the reads of one stage
     // independent of the loads in flight into another)
-    __shared__ __attribute__((aligned(1024))) uint16_t sa0[SA], sa1[SA], sa2[SA], sa3[NS > 3 ? SA : 8],
+    __shared__ __attribute__((aligned(1024))) uint16_t sa0[SA], sa1[SA], sa2[NS > 2 ? SA : 8], sa3[NS > 3 ? SA : 8],
         sa4[NS > 4 ? SA : 8];
-    __shared__ __attribute__((aligned(1024))) uint16_t sb0[SB], sb1[SB], sb2[SB], sb3[NS > 3 ? SB : 8],
+    __shared__ __attribute__((aligned(1024))) uint16_t sb0[SB], sb1[SB], sb2[NS > 2 ? SB : 8], sb3[NS > 3 ? SB : 8],
         sb4[NS > 4 ? SB : 8];
     auto stA = [&](auto J) -> uint16_t* {
         constexpr int j = decltype(J)::value % NS;
@@ -539,6 +595,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
             kchunk = g.K / 2;
             half_slot = 2 * (xcd * gs.split + (q >> 1)) + split;
         }
+    } else if constexpr (PERS) {
+        g = garg;
+        split = 0;
+        m0 = n0 = 0;
     } else {
         g = garg;
         const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BNV - 1) / BNV;
@@ -577,8 +637,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
     typedef Dma<BPITCH, NW, KB, BKC, BNV, true> DmaB;
     DmaA da;
     DmaB db;
-    da.init(g.lda, m0, g.M, wave, lane);
-    db.init(g.ldb, n0, g.N, wave, lane);
+    if constexpr (!RL) {
+        da.init(g.lda, m0, g.M, wave, lane);
+        db.init(g.ldb, n0, g.N, wave, lane);
+    }
     // The main loop, for a wave that issues CB loads of B per stage (all
     // waves issue DmaA::NIW of A).  Where the waves' B counts differ, each
     // count gets its own copy of the loop (same barriers in both).
@@ -640,23 +702,20 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
         if constexpr (NS > 3) if (kt < nk) { step(I2{}, kt); kt++; }
         if constexpr (NS > 4) if (kt < nk) { step(I3{}, kt); kt++; }
     };
-    if constexpr (DmaB::EVEN) {
-        main_loop(std::integral_constant<int, DmaB::NIW>{});
-    } else {
-        if (DmaB::count(wave) == DmaB::NIW) main_loop(std::integral_constant<int, DmaB::NIW>{});
-        else main_loop(std::integral_constant<int, DmaB::NIW - 1>{});
-    }
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());  // no load may still be writing LDS at exit
-
     // The stage buffers become the epilogue's per-wave regions once every
     // wave is past its last LDS read.
-    constexpr int RBYTES = 2 * (BN < BM ? BN : BM) * KB;  // smallest stage array
+    // (two stages: two regions in each stage array)
+    constexpr int RBYTES = 2 * (BN < BM ? BN : BM) * KB / (NS == 2 ? 2 : 1);  // smallest region
     constexpr int RH = red_bytes<32, TN>() <= RBYTES ? 32 : 16;
-    static_assert(NW <= 8 && NW <= 2 * NS && red_bytes<RH, TN>() <= RBYTES, "epilogue regions must fit the stage buffers");
-    {
+    static_assert(NW <= 8 && NW <= 2 * NS * (NS == 2 ? 2 : 1) && red_bytes<RH, TN>() <= RBYTES,
+                  "epilogue regions must fit the stage buffers");
+    auto epilogue = [&](int m0, int n0) {
         __syncthreads();
         uint16_t* region;
-        switch (wave) {
+        if constexpr (NS == 2) {
+            uint16_t* arr = (wave >> 1) == 0 ? sa0 : (wave >> 1) == 1 ? sb0 : (wave >> 1) == 2 ? sa1 : sb1;
+            region = arr + (wave & 1) * (RBYTES / 2);
+        } else switch (wave) {
             case 0: region = sa0; break;
             case 1: region = sb0; break;
             case 2: region = sa1; break;
@@ -679,14 +738,136 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
             epilogue_rows<EPI, RH>(g, acc, reinterpret_cast<float*>(region), m0 + wm * TM, n0 + wn * TN, split,
                                    (m0 / BM) * WAVES_M + wm, lane);
         }
+    };
+
+    if constexpr (RL) {
+        // Register-staged k-steps of 64 over two LDS stages: the registers
+        // hold k-step kt + 1 while k-step kt runs out of LDS; at the start of
+        // step kt they go to the other stage (free since the last barrier)
+        // and k-step kt + 2 is requested into them.
+        // PERS: one workgroup per CU slot takes, in turn, the tiles of its
+        // XCD's contiguous range that the lock-step launch would give that
+        // slot; the next tile's first k-step is requested before the current
+        // tile's epilogue.
+        const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BNV - 1) / BNV;
+        auto tile_of = [&](int bid, int& tm0, int& tn0) {
+            constexpr int GM = 8;
+            const int gi = bid / (GM * tiles_n);
+            const int first_m = gi * GM;
+            const int gsz = min(tiles_m - first_m, GM);
+            const int in = bid % (GM * tiles_n);
+            tm0 = (first_m + in % gsz) * BM;
+            tn0 = (in / gsz) * BNV;
+        };
+        int p_first = 0, p_count = 1, p_stride = 0;
+        if constexpr (PERS) {
+            const int total = tiles_m * tiles_n;
+            const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, slots = gridDim.x >> 3;
+            const int lo = (int)((int64_t)total * xcd / 8), hi = (int)((int64_t)total * (xcd + 1) / 8);
+            if (lo + slot >= hi) return;
+            p_first = lo + slot;
+            p_stride = slots;
+            p_count = (hi - p_first + slots - 1) / slots;
+            tile_of(p_first, m0, n0);
+        }
+        RegDma<NW, BM> ra;
+        RegDma<NW, BNV> rb;
+        ra.init(A, g.lda, m0, g.M, wave, lane);
+        rb.init(B, g.ldb, n0, g.N, wave, lane);
+        ra.load(kbeg);
+        rb.load(kbeg);
+        constexpr int LGKM0 = 0xC07F;  // lgkmcnt = 0, vmcnt and expcnt unconstrained
+        auto bar = [&]() {
+            __builtin_amdgcn_s_waitcnt(LGKM0);
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+        };
+        auto rstep = [&](uint16_t* cA, uint16_t* cB, uint16_t* oA, uint16_t* oB, int kt) {
+            if (kt + 1 < nk) {
+                ra.store(oA);
+                rb.store(oB);
+                if (kt + 2 < nk) {
+                    ra.load(kbeg + (kt + 2) * KB);
+                    rb.load(kbeg + (kt + 2) * KB);
+                }
+            }
+            mfma_step<BM, BN, KB, FM, FN, TM, TN, true, true, false>(acc, fa, fb, cA, cB, oA, oB, wm, wn, lane);
+            bar();
+        };
+        for (int it = 0; it < p_count; it++) {
+#pragma unroll
+            for (int i = 0; i < FM; i++)
+#pragma unroll
+                for (int j = 0; j < FN; j++)
+#pragma unroll
+                    for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
+            ra.store(sa0);
+            rb.store(sb0);
+            if (nk > 1) {
+                ra.load(kbeg + KB);
+                rb.load(kbeg + KB);
+            }
+            bar();
+            for (int kt = 0; kt < nk; kt += 2) {
+                rstep(sa0, sb0, sa1, sb1, kt);
+                if (kt + 1 < nk) rstep(sa1, sb1, sa0, sb0, kt + 1);
+            }
+            const int cm0 = m0, cn0 = n0;
+            if (PERS && it + 1 < p_count) {
+                tile_of(p_first + (it + 1) * p_stride, m0, n0);
+                ra.init(A, g.lda, m0, g.M, wave, lane);
+                rb.init(B, g.ldb, n0, g.N, wave, lane);
+                ra.load(kbeg);
+                rb.load(kbeg);
+            }
+            epilogue(cm0, cn0);
+            if (PERS && it + 1 < p_count) __syncthreads();  // epilogue regions read before stage 0 is refilled
+        }
+        return;
+    } else if constexpr (DmaB::EVEN) {
+        main_loop(std::integral_constant<int, DmaB::NIW>{});
+    } else {
+        if (DmaB::count(wave) == DmaB::NIW) main_loop(std::integral_constant<int, DmaB::NIW>{});
+        else main_loop(std::integral_constant<int, DmaB::NIW - 1>{});
     }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());  // no load may still be writing LDS at exit
+
+    epilogue(m0, n0);
+}
+
+// CUs of the current device (cached per device), rounded down to a multiple of 8.
+int device_slots() {
+    static int cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!cache[dev]) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 8) cus = 256;
+        cache[dev] = cus / 8 * 8;
+    }
+    return cache[dev];
+}
+
+// The register-staged kernel (both operands k-contiguous, k-step 64, two LDS
+// stages): persistent over wgs workgroups when the tiles outnumber them.
+template <int BM, int BN, int NW, int WAVES_M, int EPI, int BNV = BN>
+hipError_t launch_pers(const GemmArgs& g, hipStream_t s, int wgs) {
+    const int tiles = (int)(cdiv(g.M, BM) * cdiv(g.N, BNV));
+    if (tiles <= wgs)
+        gemm_big_kernel<BM, BN, NW, WAVES_M, 64, 2, false, true, true, EPI, 2, BNV, false, true, false>
+            <<<tiles, NW * 64, 0, s>>>(g, g.K, GroupSched{});
+    else
+        gemm_big_kernel<BM, BN, NW, WAVES_M, 64, 2, false, true, true, EPI, 2, BNV, false, true, true>
+            <<<wgs, NW * 64, 0, s>>>(g, g.K, GroupSched{});
+    return hipGetLastError();
 }
 
 template <int BM, int BN, int NW, int WAVES_M, int KB, int NS, bool XPF, bool AK, bool BKC, int EPI, int OCC = 2,
-          int BNV = BN>
+          int BNV = BN, bool RL = false>
 hipError_t launch_big(const GemmArgs& g, hipStream_t s, int splits = 1, int kchunk = 0) {
     dim3 grid(cdiv(g.M, BM) * cdiv(g.N, BNV), splits);
-    gemm_big_kernel<BM, BN, NW, WAVES_M, KB, NS, XPF, AK, BKC, EPI, OCC, BNV>
+    gemm_big_kernel<BM, BN, NW, WAVES_M, KB, NS, XPF, AK, BKC, EPI, OCC, BNV, false, RL>
         <<<grid, NW * 64, 0, s>>>(g, kchunk ? kchunk : g.K, GroupSched{});
     return hipGetLastError();
 }
@@ -902,6 +1083,14 @@ hipError_t gemm_mfma_bf16(const GemmArgs& g, hipStream_t s) {
 #define BIG192(AKC, BKCC, E) launch_big<256, 256, 8, 4, 32, GEMM_BIG_NS, GEMM_BIG_XPF, AKC, BKCC, E, 2, 192>(g, s)
     const bool w192 = use_192(g.M, g.N);
     if (g.a_kcontig && g.b_kcontig) {
+        // A plain-store product over at least two rounds of 256 x 256 tiles
+        // (the classifier's logits: 49 rounds at B*T = 16384) runs the
+        // persistent register-staged kernel; its buffer resources span each
+        // operand's rows, whose byte extent must fit the 31-bit record count.
+        const int wgs = device_slots();
+        if (g.epi == EPI_STORE && !w192 && cdiv(g.M, 256) * cdiv(g.N, 256) >= 2 * wgs &&
+            (int64_t)g.M * g.lda * 2 < ((int64_t)1 << 31) && (int64_t)g.N * g.ldb * 2 < ((int64_t)1 << 31))
+            return launch_pers<256, 256, 8, 2, EPI_STORE>(g, s, wgs);
         switch (g.epi) {
             case EPI_STORE: return w192 ? BIG192(true, true, EPI_STORE) : BIG256(true, true, EPI_STORE);
             case EPI_BIAS: return w192 ? BIG192(true, true, EPI_BIAS) : BIG256(true, true, EPI_BIAS);

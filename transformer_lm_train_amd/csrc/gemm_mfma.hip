@@ -1083,20 +1083,28 @@ hipError_t gemm_mfma_bf16(const GemmArgs& g, hipStream_t s) {
 #define BIG192(AKC, BKCC, E) launch_big<256, 256, 8, 4, 32, GEMM_BIG_NS, GEMM_BIG_XPF, AKC, BKCC, E, 2, 192>(g, s)
     const bool w192 = use_192(g.M, g.N);
     if (g.a_kcontig && g.b_kcontig) {
-        // A plain-store product over at least two rounds of 256 x 256 tiles
-        // (the classifier's logits: 49 rounds at B*T = 16384) runs the
-        // persistent register-staged kernel; its buffer resources span each
-        // operand's rows, whose byte extent must fit the 31-bit record count.
+        // 256-wide tiles take the register-staged kernel (its buffer
+        // resources span each operand's rows, whose byte extent must fit the
+        // 31-bit record count): persistent for a plain store over at least
+        // two rounds of tiles (the classifier's logits: 49 rounds at B*T =
+        // 16384), one tile per workgroup for the bias epilogues, whose
+        // operand loads would otherwise queue behind the next tile's.
+        const bool rl = !w192 && (int64_t)g.M * g.lda * 2 < ((int64_t)1 << 31) &&
+                        (int64_t)g.N * g.ldb * 2 < ((int64_t)1 << 31);
         const int wgs = device_slots();
-        if (g.epi == EPI_STORE && !w192 && cdiv(g.M, 256) * cdiv(g.N, 256) >= 2 * wgs &&
-            (int64_t)g.M * g.lda * 2 < ((int64_t)1 << 31) && (int64_t)g.N * g.ldb * 2 < ((int64_t)1 << 31))
+        if (rl && g.epi == EPI_STORE && cdiv(g.M, 256) * cdiv(g.N, 256) >= 2 * wgs)
             return launch_pers<256, 256, 8, 2, EPI_STORE>(g, s, wgs);
+#define RL256(E) launch_pers<256, 256, 8, 2, E>(g, s, 1 << 30)
         switch (g.epi) {
             case EPI_STORE: return w192 ? BIG192(true, true, EPI_STORE) : BIG256(true, true, EPI_STORE);
-            case EPI_BIAS: return w192 ? BIG192(true, true, EPI_BIAS) : BIG256(true, true, EPI_BIAS);
+            case EPI_BIAS: return w192 ? BIG192(true, true, EPI_BIAS) : rl ? RL256(EPI_BIAS) : BIG256(true, true, EPI_BIAS);
             case EPI_BIAS_RESID:
-                return w192 ? BIG192(true, true, EPI_BIAS_RESID) : BIG256(true, true, EPI_BIAS_RESID);
-            case EPI_BIAS_GELU: return w192 ? BIG192(true, true, EPI_BIAS_GELU) : BIG256(true, true, EPI_BIAS_GELU);
+                return w192 ? BIG192(true, true, EPI_BIAS_RESID)
+                            : rl ? RL256(EPI_BIAS_RESID) : BIG256(true, true, EPI_BIAS_RESID);
+            case EPI_BIAS_GELU:
+                return w192 ? BIG192(true, true, EPI_BIAS_GELU)
+                            : rl ? RL256(EPI_BIAS_GELU) : BIG256(true, true, EPI_BIAS_GELU);
+#undef RL256
             // the fused classifier: 256-wide tiles, whose waves' 64-column
             // groups are the statistics' column groups
             case EPI_CE_STATS:

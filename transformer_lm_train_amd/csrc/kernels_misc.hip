@@ -645,6 +645,130 @@ void layernorm_bwd_kernel(T* dout, const T* din, const T* dy, const T* x, const 
     }
 }
 
+// Rows of 129-256 16-byte chunks (C = 1032 ... 2048 in bf16): each row is
+// split over a pair of waves, wave h of the pair taking half h of its chunks,
+// so a lane holds at most two chunks of each operand and the kernel keeps two
+// waves per SIMD (the whole-row kernel needs one wave per SIMD there).  The
+// block's two pairs work rows rbase and rbase + 1 of each step; the pair adds
+// its two halves of the row sums (half 0 first) through a double-buffered LDS
+// slot, one barrier per step, and every wave runs the same steps, so all of
+// them reach every barrier.  Channel sums as above, per pair, then the two
+// pairs added: partial[k][block][c], the same layout.
+template <typename T, int NP>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void layernorm_bwd_split_kernel(T* dout, const T* din, const T* dy, const T* x, const float* w, const float* mean,
+                                const float* rstd, float* partial, int N, int C) {
+    constexpr int VN = Vec16<T>::N, MAXV = 2;
+    extern __shared__ float smem[];  // [2 pairs][NP][C]
+    __shared__ float rsum[2][2][2][2];  // [buffer][pair][half][sum g, sum g*xhat]
+    const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform
+    const int pair = wv >> 1, half = wv & 1;
+    const int chunks = C / VN, H = (chunks + 1) / 2;
+    const int cbeg = half * H, cend = min(chunks, cbeg + H);
+    const int step = gridDim.x * 2;
+    float acc[NP][MAXV][VN];
+    float wr[MAXV][VN];
+#pragma unroll
+    for (int i = 0; i < MAXV; i++) {
+        const int ch = cbeg + lane + i * 64;
+#pragma unroll
+        for (int j = 0; j < VN; j++) {
+            wr[i][j] = ch < cend ? w[ch * VN + j] : 0.f;
+#pragma unroll
+            for (int k = 0; k < NP; k++) acc[k][i][j] = 0.f;
+        }
+    }
+    Vec16<T> xc[MAXV], dc[MAXV], oc[MAXV], xn[MAXV], dn[MAXV], on[MAXV];
+    float mun = 0.f, rsn = 0.f;
+    auto load = [&](int row) {
+        if (row >= N) return;
+        const int64_t o = (int64_t)row * C;
+#pragma unroll
+        for (int i = 0; i < MAXV; i++) {
+            const int ch = cbeg + lane + i * 64;
+            if (ch < cend) {
+                xn[i] = ld16(x + o + ch * VN);
+                dn[i] = ld16(dy + o + ch * VN);
+                if (din) on[i] = ld16(din + o + ch * VN);
+            }
+        }
+        mun = mean[row];
+        rsn = rstd[row];
+    };
+    int buf = 0;
+    load(blockIdx.x * 2 + pair);
+    for (int rbase = blockIdx.x * 2; rbase < N; rbase += step, buf ^= 1) {
+        const int row = rbase + pair;
+        const float mu = mun, rs = rsn;
+#pragma unroll
+        for (int i = 0; i < MAXV; i++) { xc[i] = xn[i]; dc[i] = dn[i]; oc[i] = on[i]; }
+        load(rbase + step + pair);
+        float sg = 0.f, sgx = 0.f;
+        if (row < N) {
+#pragma unroll
+            for (int i = 0; i < MAXV; i++) {
+                if (cbeg + lane + i * 64 < cend) {
+#pragma unroll
+                    for (int j = 0; j < VN; j++) {
+                        const float d = to_f32(dc[i].v[j]);
+                        const float xh = (to_f32(xc[i].v[j]) - mu) * rs;
+                        const float gg = d * wr[i][j];
+                        sg += gg;
+                        sgx += gg * xh;
+                        acc[0][i][j] += d * xh;
+                        acc[1][i][j] += d;
+                    }
+                }
+            }
+        }
+        sg = wave_sum(sg);
+        sgx = wave_sum(sgx);
+        if (lane == 0) {
+            rsum[buf][pair][half][0] = sg;
+            rsum[buf][pair][half][1] = sgx;
+        }
+        __syncthreads();
+        const float SG = (rsum[buf][pair][0][0] + rsum[buf][pair][1][0]) / C;
+        const float SGX = (rsum[buf][pair][0][1] + rsum[buf][pair][1][1]) / C;
+        if (row < N) {
+            T* orow = dout + (int64_t)row * C;
+#pragma unroll
+            for (int i = 0; i < MAXV; i++) {
+                const int ch = cbeg + lane + i * 64;
+                if (ch < cend) {
+                    Vec16<T> o;
+#pragma unroll
+                    for (int j = 0; j < VN; j++) {
+                        const float xh = (to_f32(xc[i].v[j]) - mu) * rs;
+                        const float gg = to_f32(dc[i].v[j]) * wr[i][j];
+                        const float dx = rs * (gg - SG - xh * SGX);
+                        const T v = from_f32<T>(din ? to_f32(oc[i].v[j]) + dx : dx);
+                        o.v[j] = v;
+                        if constexpr (NP == 3) acc[2][i][j] += to_f32(v);
+                    }
+                    st16(orow + ch * VN, o);
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < MAXV; i++) {
+        const int ch = cbeg + lane + i * 64;
+        if (ch < cend) {
+#pragma unroll
+            for (int k = 0; k < NP; k++)
+#pragma unroll
+                for (int j = 0; j < VN; j++) smem[(pair * NP + k) * C + ch * VN + j] = acc[k][i][j];
+        }
+    }
+    __syncthreads();
+    for (int c = threadIdx.x; c < C; c += 256) {
+#pragma unroll
+        for (int k = 0; k < NP; k++)
+            partial[((int64_t)k * gridDim.x + blockIdx.x) * C + c] = smem[k * C + c] + smem[(NP + k) * C + c];
+    }
+}
+
 // For each job, out_k[c] += sum_g partial[k*G + g][c] for its non-null out_k
 // (k < 3).  Block: 64 columns x 64 row lanes of one job (the jobs' blocks are
 // laid end to end); each lane holds 4 consecutive columns (16 lanes read 256
@@ -756,7 +880,13 @@ hipError_t layernorm_bwd(T* dout, const T* din, const T* dy, const T* x, const f
     // larger grid gain nothing and add partial rows)
     if (per_lane <= 1) LN_BWD(1, 2);
     else if (per_lane <= 2) LN_BWD(2, 1);
-    else if (per_lane <= 4) LN_BWD(4, 2);
+    else if (per_lane <= 4 && (C / Vec16<T>::N + 1) / 2 <= 128) {
+        // rows split over two waves (C = 1600 in bf16, 8192 rows: 37.8 -> 25.5 us per
+        // launch against the whole-row kernel at one wave per SIMD)
+        const size_t lds2 = sizeof(float) * 2 * NP * C;
+        if (dsum) layernorm_bwd_split_kernel<T, 3><<<G, 256, lds2, s>>>(dout, din, dy, x, w, mean, rstd, partial, N, C);
+        else layernorm_bwd_split_kernel<T, 2><<<G, 256, lds2, s>>>(dout, din, dy, x, w, mean, rstd, partial, N, C);
+    } else if (per_lane <= 4) LN_BWD(4, 2);
     else LN_BWD(8, 1);
 #undef LN_BWD
     return LAUNCH_CHECK();
@@ -1016,14 +1146,27 @@ hipError_t loss_mean(float* out, const float* losses, int n, hipStream_t s) {
 // ============================================================================
 constexpr int NORM_G = 1024;
 
+// Each pass of a block reads NORM_U x 256 float4 groups (group u at
+// (block * NORM_U + u) * 256 + thread), all requested before any is used,
+// with non-temporal loads: 0.5 GB of gradients at 124M, 122 -> 73 us from
+// cold caches against plain loads one group at a time (6.8 TB/s).
+constexpr int NORM_U = 4;
 __global__ __launch_bounds__(256) void sumsq_kernel(float* partial, const float* g, size_t n) {
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
     __shared__ float red[4];
     float s = 0.f;
-    size_t n4 = n / 4;
-    const float4* g4 = reinterpret_cast<const float4*>(g);
-    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (size_t)gridDim.x * 256) {
-        float4 q = g4[i];
-        s += q.x * q.x + q.y * q.y + q.z * q.z + q.w * q.w;
+    const size_t n4 = n / 4;
+    const f32x4* g4 = reinterpret_cast<const f32x4*>(g);
+    const size_t stride = (size_t)gridDim.x * NORM_U * 256;
+    for (size_t base = (size_t)blockIdx.x * NORM_U * 256 + threadIdx.x; base < n4; base += stride) {
+        f32x4 q[NORM_U];
+#pragma unroll
+        for (int u = 0; u < NORM_U; u++) {
+            const size_t i = base + (size_t)u * 256;
+            q[u] = i < n4 ? __builtin_nontemporal_load(g4 + i) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int u = 0; u < NORM_U; u++) s += q[u].x * q[u].x + q[u].y * q[u].y + q[u].z * q[u].z + q[u].w * q[u].w;
     }
     if (blockIdx.x == 0 && threadIdx.x < (n & 3)) {
         float q = g[n4 * 4 + threadIdx.x];

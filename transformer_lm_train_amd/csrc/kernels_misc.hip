@@ -782,6 +782,13 @@ struct SumBatch {
     int overwrite;  // out = sum instead of out += sum
 };
 
+// Each partial row is read once, long after it was written: non-temporal
+// loads (the step's batch, ~146 MB from cold caches: 71.6 -> 34.8 us).
+DEVI float4 ld_f4_stream(const float* p) {
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    const f32x4 t = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+    return make_float4(t.x, t.y, t.z, t.w);
+}
 __global__ __launch_bounds__(1024) void sum_partials_kernel(SumBatch bt) {
     __shared__ __attribute__((aligned(16))) float red[3][64][68];  // read and written as float4
     // the job whose block range holds this block: the last k with start[k] <= blockIdx.x
@@ -810,9 +817,9 @@ __global__ __launch_bounds__(1024) void sum_partials_kernel(SumBatch bt) {
             for (int u = 0; u < U; u++) {
                 const int g = g0 + 64 * u;
                 const float* pr = partial + (int64_t)g * C + c0;
-                v0[u] = g < G ? *reinterpret_cast<const float4*>(pr) : z4;
-                v1[u] = nk > 1 && g < G ? *reinterpret_cast<const float4*>(pr + (int64_t)G * C) : z4;
-                v2[u] = nk > 2 && g < G ? *reinterpret_cast<const float4*>(pr + 2 * (int64_t)G * C) : z4;
+                v0[u] = g < G ? ld_f4_stream(pr) : z4;
+                v1[u] = nk > 1 && g < G ? ld_f4_stream(pr + (int64_t)G * C) : z4;
+                v2[u] = nk > 2 && g < G ? ld_f4_stream(pr + 2 * (int64_t)G * C) : z4;
             }
 #pragma unroll
             for (int u = 0; u < U; u++) {

@@ -850,7 +850,15 @@ int device_slots() {
 }
 
 // The register-staged kernel (both operands k-contiguous, k-step 64, two LDS
-// stages): persistent over wgs workgroups when the tiles outnumber them.
+// stages), one tile per workgroup.
+template <int BM, int BN, int NW, int WAVES_M, int EPI, int BNV = BN>
+hipError_t launch_rl(const GemmArgs& g, hipStream_t s) {
+    gemm_big_kernel<BM, BN, NW, WAVES_M, 64, 2, false, true, true, EPI, 2, BNV, false, true, false>
+        <<<(unsigned)(cdiv(g.M, BM) * cdiv(g.N, BNV)), NW * 64, 0, s>>>(g, g.K, GroupSched{});
+    return hipGetLastError();
+}
+
+// The same kernel, persistent over wgs workgroups when the tiles outnumber them.
 template <int BM, int BN, int NW, int WAVES_M, int EPI, int BNV = BN>
 hipError_t launch_pers(const GemmArgs& g, hipStream_t s, int wgs) {
     const int tiles = (int)(cdiv(g.M, BM) * cdiv(g.N, BNV));
@@ -1094,7 +1102,7 @@ hipError_t gemm_mfma_bf16(const GemmArgs& g, hipStream_t s) {
         const int wgs = device_slots();
         if (rl && g.epi == EPI_STORE && cdiv(g.M, 256) * cdiv(g.N, 256) >= 2 * wgs)
             return launch_pers<256, 256, 8, 2, EPI_STORE>(g, s, wgs);
-#define RL256(E) launch_pers<256, 256, 8, 2, E>(g, s, 1 << 30)
+#define RL256(E) launch_rl<256, 256, 8, 2, E>(g, s)
         switch (g.epi) {
             case EPI_STORE: return w192 ? BIG192(true, true, EPI_STORE) : BIG256(true, true, EPI_STORE);
             case EPI_BIAS: return w192 ? BIG192(true, true, EPI_BIAS) : rl ? RL256(EPI_BIAS) : BIG256(true, true, EPI_BIAS);

@@ -1112,17 +1112,17 @@ hipError_t gemm_mfma_bf16(const GemmArgs& g, hipStream_t s) {
             case EPI_BIAS_GELU:
                 return w192 ? BIG192(true, true, EPI_BIAS_GELU)
                             : rl ? RL256(EPI_BIAS_GELU) : BIG256(true, true, EPI_BIAS_GELU);
-#undef RL256
             // the fused classifier: 256-wide tiles, whose waves' 64-column
             // groups are the statistics' column groups
             case EPI_CE_STATS:
                 if (!g.ce_targets || !g.ce_stats || !g.ce_zt || g.ce_ld != (int)cdiv(g.N, 64)) return hipErrorInvalidValue;
-                return BIG256(true, true, EPI_CE_STATS);
+                return rl ? RL256(EPI_CE_STATS) : BIG256(true, true, EPI_CE_STATS);
             case EPI_CE_GRAD:
                 if (!g.ce_targets || !g.ce_lse2 || !g.out) return hipErrorInvalidValue;
-                return BIG256(true, true, EPI_CE_GRAD);
+                return rl ? RL256(EPI_CE_GRAD) : BIG256(true, true, EPI_CE_GRAD);
             default: return hipErrorInvalidValue;
         }
+#undef RL256
     }
     if (g.a_kcontig && !g.b_kcontig) {
         if (g.epi == EPI_STORE && g.ws && g.N % 4 == 0 && g.ldo % 4 == 0) {

@@ -114,5 +114,12 @@ DEVI float gelu_grad_f(float u) {
     const float dv = fmaf(6.f * GELU_K * GELU_C, u * u, 2.f * GELU_K);  // v'
     return s * fmaf(u * dv, 1.f - s, 1.f);
 }
+// both from one sigmoid: gelu(u) into y, gelu'(u) into dy
+DEVI void gelu_and_grad(float u, float& y, float& dy) {
+    const float s = gelu_sig(u);
+    const float dv = fmaf(6.f * GELU_K * GELU_C, u * u, 2.f * GELU_K);
+    y = u * s;
+    dy = s * fmaf(u * dv, 1.f - s, 1.f);
+}
 
 static inline unsigned cdiv(size_t a, size_t b) { return (unsigned)((a + b - 1) / b); }

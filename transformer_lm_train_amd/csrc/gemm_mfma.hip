@@ -75,10 +75,10 @@ DEVI void epilogue_rows(const GemmArgs& g, const f32x16 (&acc)[FM][FN], float* r
     constexpr int RPI = 64 / LPR;  // rows per access instruction
     constexpr int NR = RH / RPI;   // row groups per pass
     static_assert(RH == 32 || RH == 16, "rows per pass");
-    constexpr bool BIAS = EPI == EPI_BIAS || EPI == EPI_BIAS_RESID || EPI == EPI_BIAS_GELU;
+    constexpr bool BIAS = EPI == EPI_BIAS || EPI == EPI_BIAS_RESID || EPI == EPI_BIAS_GELU || EPI == EPI_BIAS_GELU_D;
     typedef bf16 bf16x8_t __attribute__((ext_vector_type(8)));
     const int hi = lane >> 5, l32 = lane & 31;
-    constexpr bool CSUM = EPI == EPI_GELU_BWD;  // column sums of the outputs, if g.colsum_ws
+    constexpr bool CSUM = EPI == EPI_GELU_BWD || EPI == EPI_MUL_AUX;  // column sums of the outputs, if g.colsum_ws
     float cs[NCG][8];
 #pragma unroll
     for (int cg = 0; cg < NCG; cg++)
@@ -113,7 +113,7 @@ DEVI void epilogue_rows(const GemmArgs& g, const f32x16 (&acc)[FM][FN], float* r
                 const int64_t o = (int64_t)m * g.ldo + n;
                 if constexpr (EPI == EPI_BIAS_RESID)
                     r16[cg][rr] = ok ? *reinterpret_cast<const bf16x8_t*>((const bf16*)g.resid + o) : bf16x8_t{};
-                if constexpr (EPI == EPI_GELU_BWD)
+                if constexpr (EPI == EPI_GELU_BWD || EPI == EPI_MUL_AUX)
                     r16[cg][rr] = ok ? *reinterpret_cast<const bf16x8_t*>((const bf16*)g.aux + o) : bf16x8_t{};
                 if constexpr (EPI == EPI_ACC_F32) {
                     const bool rd = ok && !g.acc_overwrite;
@@ -208,8 +208,24 @@ DEVI void epilogue_rows(const GemmArgs& g, const f32x16 (&acc)[FM][FN], float* r
                     if constexpr (BIAS) y[e] += b8[cg][e];
                     if constexpr (EPI == EPI_BIAS_RESID) y[e] += (float)r16[cg][rr][e];
                     if constexpr (EPI == EPI_GELU_BWD) y[e] *= gelu_grad_f((float)r16[cg][rr][e]);
+                    if constexpr (EPI == EPI_MUL_AUX) y[e] *= (float)r16[cg][rr][e];
                 }
                 bf16x8_t out;
+                if constexpr (EPI == EPI_BIAS_GELU_D) {
+                    // GELU' (read by the backward, long after: non-temporal, as
+                    // the pre-activation below) and GELU (the next product's input)
+                    bf16x8_t act;
+#pragma unroll
+                    for (int e = 0; e < 8; e++) {
+                        float a, d;
+                        gelu_and_grad(y[e], a, d);
+                        act[e] = (bf16)a;
+                        out[e] = (bf16)d;
+                    }
+                    __builtin_nontemporal_store(out, reinterpret_cast<bf16x8_t*>((bf16*)g.out + o));
+                    *reinterpret_cast<bf16x8_t*>((bf16*)g.out2 + o) = act;
+                    continue;
+                }
 #pragma unroll
                 for (int e = 0; e < 8; e++) out[e] = (bf16)y[e];
                 if constexpr (EPI == EPI_BIAS_GELU)
@@ -1112,6 +1128,11 @@ hipError_t gemm_mfma_bf16(const GemmArgs& g, hipStream_t s) {
             case EPI_BIAS_GELU:
                 return w192 ? BIG192(true, true, EPI_BIAS_GELU)
                             : rl ? RL256(EPI_BIAS_GELU) : BIG256(true, true, EPI_BIAS_GELU);
+            case EPI_BIAS_GELU_D:
+                return w192 ? BIG192(true, true, EPI_BIAS_GELU_D)
+                            : rl ? RL256(EPI_BIAS_GELU_D) : BIG256(true, true, EPI_BIAS_GELU_D);
+            case EPI_MUL_AUX:
+                return w192 ? BIG192(true, true, EPI_MUL_AUX) : rl ? RL256(EPI_MUL_AUX) : BIG256(true, true, EPI_MUL_AUX);
             // the fused classifier: 256-wide tiles, whose waves' 64-column
             // groups are the statistics' column groups
             case EPI_CE_STATS:
@@ -1141,6 +1162,11 @@ hipError_t gemm_mfma_bf16(const GemmArgs& g, hipStream_t s) {
         switch (g.epi) {
             case EPI_STORE: return w192 ? BIG192(true, false, EPI_STORE) : BIG256(true, false, EPI_STORE);
             case EPI_GELU_BWD: return w192 ? BIG192(true, false, EPI_GELU_BWD) : BIG256(true, false, EPI_GELU_BWD);
+            case EPI_MUL_AUX: return w192 ? BIG192(true, false, EPI_MUL_AUX) : BIG256(true, false, EPI_MUL_AUX);
+            case EPI_BIAS: return w192 ? BIG192(true, false, EPI_BIAS) : BIG256(true, false, EPI_BIAS);
+            case EPI_BIAS_RESID: return w192 ? BIG192(true, false, EPI_BIAS_RESID) : BIG256(true, false, EPI_BIAS_RESID);
+            case EPI_BIAS_GELU_D:
+                return w192 ? BIG192(true, false, EPI_BIAS_GELU_D) : BIG256(true, false, EPI_BIAS_GELU_D);
             default: return hipErrorInvalidValue;
         }
     }

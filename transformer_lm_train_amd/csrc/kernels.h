@@ -24,6 +24,10 @@ enum GemmEpi {
                          // units, and sum of 2^(z log2 e - that max)); ce_zt[m] = z at n = targets[m]
     EPI_CE_GRAD = 7,     // out (bf16) = (softmax - onehot(targets[m])) * ce_scale, i.e.
                          // (2^(z log2 e - ce_lse2[m]) - [n == targets[m]]) * ce_scale, 0 for n >= ce_V
+    // The GELU pair of the bf16 MFMA path: the forward keeps the derivative
+    // instead of the pre-activation, so that the backward's product only scales.
+    EPI_BIAS_GELU_D = 8,  // u = acc + bias[n]: out = GELU'(u), out2 = GELU(u)
+    EPI_MUL_AUX = 9,      // out = acc * aux[m][n] (column sums as EPI_GELU_BWD)
 };
 // EPI_ACC_F32 may split the reduction over several workgroups: each writes
 // its fp32 partial tile to ws[split][M][N] and a second kernel adds the
@@ -48,7 +52,7 @@ struct GemmArgs {
     float* ws;           // split-K workspace (EPI_ACC_F32), may be NULL
     size_t ws_bytes;
     bool acc_overwrite;  // EPI_ACC_F32: out = acc (out's old contents are not read)
-    // EPI_GELU_BWD, bf16 MFMA path: partial column sums of out (the bias
+    // EPI_GELU_BWD and EPI_MUL_AUX, bf16 MFMA path: partial column sums of out (the bias
     // gradient of the layer whose output gradient this product produces),
     // one row per wave row block: colsum_ws [gemm_colsum_rows(M, N)][N].
     // The caller sums them (sum_partials_batch).  NULL: off.

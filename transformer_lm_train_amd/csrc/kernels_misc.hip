@@ -989,6 +989,13 @@ template <typename T> DEVI void keep_packed(Vec16<T>& q) {
 // per CU and the block reductions are short.  Rows are streamed with
 // non-temporal loads and stores (3.3 GB per step at 124M, far above the
 // caches: 0.66 -> 0.63 ms per step against plain accesses).
+//
+// The three passes over the registers (max, sum of exponentials, gradient)
+// are vector-ALU bound, so the per-element work is kept to the widening, one
+// FMA and one exp2 (plus the max, the add or the scale and the packing):
+// only the chunk that holds the vocabulary's end tests columns against V,
+// the target logit is read separately by one thread, and the -1 of the
+// target is applied by the one thread whose chunk holds it.
 template <typename T, int NT, int MAXC>
 __global__ __launch_bounds__(NT) void softmax_ce_kernel(T* logits, float* losses, const int* targets, int V, int Vp,
                                                         float dscale, int* err) {
@@ -999,28 +1006,33 @@ __global__ __launch_bounds__(NT) void softmax_ce_kernel(T* logits, float* losses
     const int row = blockIdx.x;
     T* z = logits + (int64_t)row * Vp;
     const int chunks = Vp / VN;
+    const int full = V / VN;  // chunks whose columns are all below V
     int tgt = targets[row];
     if (tgt < 0 || tgt >= V) {
         if (threadIdx.x == 0) atomicOr(err, 2);
         tgt = 0;
     }
+    const int tch = tgt / VN, tj = tgt - tch * VN;
     Vec16<T> q[MAXC];
 #pragma unroll
     for (int i = 0; i < MAXC; i++) {
         const int ch = threadIdx.x + i * NT;
         if (ch < chunks) q[i] = ld16_stream(z + ch * VN);
     }
+    // read before any thread of the block overwrites the row (the stores
+    // follow the two block reductions and their barriers)
+    if (threadIdx.x == 0) s_zt = to_f32(z[tgt]);
     float mx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < MAXC; i++) {
         const int ch = threadIdx.x + i * NT;
-        if (ch < chunks) {
+        if (ch < full) {
 #pragma unroll
-            for (int j = 0; j < VN; j++) {
-                const float x = to_f32(q[i].v[j]);
-                if (ch * VN + j < V) mx = fmaxf(mx, x);
-                if (ch * VN + j == tgt) s_zt = x;  // static index: the row stays in registers
-            }
+            for (int j = 0; j < VN; j++) mx = fmaxf(mx, to_f32(q[i].v[j]));
+        } else if (ch < chunks) {
+#pragma unroll
+            for (int j = 0; j < VN; j++)
+                if (ch * VN + j < V) mx = fmaxf(mx, to_f32(q[i].v[j]));
         }
     }
     const float M2 = block_max<NT>(mx, sh) * L2E;  // row max, log2 units
@@ -1030,7 +1042,10 @@ __global__ __launch_bounds__(NT) void softmax_ce_kernel(T* logits, float* losses
 #pragma unroll
     for (int i = 0; i < MAXC; i++) {
         const int ch = threadIdx.x + i * NT;
-        if (ch < chunks) {
+        if (ch < full) {
+#pragma unroll
+            for (int j = 0; j < VN; j++) se += __builtin_amdgcn_exp2f(fmaf(to_f32(q[i].v[j]), L2E, -M2));
+        } else if (ch < chunks) {
 #pragma unroll
             for (int j = 0; j < VN; j++)
                 if (ch * VN + j < V) se += __builtin_amdgcn_exp2f(fmaf(to_f32(q[i].v[j]), L2E, -M2));
@@ -1045,14 +1060,23 @@ __global__ __launch_bounds__(NT) void softmax_ce_kernel(T* logits, float* losses
     for (int i = 0; i < MAXC; i++) {
         const int ch = threadIdx.x + i * NT;
         if (ch < chunks) {
+            float d[VN];
+            if (ch < full) {
+#pragma unroll
+                for (int j = 0; j < VN; j++) d[j] = __builtin_amdgcn_exp2f(fmaf(to_f32(q[i].v[j]), L2E, -M2)) * ps;
+            } else {
+#pragma unroll
+                for (int j = 0; j < VN; j++)
+                    d[j] = ch * VN + j < V ? __builtin_amdgcn_exp2f(fmaf(to_f32(q[i].v[j]), L2E, -M2)) * ps : 0.f;
+            }
+            if (ch == tch) {
+#pragma unroll
+                for (int j = 0; j < VN; j++)
+                    if (j == tj) d[j] -= dscale;
+            }
             Vec16<T> o;
 #pragma unroll
-            for (int j = 0; j < VN; j++) {
-                const int v = ch * VN + j;
-                float d = v < V ? __builtin_amdgcn_exp2f(fmaf(to_f32(q[i].v[j]), L2E, -M2)) * ps : 0.f;
-                if (v == tgt) d -= dscale;
-                o.v[j] = from_f32<T>(d);
-            }
+            for (int j = 0; j < VN; j++) o.v[j] = from_f32<T>(d[j]);
             st16_stream(z + ch * VN, o);
         }
     }

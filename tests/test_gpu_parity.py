@@ -228,12 +228,15 @@ def compare_blocks(got, ref, cfg, tol, names=SUMMED):
 #    reduction) on two thin blocks;
 #  * width 768: one block of the 124M width at B=16, T=1024, so the LayerNorm,
 #    attention and product kernels are the benchmark's own instantiations;
+#  * width 1024 (the 350M width, 16 heads) at B=16, T=1024: its LayerNorm
+#    rows fill both chunks of every lane;
 #  * 124M at B=1, T=1024: the whole benchmark model at its sequence length;
 #  * width 1600 (the 1.6B width, 25 heads): the LayerNorm kernels for rows
 #    over 1024 bf16 channels, with 4 rows per backward wave.
 FULL = {
     "narrow": (dict(L=2, C=128, NH=2, maxT=1024, V=1024, Vp=1024), 16, 1024),
     "w768": (dict(L=1, C=768, NH=12, maxT=1024, V=2048, Vp=2048), 16, 1024),
+    "w1024": (dict(L=1, C=1024, NH=16, maxT=1024, V=2048, Vp=2048), 16, 1024),
     "124m_b1": (M124, 1, 1024),
     "w1600": (dict(L=1, C=1600, NH=25, maxT=256, V=1000, Vp=1024), 32, 256),
 }

@@ -645,6 +645,139 @@ void layernorm_bwd_kernel(T* dout, const T* din, const T* dy, const T* x, const 
     }
 }
 
+// Rows of 32*CPL 16-byte chunks with CPL odd (C = 768 in bf16: CPL = 3),
+// which the whole-wave kernel spreads unevenly (lanes 0-31 two chunks, lanes
+// 32-63 one): each half-wave takes a row of its own, lane l of the half the
+// chunks l, l + 32, ...; the wave works two rows at a time (its next two
+// requested first), with the same per-row arithmetic.  The halves' row sums
+// come out of one pass of row-wise DPP adds (lanes 16r hold the sums of the
+// 16-lane rows r; the half h adds rows 2h and 2h + 1).  Channel sums as in the
+// whole-wave kernel, the two halves added (half 0 first), then the 4 waves:
+// partial[k][block][c], the same layout.
+DEVI void half_sums(float x, int h, float& s) {
+    x += dpp_mov<0xB1>(x);
+    x += dpp_mov<0x4E>(x);
+    x += dpp_mov<0x124>(x);
+    x += dpp_mov<0x128>(x);
+    const float s0 = lane_value(x, 0) + lane_value(x, 16), s1 = lane_value(x, 32) + lane_value(x, 48);
+    s = h ? s1 : s0;
+}
+
+template <typename T, int CPL, int NP>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void layernorm_bwd_half_kernel(T* dout, const T* din, const T* dy, const T* x, const float* w, const float* mean,
+                               const float* rstd, float* partial, int N, int C) {
+    constexpr int VN = Vec16<T>::N;
+    extern __shared__ float smem[];  // [4][NP][C]
+    const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform
+    const int h = lane >> 5, l32 = lane & 31;
+    const int step = gridDim.x * 8;                  // rows between a wave's consecutive pairs
+    const int row0 = (blockIdx.x * 4 + wv) * 2 + h;  // this half's first row
+    float acc[NP][CPL][VN];
+    float wr[CPL][VN];
+#pragma unroll
+    for (int i = 0; i < CPL; i++) {
+        const int ch = l32 + i * 32;
+#pragma unroll
+        for (int j = 0; j < VN; j++) {
+            wr[i][j] = w[ch * VN + j];
+#pragma unroll
+            for (int k = 0; k < NP; k++) acc[k][i][j] = 0.f;
+        }
+    }
+    Vec16<T> xc[CPL], dc[CPL], oc[CPL], xn[CPL], dn[CPL], on[CPL];
+    float mun = 0.f, rsn = 0.f;
+    auto load = [&](int row) {
+        if (row >= N) return;
+        const int64_t o = (int64_t)row * C;
+#pragma unroll
+        for (int i = 0; i < CPL; i++) {
+            const int ch = l32 + i * 32;
+            xn[i] = ld16(x + o + ch * VN);
+            dn[i] = ld16(dy + o + ch * VN);
+            if (din) on[i] = ld16(din + o + ch * VN);
+        }
+        mun = mean[row];
+        rsn = rstd[row];
+    };
+    load(row0);
+    // every wave runs while either of its halves has a row (both halves take
+    // part in the row sums' lane reads)
+    for (int r = row0 - h; r < N; r += step) {
+        const int row = r + h;
+        const bool ok = row < N;
+        const float mu = mun, rs = rsn;
+#pragma unroll
+        for (int i = 0; i < CPL; i++) { xc[i] = xn[i]; dc[i] = dn[i]; oc[i] = on[i]; }
+        load(row + step);
+        float sg = 0.f, sgx = 0.f;
+        if (ok) {
+#pragma unroll
+            for (int i = 0; i < CPL; i++)
+#pragma unroll
+                for (int j = 0; j < VN; j++) {
+                    const float d = to_f32(dc[i].v[j]);
+                    const float xh = (to_f32(xc[i].v[j]) - mu) * rs;
+                    const float gg = d * wr[i][j];
+                    sg += gg;
+                    sgx += gg * xh;
+                    acc[0][i][j] += d * xh;
+                    acc[1][i][j] += d;
+                }
+        }
+        half_sums(sg, h, sg);
+        half_sums(sgx, h, sgx);
+        sg /= C;
+        sgx /= C;
+        if (!ok) continue;
+        T* orow = dout + (int64_t)row * C;
+#pragma unroll
+        for (int i = 0; i < CPL; i++) {
+            const int ch = l32 + i * 32;
+            Vec16<T> o;
+#pragma unroll
+            for (int j = 0; j < VN; j++) {
+                const float xh = (to_f32(xc[i].v[j]) - mu) * rs;
+                const float gg = to_f32(dc[i].v[j]) * wr[i][j];
+                const float dx = rs * (gg - sg - xh * sgx);
+                const T v = from_f32<T>(din ? to_f32(oc[i].v[j]) + dx : dx);
+                o.v[j] = v;
+                if constexpr (NP == 3) acc[2][i][j] += to_f32(v);
+            }
+            st16(orow + ch * VN, o);
+        }
+    }
+    // the halves' channel sums (half 0 first), then the block's 4 waves
+#pragma unroll
+    for (int k = 0; k < NP; k++)
+#pragma unroll
+        for (int i = 0; i < CPL; i++)
+#pragma unroll
+            for (int j = 0; j < VN; j++) {
+                const float other = __shfl_xor(acc[k][i][j], 32, 64);
+                acc[k][i][j] = h ? other + acc[k][i][j] : acc[k][i][j] + other;
+            }
+    if (h == 0) {
+#pragma unroll
+        for (int i = 0; i < CPL; i++) {
+            const int ch = l32 + i * 32;
+#pragma unroll
+            for (int k = 0; k < NP; k++)
+#pragma unroll
+                for (int j = 0; j < VN; j++) smem[(wv * NP + k) * C + ch * VN + j] = acc[k][i][j];
+        }
+    }
+    __syncthreads();
+    for (int c = threadIdx.x; c < C; c += 256) {
+#pragma unroll
+        for (int k = 0; k < NP; k++) {
+            float t = 0.f;
+            for (int q = 0; q < 4; q++) t += smem[(q * NP + k) * C + c];
+            partial[((int64_t)k * gridDim.x + blockIdx.x) * C + c] = t;
+        }
+    }
+}
+
 // Rows of 129-256 16-byte chunks (C = 1032 ... 2048 in bf16): each row is
 // split over a pair of waves, wave h of the pair taking half h of its chunks,
 // so a lane holds at most two chunks of each operand and the kernel keeps two
@@ -886,7 +1019,11 @@ hipError_t layernorm_bwd(T* dout, const T* din, const T* dy, const T* x, const f
     // requested first, measured ~5% faster than two (more waves per SIMD or a
     // larger grid gain nothing and add partial rows)
     if (per_lane <= 1) LN_BWD(1, 2);
-    else if (per_lane <= 2) LN_BWD(2, 1);
+    else if (C / Vec16<T>::N == 96) {
+        // C = 768 in bf16: rows per half-wave
+        if (dsum) layernorm_bwd_half_kernel<T, 3, 3><<<G, 256, lds, s>>>(dout, din, dy, x, w, mean, rstd, partial, N, C);
+        else layernorm_bwd_half_kernel<T, 3, 2><<<G, 256, lds, s>>>(dout, din, dy, x, w, mean, rstd, partial, N, C);
+    } else if (per_lane <= 2) LN_BWD(2, 1);
     else if (per_lane <= 4 && (C / Vec16<T>::N + 1) / 2 <= 128) {
         // rows split over two waves (C = 1600 in bf16, 8192 rows: 37.8 -> 25.5 us per
         // launch against the whole-row kernel at one wave per SIMD)

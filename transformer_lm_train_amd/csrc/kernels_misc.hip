@@ -468,6 +468,91 @@ __global__ __launch_bounds__(256) void layernorm_fwd_rows_kernel(T* out, float* 
     }
 }
 
+// Sums over each half-wave of x, for the half h the lane is in: row-wise DPP
+// adds leave the sum of the 16-lane row r in lane 16r, and half h adds rows
+// 2h and 2h + 1.
+DEVI void half_sums(float x, int h, float& s) {
+    x += dpp_mov<0xB1>(x);
+    x += dpp_mov<0x4E>(x);
+    x += dpp_mov<0x124>(x);
+    x += dpp_mov<0x128>(x);
+    const float s0 = lane_value(x, 0) + lane_value(x, 16), s1 = lane_value(x, 32) + lane_value(x, 48);
+    s = h ? s1 : s0;
+}
+
+// Rows of 32*CPL 16-byte chunks with CPL odd (C = 768 in bf16): one row per
+// half-wave, lane l of the half holding the chunks l, l + 32, ... (every lane
+// CPL chunks, where the whole-wave kernel leaves half the lanes idle in its
+// last chunk); the wave works rows r + h, r + step + h, ... two at a time,
+// the next two requested first.  Row sums as in the LayerNorm backward's
+// half-wave kernel.
+template <typename T, int CPL>
+__global__ __launch_bounds__(256) void layernorm_fwd_half_kernel(T* out, float* mean, float* rstd, const T* x,
+                                                                 const float* w, const float* b, int N, int C) {
+    constexpr int VN = Vec16<T>::N;
+    const int lane = threadIdx.x & 63, h = lane >> 5, l32 = lane & 31;
+    const int step = gridDim.x * 8;
+    const int r0 = (blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) * 2;
+    float wr[CPL][VN], br[CPL][VN];
+#pragma unroll
+    for (int i = 0; i < CPL; i++) {
+        const int ch = l32 + i * 32;
+#pragma unroll
+        for (int j = 0; j < VN; j += 4) {
+            const float4 u = *reinterpret_cast<const float4*>(w + ch * VN + j);
+            const float4 v = *reinterpret_cast<const float4*>(b + ch * VN + j);
+            wr[i][j] = u.x; wr[i][j + 1] = u.y; wr[i][j + 2] = u.z; wr[i][j + 3] = u.w;
+            br[i][j] = v.x; br[i][j + 1] = v.y; br[i][j + 2] = v.z; br[i][j + 3] = v.w;
+        }
+    }
+    Vec16<T> q[CPL], qn[CPL];
+    auto load = [&](Vec16<T>(&dst)[CPL], int row) {
+        if (row >= N) return;
+#pragma unroll
+        for (int i = 0; i < CPL; i++) dst[i] = ld16(x + (int64_t)row * C + (l32 + i * 32) * VN);
+    };
+    load(q, r0 + h);
+    // both halves run every pair (they share the row sums' lane reads)
+    for (int r = r0; r < N; r += step) {
+        const int row = r + h;
+        load(qn, row + step);
+        float s = 0.f;
+#pragma unroll
+        for (int i = 0; i < CPL; i++)
+#pragma unroll
+            for (int j = 0; j < VN; j++) s += to_f32(q[i].v[j]);
+        half_sums(s, h, s);
+        const float mu = s / C;
+        float ss = 0.f;
+#pragma unroll
+        for (int i = 0; i < CPL; i++)
+#pragma unroll
+            for (int j = 0; j < VN; j++) {
+                const float d = to_f32(q[i].v[j]) - mu;
+                ss += d * d;
+            }
+        half_sums(ss, h, ss);
+        const float rs = rsqrtf(ss / C + 1e-5f);
+        if (row < N) {
+            T* orow = out + (int64_t)row * C;
+#pragma unroll
+            for (int i = 0; i < CPL; i++) {
+                const int ch = l32 + i * 32;
+                Vec16<T> o;
+#pragma unroll
+                for (int j = 0; j < VN; j++) o.v[j] = from_f32<T>((to_f32(q[i].v[j]) - mu) * rs * wr[i][j] + br[i][j]);
+                st16(orow + ch * VN, o);
+            }
+            if (l32 == 0) {
+                mean[row] = mu;
+                rstd[row] = rs;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < CPL; i++) q[i] = qn[i];
+    }
+}
+
 #ifndef LN_FWD_ROWS_PER_WAVE
 #define LN_FWD_ROWS_PER_WAVE 4
 #endif
@@ -484,6 +569,8 @@ hipError_t layernorm_fwd(T* out, float* mean, float* rstd, const T* x, const flo
 #define LN_FWD_ROWS(V)                                                                                            \
     layernorm_fwd_rows_kernel<T, V><<<cdiv(N, 4 * LN_FWD_ROWS_PER_WAVE), 256, 0, s>>>(out, mean, rstd, x, w, b, N, C)
     if (per_lane <= 1) LN_FWD(1, 4);
+    else if (C / Vec16<T>::N == 96)  // C = 768 in bf16: a row per half-wave, 4 rows per wave
+        layernorm_fwd_half_kernel<T, 3><<<cdiv(N, 16), 256, 0, s>>>(out, mean, rstd, x, w, b, N, C);
     else if (per_lane <= 2) LN_FWD_ROWS(2);
     else if (per_lane <= 4) LN_FWD_ROWS(4);
     else LN_FWD(8, 1);
@@ -654,14 +741,6 @@ void layernorm_bwd_kernel(T* dout, const T* din, const T* dy, const T* x, const 
 // 16-lane rows r; the half h adds rows 2h and 2h + 1).  Channel sums as in the
 // whole-wave kernel, the two halves added (half 0 first), then the 4 waves:
 // partial[k][block][c], the same layout.
-DEVI void half_sums(float x, int h, float& s) {
-    x += dpp_mov<0xB1>(x);
-    x += dpp_mov<0x4E>(x);
-    x += dpp_mov<0x124>(x);
-    x += dpp_mov<0x128>(x);
-    const float s0 = lane_value(x, 0) + lane_value(x, 16), s1 = lane_value(x, 32) + lane_value(x, 48);
-    s = h ? s1 : s0;
-}
 
 template <typename T, int CPL, int NP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))

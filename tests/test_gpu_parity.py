@@ -545,18 +545,25 @@ def test_zero_grad_deferred_store_and_accumulation():
     assert not np.any(gs["wpe"][T * d["C"]:]) and not np.any(g2["wpe"][T * d["C"]:])
 
 
-def test_embedding_backward_repeated_tokens():
-    """Token-embedding gradient with heavy repetition: one id at every other
-    position and a few ids elsewhere, so the sorted runs span many of the
-    embedding backward's 32-slot chunks and several 1024-position blocks;
-    compared with the oracle (fp32 mode, 1e-4) and bit-identical run to run."""
+@pytest.mark.parametrize("pattern", ["repeated", "spread"])
+def test_embedding_backward_repeated_tokens(pattern):
+    """Token-embedding gradient with repetition.  repeated: one id at every
+    other position and a few ids elsewhere, so the sorted runs span many of
+    the embedding backward's 32-slot chunks and several 1024-position blocks.
+    spread: every id about 7 times, so most ids' sorted ranges lie inside one
+    chunk (added to the gradient by the chunk pass) and some straddle a chunk
+    boundary (added by the segment pass).  Compared with the oracle (fp32
+    mode, 1e-4) and bit-identical run to run."""
     d = dict(L=1, C=64, NH=4, maxT=512, V=300, Vp=320)
     B, T = 4, 512
     rng = np.random.default_rng(11)
-    x = rng.integers(0, 5, (B, T)).astype(np.int32)
-    x[:, ::2] = 7
+    if pattern == "repeated":
+        x = rng.integers(0, 5, (B, T)).astype(np.int32)
+        x[:, ::2] = 7
+    else:
+        x = ((np.arange(B * T) * 7) % d["V"]).astype(np.int32).reshape(B, T)
     y = rng.integers(0, d["V"], (B, T)).astype(np.int32)
-    print(f"embedding backward B={B} T={T} repeated ids", flush=True)
+    print(f"embedding backward B={B} T={T} {pattern} ids", flush=True)
     grads = []
     for _ in range(2):
         m = G.Model(gcfg(d, B, T, G.GPT2_FP32), 3, device="cuda:0")

@@ -203,21 +203,16 @@ __global__ __launch_bounds__(ENC_B) void enc_scatter_kernel(const int* tokens, i
 }
 
 // one block per ENC_S sorted slots, one thread per 4 channels; the slots'
-// rows are all requested before the runs are summed.  A run that is its id's
-// whole range (most ids: the range lies inside one chunk) goes straight into
-// dwte, as the segment pass would add it (dwte + the run's sum); the other
-// runs leave their partial row in Q for the segment pass.
+// rows are all requested before the runs are summed
 template <typename T>
-__global__ __launch_bounds__(1024) void enc_chunk_kernel(const T* dx, const int* perm, const int* sid, const int* tot,
-                                                         int BT, int C, int V, float* Q, float* dwte) {
+__global__ __launch_bounds__(1024) void enc_chunk_kernel(const T* dx, const int* perm, const int* sid, int BT, int C,
+                                                         float* Q) {
     __shared__ int sp[ENC_S], si[ENC_S];
-    __shared__ int s_prev;  // id of the slot before the chunk (-1 at the first chunk)
     const int k0 = blockIdx.x * ENC_S, n = min(BT - k0, ENC_S);
     if ((int)threadIdx.x < n) {
         sp[threadIdx.x] = perm[k0 + threadIdx.x];
         si[threadIdx.x] = sid[k0 + threadIdx.x];
     }
-    if (threadIdx.x == 0) s_prev = k0 > 0 ? sid[k0 - 1] : -1;
     __syncthreads();
     const int c = threadIdx.x * 4;
     if (c >= C) return;
@@ -240,24 +235,11 @@ __global__ __launch_bounds__(1024) void enc_chunk_kernel(const T* dx, const int*
     }
     float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
     int run = 0;
-    // the run [run, end) of id si[run]: into dwte if it is the id's whole
-    // range, else its partial row into Q
-    auto flush = [&](int end) {
-        const int id = si[run];
-        const bool first = run > 0 || s_prev != id;
-        if (first && id < V && end - run == tot[id]) {
-            float4* o = reinterpret_cast<float4*>(dwte + (int64_t)id * C + c);
-            const float4 cur = *o;
-            *o = make_float4(cur.x + a0, cur.y + a1, cur.z + a2, cur.w + a3);
-        } else {
-            *reinterpret_cast<float4*>(Q + (int64_t)(k0 + run) * C + c) = make_float4(a0, a1, a2, a3);
-        }
-    };
 #pragma unroll
     for (int k = 0; k < ENC_S; k++) {
         if (k >= n) break;
         if (k > 0 && si[k] != si[k - 1]) {
-            flush(k);
+            *reinterpret_cast<float4*>(Q + (int64_t)(k0 + run) * C + c) = make_float4(a0, a1, a2, a3);
             a0 = a1 = a2 = a3 = 0.f;
             run = k;
         }
@@ -266,11 +248,10 @@ __global__ __launch_bounds__(1024) void enc_chunk_kernel(const T* dx, const int*
         a2 += v[k][2];
         a3 += v[k][3];
     }
-    flush(n);
+    *reinterpret_cast<float4*>(Q + (int64_t)(k0 + run) * C + c) = make_float4(a0, a1, a2, a3);
 }
 
 // one wave per sorted slot; at an id's first slot, its pieces go into dwte
-// (ids whose range lies inside one chunk were added by the chunk pass)
 __global__ __launch_bounds__(256) void enc_segment_kernel(const int* sid, const int* tot, const float* Q, int BT,
                                                           int V, int C, float* dwte) {
     const int k = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -278,7 +259,6 @@ __global__ __launch_bounds__(256) void enc_segment_kernel(const int* sid, const 
     const int id = sid[k];
     if (id >= V || (k > 0 && sid[k - 1] == id)) return;
     const int end = k + tot[id];
-    if (end <= (k / ENC_S + 1) * ENC_S) return;
     for (int c = lane * 4; c < C; c += 256) {
         float4 a = *reinterpret_cast<const float4*>(Q + (int64_t)k * C + c);
         // the pieces in order, 8 requested at a time
@@ -340,7 +320,7 @@ hipError_t encoder_bwd(float* dwte, float* dwpe, const T* dx, const int* tokens,
     enc_group_kernel<<<NG, ENC_G, 0, s>>>(w.H, NB, V, w.tot, w.lbase, w.goff);
     enc_scatter_kernel<<<NB, ENC_B, 0, s>>>(tokens, BT, V, w.H, w.R, w.lbase, w.goff, NG, w.perm, w.sid);
     const int nt = (int)cdiv(C / 4, 64) * 64;
-    enc_chunk_kernel<T><<<(unsigned)cdiv(BT, ENC_S), nt, 0, s>>>(dx, w.perm, w.sid, w.tot, BT, C, V, w.Q, dwte);
+    enc_chunk_kernel<T><<<(unsigned)cdiv(BT, ENC_S), nt, 0, s>>>(dx, w.perm, w.sid, BT, C, w.Q);
     enc_segment_kernel<<<(unsigned)cdiv(BT, 4), 256, 0, s>>>(w.sid, w.tot, w.Q, BT, V, C, dwte);
     encoder_bwd_wpe_kernel<T><<<cdiv((int64_t)maxT * (C / Vec16<T>::N), 256), 256, 0, s>>>(dwpe, dx, B, T_, maxT, C,
                                                                                             overwrite);

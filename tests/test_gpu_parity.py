@@ -551,9 +551,9 @@ def test_embedding_backward_repeated_tokens(pattern):
     other position and a few ids elsewhere, so the sorted runs span many of
     the embedding backward's 32-slot chunks and several 1024-position blocks.
     spread: every id about 7 times, so most ids' sorted ranges lie inside one
-    chunk (added to the gradient by the chunk pass) and some straddle a chunk
-    boundary (added by the segment pass).  Compared with the oracle (fp32
-    mode, 1e-4) and bit-identical run to run."""
+    chunk (one partial row each) and some straddle a chunk boundary (two
+    partial rows, added in order).  Compared with the oracle (fp32 mode,
+    1e-4) and bit-identical run to run."""
     d = dict(L=1, C=64, NH=4, maxT=512, V=300, Vp=320)
     B, T = 4, 512
     rng = np.random.default_rng(11)

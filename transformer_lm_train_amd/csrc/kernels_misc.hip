@@ -581,7 +581,7 @@ hipError_t layernorm_fwd(T* out, float* mean, float* rstd, const T* x, const flo
 #define LN_FWD_ROWS(V)                                                                                            \
     layernorm_fwd_rows_kernel<T, V><<<cdiv(N, 4 * LN_FWD_ROWS_PER_WAVE), 256, 0, s>>>(out, mean, rstd, x, w, b, N, C)
     if (per_lane <= 1) LN_FWD(1, 4);
-    else if (C / Vec16<T>::N == 96)  // C = 768 in bf16: a row per half-wave, 4 rows per wave
+    else if (std::is_same<T, bf16>::value && C == 768)  // a row per half-wave, 4 rows per wave
         layernorm_fwd_half_kernel<T, 3><<<cdiv(N, 16), 256, 0, s>>>(out, mean, rstd, x, w, b, N, C);
     else if (per_lane <= 2) LN_FWD_ROWS(2);
     else if (per_lane <= 4) LN_FWD_ROWS(4);
@@ -1110,8 +1110,8 @@ hipError_t layernorm_bwd(T* dout, const T* din, const T* dy, const T* x, const f
     // requested first, measured ~5% faster than two (more waves per SIMD or a
     // larger grid gain nothing and add partial rows)
     if (per_lane <= 1) LN_BWD(1, 2);
-    else if (C / Vec16<T>::N == 96) {
-        // C = 768 in bf16: rows per half-wave
+    else if (std::is_same<T, bf16>::value && C == 768) {
+        // rows per half-wave
         if (dsum) layernorm_bwd_half_kernel<T, 3, 3><<<G, 256, lds, s>>>(dout, din, dy, x, w, mean, rstd, partial, N, C);
         else layernorm_bwd_half_kernel<T, 3, 2><<<G, 256, lds, s>>>(dout, din, dy, x, w, mean, rstd, partial, N, C);
     } else if (per_lane <= 2) LN_BWD(2, 1);

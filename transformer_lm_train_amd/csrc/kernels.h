@@ -134,10 +134,10 @@ hipError_t layernorm_fwd(T* out, float* mean, float* rstd, const T* x, const flo
                          int N, int C, hipStream_t s);
 // dout = din + LN backward of dy (din NULL: dout = the LN backward alone;
 // din may equal dout).  Per-block partial sums go to partial[NP][G][C] with
-// G = layernorm_bwd_blocks(N) <= 512: dw, db and, if dsum (NP = 3), the
-// column sums of dout.  The caller adds them to their outputs with
-// sum_partials_batch ({dw, db, dsum-target}, partial, G, C).
-int layernorm_bwd_blocks(int N);
+// G = layernorm_bwd_blocks(N, C, T is bf16) <= 512: dw, db and, if dsum
+// (NP = 3), the column sums of dout.  The caller adds them to their outputs
+// with sum_partials_batch ({dw, db, dsum-target}, partial, G, C).
+int layernorm_bwd_blocks(int N, int C, bool bf16);
 template <typename T>
 hipError_t layernorm_bwd(T* dout, const T* din, const T* dy, const T* x, const float* w, const float* mean,
                          const float* rstd, float* partial, int N, int C, bool dsum, hipStream_t s);

@@ -606,7 +606,12 @@ hipError_t layernorm_fwd(T* out, float* mean, float* rstd, const T* x, const flo
 // ============================================================================
 constexpr int LN_BWD_G = 512;
 
-int layernorm_bwd_blocks(int N) { return (int)std::min<int64_t>(cdiv(N, 4), LN_BWD_G); }
+// bf16 rows of 768 (the half-wave kernel): blocks of 8 waves, so half as many
+// partial rows for the same waves (the partial sums read them back from HBM)
+int layernorm_bwd_blocks(int N, int C, bool bf16) {
+    if (bf16 && C == 768) return (int)std::min<int64_t>(cdiv(N, 16), LN_BWD_G / 2);
+    return (int)std::min<int64_t>(cdiv(N, 4), LN_BWD_G);
+}
 
 // Register budget: two waves per SIMD (256 VGPRs) up to 2 chunks per lane;
 // wider rows (C > 1024 in bf16) hold 4 or 8 chunks of three operands plus
@@ -751,19 +756,20 @@ void layernorm_bwd_kernel(T* dout, const T* din, const T* dy, const T* x, const 
 // requested first), with the same per-row arithmetic.  The halves' row sums
 // come out of one pass of row-wise DPP adds (lanes 16r hold the sums of the
 // 16-lane rows r; the half h adds rows 2h and 2h + 1).  Channel sums as in the
-// whole-wave kernel, the two halves added (half 0 first), then the 4 waves:
-// partial[k][block][c], the same layout.
+// whole-wave kernel, the two halves added (half 0 first), then the block's 8
+// waves: partial[k][block][c], the same layout.
+constexpr int LN_HALF_NW = 8;  // waves per block
 
 template <typename T, int CPL, int NP>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(LN_HALF_NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void layernorm_bwd_half_kernel(T* dout, const T* din, const T* dy, const T* x, const float* w, const float* mean,
                                const float* rstd, float* partial, int N, int C) {
     constexpr int VN = Vec16<T>::N;
-    extern __shared__ float smem[];  // [4][NP][C]
+    extern __shared__ float smem[];  // [LN_HALF_NW][NP][C]
     const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform
     const int h = lane >> 5, l32 = lane & 31;
-    const int step = gridDim.x * 8;                  // rows between a wave's consecutive pairs
-    const int row0 = (blockIdx.x * 4 + wv) * 2 + h;  // this half's first row
+    const int step = gridDim.x * LN_HALF_NW * 2;               // rows between a wave's consecutive pairs
+    const int row0 = (blockIdx.x * LN_HALF_NW + wv) * 2 + h;  // this half's first row
     float acc[NP][CPL][VN];
     float wr[CPL][VN];
 #pragma unroll
@@ -838,7 +844,7 @@ void layernorm_bwd_half_kernel(T* dout, const T* din, const T* dy, const T* x, c
             st16(orow + ch * VN, o);
         }
     }
-    // the halves' channel sums (half 0 first), then the block's 4 waves
+    // the halves' channel sums (half 0 first), then the block's waves
 #pragma unroll
     for (int k = 0; k < NP; k++)
 #pragma unroll
@@ -859,11 +865,11 @@ void layernorm_bwd_half_kernel(T* dout, const T* din, const T* dy, const T* x, c
         }
     }
     __syncthreads();
-    for (int c = threadIdx.x; c < C; c += 256) {
+    for (int c = threadIdx.x; c < C; c += LN_HALF_NW * 64) {
 #pragma unroll
         for (int k = 0; k < NP; k++) {
             float t = 0.f;
-            for (int q = 0; q < 4; q++) t += smem[(q * NP + k) * C + c];
+            for (int q = 0; q < LN_HALF_NW; q++) t += smem[(q * NP + k) * C + c];
             partial[((int64_t)k * gridDim.x + blockIdx.x) * C + c] = t;
         }
     }
@@ -1099,7 +1105,7 @@ template <typename T>
 hipError_t layernorm_bwd(T* dout, const T* din, const T* dy, const T* x, const float* w, const float* mean,
                          const float* rstd, float* partial, int N, int C, bool dsum, hipStream_t s) {
     if (C % Vec16<T>::N || C / Vec16<T>::N > LN_MAXV * 64 || N <= 0) return hipErrorInvalidValue;
-    const int G = layernorm_bwd_blocks(N);
+    const int G = layernorm_bwd_blocks(N, C, std::is_same<T, bf16>::value);
     const int NP = dsum ? 3 : 2;
     const size_t lds = sizeof(float) * 4 * NP * C;
     const int per_lane = (int)cdiv(C / Vec16<T>::N, 64);
@@ -1112,8 +1118,11 @@ hipError_t layernorm_bwd(T* dout, const T* din, const T* dy, const T* x, const f
     if (per_lane <= 1) LN_BWD(1, 2);
     else if (std::is_same<T, bf16>::value && C == 768) {
         // rows per half-wave
-        if (dsum) layernorm_bwd_half_kernel<T, 3, 3><<<G, 256, lds, s>>>(dout, din, dy, x, w, mean, rstd, partial, N, C);
-        else layernorm_bwd_half_kernel<T, 3, 2><<<G, 256, lds, s>>>(dout, din, dy, x, w, mean, rstd, partial, N, C);
+        const size_t ldsh = sizeof(float) * LN_HALF_NW * NP * C;
+        if (dsum)
+            layernorm_bwd_half_kernel<T, 3, 3><<<G, LN_HALF_NW * 64, ldsh, s>>>(dout, din, dy, x, w, mean, rstd, partial, N, C);
+        else
+            layernorm_bwd_half_kernel<T, 3, 2><<<G, LN_HALF_NW * 64, ldsh, s>>>(dout, din, dy, x, w, mean, rstd, partial, N, C);
     } else if (per_lane <= 2) LN_BWD(2, 1);
     else if (per_lane <= 4 && (C / Vec16<T>::N + 1) / 2 <= 128) {
         // rows split over two waves (C = 1600 in bf16, 8192 rows: 37.8 -> 25.5 us per

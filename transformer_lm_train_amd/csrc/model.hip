@@ -205,7 +205,7 @@ Layout make_layout(const gpt2_config& c) {
         // rows per 256 tokens, 4C wide, or the stand-alone column sums' 256
         // rows in fp32 mode) and the qkv bias (attention's row per
         // 128-token block, 3C wide, or the stand-alone column sums).
-        const size_t ln = 3 * (size_t)layernorm_bwd_blocks((int)BT) * C;
+        const size_t ln = 3 * (size_t)layernorm_bwd_blocks((int)BT, (int)C, is_bf16(c.precision)) * C;
         const size_t fc = std::max<size_t>(cdiv(BT, 256) * 4, 256) * 4 * C;
         const size_t qk = std::max<size_t>((size_t)c.batch_size * cdiv(c.seq_len, 128), 256) * 3 * C;
         L.part_fin = add(4 * ln);
@@ -631,7 +631,7 @@ template <typename T> int backward_impl(gpt2_t* M) {
     float* pfc_all = M->P<float>(M->L.part_fc);
     float* pqkv_all = M->P<float>(M->L.part_qkv);
     float* attD = M->P<float>(M->L.attD);
-    const int Gln = layernorm_bwd_blocks(BT);
+    const int Gln = layernorm_bwd_blocks(BT, C, M->bf16mode());
     // output gradients kept for the weight-gradient products
     auto G3 = [&](int l) { return a.gres3 + (size_t)(l + 1) * BTC; };  // d res3 of block l (l = -1: d encoded)
     auto G2 = [&](int l) { return a.gres2 + (size_t)l * BTC; };        // d res2

@@ -118,10 +118,13 @@ int gpt2_build(const gpt2_config* cfg, uint64_t seed, void* device_buf, size_t b
 int gpt2_forward(gpt2_t* m, const int32_t* tokens, const int32_t* targets, float* mean_loss);
 
 /* As gpt2_forward, but tokens and targets are device int32 arrays already
- * resident on the GPU (targets may be NULL).  Ids are checked on the device:
- * an id outside [0,V) is replaced by 0 and flagged, and the next call that
- * reads a value back (mean_loss here, or gpt2_read_loss) reports
- * GPT2_EINVAL. */
+ * resident on the GPU (targets may be NULL).  They are read in stream order
+ * by the forward's first kernel, which copies them into the model (the
+ * caller keeps them unchanged until the stream has reached that point, as for
+ * an asynchronous copy; the model keeps no reference after it).  Ids are
+ * checked on the device: an id outside [0,V) is replaced by 0 in the model's
+ * copy and flagged, and the next call that reads a value back (mean_loss
+ * here, or gpt2_read_loss) reports GPT2_EINVAL. */
 int gpt2_forward_device(gpt2_t* m, const int32_t* d_tokens, const int32_t* d_targets,
                         float* mean_loss);
 

@@ -117,11 +117,12 @@ hipError_t gemm_mfma_bf16(const GemmArgs& g, hipStream_t s);
 // ---- element-wise and row kernels ------------------------------------------
 // W: the type of the wte / wpe tables (fp32 masters, or the bf16 parameters
 // of the stochastic-rounding mode)
-// Ids outside [0, V) (tokens, and targets when not NULL) are replaced by 0
-// in place and flagged in err_flag (1: a token, 2: a target).
+// The ids are read from tok_src (and tgt_src, when targets is not NULL) and
+// copied into tokens (targets), ids outside [0, V) replaced by 0 and flagged
+// in err_flag (1: a token, 2: a target); the sources may be those arrays.
 template <typename T, typename W>
-hipError_t encoder_fwd(T* out, int* tokens, int* targets, const W* wte, const W* wpe, int B, int T_,
-                       int C, int V, int* err_flag, hipStream_t s);
+hipError_t encoder_fwd(T* out, int* tokens, int* targets, const int* tok_src, const int* tgt_src, const W* wte,
+                       const W* wpe, int B, int T_, int C, int V, int* err_flag, hipStream_t s);
 // dwte[tokens[i]] += dx[i] for every position (sorted by token and summed in
 // position order: deterministic), dwpe[t] (+)= sum_b dx[b][t] (overwrite:
 // =, all maxT positions).  ws: encoder_bwd_ws_bytes(B*T, V, C) bytes.

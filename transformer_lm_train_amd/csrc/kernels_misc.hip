@@ -14,8 +14,8 @@
 // encoder_forward, token + position embedding)
 // ============================================================================
 template <typename T, typename W>
-__global__ void encoder_fwd_kernel(T* out, int* tokens, int* targets, const W* wte, const W* wpe, int T_,
-                                   int C, int V, int BT, int* err) {
+__global__ void encoder_fwd_kernel(T* out, int* tokens, int* targets, const int* tok_src, const int* tgt_src,
+                                   const W* wte, const W* wpe, int T_, int C, int V, int BT, int* err) {
     constexpr int VN = Vec16<T>::N;
     int chunks = C / VN;
     int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -23,23 +23,23 @@ __global__ void encoder_fwd_kernel(T* out, int* tokens, int* targets, const W* w
     int row = (int)(i / chunks), ch = (int)(i % chunks);
     int t = row % T_;
     if (targets && ch == 0) {
-        // targets (when given) are checked here as well, before any reader
-        const int y = targets[row];
-        if (y < 0 || y >= V) {
-            atomicOr(err, 2);
-            targets[row] = 0;
-        }
+        // targets (when given) are checked here as well, before any reader,
+        // and copied into the model's own array
+        const int y = tgt_src[row];
+        const bool ok = y >= 0 && y < V;
+        if (!ok) atomicOr(err, 2);
+        targets[row] = ok ? y : 0;
     }
-    int tok = tokens[row];
+    int tok = tok_src[row];
     if (tok < 0 || tok >= V) {
-        // flag it and replace it by 0 in the model's own token copy, so the
+        // flagged, and 0 in the model's own token copy, so that the
         // backward's scatter into dwte stays in bounds
-        if (ch == 0) {
-            atomicOr(err, 1);
-            tokens[row] = 0;
-        }
+        if (ch == 0) atomicOr(err, 1);
         tok = 0;
     }
+    // (tok_src may be the model's array itself: the other lanes of the row
+    // then read either the original id or the 0 that replaces an invalid one)
+    if (ch == 0) tokens[row] = tok;
     const W* we = wte + (int64_t)tok * C + ch * VN;
     const W* pe = wpe + (int64_t)t * C + ch * VN;
     Vec16<T> o;
@@ -63,11 +63,13 @@ __global__ void encoder_fwd_kernel(T* out, int* tokens, int* targets, const W* w
 }
 
 template <typename T, typename W>
-hipError_t encoder_fwd(T* out, int* tokens, int* targets, const W* wte, const W* wpe, int B, int T_, int C,
-                       int V, int* err, hipStream_t s) {
+hipError_t encoder_fwd(T* out, int* tokens, int* targets, const int* tok_src, const int* tgt_src, const W* wte,
+                       const W* wpe, int B, int T_, int C, int V, int* err, hipStream_t s) {
+    if (!tok_src || (targets && !tgt_src)) return hipErrorInvalidValue;
     int BT = B * T_;
     int64_t n = (int64_t)BT * (C / Vec16<T>::N);
-    encoder_fwd_kernel<T, W><<<cdiv(n, 256), 256, 0, s>>>(out, tokens, targets, wte, wpe, T_, C, V, BT, err);
+    encoder_fwd_kernel<T, W><<<cdiv(n, 256), 256, 0, s>>>(out, tokens, targets, tok_src, tgt_src, wte, wpe, T_, C, V,
+                                                          BT, err);
     return LAUNCH_CHECK();
 }
 
@@ -1655,8 +1657,8 @@ template <typename T> hipError_t widen_f32(float* dst, const T* src, size_t n, h
 
 // ---- explicit instantiations ------------------------------------------------
 #define INST(T)                                                                                              \
-    template hipError_t encoder_fwd<T, float>(T*, int*, int*, const float*, const float*, int, int, int, int,  \
-                                              int*, hipStream_t);                                            \
+    template hipError_t encoder_fwd<T, float>(T*, int*, int*, const int*, const int*, const float*, const float*,  \
+                                              int, int, int, int, int*, hipStream_t);                            \
     template hipError_t encoder_bwd<T>(float*, float*, const T*, const int*, int, int, int, int, int, void*,  \
                                         bool, hipStream_t);                                                  \
     template hipError_t layernorm_fwd<T>(T*, float*, float*, const T*, const float*, const float*, int, int, \
@@ -1668,5 +1670,5 @@ template <typename T> hipError_t widen_f32(float* dst, const T* src, size_t n, h
     template hipError_t widen_f32<T>(float*, const T*, size_t, hipStream_t);
 INST(float)
 INST(bf16)
-template hipError_t encoder_fwd<bf16, bf16>(bf16*, int*, int*, const bf16*, const bf16*, int, int, int, int, int*,
-                                            hipStream_t);
+template hipError_t encoder_fwd<bf16, bf16>(bf16*, int*, int*, const int*, const int*, const bf16*, const bf16*, int,
+                                            int, int, int, int*, hipStream_t);

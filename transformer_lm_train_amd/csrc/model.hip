@@ -346,6 +346,8 @@ struct gpt2_model {
     float* h_scalars;    // pinned readback
     hipEvent_t staged;   // last H2D from the staging buffer
     bool have_targets = false;
+    const int32_t* src_tokens = nullptr;   // ids of the forward being queued, when the caller's
+    const int32_t* src_targets = nullptr;  // device arrays (else the model's own arrays)
     bool logits_valid = false;
     bool norm_bad = false;
     bool clip_pending = false;  // gpt2_clip_grad_norm ran since the last update
@@ -530,15 +532,22 @@ template <typename T> int forward_impl(gpt2_t* M, bool with_targets) {
     int* err = M->P<int>(M->L.err);
     int* tok = M->P<int>(M->L.tokens);
     int* tgt = with_targets ? M->P<int>(M->L.targets) : nullptr;
+    // the ids come from the caller's device arrays (gpt2_forward_device) or
+    // from the model's own, filled from the host (gpt2_forward)
+    const int* tsrc = M->src_tokens ? M->src_tokens : tok;
+    const int* ysrc = M->src_targets ? M->src_targets : tgt;
 
     if constexpr (std::is_same<T, bf16>::value) {
         if (M->srmode()) {  // the bf16 tables are the parameters
-            RUN("encoder_fwd", encoder_fwd<T>(a.encoded, tok, tgt, w + po[P_WTE], w + po[P_WPE], B, T_, C, V, err, s));
+            RUN("encoder_fwd", encoder_fwd<T>(a.encoded, tok, tgt, tsrc, ysrc, w + po[P_WTE], w + po[P_WPE], B, T_, C, V,
+                                              err, s));
         } else {
-            RUN("encoder_fwd", encoder_fwd<T>(a.encoded, tok, tgt, p + pf[P_WTE], p + pf[P_WPE], B, T_, C, V, err, s));
+            RUN("encoder_fwd", encoder_fwd<T>(a.encoded, tok, tgt, tsrc, ysrc, p + pf[P_WTE], p + pf[P_WPE], B, T_, C, V,
+                                              err, s));
         }
     } else {
-        RUN("encoder_fwd", encoder_fwd<T>(a.encoded, tok, tgt, p + pf[P_WTE], p + pf[P_WPE], B, T_, C, V, err, s));
+        RUN("encoder_fwd", encoder_fwd<T>(a.encoded, tok, tgt, tsrc, ysrc, p + pf[P_WTE], p + pf[P_WPE], B, T_, C, V,
+                                              err, s));
     }
     const T* x = a.encoded;
     for (int l = 0; l < Ly; l++) {
@@ -951,11 +960,12 @@ int gpt2_forward(gpt2_t* M, const int32_t* tokens, const int32_t* targets, float
 
 int gpt2_forward_device(gpt2_t* M, const int32_t* d_tokens, const int32_t* d_targets, float* mean_loss) {
     if (!M || !d_tokens) return fail(GPT2_EINVAL, "NULL model or tokens");
-    size_t BT = (size_t)M->cfg.batch_size * M->cfg.seq_len;
-    HIPCHK(hipMemcpyAsync(M->P<int>(M->L.tokens), d_tokens, 4 * BT, hipMemcpyDeviceToDevice, M->stream));
-    if (d_targets)
-        HIPCHK(hipMemcpyAsync(M->P<int>(M->L.targets), d_targets, 4 * BT, hipMemcpyDeviceToDevice, M->stream));
-    return forward_common(M, d_targets != nullptr, mean_loss);
+    // the embedding kernel reads the caller's arrays and writes the model's copies
+    M->src_tokens = d_tokens;
+    M->src_targets = d_targets;
+    const int rc = forward_common(M, d_targets != nullptr, mean_loss);
+    M->src_tokens = M->src_targets = nullptr;
+    return rc;
 }
 
 int gpt2_read_loss(gpt2_t* M, float* mean_loss) {

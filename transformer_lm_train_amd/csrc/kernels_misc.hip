@@ -261,25 +261,48 @@ __global__ __launch_bounds__(256) void enc_segment_kernel(const int* sid, const 
     const int id = sid[k];
     if (id >= V || (k > 0 && sid[k - 1] == id)) return;
     const int end = k + tot[id];
-    for (int c = lane * 4; c < C; c += 256) {
-        float4 a = *reinterpret_cast<const float4*>(Q + (int64_t)k * C + c);
-        // the pieces in order, 8 requested at a time
-        constexpr int U = 8;
-        for (int m0 = (k / ENC_S + 1) * ENC_S; m0 < end; m0 += U * ENC_S) {
-            float4 q[U];
+    // up to 4 float4 columns per lane at a time (C <= 1024 in one pass): the
+    // first piece and the current gradient rows are requested together
+    constexpr int NCH = 4;
+    for (int c0 = lane * 4; c0 < C; c0 += 256 * NCH) {
+        float4 a[NCH], cur[NCH];
 #pragma unroll
-            for (int u = 0; u < U; u++) {
-                const int m = m0 + u * ENC_S;
-                q[u] = m < end ? *reinterpret_cast<const float4*>(Q + (int64_t)m * C + c)
-                               : make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int j = 0; j < NCH; j++) {
+            const int c = c0 + j * 256;
+            if (c < C) {
+                a[j] = *reinterpret_cast<const float4*>(Q + (int64_t)k * C + c);
+                cur[j] = *reinterpret_cast<const float4*>(dwte + (int64_t)id * C + c);
             }
+        }
+        // the further pieces in order (ids whose range crosses a chunk), U at
+        // a time
+        constexpr int U = 4;
+        for (int m0 = (k / ENC_S + 1) * ENC_S; m0 < end; m0 += U * ENC_S) {
+            float4 q[U][NCH];
 #pragma unroll
             for (int u = 0; u < U; u++)
-                if (m0 + u * ENC_S < end) { a.x += q[u].x; a.y += q[u].y; a.z += q[u].z; a.w += q[u].w; }
+#pragma unroll
+                for (int j = 0; j < NCH; j++) {
+                    const int m = m0 + u * ENC_S, c = c0 + j * 256;
+                    q[u][j] = m < end && c < C ? *reinterpret_cast<const float4*>(Q + (int64_t)m * C + c)
+                                               : make_float4(0.f, 0.f, 0.f, 0.f);
+                }
+#pragma unroll
+            for (int u = 0; u < U; u++)
+                if (m0 + u * ENC_S < end) {
+#pragma unroll
+                    for (int j = 0; j < NCH; j++) {
+                        a[j].x += q[u][j].x; a[j].y += q[u][j].y; a[j].z += q[u][j].z; a[j].w += q[u][j].w;
+                    }
+                }
         }
-        float4* o = reinterpret_cast<float4*>(dwte + (int64_t)id * C + c);
-        const float4 cur = *o;
-        *o = make_float4(cur.x + a.x, cur.y + a.y, cur.z + a.z, cur.w + a.w);
+#pragma unroll
+        for (int j = 0; j < NCH; j++) {
+            const int c = c0 + j * 256;
+            if (c < C)
+                *reinterpret_cast<float4*>(dwte + (int64_t)id * C + c) =
+                    make_float4(cur[j].x + a[j].x, cur[j].y + a[j].y, cur[j].z + a[j].z, cur[j].w + a[j].w);
+        }
     }
 }
 

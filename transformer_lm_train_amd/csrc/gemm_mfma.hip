@@ -40,6 +40,9 @@ constexpr int KALIGN = 64;  // K, and every split-K chunk, is a multiple of this
 #ifndef GEMM_GROUP_XPF
 #define GEMM_GROUP_XPF false
 #endif
+#ifndef GEMM_PERS_GELU
+#define GEMM_PERS_GELU 1
+#endif
 #ifndef GEMM_SPLIT_NS
 #define GEMM_SPLIT_NS 5
 #endif
@@ -65,9 +68,32 @@ constexpr int EPI_PARTIAL = 100;  // split-K partial tile into g.ws[split][M][N]
 // program order, so the region needs no synchronisation between the blocks.
 template <int RH, int TN> constexpr int red_bytes() { return RH * (TN + 4) * 4; }
 
-template <int EPI, int RH, int FM, int FN>
+// Bias values of the 8 columns each lane finishes, per column group: the
+// epilogue's layout (lane % LPR covers 8 columns of each CG-wide group).
+template <int EPI, int FN>
+DEVI void epilogue_bias(const GemmArgs& g, float* b8, int ncol0, int lane) {
+    constexpr int TN = FN * 32;
+    constexpr int CG = TN % 64 == 0 ? 64 : 32;
+    constexpr int NCG = TN / CG, LPR = CG / 8;
+    constexpr bool BIAS = EPI == EPI_BIAS || EPI == EPI_BIAS_RESID || EPI == EPI_BIAS_GELU || EPI == EPI_BIAS_GELU_D;
+#pragma unroll
+    for (int cg = 0; cg < NCG; cg++) {
+        const int n = ncol0 + cg * CG + (lane % LPR) * 8;
+#pragma unroll
+        for (int e = 0; e < 8; e++) b8[cg * 8 + e] = 0.f;
+        if (BIAS && g.bias && n < g.N) {
+            const float4 u = *reinterpret_cast<const float4*>(g.bias + n);
+            const float4 v = *reinterpret_cast<const float4*>(g.bias + n + 4);
+            b8[cg * 8 + 0] = u.x; b8[cg * 8 + 1] = u.y; b8[cg * 8 + 2] = u.z; b8[cg * 8 + 3] = u.w;
+            b8[cg * 8 + 4] = v.x; b8[cg * 8 + 5] = v.y; b8[cg * 8 + 6] = v.z; b8[cg * 8 + 7] = v.w;
+        }
+    }
+}
+
+// PRE: the bias values were loaded beforehand (epilogue_bias) into bpre.
+template <int EPI, int RH, int FM, int FN, bool PRE = false>
 DEVI void epilogue_rows(const GemmArgs& g, const f32x16 (&acc)[FM][FN], float* red, int mrow0, int ncol0, int split,
-                        int prow, int lane) {
+                        int prow, int lane, const float* bpre = nullptr) {
     constexpr int TN = FN * 32, P = TN + 4;
     constexpr int CG = TN % 64 == 0 ? 64 : 32;  // columns read back per group
     constexpr int NCG = TN / CG;
@@ -85,17 +111,13 @@ DEVI void epilogue_rows(const GemmArgs& g, const f32x16 (&acc)[FM][FN], float* r
 #pragma unroll
         for (int e = 0; e < 8; e++) cs[cg][e] = 0.f;
     float b8[NCG][8];
+    if constexpr (PRE) {
 #pragma unroll
-    for (int cg = 0; cg < NCG; cg++) {
-        const int n = ncol0 + cg * CG + (lane % LPR) * 8;
+        for (int cg = 0; cg < NCG; cg++)
 #pragma unroll
-        for (int e = 0; e < 8; e++) b8[cg][e] = 0.f;
-        if (BIAS && g.bias && n < g.N) {
-            const float4 u = *reinterpret_cast<const float4*>(g.bias + n);
-            const float4 v = *reinterpret_cast<const float4*>(g.bias + n + 4);
-            b8[cg][0] = u.x; b8[cg][1] = u.y; b8[cg][2] = u.z; b8[cg][3] = u.w;
-            b8[cg][4] = v.x; b8[cg][5] = v.y; b8[cg][6] = v.z; b8[cg][7] = v.w;
-        }
+            for (int e = 0; e < 8; e++) b8[cg][e] = bpre[cg * 8 + e];
+    } else {
+        epilogue_bias<EPI, FN>(g, &b8[0][0], ncol0, lane);
     }
 #pragma unroll
     for (int pass = 0; pass < FM * (32 / RH); pass++) {
@@ -725,7 +747,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
     constexpr int RH = red_bytes<32, TN>() <= RBYTES ? 32 : 16;
     static_assert(NW <= 8 && NW <= 2 * NS * (NS == 2 ? 2 : 1) && red_bytes<RH, TN>() <= RBYTES,
                   "epilogue regions must fit the stage buffers");
-    auto epilogue = [&](int m0, int n0) {
+    // persistent: the bias goes to registers before the next tile's loads,
+    // behind which it would otherwise wait (loads complete in order)
+    constexpr bool PREB = PERS && (EPI == EPI_BIAS || EPI == EPI_BIAS_RESID || EPI == EPI_BIAS_GELU ||
+                                   EPI == EPI_BIAS_GELU_D);
+    constexpr int ENCG = TN % 64 == 0 ? TN / 64 : TN / 32;
+    auto epilogue = [&](int m0, int n0, const float* bpre) {
         __syncthreads();
         uint16_t* region;
         if constexpr (NS == 2) {
@@ -751,8 +778,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
             h.acc_overwrite = true;
             epilogue_rows<EPI, RH>(h, acc, reinterpret_cast<float*>(region), wm * TM, wn * TN, 0, 0, lane);
         } else {
-            epilogue_rows<EPI, RH>(g, acc, reinterpret_cast<float*>(region), m0 + wm * TM, n0 + wn * TN, split,
-                                   (m0 / BM) * WAVES_M + wm, lane);
+            epilogue_rows<EPI, RH, FM, FN, PREB>(g, acc, reinterpret_cast<float*>(region), m0 + wm * TM,
+                                                 n0 + wn * TN, split, (m0 / BM) * WAVES_M + wm, lane, bpre);
         }
     };
 
@@ -830,6 +857,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
                 if (kt + 1 < nk) rstep(sa1, sb1, sa0, sb0, kt + 1);
             }
             const int cm0 = m0, cn0 = n0;
+            float bpre[8 * ENCG];
+            if constexpr (PREB) epilogue_bias<EPI, FN>(g, bpre, cn0 + wn * TN, lane);
             if (PERS && it + 1 < p_count) {
                 tile_of(p_first + (it + 1) * p_stride, m0, n0);
                 ra.init(A, g.lda, m0, g.M, wave, lane);
@@ -837,7 +866,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
                 ra.load(kbeg);
                 rb.load(kbeg);
             }
-            epilogue(cm0, cn0);
+            epilogue(cm0, cn0, bpre);
             if (PERS && it + 1 < p_count) __syncthreads();  // epilogue regions read before stage 0 is refilled
         }
         return;
@@ -849,7 +878,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC, OC
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());  // no load may still be writing LDS at exit
 
-    epilogue(m0, n0);
+    epilogue(m0, n0, nullptr);
 }
 
 // CUs of the current device (cached per device), rounded down to a multiple of 8.
@@ -1111,9 +1140,11 @@ hipError_t gemm_mfma_bf16(const GemmArgs& g, hipStream_t s) {
         // resources span each operand's rows, whose byte extent must fit the
         // 31-bit record count): persistent for a plain store over at least
         // two rounds of tiles (the classifier's logits: 49 rounds at B*T =
-        // 16384) and for the fused classifier's statistics (as many rounds),
-        // one tile per workgroup for the bias epilogues, whose operand loads
-        // would otherwise queue behind the next tile's.
+        // 16384), for the fused classifier's statistics (as many rounds) and
+        // for bias + GELU/GELU' over two rounds or more (the fc forward: 3
+        // rounds at 124M; its bias is read before the next tile's loads are
+        // requested, 104 -> 99.5 us per launch), one tile per workgroup for
+        // the other bias epilogues.
         const bool rl = !w192 && (int64_t)g.M * g.lda * 2 < ((int64_t)1 << 31) &&
                         (int64_t)g.N * g.ldb * 2 < ((int64_t)1 << 31);
         const int wgs = device_slots();
@@ -1130,6 +1161,8 @@ hipError_t gemm_mfma_bf16(const GemmArgs& g, hipStream_t s) {
                 return w192 ? BIG192(true, true, EPI_BIAS_GELU)
                             : rl ? RL256(EPI_BIAS_GELU) : BIG256(true, true, EPI_BIAS_GELU);
             case EPI_BIAS_GELU_D:
+                if (GEMM_PERS_GELU && rl && cdiv(g.M, 256) * cdiv(g.N, 256) >= 2 * wgs)
+                    return launch_pers<256, 256, 8, 2, EPI_BIAS_GELU_D>(g, s, wgs);
                 return w192 ? BIG192(true, true, EPI_BIAS_GELU_D)
                             : rl ? RL256(EPI_BIAS_GELU_D) : BIG256(true, true, EPI_BIAS_GELU_D);
             case EPI_MUL_AUX:

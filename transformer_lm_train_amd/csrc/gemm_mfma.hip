@@ -40,6 +40,9 @@ constexpr int KALIGN = 64;  // K, and every split-K chunk, is a multiple of this
 #ifndef GEMM_GROUP_XPF
 #define GEMM_GROUP_XPF false
 #endif
+#ifndef GEMM_PERS_BIAS
+#define GEMM_PERS_BIAS 1
+#endif
 #ifndef GEMM_PERS_GELU
 #define GEMM_PERS_GELU 1
 #endif
@@ -1141,10 +1144,11 @@ hipError_t gemm_mfma_bf16(const GemmArgs& g, hipStream_t s) {
         // 31-bit record count): persistent for a plain store over at least
         // two rounds of tiles (the classifier's logits: 49 rounds at B*T =
         // 16384), for the fused classifier's statistics (as many rounds) and
-        // for bias + GELU/GELU' over two rounds or more (the fc forward: 3
-        // rounds at 124M; its bias is read before the next tile's loads are
-        // requested, 104 -> 99.5 us per launch), one tile per workgroup for
-        // the other bias epilogues.
+        // for bias (+ GELU/GELU') over two rounds or more (the fc forward: 3
+        // rounds at 124M, 104 -> 99.5 us per launch; the qkv forward at the
+        // 350M width), whose bias is read before the next tile's loads are
+        // requested; one tile per workgroup for the residual epilogue (its
+        // persistent form spills).
         const bool rl = !w192 && (int64_t)g.M * g.lda * 2 < ((int64_t)1 << 31) &&
                         (int64_t)g.N * g.ldb * 2 < ((int64_t)1 << 31);
         const int wgs = device_slots();
@@ -1153,7 +1157,10 @@ hipError_t gemm_mfma_bf16(const GemmArgs& g, hipStream_t s) {
 #define RL256(E) launch_rl<256, 256, 8, 2, E>(g, s)
         switch (g.epi) {
             case EPI_STORE: return w192 ? BIG192(true, true, EPI_STORE) : BIG256(true, true, EPI_STORE);
-            case EPI_BIAS: return w192 ? BIG192(true, true, EPI_BIAS) : rl ? RL256(EPI_BIAS) : BIG256(true, true, EPI_BIAS);
+            case EPI_BIAS:
+                if (GEMM_PERS_BIAS && rl && cdiv(g.M, 256) * cdiv(g.N, 256) >= 2 * wgs)
+                    return launch_pers<256, 256, 8, 2, EPI_BIAS>(g, s, wgs);
+                return w192 ? BIG192(true, true, EPI_BIAS) : rl ? RL256(EPI_BIAS) : BIG256(true, true, EPI_BIAS);
             case EPI_BIAS_RESID:
                 return w192 ? BIG192(true, true, EPI_BIAS_RESID)
                             : rl ? RL256(EPI_BIAS_RESID) : BIG256(true, true, EPI_BIAS_RESID);

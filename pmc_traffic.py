@@ -313,8 +313,16 @@ def summary(run, out_md, config=RECORDED_CONFIG):
             continue
         name = r["Name"].replace("(anonymous namespace)::", "").split("(GemmArgs")[0]
         lines.append(f"| {ms:.3f} | {int(r['Calls']) / steps:.1f} | {float(r['AverageNs']) / 1e3:.1f} | `{name[:110]}` |")
+    # a header written by hand above the generated table (title, commands) is kept
+    head = []
+    if os.path.exists(out_md):
+        with open(out_md) as f:
+            for ln in f:
+                if ln.startswith("Trace run:"):
+                    break
+                head.append(ln)
     with open(out_md, "w") as f:
-        f.write("\n".join(lines) + "\n")
+        f.write("".join(head) + "\n".join(lines) + "\n")
     srcs = kernel_sources()
     data = {}
     for k, (fb, wb, n) in traffic.items():

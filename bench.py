@@ -46,12 +46,15 @@ def flops_per_token(c):
     return 3 * (L * (24 * C * C + 2 * C * (T + 1)) + 2 * C * V)
 
 
-def class_work(c, sr=False, fused=False):
+def class_work(c, sr=False, fused=False, recompute=False):
     """Algorithmic work per step of each timed kernel class: (amount, unit,
     launches per step).  With the fused classifier the logits are recomputed
     in the backward (a class of its own, counted at the classifier's FLOPs)
     in chunks of up to 4096 rows, each with its dX and dwte products, and the
-    loss pass only combines the per-row statistics."""
+    loss pass only combines the per-row statistics.  With the GELU recompute
+    each layer's GELU output is formed again in the backward (read the bf16
+    pre-activation, write the output) and the fcproj weight gradients run as
+    one launch per layer beside the grouped launch."""
     L, C, T, V, B, NH = c["L"], c["C"], c["T"], c["V"], c["B"], c["NH"]
     BT = B * T
     lin = L * 2 * BT * 12 * C * C
@@ -86,6 +89,10 @@ def class_work(c, sr=False, fused=False):
             "attention_bwd": (2 * att, "flop", L),
             "softmax_ce": (2 * BT * Vp * 2, "byte", 1),
         }
+    if recompute:
+        amount, unit, n = head["gemm_dw"]
+        head["gemm_dw"] = (amount, unit, n + L)
+        head["gelu_recompute"] = (L * BT * 4 * C * 2 * 2, "byte", L)
     return {
         **head,
         # fp32 master: read theta, g, m, v, write theta, m, v, bf16 copy; stochastic
@@ -163,6 +170,9 @@ def main():
     ap.add_argument("--fused-classifier", action="store_true",
                     help="classifier product fused with the softmax cross-entropy: no logits stored, the backward "
                          "recomputes them in chunks")
+    ap.add_argument("--recompute-gelu", action="store_true",
+                    help="keep only the pre-activation of the MLP and form its GELU again in the backward "
+                         "(less activation memory, one GELU pass per layer more)")
     ap.add_argument("--host-tokens", action="store_true",
                     help="tokens and targets handed over as host arrays (gpt2_forward: the PCIe copy inside the "
                          "step) instead of device arrays already in HBM")
@@ -182,7 +192,7 @@ def main():
     torch.cuda.set_device(0)
     prec = G.GPT2_BF16_SR if args.sr else G.GPT2_BF16_MIXED
     cfg = G.make_config(c["L"], c["C"], c["NH"], c["maxT"], c["V"], c["Vp"], c["B"], c["T"], prec,
-                        args.fused_classifier)
+                        args.fused_classifier, args.recompute_gelu)
     m = G.Model(cfg, args.seed, device="cuda:0")
     B, T = c["B"], c["T"]
     nb = args.warmup + args.steps + 16
@@ -216,7 +226,7 @@ def main():
         loss = step(i)
         print(f"warmup step {i} loss {loss:.4f}", flush=True)
 
-    work = class_work(c, args.sr, args.fused_classifier)
+    work = class_work(c, args.sr, args.fused_classifier, args.recompute_gelu)
     per_class = {}
     # choose the dominant kernel class: one untimed-region step per class
     if args.timing_class == "auto":
@@ -318,6 +328,7 @@ def main():
                                   "bf16 mixed (fp32 master/AdamW), ")
                                + ("classifier fused with the softmax cross-entropy (logits recomputed in the "
                                   "backward), " if args.fused_classifier else "")
+                               + ("GELU output recomputed in the backward, " if args.recompute_gelu else "")
                                + "Zipf(1.1) synthetic tokens"
                                + (", tokens copied from host memory inside the step" if args.host_tokens else ""),
                    "batch": B, "seq_len": T,

@@ -83,6 +83,15 @@ typedef struct {
                                   tour's fused classifier; "llm.c's Origin and the Future of LLM
                                   Compilers", "Avengers": recompute during the backward).  Uses
                                   less memory, adds one classifier product. */
+    int32_t recompute_gelu;    /* 0: the forward keeps every layer's GELU output (the fcproj input
+                                  its weight gradient reads) beside GELU'.  1 (bf16 modes only):
+                                  it keeps only the pre-activation, rounded to bf16, and one layer's
+                                  GELU output for the next product; the backward recomputes each
+                                  layer's GELU output from the kept pre-activation (the same values
+                                  the forward used) for that layer's fcproj weight gradient, and
+                                  GELU' in the fcproj backward-data product ("llm.c's Origin and
+                                  the Future of LLM Compilers", "Avengers": recompute settings).
+                                  Saves (L-1)*B*T*4C*2 bytes, costs one GELU pass per layer. */
 } gpt2_config;
 
 typedef struct gpt2_model gpt2_t;

@@ -39,10 +39,10 @@ def test_binding_covers_the_abi():
 
 def _cfg(**kw):
     base = dict(L=12, C=768, NH=12, maxT=1024, V=50257, Vp=50304, B=16, T=1024, precision=G.GPT2_BF16_MIXED,
-                fused=False)
+                fused=False, recompute=False)
     base.update(kw)
     return G.make_config(base["L"], base["C"], base["NH"], base["maxT"], base["V"], base["Vp"], base["B"],
-                         base["T"], base["precision"], base["fused"])
+                         base["T"], base["precision"], base["fused"], base["recompute"])
 
 
 def test_plan_sizes():
@@ -103,3 +103,18 @@ def test_plan_fused_classifier():
     with pytest.raises(G.GPT2Error) as e:
         G.gpt2_plan(_cfg(B=4, T=64, precision=G.GPT2_FP32, fused=True))
     assert e.value.code == G.GPT2_EINVAL and "bf16" in str(e.value)
+
+
+def test_plan_recompute_gelu():
+    # one layer's GELU output instead of L: (L - 1) * B*T * 4C bf16 values fewer
+    # (the grouped weight-gradient tile list loses the fcproj tiles, a few KB)
+    L, C, BT = 12, 768, 16 * 1024
+    saved = G.gpt2_plan(_cfg()) - G.gpt2_plan(_cfg(recompute=True))
+    expect = (L - 1) * BT * 4 * C * 2
+    assert expect <= saved <= expect + 65536
+    bad = _cfg()
+    bad.recompute_gelu = 2
+    for cfg, msg in ((_cfg(B=4, T=64, precision=G.GPT2_FP32, recompute=True), "bf16"), (bad, "recompute_gelu")):
+        with pytest.raises(G.GPT2Error) as e:
+            G.gpt2_plan(cfg)
+        assert e.value.code == G.GPT2_EINVAL and msg in str(e.value)

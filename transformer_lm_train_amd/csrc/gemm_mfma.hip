@@ -266,8 +266,10 @@ DEVI void epilogue_rows(const GemmArgs& g, const f32x16 (&acc)[FM][FN], float* r
                     for (int e = 0; e < 8; e++) cs[cg][e] += (float)out[e];
                 }
                 if constexpr (EPI == EPI_BIAS_GELU) {
+                    // GELU of the stored (bf16) pre-activation, which a backward
+                    // that recomputes this output starts from as well
 #pragma unroll
-                    for (int e = 0; e < 8; e++) out[e] = (bf16)gelu_f(y[e]);
+                    for (int e = 0; e < 8; e++) out[e] = (bf16)gelu_f((float)out[e]);
                     *reinterpret_cast<bf16x8_t*>((bf16*)g.out2 + o) = out;
                 }
             }
@@ -1165,6 +1167,8 @@ hipError_t gemm_mfma_bf16(const GemmArgs& g, hipStream_t s) {
                 return w192 ? BIG192(true, true, EPI_BIAS_RESID)
                             : rl ? RL256(EPI_BIAS_RESID) : BIG256(true, true, EPI_BIAS_RESID);
             case EPI_BIAS_GELU:
+                if (GEMM_PERS_GELU && rl && cdiv(g.M, 256) * cdiv(g.N, 256) >= 2 * wgs)
+                    return launch_pers<256, 256, 8, 2, EPI_BIAS_GELU>(g, s, wgs);
                 return w192 ? BIG192(true, true, EPI_BIAS_GELU)
                             : rl ? RL256(EPI_BIAS_GELU) : BIG256(true, true, EPI_BIAS_GELU);
             case EPI_BIAS_GELU_D:

@@ -14,7 +14,7 @@ enum GemmEpi {
     EPI_STORE = 0,       // out = acc
     EPI_BIAS = 1,        // out = acc + bias[n]
     EPI_BIAS_RESID = 2,  // out = resid[m][n] + acc + bias[n]
-    EPI_BIAS_GELU = 3,   // out = acc + bias[n] (pre-activation); out2 = GELU(that)
+    EPI_BIAS_GELU = 3,   // out = acc + bias[n] (pre-activation); out2 = GELU(that) (bf16: GELU of the stored out)
     EPI_GELU_BWD = 4,    // out = acc * GELU'(aux[m][n])
     EPI_ACC_F32 = 5,     // out (fp32) += acc
     // The classifier fused with the softmax cross-entropy (acc = logits z of
@@ -130,6 +130,9 @@ size_t encoder_bwd_ws_bytes(int BT, int V, int C);
 template <typename T>
 hipError_t encoder_bwd(float* dwte, float* dwpe, const T* dx, const int* tokens, int B, int T_, int maxT, int C,
                        int V, void* ws, bool overwrite, hipStream_t s);
+// out[i] = GELU(u[i]) for n bf16 values (the epilogue's GELU of the same
+// bf16 pre-activation, so the same results); n % 8 == 0, 16-byte aligned
+hipError_t gelu_recompute(bf16* out, const bf16* u, size_t n, hipStream_t s);
 template <typename T>
 hipError_t layernorm_fwd(T* out, float* mean, float* rstd, const T* x, const float* w, const float* b,
                          int N, int C, hipStream_t s);

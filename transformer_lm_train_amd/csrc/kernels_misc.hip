@@ -1660,6 +1660,28 @@ __global__ void cast_bf16_kernel(bf16* dst, const float* src, size_t n) {
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
         dst[i] = (bf16)src[i];
 }
+// GELU of the kept bf16 pre-activation, 8 values per thread and step; the
+// pre-activation is read once (non-temporal), the output is read next by
+// the weight-gradient product
+__global__ __launch_bounds__(256) void gelu_recompute_kernel(bf16* out, const bf16* u, size_t n8) {
+    typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8; i += (size_t)gridDim.x * blockDim.x) {
+        const bf16x8_t x = __builtin_nontemporal_load(reinterpret_cast<const bf16x8_t*>(u) + i);
+        bf16x8_t y;
+#pragma unroll
+        for (int e = 0; e < 8; e++) y[e] = (bf16)gelu_f((float)x[e]);
+        reinterpret_cast<bf16x8_t*>(out)[i] = y;
+    }
+}
+hipError_t gelu_recompute(bf16* out, const bf16* u, size_t n, hipStream_t s) {
+    if (n % 8 || (reinterpret_cast<uintptr_t>(out) | reinterpret_cast<uintptr_t>(u)) % 16) return hipErrorInvalidValue;
+    const size_t n8 = n / 8;
+    size_t blocks = cdiv(n8, 256);
+    if (blocks > 8192) blocks = 8192;
+    gelu_recompute_kernel<<<(unsigned)blocks, 256, 0, s>>>(out, u, n8);
+    return LAUNCH_CHECK();
+}
+
 hipError_t cast_bf16(bf16* dst, const float* src, size_t n, hipStream_t s) {
     size_t blocks = cdiv(n, 256);
     if (blocks > 8192) blocks = 8192;

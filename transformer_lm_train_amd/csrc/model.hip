@@ -120,6 +120,9 @@ int validate(const gpt2_config* c) {
     if (c->fused_classifier != 0 && c->fused_classifier != 1) return fail(GPT2_EINVAL, "fused_classifier must be 0 or 1");
     if (c->fused_classifier && !is_bf16(c->precision))
         return fail(GPT2_EINVAL, "the fused classifier needs a bf16 mode");
+    if (c->recompute_gelu != 0 && c->recompute_gelu != 1) return fail(GPT2_EINVAL, "recompute_gelu must be 0 or 1");
+    if (c->recompute_gelu && !is_bf16(c->precision))
+        return fail(GPT2_EINVAL, "recompute_gelu needs a bf16 mode");
     if (is_bf16(c->precision)) {
         if (hs != 64) return fail(GPT2_EINVAL, "the bf16 modes need head size 64");
         if (c->channels % 64 || c->padded_vocab_size % 64 || c->seq_len % 64)
@@ -165,7 +168,9 @@ Layout make_layout(const gpt2_config& c) {
     L.res2 = add(A * Ly * BT * C);
     L.ln2 = add(A * Ly * BT * C);
     L.fch = add(A * Ly * BT * 4 * C);
-    L.fchg = add(A * Ly * BT * 4 * C);
+    // GELU outputs: every layer's, or with recompute_gelu the one layer the
+    // next product (forward) or the fcproj weight gradient (backward) reads
+    L.fchg = add(A * (c.recompute_gelu ? 1 : Ly) * BT * 4 * C);
     L.res3 = add(A * Ly * BT * C);
     L.lnf = add(A * BT * C);
     if (c.fused_classifier) {
@@ -234,7 +239,9 @@ Layout make_layout(const gpt2_config& c) {
     // the token-sorted embedding backward: per-block counts, ranks, offsets,
     // the sorted positions and one fp32 partial row per sorted position
     L.encws = add(encoder_bwd_ws_bytes((int)BT, c.vocab_size, (int)C));
-    L.dw_n = 4 * c.num_layers + (c.fused_classifier ? 0 : 1);  // the fused classifier's runs in its chunks
+    // the fused classifier's run in its chunks; with recompute_gelu the fcproj
+    // products run in the block loop, each after its layer's GELU output is recomputed
+    L.dw_n = (c.recompute_gelu ? 3 : 4) * c.num_layers + (c.fused_classifier ? 0 : 1);
     L.dw_probs = add(sizeof(GemmArgs) * L.dw_n);
     L.dw_ntiles = 0;
     if (is_bf16(c.precision)) {
@@ -275,8 +282,9 @@ void dw_problems(const gpt2_config& c, const Layout& L, char* base, GemmArgs* ou
     if (!c.fused_classifier) out[n++] = prob(g + L.poff[P_WTE], act(L.logits, 0), act(L.lnf, 0), c.padded_vocab_size, C);
     for (int l = c.num_layers - 1; l >= 0; l--) {
         const size_t lC = (size_t)l * C;
-        out[n++] = prob(g + L.poff[P_FCPROJW] + lC * 4 * C, act(L.gres3, (l + 1) * BTC), act(L.fchg, l * BTC * 4), C,
-                        4 * C);
+        if (!c.recompute_gelu)
+            out[n++] = prob(g + L.poff[P_FCPROJW] + lC * 4 * C, act(L.gres3, (l + 1) * BTC), act(L.fchg, l * BTC * 4),
+                            C, 4 * C);
         out[n++] = prob(g + L.poff[P_FCW] + lC * 4 * C, act(L.gfch, l * BTC * 4), act(L.ln2, l * BTC), 4 * C, C);
         out[n++] = prob(g + L.poff[P_ATTPROJW] + lC * C, act(L.gres2, l * BTC), act(L.atty, l * BTC), C, C);
         out[n++] = prob(g + L.poff[P_QKVW] + lC * 3 * C, act(L.gqkv, l * BTC * 3), act(L.ln1, l * BTC), 3 * C, C);
@@ -557,7 +565,7 @@ template <typename T> int forward_impl(gpt2_t* M, bool with_targets) {
         T* res2 = a.res2 + l * BTC;
         T* ln2 = a.ln2 + l * BTC;
         T* fch = a.fch + l * BTC * 4;
-        T* fchg = a.fchg + l * BTC * 4;
+        T* fchg = a.fchg + (c.recompute_gelu ? 0 : l * BTC * 4);
         T* res3 = a.res3 + l * BTC;
         const size_t lC = (size_t)l * C;
         RUN("layernorm_fwd", layernorm_fwd<T>(ln1, a.ln1m + (size_t)l * BT, a.ln1r + (size_t)l * BT, x,
@@ -570,9 +578,10 @@ template <typename T> int forward_impl(gpt2_t* M, bool with_targets) {
         RUN("layernorm_fwd", layernorm_fwd<T>(ln2, a.ln2m + (size_t)l * BT, a.ln2r + (size_t)l * BT, res2,
                                               p + pf[P_LN2W] + lC, p + pf[P_LN2B] + lC, BT, C, s));
         // fch: the pre-activation (fp32), or in the bf16 modes GELU' of it, so
-        // that the backward's product only scales by it
+        // that the backward's product only scales by it; with recompute_gelu
+        // the bf16 pre-activation, whose GELU the backward forms again
         RUN("gemm_fwd", lin_fwd<T>(M, fch, ln2, w + po[P_FCW] + lC * 4 * C, p + pf[P_FCB] + lC * 4, BT, 4 * C, C,
-                                   kGeluFwdEpi<T>, nullptr, fchg));
+                                   c.recompute_gelu ? EPI_BIAS_GELU : kGeluFwdEpi<T>, nullptr, fchg));
         RUN("gemm_fwd", lin_fwd<T>(M, res3, fchg, w + po[P_FCPROJW] + lC * 4 * C, p + pf[P_FCPROJB] + lC, BT, C,
                                    4 * C, EPI_BIAS_RESID, res2));
         x = res3;
@@ -715,8 +724,24 @@ template <typename T> int backward_impl(gpt2_t* M) {
         float* pqkv = pqkv_all + l * M->L.part_stride_qkv;
         if (l == Ly - 1) jobs.push_back(SumJob{{g + po[P_LNFW], g + po[P_LNFB], g + po[P_FCPROJB] + lC}, pfin, Gln, C});
         // fcproj: res3 = res2 + fchg Wfp^T + b  ->  d fch = (d res3 Wfp) * GELU'(pre-activation)
-        RUN("gemm_dx", lin_dx<T>(M, GF(l), G3(l), w + po[P_FCPROJW] + lC * 4 * C, BT, C, 4 * C, kGeluBwdEpi<T>, fch,
-                                 fused ? pfc : nullptr));
+        RUN("gemm_dx", lin_dx<T>(M, GF(l), G3(l), w + po[P_FCPROJW] + lC * 4 * C, BT, C, 4 * C,
+                                 c.recompute_gelu ? EPI_GELU_BWD : kGeluBwdEpi<T>, fch, fused ? pfc : nullptr));
+        if constexpr (std::is_same<T, bf16>::value) {
+            if (c.recompute_gelu) {
+                // this layer's GELU output again, from the kept bf16 pre-activation
+                // (the values the forward's fcproj product read), then its weight gradient
+                RUN("gelu_recompute", gelu_recompute(a.fchg, fch, BTC * 4, s));
+                GemmArgs d{};
+                d.M = C; d.N = 4 * C; d.K = BT;
+                d.a = G3(l); d.lda = C; d.a_kcontig = false;
+                d.b = a.fchg; d.ldb = 4 * C; d.b_kcontig = false;
+                d.out = g + po[P_FCPROJW] + lC * 4 * C; d.ldo = 4 * C; d.epi = EPI_ACC_F32;
+                d.ws = M->P<float>(M->L.splitk);
+                d.ws_bytes = M->L.splitk_bytes;
+                d.acc_overwrite = ow;
+                RUN("gemm_dw", gemm<T>(M, d));
+            }
+        }
         if (fused) jobs.push_back(SumJob{{g + po[P_FCB] + lC * 4}, pfc, gemm_colsum_rows(BT, 4 * C), 4 * C});
         // fc: fch = ln2 Wfc^T + b  ->  d ln2
         RUN("gemm_dx", lin_dx<T>(M, a.dmid, GF(l), w + po[P_FCW] + lC * 4 * C, BT, 4 * C, C, EPI_STORE));

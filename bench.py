@@ -46,7 +46,7 @@ def flops_per_token(c):
     return 3 * (L * (24 * C * C + 2 * C * (T + 1)) + 2 * C * V)
 
 
-def class_work(c, sr=False, fused=False, recompute=False):
+def class_work(c, sr=False, fused=False, recompute=False, recompute_ln=False):
     """Algorithmic work per step of each timed kernel class: (amount, unit,
     launches per step).  With the fused classifier the logits are recomputed
     in the backward (a class of its own, counted at the classifier's FLOPs)
@@ -54,7 +54,9 @@ def class_work(c, sr=False, fused=False, recompute=False):
     loss pass only combines the per-row statistics.  With the GELU recompute
     each layer's GELU output is formed again in the backward (read the bf16
     pre-activation, write the output) and the fcproj weight gradients run as
-    one launch per layer beside the grouped launch."""
+    one launch per layer beside the grouped launch; with the LayerNorm
+    recompute each layer's two LayerNorm forwards run again (their bytes as in
+    the forward) and the qkv and fc weight gradients run per layer."""
     L, C, T, V, B, NH = c["L"], c["C"], c["T"], c["V"], c["B"], c["NH"]
     BT = B * T
     lin = L * 2 * BT * 12 * C * C
@@ -93,6 +95,10 @@ def class_work(c, sr=False, fused=False, recompute=False):
         amount, unit, n = head["gemm_dw"]
         head["gemm_dw"] = (amount, unit, n + L)
         head["gelu_recompute"] = (L * BT * 4 * C * 2 * 2, "byte", L)
+    if recompute_ln:
+        amount, unit, n = head["gemm_dw"]
+        head["gemm_dw"] = (amount, unit, n + 2 * L)
+        head["layernorm_recompute"] = (2 * L * (BT * C * 2 * 2 + 8 * BT), "byte", 2 * L)
     return {
         **head,
         # fp32 master: read theta, g, m, v, write theta, m, v, bf16 copy; stochastic
@@ -173,6 +179,9 @@ def main():
     ap.add_argument("--recompute-gelu", action="store_true",
                     help="keep only the pre-activation of the MLP and form its GELU again in the backward "
                          "(less activation memory, one GELU pass per layer more)")
+    ap.add_argument("--recompute-layernorm", action="store_true",
+                    help="keep one layer's LayerNorm outputs and run each layer's LayerNorm forwards again in "
+                         "the backward (less activation memory)")
     ap.add_argument("--host-tokens", action="store_true",
                     help="tokens and targets handed over as host arrays (gpt2_forward: the PCIe copy inside the "
                          "step) instead of device arrays already in HBM")
@@ -192,7 +201,7 @@ def main():
     torch.cuda.set_device(0)
     prec = G.GPT2_BF16_SR if args.sr else G.GPT2_BF16_MIXED
     cfg = G.make_config(c["L"], c["C"], c["NH"], c["maxT"], c["V"], c["Vp"], c["B"], c["T"], prec,
-                        args.fused_classifier, args.recompute_gelu)
+                        args.fused_classifier, args.recompute_gelu, args.recompute_layernorm)
     m = G.Model(cfg, args.seed, device="cuda:0")
     B, T = c["B"], c["T"]
     nb = args.warmup + args.steps + 16
@@ -226,7 +235,7 @@ def main():
         loss = step(i)
         print(f"warmup step {i} loss {loss:.4f}", flush=True)
 
-    work = class_work(c, args.sr, args.fused_classifier, args.recompute_gelu)
+    work = class_work(c, args.sr, args.fused_classifier, args.recompute_gelu, args.recompute_layernorm)
     per_class = {}
     # choose the dominant kernel class: one untimed-region step per class
     if args.timing_class == "auto":
@@ -329,6 +338,7 @@ def main():
                                + ("classifier fused with the softmax cross-entropy (logits recomputed in the "
                                   "backward), " if args.fused_classifier else "")
                                + ("GELU output recomputed in the backward, " if args.recompute_gelu else "")
+                               + ("LayerNorm outputs recomputed in the backward, " if args.recompute_layernorm else "")
                                + "Zipf(1.1) synthetic tokens"
                                + (", tokens copied from host memory inside the step" if args.host_tokens else ""),
                    "batch": B, "seq_len": T,

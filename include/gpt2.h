@@ -92,6 +92,13 @@ typedef struct {
                                   GELU' in the fcproj backward-data product ("llm.c's Origin and
                                   the Future of LLM Compilers", "Avengers": recompute settings).
                                   Saves (L-1)*B*T*4C*2 bytes, costs one GELU pass per layer. */
+    int32_t recompute_layernorm; /* 0: the forward keeps every layer's two LayerNorm outputs (the
+                                  qkv and fc inputs their weight gradients read).  1 (bf16 modes
+                                  only): it keeps one layer's of each; the backward runs each
+                                  layer's LayerNorm forwards again (the same kernel on the same
+                                  inputs: the same values) before that layer's qkv and fc weight
+                                  gradients, which then run in the block loop.  Saves
+                                  2*(L-1)*B*T*C*2 bytes (same recompute settings as above). */
 } gpt2_config;
 
 typedef struct gpt2_model gpt2_t;

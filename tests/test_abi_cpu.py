@@ -39,10 +39,10 @@ def test_binding_covers_the_abi():
 
 def _cfg(**kw):
     base = dict(L=12, C=768, NH=12, maxT=1024, V=50257, Vp=50304, B=16, T=1024, precision=G.GPT2_BF16_MIXED,
-                fused=False, recompute=False)
+                fused=False, recompute=False, recompute_ln=False)
     base.update(kw)
     return G.make_config(base["L"], base["C"], base["NH"], base["maxT"], base["V"], base["Vp"], base["B"],
-                         base["T"], base["precision"], base["fused"], base["recompute"])
+                         base["T"], base["precision"], base["fused"], base["recompute"], base["recompute_ln"])
 
 
 def test_plan_sizes():
@@ -115,6 +115,24 @@ def test_plan_recompute_gelu():
     bad = _cfg()
     bad.recompute_gelu = 2
     for cfg, msg in ((_cfg(B=4, T=64, precision=G.GPT2_FP32, recompute=True), "bf16"), (bad, "recompute_gelu")):
+        with pytest.raises(G.GPT2Error) as e:
+            G.gpt2_plan(cfg)
+        assert e.value.code == G.GPT2_EINVAL and msg in str(e.value)
+
+
+def test_plan_recompute_layernorm():
+    # one layer's LN1 and LN2 outputs instead of L: 2 (L - 1) * B*T * C bf16 values
+    # fewer (the grouped tile list loses the qkv and fc tiles, a few KB)
+    L, C, BT = 12, 768, 16 * 1024
+    saved = G.gpt2_plan(_cfg()) - G.gpt2_plan(_cfg(recompute_ln=True))
+    expect = 2 * (L - 1) * BT * C * 2
+    assert expect <= saved <= expect + 65536
+    both = G.gpt2_plan(_cfg()) - G.gpt2_plan(_cfg(recompute=True, recompute_ln=True))
+    assert expect + (L - 1) * BT * 4 * C * 2 <= both <= expect + (L - 1) * BT * 4 * C * 2 + 131072
+    bad = _cfg()
+    bad.recompute_layernorm = 3
+    for cfg, msg in ((_cfg(B=4, T=64, precision=G.GPT2_FP32, recompute_ln=True), "bf16"),
+                     (bad, "recompute_layernorm")):
         with pytest.raises(G.GPT2Error) as e:
             G.gpt2_plan(cfg)
         assert e.value.code == G.GPT2_EINVAL and msg in str(e.value)

@@ -39,8 +39,10 @@ def ocfg(d):
     return O.Config(L=d["L"], C=d["C"], NH=d["NH"], maxT=d["maxT"], V=d["V"], Vp=d["Vp"])
 
 
-def gcfg(d, B, T, prec, fused=False, recompute=False):
-    return G.make_config(d["L"], d["C"], d["NH"], d["maxT"], d["V"], d["Vp"], B, T, prec, fused, recompute)
+def gcfg(d, B, T, prec, fused=False, recompute=""):
+    """recompute: "" (keep every activation), "gelu", "ln" or "gelu+ln"."""
+    return G.make_config(d["L"], d["C"], d["NH"], d["maxT"], d["V"], d["Vp"], B, T, prec, fused,
+                         "gelu" in recompute, "ln" in recompute)
 
 
 def split(flat, cfg):
@@ -246,22 +248,22 @@ FULL = {
 # chunks of up to 4096 rows) on the narrow model (B*T = 16384: four chunks)
 # and the whole 124M model (the full vocabulary, one chunk).
 FUSED = ["narrow", "124m_b1"]
-# The GELU recompute mode (each layer's GELU output formed again in the
-# backward, the fcproj weight gradients in the block loop) on the same two.
-RECOMPUTE = ["narrow", "124m_b1"]
+# The recompute modes (each layer's GELU output and/or LayerNorm outputs
+# formed again in the backward, their weight gradients in the block loop).
+RECOMPUTE = [("narrow", "gelu"), ("narrow", "ln"), ("narrow", "gelu+ln"), ("124m_b1", "gelu+ln")]
 
 
 @pytest.mark.timeout(1200)
 @pytest.mark.parametrize("name,fused,recompute",
-                         [(n, False, False) for n in FULL] + [(n, True, False) for n in FUSED] +
-                         [(n, False, True) for n in RECOMPUTE],
+                         [(n, False, "") for n in FULL] + [(n, True, "") for n in FUSED] +
+                         [(n, False, r) for n, r in RECOMPUTE],
                          ids=list(FULL) + [n + "_fused_classifier" for n in FUSED] +
-                         [n + "_recompute_gelu" for n in RECOMPUTE])
+                         [f"{n}_recompute_{r}" for n, r in RECOMPUTE])
 def test_bf16_gradients_full_token_count(name, fused, recompute):
     cfg, B, T = FULL[name]
     seed = 1337
     print(f"bf16 gradients {name}: L={cfg['L']} C={cfg['C']} NH={cfg['NH']} V={cfg['V']} B={B} T={T} "
-          f"fused classifier {fused} recompute GELU {recompute}", flush=True)
+          f"fused classifier {fused} recompute {recompute or 'none'}", flush=True)
     x, y = synth.batch(seed, 0, B, T, cfg["V"], "zipf")
     m = G.Model(gcfg(cfg, B, T, G.GPT2_BF16_MIXED, fused, recompute), seed)
     loss = m.forward(x, y)
@@ -479,7 +481,7 @@ def test_fused_classifier_training_steps():
     m.close()
 
 
-def gpu_run_mode(cfg, B, T, fused, recompute=False, **kw):
+def gpu_run_mode(cfg, B, T, fused, recompute="", **kw):
     """gpu_run in bf16 mixed mode with or without the fused classifier or the
     GELU recompute (no logits read)."""
     m = G.Model(gcfg(cfg, B, T, G.GPT2_BF16_MIXED, fused, recompute), kw["seed"])
@@ -501,18 +503,18 @@ def gpu_run_mode(cfg, B, T, fused, recompute=False, **kw):
 
 
 @pytest.mark.timeout(900)
-def test_recompute_gelu_training_steps():
-    """Three clipped AdamW steps with the GELU output recomputed in the
-    backward, against the oracle (losses within 1e-2 at each of four
-    forwards, gradients and parameters after the steps within 5e-2 per
-    tensor) and against the mode that keeps the GELU outputs, on the GPU."""
+def test_recompute_training_steps():
+    """Three clipped AdamW steps with the GELU and LayerNorm outputs
+    recomputed in the backward, against the oracle (losses within 1e-2 at
+    each of four forwards, gradients and parameters after the steps within
+    5e-2 per tensor) and against the mode that keeps them, on the GPU."""
     d = dict(L=2, C=128, NH=2, maxT=1024, V=1000, Vp=1024)
     B, T = 8, 1024
     kw = dict(seed=23, dist="zipf", steps=3, lr=3e-4, wd=0.1, clip=1.0, final_loss=True)
-    print(f"recompute GELU training B={B} T={T}", flush=True)
+    print(f"recompute GELU and LayerNorm training B={B} T={T}", flush=True)
     o = oracle_run(d, B, T, **kw)
-    gr = gpu_run_mode(d, B, T, fused=False, recompute=True, **kw)
-    gk = gpu_run_mode(d, B, T, fused=False, recompute=False, **kw)
+    gr = gpu_run_mode(d, B, T, fused=False, recompute="gelu+ln", **kw)
+    gk = gpu_run_mode(d, B, T, fused=False, recompute="", **kw)
     print(f"losses recompute {np.round(gr['losses'], 5)} kept {np.round(gk['losses'], 5)} "
           f"oracle {np.round(o['losses'], 5)}", flush=True)
     for a, b, c in zip(gr["losses"], o["losses"], gk["losses"]):

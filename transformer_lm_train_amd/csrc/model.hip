@@ -123,6 +123,10 @@ int validate(const gpt2_config* c) {
     if (c->recompute_gelu != 0 && c->recompute_gelu != 1) return fail(GPT2_EINVAL, "recompute_gelu must be 0 or 1");
     if (c->recompute_gelu && !is_bf16(c->precision))
         return fail(GPT2_EINVAL, "recompute_gelu needs a bf16 mode");
+    if (c->recompute_layernorm != 0 && c->recompute_layernorm != 1)
+        return fail(GPT2_EINVAL, "recompute_layernorm must be 0 or 1");
+    if (c->recompute_layernorm && !is_bf16(c->precision))
+        return fail(GPT2_EINVAL, "recompute_layernorm needs a bf16 mode");
     if (is_bf16(c->precision)) {
         if (hs != 64) return fail(GPT2_EINVAL, "the bf16 modes need head size 64");
         if (c->channels % 64 || c->padded_vocab_size % 64 || c->seq_len % 64)
@@ -162,11 +166,14 @@ Layout make_layout(const gpt2_config& c) {
     L.v = add(4 * L.N);
     L.shadow = is_bf16(c.precision) ? add(2 * L.N) : 0;
     L.encoded = add(A * BT * C);
-    L.ln1 = add(A * Ly * BT * C);
+    // LayerNorm outputs: every layer's, or with recompute_layernorm one layer's
+    // (formed again by the backward for that layer's weight gradients)
+    const size_t Lln = c.recompute_layernorm ? 1 : Ly;
+    L.ln1 = add(A * Lln * BT * C);
     L.qkv = add(A * Ly * BT * 3 * C);
     L.atty = add(A * Ly * BT * C);
     L.res2 = add(A * Ly * BT * C);
-    L.ln2 = add(A * Ly * BT * C);
+    L.ln2 = add(A * Lln * BT * C);
     L.fch = add(A * Ly * BT * 4 * C);
     // GELU outputs: every layer's, or with recompute_gelu the one layer the
     // next product (forward) or the fcproj weight gradient (backward) reads
@@ -241,7 +248,9 @@ Layout make_layout(const gpt2_config& c) {
     L.encws = add(encoder_bwd_ws_bytes((int)BT, c.vocab_size, (int)C));
     // the fused classifier's run in its chunks; with recompute_gelu the fcproj
     // products run in the block loop, each after its layer's GELU output is recomputed
-    L.dw_n = (c.recompute_gelu ? 3 : 4) * c.num_layers + (c.fused_classifier ? 0 : 1);
+    // (and with recompute_layernorm the qkv and fc products, after their layer's LayerNorms)
+    L.dw_n = (4 - (c.recompute_gelu ? 1 : 0) - (c.recompute_layernorm ? 2 : 0)) * c.num_layers +
+             (c.fused_classifier ? 0 : 1);
     L.dw_probs = add(sizeof(GemmArgs) * L.dw_n);
     L.dw_ntiles = 0;
     if (is_bf16(c.precision)) {
@@ -285,9 +294,11 @@ void dw_problems(const gpt2_config& c, const Layout& L, char* base, GemmArgs* ou
         if (!c.recompute_gelu)
             out[n++] = prob(g + L.poff[P_FCPROJW] + lC * 4 * C, act(L.gres3, (l + 1) * BTC), act(L.fchg, l * BTC * 4),
                             C, 4 * C);
-        out[n++] = prob(g + L.poff[P_FCW] + lC * 4 * C, act(L.gfch, l * BTC * 4), act(L.ln2, l * BTC), 4 * C, C);
+        if (!c.recompute_layernorm)
+            out[n++] = prob(g + L.poff[P_FCW] + lC * 4 * C, act(L.gfch, l * BTC * 4), act(L.ln2, l * BTC), 4 * C, C);
         out[n++] = prob(g + L.poff[P_ATTPROJW] + lC * C, act(L.gres2, l * BTC), act(L.atty, l * BTC), C, C);
-        out[n++] = prob(g + L.poff[P_QKVW] + lC * 3 * C, act(L.gqkv, l * BTC * 3), act(L.ln1, l * BTC), 3 * C, C);
+        if (!c.recompute_layernorm)
+            out[n++] = prob(g + L.poff[P_QKVW] + lC * 3 * C, act(L.gqkv, l * BTC * 3), act(L.ln1, l * BTC), 3 * C, C);
     }
 }
 
@@ -559,11 +570,11 @@ template <typename T> int forward_impl(gpt2_t* M, bool with_targets) {
     }
     const T* x = a.encoded;
     for (int l = 0; l < Ly; l++) {
-        T* ln1 = a.ln1 + l * BTC;
+        T* ln1 = a.ln1 + (c.recompute_layernorm ? 0 : l * BTC);
         T* qkv = a.qkv + l * BTC * 3;
         T* atty = a.atty + l * BTC;
         T* res2 = a.res2 + l * BTC;
-        T* ln2 = a.ln2 + l * BTC;
+        T* ln2 = a.ln2 + (c.recompute_layernorm ? 0 : l * BTC);
         T* fch = a.fch + l * BTC * 4;
         T* fchg = a.fchg + (c.recompute_gelu ? 0 : l * BTC * 4);
         T* res3 = a.res3 + l * BTC;
@@ -658,6 +669,19 @@ template <typename T> int backward_impl(gpt2_t* M) {
 
     // first backward since gpt2_zero_grad: every gradient's one first writer stores
     const bool ow = M->grads_zero;
+    // one weight gradient outside the grouped launch (the recompute modes):
+    // dW[N, K] (+)= dY[BT, N]^T X[BT, K], its reduction split over the workspace
+    auto dw_now = [&](float* dW, const T* dY, int N_, const T* X, int K_) {
+        GemmArgs d{};
+        d.M = N_; d.N = K_; d.K = BT;
+        d.a = dY; d.lda = N_; d.a_kcontig = false;
+        d.b = X; d.ldb = K_; d.b_kcontig = false;
+        d.out = dW; d.ldo = K_; d.epi = EPI_ACC_F32;
+        d.ws = M->P<float>(M->L.splitk);
+        d.ws_bytes = M->L.splitk_bytes;
+        d.acc_overwrite = ow;
+        return gemm<T>(M, d);
+    };
     if (c.fused_classifier) {
         if constexpr (std::is_same<T, bf16>::value) {
             // the logits were never stored: per chunk of rows, recompute them
@@ -731,21 +755,20 @@ template <typename T> int backward_impl(gpt2_t* M) {
                 // this layer's GELU output again, from the kept bf16 pre-activation
                 // (the values the forward's fcproj product read), then its weight gradient
                 RUN("gelu_recompute", gelu_recompute(a.fchg, fch, BTC * 4, s));
-                GemmArgs d{};
-                d.M = C; d.N = 4 * C; d.K = BT;
-                d.a = G3(l); d.lda = C; d.a_kcontig = false;
-                d.b = a.fchg; d.ldb = 4 * C; d.b_kcontig = false;
-                d.out = g + po[P_FCPROJW] + lC * 4 * C; d.ldo = 4 * C; d.epi = EPI_ACC_F32;
-                d.ws = M->P<float>(M->L.splitk);
-                d.ws_bytes = M->L.splitk_bytes;
-                d.acc_overwrite = ow;
-                RUN("gemm_dw", gemm<T>(M, d));
+                RUN("gemm_dw", dw_now(g + po[P_FCPROJW] + lC * 4 * C, G3(l), C, a.fchg, 4 * C));
             }
         }
         if (fused) jobs.push_back(SumJob{{g + po[P_FCB] + lC * 4}, pfc, gemm_colsum_rows(BT, 4 * C), 4 * C});
         // fc: fch = ln2 Wfc^T + b  ->  d ln2
         RUN("gemm_dx", lin_dx<T>(M, a.dmid, GF(l), w + po[P_FCW] + lC * 4 * C, BT, 4 * C, C, EPI_STORE));
         if (!fused) RUN("colsum", colsum_accum<T>(g + po[P_FCB] + lC * 4, GF(l), BT, 4 * C, pfc, s));
+        if (c.recompute_layernorm) {
+            // this layer's LN2 output again (the forward's kernel on the same inputs:
+            // the same values, mean and rstd rewritten unchanged), then the fc weight gradient
+            RUN("layernorm_recompute", layernorm_fwd<T>(a.ln2, a.ln2m + (size_t)l * BT, a.ln2r + (size_t)l * BT, res2,
+                                                        p + pf[P_LN2W] + lC, p + pf[P_LN2B] + lC, BT, C, s));
+            RUN("gemm_dw", dw_now(g + po[P_FCW] + lC * 4 * C, GF(l), 4 * C, a.ln2, C));
+        }
         // ln2: d res2 = d res3 + LN2'(d ln2)
         RUN("layernorm_bwd", layernorm_bwd<T>(G2(l), G3(l), a.dmid, res2, p + pf[P_LN2W] + lC, a.ln2m + (size_t)l * BT,
                                               a.ln2r + (size_t)l * BT, pln2, BT, C, true, s));
@@ -759,6 +782,11 @@ template <typename T> int backward_impl(gpt2_t* M) {
         // qkv: qkv = ln1 Wqkv^T + b  ->  d ln1
         RUN("gemm_dx", lin_dx<T>(M, a.dmid, GQ(l), w + po[P_QKVW] + lC * 3 * C, BT, 3 * C, C, EPI_STORE));
         if (!fused) RUN("colsum", colsum_accum<T>(g + po[P_QKVB] + lC * 3, GQ(l), BT, 3 * C, pqkv, s));
+        if (c.recompute_layernorm) {  // as LN2 above: this layer's LN1 output, then the qkv weight gradient
+            RUN("layernorm_recompute", layernorm_fwd<T>(a.ln1, a.ln1m + (size_t)l * BT, a.ln1r + (size_t)l * BT, xin,
+                                                        p + pf[P_LN1W] + lC, p + pf[P_LN1B] + lC, BT, C, s));
+            RUN("gemm_dw", dw_now(g + po[P_QKVW] + lC * 3 * C, GQ(l), 3 * C, a.ln1, C));
+        }
         // ln1: d xin = d res2 + LN1'(d ln1), whose column sums are the fcproj
         // bias gradient of the block below
         RUN("layernorm_bwd", layernorm_bwd<T>(G3(l - 1), G2(l), a.dmid, xin, p + pf[P_LN1W] + lC,

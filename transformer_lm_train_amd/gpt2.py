@@ -33,7 +33,7 @@ class gpt2_config(ctypes.Structure):
                 ("vocab_size", ctypes.c_int32), ("padded_vocab_size", ctypes.c_int32),
                 ("batch_size", ctypes.c_int32), ("seq_len", ctypes.c_int32),
                 ("precision", ctypes.c_int32), ("fused_classifier", ctypes.c_int32),
-                ("recompute_gelu", ctypes.c_int32)]
+                ("recompute_gelu", ctypes.c_int32), ("recompute_layernorm", ctypes.c_int32)]
 
 
 class GPT2Error(RuntimeError):
@@ -117,9 +117,10 @@ def _iptr(a):
     return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
 
 
-def make_config(L, C, NH, maxT, V, Vp, B, T, precision, fused_classifier=False, recompute_gelu=False):
+def make_config(L, C, NH, maxT, V, Vp, B, T, precision, fused_classifier=False, recompute_gelu=False,
+                recompute_layernorm=False):
     return gpt2_config(L, C, NH, maxT, V, Vp, B, T, precision, 1 if fused_classifier else 0,
-                       1 if recompute_gelu else 0)
+                       1 if recompute_gelu else 0, 1 if recompute_layernorm else 0)
 
 
 # ---- the C ABI, one Python function per entry point ------------------------

@@ -171,6 +171,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="124m", choices=sorted(CONFIGS))
     ap.add_argument("--seed", type=int, default=1337)
+    ap.add_argument("--batch", type=int, default=0,
+                    help="batch size in place of the configuration's (the line's metric names it)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--timing-class", default="auto")
     ap.add_argument("--fused-classifier", action="store_true",
@@ -197,7 +199,9 @@ def main():
     from transformer_lm_train_amd import gpt2 as G
     from transformer_lm_train_amd import synth
 
-    c = CONFIGS[args.config]
+    c = dict(CONFIGS[args.config])
+    if args.batch > 0:
+        c["B"] = args.batch
     torch.cuda.set_device(0)
     prec = G.GPT2_BF16_SR if args.sr else G.GPT2_BF16_MIXED
     cfg = G.make_config(c["L"], c["C"], c["NH"], c["maxT"], c["V"], c["Vp"], c["B"], c["T"], prec,

@@ -256,9 +256,9 @@ RECOMPUTE = [("narrow", "gelu"), ("narrow", "ln"), ("narrow", "gelu+ln"), ("124m
 @pytest.mark.timeout(1200)
 @pytest.mark.parametrize("name,fused,recompute",
                          [(n, False, "") for n in FULL] + [(n, True, "") for n in FUSED] +
-                         [(n, False, r) for n, r in RECOMPUTE],
+                         [(n, False, r) for n, r in RECOMPUTE] + [("narrow", True, "gelu+ln")],
                          ids=list(FULL) + [n + "_fused_classifier" for n in FUSED] +
-                         [f"{n}_recompute_{r}" for n, r in RECOMPUTE])
+                         [f"{n}_recompute_{r}" for n, r in RECOMPUTE] + ["narrow_fused_classifier_recompute_gelu+ln"])
 def test_bf16_gradients_full_token_count(name, fused, recompute):
     cfg, B, T = FULL[name]
     seed = 1337

@@ -527,11 +527,12 @@ def test_recompute_training_steps():
 def test_determinism_fp32_and_bf16():
     """The same step twice gives bit-identical outputs (no LDS race shows up,
     and no float atomics anywhere: the embedding backward sums each token's
-    rows in position order)."""
-    for prec, cfg, B, T in ((G.GPT2_FP32, TINY, 4, 32), (G.GPT2_BF16_MIXED, dict(M124, L=2), 2, 128)):
+    rows in position order), also with the GELU and LayerNorm recomputes."""
+    for prec, cfg, B, T, rc in ((G.GPT2_FP32, TINY, 4, 32, ""), (G.GPT2_BF16_MIXED, dict(M124, L=2), 2, 128, ""),
+                                (G.GPT2_BF16_MIXED, dict(M124, L=2), 2, 128, "gelu+ln")):
         res = []
         for _ in range(2):
-            m = G.Model(gcfg(cfg, B, T, prec), 7)
+            m = G.Model(gcfg(cfg, B, T, prec, recompute=rc), 7)
             x, y = synth.batch(7, 0, B, T, cfg["V"], "zipf")
             loss = m.forward(x, y)
             m.zero_grad()
